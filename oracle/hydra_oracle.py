@@ -1,0 +1,525 @@
+"""Oracle: a plain, slow CPU implementation of one Hydra/Medusa round.
+
+TEST INFRASTRUCTURE ONLY. This module exists to check the device path. Only
+``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import it. The product never calls it, and it shares no code
+with the product (no helpers, tables or constants); the two meet only through
+the seeded arrays that ``hydra_inputs`` generates.
+
+Sources (cited by page title and section):
+
+* [HG] "Hydra Guide: Sequentially-Dependent Speculative AI" (AiFetchly blog).
+* [SD] "Speculative Decoding" (thegustafson.com blog).
+* [MH] "Medusa Heads" (Ultralytics glossary, German).
+
+Arithmetic is float64 throughout. For bfloat16 workloads the inputs arrive
+already rounded to bfloat16, and the oracle rounds to bfloat16 (round to
+nearest even) at exactly the two points where the device path stores a
+bfloat16 tensor: the head hidden state ``u`` and the attention output ``O``.
+Logits, log-sum-exps and cumulative log-probabilities stay float64.
+
+Readings of points the pages leave open (each is listed in the design doc):
+
+* Hydra head form: one layer, ``u = h + SiLU(W1 [h || e(parent)] + b1)``; the
+  residual on ``h`` is the Medusa block with its input widened.
+* The root of the tree is the last known token that is not yet in the KV
+  cache; it is row 0 of the verify pass and attends to the prefix and itself.
+* Ties in top-k and argmax go to the lowest token id; top-k output is sorted by
+  (logit descending, id ascending).
+* Cumulative score of a node is the sum of log-softmax values on its path.
+* Dense tree pruning keeps the root plus the best ``n_keep - 1`` nodes by
+  (cumulative log-prob descending, depth ascending, full-tree index ascending)
+  and renumbers the survivors in breadth-first order.
+* Sparse template: rank paths with ranks below the per-depth fan-out caps,
+  ordered by (2**depth * prod(rank + 1), depth, path) ascending; the first
+  ``n_nodes - 1`` plus the root.
+* Stochastic acceptance on a tree (rule S1): siblings are tried in rank order;
+  after each rejection the target becomes the normalised residual while the
+  draft distribution stays the same.
+
+Parity unpinned: the choice of nodes in the sparse template beyond its
+invariants (it is this build's own construction), and rule S1 on a tree whose
+children are deterministic top-k tokens (the pages prove exactness only for a
+drafted chain).
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+
+import numpy as np
+
+__all__ = [
+    "round_bf16", "silu", "logsumexp", "softmax", "topk_sorted", "topk_margin",
+    "TreePlan", "plan_cartesian", "plan_sparse_template", "head_rows",
+    "head_hidden", "head_logits", "draft_heads", "prune_tree", "ancestors",
+    "tree_mask", "tree_attention", "target_logits", "argmax_lowest",
+    "greedy_accept", "residual", "sample_inverse_cdf", "rejection_accept",
+]
+
+
+# ---------------------------------------------------------------------------
+# Scalar building blocks
+# ---------------------------------------------------------------------------
+
+def round_bf16(x):
+    """Round float64 values to the nearest bfloat16 value, ties to even.
+
+    bfloat16 keeps 8 significant bits (7 stored plus the implicit one) and the
+    float32 exponent range. Written as: split x = m * 2**e with 0.5 <= |m| < 1,
+    round m * 2**8 to the nearest integer (ties to even), scale back.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    m, e = np.frexp(x)
+    return np.ldexp(np.rint(m * 256.0) / 256.0, e)
+
+
+def silu(a):
+    """SiLU(a) = a * sigmoid(a) = a / (1 + exp(-a))  [MH, "So sagen die Köpfe voraus"]."""
+    a = np.asarray(a, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        return a / (1.0 + np.exp(-a))
+
+
+def logsumexp(z):
+    """log(sum(exp(z))) with the maximum factored out."""
+    z = np.asarray(z, dtype=np.float64)
+    m = np.max(z)
+    return float(m + np.log(np.sum(np.exp(z - m))))
+
+
+def softmax(z):
+    z = np.asarray(z, dtype=np.float64)
+    e = np.exp(z - np.max(z))
+    return e / np.sum(e)
+
+
+def topk_sorted(z, k):
+    """Ids of the k largest entries, sorted by (value descending, id ascending).
+
+    [HG, "Candidate Tree Construction"]: head k keeps its top-b_k tokens.
+    np.lexsort sorts by its last key first: -z ascending, then id ascending.
+    """
+    z = np.asarray(z, dtype=np.float64)
+    order = np.lexsort((np.arange(z.shape[0]), -z))
+    return order[:k].astype(np.int64)
+
+
+def topk_margin(z, k):
+    """Smallest gap between consecutive sorted values among the first k+1.
+
+    A top-k decision (which ids, in which order) can only change under a
+    perturbation of z larger than half this gap.
+    """
+    s = np.sort(np.asarray(z, dtype=np.float64))[::-1][: k + 1]
+    if s.shape[0] < 2:
+        return math.inf
+    return float(np.min(s[:-1] - s[1:]))
+
+
+def argmax_lowest(z):
+    """Arg max with ties going to the lowest id."""
+    z = np.asarray(z, dtype=np.float64)
+    return int(np.flatnonzero(z == np.max(z))[0])
+
+
+# ---------------------------------------------------------------------------
+# Tree plans (shape of the candidate tree, independent of token values)
+# ---------------------------------------------------------------------------
+
+@dataclass
+class TreePlan:
+    """A candidate tree in breadth-first order.
+
+    Node 0 is the root. ``parent[i] < i``; the children of a node are
+    contiguous and sorted by ``rank`` (which entry of the parent's top-k list
+    the child takes).
+    """
+    parent: np.ndarray
+    rank: np.ndarray
+    depth: np.ndarray
+
+    @property
+    def n(self) -> int:
+        return int(self.parent.shape[0])
+
+    @property
+    def dmax(self) -> int:
+        return int(self.depth.max())
+
+    def children(self, u):
+        return [int(c) for c in np.flatnonzero(self.parent == u)]
+
+
+def _plan_from_paths(paths):
+    """Build a breadth-first plan from a prefix-closed set of rank paths."""
+    paths = sorted(set(tuple(p) for p in paths), key=lambda p: (len(p), p))
+    index = {(): 0}
+    parent, rank, depth = [-1], [-1], [0]
+    for p in paths:
+        index[p] = len(parent)
+        parent.append(index[p[:-1]])
+        rank.append(p[-1])
+        depth.append(len(p))
+    return TreePlan(np.array(parent), np.array(rank), np.array(depth))
+
+
+def plan_cartesian(b):
+    """Cartesian tree from a branching vector b = [b_1 .. b_K].
+
+    [HG, "Candidate Tree Construction"]: head 1 keeps its top-b_1 tokens and,
+    for every node at depth k-1, head k keeps its top-b_k continuations, so the
+    tree has sum_k prod_{j<=k} b_j candidate nodes (plus the root here).
+    """
+    paths = []
+    frontier = [()]
+    for bk in b:
+        frontier = [p + (r,) for p in frontier for r in range(bk)]
+        paths.extend(frontier)
+    return _plan_from_paths(paths)
+
+
+def plan_sparse_template(caps=(10, 4, 2, 1), n_nodes=64):
+    """Static sparse tree of n_nodes rows (root included).
+
+    [MH, "Tree Attention und Akzeptanz"] only says the 64-node sparse tree is
+    made of the most accurate combinations. With no accuracy statistics, the
+    rank paths are ordered by the prior 2**depth * prod(rank + 1) (then depth,
+    then the path itself) and the first n_nodes - 1 are kept.
+    """
+    cands = []
+    frontier = [()]
+    for cap in caps:
+        frontier = [p + (r,) for p in frontier for r in range(cap)]
+        cands.extend(frontier)
+
+    def key(p):
+        s = 2 ** len(p)
+        for r in p:
+            s *= r + 1
+        return (s, len(p), p)
+
+    cands.sort(key=key)
+    return _plan_from_paths(cands[: n_nodes - 1])
+
+
+def head_rows(plan: TreePlan, hydra: bool):
+    """Head rows of a round: which node each row conditions on, and per node
+    the row whose top-k list gives that node's children.
+
+    Hydra [HG, "Candidate Tree Construction"]: head k runs once for every node
+    at depth k-1 that has children, on [h || e(token of that node)].
+    Medusa [MH, "Tree Attention und Akzeptanz"]: head k reads only h, so one
+    row per depth serves every parent at that depth.
+    Returns (row_node, row_depth, node_row) where row_depth is the head index
+    (1-based) and node_row[u] = -1 for a node without children.
+    """
+    n = plan.n
+    has_child = np.zeros(n, dtype=bool)
+    has_child[plan.parent[1:]] = True
+    node_row = -np.ones(n, dtype=np.int64)
+    row_node, row_depth = [], []
+    if hydra:
+        for u in range(n):
+            if has_child[u]:
+                node_row[u] = len(row_node)
+                row_node.append(u)
+                row_depth.append(int(plan.depth[u]) + 1)
+    else:
+        for k in range(plan.dmax):
+            row_node.append(-1)
+            row_depth.append(k + 1)
+        for u in range(n):
+            if has_child[u]:
+                node_row[u] = int(plan.depth[u])
+    return np.array(row_node), np.array(row_depth), node_row
+
+
+# ---------------------------------------------------------------------------
+# Stage 1: draft heads
+# ---------------------------------------------------------------------------
+
+def head_hidden(h, e, W1, b1, residual=True, bf16=False):
+    """Hidden state of one head row.
+
+    Medusa [MH, "So sagen die Köpfe voraus"]: one feed-forward layer with SiLU
+    and a residual connection, u = h + SiLU(W1 h + b1). Hydra
+    [HG, "1. Embedding Conditioning Mechanics"]: the layer reads
+    [h || e(x_parent)] instead of h. W1 has shape [d, in] (in = d or 2 d).
+    """
+    h = np.asarray(h, dtype=np.float64)
+    x = h if e is None else np.concatenate([h, np.asarray(e, dtype=np.float64)])
+    a = np.asarray(W1, dtype=np.float64) @ x + np.asarray(b1, dtype=np.float64)
+    u = h + silu(a) if residual else silu(a)
+    return round_bf16(u) if bf16 else u
+
+
+def head_logits(u, W2):
+    """Vocabulary projection of a head, z = W2 u (W2 has no bias)."""
+    return np.asarray(W2, dtype=np.float64) @ np.asarray(u, dtype=np.float64)
+
+
+def draft_heads(h, root_tok, E, heads, plan: TreePlan, hydra=True,
+                residual=True, bf16=False, forced_tok=None):
+    """All draft heads of one round, filling the candidate tree.
+
+    h [B, d], root_tok [B], E [V, d] (Hydra only), heads = list of (W1, b1, W2)
+    with head k at index k-1. Node c at depth k takes entry rank[c] of the
+    top-k list of the row that expanded its parent; its cumulative score adds
+    that token's log-softmax to the parent's.
+
+    ``forced_tok`` [B, N] (stage-wise checking): when given, conditioning
+    tokens and cumulative scores follow these tokens instead of the oracle's
+    own decisions, while ``tok`` still reports the oracle's own choice.
+    """
+    B = h.shape[0]
+    N = plan.n
+    row_node, row_depth, node_row = head_rows(plan, hydra)
+    R = len(row_node)
+    d = h.shape[1]
+    V = heads[0][2].shape[0]
+    tok = -np.ones((B, N), dtype=np.int64)
+    logp = np.zeros((B, N), dtype=np.float64)
+    u_all = np.zeros((B, R, d))
+    z_all = np.zeros((B, R, V))
+    lse_all = np.zeros((B, R))
+    margin = np.full((B, R), math.inf)
+    kmax = {}
+    for c in range(1, N):
+        r = node_row[plan.parent[c]]
+        kmax[r] = max(kmax.get(r, 0), int(plan.rank[c]) + 1)
+    for b in range(B):
+        tok[b, 0] = root_tok[b]
+        follow = tok if forced_tok is None else np.asarray(forced_tok)
+        for k in range(1, plan.dmax + 1):
+            W1, b1, W2 = heads[k - 1]
+            for r in np.flatnonzero(row_depth == k):
+                if hydra:
+                    p = row_node[r]
+                    ptok = int(root_tok[b]) if p == 0 else int(follow[b, p])
+                    e = np.asarray(E[ptok], dtype=np.float64)
+                else:
+                    e = None
+                u = head_hidden(h[b], e, W1, b1, residual, bf16)
+                z = head_logits(u, W2)
+                lse = logsumexp(z)
+                u_all[b, r], z_all[b, r], lse_all[b, r] = u, z, lse
+                ids = topk_sorted(z, kmax[r])
+                margin[b, r] = topk_margin(z, kmax[r])
+                for c in range(1, N):
+                    if plan.depth[c] == k and node_row[plan.parent[c]] == r:
+                        tok[b, c] = ids[plan.rank[c]]
+                        t = int(follow[b, c]) if forced_tok is not None else int(tok[b, c])
+                        logp[b, c] = logp[b, plan.parent[c]] + z[t] - lse
+    return dict(tok=tok, logp=logp, u=u_all, z=z_all, lse=lse_all,
+                margin=margin, row_node=row_node, row_depth=row_depth,
+                node_row=node_row)
+
+
+# ---------------------------------------------------------------------------
+# Stage 2: tree build
+# ---------------------------------------------------------------------------
+
+def prune_tree(plan: TreePlan, logp, n_keep):
+    """Keep the root and the best n_keep - 1 candidates, renumbered breadth-first.
+
+    Candidates are ranked by (cumulative log-prob descending, depth ascending,
+    full-tree index ascending); since log-probs are <= 0 a child never beats
+    its parent, so the kept set is closed under taking parents. The survivors
+    are renumbered depth by depth, ordered by (new index of the parent, rank).
+    Returns (kept_plan, src) where src[new] = index in the full tree.
+    """
+    N = plan.n
+    cand = sorted(range(1, N), key=lambda i: (-float(logp[i]), int(plan.depth[i]), i))
+    kept = {0} | set(cand[: n_keep - 1])
+    new_index = {0: 0}
+    src = [0]
+    for k in range(1, plan.dmax + 1):
+        level = [i for i in kept if plan.depth[i] == k]
+        level.sort(key=lambda i: (new_index[int(plan.parent[i])], int(plan.rank[i])))
+        for i in level:
+            new_index[i] = len(src)
+            src.append(i)
+    src = np.array(src)
+    parent = np.array([-1] + [new_index[int(plan.parent[i])] for i in src[1:]])
+    return TreePlan(parent, plan.rank[src].copy(), plan.depth[src].copy()), src
+
+
+def ancestors(parent, dmax):
+    """anc[u][j] = the node at depth j on the path root -> u (u itself at its
+    own depth), -1 beyond depth(u)."""
+    parent = np.asarray(parent)
+    N = parent.shape[0]
+    anc = -np.ones((N, dmax + 1), dtype=np.int64)
+    for u in range(N):
+        chain = [u]
+        while parent[chain[-1]] >= 0:
+            chain.append(int(parent[chain[-1]]))
+        chain.reverse()
+        anc[u, : len(chain)] = chain
+    return anc
+
+
+def tree_mask(parent):
+    """Dense topology mask over the tree nodes [HG, "Tree Attention Matrix with
+    Topology-Aware Causal Masking"]: M(u, v) = 0 if v is an ancestor of u or
+    u == v, and -inf otherwise. parent[i] = -1 marks a node that hangs off the
+    prefix directly."""
+    parent = np.asarray(parent)
+    N = parent.shape[0]
+    M = np.full((N, N), -np.inf)
+    for u in range(N):
+        v = u
+        while v >= 0:
+            M[u, v] = 0.0
+            v = int(parent[v])
+    return M
+
+
+# ---------------------------------------------------------------------------
+# Stage 3: tree-masked attention verify (one attention layer's share)
+# ---------------------------------------------------------------------------
+
+def tree_attention(q, k_tree, v_tree, k_prefix, v_prefix, anc, bf16=False):
+    """Attention of every tree node over the prefix plus its own ancestors.
+
+    [HG, "Tree Attention Matrix with Topology-Aware Causal Masking"]: the tree
+    is flattened after the prefix and node u sees the prompt history and the
+    nodes v with M(u, v) = 0. [MH, "Tree Attention und Akzeptanz"] says the
+    same. Scores are q.k / sqrt(D); softmax over the visible keys.
+
+    q [B, N, Hq, D], k_tree/v_tree [B, N, Hkv, D], k_prefix/v_prefix: per
+    sequence arrays [L_b, Hkv, D], anc [B, N, Dmax+1]. Query head hq reads key
+    head hq // (Hq // Hkv). Returns (O [B, N, Hq, D], lse [B, N, Hq]).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    B, N, Hq, D = q.shape
+    Hkv = k_tree.shape[2]
+    G = Hq // Hkv
+    scale = 1.0 / math.sqrt(D)
+    out = np.zeros((B, N, Hq, D))
+    lse = np.zeros((B, N, Hq))
+    for b in range(B):
+        kp = np.asarray(k_prefix[b], dtype=np.float64)
+        vp = np.asarray(v_prefix[b], dtype=np.float64)
+        kt = np.asarray(k_tree[b], dtype=np.float64)
+        vt = np.asarray(v_tree[b], dtype=np.float64)
+        for hk in range(Hkv):
+            for u in range(N):
+                vis = [int(a) for a in anc[b][u] if a >= 0]
+                keys = np.concatenate([kp[:, hk, :], kt[vis, hk, :]], axis=0)
+                vals = np.concatenate([vp[:, hk, :], vt[vis, hk, :]], axis=0)
+                for hq in range(hk * G, (hk + 1) * G):
+                    s = keys @ q[b, u, hq] * scale
+                    m = np.max(s)
+                    w = np.exp(s - m)
+                    out[b, u, hq] = (w @ vals) / np.sum(w)
+                    lse[b, u, hq] = m + np.log(np.sum(w))
+    if bf16:
+        out = round_bf16(out)
+    return out, lse
+
+
+# ---------------------------------------------------------------------------
+# Stage 4: target projection and acceptance
+# ---------------------------------------------------------------------------
+
+def target_logits(O, W_t):
+    """Target logits of every tree row: Z = W_t O, with O flattened over
+    (query head, head dim) into the hidden size."""
+    O = np.asarray(O, dtype=np.float64)
+    B, N = O.shape[:2]
+    flat = O.reshape(B * N, -1)
+    return (flat @ np.asarray(W_t, dtype=np.float64).T).reshape(B, N, -1)
+
+
+def greedy_accept(Z, tok, parent, dmax):
+    """Greedy longest-accepted-branch walk [HG, "Parallel Verification and
+    Greedy Acceptance Algorithm"].
+
+    From the root: take the target's arg max at the current node; if a child
+    carries that token, accept it and move there; otherwise stop. The target
+    token at the stopping node is emitted as the bonus, so m accepted drafts
+    give m + 1 tokens. Z [N, V], tok [N], parent [N] for one sequence.
+    Returns (m, path, out) with path starting at the root.
+    """
+    u, path, out = 0, [0], []
+    while True:
+        y = argmax_lowest(Z[u])
+        nxt = [c for c in range(len(parent)) if parent[c] == u and tok[c] == y]
+        out.append(y)
+        if not nxt:
+            break
+        u = nxt[0]
+        path.append(u)
+    m = len(path) - 1
+    assert m <= dmax
+    return m, path, out
+
+
+def residual(r, q):
+    """Residual target after a rejection [SD, "The acceptance criterion" and
+    "The correctness guarantee"]: norm(max(r - q, 0)). Returns None when the
+    residual has no mass."""
+    res = np.maximum(np.asarray(r, dtype=np.float64) - np.asarray(q, dtype=np.float64), 0.0)
+    s = np.sum(res)
+    return None if s <= 0.0 else res / s
+
+
+def sample_inverse_cdf(r, u):
+    """Inverse-CDF draw: the smallest id x with sum_{y<=x} r(y) > u * sum(r),
+    scanning ids in ascending order."""
+    r = np.asarray(r, dtype=np.float64)
+    c = np.cumsum(r)
+    thr = u * c[-1]
+    for x in range(r.shape[0]):
+        if c[x] > thr:
+            return x
+    return int(np.flatnonzero(r > 0)[-1])
+
+
+def rejection_accept(Z, head_z, q_row, tok, parent, u_acc, u_res, T):
+    """Stochastic acceptance on a tree (rule S1), for one sequence.
+
+    Chain rule [SD, "The acceptance criterion"]: accept a drafted token x with
+    probability min(1, p(x)/q(x)); on rejection resample from
+    norm(max(p - q, 0)) and discard the rest. With a uniform draw u the test
+    "u < p/q" is written without a division as u * q(x) < p(x). Both p and q
+    are the post-temperature distributions [SD, "Common misconceptions"].
+
+    On a tree the children of the current node are tried in rank order; after
+    each rejection the target becomes the residual and q stays the same. At a
+    node without children, or after every child is rejected, one token is
+    drawn from the current target with that node's residual uniform. If a
+    residual has no mass, the draw uses the target before that rejection.
+
+    Z [N, V] target logits, head_z [R, V] head logits, q_row [N] the head row
+    whose distribution drafted each node's children, u_acc [N] (used when the
+    node is tested as a child), u_res [N] (used when a draw happens at it).
+    Returns (m, path, out).
+    """
+    u, path, out = 0, [0], []
+    while True:
+        p = softmax(np.asarray(Z[u], dtype=np.float64) / T)
+        kids = [c for c in range(len(parent)) if parent[c] == u]
+        if not kids:
+            out.append(sample_inverse_cdf(p, u_res[u]))
+            break
+        q = softmax(np.asarray(head_z[q_row[u]], dtype=np.float64) / T)
+        r = p
+        moved = False
+        for c in kids:
+            x = int(tok[c])
+            if u_acc[c] * q[x] < r[x]:
+                out.append(x)
+                path.append(c)
+                u = c
+                moved = True
+                break
+            nr = residual(r, q)
+            if nr is not None:
+                r = nr
+        if not moved:
+            out.append(sample_inverse_cdf(r, u_res[u]))
+            break
+    return len(path) - 1, path, out

@@ -1,0 +1,483 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Each test checks the oracle against something other than itself: values the
+pages print (fixtures under tests/golden/), library routines (torch, numpy,
+scipy), closed forms, or brute force on small inputs. Chosen so that a dropped
+term, a wrong sign or index, or a transposed operand fails at least one.
+"""
+import math
+
+import numpy as np
+import pytest
+import scipy.stats
+import torch
+
+import oracle
+from oracle import hydra_oracle as H
+
+
+# --------------------------------------------------------------------- scalars
+
+def test_round_bf16_matches_torch_conversion():
+    rng = np.random.default_rng(0)
+    x = (rng.standard_normal(200000) * 10.0 ** rng.integers(-6, 6, 200000)).astype(np.float32)
+    # exact ties: low 16 bits = 0x8000 with both parities of the kept lsb
+    bits = rng.integers(0, 2**31, 20000, dtype=np.uint64).astype(np.uint32)
+    bits = (bits & np.uint32(0xFFFF0000)) | np.uint32(0x8000)
+    ties = bits.view(np.float32)
+    ties = ties[np.isfinite(ties) & (np.abs(ties) > 1e-30) & (np.abs(ties) < 1e30)]
+    x = np.concatenate([x, ties, -ties])
+    ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
+    got = H.round_bf16(x.astype(np.float64))
+    assert np.array_equal(got, ref)
+
+
+def test_silu_matches_torch():
+    a = np.linspace(-40, 40, 10001)
+    ref = torch.nn.functional.silu(torch.from_numpy(a)).numpy()
+    assert np.allclose(H.silu(a), ref, rtol=1e-14, atol=1e-300)
+
+
+def test_topk_sorted_matches_stable_argsort_and_ties():
+    rng = np.random.default_rng(1)
+    for _ in range(50):
+        z = rng.integers(0, 20, 300).astype(np.float64)  # many ties
+        k = int(rng.integers(1, 30))
+        ref = np.argsort(-z, kind="stable")[:k]
+        assert np.array_equal(H.topk_sorted(z, k), ref)
+    z = np.array([1.0, 3.0, 3.0, 2.0, 3.0])
+    assert list(H.topk_sorted(z, 4)) == [1, 2, 4, 3]
+    assert H.argmax_lowest(z) == 1
+
+
+def test_logsumexp_matches_scipy():
+    rng = np.random.default_rng(2)
+    z = rng.standard_normal(5000) * 30
+    assert math.isclose(H.logsumexp(z), float(scipy.special.logsumexp(z)), rel_tol=1e-13)
+
+
+def test_inverse_cdf_matches_searchsorted():
+    rng = np.random.default_rng(3)
+    for _ in range(200):
+        r = rng.random(37) * (rng.random(37) < 0.6)
+        if r.sum() == 0:
+            continue
+        u = rng.random()
+        ref = int(np.searchsorted(np.cumsum(r), u * r.sum(), side="right"))
+        assert H.sample_inverse_cdf(r, u) == ref
+
+
+# ------------------------------------------------------------------- heads
+
+def test_medusa_zero_init_reproduces_lm_head(golden):
+    spec = dict(ln.split(None, 1) for ln in golden("medusa_zero_init.txt"))
+    d, V, K = int(spec["hidden"]), int(spec["vocab"]), int(spec["heads"])
+    expected = [s == "True" for s in spec["expected"].split()]
+    rng = np.random.default_rng(4)
+    lm_head = rng.standard_normal((V, d)) * 0.02
+    h = rng.standard_normal(d)
+    # The page applies one projection routine to u and to h; the check is exact
+    # because the zero-initialised layer leaves u bit-identical to h.
+    base = H.head_logits(h, lm_head)
+    got = []
+    for _ in range(K):
+        u = H.head_hidden(h, None, np.zeros((d, d)), np.zeros(d))
+        assert np.array_equal(u, h)
+        got.append(bool(np.array_equal(H.head_logits(u, lm_head), base)))
+    assert got == expected
+    # and the projection is the base model's head (torch's routine, to rounding)
+    ref = (torch.from_numpy(lm_head) @ torch.from_numpy(h)).numpy()
+    assert np.allclose(base, ref, rtol=0, atol=1e-12)
+    # Hydra head under the same initialisation (wider input) reduces the same way
+    e = rng.standard_normal(d)
+    u = H.head_hidden(h, e, np.zeros((d, 2 * d)), np.zeros(d))
+    assert np.array_equal(u, h) and np.array_equal(H.head_logits(u, lm_head), base)
+    # the residual connection is what makes it exact: without it, logits vanish
+    u0 = H.head_hidden(h, None, np.zeros((d, d)), np.zeros(d), residual=False)
+    assert not np.array_equal(H.head_logits(u0, lm_head), base)
+
+
+def test_head_matches_torch_modules():
+    rng = np.random.default_rng(5)
+    d, V = 48, 97
+    for hydra in (False, True):
+        ind = 2 * d if hydra else d
+        lin1 = torch.nn.Linear(ind, d).double()
+        lin2 = torch.nn.Linear(d, V, bias=False).double()
+        h = rng.standard_normal(d)
+        e = rng.standard_normal(d) if hydra else None
+        x = torch.from_numpy(np.concatenate([h, e]) if hydra else h)
+        ref = lin2(torch.from_numpy(h) + torch.nn.functional.silu(lin1(x))).detach().numpy()
+        u = H.head_hidden(h, e, lin1.weight.detach().numpy(), lin1.bias.detach().numpy())
+        got = H.head_logits(u, lin2.weight.detach().numpy())
+        assert np.allclose(got, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_head_bf16_rounds_hidden_state():
+    rng = np.random.default_rng(6)
+    d = 32
+    W1, b1 = rng.standard_normal((d, d)), rng.standard_normal(d)
+    h = rng.standard_normal(d)
+    u = H.head_hidden(h, None, W1, b1, bf16=True)
+    ref = torch.from_numpy(h + H.silu(W1 @ h + b1)).float().to(torch.bfloat16).double().numpy()
+    assert np.array_equal(u, ref)
+
+
+# -------------------------------------------------------------------- trees
+
+def test_cartesian_counts(golden):
+    for ln in golden("tree_counts.txt"):
+        b, total, per = [s.strip() for s in ln.split("|")]
+        b = [int(x) for x in b.split(",")]
+        plan = H.plan_cartesian(b)
+        assert plan.n - 1 == int(total)
+        counts = [int(np.sum(plan.depth == k)) for k in range(1, len(b) + 1)]
+        assert counts == [int(x) for x in per.split()]
+    rng = np.random.default_rng(7)
+    for _ in range(20):
+        b = list(rng.integers(1, 5, rng.integers(1, 5)))
+        closed = sum(math.prod(b[: k + 1]) for k in range(len(b)))
+        assert H.plan_cartesian(b).n - 1 == closed
+
+
+def test_cartesian_2x3_six_candidates_share_prefixes():
+    plan = H.plan_cartesian([2, 3])
+    leaves = [u for u in range(plan.n) if not plan.children(u)]
+    assert len(leaves) == 6
+    d1 = plan.children(0)
+    assert len(d1) == 2
+    for a in d1:
+        assert [int(plan.rank[c]) for c in plan.children(a)] == [0, 1, 2]
+    paths = {tuple(int(x) for x in H.ancestors(plan.parent, 2)[u]) for u in leaves}
+    assert len(paths) == 6 and {p[1] for p in paths} == set(d1)
+
+
+def _tiny_heads(rng, d, V, K, hydra):
+    ind = 2 * d if hydra else d
+    return [(rng.standard_normal((d, ind)) * 0.02, rng.standard_normal(d) * 0.02,
+             rng.standard_normal((V, d)) * 0.02) for _ in range(K)]
+
+
+def test_medusa_same_tokens_under_every_parent():
+    rng = np.random.default_rng(8)
+    d, V = 64, 200
+    plan = H.plan_cartesian([2, 3])
+    h = rng.standard_normal((1, d))
+    E = rng.standard_normal((V, d))
+    res = H.draft_heads(h, [5], E, _tiny_heads(rng, d, V, 3, False), plan, hydra=False)
+    sets = [tuple(res["tok"][0, plan.children(a)]) for a in plan.children(0)]
+    assert sets[0] == sets[1]
+    # Hydra conditions head 2 on the parent token: lists differ under each parent
+    heads = [(W1 * 25.0, b1, W2) for W1, b1, W2 in _tiny_heads(rng, d, V, 3, True)]
+    res = H.draft_heads(h, [5], E, heads, plan, hydra=True)
+    sets = [tuple(res["tok"][0, plan.children(a)]) for a in plan.children(0)]
+    assert sets[0] != sets[1]
+    # depth-1 node tokens are head 1's top-2 and depth-2 its rows' top-3
+    for a in plan.children(0):
+        z = res["z"][0, res["node_row"][a]]
+        assert list(res["tok"][0, plan.children(a)]) == list(np.argsort(-z, kind="stable")[:3])
+
+
+def test_cumulative_logp_is_sum_of_log_softmax():
+    rng = np.random.default_rng(9)
+    d, V = 32, 50
+    plan = H.plan_cartesian([3, 2, 2])
+    h = rng.standard_normal((1, d))
+    E = rng.standard_normal((V, d))
+    res = H.draft_heads(h, [7], E, _tiny_heads(rng, d, V, 3, True), plan)
+    for c in range(1, plan.n):
+        chain = [int(a) for a in H.ancestors(plan.parent, 3)[c] if a >= 0]
+        tot = 0.0
+        for a, b in zip(chain[:-1], chain[1:]):
+            z = torch.from_numpy(res["z"][0, res["node_row"][a]])
+            tot += float(torch.log_softmax(z, 0)[res["tok"][0, b]])
+        assert math.isclose(res["logp"][0, c], tot, rel_tol=1e-12, abs_tol=1e-12)
+
+
+def test_sparse_template_invariants():
+    plan = H.plan_sparse_template((10, 4, 2, 1), 64)
+    assert plan.n == 64
+    assert all(plan.parent[i] < i for i in range(1, 64))
+    assert [int(np.sum(plan.depth == k)) for k in range(1, 5)] == [10, 27, 20, 6]
+    fan = {}
+    for u in range(64):
+        kids = plan.children(u)
+        if kids:
+            assert kids == list(range(kids[0], kids[0] + len(kids)))
+            assert [int(plan.rank[c]) for c in kids] == list(range(len(kids)))
+            k = int(plan.depth[u]) + 1
+            fan[k] = max(fan.get(k, 0), len(kids))
+    assert fan == {1: 10, 2: 4, 3: 2, 4: 1}
+    _, row_depth, _ = H.head_rows(plan, True)
+    assert [int(np.sum(row_depth == k)) for k in range(1, 5)] == [1, 10, 13, 6]
+    _, row_depth, _ = H.head_rows(plan, False)
+    assert list(row_depth) == [1, 2, 3, 4]
+
+
+def _brute_prune(plan, logp, n_keep):
+    recs = np.array([(-logp[i], plan.depth[i], i) for i in range(1, plan.n)],
+                    dtype=[("a", "f8"), ("b", "i8"), ("c", "i8")])
+    order = np.argsort(recs, order=("a", "b", "c"))
+    return {0} | {int(recs[j]["c"]) for j in order[: n_keep - 1]}
+
+
+def test_prune_matches_brute_force():
+    rng = np.random.default_rng(10)
+    plan = H.plan_cartesian([4, 4, 4, 4])
+    assert plan.n == 341
+    for trial in range(20):
+        step = np.log(rng.dirichlet(np.ones(4), size=plan.n))
+        if trial % 4 == 0:
+            step = np.round(step, 1)  # force ties
+        logp = np.zeros(plan.n)
+        for c in range(1, plan.n):
+            logp[c] = logp[plan.parent[c]] + step[plan.parent[c], plan.rank[c]]
+        kept, src = H.prune_tree(plan, logp, 256)
+        assert set(int(s) for s in src) == _brute_prune(plan, logp, 256)
+        assert kept.n == 256
+        # breadth-first: parents first, depth non-decreasing, siblings by rank
+        assert all(kept.parent[i] < i for i in range(1, 256))
+        assert all(np.diff(kept.depth) >= 0)
+        for i in range(1, 256):
+            assert src[kept.parent[i]] == plan.parent[src[i]]
+        for i in range(2, 256):
+            if kept.parent[i] == kept.parent[i - 1]:
+                assert kept.rank[i] > kept.rank[i - 1]
+            elif kept.depth[i] == kept.depth[i - 1]:
+                assert kept.parent[i] > kept.parent[i - 1]
+
+
+def test_ancestors_follow_parent_chain():
+    plan = H.plan_sparse_template((10, 4, 2, 1), 64)
+    anc = H.ancestors(plan.parent, 4)
+    for u in range(64):
+        d = int(plan.depth[u])
+        assert anc[u, d] == u and anc[u, 0] == 0
+        assert all(anc[u, d + 1:] == -1)
+        for j in range(1, d + 1):
+            assert plan.parent[anc[u, j]] == anc[u, j - 1]
+
+
+def test_tree_mask_matches_printed_table(golden):
+    names, parents, rows = [], [], []
+    for ln in golden("tree_mask_2x2.txt"):
+        left, right = ln.split("|")
+        nm, par = left.split()
+        names.append(nm)
+        parents.append(par)
+        rows.append([0.0 if t == "0" else -np.inf for t in right.split()])
+    parent = [-1 if p == "-" else names.index(p) for p in parents]
+    M = H.tree_mask(parent)
+    printed = np.array(rows)
+    assert np.all(printed[:, 0] == 0.0)  # every node sees the prompt history
+    assert np.array_equal(M, printed[:, 1:])
+
+
+# ---------------------------------------------------------------- attention
+
+def _causal_sdpa(q, k, v):
+    """torch's attention with a causal mask; q [S, H, D], k/v [S, Hkv, D]."""
+    G = q.shape[1] // k.shape[1]
+    k = k.repeat_interleave(G, dim=1)
+    v = v.repeat_interleave(G, dim=1)
+    o = torch.nn.functional.scaled_dot_product_attention(
+        q.transpose(0, 1), k.transpose(0, 1), v.transpose(0, 1), is_causal=True)
+    return o.transpose(0, 1)
+
+
+@pytest.mark.parametrize("L,tree", [(11, [2, 3]), (0, [2, 2, 2]), (5, [1, 1, 1, 1]), (7, [])])
+def test_tree_attention_equals_causal_attention_per_branch(L, tree):
+    rng = np.random.default_rng(11 + L)
+    plan = H.plan_cartesian(tree) if tree else H.TreePlan(np.array([-1]), np.array([-1]), np.array([0]))
+    N, Hq, Hkv, D, B = plan.n, 4, 2, 16, 2
+    dmax = max(plan.dmax, 1)
+    q = rng.standard_normal((B, N, Hq, D))
+    kt, vt = rng.standard_normal((B, N, Hkv, D)), rng.standard_normal((B, N, Hkv, D))
+    kp = [rng.standard_normal((L, Hkv, D)) for _ in range(B)]
+    vp = [rng.standard_normal((L, Hkv, D)) for _ in range(B)]
+    anc = np.stack([H.ancestors(plan.parent, dmax)] * B)
+    out, lse = H.tree_attention(q, kt, vt, kp, vp, anc)
+    for b in range(B):
+        for leaf in [u for u in range(N) if not plan.children(u)]:
+            branch = [int(a) for a in anc[b, leaf] if a >= 0]
+            qs = torch.from_numpy(np.concatenate([np.zeros((L, Hq, D)), q[b, branch]]))
+            ks = torch.from_numpy(np.concatenate([kp[b], kt[b, branch]]))
+            vs = torch.from_numpy(np.concatenate([vp[b], vt[b, branch]]))
+            ref = _causal_sdpa(qs, ks, vs).numpy()[L:]
+            assert np.allclose(out[b, branch], ref, rtol=1e-10, atol=1e-12)
+    if N == 1:  # single-query decode: softmax over the prefix plus the row itself
+        s = np.concatenate([kp[0][:, 0], kt[0, [0], 0]]) @ q[0, 0, 0] / 4.0
+        assert math.isclose(lse[0, 0, 0], float(scipy.special.logsumexp(s)), rel_tol=1e-12)
+
+
+# --------------------------------------------------------------- acceptance
+
+def _planted_Z(rng, plan, tok, path, stop_tok, V):
+    Z = rng.standard_normal((plan.n, V))
+    for a, b in zip(path[:-1], path[1:]):
+        Z[a, tok[b]] = 50.0
+    Z[path[-1], stop_tok] = 50.0
+    return Z
+
+
+def test_greedy_planted_paths():
+    rng = np.random.default_rng(12)
+    V = 40
+    plan = H.plan_sparse_template((4, 3, 2, 1), 30)
+    anc = H.ancestors(plan.parent, plan.dmax)
+    for trial in range(200):
+        tok = np.zeros(plan.n, dtype=np.int64)
+        for u in range(plan.n):
+            kids = plan.children(u)
+            tok[kids] = rng.choice(V, len(kids), replace=False)
+        target = int(rng.integers(0, plan.n))
+        path = [int(a) for a in anc[target] if a >= 0]
+        kid_toks = {int(tok[c]) for c in plan.children(target)}
+        stop = int(rng.choice([t for t in range(V) if t not in kid_toks]))
+        Z = _planted_Z(rng, plan, tok, path, stop, V)
+        m, got_path, out = H.greedy_accept(Z, tok, plan.parent, plan.dmax)
+        assert m == len(path) - 1 and got_path == path
+        assert out == [int(tok[c]) for c in path[1:]] + [stop]
+
+
+def test_greedy_chain_is_longest_matching_prefix():
+    rng = np.random.default_rng(13)
+    V, k = 6, 5
+    plan = H.plan_cartesian([1] * k)
+    for _ in range(300):
+        tok = rng.integers(0, V, k + 1)
+        Z = rng.standard_normal((k + 1, V))
+        m, _, out = H.greedy_accept(Z, tok, plan.parent, k)
+        top = Z.argmax(axis=1)
+        expect = 0
+        while expect < k and tok[expect + 1] == top[expect]:
+            expect += 1
+        assert m == expect and out[-1] == top[expect] and len(out) == m + 1
+
+
+def _chain_case(p_rows, q_rows, toks):
+    """Chain tree: node i+1 carries toks[i]; Z[i] = log p_rows[i]; head row i =
+    log q_rows[i]."""
+    k = len(toks)
+    parent = np.arange(-1, k)
+    tok = np.array([0] + list(toks))
+    with np.errstate(divide="ignore"):
+        Z = np.log(np.asarray(p_rows, dtype=np.float64))
+        hz = np.log(np.asarray(q_rows, dtype=np.float64))
+    q_row = np.array(list(range(k)) + [-1])
+    return parent, tok, Z, hz, q_row
+
+
+def test_rejection_worked_example(golden):
+    rows = [ln.split() for ln in golden("rejection_worked_example.txt")]
+    total = int(rows[-1][1])
+    drafted = rows[:-1]
+    V = 10
+    words = [r[0] for r in drafted]
+    ids = {w: i for i, w in enumerate(words)}  # The=0 cat=1 sat=2 on=3 the=4
+    ids["down"] = 7
+    p_rows, q_rows = [], []
+    for i, r in enumerate(drafted):
+        p, q = np.full(V, 0.0), np.full(V, 0.0)
+        if r[1] != "-":
+            p[ids[r[0]]], q[ids[r[0]]] = float(r[1]), float(r[2])
+        if r[0] == "on":  # the residual puts its mass where p exceeds q
+            p[ids["down"]] += 0.5
+            q[ids["down"]] += 0.05
+        p += (1.0 - p.sum()) / V
+        q += (1.0 - q.sum()) / V
+        p_rows.append(p)
+        q_rows.append(q)
+    p_rows.append(np.full(V, 1.0 / V))  # after the last drafted token
+    toks = [ids[w] for w in words]
+    parent, tok, Z, hz, q_row = _chain_case(p_rows, q_rows, toks)
+    n = len(tok)
+    # the coin for "on" comes up reject: any u above p/q = 1/3 of that token
+    pq = p_rows[3][ids["on"]] / q_rows[3][ids["on"]]
+    u_acc = np.full(n, 0.99)
+    u_acc[4] = 0.5
+    assert u_acc[4] >= pq
+    res = H.residual(p_rows[3], q_rows[3])
+    u_res = np.zeros(n)
+    u_res[3] = (np.cumsum(res)[ids["down"] - 1] + 0.5 * res[ids["down"]]) / res.sum()
+    m, path, out = H.rejection_accept(Z, hz, q_row, tok, parent, u_acc, u_res, 1.0)
+    verdict = [r[3] for r in drafted]
+    assert m == verdict.count("accept") == 3
+    assert len(out) == total
+    assert out[:3] == toks[:3] and out[3] == ids["down"]
+    assert p_rows[3][out[3]] > q_rows[3][out[3]]  # drawn from the residual support
+    # a coin below p/q accepts "on" instead
+    u_acc[4] = 0.3
+    m2, _, out2 = H.rejection_accept(Z, hz, q_row, tok, parent, u_acc, u_res, 1.0)
+    assert m2 >= 4 and out2[3] == ids["on"]
+
+
+def _first_token_histogram(p, q, trials, rng):
+    parent, tok, Z, hz, q_row = _chain_case([p, p], [q], [0])
+    counts = np.zeros(len(p))
+    cq = np.cumsum(q)
+    for _ in range(trials):
+        x = int(np.searchsorted(cq, rng.random() * cq[-1], side="right"))
+        tok[1] = x
+        u = rng.random(2)
+        _, _, out = H.rejection_accept(Z, hz, q_row, tok, parent, u, rng.random(2), 1.0)
+        counts[out[0]] += 1
+    return counts
+
+
+def test_rejection_identity_chi_square(monkeypatch):
+    rng = np.random.default_rng(14)
+    V = 8
+    p = rng.dirichlet(np.ones(V))
+    q = rng.dirichlet(np.ones(V) * 0.3)
+    alpha = np.minimum(p, q).sum()
+    assert 0.2 < alpha < 0.9
+    trials = 20000
+    counts = _first_token_histogram(p, q, trials, rng)
+    assert scipy.stats.chisquare(counts, p * trials).pvalue > 1e-3
+    # planted mistake: resample from the target itself instead of the residual
+    monkeypatch.setattr(H, "residual", lambda r, qq: np.asarray(r, dtype=np.float64))
+    naive = _first_token_histogram(p, q, trials, rng)
+    assert scipy.stats.chisquare(naive, p * trials).pvalue < 1e-6
+    mix = np.minimum(p, q) + (1 - alpha) * p  # the pages' closed form for this mistake
+    assert scipy.stats.chisquare(naive, mix * trials).pvalue > 1e-3
+
+
+def test_rejection_equal_distributions_never_resample():
+    rng = np.random.default_rng(15)
+    V = 6
+    for _ in range(200):
+        p = rng.dirichlet(np.ones(V))
+        parent, tok, Z, hz, q_row = _chain_case([p, p], [p], [int(rng.integers(V))])
+        m, _, _ = H.rejection_accept(Z, hz, q_row, tok, parent, rng.random(2), rng.random(2), 1.0)
+        assert m == 1  # alpha = 1: p >= q everywhere, the draft is always accepted
+        q = rng.dirichlet(np.ones(V))
+        x = int(np.argmax(p - q))  # a token with p >= q
+        parent, tok, Z, hz, q_row = _chain_case([p, p], [q], [x])
+        m, _, _ = H.rejection_accept(Z, hz, q_row, tok, parent, rng.random(2), rng.random(2), 1.0)
+        assert m == 1
+
+
+def test_expected_yield_monte_carlo(golden):
+    rng = np.random.default_rng(16)
+    trials = 6000
+    for ln in golden("yield_examples.txt"):
+        alpha, k, printed = float(ln.split()[0]), int(ln.split()[1]), float(ln.split()[2])
+        # closed form (1 - alpha^(k+1)) / (1 - alpha), reading of the garbled formula
+        assert round((1 - alpha ** (k + 1)) / (1 - alpha), 1) == printed
+        V = 4
+        q = np.array([1.0, 1e-300, 1e-300, 1e-300])
+        p = np.array([alpha] + [(1 - alpha) / 3] * 3)
+        parent, tok, Z, hz, q_row = _chain_case([p] * (k + 1), [q] * k, [0] * k)
+        n_out = []
+        for _ in range(trials):
+            _, _, out = H.rejection_accept(Z, hz, q_row, tok, parent, rng.random(k + 1),
+                                           rng.random(k + 1), 1.0)
+            n_out.append(len(out))
+        mean, se = np.mean(n_out), np.std(n_out) / math.sqrt(trials)
+        assert abs(mean - printed) < 0.05 + 4 * se, (alpha, k, mean)
+
+
+def test_oracle_package_exports():
+    for name in H.__all__:
+        assert hasattr(oracle, name)

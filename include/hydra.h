@@ -1,0 +1,287 @@
+/*
+ * hydra.h - C ABI of libhydra: one Hydra/Medusa draft-and-verify round on an
+ * AMD Instinct MI355X (gfx950).
+ *
+ * A round has four stages, one entry point each:
+ *   hydra_draft_heads      draft heads + per-head top-k, filling the candidate tree
+ *   tree_build             final tree (identity or pruned), ancestor table
+ *   tree_attention_verify  tree-masked attention over a paged KV prefix
+ *   tree_accept            target vocabulary projection + acceptance walk
+ * plus host-side tree-plan builders, workspace-size queries and status strings.
+ *
+ * Sources (cited by page title and section):
+ *   [HG] "Hydra Guide: Sequentially-Dependent Speculative AI" (AiFetchly blog)
+ *   [SD] "Speculative Decoding" (thegustafson.com blog)
+ *   [MH] "Medusa Heads" (Ultralytics glossary)
+ *
+ * Conventions for every entry point
+ *   - Pointers are DEVICE pointers unless marked "host". The caller owns every
+ *     buffer; the library allocates and frees nothing. Scratch memory comes
+ *     from a caller-provided workspace `ws` of at least the size the matching
+ *     *_workspace_size query returns (ws may be NULL when that size is 0).
+ *   - Work is enqueued on `stream` (a hipStream_t passed as void*; NULL = the
+ *     null stream) and the call returns without synchronising. Faults inside
+ *     kernels surface at the caller's next synchronisation.
+ *   - Return value: HYDRA_OK (0) or a negative HYDRA_ERR_* code. On error no
+ *     work has been enqueued (argument checks happen first) except for
+ *     HYDRA_ERR_HIP, which reports a failed launch. hydra_last_error()
+ *     returns a thread-local message describing the last failure.
+ *   - Layouts are row-major and dense. dtype selects the element type of the
+ *     activation and weight tensors: HYDRA_F32 (float) or HYDRA_BF16
+ *     (bfloat16 bits in uint16). Logits, log-sum-exps and cumulative
+ *     log-probabilities are always float32; token ids and indices int32.
+ *   - Entry points are stateless and reentrant; calls that share a workspace
+ *     must be ordered on one stream.
+ */
+#ifndef HYDRA_H
+#define HYDRA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define HYDRA_OK 0
+#define HYDRA_ERR_INVALID (-1)     /* bad pointer, size or index */
+#define HYDRA_ERR_UNSUPPORTED (-2) /* valid but unsupported shape or dtype */
+#define HYDRA_ERR_WORKSPACE (-3)   /* workspace smaller than required */
+#define HYDRA_ERR_HIP (-4)         /* a HIP launch failed */
+
+#define HYDRA_F32 0
+#define HYDRA_BF16 1
+
+#define HYDRA_MAX_DEPTH 8     /* deepest tree (number of draft heads used) */
+#define HYDRA_MAX_TOPK 16     /* widest fan-out of one node */
+#define HYDRA_MAX_TREE 1024   /* nodes of a candidate tree before pruning */
+#define HYDRA_MAX_VERIFY 256  /* rows of the tree that is verified */
+
+/* Human-readable name of a status code (static string). */
+const char* hydra_status_string(int code);
+/* Message of the last failing call on this thread ("" if none). */
+const char* hydra_last_error(void);
+/* Version of this interface; bumps when a signature changes. */
+int hydra_abi_version(void);
+
+/* ------------------------------------------------------------------------
+ * Tree plans (host only, no device work)
+ *
+ * A plan is the shape of a candidate tree, independent of token values, in
+ * breadth-first order: node 0 is the root (the last known token, not yet in
+ * the KV cache); parent[i] < i; the children of a node are contiguous and
+ * sorted by rank, where rank is the entry of the parent's top-k list that the
+ * child takes. All arrays are host int32 of length max_nodes (capacity).
+ * Return value: number of nodes N (> 0), or a negative error code.
+ * ---------------------------------------------------------------------- */
+
+/* Cartesian tree from a branching vector b[0..K-1]: head k keeps its top-b_k
+ * continuations of every node at depth k-1, giving sum_k prod_{j<=k} b_j
+ * candidates plus the root ([HG] "Candidate Tree Construction"; [MH] "Tree
+ * Attention und Akzeptanz", top-2 x top-3 = six candidates). */
+int hydra_plan_cartesian(const int32_t* b, int K, int max_nodes,
+                         int32_t* parent, int32_t* rank, int32_t* depth);
+
+/* Static sparse tree of n_nodes rows, root included ([MH] "Tree Attention und
+ * Akzeptanz": a 64-node sparse tree of the most accurate combinations). With no
+ * accuracy statistics available, rank paths (r_1..r_d) with r_j < caps[j-1]
+ * are ordered by (2^d * prod(r_j + 1), d, path) ascending and the first
+ * n_nodes - 1 are kept. caps[0..K-1], K <= HYDRA_MAX_DEPTH. */
+int hydra_plan_sparse(const int32_t* caps, int K, int n_nodes, int max_nodes,
+                      int32_t* parent, int32_t* rank, int32_t* depth);
+
+/* Head rows of a plan. Hydra (hydra = 1, [HG] "Candidate Tree Construction"):
+ * head k runs once for every node at depth k-1 that has children, on
+ * [h || e(token of that node)]. Medusa (hydra = 0, [MH] "Tree Attention und
+ * Akzeptanz"): one row per depth serves every parent at that depth.
+ * Outputs (host):
+ *   node_row[N]          row whose top-k list gives node i's children, -1 if none
+ *   row_node[R]          node a row conditions on (Hydra), -1 (Medusa)
+ *   row_first[Dmax+1]    rows of head k (1-based) are [row_first[k-1], row_first[k])
+ *   depth_first[Dmax+2]  nodes of depth k are [depth_first[k], depth_first[k+1])
+ *   k_per_depth[Dmax]    top-k width head k needs (widest fan-out at depth k-1)
+ * row_node needs capacity N; row_first/depth_first/k_per_depth capacity
+ * HYDRA_MAX_DEPTH + 2. Returns R (number of rows) or a negative error code. */
+int hydra_plan_rows(int N, const int32_t* parent, const int32_t* rank,
+                    const int32_t* depth, int hydra, int32_t* node_row,
+                    int32_t* row_node, int32_t* row_first, int32_t* depth_first,
+                    int32_t* k_per_depth);
+
+/* ------------------------------------------------------------------------
+ * Stage 1: draft heads
+ *
+ * For every head row r of depth k (rows of head k) and sequence b:
+ *   x   = h_b (Medusa)  or  [h_b || E[token of row_node[r]]] (Hydra)
+ *   a   = W1_k x + b1_k
+ *   u   = h_b + SiLU(a)   (residual = 1)   or   SiLU(a)   (residual = 0)
+ *   z   = W2_k u                          -> head_logits[b, r, :]
+ *   lse = log sum exp z                   -> head_lse[b, r]
+ * ([MH] "So sagen die Köpfe voraus": SiLU layer with a residual connection and
+ * a vocabulary projection; [HG] "1. Embedding Conditioning Mechanics": Hydra
+ * heads read [h || e(x_parent)].) Every child c of a node served by row r
+ * takes entry rank[c] of the row's top-k list (sorted by logit descending,
+ * ties to the lower id) and cand_logp[c] = cand_logp[parent] + z[tok] - lse.
+ * Heads run in depth order because Hydra head k needs depth k-1's tokens.
+ * In bf16 mode u is stored as bfloat16 (round to nearest even); the
+ * projections accumulate in float32.
+ *
+ * dtype        HYDRA_F32 or HYDRA_BF16 (h, emb, W1, b1, W2, head_hidden)
+ * B, d, V      sequences, hidden size, vocabulary size
+ * hydra        1: [h || e(parent)] input of width 2d; 0: Medusa, input h
+ * residual     1: u = h + SiLU(a); 0: u = SiLU(a)
+ * h            [B, d]
+ * root_tok     [B] int32, token of the root of each tree
+ * emb          [V, d] embedding table (Hydra); ignored (may be NULL) for Medusa
+ * n_heads      entries in W1/b1/W2 (>= Dmax)
+ * W1, b1, W2   host arrays of n_heads device pointers: W1_k [d, in] (in = 2d
+ *              Hydra, d Medusa), b1_k [d], W2_k [V, d]; head k at index k-1
+ * N, Dmax      plan nodes, plan depth
+ * node_parent, node_rank, node_row   device int32 [N] (plan and hydra_plan_rows)
+ * R, row_node  rows per sequence; device int32 [R]
+ * row_first, depth_first, k_per_depth  host arrays from hydra_plan_rows
+ * head_logits  out [B, R, V] float32
+ * head_lse     out [B, R] float32
+ * head_hidden  out [B, R, d] (dtype) or NULL
+ * cand_tok     out [B, N] int32 (cand_tok[b, 0] = root_tok[b])
+ * cand_logp    out [B, N] float32 (cand_logp[b, 0] = 0)
+ * Supported: bf16 needs d % 256 == 0; k_per_depth[i] <= HYDRA_MAX_TOPK <= V.
+ * ---------------------------------------------------------------------- */
+size_t hydra_draft_heads_workspace_size(int dtype, int B, int d, int V, int hydra,
+                                        int Dmax, const int32_t* row_first);
+
+int hydra_draft_heads(int dtype, int B, int d, int V, int hydra, int residual,
+                      const void* h, const int32_t* root_tok, const void* emb,
+                      int n_heads, const void* const* W1, const void* const* b1,
+                      const void* const* W2, int N, int Dmax,
+                      const int32_t* node_parent, const int32_t* node_rank,
+                      const int32_t* node_row, int R, const int32_t* row_node,
+                      const int32_t* row_first, const int32_t* depth_first,
+                      const int32_t* k_per_depth, float* head_logits, float* head_lse,
+                      void* head_hidden, int32_t* cand_tok, float* cand_logp,
+                      void* ws, size_t ws_bytes, void* stream);
+
+/* Vocabulary projection used by the heads and the target:
+ * Y[m, n] = sum_k X[m, k] * W[n, k], float32 accumulation and output.
+ * X [M, K], W [N, K] (dtype), Y [M, N] float32. bf16 needs K % 256 == 0. */
+int hydra_vocab_projection(int dtype, int M, int K, int N, const void* X,
+                           const void* W, float* Y, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Stage 2: tree build
+ *
+ * Turns the candidate tree into the tree that is verified. n_keep == N: the
+ * candidate tree itself. n_keep < N (dense tree): keep the root and the best
+ * n_keep - 1 candidates by (cand_logp descending, depth ascending, index
+ * ascending) - closed under taking parents since log-probs are <= 0 - and
+ * renumber the survivors breadth-first (by depth, new parent index, rank).
+ * Also builds the ancestor table that replaces a dense tree mask
+ * ([HG] "Tree Attention Matrix with Topology-Aware Causal Masking": node u
+ * sees v iff v is an ancestor of u or v = u).
+ *
+ * node_parent, node_rank, node_depth, node_row  device int32 [N] plan
+ * cand_tok, cand_logp   [B, N] from hydra_draft_heads
+ * tok, parent, depth    out [B, n_keep] int32 (parent of the root = -1)
+ * anc                   out [B, n_keep, Dmax+1] int32: node at depth j on the
+ *                       path root -> u (u itself at depth(u)), -1 beyond
+ * q_row                 out [B, n_keep] int32: head row that drafted the
+ *                       node's children (node_row of its source), -1 if none
+ * src                   out [B, n_keep] int32: index in the candidate tree
+ * Limits: N <= HYDRA_MAX_TREE, n_keep <= min(N, HYDRA_MAX_VERIFY).
+ * ---------------------------------------------------------------------- */
+size_t tree_build_workspace_size(int B, int N, int n_keep);
+
+int tree_build(int B, int N, int Dmax, const int32_t* node_parent,
+               const int32_t* node_rank, const int32_t* node_depth,
+               const int32_t* node_row, const int32_t* cand_tok,
+               const float* cand_logp, int n_keep, int32_t* tok, int32_t* parent,
+               int32_t* depth, int32_t* anc, int32_t* q_row, int32_t* src,
+               void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Stage 3: tree-masked attention verify (one attention layer's share)
+ *
+ * The N tree rows are appended after each sequence's KV prefix; row u (query
+ * head hq) attends to prefix positions [0, prefix_len[b]) and to the tree rows
+ * in anc[b, u, :] (its ancestors and itself) ([HG] "Tree Attention Matrix with
+ * Topology-Aware Causal Masking"; [MH] "Tree Attention und Akzeptanz"):
+ *   s_j = scale * q_u . k_j,   o_u = sum_j softmax(s)_j v_j,
+ * with query head hq reading key/value head hq / (Hq / Hkv).
+ *
+ * q                  [B, N, Hq, D]          (dtype)
+ * k_tree, v_tree     [B, N, Hkv, D]         (dtype)
+ * k_pages, v_pages   [n_pages, Hkv, page_size, D] (dtype); position p of
+ *                    sequence b lives in page block_table[b, p / page_size],
+ *                    slot p % page_size
+ * block_table        [B, max_pages] int32 page ids
+ * prefix_len         [B] int32, each <= max_prefix_len and
+ *                    <= max_pages * page_size; page ids must be < n_pages
+ *                    (out-of-range ids and positions contribute nothing)
+ * max_prefix_len     host bound on prefix_len (plans the split of the prefix)
+ * anc                [B, N, Dmax+1] int32 from tree_build
+ * depth              [B, N] int32 from tree_build
+ * out                out [B, N, Hq, D] (dtype)
+ * lse                out [B, N, Hq] float32 (natural log-sum-exp of the scaled
+ *                    scores) or NULL
+ * Limits: N <= HYDRA_MAX_VERIFY, D in {32, 64, 128}, Hq % Hkv == 0,
+ * page_size in {16, 32, 64}, Dmax <= HYDRA_MAX_DEPTH.
+ * ---------------------------------------------------------------------- */
+size_t tree_attention_verify_workspace_size(int dtype, int B, int N, int Hq, int Hkv,
+                                            int D, int max_prefix_len);
+
+int tree_attention_verify(int dtype, int B, int N, int Hq, int Hkv, int D,
+                          float scale, const void* q, const void* k_tree,
+                          const void* v_tree, const void* k_pages,
+                          const void* v_pages, int n_pages, int page_size,
+                          const int32_t* block_table, int max_pages,
+                          const int32_t* prefix_len, int max_prefix_len,
+                          const int32_t* anc, const int32_t* depth, int Dmax,
+                          void* out, float* lse, void* ws, size_t ws_bytes,
+                          void* stream);
+
+/* ------------------------------------------------------------------------
+ * Stage 4: acceptance
+ *
+ * Target logits Z[b, u, :] = W_t o[b, u, :] for every tree row (o flattened
+ * over heads into the hidden size d), then one walk per sequence from the
+ * root:
+ *   mode 0, greedy ([HG] "Parallel Verification and Greedy Acceptance
+ *     Algorithm"): y = arg max Z[u] (ties to the lower id); if a child of u
+ *     carries y, accept it and continue there; otherwise stop and emit y as
+ *     the bonus token.
+ *   mode 1, rejection ([SD] "The acceptance criterion", "The correctness
+ *     guarantee"): p = softmax(Z[u] / T), q = softmax(head_logits[q_row[u]] / T);
+ *     children are tried in rank order, child c is accepted iff
+ *     u_acc[c] * q(tok_c) < r(tok_c) where r starts at p and becomes
+ *     norm(max(r - q, 0)) after each rejection; when u has no children or
+ *     every child is rejected, one token is drawn from r by inverse CDF with
+ *     u_res[u] (smallest id whose cumulative mass exceeds u_res * total). If
+ *     a residual has no mass the previous r is kept.
+ * Outputs: n_accepted[b] = m accepted drafts; path[b, 0..m] tree rows from
+ * the root, -1 after; out_tok[b, 0..m] the m accepted tokens then the bonus
+ * or resampled token, -1 after.
+ *
+ * o                 [B, N, d] (dtype), d = Hq * D of the attention layer
+ * W_t               [V, d] (dtype)
+ * tok, parent       [B, N] int32 from tree_build (children sorted by rank)
+ * q_row             [B, N] int32 from tree_build (mode 1)
+ * head_logits       [B, R, V] float32 from hydra_draft_heads (mode 1)
+ * u_acc, u_res      [B, N] float32 in [0, 1) (mode 1)
+ * target_logits     out [B, N, V] float32
+ * n_accepted        out [B] int32
+ * path, out_tok     out [B, Dmax+1] int32
+ * ---------------------------------------------------------------------- */
+size_t tree_accept_workspace_size(int mode, int B, int N, int V);
+
+int tree_accept(int dtype, int mode, int B, int N, int d, int V, int Dmax,
+                const void* o, const void* W_t, float temperature,
+                const int32_t* tok, const int32_t* parent, const int32_t* q_row,
+                const float* head_logits, int R, const float* u_acc,
+                const float* u_res, float* target_logits, int32_t* n_accepted,
+                int32_t* path, int32_t* out_tok, void* ws, size_t ws_bytes,
+                void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HYDRA_H */

@@ -1,0 +1,13 @@
+"""MI355X-native Hydra/Medusa draft-and-verify round (libhydra, HIP for gfx950).
+
+The four stages are the C entry points of include/hydra.h, bound under the same
+names in ``speculative_decoding_hydra_amd.hydra``; ``HydraRound`` allocates the
+buffers of a round and calls them in order.
+"""
+from .hydra import (  # noqa: F401
+    DevicePlan, HydraError, PlanRows, TreePlan, hydra_draft_heads, hydra_draft_heads_workspace_size,
+    hydra_plan_cartesian, hydra_plan_rows, hydra_plan_sparse, hydra_vocab_projection, tree_accept,
+    tree_accept_workspace_size, tree_attention_verify, tree_attention_verify_workspace_size, tree_build,
+    tree_build_workspace_size,
+)
+from .round import HydraRound, make_plan  # noqa: F401

@@ -1,0 +1,351 @@
+// Stage 4: target vocabulary projection and acceptance walk.
+//
+// Greedy: "Hydra Guide: Sequentially-Dependent Speculative AI", section
+// "Parallel Verification and Greedy Acceptance Algorithm": follow the branch
+// whose tokens equal the target's arg max, stop at the first mismatch and emit
+// the target's token there as the bonus (m accepted drafts give m + 1 tokens).
+//
+// Rejection: "Speculative Decoding", sections "The acceptance criterion" and
+// "The correctness guarantee": accept a drafted x with probability
+// min(1, p(x)/q(x)), written division-free as u * q(x) < p(x); on rejection
+// the target becomes norm(max(p - q, 0)). On a tree the children of the
+// current node are tried in rank order against the current residual with q
+// unchanged; a node without children, or with every child rejected, ends the
+// walk with one inverse-CDF draw from the current target ("How much faster?":
+// the bonus token is drawn from the target distribution when every draft is
+// accepted). p and q are the post-temperature distributions ("Common
+// misconceptions").
+#include "common.h"
+
+namespace hydra {
+namespace {
+
+__global__ __launch_bounds__(256) void row_argmax(int V, const float* __restrict__ Z, int32_t* __restrict__ amax) {
+  __shared__ uint64_t wbest[4];
+  const float* z = Z + static_cast<size_t>(blockIdx.x) * V;
+  uint64_t best = 0;
+  if ((V & 3) == 0) {
+    const float4* z4 = reinterpret_cast<const float4*>(z);
+    for (int i = threadIdx.x; i < V / 4; i += 256) {
+      const float4 q = z4[i];
+      uint64_t k = topk_key(q.x, 4 * i);
+      best = k > best ? k : best;
+      k = topk_key(q.y, 4 * i + 1);
+      best = k > best ? k : best;
+      k = topk_key(q.z, 4 * i + 2);
+      best = k > best ? k : best;
+      k = topk_key(q.w, 4 * i + 3);
+      best = k > best ? k : best;
+    }
+  } else {
+    for (int i = threadIdx.x; i < V; i += 256) {
+      const uint64_t k = topk_key(z[i], i);
+      best = k > best ? k : best;
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const uint64_t o = shfl_xor_u64(best, off);
+    best = o > best ? o : best;
+  }
+  if ((threadIdx.x & 63) == 0) wbest[threadIdx.x >> 6] = best;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < 4; ++w) best = wbest[w] > best ? wbest[w] : best;
+    best = wbest[0] > best ? wbest[0] : best;
+    amax[blockIdx.x] = key_id(best);
+  }
+}
+
+// One wave per sequence.
+__global__ __launch_bounds__(64) void greedy_walk(int N, int Dmax, const int32_t* __restrict__ amax,
+                                                  const int32_t* __restrict__ tok,
+                                                  const int32_t* __restrict__ parent,
+                                                  int32_t* __restrict__ n_accepted, int32_t* __restrict__ path,
+                                                  int32_t* __restrict__ out_tok) {
+  __shared__ int s_path[HYDRA_MAX_DEPTH + 1], s_out[HYDRA_MAX_DEPTH + 1];
+  const int b = blockIdx.x, lane = threadIdx.x;
+  if (lane <= Dmax) {
+    s_path[lane] = -1;
+    s_out[lane] = -1;
+  }
+  __syncthreads();
+  const int32_t* tb = tok + static_cast<size_t>(b) * N;
+  const int32_t* pb = parent + static_cast<size_t>(b) * N;
+  int u = 0, m = 0;
+  if (lane == 0) s_path[0] = 0;
+  while (true) {
+    const int y = amax[static_cast<size_t>(b) * N + u];
+    int found = -1;
+    for (int c0 = 0; c0 < N && found < 0; c0 += 64) {
+      const int c = c0 + lane;
+      const bool hit = c < N && pb[c] == u && tb[c] == y;
+      const unsigned long long mask = __ballot(hit);
+      if (mask) found = c0 + __ffsll(static_cast<long long>(mask)) - 1;
+    }
+    if (lane == 0) s_out[m] = y;
+    if (found < 0 || m >= Dmax) break;
+    ++m;
+    u = found;
+    if (lane == 0) s_path[m] = u;
+  }
+  __syncthreads();
+  if (lane <= Dmax) {
+    path[static_cast<size_t>(b) * (Dmax + 1) + lane] = s_path[lane];
+    out_tok[static_cast<size_t>(b) * (Dmax + 1) + lane] = s_out[lane];
+  }
+  if (lane == 0) n_accepted[b] = m;
+}
+
+constexpr int kWalkThreads = 1024;
+constexpr int kWalkWaves = kWalkThreads / 64;
+
+__device__ double block_sum_d(double v, double* red) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __syncthreads();
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  double t = 0.0;
+  for (int w = 0; w < kWalkWaves; ++w) t += red[w];
+  return t;
+}
+
+__device__ float block_max_f(float v, float* red) {
+  v = wave_max(v);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __syncthreads();
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  float t = -INFINITY;
+  for (int w = 0; w < kWalkWaves; ++w) t = fmaxf(t, red[w]);
+  return t;
+}
+
+// Unnormalised current target r at x: from the logits (mode < 0) or from a
+// residual buffer.
+struct Target {
+  const float* z;   // logits row (mode < 0)
+  float invT, m;    // scaled max of the row
+  const float* buf; // residual buffer (mode >= 0)
+  double total;     // sum of the unnormalised values
+  __device__ __forceinline__ float at(int x) const {
+    return buf ? buf[x] : exp2f((z[x] * invT - m) * 1.4426950408889634f);
+  }
+};
+
+// Inverse-CDF draw: the smallest x with cumsum_{y<=x} r(y) > u * total.
+__device__ int block_sample(const Target& r, int V, float u, double* red, int* s_pick) {
+  const int tid = threadIdx.x;
+  const int C = (V + kWalkThreads - 1) / kWalkThreads;
+  const int lo = tid * C, hi = min(V, lo + C);
+  double part = 0.0;
+  int lastpos = -1;
+  for (int x = lo; x < hi; ++x) {
+    const float v = r.at(x);
+    part += v;
+    if (v > 0.f) lastpos = x;
+  }
+  // exclusive scan of the chunk sums across the block
+  const int lane = tid & 63, wave = tid >> 6;
+  double incl = part;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const double o = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += o;
+  }
+  __syncthreads();
+  if (lane == 63) red[wave] = incl;
+  if (tid == 0) {
+    s_pick[0] = -1;
+    s_pick[1] = -1;
+  }
+  __syncthreads();
+  double before = 0.0, total = 0.0;
+  for (int w = 0; w < kWalkWaves; ++w) {
+    if (w < wave) before += red[w];
+    total += red[w];
+  }
+  const double excl = before + incl - part;
+  const double thr = static_cast<double>(u) * total;
+  if (lastpos >= 0) atomicMax(&s_pick[1], lastpos);
+  if (excl <= thr && thr < excl + part) {
+    double run = excl;
+    for (int x = lo; x < hi; ++x) {
+      run += r.at(x);
+      if (run > thr) {
+        s_pick[0] = x;
+        break;
+      }
+    }
+  }
+  __syncthreads();
+  const int pick = s_pick[0] >= 0 ? s_pick[0] : s_pick[1];
+  __syncthreads();
+  return pick;
+}
+
+__global__ __launch_bounds__(kWalkThreads) void reject_walk(
+    int N, int V, int R, int Dmax, float invT, const float* __restrict__ Z, const float* __restrict__ HZ,
+    const int32_t* __restrict__ tok, const int32_t* __restrict__ parent, const int32_t* __restrict__ q_row,
+    const float* __restrict__ u_acc, const float* __restrict__ u_res, float* __restrict__ rbuf,
+    int32_t* __restrict__ n_accepted, int32_t* __restrict__ path, int32_t* __restrict__ out_tok) {
+  __shared__ double red[kWalkWaves];
+  __shared__ float redf[kWalkWaves];
+  __shared__ int s_path[HYDRA_MAX_DEPTH + 1], s_out[HYDRA_MAX_DEPTH + 1];
+  __shared__ int s_pick[2];
+  __shared__ int s_kid[2];
+  const int b = blockIdx.x, tid = threadIdx.x;
+  if (tid <= Dmax) {
+    s_path[tid] = -1;
+    s_out[tid] = -1;
+  }
+  if (tid == 0) s_path[0] = 0;
+  const int32_t* tb = tok + static_cast<size_t>(b) * N;
+  const int32_t* pb = parent + static_cast<size_t>(b) * N;
+  float* buf[2] = {rbuf + static_cast<size_t>(b) * 2 * V, rbuf + (static_cast<size_t>(b) * 2 + 1) * V};
+  int u = 0, m = 0;
+  while (true) {
+    // p at u
+    const float* zu = Z + (static_cast<size_t>(b) * N + u) * V;
+    float mx = -INFINITY;
+    for (int x = tid; x < V; x += kWalkThreads) mx = fmaxf(mx, zu[x] * invT);
+    Target r{zu, invT, block_max_f(mx, redf), nullptr, 0.0};
+    double s = 0.0;
+    for (int x = tid; x < V; x += kWalkThreads) s += r.at(x);
+    r.total = block_sum_d(s, red);
+    // children of u: contiguous, in rank order
+    if (tid == 0) {
+      s_kid[0] = N;
+      s_kid[1] = 0;
+    }
+    __syncthreads();
+    for (int c = tid; c < N; c += kWalkThreads)
+      if (pb[c] == u) {
+        atomicMin(&s_kid[0], c);
+        atomicAdd(&s_kid[1], 1);
+      }
+    __syncthreads();
+    const int c0 = s_kid[0], cnt = s_kid[1];
+    __syncthreads();
+    if (cnt == 0 || m >= Dmax) {
+      const int x = block_sample(r, V, u_res[static_cast<size_t>(b) * N + u], red, s_pick);
+      if (tid == 0) s_out[m] = x;
+      break;
+    }
+    // q at u: the head row that drafted u's children
+    const int qr = q_row[static_cast<size_t>(b) * N + u];
+    const float* hz = HZ + (static_cast<size_t>(b) * R + (qr < 0 ? 0 : qr)) * V;
+    float qm = -INFINITY;
+    for (int x = tid; x < V; x += kWalkThreads) qm = fmaxf(qm, hz[x] * invT);
+    qm = block_max_f(qm, redf);
+    double qs = 0.0;
+    for (int x = tid; x < V; x += kWalkThreads) qs += exp2f((hz[x] * invT - qm) * 1.4426950408889634f);
+    const float qinv = static_cast<float>(1.0 / block_sum_d(qs, red));
+    int nb = 0;
+    bool moved = false;
+    for (int j = 0; j < cnt; ++j) {
+      const int c = c0 + j;
+      const int x = tb[c];
+      const float rx = static_cast<float>(r.at(x) / r.total);
+      const float qx = exp2f((hz[x] * invT - qm) * 1.4426950408889634f) * qinv;
+      if (u_acc[static_cast<size_t>(b) * N + c] * qx < rx) {
+        ++m;
+        if (tid == 0) {
+          s_path[m] = c;
+          s_out[m - 1] = x;
+        }
+        u = c;
+        moved = true;
+        break;
+      }
+      // residual: norm(max(r - q, 0)), kept unless it has no mass
+      const float rinv = static_cast<float>(1.0 / r.total);
+      float* dst = buf[nb];
+      double ns = 0.0;
+      for (int y = tid; y < V; y += kWalkThreads) {
+        const float v = fmaxf(r.at(y) * rinv - exp2f((hz[y] * invT - qm) * 1.4426950408889634f) * qinv, 0.f);
+        dst[y] = v;
+        ns += v;
+      }
+      ns = block_sum_d(ns, red);
+      if (ns > 0.0) {
+        r.buf = dst;
+        r.total = ns;
+        nb ^= 1;
+      }
+      __syncthreads();
+    }
+    if (!moved) {
+      const int x = block_sample(r, V, u_res[static_cast<size_t>(b) * N + u], red, s_pick);
+      if (tid == 0) s_out[m] = x;
+      break;
+    }
+  }
+  __syncthreads();
+  if (tid <= Dmax) {
+    path[static_cast<size_t>(b) * (Dmax + 1) + tid] = s_path[tid];
+    out_tok[static_cast<size_t>(b) * (Dmax + 1) + tid] = s_out[tid];
+  }
+  if (tid == 0) n_accepted[b] = m;
+}
+
+}  // namespace
+}  // namespace hydra
+
+using namespace hydra;
+
+extern "C" size_t tree_accept_workspace_size(int mode, int B, int N, int V) {
+  if (B <= 0 || N <= 0 || V <= 0) return 0;
+  if (mode == 0) return align_up(static_cast<size_t>(B) * N * sizeof(int32_t), 256) + 256;
+  return align_up(static_cast<size_t>(B) * 2 * V * sizeof(float), 256) + 256;
+}
+
+extern "C" int tree_accept(int dtype, int mode, int B, int N, int d, int V, int Dmax, const void* o,
+                           const void* W_t, float temperature, const int32_t* tok, const int32_t* parent,
+                           const int32_t* q_row, const float* head_logits, int R, const float* u_acc,
+                           const float* u_res, float* target_logits, int32_t* n_accepted, int32_t* path,
+                           int32_t* out_tok, void* ws, size_t ws_bytes, void* stream_) {
+  clear_error();
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+  HY_CHECK(dtype == HYDRA_F32 || dtype == HYDRA_BF16, HYDRA_ERR_INVALID, "tree_accept: bad dtype %d", dtype);
+  HY_CHECK(mode == 0 || mode == 1, HYDRA_ERR_INVALID, "tree_accept: mode %d not in {0, 1}", mode);
+  HY_CHECK(B > 0 && N > 0 && d > 0 && V > 0, HYDRA_ERR_INVALID, "tree_accept: bad sizes B=%d N=%d d=%d V=%d", B, N,
+           d, V);
+  HY_CHECK(N <= HYDRA_MAX_VERIFY, HYDRA_ERR_INVALID, "tree_accept: N=%d > %d", N, HYDRA_MAX_VERIFY);
+  HY_CHECK(Dmax >= 1 && Dmax <= HYDRA_MAX_DEPTH, HYDRA_ERR_INVALID, "tree_accept: Dmax=%d", Dmax);
+  HY_CHECK(o && W_t && tok && parent && target_logits && n_accepted && path && out_tok, HYDRA_ERR_INVALID,
+           "tree_accept: null pointer");
+  HY_CHECK(dtype == HYDRA_F32 || d % 256 == 0, HYDRA_ERR_UNSUPPORTED, "tree_accept: bf16 needs d %% 256 == 0 (d=%d)",
+           d);
+  if (mode == 1) {
+    HY_CHECK(q_row && head_logits && u_acc && u_res && R > 0, HYDRA_ERR_INVALID,
+             "tree_accept: rejection mode needs q_row, head_logits, R, u_acc and u_res");
+    HY_CHECK(temperature > 0.f, HYDRA_ERR_INVALID, "tree_accept: temperature must be > 0");
+  }
+  const size_t need = tree_accept_workspace_size(mode, B, N, V);
+  HY_CHECK(ws_bytes >= need && ws, HYDRA_ERR_WORKSPACE, "tree_accept: workspace %zu < %zu", ws_bytes, need);
+
+  XSource xs{};
+  xs.x = o;
+  xs.ldx = d;
+  xs.mode = 0;
+  const int M = B * N;
+  int rc = launch_projection(dtype, M, d, V, xs, W_t, target_logits, RowMap{M, 0, 0}, V, 1, nullptr, stream);
+  if (rc != HYDRA_OK) return rc;
+  Arena arena(ws, ws_bytes);
+  if (mode == 0) {
+    int32_t* amax = arena.take<int32_t>(static_cast<size_t>(M));
+    row_argmax<<<M, 256, 0, stream>>>(V, target_logits, amax);
+    HY_LAUNCH_CHECK("tree_accept: argmax");
+    greedy_walk<<<B, 64, 0, stream>>>(N, Dmax, amax, tok, parent, n_accepted, path, out_tok);
+    HY_LAUNCH_CHECK("tree_accept: greedy walk");
+  } else {
+    float* rbuf = arena.take<float>(static_cast<size_t>(B) * 2 * V);
+    reject_walk<<<B, kWalkThreads, 0, stream>>>(N, V, R, Dmax, 1.0f / temperature, target_logits, head_logits, tok,
+                                                parent, q_row, u_acc, u_res, rbuf, n_accepted, path, out_tok);
+    HY_LAUNCH_CHECK("tree_accept: rejection walk");
+  }
+  return HYDRA_OK;
+}

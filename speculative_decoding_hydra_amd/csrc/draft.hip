@@ -1,0 +1,323 @@
+// Stage 1: draft heads, per-head top-k and candidate-tree fill.
+//
+// "Medusa Heads" (Ultralytics glossary), section "So sagen die Köpfe voraus":
+// a head is one feed-forward layer with SiLU and a residual connection,
+// followed by a vocabulary projection. "Hydra Guide: Sequentially-Dependent
+// Speculative AI", sections "1. Embedding Conditioning Mechanics" and
+// "Candidate Tree Construction": Hydra head k reads [h || e(x_parent)] and
+// runs once per expanded node at depth k-1, keeping its top-b_k tokens.
+//
+// Per depth k (sequential: Hydra head k needs the tokens of depth k-1):
+//   1. projection W1 over the gathered rows [h_b || E[token]] (split-K),
+//   2. epilogue: sum of the splits + b1, SiLU, residual, rounded to dtype,
+//   3. projection W2 -> head logits,
+//   4. one workgroup per head row: log-sum-exp, top-k, and the tree fill of
+//      every child that takes its token from that row.
+#include "common.h"
+
+namespace hydra {
+namespace {
+
+template <class T>
+__global__ __launch_bounds__(256) void head_mlp_epilogue(int M, int d, int nsplit,
+                                                         const float* __restrict__ part,
+                                                         const T* __restrict__ b1,
+                                                         const T* __restrict__ h, int P,
+                                                         int residual, T* __restrict__ U,
+                                                         T* __restrict__ hidden, RowMap map) {
+  const size_t total = static_cast<size_t>(M) * d;
+  for (size_t idx = blockIdx.x * 256ull + threadIdx.x; idx < total; idx += gridDim.x * 256ull) {
+    const int m = static_cast<int>(idx / d);
+    const int j = static_cast<int>(idx % d);
+    float a = 0.f;
+    for (int s = 0; s < nsplit; ++s) a += part[static_cast<size_t>(s) * total + idx];
+    a += load_f(b1, j);
+    const float act = a / (1.0f + expf(-a));  // SiLU(a) = a * sigmoid(a)
+    const float u = residual ? load_f(h, static_cast<size_t>(m / P) * d + j) + act : act;
+    store_f(U, idx, u);
+    if (hidden) store_f(hidden, static_cast<size_t>(map(m)) * d + j, u);
+  }
+}
+
+// Insert key x into a descending list of length K held in registers.
+template <int K>
+__device__ __forceinline__ void list_insert(uint64_t (&l)[K], uint64_t x) {
+  if (x <= l[K - 1]) return;
+#pragma unroll
+  for (int j = K - 1; j > 0; --j) {
+    const uint64_t prev = l[j - 1];
+    l[j] = prev < x ? prev : (l[j] < x ? x : l[j]);
+  }
+  l[0] = l[0] < x ? x : l[0];
+}
+
+constexpr int kRowThreads = 512;
+constexpr int kRowWaves = kRowThreads / 64;
+
+// One workgroup per head row (b, r): log-sum-exp, sorted top-k (logit
+// descending, lower id first), then the tree fill.
+template <int KMAX>
+__global__ __launch_bounds__(kRowThreads) void row_topk_fill(
+    int V, int R, int P, int r0, int k, const float* __restrict__ logits,
+    float* __restrict__ head_lse, int N, int node_lo, int node_hi,
+    const int32_t* __restrict__ node_parent, const int32_t* __restrict__ node_rank,
+    const int32_t* __restrict__ node_row, const int32_t* __restrict__ root_tok,
+    int32_t* __restrict__ cand_tok, float* __restrict__ cand_logp) {
+  __shared__ uint64_t wtop[kRowWaves][KMAX];
+  __shared__ float wm[kRowWaves], ws[kRowWaves];
+  __shared__ uint64_t top[KMAX];
+  __shared__ float s_lse;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int b = blockIdx.x / P;
+  const int r = r0 + blockIdx.x % P;
+  const float* z = logits + (static_cast<size_t>(b) * R + r) * V;
+
+  uint64_t l[KMAX];
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) l[j] = 0;
+  float m = -INFINITY, s = 0.f;
+  auto consume = [&](float v, int id) {
+    if (v > m) {
+      s = s * expf(m - v) + 1.0f;
+      m = v;
+    } else {
+      s += expf(v - m);
+    }
+    list_insert<KMAX>(l, topk_key(v, id));
+  };
+  if ((V & 3) == 0) {
+    const float4* z4 = reinterpret_cast<const float4*>(z);
+    for (int i = tid; i < V / 4; i += kRowThreads) {
+      const float4 q = z4[i];
+      consume(q.x, 4 * i);
+      consume(q.y, 4 * i + 1);
+      consume(q.z, 4 * i + 2);
+      consume(q.w, 4 * i + 3);
+    }
+  } else {
+    for (int i = tid; i < V; i += kRowThreads) consume(z[i], i);
+  }
+
+  // (max, sum) across the wave, then across waves
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const float om = __shfl_xor(m, off, 64);
+    const float os = __shfl_xor(s, off, 64);
+    const float nm = fmaxf(m, om);
+    s = (m == -INFINITY ? 0.f : s * expf(m - nm)) + (om == -INFINITY ? 0.f : os * expf(om - nm));
+    m = nm;
+  }
+  // wave top-k: k rounds of a wave-wide max over the list heads
+  for (int j = 0; j < k; ++j) {
+    uint64_t best = l[0];
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const uint64_t o = shfl_xor_u64(best, off);
+      best = o > best ? o : best;
+    }
+    if (l[0] == best && best != 0) {
+#pragma unroll
+      for (int q = 0; q < KMAX - 1; ++q) l[q] = l[q + 1];
+      l[KMAX - 1] = 0;
+    }
+    if (lane == 0) wtop[wave][j] = best;
+  }
+  if (lane == 0) {
+    wm[wave] = m;
+    ws[wave] = s;
+  }
+  __syncthreads();
+  if (wave == 0) {
+    // merge the per-wave sorted lists: lane w < kRowWaves walks list w
+    int ptr = 0;
+    for (int j = 0; j < k; ++j) {
+      uint64_t cand = (lane < kRowWaves && ptr < k) ? wtop[lane][ptr] : 0;
+      uint64_t best = cand;
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) {
+        const uint64_t o = shfl_xor_u64(best, off);
+        best = o > best ? o : best;
+      }
+      if (lane < kRowWaves && cand == best && best != 0) ++ptr;
+      if (lane == 0) top[j] = best;
+    }
+    if (lane == 0) {
+      float M = -INFINITY;
+      for (int w = 0; w < kRowWaves; ++w) M = fmaxf(M, wm[w]);
+      float S = 0.f;
+      for (int w = 0; w < kRowWaves; ++w)
+        if (wm[w] != -INFINITY) S += ws[w] * expf(wm[w] - M);
+      s_lse = M + logf(S);
+      head_lse[static_cast<size_t>(b) * R + r] = s_lse;
+    }
+  }
+  __syncthreads();
+  const float lse = s_lse;
+  if (blockIdx.x % P == 0 && r == 0 && tid == 0) {
+    cand_tok[static_cast<size_t>(b) * N] = root_tok[b];
+    cand_logp[static_cast<size_t>(b) * N] = 0.f;
+  }
+  // children whose parent is expanded by this row take entry rank of the list
+  for (int c = node_lo + tid; c < node_hi; c += kRowThreads) {
+    const int p = node_parent[c];
+    if (p < 0 || node_row[p] != r) continue;
+    const int rk = node_rank[c];
+    if (rk < 0 || rk >= k) continue;
+    const uint64_t key = top[rk];
+    const float plogp = p == 0 ? 0.f : cand_logp[static_cast<size_t>(b) * N + p];
+    cand_tok[static_cast<size_t>(b) * N + c] = key_id(key);
+    cand_logp[static_cast<size_t>(b) * N + c] = plogp + (key_value(key) - lse);
+  }
+}
+
+struct DraftPlan {
+  int max_rows;  // max over depths of B * rows-of-depth
+  int nsplit;
+};
+
+int w1_splits(int dtype, int in_dim, int d) {
+  if (dtype == HYDRA_F32) return 1;
+  // enough workgroups for 256 CUs: d / 64 row tiles times the splits
+  int s = 1;
+  while ((d / 64) * s < 512 && (in_dim / (s * 2)) % 256 == 0 && s < 16) s *= 2;
+  return s;
+}
+
+}  // namespace
+}  // namespace hydra
+
+using namespace hydra;
+
+extern "C" size_t hydra_draft_heads_workspace_size(int dtype, int B, int d, int V, int hydra_mode,
+                                                   int Dmax, const int32_t* row_first) {
+  (void)V;
+  if (B <= 0 || d <= 0 || Dmax <= 0 || Dmax > HYDRA_MAX_DEPTH || !row_first) return 0;
+  int maxP = 0;
+  for (int k = 1; k <= Dmax; ++k) {
+    const int P = row_first[k] - row_first[k - 1];
+    maxP = P > maxP ? P : maxP;
+  }
+  const size_t M = static_cast<size_t>(B) * maxP;
+  const int in_dim = hydra_mode ? 2 * d : d;
+  const int ns = w1_splits(dtype, in_dim, d);
+  const size_t esz = dtype == HYDRA_F32 ? 4 : 2;
+  size_t bytes = 0;
+  bytes += align_up(ns * M * d * sizeof(float), 256);  // W1 partials
+  bytes += align_up(M * d * esz, 256);                   // u
+  return bytes + 256;
+}
+
+extern "C" int hydra_draft_heads(int dtype, int B, int d, int V, int hydra_mode, int residual,
+                                 const void* h, const int32_t* root_tok, const void* emb,
+                                 int n_heads, const void* const* W1, const void* const* b1,
+                                 const void* const* W2, int N, int Dmax,
+                                 const int32_t* node_parent, const int32_t* node_rank,
+                                 const int32_t* node_row, int R, const int32_t* row_node,
+                                 const int32_t* row_first, const int32_t* depth_first,
+                                 const int32_t* k_per_depth, float* head_logits,
+                                 float* head_lse, void* head_hidden, int32_t* cand_tok,
+                                 float* cand_logp, void* ws, size_t ws_bytes, void* stream_) {
+  clear_error();
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+  HY_CHECK(dtype == HYDRA_F32 || dtype == HYDRA_BF16, HYDRA_ERR_INVALID, "draft_heads: bad dtype %d", dtype);
+  HY_CHECK(B > 0 && d > 0 && V > 0, HYDRA_ERR_INVALID, "draft_heads: bad sizes B=%d d=%d V=%d", B, d, V);
+  HY_CHECK(Dmax >= 1 && Dmax <= HYDRA_MAX_DEPTH, HYDRA_ERR_INVALID, "draft_heads: Dmax=%d out of [1, %d]", Dmax, HYDRA_MAX_DEPTH);
+  HY_CHECK(n_heads >= Dmax, HYDRA_ERR_INVALID, "draft_heads: n_heads=%d < Dmax=%d", n_heads, Dmax);
+  HY_CHECK(N >= 2 && N <= HYDRA_MAX_TREE, HYDRA_ERR_INVALID, "draft_heads: N=%d out of [2, %d]", N, HYDRA_MAX_TREE);
+  HY_CHECK(h && root_tok && W1 && b1 && W2 && node_parent && node_rank && node_row && row_first &&
+               depth_first && k_per_depth && head_logits && head_lse && cand_tok && cand_logp,
+           HYDRA_ERR_INVALID, "draft_heads: null pointer");
+  HY_CHECK(!hydra_mode || (emb && row_node), HYDRA_ERR_INVALID, "draft_heads: Hydra mode needs emb and row_node");
+  HY_CHECK(dtype == HYDRA_F32 || d % 256 == 0, HYDRA_ERR_UNSUPPORTED, "draft_heads: bf16 needs d %% 256 == 0 (d=%d)", d);
+  HY_CHECK(row_first[0] == 0 && row_first[Dmax] == R, HYDRA_ERR_INVALID, "draft_heads: row_first must span [0, R=%d)", R);
+  HY_CHECK(depth_first[0] == 0 && depth_first[1] == 1 && depth_first[Dmax + 1] == N, HYDRA_ERR_INVALID,
+           "draft_heads: depth_first must start 0, 1 and end at N=%d", N);
+  for (int k = 1; k <= Dmax; ++k) {
+    HY_CHECK(row_first[k] > row_first[k - 1], HYDRA_ERR_INVALID, "draft_heads: depth %d has no head rows", k);
+    HY_CHECK(depth_first[k + 1] > depth_first[k], HYDRA_ERR_INVALID, "draft_heads: depth %d has no nodes", k);
+    HY_CHECK(k_per_depth[k - 1] >= 1 && k_per_depth[k - 1] <= HYDRA_MAX_TOPK && k_per_depth[k - 1] <= V,
+             HYDRA_ERR_UNSUPPORTED, "draft_heads: top-k %d at depth %d out of [1, %d]", k_per_depth[k - 1], k,
+             HYDRA_MAX_TOPK);
+    HY_CHECK(W1[k - 1] && b1[k - 1] && W2[k - 1], HYDRA_ERR_INVALID, "draft_heads: null weight of head %d", k);
+    HY_CHECK(hydra_mode || row_first[k] - row_first[k - 1] == 1, HYDRA_ERR_INVALID,
+             "draft_heads: Medusa mode has one row per depth");
+  }
+  const size_t need = hydra_draft_heads_workspace_size(dtype, B, d, V, hydra_mode, Dmax, row_first);
+  HY_CHECK(ws_bytes >= need && (need == 0 || ws), HYDRA_ERR_WORKSPACE,
+           "draft_heads: workspace %zu < required %zu", ws_bytes, need);
+
+  int maxP = 0;
+  for (int k = 1; k <= Dmax; ++k) maxP = std::max(maxP, row_first[k] - row_first[k - 1]);
+  const size_t Mmax = static_cast<size_t>(B) * maxP;
+  const int in_dim = hydra_mode ? 2 * d : d;
+  const int ns = w1_splits(dtype, in_dim, d);
+  const size_t esz = dtype == HYDRA_F32 ? 4 : 2;
+  Arena arena(ws, ws_bytes);
+  float* part = arena.take<float>(ns * Mmax * d);
+  char* U = arena.take<char>(Mmax * d * esz);
+
+  for (int k = 1; k <= Dmax; ++k) {
+    const int P = row_first[k] - row_first[k - 1];
+    const int r0 = row_first[k - 1];
+    const int M = B * P;
+    RowMap map{P, R, r0};
+    // 1. W1 over [h || e(parent)] (Hydra) or h (Medusa)
+    XSource xs{};
+    xs.x = h;
+    xs.ldx = d;
+    xs.mode = hydra_mode ? 1 : 0;
+    xs.emb = emb;
+    xs.tok = cand_tok;
+    xs.root_tok = root_tok;
+    xs.V = V;
+    xs.row_node = row_node;
+    xs.ntree = N;
+    xs.P = P;
+    xs.r0 = r0;
+    xs.d = d;
+    if (!hydra_mode) {
+      // Medusa: every row of sequence b is h_b, so M = B rows of h
+      xs.mode = 0;
+    }
+    const int nsk = ns;
+    int rc = launch_projection(dtype, M, in_dim, d, xs, W1[k - 1], dtype == HYDRA_F32 ? part : nullptr,
+                               RowMap{M, 0, 0}, d, nsk, dtype == HYDRA_F32 ? nullptr : part, stream);
+    if (rc != HYDRA_OK) return rc;
+    // 2. epilogue: u = h + SiLU(sum + b1)
+    {
+      const size_t total = static_cast<size_t>(M) * d;
+      const int grid = static_cast<int>(std::min<size_t>((total + 255) / 256, 4096));
+      const int nsum = dtype == HYDRA_F32 ? 1 : nsk;
+      if (dtype == HYDRA_F32) {
+        head_mlp_epilogue<float><<<grid, 256, 0, stream>>>(
+            M, d, nsum, part, static_cast<const float*>(b1[k - 1]), static_cast<const float*>(h), P, residual,
+            reinterpret_cast<float*>(U), static_cast<float*>(head_hidden), map);
+      } else {
+        head_mlp_epilogue<bf16_t><<<grid, 256, 0, stream>>>(
+            M, d, nsum, part, static_cast<const bf16_t*>(b1[k - 1]), static_cast<const bf16_t*>(h), P,
+            residual, reinterpret_cast<bf16_t*>(U), static_cast<bf16_t*>(head_hidden), map);
+      }
+      HY_LAUNCH_CHECK("draft_heads: mlp epilogue");
+    }
+    // 3. W2: head logits
+    XSource xu{};
+    xu.x = U;
+    xu.ldx = d;
+    xu.mode = 0;
+    rc = launch_projection(dtype, M, d, V, xu, W2[k - 1], head_logits, map, V, 1, nullptr, stream);
+    if (rc != HYDRA_OK) return rc;
+    // 4. log-sum-exp, top-k, tree fill
+    const int kk = k_per_depth[k - 1];
+    const int lo = depth_first[k], hi = depth_first[k + 1];
+#define HY_ROW(KM)                                                                                   \
+  row_topk_fill<KM><<<M, kRowThreads, 0, stream>>>(V, R, P, r0, kk, head_logits, head_lse, N, lo, hi, \
+                                                   node_parent, node_rank, node_row, root_tok,       \
+                                                   cand_tok, cand_logp)
+    if (kk <= 4) HY_ROW(4);
+    else HY_ROW(16);
+#undef HY_ROW
+    HY_LAUNCH_CHECK("draft_heads: top-k");
+  }
+  return HYDRA_OK;
+}

@@ -1,0 +1,280 @@
+"""Python binding of libhydra, one function per C entry point (same names).
+
+Argument marshalling only: tensors are checked for device, dtype and layout,
+turned into pointers and sizes, and passed to the library, which does all of
+the work in its HIP kernels on the given stream. PyTorch provides device
+memory and streams.
+"""
+from __future__ import annotations
+
+import ctypes as C
+from dataclasses import dataclass
+
+import numpy as np
+import torch
+
+from ._lib import lib
+
+HYDRA_F32, HYDRA_BF16 = 0, 1
+MAX_DEPTH, MAX_TOPK, MAX_TREE, MAX_VERIFY = 8, 16, 1024, 256
+
+
+class HydraError(RuntimeError):
+    def __init__(self, fn, code):
+        L = lib()
+        msg = L.hydra_last_error().decode()
+        super().__init__(f"{fn}: {L.hydra_status_string(code).decode()} ({code}): {msg}")
+        self.code = code
+
+
+def _check(fn, rc):
+    if rc != 0:
+        raise HydraError(fn, rc)
+    return rc
+
+
+def _dtype_code(t):
+    if t.dtype == torch.float32:
+        return HYDRA_F32
+    if t.dtype == torch.bfloat16:
+        return HYDRA_BF16
+    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _dev(t, name, dtype=None):
+    """Device pointer of a contiguous GPU tensor (None -> NULL)."""
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name}: must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
+def _host_i32(a):
+    a = np.ascontiguousarray(np.asarray(a, dtype=np.int32))
+    return a, a.ctypes.data_as(C.POINTER(C.c_int32))
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+
+
+def _ws(ws):
+    if ws is None:
+        return None, 0
+    return _dev(ws, "ws"), ws.numel() * ws.element_size()
+
+
+# --------------------------------------------------------------- tree plans
+
+@dataclass
+class TreePlan:
+    """Breadth-first candidate tree shape (host int32 arrays)."""
+    parent: np.ndarray
+    rank: np.ndarray
+    depth: np.ndarray
+
+    @property
+    def n(self):
+        return int(self.parent.shape[0])
+
+    @property
+    def dmax(self):
+        return int(self.depth.max())
+
+
+@dataclass
+class PlanRows:
+    node_row: np.ndarray
+    row_node: np.ndarray
+    row_first: np.ndarray
+    depth_first: np.ndarray
+    k_per_depth: np.ndarray
+    R: int
+
+
+def _plan_out(n):
+    return [np.zeros(n, dtype=np.int32) for _ in range(3)]
+
+
+def hydra_plan_cartesian(b):
+    b, bp = _host_i32(b)
+    par, rk, dp = _plan_out(MAX_TREE)
+    P = C.POINTER(C.c_int32)
+    n = lib().hydra_plan_cartesian(bp, len(b), MAX_TREE, par.ctypes.data_as(P), rk.ctypes.data_as(P),
+                                   dp.ctypes.data_as(P))
+    if n < 0:
+        raise HydraError("hydra_plan_cartesian", n)
+    return TreePlan(par[:n].copy(), rk[:n].copy(), dp[:n].copy())
+
+
+def hydra_plan_sparse(caps, n_nodes):
+    caps, cp = _host_i32(caps)
+    par, rk, dp = _plan_out(MAX_TREE)
+    P = C.POINTER(C.c_int32)
+    n = lib().hydra_plan_sparse(cp, len(caps), int(n_nodes), MAX_TREE, par.ctypes.data_as(P),
+                                rk.ctypes.data_as(P), dp.ctypes.data_as(P))
+    if n < 0:
+        raise HydraError("hydra_plan_sparse", n)
+    return TreePlan(par[:n].copy(), rk[:n].copy(), dp[:n].copy())
+
+
+def hydra_plan_rows(plan: TreePlan, hydra: bool):
+    P = C.POINTER(C.c_int32)
+    N = plan.n
+    par, _ = _host_i32(plan.parent)
+    rk, _ = _host_i32(plan.rank)
+    dp, _ = _host_i32(plan.depth)
+    node_row = np.zeros(N, dtype=np.int32)
+    row_node = np.zeros(N, dtype=np.int32)
+    row_first = np.zeros(MAX_DEPTH + 2, dtype=np.int32)
+    depth_first = np.zeros(MAX_DEPTH + 2, dtype=np.int32)
+    k_per_depth = np.zeros(MAX_DEPTH + 2, dtype=np.int32)
+    R = lib().hydra_plan_rows(N, par.ctypes.data_as(P), rk.ctypes.data_as(P), dp.ctypes.data_as(P),
+                              int(bool(hydra)), node_row.ctypes.data_as(P), row_node.ctypes.data_as(P),
+                              row_first.ctypes.data_as(P), depth_first.ctypes.data_as(P),
+                              k_per_depth.ctypes.data_as(P))
+    if R < 0:
+        raise HydraError("hydra_plan_rows", R)
+    dmax = plan.dmax
+    return PlanRows(node_row, row_node[:R].copy(), row_first[: dmax + 1].copy(),
+                    depth_first[: dmax + 2].copy(), k_per_depth[:dmax].copy(), int(R))
+
+
+class DevicePlan:
+    """A tree plan and its head rows, with device copies of the arrays the
+    kernels read."""
+
+    def __init__(self, plan: TreePlan, hydra: bool, device="cuda"):
+        self.plan = plan
+        self.hydra = bool(hydra)
+        self.rows = hydra_plan_rows(plan, hydra)
+        self.N, self.dmax, self.R = plan.n, plan.dmax, self.rows.R
+
+        def up(a):
+            return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(device)
+
+        self.parent = up(plan.parent)
+        self.rank = up(plan.rank)
+        self.depth = up(plan.depth)
+        self.node_row = up(self.rows.node_row)
+        self.row_node = up(self.rows.row_node)
+
+
+# ------------------------------------------------------------------ stages
+
+def hydra_draft_heads_workspace_size(dtype_code, B, d, V, hydra, dplan: DevicePlan):
+    rf, rfp = _host_i32(dplan.rows.row_first)
+    return int(lib().hydra_draft_heads_workspace_size(dtype_code, B, d, V, int(hydra), dplan.dmax, rfp))
+
+
+def hydra_draft_heads(h, root_tok, emb, W1, b1, W2, dplan: DevicePlan, head_logits, head_lse,
+                      cand_tok, cand_logp, ws, head_hidden=None, residual=True, stream=None):
+    """Stage 1 (see include/hydra.h). h [B, d]; W1/b1/W2: lists, head k at k-1."""
+    dt = _dtype_code(h)
+    B, d = h.shape
+    V = W2[0].shape[0]
+    n_heads = len(W2)
+    if not (len(W1) == len(b1) == n_heads):
+        raise ValueError("W1, b1 and W2 need one entry per head")
+    arr = C.c_void_p * n_heads
+    w1 = arr(*[_dev(w, "W1", h.dtype) for w in W1])
+    bb = arr(*[_dev(w, "b1", h.dtype) for w in b1])
+    w2 = arr(*[_dev(w, "W2", h.dtype) for w in W2])
+    rows = dplan.rows
+    rf, rfp = _host_i32(rows.row_first)
+    df, dfp = _host_i32(rows.depth_first)
+    kp, kpp = _host_i32(rows.k_per_depth)
+    wsp, wsb = _ws(ws)
+    rc = lib().hydra_draft_heads(
+        dt, B, d, V, int(dplan.hydra), int(bool(residual)), _dev(h, "h"), _dev(root_tok, "root_tok", torch.int32),
+        _dev(emb, "emb", h.dtype) if dplan.hydra else None, n_heads, w1, bb, w2, dplan.N, dplan.dmax,
+        _dev(dplan.parent, "parent"), _dev(dplan.rank, "rank"), _dev(dplan.node_row, "node_row"), dplan.R,
+        _dev(dplan.row_node, "row_node"), rfp, dfp, kpp, _dev(head_logits, "head_logits", torch.float32),
+        _dev(head_lse, "head_lse", torch.float32), _dev(head_hidden, "head_hidden", h.dtype),
+        _dev(cand_tok, "cand_tok", torch.int32), _dev(cand_logp, "cand_logp", torch.float32), wsp, wsb,
+        _stream(stream))
+    return _check("hydra_draft_heads", rc)
+
+
+def hydra_vocab_projection(X, W, Y, stream=None):
+    """Y[M, N] = X[M, K] . W[N, K]^T in float32."""
+    M, K = X.shape
+    N = W.shape[0]
+    rc = lib().hydra_vocab_projection(_dtype_code(X), M, K, N, _dev(X, "X"), _dev(W, "W", X.dtype),
+                                      _dev(Y, "Y", torch.float32), _stream(stream))
+    return _check("hydra_vocab_projection", rc)
+
+
+def tree_build_workspace_size(B, N, n_keep):
+    return int(lib().tree_build_workspace_size(B, N, n_keep))
+
+
+def tree_build(dplan: DevicePlan, cand_tok, cand_logp, n_keep, tok, parent, depth, anc, q_row, src,
+               ws=None, stream=None):
+    """Stage 2 (see include/hydra.h)."""
+    B = cand_tok.shape[0]
+    wsp, wsb = _ws(ws)
+    rc = lib().tree_build(B, dplan.N, dplan.dmax, _dev(dplan.parent, "parent"), _dev(dplan.rank, "rank"),
+                          _dev(dplan.depth, "depth"), _dev(dplan.node_row, "node_row"),
+                          _dev(cand_tok, "cand_tok", torch.int32), _dev(cand_logp, "cand_logp", torch.float32),
+                          int(n_keep), _dev(tok, "tok", torch.int32), _dev(parent, "parent", torch.int32),
+                          _dev(depth, "depth", torch.int32), _dev(anc, "anc", torch.int32),
+                          _dev(q_row, "q_row", torch.int32), _dev(src, "src", torch.int32), wsp, wsb,
+                          _stream(stream))
+    return _check("tree_build", rc)
+
+
+def tree_attention_verify_workspace_size(dtype_code, B, N, Hq, Hkv, D, max_prefix_len):
+    return int(lib().tree_attention_verify_workspace_size(dtype_code, B, N, Hq, Hkv, D, max_prefix_len))
+
+
+def tree_attention_verify(q, k_tree, v_tree, k_pages, v_pages, block_table, prefix_len, max_prefix_len,
+                          anc, depth, out, lse=None, ws=None, scale=None, stream=None):
+    """Stage 3 (see include/hydra.h). q [B, N, Hq, D]; pages [n_pages, Hkv, page, D]."""
+    B, N, Hq, D = q.shape
+    Hkv = k_tree.shape[2]
+    n_pages, _, page_size, _ = k_pages.shape
+    max_pages = block_table.shape[1]
+    Dmax = anc.shape[2] - 1
+    if scale is None:
+        scale = 1.0 / float(D) ** 0.5
+    wsp, wsb = _ws(ws)
+    rc = lib().tree_attention_verify(
+        _dtype_code(q), B, N, Hq, Hkv, D, float(scale), _dev(q, "q"), _dev(k_tree, "k_tree", q.dtype),
+        _dev(v_tree, "v_tree", q.dtype), _dev(k_pages, "k_pages", q.dtype), _dev(v_pages, "v_pages", q.dtype),
+        n_pages, page_size, _dev(block_table, "block_table", torch.int32), max_pages,
+        _dev(prefix_len, "prefix_len", torch.int32), int(max_prefix_len), _dev(anc, "anc", torch.int32),
+        _dev(depth, "depth", torch.int32), Dmax, _dev(out, "out", q.dtype), _dev(lse, "lse", torch.float32),
+        wsp, wsb, _stream(stream))
+    return _check("tree_attention_verify", rc)
+
+
+def tree_accept_workspace_size(mode, B, N, V):
+    return int(lib().tree_accept_workspace_size(mode, B, N, V))
+
+
+def tree_accept(o, W_t, tok, parent, target_logits, n_accepted, path, out_tok, ws, mode=0, temperature=1.0,
+                q_row=None, head_logits=None, u_acc=None, u_res=None, stream=None):
+    """Stage 4 (see include/hydra.h). o [B, N, d]."""
+    B, N, d = o.shape
+    V = W_t.shape[0]
+    Dmax = path.shape[1] - 1
+    R = head_logits.shape[1] if head_logits is not None else 0
+    wsp, wsb = _ws(ws)
+    rc = lib().tree_accept(
+        _dtype_code(o), int(mode), B, N, d, V, Dmax, _dev(o, "o"), _dev(W_t, "W_t", o.dtype), float(temperature),
+        _dev(tok, "tok", torch.int32), _dev(parent, "parent", torch.int32), _dev(q_row, "q_row", torch.int32),
+        _dev(head_logits, "head_logits", torch.float32), R, _dev(u_acc, "u_acc", torch.float32),
+        _dev(u_res, "u_res", torch.float32), _dev(target_logits, "target_logits", torch.float32),
+        _dev(n_accepted, "n_accepted", torch.int32), _dev(path, "path", torch.int32),
+        _dev(out_tok, "out_tok", torch.int32), wsp, wsb, _stream(stream))
+    return _check("tree_accept", rc)

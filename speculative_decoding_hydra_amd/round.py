@@ -1,0 +1,99 @@
+"""One draft-and-verify round: buffers plus the four library calls in order.
+
+Allocation and sequencing only; every step of the round runs in libhydra's
+kernels. Buffers are allocated once per shape so a round can be replayed (or
+captured in a HIP graph) without allocating.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import hydra as H
+
+
+def make_plan(tree):
+    """Tree plan from a spec: ("cartesian", b), ("sparse", caps, n_nodes) or
+    ("dense", b, n_keep). Returns (plan, n_keep)."""
+    kind = tree[0]
+    if kind == "cartesian":
+        p = H.hydra_plan_cartesian(tree[1])
+        return p, p.n
+    if kind == "sparse":
+        p = H.hydra_plan_sparse(tree[1], tree[2])
+        return p, p.n
+    if kind == "dense":
+        return H.hydra_plan_cartesian(tree[1]), int(tree[2])
+    raise ValueError(f"unknown tree kind {kind!r}")
+
+
+class HydraRound:
+    """Buffers and calls for one round of B sequences.
+
+    weights: dict with emb [V, d] (Hydra), W1/b1/W2 lists, W_t [V, d].
+    shape: dict with B, d, V, Hq, Hkv, D, max_prefix_len.
+    """
+
+    def __init__(self, weights, tree, shape, hydra=True, mode=0, temperature=1.0, residual=True,
+                 keep_hidden=False, device="cuda"):
+        self.w = weights
+        plan, n_keep = make_plan(tree)
+        self.dplan = H.DevicePlan(plan, hydra, device)
+        self.n_keep = n_keep
+        self.hydra, self.mode, self.T, self.residual = hydra, int(mode), float(temperature), residual
+        B, d, V = shape["B"], shape["d"], shape["V"]
+        Hq, Hkv, D = shape["Hq"], shape["Hkv"], shape["D"]
+        self.shape = dict(shape)
+        dt = weights["W_t"].dtype
+        self.dtype = dt
+        code = H.HYDRA_F32 if dt == torch.float32 else H.HYDRA_BF16
+        N, R, Dm, K = self.dplan.N, self.dplan.R, self.dplan.dmax, n_keep
+        i32, f32 = torch.int32, torch.float32
+        z = lambda *s, dtype=f32: torch.empty(*s, dtype=dtype, device=device)  # noqa: E731
+        self.head_logits = z(B, R, V)
+        self.head_lse = z(B, R)
+        self.head_hidden = z(B, R, d, dtype=dt) if keep_hidden else None
+        self.cand_tok = z(B, N, dtype=i32)
+        self.cand_logp = z(B, N)
+        self.tok, self.parent, self.depth = z(B, K, dtype=i32), z(B, K, dtype=i32), z(B, K, dtype=i32)
+        self.q_row, self.src = z(B, K, dtype=i32), z(B, K, dtype=i32)
+        self.anc = z(B, K, Dm + 1, dtype=i32)
+        self.attn_out = z(B, K, Hq, D, dtype=dt)
+        self.attn_lse = z(B, K, Hq)
+        self.target_logits = z(B, K, V)
+        self.n_accepted = z(B, dtype=i32)
+        self.path = z(B, Dm + 1, dtype=i32)
+        self.out_tok = z(B, Dm + 1, dtype=i32)
+        nb = lambda n: torch.empty(max(int(n), 1), dtype=torch.uint8, device=device)  # noqa: E731
+        self.ws_draft = nb(H.hydra_draft_heads_workspace_size(code, B, d, V, hydra, self.dplan))
+        self.ws_build = nb(H.tree_build_workspace_size(B, N, K))
+        self.ws_attn = nb(H.tree_attention_verify_workspace_size(code, B, K, Hq, Hkv, D,
+                                                                 shape["max_prefix_len"]))
+        self.ws_accept = nb(H.tree_accept_workspace_size(self.mode, B, K, V))
+
+    def draft(self, h, root_tok, stream=None):
+        H.hydra_draft_heads(h, root_tok, self.w.get("emb"), self.w["W1"], self.w["b1"], self.w["W2"], self.dplan,
+                            self.head_logits, self.head_lse, self.cand_tok, self.cand_logp, self.ws_draft,
+                            head_hidden=self.head_hidden, residual=self.residual, stream=stream)
+
+    def build(self, stream=None):
+        H.tree_build(self.dplan, self.cand_tok, self.cand_logp, self.n_keep, self.tok, self.parent, self.depth,
+                     self.anc, self.q_row, self.src, self.ws_build, stream=stream)
+
+    def attend(self, q, k_tree, v_tree, k_pages, v_pages, block_table, prefix_len, stream=None):
+        H.tree_attention_verify(q, k_tree, v_tree, k_pages, v_pages, block_table, prefix_len,
+                                self.shape["max_prefix_len"], self.anc, self.depth, self.attn_out, self.attn_lse,
+                                self.ws_attn, stream=stream)
+
+    def accept(self, u_acc=None, u_res=None, stream=None):
+        B, K = self.attn_out.shape[:2]
+        H.tree_accept(self.attn_out.view(B, K, -1), self.w["W_t"], self.tok, self.parent, self.target_logits,
+                      self.n_accepted, self.path, self.out_tok, self.ws_accept, mode=self.mode,
+                      temperature=self.T, q_row=self.q_row, head_logits=self.head_logits, u_acc=u_acc,
+                      u_res=u_res, stream=stream)
+
+    def run(self, h, root_tok, q, k_tree, v_tree, k_pages, v_pages, block_table, prefix_len, u_acc=None,
+            u_res=None, stream=None):
+        self.draft(h, root_tok, stream)
+        self.build(stream)
+        self.attend(q, k_tree, v_tree, k_pages, v_pages, block_table, prefix_len, stream)
+        self.accept(u_acc, u_res, stream)

@@ -1,0 +1,234 @@
+"""Shared pieces of the GPU parity tests and the smoke check.
+
+Parity is stage-wise: each oracle stage is fed the device's upstream outputs
+(parent tokens, hidden states, tree, attention output), so that one
+near-tie at depth 1 cannot cascade, and the float and integer results of
+every stage are compared with the oracle on the same inputs:
+
+* head hidden state u: oracle from the device's parent tokens;
+* head logits z and log-sum-exp: oracle projection of the device's u;
+* top-k tokens: bit-exact, except where the oracle's margin between
+  consecutive sorted logits is below 1e-4, where the decision is recomputed
+  on the CPU from the device's logits;
+* tree: oracle prune / ancestors from the device's cumulative scores;
+* attention output: oracle from the device's ancestor table;
+* target logits: oracle projection of the device's attention output;
+* acceptance: oracle walk on the device's logits.
+
+Tolerances (max-abs): 1e-4 in float32 mode and 2e-2 for bfloat16 inputs
+with float32 accumulation.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import torch
+
+import hydra_inputs as HI
+from oracle import hydra_oracle as O
+
+MARGIN = 1e-4
+
+
+def tol(w):
+    return 1e-4 if w.dtype == "fp32" else 2e-2
+
+
+def oracle_plan(tree):
+    kind = tree[0]
+    if kind == "cartesian":
+        return O.plan_cartesian(tree[1]), None
+    if kind == "sparse":
+        return O.plan_sparse_template(tree[1], tree[2]), None
+    return O.plan_cartesian(tree[1]), tree[2]
+
+
+def round_inputs(inp, device="cuda", keep_hidden=True):
+    """HydraRound plus device copies of one generated workload."""
+    from speculative_decoding_hydra_amd import HydraRound
+
+    w = inp["workload"]
+    to = lambda t: t.to(device).contiguous()  # noqa: E731
+    weights = dict(emb=to(inp["E"]) if w.hydra else None, W1=[to(x) for x in inp["W1"]],
+                   b1=[to(x) for x in inp["b1"]], W2=[to(x) for x in inp["W2"]], W_t=to(inp["W_t"]))
+    shape = dict(B=w.B, d=w.d, V=w.V, Hq=w.Hq, Hkv=w.Hkv, D=w.D,
+                 max_prefix_len=int(inp["prefix_len"].max()))
+    rnd = HydraRound(weights, w.tree, shape, hydra=w.hydra, mode=0 if w.mode == "greedy" else 1,
+                     temperature=w.T, keep_hidden=keep_hidden, device=device)
+    dev = dict(h=to(inp["h"]), root_tok=to(inp["root_tok"]), q=to(inp["q_tree"]), k_tree=to(inp["k_tree"]),
+               v_tree=to(inp["v_tree"]), k_pages=to(inp["k_pages"]), v_pages=to(inp["v_pages"]),
+               block_table=to(inp["block_table"]), prefix_len=to(inp["prefix_len"]))
+    if w.mode == "stochastic":
+        dev["u_acc"], dev["u_res"] = to(inp["u_acc"]), to(inp["u_res"])
+    return rnd, dev
+
+
+def run_round(rnd, dev, stream=None):
+    rnd.run(dev["h"], dev["root_tok"], dev["q"], dev["k_tree"], dev["v_tree"], dev["k_pages"], dev["v_pages"],
+            dev["block_table"], dev["prefix_len"], dev.get("u_acc"), dev.get("u_res"), stream=stream)
+
+
+def np_(t):
+    return t.detach().cpu().to(torch.float64).numpy() if t.is_floating_point() else t.detach().cpu().numpy()
+
+
+def check_topk(z_oracle, z_dev, k, got_ids, where):
+    """Top-k decision of one row: bit-exact unless the oracle margin < 1e-4."""
+    mine = O.topk_sorted(z_oracle, k)
+    if np.array_equal(mine, got_ids):
+        return False
+    margin = O.topk_margin(z_oracle, k)
+    assert margin < MARGIN, f"{where}: top-{k} {list(got_ids)} != oracle {list(mine)} (margin {margin:.3g})"
+    recomputed = O.topk_sorted(z_dev, k)
+    assert np.array_equal(recomputed, got_ids), f"{where}: top-{k} differs from the CPU on the device logits"
+    return True
+
+
+def check_draft(inp, rnd, seqs=None, rows=None):
+    """Stage 1, stage-wise. Returns max errors."""
+    w = inp["workload"]
+    t = tol(w)
+    bf16 = w.dtype == "bf16"
+    plan, _ = oracle_plan(w.tree)
+    dp = rnd.dplan
+    assert np.array_equal(plan.parent, dp.plan.parent) and np.array_equal(plan.rank, dp.plan.rank)
+    row_node, row_depth, node_row = O.head_rows(plan, w.hydra)
+    assert np.array_equal(node_row, dp.rows.node_row)
+    if w.hydra:
+        assert np.array_equal(row_node, dp.rows.row_node)
+    kmax = {}
+    for c in range(1, plan.n):
+        r = node_row[plan.parent[c]]
+        kmax[r] = max(kmax.get(r, 0), int(plan.rank[c]) + 1)
+    logits = np_(rnd.head_logits)
+    lse = np_(rnd.head_lse)
+    hidden = np_(rnd.head_hidden)
+    ctok = np_(rnd.cand_tok)
+    clogp = np_(rnd.cand_logp)
+    h = HI.as_f64(inp["h"])
+    seqs = range(w.B) if seqs is None else seqs
+    rows = range(len(row_node)) if rows is None else rows
+    err = dict(u=0.0, z=0.0, lse=0.0, logp=0.0, flips=0)
+    W1c, W2c = {}, {}
+    for r in rows:
+        k = int(row_depth[r])
+        if k not in W1c:
+            W1c[k] = HI.as_f64(inp["W1"][k - 1])
+            W2c[k] = HI.as_f64(inp["W2"][k - 1])
+        W1, W2 = W1c[k], W2c[k]
+        b1 = HI.as_f64(inp["b1"][k - 1])
+        for b in seqs:
+            e = None
+            if w.hydra:
+                p = int(row_node[r])
+                ptok = int(inp["root_tok"][b]) if p == 0 else int(ctok[b, p])
+                e = HI.as_f64(inp["E"][ptok])
+            u = O.head_hidden(h[b], e, W1, b1, True, bf16)
+            err["u"] = max(err["u"], float(np.max(np.abs(u - hidden[b, r]))))
+            z = O.head_logits(hidden[b, r], W2)
+            err["z"] = max(err["z"], float(np.max(np.abs(z - logits[b, r]))))
+            err["lse"] = max(err["lse"], abs(O.logsumexp(z) - lse[b, r]))
+            kids = [c for c in range(1, plan.n) if node_row[plan.parent[c]] == r]
+            ids = np.array([ctok[b, c] for c in sorted(kids, key=lambda c: plan.rank[c])])
+            err["flips"] += check_topk(z, logits[b, r], kmax[r], ids, f"seq {b} row {r}")
+            # device decision equals the CPU's on the device logits, always
+            assert np.array_equal(O.topk_sorted(logits[b, r], kmax[r]), ids), f"seq {b} row {r}: top-k"
+            for c in kids:
+                ref = clogp[b, plan.parent[c]] + logits[b, r, ctok[b, c]] - O.logsumexp(logits[b, r])
+                err["logp"] = max(err["logp"], abs(ref - clogp[b, c]))
+    assert err["u"] <= t, f"head hidden max-abs {err['u']:.3g} > {t}"
+    assert err["z"] <= t, f"head logits max-abs {err['z']:.3g} > {t}"
+    assert err["lse"] <= t and err["logp"] <= t, (err["lse"], err["logp"])
+    for b in seqs:
+        assert ctok[b, 0] == int(inp["root_tok"][b]) and clogp[b, 0] == 0.0
+    return err
+
+
+def check_build(inp, rnd, seqs=None):
+    w = inp["workload"]
+    plan, n_keep = oracle_plan(w.tree)
+    ctok, clogp = np_(rnd.cand_tok), np_(rnd.cand_logp)
+    tok, par, dep = np_(rnd.tok), np_(rnd.parent), np_(rnd.depth)
+    anc, qrow, src = np_(rnd.anc), np_(rnd.q_row), np_(rnd.src)
+    _, _, node_row = O.head_rows(plan, w.hydra)
+    seqs = range(w.B) if seqs is None else seqs
+    for b in seqs:
+        if n_keep is None:
+            kept, s = plan, np.arange(plan.n)
+        else:
+            kept, s = O.prune_tree(plan, clogp[b], n_keep)
+        assert np.array_equal(src[b], s), f"seq {b}: kept set / order"
+        assert np.array_equal(par[b], kept.parent) and np.array_equal(dep[b], kept.depth)
+        assert np.array_equal(tok[b], ctok[b][s])
+        assert np.array_equal(anc[b], O.ancestors(kept.parent, plan.dmax))
+        assert np.array_equal(qrow[b], node_row[s])
+
+
+def check_attention(inp, rnd, seqs=None):
+    w = inp["workload"]
+    t = tol(w)
+    seqs = list(range(w.B)) if seqs is None else list(seqs)
+    anc = np_(rnd.anc)[seqs]
+    sub = lambda x: HI.as_f64(x[seqs])  # noqa: E731
+    kp = [HI.as_f64(inp["k_prefix"][b]) for b in seqs]
+    vp = [HI.as_f64(inp["v_prefix"][b]) for b in seqs]
+    out, lse = O.tree_attention(sub(inp["q_tree"]), sub(inp["k_tree"]), sub(inp["v_tree"]), kp, vp, anc,
+                                bf16=w.dtype == "bf16")
+    got = np_(rnd.attn_out)[seqs]
+    e_o = float(np.max(np.abs(out - got)))
+    e_l = float(np.max(np.abs(lse - np_(rnd.attn_lse)[seqs])))
+    assert e_o <= t, f"attention output max-abs {e_o:.3g} > {t}"
+    assert e_l <= t, f"attention lse max-abs {e_l:.3g} > {t}"
+    return dict(o=e_o, lse=e_l)
+
+
+def check_accept(inp, rnd, seqs=None):
+    w = inp["workload"]
+    t = tol(w)
+    seqs = range(w.B) if seqs is None else seqs
+    O_dev = np_(rnd.attn_out)
+    Z_dev = np_(rnd.target_logits)
+    Wt = HI.as_f64(inp["W_t"])
+    tok, par, qrow = np_(rnd.tok), np_(rnd.parent), np_(rnd.q_row)
+    n_acc, path, out = np_(rnd.n_accepted), np_(rnd.path), np_(rnd.out_tok)
+    Dm = rnd.dplan.dmax
+    e_z = 0.0
+    amb = 0
+    for b in seqs:
+        Z = O.target_logits(O_dev[b: b + 1], Wt)[0]
+        e_z = max(e_z, float(np.max(np.abs(Z - Z_dev[b]))))
+        if w.mode == "greedy":
+            m, p, o = O.greedy_accept(Z_dev[b], tok[b], par[b], Dm)
+        else:
+            hz = np_(rnd.head_logits)[b]
+            m, p, o = O.rejection_accept(Z_dev[b], hz, qrow[b], tok[b], par[b], np_(inp["u_acc"])[b],
+                                         np_(inp["u_res"])[b], w.T)
+        got_p = [int(x) for x in path[b] if x >= 0]
+        got_o = [int(x) for x in out[b] if x >= 0]
+        if w.mode == "greedy":
+            assert n_acc[b] == m and got_p == p and got_o == o, f"seq {b}: greedy walk {got_p}/{got_o} vs {p}/{o}"
+        elif not (n_acc[b] == m and got_p == p and got_o == o):
+            amb += 1
+            assert got_p[: len(p)] == p[: len(got_p)] or got_p[:-1] == p[:-1], f"seq {b}: rejection walk diverged"
+    assert e_z <= t, f"target logits max-abs {e_z:.3g} > {t}"
+    return dict(z=e_z, ambiguous=amb)
+
+
+def oracle_round_checks(inp, rnd, seqs=None, rows=None):
+    rep = {}
+    for k, v in check_draft(inp, rnd, seqs, rows).items():
+        rep["draft_" + k] = v
+    check_build(inp, rnd, seqs)
+    for k, v in check_attention(inp, rnd, seqs).items():
+        rep["attn_" + k] = v
+    for k, v in check_accept(inp, rnd, seqs).items():
+        rep["accept_" + k] = v
+    return rep
+
+
+def ambiguous_sample(r, u, eps=1e-6):
+    """True if u * sum(r) lies within eps * sum(r) of a cumulative boundary."""
+    c = np.cumsum(np.asarray(r, dtype=np.float64))
+    thr = u * c[-1]
+    return float(np.min(np.abs(c - thr))) < eps * c[-1] or math.isclose(thr, 0.0)

@@ -1,0 +1,155 @@
+"""C ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, and its host-side tree-plan builders agree with the
+oracle's independent ones."""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+from oracle import hydra_oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hydra.h")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b(\w+)\s*\(", text, flags=re.M)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from speculative_decoding_hydra_amd._lib import LIB_PATH, lib as load
+
+    if not os.path.exists(LIB_PATH):
+        from speculative_decoding_hydra_amd.build import build
+
+        build()
+    return load()
+
+
+def test_header_declares_the_four_stages():
+    names = set(header_functions())
+    for fn in ("hydra_draft_heads", "tree_build", "tree_attention_verify", "tree_accept"):
+        assert fn in names
+
+
+def test_every_declared_symbol_is_exported_and_bound(lib):
+    from speculative_decoding_hydra_amd._lib import SIGNATURES
+
+    names = header_functions()
+    assert len(names) >= 15
+    for name in names:
+        assert hasattr(lib, name), f"{name} not exported"
+        assert name in SIGNATURES, f"{name} has no binding signature"
+    assert set(SIGNATURES) == set(names)
+    raw = C.CDLL(os.path.join(ROOT, "speculative_decoding_hydra_amd", "libhydra.so"))
+    for name in names:
+        getattr(raw, name)
+
+
+def test_status_strings(lib):
+    assert lib.hydra_status_string(0) == b"ok"
+    assert lib.hydra_status_string(-3) == b"workspace too small"
+    assert lib.hydra_abi_version() == 1
+
+
+@pytest.mark.parametrize("b", [[2, 3], [3, 2, 2], [4, 4, 4, 4], [1, 1, 1, 1, 1], [5, 2], [2, 1, 3]])
+def test_cartesian_plan_matches_oracle(lib, b):
+    import speculative_decoding_hydra_amd as S
+
+    got = S.hydra_plan_cartesian(b)
+    ref = O.plan_cartesian(b)
+    assert np.array_equal(got.parent, ref.parent)
+    assert np.array_equal(got.rank, ref.rank)
+    assert np.array_equal(got.depth, ref.depth)
+
+
+@pytest.mark.parametrize("caps,n", [((10, 4, 2, 1), 64), ((4, 3, 2, 1), 30), ((6, 6, 6), 100), ((3,), 4)])
+def test_sparse_plan_matches_oracle(lib, caps, n):
+    import speculative_decoding_hydra_amd as S
+
+    got = S.hydra_plan_sparse(caps, n)
+    ref = O.plan_sparse_template(caps, n)
+    assert np.array_equal(got.parent, ref.parent)
+    assert np.array_equal(got.rank, ref.rank)
+    assert np.array_equal(got.depth, ref.depth)
+
+
+@pytest.mark.parametrize("hydra", [True, False])
+@pytest.mark.parametrize("tree", [("c", [2, 3]), ("s", ((10, 4, 2, 1), 64)), ("c", [4, 4, 4, 4])])
+def test_plan_rows_match_oracle(lib, hydra, tree):
+    import speculative_decoding_hydra_amd as S
+
+    if tree[0] == "c":
+        plan = S.hydra_plan_cartesian(tree[1])
+    else:
+        plan = S.hydra_plan_sparse(*tree[1])
+    rows = S.hydra_plan_rows(plan, hydra)
+    op = O.TreePlan(plan.parent.astype(np.int64), plan.rank.astype(np.int64), plan.depth.astype(np.int64))
+    row_node, row_depth, node_row = O.head_rows(op, hydra)
+    assert rows.R == len(row_node)
+    assert np.array_equal(rows.node_row, node_row)
+    if hydra:
+        assert np.array_equal(rows.row_node, row_node)
+    for k in range(1, plan.dmax + 1):
+        assert list(range(rows.row_first[k - 1], rows.row_first[k])) == list(np.flatnonzero(row_depth == k))
+        nodes = np.flatnonzero(plan.depth == k)
+        assert rows.depth_first[k] == nodes[0] and rows.depth_first[k + 1] == nodes[-1] + 1
+        fan = max(len(op.children(u)) for u in np.flatnonzero(plan.depth == k - 1))
+        assert rows.k_per_depth[k - 1] == fan
+
+
+def test_plan_rows_rejects_bad_trees(lib):
+    import speculative_decoding_hydra_amd as S
+
+    good = S.hydra_plan_cartesian([2, 2])
+    for mutate in ("parent", "rank", "depth"):
+        bad = S.TreePlan(good.parent.copy(), good.rank.copy(), good.depth.copy())
+        if mutate == "parent":
+            bad.parent[3] = 5  # parent after child
+        elif mutate == "rank":
+            bad.rank[4] = 0    # siblings 0, 0
+        else:
+            bad.depth[2] = 2
+        with pytest.raises(S.HydraError):
+            S.hydra_plan_rows(bad, True)
+
+
+def test_plan_builders_reject_bad_arguments(lib):
+    import speculative_decoding_hydra_amd as S
+
+    with pytest.raises(S.HydraError):
+        S.hydra_plan_cartesian([0, 2])
+    with pytest.raises(S.HydraError):
+        S.hydra_plan_cartesian([17])
+    with pytest.raises(S.HydraError):
+        S.hydra_plan_sparse((2, 2), 100)  # only 6 candidates
+
+
+def test_workspace_queries(lib):
+    import speculative_decoding_hydra_amd as S
+
+    assert S.tree_attention_verify_workspace_size(1, 1, 64, 32, 32, 128, 2048) > 0
+    assert S.tree_attention_verify_workspace_size(0, 1, 9, 8, 8, 32, 128) == 0  # float32 path needs none
+    assert S.tree_accept_workspace_size(0, 1, 64, 32000) >= 64 * 4
+    assert S.tree_accept_workspace_size(1, 4, 64, 32000) >= 4 * 2 * 32000 * 4
+    plan = S.hydra_plan_sparse((10, 4, 2, 1), 64)
+
+    class P:
+        rows = S.hydra_plan_rows(plan, True)
+        dmax = 4
+
+    assert S.hydra_draft_heads_workspace_size(1, 1, 4096, 32000, True, P) >= 13 * 4096 * (4 + 2)
+
+
+def test_binding_fails_loudly_without_the_library(monkeypatch):
+    import speculative_decoding_hydra_amd._lib as L
+
+    monkeypatch.setattr(L, "LIB_PATH", "/nonexistent/libhydra.so")
+    monkeypatch.setattr(L, "_lib", None)
+    with pytest.raises(RuntimeError, match="no fallback"):
+        L.lib()

@@ -1,0 +1,282 @@
+"""Device path against the CPU oracle, through the C ABI (needs an MI355X).
+
+Float tolerances (max-abs): 1e-4 in float32 mode, 2e-2 for bfloat16 inputs
+with float32 accumulation. Integer results (tokens, tree indices, accepted
+lengths) are bit-exact, with the 1e-4 margin rule of tests/helpers.py for
+top-k decisions.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import hydra_inputs as HI
+from oracle import hydra_oracle as O
+from tests import helpers as T
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    import speculative_decoding_hydra_amd._lib as L
+
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    L.lib()  # fails loudly if libhydra.so is missing
+    torch.cuda.set_device(0)
+
+
+def _bf16(x):
+    return x.to(torch.bfloat16)
+
+
+# ------------------------------------------------------------ projections
+
+@pytest.mark.parametrize("M,K,N", [(1, 256, 1000), (5, 512, 640), (16, 4096, 4096), (17, 256, 2000),
+                                   (33, 1024, 777), (64, 4096, 32000), (100, 512, 1000), (256, 256, 512),
+                                   (300, 256, 130), (13, 8192, 4096), (0, 256, 64)])
+def test_projection_bf16(M, K, N):
+    from speculative_decoding_hydra_amd import hydra_vocab_projection
+
+    print(f"projection bf16 M={M} K={K} N={N}", flush=True)
+    g = torch.Generator().manual_seed(M * 7 + K + N)
+    X = _bf16(torch.randn(M, K, generator=g))
+    W = _bf16(torch.randn(N, K, generator=g) * 0.02)
+    Y = torch.full((M, N), float("nan"), device="cuda")
+    hydra_vocab_projection(X.cuda(), W.cuda(), Y)
+    torch.cuda.synchronize()
+    if M == 0:
+        return
+    ref = HI.as_f64(X) @ HI.as_f64(W).T
+    err = float(np.max(np.abs(Y.cpu().double().numpy() - ref)))
+    assert err <= 1e-3, err  # bf16 inputs are exact in fp32; only the summation order differs
+
+
+@pytest.mark.parametrize("M,K,N", [(1, 256, 1000), (9, 256, 1000), (7, 100, 33)])
+def test_projection_f32(M, K, N):
+    from speculative_decoding_hydra_amd import hydra_vocab_projection
+
+    g = torch.Generator().manual_seed(M + K + N)
+    X = torch.randn(M, K, generator=g)
+    W = torch.randn(N, K, generator=g) * 0.02
+    Y = torch.empty(M, N, device="cuda")
+    hydra_vocab_projection(X.cuda(), W.cuda(), Y)
+    torch.cuda.synchronize()
+    ref = X.double().numpy() @ W.double().numpy().T
+    assert float(np.max(np.abs(Y.cpu().double().numpy() - ref))) <= 1e-5
+
+
+# -------------------------------------------------------------- attention
+
+def _attn_case(B, N, Hq, Hkv, D, lens, dtype, seed, tree=None, scattered=True, page=16):
+    g = torch.Generator().manual_seed(seed)
+    dt = torch.float32 if dtype == "fp32" else torch.bfloat16
+    if tree is None:
+        # random breadth-first tree: parent[i] uniform over earlier nodes, depth <= 8
+        parent = [-1]
+        depth = [0]
+        for i in range(1, N):
+            while True:
+                p = int(torch.randint(0, i, (1,), generator=g))
+                if depth[p] < 8:
+                    break
+            parent.append(p)
+            depth.append(depth[p] + 1)
+        order = sorted(range(N), key=lambda i: (depth[i], i))
+        new = {o: k for k, o in enumerate(order)}
+        parent = [-1 if parent[o] < 0 else new[parent[o]] for o in order]
+        parent = np.array(parent)
+    else:
+        parent = tree
+    dm = 1
+    anc = O.ancestors(parent, 8)
+    dep = np.array([int(np.sum(a >= 0)) - 1 for a in anc])
+    dm = max(1, int(dep.max()))
+    anc = anc[:, : dm + 1]
+    q = torch.randn(B, N, Hq, D, generator=g).to(dt)
+    kt = torch.randn(B, N, Hkv, D, generator=g).to(dt)
+    vt = torch.randn(B, N, Hkv, D, generator=g).to(dt)
+    kp = [torch.randn(L, Hkv, D, generator=g).to(dt) for L in lens]
+    vp = [torch.randn(L, Hkv, D, generator=g).to(dt) for L in lens]
+    per = [max(1, math.ceil(L / page)) for L in lens]
+    n_pages = sum(per)
+    order = torch.randperm(n_pages, generator=g) if scattered else torch.arange(n_pages)
+    kpool = torch.zeros(n_pages, Hkv, page, D, dtype=dt)
+    vpool = torch.zeros(n_pages, Hkv, page, D, dtype=dt)
+    bt = torch.full((B, max(per)), -1, dtype=torch.int32)
+    nxt = 0
+    for b, L in enumerate(lens):
+        for j in range(per[b]):
+            pid = int(order[nxt])
+            nxt += 1
+            bt[b, j] = pid
+            lo, hi = j * page, min(L, (j + 1) * page)
+            if hi > lo:
+                kpool[pid, :, : hi - lo] = kp[b][lo:hi].transpose(0, 1)
+                vpool[pid, :, : hi - lo] = vp[b][lo:hi].transpose(0, 1)
+    ancB = np.stack([anc] * B).astype(np.int32)
+    depB = np.stack([dep] * B).astype(np.int32)
+    return dict(q=q, kt=kt, vt=vt, kp=kp, vp=vp, kpool=kpool, vpool=vpool, bt=bt,
+                lens=torch.tensor(lens, dtype=torch.int32), anc=ancB, dep=depB, dt=dt)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("B,N,Hq,Hkv,D,lens", [
+    (1, 9, 8, 8, 32, [128]),
+    (1, 64, 4, 4, 128, [2048 + 5]),
+    (2, 64, 8, 1, 128, [300, 17]),
+    (3, 100, 16, 2, 128, [0, 1, 777]),
+    (1, 1, 4, 4, 128, [64]),
+    (2, 256, 2, 2, 128, [1000, 64]),
+    (1, 37, 4, 2, 64, [129]),
+])
+def test_tree_attention(dtype, B, N, Hq, Hkv, D, lens):
+    from speculative_decoding_hydra_amd import tree_attention_verify, tree_attention_verify_workspace_size
+
+    print(f"attention {dtype} B={B} N={N} Hq={Hq} Hkv={Hkv} D={D} L={lens}", flush=True)
+    c = _attn_case(B, N, Hq, Hkv, D, lens, dtype, seed=N * 31 + Hq + sum(lens))
+    dev = lambda t: t.cuda().contiguous()  # noqa: E731
+    out = torch.full((B, N, Hq, D), float("nan"), dtype=c["dt"], device="cuda")
+    lse = torch.empty(B, N, Hq, device="cuda")
+    code = 0 if dtype == "fp32" else 1
+    ws = torch.empty(max(1, tree_attention_verify_workspace_size(code, B, N, Hq, Hkv, D, max(lens))),
+                     dtype=torch.uint8, device="cuda")
+    tree_attention_verify(dev(c["q"]), dev(c["kt"]), dev(c["vt"]), dev(c["kpool"]), dev(c["vpool"]), dev(c["bt"]),
+                          dev(c["lens"]), max(lens), dev(torch.from_numpy(c["anc"])), dev(torch.from_numpy(c["dep"])),
+                          out, lse, ws)
+    torch.cuda.synchronize()
+    f = HI.as_f64
+    ref, ref_lse = O.tree_attention(f(c["q"]), f(c["kt"]), f(c["vt"]), [f(x) for x in c["kp"]],
+                                    [f(x) for x in c["vp"]], c["anc"], bf16=dtype == "bf16")
+    t = 1e-4 if dtype == "fp32" else 2e-2
+    e = float(np.max(np.abs(out.cpu().double().numpy() - ref)))
+    el = float(np.max(np.abs(lse.cpu().double().numpy() - ref_lse)))
+    print(f"  max-abs out {e:.3g} lse {el:.3g}", flush=True)
+    assert e <= t and el <= t
+
+
+# ------------------------------------------------------------ whole rounds
+
+_cache = {}
+
+
+def _round(name, **over):
+    key = (name, tuple(sorted(over.items())))
+    if key not in _cache:
+        w = HI.workload(name, **over)
+        print(f"round {name} {over}: generating", flush=True)
+        inp = HI.generate(w)
+        rnd, dev = T.round_inputs(inp)
+        print(f"round {name}: running on the device", flush=True)
+        T.run_round(rnd, dev)
+        torch.cuda.synchronize()
+        _cache.clear()
+        _cache[key] = (inp, rnd, dev)
+    return _cache[key]
+
+
+@pytest.mark.parametrize("name", ["tiny", "tiny_medusa"])
+def test_tiny_round_stagewise(name):
+    inp, rnd, _ = _round(name)
+    rep = T.oracle_round_checks(inp, rnd)
+    print(rep, flush=True)
+
+
+@pytest.mark.parametrize("name", ["tiny", "tiny_medusa"])
+def test_tiny_round_end_to_end(name):
+    """Float32 workload: the oracle's own round from the inputs alone."""
+    inp, rnd, _ = _round(name)
+    w = inp["workload"]
+    plan, _ = T.oracle_plan(w.tree)
+    f = HI.as_f64
+    heads = [(f(a), f(b), f(c)) for a, b, c in zip(inp["W1"], inp["b1"], inp["W2"])]
+    res = O.draft_heads(f(inp["h"]), inp["root_tok"].numpy(), f(inp["E"]), heads, plan, hydra=w.hydra)
+    for r in range(res["z"].shape[1]):
+        assert res["margin"][0, r] > T.MARGIN, "near tie: seed would need the margin rule"
+    assert np.array_equal(res["tok"], rnd.cand_tok.cpu().numpy())
+    anc = O.ancestors(plan.parent, plan.dmax)[None]
+    out, _ = O.tree_attention(f(inp["q_tree"]), f(inp["k_tree"]), f(inp["v_tree"]),
+                              [f(x) for x in inp["k_prefix"]], [f(x) for x in inp["v_prefix"]], anc)
+    Z = O.target_logits(out, f(inp["W_t"]))[0]
+    m, path, toks = O.greedy_accept(Z, res["tok"][0], plan.parent, plan.dmax)
+    assert int(rnd.n_accepted[0]) == m
+    assert [int(x) for x in rnd.out_tok[0] if x >= 0] == toks
+    assert [int(x) for x in rnd.path[0] if x >= 0] == path
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("hydra", [False, True])
+def test_zero_init_heads_reproduce_lm_head_exactly(dtype, hydra):
+    """Zero-initialised heads whose vocabulary projection is a copy of the
+    base head give that head's logits bit for bit (same projection kernel)."""
+    from speculative_decoding_hydra_amd import hydra_vocab_projection
+
+    over = dict(zero_init=True)
+    if dtype == "bf16":
+        over.update(dtype="bf16", d=256)
+    inp, rnd, dev = _round("tiny" if hydra else "tiny_medusa", **over)
+    base = torch.empty(1, inp["workload"].V, device="cuda")
+    hydra_vocab_projection(dev["h"], rnd.w["W_t"], base)
+    torch.cuda.synchronize()
+    got = rnd.head_logits[0]
+    assert torch.equal(rnd.head_hidden[0], dev["h"].expand_as(rnd.head_hidden[0]))
+    assert all(torch.equal(got[r], base[0]) for r in range(got.shape[0]))
+
+
+def test_greedy_planted_paths():
+    """Target logits forced along a chosen branch give that accepted length."""
+    from speculative_decoding_hydra_amd import tree_accept, tree_accept_workspace_size
+
+    g = np.random.default_rng(0)
+    V, d, B = 1000, 256, 4
+    plan = O.plan_cartesian([2, 3, 2])
+    N = plan.n
+    anc = O.ancestors(plan.parent, plan.dmax)
+    W = g.standard_normal((V, d)) * 0.02
+    for trial in range(6):
+        tok = np.zeros((B, N), dtype=np.int32)
+        o = g.standard_normal((B, N, d)) * 0.1
+        want = []
+        for b in range(B):
+            for u in range(N):
+                kids = plan.children(u)
+                tok[b, kids] = g.choice(V, len(kids), replace=False)
+            target = int(g.integers(0, N)) if trial else 0
+            path = [int(a) for a in anc[target] if a >= 0]
+            kid = set(int(tok[b, c]) for c in plan.children(target))
+            stop = int(g.choice([t for t in range(V) if t not in kid]))
+            for a, nx in zip(path[:-1], path[1:]):
+                o[b, a] = W[tok[b, nx]] * 40.0
+            o[b, path[-1]] = W[stop] * 40.0
+            want.append((len(path) - 1, path, [int(tok[b, c]) for c in path[1:]] + [stop]))
+        ot = torch.tensor(o, dtype=torch.float32).cuda()
+        Wt = torch.tensor(W, dtype=torch.float32).cuda()
+        tk = torch.tensor(tok).cuda()
+        par = torch.tensor(np.stack([plan.parent] * B).astype(np.int32)).cuda()
+        Z = torch.empty(B, N, V, device="cuda")
+        n_acc = torch.empty(B, dtype=torch.int32, device="cuda")
+        path_t = torch.empty(B, plan.dmax + 1, dtype=torch.int32, device="cuda")
+        out_t = torch.empty_like(path_t)
+        ws = torch.empty(tree_accept_workspace_size(0, B, N, V), dtype=torch.uint8, device="cuda")
+        tree_accept(ot, Wt, tk, par, Z, n_acc, path_t, out_t, ws)
+        torch.cuda.synchronize()
+        for b in range(B):
+            m, path, toks = want[b]
+            ref = O.greedy_accept(Z[b].cpu().double().numpy(), tok[b], plan.parent, plan.dmax)
+            assert ref == (m, path, toks), "planted branch not the oracle's"
+            assert int(n_acc[b]) == m
+            assert [int(x) for x in path_t[b] if x >= 0] == path
+            assert [int(x) for x in out_t[b] if x >= 0] == toks
+
+
+def test_7b_sparse64_round():
+    inp, rnd, _ = _round("7b_sparse64")
+    rep = T.oracle_round_checks(inp, rnd)
+    print(rep, flush=True)
+
+
+def test_7b_dense256_round():
+    inp, rnd, _ = _round("7b_dense256")
+    rep = T.oracle_round_checks(inp, rnd)
+    print(rep, flush=True)

@@ -1,0 +1,243 @@
+"""Throughput of one Hydra draft-and-verify round on one MI355X.
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-graph] [--no-cpu]
+
+A step is one whole round (draft heads -> tree build -> tree-attention verify
+-> accept) over the workload's synthetic batch, with every input resident in
+HBM before timing starts. The default workload is the Vicuna-7B-shaped layer
+with the 64-node sparse tree and a 2048-token prefix (batch 1). The value is
+verified tree rows per second, B * N / t_round.
+
+The JSON line also carries
+  roofline      the dominant kernel (the head/target vocabulary projection
+                that streams a [V, d] bf16 matrix): algorithmic bytes per
+                launch / average launch duration from HIP events on its stream,
+                against the 8 TB/s HBM peak;
+  cpu_baseline  the CPU oracle timed on this host on one full round of the
+                same workload (rank 0, one GPU only).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "verified tree-tokens/sec per round + % HBM roofline (64-node tree, 7B-shape)"
+HBM_PEAK_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "vocab_projection_7b_traffic.json")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="7b_sparse64")
+    ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--kernel-reps", type=int, default=20)
+    return ap.parse_args()
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_hash():
+    import hashlib
+
+    h = hashlib.sha256()
+    with open(os.path.join(ROOT, "speculative_decoding_hydra_amd", "csrc", "proj.hip"), "rb") as f:
+        h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """Per-launch HBM bytes of the projection kernel from committed counter
+    runs, or None when they are missing or the kernel changed since."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    return t.get("bytes_per_launch") if t.get("proj_hip_sha256_16") == source_hash() else None
+
+
+def cpu_baseline(inp, n_rows):
+    """The oracle, as it stands, on one full round of the same workload."""
+    import numpy as np
+
+    import hydra_inputs as HI
+    from oracle import hydra_oracle as O
+
+    w = inp["workload"]
+    f = HI.as_f64
+    heads = [(f(a), f(b), f(c)) for a, b, c in zip(inp["W1"], inp["b1"], inp["W2"])]
+    E, Wt, h = f(inp["E"]), f(inp["W_t"]), f(inp["h"])
+    kp = [f(x) for x in inp["k_prefix"]]
+    vp = [f(x) for x in inp["v_prefix"]]
+    q, kt, vt = f(inp["q_tree"]), f(inp["k_tree"]), f(inp["v_tree"])
+    kind = w.tree[0]
+    plan = O.plan_sparse_template(w.tree[1], w.tree[2]) if kind == "sparse" else O.plan_cartesian(w.tree[1])
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:  # noqa: BLE001
+        threads = os.cpu_count() or 1
+    reps, total = 0, 0.0
+    while reps < 5 and total < 10.0:  # a bounded sample: whole rounds, about 10 s
+        t0 = time.perf_counter()
+        res = O.draft_heads(h, inp["root_tok"].numpy(), E, heads, plan, hydra=w.hydra, bf16=w.dtype == "bf16")
+        if kind == "dense":
+            trees = [O.prune_tree(plan, res["logp"][b], w.tree[2]) for b in range(w.B)]
+        else:
+            trees = [(plan, np.arange(plan.n)) for _ in range(w.B)]
+        anc = np.stack([O.ancestors(t.parent, plan.dmax) for t, _ in trees])
+        out, _ = O.tree_attention(q, kt, vt, kp, vp, anc, bf16=w.dtype == "bf16")
+        Z = O.target_logits(out, Wt)
+        for b, (t, s) in enumerate(trees):
+            O.greedy_accept(Z[b], res["tok"][b][s], t.parent, plan.dmax)
+        total += time.perf_counter() - t0
+        reps += 1
+    dt = total / reps
+    return {"value": n_rows / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{reps} full round(s) of {w.name} (B={w.B}, N={n_rows // w.B}) in float64 NumPy, "
+                      f"{dt:.2f} s per round; inputs converted to float64 before timing"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (each sequence "
+              "batch shards across GPUs with no exchange; see DESIGN.md). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import hydra_inputs as HI
+    from speculative_decoding_hydra_amd import hydra_vocab_projection, round_from_inputs, run_round
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    w = HI.workload(args.workload)
+    log(f"[bench] generating {w.name}")
+    inp = HI.generate(w)
+    rnd, dev = round_from_inputs(inp, device="cuda:0", keep_hidden=False)
+    N = rnd.n_keep
+    rows = w.B * N
+    stream = torch.cuda.current_stream()
+
+    for _ in range(max(1, args.warmup)):
+        run_round(rnd, dev)
+    torch.cuda.synchronize()
+
+    graph = None
+    if not args.no_graph:
+        try:
+            s = torch.cuda.Stream()
+            s.wait_stream(stream)
+            with torch.cuda.stream(s):
+                run_round(rnd, dev)
+            stream.wait_stream(s)
+            torch.cuda.synchronize()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                run_round(rnd, dev)
+            torch.cuda.synchronize()
+            for _ in range(max(1, args.warmup)):
+                graph.replay()
+            torch.cuda.synchronize()
+        except Exception as e:  # noqa: BLE001
+            log(f"[bench] graph capture unavailable ({e}); timing eager launches")
+            graph = None
+
+    log(f"[bench] timing {args.steps} rounds ({'graph' if graph else 'eager'})")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        if graph is not None:
+            graph.replay()
+        else:
+            run_round(rnd, dev)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms = elapsed / args.steps * 1e3
+
+    # per-stage times (eager, events on the launch stream)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+    stage_ms = [0.0] * 4
+    reps = 10
+    for _ in range(reps):
+        ev[0].record(stream)
+        rnd.draft(dev["h"], dev["root_tok"])
+        ev[1].record(stream)
+        rnd.build()
+        ev[2].record(stream)
+        rnd.attend(dev["q"], dev["k_tree"], dev["v_tree"], dev["k_pages"], dev["v_pages"], dev["block_table"],
+                   dev["prefix_len"])
+        ev[3].record(stream)
+        rnd.accept(dev.get("u_acc"), dev.get("u_res"))
+        ev[4].record(stream)
+        torch.cuda.synchronize()
+        for i in range(4):
+            stage_ms[i] += ev[i].elapsed_time(ev[i + 1]) / reps
+
+    # dominant kernel: the [V, d] vocabulary projection of a head (largest row count of the round)
+    M = int(max(rnd.dplan.rows.row_first[1:] - rnd.dplan.rows.row_first[:-1])) * w.B
+    X = torch.randn(M, w.d, device="cuda").to(rnd.dtype)
+    Y = torch.empty(M, w.V, device="cuda")
+    W2 = rnd.w["W2"][0]
+    for _ in range(3):
+        hydra_vocab_projection(X, W2, Y)
+    ka, kb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ka.record(stream)
+    for i in range(args.kernel_reps):
+        hydra_vocab_projection(X, rnd.w["W2"][i % len(rnd.w["W2"])], Y)
+    kb.record(stream)
+    torch.cuda.synchronize()
+    k_ms = ka.elapsed_time(kb) / args.kernel_reps
+    esz = X.element_size()
+    alg_bytes = w.V * w.d * esz + M * w.d * esz + M * w.V * 4
+    achieved = alg_bytes / (k_ms * 1e-3) / 1e9
+
+    cpu = None
+    if not args.no_cpu:
+        log("[bench] timing the CPU oracle on one round")
+        cpu = cpu_baseline(inp, rows)
+
+    res = {
+        "metric": METRIC,
+        "value": rows / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded N(0,1) activations, N(0,0.02) weights; no checkpoint)",
+        "config": {"workload": w.name, "batch": w.B, "tree_rows": N, "hidden": w.d, "vocab": w.V,
+                   "heads": w.n_heads, "q_heads": w.Hq, "kv_heads": w.Hkv, "head_dim": w.D,
+                   "prefix": list(w.L), "tree": str(w.tree[0]), "acceptance": w.mode,
+                   "launch": "hip-graph" if graph is not None else "eager"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(),
+                     "kernel": "proj_bf16_kernel<1,256,false> (vocabulary projection)",
+                     "bytes_per_launch": alg_bytes, "rows": M, "avg_launch_ms": k_ms},
+        "stages_ms": {"draft": stage_ms[0], "build": stage_ms[1], "attention": stage_ms[2],
+                      "accept": stage_ms[3]},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

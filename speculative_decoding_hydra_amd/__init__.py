@@ -10,4 +10,4 @@ from .hydra import (  # noqa: F401
     tree_accept_workspace_size, tree_attention_verify, tree_attention_verify_workspace_size, tree_build,
     tree_build_workspace_size,
 )
-from .round import HydraRound, make_plan  # noqa: F401
+from .round import HydraRound, make_plan, round_from_inputs, run_round  # noqa: F401

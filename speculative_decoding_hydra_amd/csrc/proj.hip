@@ -27,7 +27,7 @@ struct RowPtrs {
   const bf16_t* p1;  // segment for k >= K0 (pre-offset by -K0)
 };
 
-template <int MT, int KC>
+template <int MT, int KC, bool SPLIT>
 __global__ __launch_bounds__(256) void proj_bf16_kernel(int M, int K, int N, XSource xs,
                                                         const bf16_t* __restrict__ W,
                                                         float* __restrict__ Y, RowMap map,
@@ -134,12 +134,12 @@ __global__ __launch_bounds__(256) void proj_bf16_kernel(int M, int K, int N, XSo
     const int m = m_base + t * 16 + (lane & 15);
     if (m >= M) continue;
     float* dst;
-    if (part) {
+    if constexpr (SPLIT) {
       dst = part + (static_cast<size_t>(blockIdx.y) * M + m) * N;
     } else {
       dst = Y + static_cast<size_t>(map(m)) * ldy;
     }
-    if (n0 + 3 < N && (N & 3) == 0 && (part || (ldy & 3) == 0)) {
+    if (n0 + 3 < N && (N & 3) == 0 && (SPLIT || (ldy & 3) == 0)) {
       *reinterpret_cast<float4*>(dst + n0) = make_float4(acc[t][0], acc[t][1], acc[t][2], acc[t][3]);
     } else {
 #pragma unroll
@@ -187,8 +187,14 @@ int launch_bf16(int M, int K, int N, XSource xs, const void* W, float* Y, RowMap
   constexpr int KC = MT <= 4 ? 256 : (MT <= 8 ? 128 : 64);
   const int kper = K / nsplit;
   dim3 grid((N + kRowsPerWG - 1) / kRowsPerWG, nsplit);
-  proj_bf16_kernel<MT, KC><<<grid, 256, 0, stream>>>(
-      M, K, N, xs, static_cast<const bf16_t*>(W), Y, map, ldy, kper, m_base, part);
+  // split-K launches (partials) and direct launches are separate instances
+  if (part) {
+    proj_bf16_kernel<MT, KC, true><<<grid, 256, 0, stream>>>(
+        M, K, N, xs, static_cast<const bf16_t*>(W), Y, map, ldy, kper, m_base, part);
+  } else {
+    proj_bf16_kernel<MT, KC, false><<<grid, 256, 0, stream>>>(
+        M, K, N, xs, static_cast<const bf16_t*>(W), Y, map, ldy, kper, m_base, part);
+  }
   HY_LAUNCH_CHECK("projection(bf16)");
   return HYDRA_OK;
 }

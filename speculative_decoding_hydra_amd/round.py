@@ -97,3 +97,32 @@ class HydraRound:
         self.build(stream)
         self.attend(q, k_tree, v_tree, k_pages, v_pages, block_table, prefix_len, stream)
         self.accept(u_acc, u_res, stream)
+
+
+def round_from_inputs(inp, device="cuda", keep_hidden=True):
+    """HydraRound plus device copies of a dict of named input tensors.
+
+    Keys: workload (sizes, tree, dtype, mode), root_tok, h, E, W1, b1, W2, W_t,
+    q_tree, k_tree, v_tree, k_pages, v_pages, block_table, prefix_len and, for
+    the rejection mode, u_acc and u_res. Returns (round, device tensors).
+    """
+    w = inp["workload"]
+    to = lambda t: t.to(device).contiguous()  # noqa: E731
+    weights = dict(emb=to(inp["E"]) if w.hydra else None, W1=[to(x) for x in inp["W1"]],
+                   b1=[to(x) for x in inp["b1"]], W2=[to(x) for x in inp["W2"]], W_t=to(inp["W_t"]))
+    shape = dict(B=w.B, d=w.d, V=w.V, Hq=w.Hq, Hkv=w.Hkv, D=w.D,
+                 max_prefix_len=int(inp["prefix_len"].max()))
+    rnd = HydraRound(weights, w.tree, shape, hydra=w.hydra, mode=0 if w.mode == "greedy" else 1,
+                     temperature=w.T, keep_hidden=keep_hidden, device=device)
+    dev = dict(h=to(inp["h"]), root_tok=to(inp["root_tok"]), q=to(inp["q_tree"]), k_tree=to(inp["k_tree"]),
+               v_tree=to(inp["v_tree"]), k_pages=to(inp["k_pages"]), v_pages=to(inp["v_pages"]),
+               block_table=to(inp["block_table"]), prefix_len=to(inp["prefix_len"]))
+    if w.mode == "stochastic":
+        dev["u_acc"], dev["u_res"] = to(inp["u_acc"]), to(inp["u_res"])
+    return rnd, dev
+
+
+def run_round(rnd, dev, stream=None):
+    """One round on the device tensors returned by round_from_inputs."""
+    rnd.run(dev["h"], dev["root_tok"], dev["q"], dev["k_tree"], dev["v_tree"], dev["k_pages"], dev["v_pages"],
+            dev["block_table"], dev["prefix_len"], dev.get("u_acc"), dev.get("u_res"), stream=stream)

@@ -45,28 +45,15 @@ def oracle_plan(tree):
 
 
 def round_inputs(inp, device="cuda", keep_hidden=True):
-    """HydraRound plus device copies of one generated workload."""
-    from speculative_decoding_hydra_amd import HydraRound
+    from speculative_decoding_hydra_amd import round_from_inputs
 
-    w = inp["workload"]
-    to = lambda t: t.to(device).contiguous()  # noqa: E731
-    weights = dict(emb=to(inp["E"]) if w.hydra else None, W1=[to(x) for x in inp["W1"]],
-                   b1=[to(x) for x in inp["b1"]], W2=[to(x) for x in inp["W2"]], W_t=to(inp["W_t"]))
-    shape = dict(B=w.B, d=w.d, V=w.V, Hq=w.Hq, Hkv=w.Hkv, D=w.D,
-                 max_prefix_len=int(inp["prefix_len"].max()))
-    rnd = HydraRound(weights, w.tree, shape, hydra=w.hydra, mode=0 if w.mode == "greedy" else 1,
-                     temperature=w.T, keep_hidden=keep_hidden, device=device)
-    dev = dict(h=to(inp["h"]), root_tok=to(inp["root_tok"]), q=to(inp["q_tree"]), k_tree=to(inp["k_tree"]),
-               v_tree=to(inp["v_tree"]), k_pages=to(inp["k_pages"]), v_pages=to(inp["v_pages"]),
-               block_table=to(inp["block_table"]), prefix_len=to(inp["prefix_len"]))
-    if w.mode == "stochastic":
-        dev["u_acc"], dev["u_res"] = to(inp["u_acc"]), to(inp["u_res"])
-    return rnd, dev
+    return round_from_inputs(inp, device=device, keep_hidden=keep_hidden)
 
 
 def run_round(rnd, dev, stream=None):
-    rnd.run(dev["h"], dev["root_tok"], dev["q"], dev["k_tree"], dev["v_tree"], dev["k_pages"], dev["v_pages"],
-            dev["block_table"], dev["prefix_len"], dev.get("u_acc"), dev.get("u_res"), stream=stream)
+    from speculative_decoding_hydra_amd import run_round as _run
+
+    _run(rnd, dev, stream)
 
 
 def np_(t):
@@ -130,7 +117,13 @@ def check_draft(inp, rnd, seqs=None, rows=None):
             err["z"] = max(err["z"], float(np.max(np.abs(z - logits[b, r]))))
             err["lse"] = max(err["lse"], abs(O.logsumexp(z) - lse[b, r]))
             kids = [c for c in range(1, plan.n) if node_row[plan.parent[c]] == r]
-            ids = np.array([ctok[b, c] for c in sorted(kids, key=lambda c: plan.rank[c])])
+            # every parent served by the row takes a prefix of the row's list
+            lists = [[int(ctok[b, c]) for c in sorted(plan.children(p), key=lambda c: plan.rank[c])]
+                     for p in range(plan.n) if node_row[p] == r]
+            ids = np.array(max(lists, key=len))
+            assert len(ids) == kmax[r]
+            for lst in lists:
+                assert lst == list(ids[: len(lst)]), f"seq {b} row {r}: parents disagree"
             err["flips"] += check_topk(z, logits[b, r], kmax[r], ids, f"seq {b} row {r}")
             # device decision equals the CPU's on the device logits, always
             assert np.array_equal(O.topk_sorted(logits[b, r], kmax[r]), ids), f"seq {b} row {r}: top-k"

@@ -120,7 +120,8 @@ def main():
     import torch
 
     import hydra_inputs as HI
-    from speculative_decoding_hydra_amd import hydra_vocab_projection, round_from_inputs, run_round
+    from speculative_decoding_hydra_amd import (hydra_vocab_projection, hydra_vocab_projection_workspace_size,
+                                                 round_from_inputs, run_round)
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
@@ -188,17 +189,42 @@ def main():
             stage_ms[i] += ev[i].elapsed_time(ev[i + 1]) / reps
 
     # dominant kernel: the [V, d] vocabulary projection of a head (largest row count of the round)
+    # (same kernel instance as the round's head launches: fused top-k epilogue)
     M = int(max(rnd.dplan.rows.row_first[1:] - rnd.dplan.rows.row_first[:-1])) * w.B
+    kk = int(max(rnd.dplan.rows.k_per_depth))
     X = torch.randn(M, w.d, device="cuda").to(rnd.dtype)
     Y = torch.empty(M, w.V, device="cuda")
+    kws = torch.empty(hydra_vocab_projection_workspace_size(M, w.V, kk), dtype=torch.uint8, device="cuda")
     W2 = rnd.w["W2"][0]
+    proj = lambda Wm: hydra_vocab_projection(X, Wm, Y, kk, kws)  # noqa: E731
     for _ in range(3):
-        hydra_vocab_projection(X, W2, Y)
+        proj(W2)
+    torch.cuda.synchronize()
+    kgraph = None
+    try:  # back-to-back launches from a graph, so the events see no launch gaps
+        s2 = torch.cuda.Stream()
+        s2.wait_stream(stream)
+        with torch.cuda.stream(s2):
+            proj(W2)
+        stream.wait_stream(s2)
+        torch.cuda.synchronize()
+        kgraph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(kgraph):
+            for i in range(args.kernel_reps):
+                proj(rnd.w["W2"][i % len(rnd.w["W2"])])
+        kgraph.replay()
+        torch.cuda.synchronize()
+    except Exception as e:  # noqa: BLE001
+        log(f"[bench] kernel graph unavailable ({e}); eager launches")
+        kgraph = None
     ka, kb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     ka.record(stream)
-    for i in range(args.kernel_reps):
-        hydra_vocab_projection(X, rnd.w["W2"][i % len(rnd.w["W2"])], Y)
+    if kgraph is not None:
+        kgraph.replay()
+    else:
+        for i in range(args.kernel_reps):
+            proj(rnd.w["W2"][i % len(rnd.w["W2"])])
     kb.record(stream)
     torch.cuda.synchronize()
     k_ms = ka.elapsed_time(kb) / args.kernel_reps
@@ -230,8 +256,8 @@ def main():
                    "launch": "hip-graph" if graph is not None else "eager"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(),
-                     "kernel": "proj_bf16_kernel<1,256,false> (vocabulary projection)",
-                     "bytes_per_launch": alg_bytes, "rows": M, "avg_launch_ms": k_ms},
+                     "kernel": "proj_bf16_kernel<1,256,2,false,true> (vocabulary projection, fused top-k)",
+                     "bytes_per_launch": alg_bytes, "rows": M, "topk": kk, "avg_launch_ms": k_ms},
         "stages_ms": {"draft": stage_ms[0], "build": stage_ms[1], "attention": stage_ms[2],
                       "accept": stage_ms[3]},
         "cpu_baseline": cpu,

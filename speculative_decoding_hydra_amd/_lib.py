@@ -23,7 +23,10 @@ SIGNATURES = {
                                   C.POINTER(c_void), C.POINTER(c_void), C.POINTER(c_void), c_int, c_int,
                                   c_void, c_void, c_void, c_int, c_void, i32p, i32p, i32p, c_void, c_void,
                                   c_void, c_void, c_void, c_void, c_size, c_void]),
-    "hydra_vocab_projection": (c_int, [c_int, c_int, c_int, c_int, c_void, c_void, c_void, c_void]),
+    "hydra_vocab_projection_workspace_size": (c_size, [c_int, c_int, c_int]),
+    "hydra_vocab_projection": (c_int, [c_int, c_int, c_int, c_int, c_int, c_void, c_void, c_void, c_void, c_size,
+                                       c_void]),
+    "hydra_vocab_topk": (c_int, [c_int, c_int, c_int, c_void, c_size, c_void, c_void, c_void, c_void]),
     "tree_build_workspace_size": (c_size, [c_int, c_int, c_int]),
     "tree_build": (c_int, [c_int, c_int, c_int, c_void, c_void, c_void, c_void, c_void, c_void, c_int,
                            c_void, c_void, c_void, c_void, c_void, c_void, c_void, c_size, c_void]),

@@ -20,43 +20,6 @@
 namespace hydra {
 namespace {
 
-__global__ __launch_bounds__(256) void row_argmax(int V, const float* __restrict__ Z, int32_t* __restrict__ amax) {
-  __shared__ uint64_t wbest[4];
-  const float* z = Z + static_cast<size_t>(blockIdx.x) * V;
-  uint64_t best = 0;
-  if ((V & 3) == 0) {
-    const float4* z4 = reinterpret_cast<const float4*>(z);
-    for (int i = threadIdx.x; i < V / 4; i += 256) {
-      const float4 q = z4[i];
-      uint64_t k = topk_key(q.x, 4 * i);
-      best = k > best ? k : best;
-      k = topk_key(q.y, 4 * i + 1);
-      best = k > best ? k : best;
-      k = topk_key(q.z, 4 * i + 2);
-      best = k > best ? k : best;
-      k = topk_key(q.w, 4 * i + 3);
-      best = k > best ? k : best;
-    }
-  } else {
-    for (int i = threadIdx.x; i < V; i += 256) {
-      const uint64_t k = topk_key(z[i], i);
-      best = k > best ? k : best;
-    }
-  }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    const uint64_t o = shfl_xor_u64(best, off);
-    best = o > best ? o : best;
-  }
-  if ((threadIdx.x & 63) == 0) wbest[threadIdx.x >> 6] = best;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    for (int w = 1; w < 4; ++w) best = wbest[w] > best ? wbest[w] : best;
-    best = wbest[0] > best ? wbest[0] : best;
-    amax[blockIdx.x] = key_id(best);
-  }
-}
-
 // One wave per sequence.
 __global__ __launch_bounds__(64) void greedy_walk(int N, int Dmax, const int32_t* __restrict__ amax,
                                                   const int32_t* __restrict__ tok,
@@ -298,7 +261,10 @@ using namespace hydra;
 
 extern "C" size_t tree_accept_workspace_size(int mode, int B, int N, int V) {
   if (B <= 0 || N <= 0 || V <= 0) return 0;
-  if (mode == 0) return align_up(static_cast<size_t>(B) * N * sizeof(int32_t), 256) + 256;
+  const size_t rows = static_cast<size_t>(B) * N;
+  if (mode == 0)
+    return align_up(rows * sizeof(int32_t), 256) + align_up(rows * projection_nwg(V) * sizeof(uint64_t), 256) +
+           align_up(rows * projection_nwg(V) * sizeof(float2), 256) + 256;
   return align_up(static_cast<size_t>(B) * 2 * V * sizeof(float), 256) + 256;
 }
 
@@ -332,16 +298,33 @@ extern "C" int tree_accept(int dtype, int mode, int B, int N, int d, int V, int 
   xs.ldx = d;
   xs.mode = 0;
   const int M = B * N;
-  int rc = launch_projection(dtype, M, d, V, xs, W_t, target_logits, RowMap{M, 0, 0}, V, 1, nullptr, stream);
-  if (rc != HYDRA_OK) return rc;
   Arena arena(ws, ws_bytes);
   if (mode == 0) {
+    // target logits with fused arg-max partials, merged per row, then the walk
     int32_t* amax = arena.take<int32_t>(static_cast<size_t>(M));
-    row_argmax<<<M, 256, 0, stream>>>(V, target_logits, amax);
-    HY_LAUNCH_CHECK("tree_accept: argmax");
+    const int nwg = projection_nwg(V);
+    uint64_t* keys = arena.take<uint64_t>(static_cast<size_t>(M) * nwg);
+    float2* ms = arena.take<float2>(static_cast<size_t>(M) * nwg);
+    int rc = launch_projection(dtype, M, d, V, xs, W_t, target_logits, RowMap{M, 0, 0}, V, 1, nullptr,
+                               TopkPartials{keys, ms, 1}, stream);
+    if (rc != HYDRA_OK) return rc;
+    MergeArgs ma{};
+    ma.M = M;
+    ma.nwg = nwg;
+    ma.k = 1;
+    ma.keys = keys;
+    ma.ms = ms;
+    ma.map = RowMap{M, 0, 0};
+    ma.amax = amax;
+    ma.P = 1;
+    rc = launch_topk_merge(ma, stream);
+    if (rc != HYDRA_OK) return rc;
     greedy_walk<<<B, 64, 0, stream>>>(N, Dmax, amax, tok, parent, n_accepted, path, out_tok);
     HY_LAUNCH_CHECK("tree_accept: greedy walk");
   } else {
+    int rc = launch_projection(dtype, M, d, V, xs, W_t, target_logits, RowMap{M, 0, 0}, V, 1, nullptr,
+                               TopkPartials{nullptr, nullptr, 0}, stream);
+    if (rc != HYDRA_OK) return rc;
     float* rbuf = arena.take<float>(static_cast<size_t>(B) * 2 * V);
     reject_walk<<<B, kWalkThreads, 0, stream>>>(N, V, R, Dmax, 1.0f / temperature, target_logits, head_logits, tok,
                                                 parent, q_row, u_acc, u_res, rbuf, n_accepted, path, out_tok);

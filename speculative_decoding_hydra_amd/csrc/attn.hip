@@ -29,6 +29,7 @@ namespace hydra {
 namespace {
 
 constexpr int kKT = 64;  // keys per tile
+constexpr int kMaxSplitPages = 1024;  // page ids one split stages in LDS
 
 __device__ __forceinline__ uint32_t pack2(uint16_t lo, uint16_t hi) {
   return static_cast<uint32_t>(lo) | (static_cast<uint32_t>(hi) << 16);
@@ -50,6 +51,10 @@ __global__ __launch_bounds__(256) void attn_split_mfma(
   constexpr int DD = D / 16;
   __shared__ __align__(16) bf16_t klds[kKT * KROW];
   __shared__ __align__(16) bf16_t vlds[D * VROW];
+  __shared__ bool s_ok[kKT];
+  __shared__ int s_dep[kKT];                              // depth of each tree key of the tile
+  __shared__ int s_pages[kMaxSplitPages];                 // page ids of this split
+  __shared__ int s_anc[64][HYDRA_MAX_DEPTH + 1];          // ancestor rows of the 64 query rows
 
   const int split = blockIdx.x;
   const bool tree_part = split == nsplit;
@@ -69,7 +74,7 @@ __global__ __launch_bounds__(256) void attn_split_mfma(
     const bf16_t* qp = q + ((static_cast<size_t>(b) * N + u) * Hq + hkv * G + gq) * D + 8 * g;
 #pragma unroll
     for (int j = 0; j < DJ; ++j) {
-      const uint4 v = qvalid ? *reinterpret_cast<const uint4*>(qp + 32 * j) : make_uint4(0, 0, 0, 0);
+      const u32x4_t v = qvalid ? *reinterpret_cast<const u32x4_t*>(qp + 32 * j) : u32x4_t{0u, 0u, 0u, 0u};
       qreg[j] = __builtin_bit_cast(bf16x8_t, v);
     }
   }
@@ -85,8 +90,20 @@ __global__ __launch_bounds__(256) void attn_split_mfma(
     t_begin = split * lsplit;
     t_end = min(L, t_begin + lsplit);
   }
-  const int32_t* anc_u = anc + (static_cast<size_t>(b) * N + u) * (Dmax + 1);
   const int32_t* dep_b = depth + static_cast<size_t>(b) * N;
+  const int wrow_q = wave * 16 + lq;  // this lane's query row inside the tile
+  if (tree_part) {
+    for (int e = tid; e < 64 * (Dmax + 1); e += 256) {
+      const int r = e / (Dmax + 1), j = e % (Dmax + 1);
+      const int qr = qtile * 64 + r;
+      s_anc[r][j] = qr < NQ ? anc[(static_cast<size_t>(b) * N + qr / G) * (Dmax + 1) + j] : -1;
+    }
+  } else {
+    const int p0 = t_begin / page_size;
+    const int np = t_end > t_begin ? (t_end - 1) / page_size - p0 + 1 : 0;
+    for (int e = tid; e < np; e += 256) s_pages[e] = block_table[static_cast<size_t>(b) * max_pages + p0 + e];
+  }
+  __syncthreads();
 
   float m_run = -INFINITY, l_run = 0.f;
   f32x4_t oacc[DD];
@@ -98,43 +115,56 @@ __global__ __launch_bounds__(256) void attn_split_mfma(
   const int dc = tid & 15;          // 8-dim chunk 0..15
   const int tl = 4 * tg;
 
-  for (int t0 = t_begin; t0 < t_end; t0 += kKT) {
-    uint4 kv[4], vv[4];
-    const bf16_t* kbase = nullptr;
-    const bf16_t* vbase = nullptr;
-    int stride = 0;  // elements between consecutive keys
-    int valid = 0;   // keys of this thread's group inside the range
+  u32x4_t kv[4], vv[4];
+  int kvalid = 0;  // keys of this thread's group of 4 that exist (range and page)
+  // Registers of the next tile: 4 keys x 8 dims of K and of V per thread.
+  // Loads are unconditional (invalid keys re-read a valid row and are masked
+  // through s_ok), so the compiler can keep them in flight across the tile.
+  auto load_tile = [&](int t0) {
     const int tk = t0 + tl;
-    if (tk < t_end) {
-      valid = min(4, t_end - tk);
-      if (tree_part) {
-        const size_t off = ((static_cast<size_t>(b) * N + tk) * Hkv + hkv) * D + dc * 8;
-        kbase = k_tree + off;
-        vbase = v_tree + off;
-        stride = Hkv * D;
-      } else {
-        const int pg = block_table[static_cast<size_t>(b) * max_pages + tk / page_size];
-        if (pg >= 0 && pg < n_pages) {
-          const size_t off =
-              ((static_cast<size_t>(pg) * Hkv + hkv) * page_size + tk % page_size) * D + dc * 8;
-          kbase = k_pages + off;
-          vbase = v_pages + off;
-          stride = D;
-        } else {
-          valid = 0;
-        }
+    int valid = tk < t_end ? min(4, t_end - tk) : 0;
+    const bf16_t* kb;
+    const bf16_t* vb;
+    int stride;
+    if (tree_part) {
+      const int tc = tk < N ? tk : 0;
+      const size_t off = ((static_cast<size_t>(b) * N + tc) * Hkv + hkv) * D + dc * 8;
+      kb = k_tree + off;
+      vb = v_tree + off;
+      stride = Hkv * D;
+    } else {
+      const int tc = tk < t_end ? tk : t_begin;
+      int pg = s_pages[tc / page_size - t_begin / page_size];
+      if (pg < 0 || pg >= n_pages) {
+        pg = 0;
+        valid = 0;
+      }
+      const size_t off = ((static_cast<size_t>(pg) * Hkv + hkv) * page_size + tc % page_size) * D + dc * 8;
+      kb = k_pages + off;
+      vb = v_pages + off;
+      stride = D;
+    }
+    kvalid = valid;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const size_t o = j < valid ? static_cast<size_t>(j) * stride : 0;
+      kv[j] = *reinterpret_cast<const u32x4_t*>(kb + o);
+      vv[j] = *reinterpret_cast<const u32x4_t*>(vb + o);
+    }
+  };
+  if (t_begin < t_end) load_tile(t_begin);
+
+  for (int t0 = t_begin; t0 < t_end; t0 += kKT) {
+    __syncthreads();  // previous tile fully consumed
+    if (dc == 0) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        s_ok[tl + j] = j < kvalid;
+        if (tree_part) s_dep[tl + j] = j < kvalid ? dep_b[t0 + tl + j] : -1;
       }
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      kv[j] = j < valid ? *reinterpret_cast<const uint4*>(kbase + static_cast<size_t>(j) * stride)
-                        : make_uint4(0, 0, 0, 0);
-      vv[j] = j < valid ? *reinterpret_cast<const uint4*>(vbase + static_cast<size_t>(j) * stride)
-                        : make_uint4(0, 0, 0, 0);
-    }
-    __syncthreads();  // previous tile fully consumed
-#pragma unroll
-    for (int j = 0; j < 4; ++j) *reinterpret_cast<uint4*>(&klds[(tl + j) * KROW + dc * 8]) = kv[j];
+    for (int j = 0; j < 4; ++j) *reinterpret_cast<u32x4_t*>(&klds[(tl + j) * KROW + dc * 8]) = kv[j];
     {
       typedef __attribute__((ext_vector_type(8))) uint16_t u16x8;
       const u16x8 a0 = __builtin_bit_cast(u16x8, vv[0]);
@@ -143,13 +173,14 @@ __global__ __launch_bounds__(256) void attn_split_mfma(
       const u16x8 a3 = __builtin_bit_cast(u16x8, vv[3]);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        uint2 w;
+        u32x2_t w;
         w.x = pack2(a0[e], a1[e]);
         w.y = pack2(a2[e], a3[e]);
-        *reinterpret_cast<uint2*>(&vlds[(dc * 8 + e) * VROW + tl]) = w;
+        *reinterpret_cast<u32x2_t*>(&vlds[(dc * 8 + e) * VROW + tl]) = w;
       }
     }
     __syncthreads();
+    if (t0 + kKT < t_end) load_tile(t0 + kKT);  // next tile in flight during this one
 
     // S^T tile: lane holds keys 16 tt + 4 g + i for query column lq
     f32x4_t sacc[4];
@@ -158,7 +189,7 @@ __global__ __launch_bounds__(256) void attn_split_mfma(
       sacc[tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int j = 0; j < DJ; ++j) {
-        const uint4 a = *reinterpret_cast<const uint4*>(&klds[(16 * tt + lq) * KROW + 32 * j + 8 * g]);
+        const u32x4_t a = *reinterpret_cast<const u32x4_t*>(&klds[(16 * tt + lq) * KROW + 32 * j + 8 * g]);
         sacc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), qreg[j],
                                                           sacc[tt], 0, 0, 0);
       }
@@ -170,10 +201,10 @@ __global__ __launch_bounds__(256) void attn_split_mfma(
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int t = t0 + 16 * tt + 4 * g + i;
-        bool ok = t < t_end;
-        if (tree_part && ok) {
-          const int dv = dep_b[t];
-          ok = dv >= 0 && dv <= Dmax && anc_u[dv] == t;
+        bool ok = s_ok[16 * tt + 4 * g + i];
+        if (tree_part) {
+          const int dv = s_dep[16 * tt + 4 * g + i];
+          ok = ok && dv >= 0 && dv <= Dmax && s_anc[wrow_q][dv] == t;
         }
         const float s = ok ? sacc[tt][i] * scale_log2 : -INFINITY;
         sv[tt][i] = s;
@@ -213,9 +244,9 @@ __global__ __launch_bounds__(256) void attn_split_mfma(
 #pragma unroll
       for (int dd = 0; dd < DD; ++dd) {
         const bf16_t* vr = &vlds[(16 * dd + lq) * VROW + 32 * ks + 4 * g];
-        uint4 a;
-        const uint2 lo = *reinterpret_cast<const uint2*>(vr);
-        const uint2 hi = *reinterpret_cast<const uint2*>(vr + 16);
+        u32x4_t a;
+        const u32x2_t lo = *reinterpret_cast<const u32x2_t*>(vr);
+        const u32x2_t hi = *reinterpret_cast<const u32x2_t*>(vr + 16);
         a.x = lo.x;
         a.y = lo.y;
         a.z = hi.x;
@@ -239,41 +270,48 @@ __global__ __launch_bounds__(256) void attn_split_mfma(
   }
 }
 
-// Merge the splits of one (sequence, KV head, query row): lanes over D.
+// Merge the splits of one (sequence, KV head, query row). D / 4 lanes per row,
+// four dims per lane, so a wave merges 64 * 4 / D rows at once.
 template <class T>
 __global__ __launch_bounds__(256) void attn_combine(int B, int N, int Hq, int Hkv, int D, int nparts,
                                                     int NQ, int NQpad, const float* __restrict__ opart,
                                                     const float* __restrict__ mpart,
                                                     const float* __restrict__ lpart, T* __restrict__ out,
                                                     float* __restrict__ lse) {
-  const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);  // over B * Hkv * NQ
+  const int lpr = D / 4;  // lanes per row
+  const int tid = blockIdx.x * 256 + threadIdx.x;
+  const int row = tid / lpr;  // over B * Hkv * NQ
+  const int c = tid % lpr;
   if (row >= B * Hkv * NQ) return;
   const int qi = row % NQ;
   const int bh = row / NQ;
   const int b = bh / Hkv, hkv = bh % Hkv;
   const int G = Hq / Hkv;
   const int u = qi / G, hq = hkv * G + qi % G;
+  const size_t stride = static_cast<size_t>(B) * Hkv * NQpad;
+  const size_t r0 = (static_cast<size_t>(b) * Hkv + hkv) * NQpad + qi;
   float M = -INFINITY;
-  for (int s = 0; s < nparts; ++s) {
-    const size_t r = (static_cast<size_t>(s * B + b) * Hkv + hkv) * NQpad + qi;
-    M = fmaxf(M, mpart[r]);
-  }
+  for (int s = 0; s < nparts; ++s) M = fmaxf(M, mpart[r0 + s * stride]);
   const float Mu = M == -INFINITY ? 0.f : M;
   float Lsum = 0.f;
-  float acc0 = 0.f, acc1 = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int s = 0; s < nparts; ++s) {
-    const size_t r = (static_cast<size_t>(s * B + b) * Hkv + hkv) * NQpad + qi;
+    const size_t r = r0 + s * stride;
     const float w = exp2f(mpart[r] - Mu);
     Lsum += lpart[r] * w;
-    if (lane < D) acc0 += opart[r * D + lane] * w;
-    if (lane + 64 < D) acc1 += opart[r * D + lane + 64] * w;
+    const float4 o = *reinterpret_cast<const float4*>(opart + r * D + 4 * c);
+    acc.x += o.x * w;
+    acc.y += o.y * w;
+    acc.z += o.z * w;
+    acc.w += o.w * w;
   }
   const float inv = Lsum > 0.f ? 1.0f / Lsum : 0.f;
-  T* o = out + ((static_cast<size_t>(b) * N + u) * Hq + hq) * D;
-  if (lane < D) store_f(o, lane, acc0 * inv);
-  if (lane + 64 < D) store_f(o, lane + 64, acc1 * inv);
-  if (lse && lane == 0) lse[(static_cast<size_t>(b) * N + u) * Hq + hq] = (Mu + log2f(Lsum)) * 0.69314718055994531f;
+  T* o = out + ((static_cast<size_t>(b) * N + u) * Hq + hq) * D + 4 * c;
+  store_f(o, 0, acc.x * inv);
+  store_f(o, 1, acc.y * inv);
+  store_f(o, 2, acc.z * inv);
+  store_f(o, 3, acc.w * inv);
+  if (lse && c == 0) lse[(static_cast<size_t>(b) * N + u) * Hq + hq] = (Mu + log2f(Lsum)) * 0.69314718055994531f;
 }
 
 // Generic path (float32, or D other than 128): one wave per (b, u, hq),
@@ -377,6 +415,8 @@ SplitPlan plan_splits(int B, int N, int Hq, int Hkv, int max_prefix_len) {
   if (s < 1) s = 1;
   int ls = (Lr + s - 1) / s;
   ls = (ls + kKT - 1) / kKT * kKT;
+  const int lcap = (kMaxSplitPages - 1) * 16;  // pages of a split must fit in LDS (page_size >= 16)
+  if (ls > lcap) ls = lcap / kKT * kKT;
   if (ls < kKT) ls = kKT;
   p.lsplit = ls;
   p.nsplit = Lr > 0 ? (Lr + ls - 1) / ls : 0;
@@ -423,6 +463,8 @@ extern "C" int tree_attention_verify(int dtype, int B, int N, int Hq, int Hkv, i
   HY_CHECK(q && k_tree && v_tree && block_table && prefix_len && anc && depth && out, HYDRA_ERR_INVALID,
            "tree_attention: null pointer");
   HY_CHECK(n_pages == 0 || (k_pages && v_pages), HYDRA_ERR_INVALID, "tree_attention: null page pool");
+  HY_CHECK(max_prefix_len == 0 || n_pages >= 1, HYDRA_ERR_INVALID,
+           "tree_attention: a prefix of %d tokens needs a page pool", max_prefix_len);
   const size_t need = tree_attention_verify_workspace_size(dtype, B, N, Hq, Hkv, D, max_prefix_len);
   HY_CHECK(ws_bytes >= need && (need == 0 || ws), HYDRA_ERR_WORKSPACE, "tree_attention: workspace %zu < %zu",
            ws_bytes, need);
@@ -460,8 +502,8 @@ extern "C" int tree_attention_verify(int dtype, int B, int N, int Hq, int Hkv, i
       n_pages, page_size, block_table, max_pages, prefix_len, anc, depth, Dmax, p.nsplit, p.lsplit, p.NQ, p.NQpad,
       opart, mpart, lpart);
   HY_LAUNCH_CHECK("tree_attention(split)");
-  const int crow = B * Hkv * p.NQ;
-  attn_combine<bf16_t><<<(crow + 3) / 4, 256, 0, stream>>>(B, N, Hq, Hkv, D, nparts, p.NQ, p.NQpad, opart, mpart,
+  const long long cthreads = static_cast<long long>(B) * Hkv * p.NQ * (D / 4);
+  attn_combine<bf16_t><<<static_cast<int>((cthreads + 255) / 256), 256, 0, stream>>>(B, N, Hq, Hkv, D, nparts, p.NQ, p.NQpad, opart, mpart,
                                                            lpart, static_cast<bf16_t*>(out), lse);
   HY_LAUNCH_CHECK("tree_attention(combine)");
   return HYDRA_OK;

@@ -55,6 +55,9 @@ struct Arena {
 typedef uint16_t bf16_t;
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+// 16-byte register vector; native vector types keep arrays of them in VGPRs
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
 
 __device__ __forceinline__ float bf16_to_f32(bf16_t v) {
   return __uint_as_float(static_cast<uint32_t>(v) << 16);
@@ -119,6 +122,106 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// ----------------------------------------------- DPP cross-lane reductions
+// DPP moves are VALU instructions, so a reduction over G lanes costs
+// log2(G) short dependent steps instead of LDS-routed shuffles. The patterns
+// below combine lanes within groups of 2, 4, 8 and 16 (quad swaps, then the
+// half-row and row mirrors); every lane of a group ends with the result.
+constexpr int kDppXor1 = 0xB1;         // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;         // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;  // lane j <-> 7 - j within 8
+constexpr int kDppMirror = 0x140;      // lane j <-> 15 - j within 16
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp32(uint32_t v) {
+  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(static_cast<int>(v), static_cast<int>(v), CTRL, 0xF,
+                                                           0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ float dppf(float v) {
+  return __uint_as_float(dpp32<CTRL>(__float_as_uint(v)));
+}
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp64(uint64_t v) {
+  const uint32_t lo = dpp32<CTRL>(static_cast<uint32_t>(v));
+  const uint32_t hi = dpp32<CTRL>(static_cast<uint32_t>(v >> 32));
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+// max of a key over aligned groups of G lanes (G in 1, 2, 4, 8, 16)
+template <int G>
+__device__ __forceinline__ uint64_t group_max_u64(uint64_t v) {
+  uint64_t o;
+  if constexpr (G >= 2) { o = dpp64<kDppXor1>(v); v = o > v ? o : v; }
+  if constexpr (G >= 4) { o = dpp64<kDppXor2>(v); v = o > v ? o : v; }
+  if constexpr (G >= 8) { o = dpp64<kDppHalfMirror>(v); v = o > v ? o : v; }
+  if constexpr (G >= 16) { o = dpp64<kDppMirror>(v); v = o > v ? o : v; }
+  return v;
+}
+
+// (max, sum exp(x - max)) pairs combined over aligned groups of G lanes
+__device__ __forceinline__ void ms_combine(float& m, float& s, float om, float os) {
+  const float nm = fmaxf(m, om);
+  s = (m == -INFINITY ? 0.f : s * expf(m - nm)) + (om == -INFINITY ? 0.f : os * expf(om - nm));
+  m = nm;
+}
+template <int G>
+__device__ __forceinline__ void group_ms(float& m, float& s) {
+  if constexpr (G >= 2) ms_combine(m, s, dppf<kDppXor1>(m), dppf<kDppXor1>(s));
+  if constexpr (G >= 4) ms_combine(m, s, dppf<kDppXor2>(m), dppf<kDppXor2>(s));
+  if constexpr (G >= 8) ms_combine(m, s, dppf<kDppHalfMirror>(m), dppf<kDppHalfMirror>(s));
+  if constexpr (G >= 16) ms_combine(m, s, dppf<kDppMirror>(m), dppf<kDppMirror>(s));
+}
+
+// (max, sum exp) over the whole wave, returned in every lane
+__device__ __forceinline__ void wave_ms(float& m, float& s) {
+  group_ms<16>(m, s);
+  float rm = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(m), 0));
+  float rs = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(s), 0));
+#pragma unroll
+  for (int row = 1; row < 4; ++row)
+    ms_combine(rm, rs, __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(m), row * 16)),
+               __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(s), row * 16)));
+  m = rm;
+  s = rs;
+}
+
+// max of a key over the whole wave, returned in every lane
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+  v = group_max_u64<16>(v);
+  uint64_t r = v;
+#pragma unroll
+  for (int row = 1; row < 4; ++row) {
+    const uint32_t lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(v), row * 16);
+    const uint32_t hi = __builtin_amdgcn_readlane(static_cast<uint32_t>(v >> 32), row * 16);
+    const uint64_t o = (static_cast<uint64_t>(hi) << 32) | lo;
+    r = o > r ? o : r;
+  }
+  const uint32_t lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(r), 0);
+  const uint32_t hi = __builtin_amdgcn_readlane(static_cast<uint32_t>(r >> 32), 0);
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+// Insert key x into a descending list of length K held in registers.
+template <int K>
+__device__ __forceinline__ void list_insert(uint64_t (&l)[K], uint64_t x) {
+  if (x <= l[K - 1]) return;
+#pragma unroll
+  for (int j = K - 1; j > 0; --j) {
+    const uint64_t prev = l[j - 1];
+    l[j] = prev < x ? prev : (l[j] < x ? x : l[j]);
+  }
+  l[0] = l[0] < x ? x : l[0];
+}
+
+// Drop the head of a descending register list.
+template <int K>
+__device__ __forceinline__ void list_pop(uint64_t (&l)[K]) {
+#pragma unroll
+  for (int j = 0; j < K - 1; ++j) l[j] = l[j + 1];
+  l[K - 1] = 0;
+}
+
 // ------------------------------------------------------- shared kernels
 
 // Y[M, N] (float32) = X[M, K] . W[N, K]^T for the two dtypes; out row of
@@ -141,8 +244,59 @@ struct XSource {
   int mode;
 };
 
-int launch_projection(int dtype, int M, int K, int N, XSource xs, const void* W,
-                      float* Y, RowMap map, int ldy, int nsplit, float* part,
+// Optional fused row reduction of a projection: for every row and every
+// workgroup along N, the top-k keys of that workgroup's columns (sorted,
+// topk_key order) and (max, sum exp(z - max)) over them. k = 0 disables it.
+struct TopkPartials {
+  uint64_t* keys;  // [M][nwg][k]
+  float2* ms;      // [M][nwg]
+  int k;
+};
+
+constexpr int kProjRowsPerWG = 64;
+__host__ __device__ inline int projection_nwg(int N) { return (N + kProjRowsPerWG - 1) / kProjRowsPerWG; }
+
+int launch_projection(int dtype, int M, int K, int N, XSource xs, const void* W, float* Y,
+                      RowMap map, int ldy, int nsplit, float* part, TopkPartials tp,
                       hipStream_t stream);
+
+// Finish the fused row reduction: log-sum-exp and sorted top-k of each row,
+// then either the candidate-tree fill (draft heads) or the arg max.
+struct MergeArgs {
+  int M, nwg, k;
+  const uint64_t* keys;
+  const float2* ms;
+  RowMap map;           // launch row -> output row (for head_lse)
+  float* lse;           // [out rows] or nullptr
+  int32_t* amax;        // [M] arg max (k = 1) or nullptr
+  int32_t* topk_ids;    // [M][k] or nullptr
+  float* topk_vals;     // [M][k] or nullptr
+  // tree fill (draft heads); node_hi <= node_lo disables it
+  int P, r0, N, node_lo, node_hi;
+  const int32_t* node_parent;
+  const int32_t* node_rank;
+  const int32_t* node_row;
+  const int32_t* root_tok;
+  int32_t* cand_tok;
+  float* cand_logp;
+};
+int launch_topk_merge(const MergeArgs& a, hipStream_t stream);
+
+// Fused feed-forward layer of the draft heads for few rows (bf16):
+// U[m] = h[m / P] + SiLU(W1 x_m + b1) rounded to bf16 (or SiLU(...) without
+// the residual), also written to hidden[map(m)] when hidden is set.
+struct MlpArgs {
+  int M, K, d;
+  XSource xs;
+  const bf16_t* W1;
+  const bf16_t* b1;
+  const bf16_t* h;
+  int P, residual;
+  bf16_t* U;
+  bf16_t* hidden;
+  RowMap map;
+};
+bool mlp_fused_supported(int dtype, int M, int K, int d);
+int launch_mlp_fused(const MlpArgs& a, hipStream_t stream);
 
 }  // namespace hydra

@@ -11,8 +11,9 @@
 //   1. projection W1 over the gathered rows [h_b || E[token]] (split-K),
 //   2. epilogue: sum of the splits + b1, SiLU, residual, rounded to dtype,
 //   3. projection W2 -> head logits,
-//   4. one workgroup per head row: log-sum-exp, top-k, and the tree fill of
-//      every child that takes its token from that row.
+//   4. the W2 epilogue leaves per-workgroup top-k and (max, sum exp) partials;
+//      one workgroup per head row merges them into log-sum-exp and top-k and
+//      fills every child that takes its token from that row.
 #include "common.h"
 
 namespace hydra {
@@ -39,143 +40,6 @@ __global__ __launch_bounds__(256) void head_mlp_epilogue(int M, int d, int nspli
   }
 }
 
-// Insert key x into a descending list of length K held in registers.
-template <int K>
-__device__ __forceinline__ void list_insert(uint64_t (&l)[K], uint64_t x) {
-  if (x <= l[K - 1]) return;
-#pragma unroll
-  for (int j = K - 1; j > 0; --j) {
-    const uint64_t prev = l[j - 1];
-    l[j] = prev < x ? prev : (l[j] < x ? x : l[j]);
-  }
-  l[0] = l[0] < x ? x : l[0];
-}
-
-constexpr int kRowThreads = 512;
-constexpr int kRowWaves = kRowThreads / 64;
-
-// One workgroup per head row (b, r): log-sum-exp, sorted top-k (logit
-// descending, lower id first), then the tree fill.
-template <int KMAX>
-__global__ __launch_bounds__(kRowThreads) void row_topk_fill(
-    int V, int R, int P, int r0, int k, const float* __restrict__ logits,
-    float* __restrict__ head_lse, int N, int node_lo, int node_hi,
-    const int32_t* __restrict__ node_parent, const int32_t* __restrict__ node_rank,
-    const int32_t* __restrict__ node_row, const int32_t* __restrict__ root_tok,
-    int32_t* __restrict__ cand_tok, float* __restrict__ cand_logp) {
-  __shared__ uint64_t wtop[kRowWaves][KMAX];
-  __shared__ float wm[kRowWaves], ws[kRowWaves];
-  __shared__ uint64_t top[KMAX];
-  __shared__ float s_lse;
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int b = blockIdx.x / P;
-  const int r = r0 + blockIdx.x % P;
-  const float* z = logits + (static_cast<size_t>(b) * R + r) * V;
-
-  uint64_t l[KMAX];
-#pragma unroll
-  for (int j = 0; j < KMAX; ++j) l[j] = 0;
-  float m = -INFINITY, s = 0.f;
-  auto consume = [&](float v, int id) {
-    if (v > m) {
-      s = s * expf(m - v) + 1.0f;
-      m = v;
-    } else {
-      s += expf(v - m);
-    }
-    list_insert<KMAX>(l, topk_key(v, id));
-  };
-  if ((V & 3) == 0) {
-    const float4* z4 = reinterpret_cast<const float4*>(z);
-    for (int i = tid; i < V / 4; i += kRowThreads) {
-      const float4 q = z4[i];
-      consume(q.x, 4 * i);
-      consume(q.y, 4 * i + 1);
-      consume(q.z, 4 * i + 2);
-      consume(q.w, 4 * i + 3);
-    }
-  } else {
-    for (int i = tid; i < V; i += kRowThreads) consume(z[i], i);
-  }
-
-  // (max, sum) across the wave, then across waves
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    const float om = __shfl_xor(m, off, 64);
-    const float os = __shfl_xor(s, off, 64);
-    const float nm = fmaxf(m, om);
-    s = (m == -INFINITY ? 0.f : s * expf(m - nm)) + (om == -INFINITY ? 0.f : os * expf(om - nm));
-    m = nm;
-  }
-  // wave top-k: k rounds of a wave-wide max over the list heads
-  for (int j = 0; j < k; ++j) {
-    uint64_t best = l[0];
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const uint64_t o = shfl_xor_u64(best, off);
-      best = o > best ? o : best;
-    }
-    if (l[0] == best && best != 0) {
-#pragma unroll
-      for (int q = 0; q < KMAX - 1; ++q) l[q] = l[q + 1];
-      l[KMAX - 1] = 0;
-    }
-    if (lane == 0) wtop[wave][j] = best;
-  }
-  if (lane == 0) {
-    wm[wave] = m;
-    ws[wave] = s;
-  }
-  __syncthreads();
-  if (wave == 0) {
-    // merge the per-wave sorted lists: lane w < kRowWaves walks list w
-    int ptr = 0;
-    for (int j = 0; j < k; ++j) {
-      uint64_t cand = (lane < kRowWaves && ptr < k) ? wtop[lane][ptr] : 0;
-      uint64_t best = cand;
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) {
-        const uint64_t o = shfl_xor_u64(best, off);
-        best = o > best ? o : best;
-      }
-      if (lane < kRowWaves && cand == best && best != 0) ++ptr;
-      if (lane == 0) top[j] = best;
-    }
-    if (lane == 0) {
-      float M = -INFINITY;
-      for (int w = 0; w < kRowWaves; ++w) M = fmaxf(M, wm[w]);
-      float S = 0.f;
-      for (int w = 0; w < kRowWaves; ++w)
-        if (wm[w] != -INFINITY) S += ws[w] * expf(wm[w] - M);
-      s_lse = M + logf(S);
-      head_lse[static_cast<size_t>(b) * R + r] = s_lse;
-    }
-  }
-  __syncthreads();
-  const float lse = s_lse;
-  if (blockIdx.x % P == 0 && r == 0 && tid == 0) {
-    cand_tok[static_cast<size_t>(b) * N] = root_tok[b];
-    cand_logp[static_cast<size_t>(b) * N] = 0.f;
-  }
-  // children whose parent is expanded by this row take entry rank of the list
-  for (int c = node_lo + tid; c < node_hi; c += kRowThreads) {
-    const int p = node_parent[c];
-    if (p < 0 || node_row[p] != r) continue;
-    const int rk = node_rank[c];
-    if (rk < 0 || rk >= k) continue;
-    const uint64_t key = top[rk];
-    const float plogp = p == 0 ? 0.f : cand_logp[static_cast<size_t>(b) * N + p];
-    cand_tok[static_cast<size_t>(b) * N + c] = key_id(key);
-    cand_logp[static_cast<size_t>(b) * N + c] = plogp + (key_value(key) - lse);
-  }
-}
-
-struct DraftPlan {
-  int max_rows;  // max over depths of B * rows-of-depth
-  int nsplit;
-};
-
 int w1_splits(int dtype, int in_dim, int d) {
   if (dtype == HYDRA_F32) return 1;
   // enough workgroups for 256 CUs: d / 64 row tiles times the splits
@@ -189,23 +53,36 @@ int w1_splits(int dtype, int in_dim, int d) {
 
 using namespace hydra;
 
-extern "C" size_t hydra_draft_heads_workspace_size(int dtype, int B, int d, int V, int hydra_mode,
-                                                   int Dmax, const int32_t* row_first) {
-  (void)V;
-  if (B <= 0 || d <= 0 || Dmax <= 0 || Dmax > HYDRA_MAX_DEPTH || !row_first) return 0;
-  int maxP = 0;
+namespace {
+struct DraftWs {
+  size_t part, u, keys, ms, total;
+};
+DraftWs draft_ws(int dtype, int B, int d, int V, int hydra_mode, int Dmax, const int32_t* row_first,
+                 const int32_t* k_per_depth) {
+  int maxP = 0, maxk = 1;
   for (int k = 1; k <= Dmax; ++k) {
-    const int P = row_first[k] - row_first[k - 1];
-    maxP = P > maxP ? P : maxP;
+    maxP = std::max(maxP, row_first[k] - row_first[k - 1]);
+    if (k_per_depth) maxk = std::max(maxk, static_cast<int>(k_per_depth[k - 1]));
   }
+  if (!k_per_depth) maxk = HYDRA_MAX_TOPK;
   const size_t M = static_cast<size_t>(B) * maxP;
   const int in_dim = hydra_mode ? 2 * d : d;
-  const int ns = w1_splits(dtype, in_dim, d);
   const size_t esz = dtype == HYDRA_F32 ? 4 : 2;
-  size_t bytes = 0;
-  bytes += align_up(ns * M * d * sizeof(float), 256);  // W1 partials
-  bytes += align_up(M * d * esz, 256);                   // u
-  return bytes + 256;
+  const size_t nwg = projection_nwg(V);
+  DraftWs w;
+  w.part = align_up(w1_splits(dtype, in_dim, d) * M * d * sizeof(float), 256);
+  w.u = align_up(M * d * esz, 256);
+  w.keys = align_up(M * nwg * maxk * sizeof(uint64_t), 256);
+  w.ms = align_up(M * nwg * sizeof(float2), 256);
+  w.total = w.part + w.u + w.keys + w.ms + 256;
+  return w;
+}
+}  // namespace
+
+extern "C" size_t hydra_draft_heads_workspace_size(int dtype, int B, int d, int V, int hydra_mode,
+                                                   int Dmax, const int32_t* row_first) {
+  if (B <= 0 || d <= 0 || V <= 0 || Dmax <= 0 || Dmax > HYDRA_MAX_DEPTH || !row_first) return 0;
+  return draft_ws(dtype, B, d, V, hydra_mode, Dmax, row_first, nullptr).total;
 }
 
 extern "C" int hydra_draft_heads(int dtype, int B, int d, int V, int hydra_mode, int residual,
@@ -247,15 +124,21 @@ extern "C" int hydra_draft_heads(int dtype, int B, int d, int V, int hydra_mode,
   HY_CHECK(ws_bytes >= need && (need == 0 || ws), HYDRA_ERR_WORKSPACE,
            "draft_heads: workspace %zu < required %zu", ws_bytes, need);
 
-  int maxP = 0;
-  for (int k = 1; k <= Dmax; ++k) maxP = std::max(maxP, row_first[k] - row_first[k - 1]);
+  int maxP = 0, maxk = 1;
+  for (int k = 1; k <= Dmax; ++k) {
+    maxP = std::max(maxP, row_first[k] - row_first[k - 1]);
+    maxk = std::max(maxk, static_cast<int>(k_per_depth[k - 1]));
+  }
   const size_t Mmax = static_cast<size_t>(B) * maxP;
   const int in_dim = hydra_mode ? 2 * d : d;
   const int ns = w1_splits(dtype, in_dim, d);
   const size_t esz = dtype == HYDRA_F32 ? 4 : 2;
+  const int nwg = projection_nwg(V);
   Arena arena(ws, ws_bytes);
   float* part = arena.take<float>(ns * Mmax * d);
   char* U = arena.take<char>(Mmax * d * esz);
+  uint64_t* tkeys = arena.take<uint64_t>(Mmax * nwg * maxk);
+  float2* tms = arena.take<float2>(Mmax * nwg);
 
   for (int k = 1; k <= Dmax; ++k) {
     const int P = row_first[k] - row_first[k - 1];
@@ -281,11 +164,22 @@ extern "C" int hydra_draft_heads(int dtype, int B, int d, int V, int hydra_mode,
       xs.mode = 0;
     }
     const int nsk = ns;
-    int rc = launch_projection(dtype, M, in_dim, d, xs, W1[k - 1], dtype == HYDRA_F32 ? part : nullptr,
-                               RowMap{M, 0, 0}, d, nsk, dtype == HYDRA_F32 ? nullptr : part, stream);
-    if (rc != HYDRA_OK) return rc;
+    int rc;
+    if (mlp_fused_supported(dtype, M, in_dim, d)) {
+      // 1+2 in one kernel: few rows, the waves of a workgroup split K
+      MlpArgs ma{M, in_dim, d, xs, static_cast<const bf16_t*>(W1[k - 1]), static_cast<const bf16_t*>(b1[k - 1]),
+                 static_cast<const bf16_t*>(h), P, residual, reinterpret_cast<bf16_t*>(U),
+                 static_cast<bf16_t*>(head_hidden), map};
+      rc = launch_mlp_fused(ma, stream);
+      if (rc != HYDRA_OK) return rc;
+    } else {
+      rc = launch_projection(dtype, M, in_dim, d, xs, W1[k - 1], dtype == HYDRA_F32 ? part : nullptr,
+                             RowMap{M, 0, 0}, d, nsk, dtype == HYDRA_F32 ? nullptr : part,
+                             TopkPartials{nullptr, nullptr, 0}, stream);
+      if (rc != HYDRA_OK) return rc;
+    }
     // 2. epilogue: u = h + SiLU(sum + b1)
-    {
+    if (!mlp_fused_supported(dtype, M, in_dim, d)) {
       const size_t total = static_cast<size_t>(M) * d;
       const int grid = static_cast<int>(std::min<size_t>((total + 255) / 256, 4096));
       const int nsum = dtype == HYDRA_F32 ? 1 : nsk;
@@ -305,19 +199,33 @@ extern "C" int hydra_draft_heads(int dtype, int B, int d, int V, int hydra_mode,
     xu.x = U;
     xu.ldx = d;
     xu.mode = 0;
-    rc = launch_projection(dtype, M, d, V, xu, W2[k - 1], head_logits, map, V, 1, nullptr, stream);
+    const int kk = k_per_depth[k - 1];
+    rc = launch_projection(dtype, M, d, V, xu, W2[k - 1], head_logits, map, V, 1, nullptr,
+                           TopkPartials{tkeys, tms, kk}, stream);
     if (rc != HYDRA_OK) return rc;
     // 4. log-sum-exp, top-k, tree fill
-    const int kk = k_per_depth[k - 1];
-    const int lo = depth_first[k], hi = depth_first[k + 1];
-#define HY_ROW(KM)                                                                                   \
-  row_topk_fill<KM><<<M, kRowThreads, 0, stream>>>(V, R, P, r0, kk, head_logits, head_lse, N, lo, hi, \
-                                                   node_parent, node_rank, node_row, root_tok,       \
-                                                   cand_tok, cand_logp)
-    if (kk <= 4) HY_ROW(4);
-    else HY_ROW(16);
-#undef HY_ROW
-    HY_LAUNCH_CHECK("draft_heads: top-k");
+    MergeArgs ma{};
+    ma.M = M;
+    ma.nwg = nwg;
+    ma.k = kk;
+    ma.keys = tkeys;
+    ma.ms = tms;
+    ma.map = map;
+    ma.lse = head_lse;
+    ma.amax = nullptr;
+    ma.P = P;
+    ma.r0 = r0;
+    ma.N = N;
+    ma.node_lo = depth_first[k];
+    ma.node_hi = depth_first[k + 1];
+    ma.node_parent = node_parent;
+    ma.node_rank = node_rank;
+    ma.node_row = node_row;
+    ma.root_tok = root_tok;
+    ma.cand_tok = cand_tok;
+    ma.cand_logp = cand_logp;
+    rc = launch_topk_merge(ma, stream);
+    if (rc != HYDRA_OK) return rc;
   }
   return HYDRA_OK;
 }

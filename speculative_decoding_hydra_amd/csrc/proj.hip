@@ -8,121 +8,135 @@
 // At decode shapes M (tree rows) is 1..256 while W is 67-524 MB, so the kernel
 // is bound by streaming W from HBM. Design for gfx950:
 //   * each wave owns 16 rows of W and streams them with 16-byte loads straight
-//     into registers (the MFMA A operand), one K-chunk ahead of use;
+//     into registers (the MFMA A operand), PF K-chunks ahead of use, so every
+//     wave keeps 16 KB of W in flight;
 //   * the matching chunk of X (all M rows, padded to 16 * MT) is staged once
 //     per workgroup in LDS and read as the B operand;
 //   * v_mfma_f32_16x16x32_bf16 does the contraction with float32 accumulation;
-//   * split-K over grid.y gives enough workgroups when N is small (W1: N = d).
+//   * split-K over grid.y gives enough workgroups when N is small (W1: N = d);
+//   * optional fused epilogue: per row and workgroup, the top-k of the
+//     workgroup's 64 columns and (max, sum exp) over them, so the vocabulary
+//     reductions need no second pass over the logits.
 #include "common.h"
 
 namespace hydra {
 
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kRowsPerWG = 16 * kWaves;
-
-struct RowPtrs {
-  const bf16_t* p0;  // segment for k < K0
-  const bf16_t* p1;  // segment for k >= K0 (pre-offset by -K0)
+struct ProjArgs {
+  int M, K, N;
+  XSource xs;
+  const bf16_t* W;
+  float* Y;
+  RowMap map;
+  int ldy, kper, m_base;
+  float* part;
+  TopkPartials tp;
 };
 
-template <int MT, int KC, bool SPLIT>
-__global__ __launch_bounds__(256) void proj_bf16_kernel(int M, int K, int N, XSource xs,
-                                                        const bf16_t* __restrict__ W,
-                                                        float* __restrict__ Y, RowMap map,
-                                                        int ldy, int kper, int m_base,
-                                                        float* __restrict__ part) {
+template <int MT, int KC, int PF, int WV, bool SPLIT, bool TOPK, int KCAP = HYDRA_MAX_TOPK>
+__global__ __launch_bounds__(64 * WV) void proj_bf16_kernel(ProjArgs a) {
+  constexpr int NT = 64 * WV;      // threads
+  constexpr int RPW = 16 * WV;     // rows of W per workgroup (one 16-row tile per wave)
   constexpr int MP = MT * 16;
   constexpr int LDS_ROW = KC + 8;  // 16-byte pad: rows land on different banks
   constexpr int STEPS = KC / 32;
   constexpr int VPR = KC / 8;      // 16-byte vectors per LDS row
-  constexpr int XV = (MP * VPR + 255) / 256;
-  __shared__ __align__(16) bf16_t xlds[MP * LDS_ROW];
-  __shared__ RowPtrs rows[MP];
+  constexpr int XV = MP * VPR / NT;
+  constexpr int TROW = RPW + 1;    // epilogue tile row (floats)
+  constexpr int XLDS = (TOPK && TROW * 2 > LDS_ROW) ? MP * TROW * 2 : MP * LDS_ROW;  // bf16 elements
+  static_assert(RPW % kProjRowsPerWG == 0, "partials come in 64-column blocks");
+  __shared__ __align__(16) bf16_t xlds[XLDS];
 
+  const XSource& xs = a.xs;
+  const int M = a.M, K = a.K, N = a.N, m_base = a.m_base;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int n_base = blockIdx.x * kRowsPerWG + wave * 16;
-  const int k_begin = blockIdx.y * kper;
-  const int k_end = k_begin + kper;
+  const int n_base = blockIdx.x * RPW + wave * 16;
+  const int k_begin = blockIdx.y * a.kper;
+  const int k_end = k_begin + a.kper;
   const int K0 = xs.mode == 0 ? K : xs.d;
 
-  if (tid < MP) {
-    const int m = m_base + tid;
-    RowPtrs rp{nullptr, nullptr};
-    if (m < M) {
-      if (xs.mode == 0) {
-        rp.p0 = static_cast<const bf16_t*>(xs.x) + static_cast<size_t>(m) * xs.ldx;
-        rp.p1 = rp.p0;
-      } else {
-        const int b = m / xs.P;
-        const int node = xs.row_node[xs.r0 + m % xs.P];
-        int t = node == 0 ? xs.root_tok[b] : xs.tok[static_cast<size_t>(b) * xs.ntree + node];
-        t = t < 0 ? 0 : (t >= xs.V ? xs.V - 1 : t);
-        rp.p0 = static_cast<const bf16_t*>(xs.x) + static_cast<size_t>(b) * xs.d;
-        rp.p1 = static_cast<const bf16_t*>(xs.emb) + static_cast<size_t>(t) * xs.d - xs.d;
-      }
-    }
-    rows[tid] = rp;
-  }
-  __syncthreads();
-
+  static_assert((MP * VPR) % NT == 0, "X chunk splits evenly over the workgroup");
   const int wrow = min(n_base + (lane & 15), N - 1);
-  const bf16_t* wp = W + static_cast<size_t>(wrow) * K + (lane >> 4) * 8;
+  const bf16_t* wp = a.W + static_cast<size_t>(wrow) * K + (lane >> 4) * 8;
 
   f32x4_t acc[MT];
 #pragma unroll
   for (int t = 0; t < MT; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  uint4 wbuf[STEPS];
-  uint4 xbuf[XV];
-
-  auto load_x = [&](int kc) {
+  u32x4_t wbuf[PF][STEPS];
+  u32x4_t xbuf[XV];
+  // This thread's X rows, fixed for the whole K range. Pointers come straight
+  // from the kernel arguments (global address space); rows past M read row 0,
+  // whose outputs are never stored, so every load below is unconditional.
+  const bf16_t* xp0[XV];
+  const bf16_t* xp1[XV];
+  int xo[XV];
 #pragma unroll
-    for (int v = 0; v < XV; ++v) {
-      const int idx = tid + v * 256;
-      const int r = idx / VPR;
-      const int c = (idx % VPR) * 8;
-      uint4 val = make_uint4(0, 0, 0, 0);
-      if (r < MP && m_base + r < M) {
-        const bf16_t* base = kc < K0 ? rows[r].p0 : rows[r].p1;
-        val = *reinterpret_cast<const uint4*>(base + kc + c);
-      }
-      xbuf[v] = val;
+  for (int v = 0; v < XV; ++v) {
+    const int idx = tid + v * NT;
+    const int r = idx / VPR;
+    const int c = (idx % VPR) * 8;
+    xo[v] = r * LDS_ROW + c;
+    const int m = m_base + r < M ? m_base + r : 0;
+    if (xs.mode == 0) {
+      xp0[v] = static_cast<const bf16_t*>(xs.x) + static_cast<size_t>(m) * xs.ldx + c;
+      xp1[v] = xp0[v];
+    } else {
+      const int b = m / xs.P;
+      const int node = xs.row_node[xs.r0 + m % xs.P];
+      int t = node == 0 ? xs.root_tok[b] : xs.tok[static_cast<size_t>(b) * xs.ntree + node];
+      t = t < 0 ? 0 : (t >= xs.V ? xs.V - 1 : t);
+      xp0[v] = static_cast<const bf16_t*>(xs.x) + static_cast<size_t>(b) * xs.d + c;
+      xp1[v] = static_cast<const bf16_t*>(xs.emb) + static_cast<size_t>(t) * xs.d - xs.d + c;
     }
-  };
-  auto store_x = [&]() {
-#pragma unroll
-    for (int v = 0; v < XV; ++v) {
-      const int idx = tid + v * 256;
-      const int r = idx / VPR;
-      const int c = (idx % VPR) * 8;
-      if (r < MP) *reinterpret_cast<uint4*>(&xlds[r * LDS_ROW + c]) = xbuf[v];
-    }
-  };
+  }
 
-  load_x(k_begin);
+  // prologue: PF chunks of W in flight, the first X chunk in registers
+  // (the launcher guarantees PF * KC divides the K range of the workgroup)
 #pragma unroll
-  for (int s = 0; s < STEPS; ++s) wbuf[s] = *reinterpret_cast<const uint4*>(wp + k_begin + s * 32);
+  for (int p = 0; p < PF; ++p)
+#pragma unroll
+    for (int s = 0; s < STEPS; ++s)
+      wbuf[p][s] = *reinterpret_cast<const u32x4_t*>(wp + k_begin + p * KC + s * 32);
+#pragma unroll
+  for (int v = 0; v < XV; ++v)
+    xbuf[v] = *reinterpret_cast<const u32x4_t*>((k_begin < K0 ? xp0[v] : xp1[v]) + k_begin);
 
-  for (int kc = k_begin; kc < k_end; kc += KC) {
-    __syncthreads();
-    store_x();
-    __syncthreads();
-    const int kn = kc + KC;
-    const bool more = kn < k_end;
-    if (more) load_x(kn);
+  const int k_last = k_end - KC;  // past-the-end prefetches re-read the last chunk
+  for (int kc0 = k_begin; kc0 < k_end; kc0 += PF * KC) {
 #pragma unroll
-    for (int s = 0; s < STEPS; ++s) {
-      const bf16x8_t a = __builtin_bit_cast(bf16x8_t, wbuf[s]);
-      if (more) wbuf[s] = *reinterpret_cast<const uint4*>(wp + kn + s * 32);
+    for (int p = 0; p < PF; ++p) {
+      const int kc = kc0 + p * KC;
+      __syncthreads();
 #pragma unroll
-      for (int t = 0; t < MT; ++t) {
-        const uint4 bv = *reinterpret_cast<const uint4*>(
-            &xlds[(t * 16 + (lane & 15)) * LDS_ROW + s * 32 + (lane >> 4) * 8]);
-        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8_t, bv),
-                                                        acc[t], 0, 0, 0);
+      for (int v = 0; v < XV; ++v) *reinterpret_cast<u32x4_t*>(&xlds[xo[v]]) = xbuf[v];
+      __syncthreads();
+      const int kx = kc < k_last ? kc + KC : kc;
+#pragma unroll
+      for (int v = 0; v < XV; ++v)
+        xbuf[v] = *reinterpret_cast<const u32x4_t*>((kx < K0 ? xp0[v] : xp1[v]) + kx);
+      const int kn = kc + PF * KC <= k_last ? kc + PF * KC : k_last;
+      // B operands double-buffered: step s + 1's LDS reads are in flight
+      // while step s's MFMAs run
+      const bf16_t* xrow = &xlds[(lane & 15) * LDS_ROW + (lane >> 4) * 8];
+      u32x4_t bq[2][MT];
+#pragma unroll
+      for (int t = 0; t < MT; ++t) bq[0][t] = *reinterpret_cast<const u32x4_t*>(xrow + t * 16 * LDS_ROW);
+#pragma unroll
+      for (int s = 0; s < STEPS; ++s) {
+        if (s + 1 < STEPS) {
+#pragma unroll
+          for (int t = 0; t < MT; ++t)
+            bq[(s + 1) & 1][t] = *reinterpret_cast<const u32x4_t*>(xrow + t * 16 * LDS_ROW + (s + 1) * 32);
+        }
+        const bf16x8_t av = __builtin_bit_cast(bf16x8_t, wbuf[p][s]);
+        wbuf[p][s] = *reinterpret_cast<const u32x4_t*>(wp + kn + s * 32);
+#pragma unroll
+        for (int t = 0; t < MT; ++t)
+          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8_t, bq[s & 1][t]), acc[t],
+                                                          0, 0, 0);
       }
     }
   }
@@ -135,16 +149,67 @@ __global__ __launch_bounds__(256) void proj_bf16_kernel(int M, int K, int N, XSo
     if (m >= M) continue;
     float* dst;
     if constexpr (SPLIT) {
-      dst = part + (static_cast<size_t>(blockIdx.y) * M + m) * N;
+      dst = a.part + (static_cast<size_t>(blockIdx.y) * M + m) * N;
     } else {
-      dst = Y + static_cast<size_t>(map(m)) * ldy;
+      dst = a.Y + static_cast<size_t>(a.map(m)) * a.ldy;
     }
-    if (n0 + 3 < N && (N & 3) == 0 && (SPLIT || (ldy & 3) == 0)) {
+    if (n0 + 3 < N && (N & 3) == 0 && (SPLIT || (a.ldy & 3) == 0)) {
       *reinterpret_cast<float4*>(dst + n0) = make_float4(acc[t][0], acc[t][1], acc[t][2], acc[t][3]);
     } else {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         if (n0 + i < N) dst[n0 + i] = acc[t][i];
+    }
+  }
+
+  if constexpr (TOPK) {
+    // the workgroup's [MP x RPW] tile through LDS; every 64-column block gets
+    // its own partial slot, handled by 256 threads (TPR per row)
+    constexpr int TPR = 256 / MP;
+    constexpr int VPT = kProjRowsPerWG / TPR;
+    float* tile = reinterpret_cast<float*>(xlds);
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int nl = wave * 16 + (lane >> 4) * 4 + i;
+        tile[(t * 16 + (lane & 15)) * TROW + nl] =
+            static_cast<int>(blockIdx.x) * RPW + nl < N ? acc[t][i] : -INFINITY;
+      }
+    __syncthreads();
+    const int blk = tid / 256;  // 64-column block of this thread
+    const int t2 = tid % 256;
+    const int mloc = t2 / TPR, sub = t2 % TPR;
+    const int m = m_base + mloc;
+    const int col0 = static_cast<int>(blockIdx.x) * RPW + blk * kProjRowsPerWG;
+    // a thread holds VPT values, so its list never needs more than VPT entries;
+    // rows past M skip the work (a row's TPR threads share one wave)
+    constexpr int KL = VPT < KCAP ? VPT : KCAP;
+    if (m < M && col0 < N) {
+      uint64_t l[KL];
+#pragma unroll
+      for (int j = 0; j < KL; ++j) l[j] = 0;
+      float mx = -INFINITY;
+#pragma unroll
+      for (int j = 0; j < VPT; ++j) mx = fmaxf(mx, tile[mloc * TROW + blk * kProjRowsPerWG + sub + j * TPR]);
+      float s = 0.f;
+#pragma unroll
+      for (int j = 0; j < VPT; ++j) {
+        const int nl = blk * kProjRowsPerWG + sub + j * TPR;
+        const float v = tile[mloc * TROW + nl];
+        if (v != -INFINITY) s += expf(v - mx);
+        list_insert<KL>(l, topk_key(v, static_cast<int>(blockIdx.x) * RPW + nl));
+      }
+      // combine the TPR threads of the row (an aligned lane group of one wave)
+      group_ms<TPR>(mx, s);
+      const size_t slot = static_cast<size_t>(m) * projection_nwg(N) + col0 / kProjRowsPerWG;
+      for (int j = 0; j < a.tp.k; ++j) {
+        const uint64_t best = group_max_u64<TPR>(l[0]);
+        if (l[0] == best) list_pop<KL>(l);
+        if (sub == 0) a.tp.keys[slot * a.tp.k + j] = best;
+      }
+      if (sub == 0) a.tp.ms[slot] = make_float2(mx, s);
     }
   }
 }
@@ -181,53 +246,109 @@ __global__ __launch_bounds__(256) void proj_f32_kernel(int M, int K, int N, XSou
   }
 }
 
-template <int MT>
-int launch_bf16(int M, int K, int N, XSource xs, const void* W, float* Y, RowMap map, int ldy,
-                int nsplit, float* part, int m_base, hipStream_t stream) {
+// Row-reduction partials of finished float32 logits, in the same layout the
+// fused epilogue writes: one wave per (row, 64-column slice).
+__global__ __launch_bounds__(64) void logits_partials(int M, int N, const float* __restrict__ Y, RowMap map,
+                                                      int ldy, TopkPartials tp) {
+  const int m = blockIdx.y, w = blockIdx.x, lane = threadIdx.x;
+  const int n = w * kProjRowsPerWG + lane;
+  const float v = n < N ? Y[static_cast<size_t>(map(m)) * ldy + n] : -INFINITY;
+  const float mx = wave_max(v);
+  const float s = wave_sum(v == -INFINITY ? 0.f : expf(v - mx));
+  uint64_t key = topk_key(v, n);
+  const size_t slot = static_cast<size_t>(m) * gridDim.x + w;
+  for (int j = 0; j < tp.k; ++j) {
+    uint64_t best = key;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const uint64_t o = shfl_xor_u64(best, off);
+      best = o > best ? o : best;
+    }
+    if (key == best) key = 0;
+    if (lane == 0) tp.keys[slot * tp.k + j] = best;
+  }
+  if (lane == 0) tp.ms[slot] = make_float2(mx, s);
+}
+
+template <int MT, int PF, bool TOPK>
+void launch_bf16_pf(const ProjArgs& a, int nsplit, hipStream_t stream) {
   constexpr int KC = MT <= 4 ? 256 : (MT <= 8 ? 128 : 64);
-  const int kper = K / nsplit;
-  dim3 grid((N + kRowsPerWG - 1) / kRowsPerWG, nsplit);
-  // split-K launches (partials) and direct launches are separate instances
-  if (part) {
-    proj_bf16_kernel<MT, KC, true><<<grid, 256, 0, stream>>>(
-        M, K, N, xs, static_cast<const bf16_t*>(W), Y, map, ldy, kper, m_base, part);
+  // split-K launches (partials) and direct launches are separate instances;
+  // with 4+ row tiles, 8-wave workgroups share each staged X chunk twice as far
+  if (a.part) {
+    dim3 grid((a.N + 63) / 64, nsplit);
+    proj_bf16_kernel<MT, KC, PF, 4, true, false><<<grid, 256, 0, stream>>>(a);
+  } else if constexpr (MT >= 4) {
+    dim3 grid((a.N + 127) / 128, 1);
+    if (TOPK && a.tp.k == 1)  // arg max: a one-entry list per thread
+      proj_bf16_kernel<MT, KC, PF, 8, false, TOPK, 1><<<grid, 512, 0, stream>>>(a);
+    else
+      proj_bf16_kernel<MT, KC, PF, 8, false, TOPK><<<grid, 512, 0, stream>>>(a);
   } else {
-    proj_bf16_kernel<MT, KC, false><<<grid, 256, 0, stream>>>(
-        M, K, N, xs, static_cast<const bf16_t*>(W), Y, map, ldy, kper, m_base, part);
+    dim3 grid((a.N + 63) / 64, 1);
+    if (TOPK && a.tp.k == 1)
+      proj_bf16_kernel<MT, KC, PF, 4, false, TOPK, 1><<<grid, 256, 0, stream>>>(a);
+    else
+      proj_bf16_kernel<MT, KC, PF, 4, false, TOPK><<<grid, 256, 0, stream>>>(a);
+  }
+}
+
+template <int MT, bool TOPK>
+int launch_bf16(const ProjArgs& a, int nsplit, hipStream_t stream) {
+  constexpr int KC = MT <= 4 ? 256 : (MT <= 8 ? 128 : 64);
+  constexpr int PF = MT <= 4 ? 2 : (MT <= 8 ? 4 : 8);
+  if (a.kper % (PF * KC) == 0) {
+    launch_bf16_pf<MT, PF, TOPK>(a, nsplit, stream);
+  } else {
+    launch_bf16_pf<MT, 1, TOPK>(a, nsplit, stream);  // K range of 256 .. PF*KC-256
   }
   HY_LAUNCH_CHECK("projection(bf16)");
   return HYDRA_OK;
+}
+
+template <bool TOPK>
+int launch_bf16_mt(int mc, const ProjArgs& a, int nsplit, hipStream_t stream) {
+  if (mc <= 16) return launch_bf16<1, TOPK>(a, nsplit, stream);
+  if (mc <= 32) return launch_bf16<2, TOPK>(a, nsplit, stream);
+  if (mc <= 64) return launch_bf16<4, TOPK>(a, nsplit, stream);
+  if (mc <= 128) return launch_bf16<8, TOPK>(a, nsplit, stream);
+  return launch_bf16<16, TOPK>(a, nsplit, stream);
 }
 
 }  // namespace
 
 // Launch Y = X . W^T. With nsplit > 1 (bf16 only) writes float32 partials
 // part[split][m][n] instead of Y. M is processed in chunks of up to 256 rows.
-int launch_projection(int dtype, int M, int K, int N, XSource xs, const void* W, float* Y,
-                      RowMap map, int ldy, int nsplit, float* part, hipStream_t stream) {
+int launch_projection(int dtype, int M, int K, int N, XSource xs, const void* W, float* Y, RowMap map,
+                      int ldy, int nsplit, float* part, TopkPartials tp, hipStream_t stream) {
   if (M <= 0 || N <= 0) return HYDRA_OK;
+  if (tp.k > HYDRA_MAX_TOPK || (tp.k > 0 && (part || nsplit != 1))) {
+    set_error("projection: fused top-k needs k <= %d and no split-K", HYDRA_MAX_TOPK);
+    return HYDRA_ERR_UNSUPPORTED;
+  }
   if (dtype == HYDRA_F32) {
     if (nsplit != 1) {
       set_error("projection: split-K is bf16 only");
       return HYDRA_ERR_UNSUPPORTED;
     }
-    proj_f32_kernel<<<(N + 3) / 4, 256, 0, stream>>>(M, K, N, xs, static_cast<const float*>(W),
-                                                     Y, map, ldy);
+    proj_f32_kernel<<<(N + 3) / 4, 256, 0, stream>>>(M, K, N, xs, static_cast<const float*>(W), Y, map, ldy);
     HY_LAUNCH_CHECK("projection(f32)");
+    if (tp.k > 0) {
+      logits_partials<<<dim3(projection_nwg(N), M), 64, 0, stream>>>(M, N, Y, map, ldy, tp);
+      HY_LAUNCH_CHECK("projection(f32) partials");
+    }
     return HYDRA_OK;
   }
-  if (K % 256 != 0 || (K / nsplit) % 256 != 0 || K % nsplit != 0) {
+  if (K % 256 != 0 || K % nsplit != 0 || (K / nsplit) % 256 != 0) {
     set_error("projection: bf16 needs K %% 256 == 0 per split (K=%d, splits=%d)", K, nsplit);
     return HYDRA_ERR_UNSUPPORTED;
   }
+  ProjArgs a{M, K, N, xs, static_cast<const bf16_t*>(W), Y, map, ldy, K / nsplit, 0, part, tp};
   for (int m0 = 0; m0 < M; m0 += 256) {
     const int mc = M - m0 < 256 ? M - m0 : 256;
-    int rc;
-    if (mc <= 16) rc = launch_bf16<1>(M, K, N, xs, W, Y, map, ldy, nsplit, part, m0, stream);
-    else if (mc <= 32) rc = launch_bf16<2>(M, K, N, xs, W, Y, map, ldy, nsplit, part, m0, stream);
-    else if (mc <= 64) rc = launch_bf16<4>(M, K, N, xs, W, Y, map, ldy, nsplit, part, m0, stream);
-    else if (mc <= 128) rc = launch_bf16<8>(M, K, N, xs, W, Y, map, ldy, nsplit, part, m0, stream);
-    else rc = launch_bf16<16>(M, K, N, xs, W, Y, map, ldy, nsplit, part, m0, stream);
+    a.m_base = m0;
+    const int rc =
+        tp.k > 0 ? launch_bf16_mt<true>(mc, a, nsplit, stream) : launch_bf16_mt<false>(mc, a, nsplit, stream);
     if (rc != HYDRA_OK) return rc;
   }
   return HYDRA_OK;
@@ -235,20 +356,73 @@ int launch_projection(int dtype, int M, int K, int N, XSource xs, const void* W,
 
 }  // namespace hydra
 
-extern "C" int hydra_vocab_projection(int dtype, int M, int K, int N, const void* X,
-                                      const void* W, float* Y, void* stream) {
+namespace {
+struct VocabWs {
+  size_t keys, ms, total;
+};
+VocabWs vocab_ws(int M, int N, int k) {
+  VocabWs w{0, 0, 0};
+  if (M <= 0 || N <= 0 || k <= 0) return w;
+  const size_t slots = static_cast<size_t>(M) * hydra::projection_nwg(N);
+  w.keys = hydra::align_up(slots * k * sizeof(uint64_t), 256);
+  w.ms = hydra::align_up(slots * sizeof(float2), 256);
+  w.total = w.keys + w.ms + 256;
+  return w;
+}
+}  // namespace
+
+extern "C" size_t hydra_vocab_projection_workspace_size(int M, int N, int k) { return vocab_ws(M, N, k).total; }
+
+extern "C" int hydra_vocab_projection(int dtype, int M, int K, int N, int k, const void* X, const void* W,
+                                      float* Y, void* ws, size_t ws_bytes, void* stream) {
   using namespace hydra;
   clear_error();
   HY_CHECK(dtype == HYDRA_F32 || dtype == HYDRA_BF16, HYDRA_ERR_INVALID, "vocab_projection: bad dtype %d", dtype);
   HY_CHECK(M >= 0 && K > 0 && N > 0, HYDRA_ERR_INVALID, "vocab_projection: bad sizes M=%d K=%d N=%d", M, K, N);
+  HY_CHECK(k >= 0 && k <= HYDRA_MAX_TOPK && k <= N, HYDRA_ERR_INVALID, "vocab_projection: k=%d out of [0, %d]", k,
+           HYDRA_MAX_TOPK);
   HY_CHECK(M == 0 || (X && W && Y), HYDRA_ERR_INVALID, "vocab_projection: null pointer");
   HY_CHECK(dtype == HYDRA_F32 || K % 256 == 0, HYDRA_ERR_UNSUPPORTED,
            "vocab_projection: bf16 needs K %% 256 == 0 (K=%d)", K);
+  const VocabWs w = vocab_ws(M, N, k);
+  HY_CHECK(ws_bytes >= w.total && (w.total == 0 || ws), HYDRA_ERR_WORKSPACE,
+           "vocab_projection: workspace %zu < %zu", ws_bytes, w.total);
+  TopkPartials tp{nullptr, nullptr, 0};
+  if (k > 0) {
+    Arena arena(ws, ws_bytes);
+    tp.keys = arena.take<uint64_t>(w.keys / sizeof(uint64_t));
+    tp.ms = arena.take<float2>(w.ms / sizeof(float2));
+    tp.k = k;
+  }
   XSource xs{};
   xs.x = X;
   xs.ldx = K;
   xs.mode = 0;
   RowMap map{M > 0 ? M : 1, 0, 0};
-  return launch_projection(dtype, M, K, N, xs, W, Y, map, N, 1, nullptr,
-                           static_cast<hipStream_t>(stream));
+  return launch_projection(dtype, M, K, N, xs, W, Y, map, N, 1, nullptr, tp, static_cast<hipStream_t>(stream));
+}
+
+extern "C" int hydra_vocab_topk(int M, int N, int k, const void* ws, size_t ws_bytes, float* lse, int32_t* ids,
+                                float* vals, void* stream) {
+  using namespace hydra;
+  clear_error();
+  HY_CHECK(M >= 0 && N > 0 && k >= 1 && k <= HYDRA_MAX_TOPK && k <= N, HYDRA_ERR_INVALID,
+           "vocab_topk: bad sizes M=%d N=%d k=%d", M, N, k);
+  const VocabWs w = vocab_ws(M, N, k);
+  HY_CHECK(ws_bytes >= w.total && (w.total == 0 || ws), HYDRA_ERR_WORKSPACE, "vocab_topk: workspace %zu < %zu",
+           ws_bytes, w.total);
+  if (M == 0) return HYDRA_OK;
+  Arena arena(const_cast<void*>(ws), ws_bytes);
+  MergeArgs ma{};
+  ma.M = M;
+  ma.nwg = projection_nwg(N);
+  ma.k = k;
+  ma.keys = arena.take<uint64_t>(w.keys / sizeof(uint64_t));
+  ma.ms = arena.take<float2>(w.ms / sizeof(float2));
+  ma.map = RowMap{M, 0, 0};
+  ma.lse = lse;
+  ma.topk_ids = ids;
+  ma.topk_vals = vals;
+  ma.P = 1;
+  return launch_topk_merge(ma, static_cast<hipStream_t>(stream));
 }

@@ -205,13 +205,27 @@ def hydra_draft_heads(h, root_tok, emb, W1, b1, W2, dplan: DevicePlan, head_logi
     return _check("hydra_draft_heads", rc)
 
 
-def hydra_vocab_projection(X, W, Y, stream=None):
-    """Y[M, N] = X[M, K] . W[N, K]^T in float32."""
+def hydra_vocab_projection_workspace_size(M, N, k):
+    return int(lib().hydra_vocab_projection_workspace_size(M, N, k))
+
+
+def hydra_vocab_projection(X, W, Y, k=0, ws=None, stream=None):
+    """Y[M, N] = X[M, K] . W[N, K]^T in float32; with k > 0 also the fused
+    top-k partials in ws (finish with hydra_vocab_topk)."""
     M, K = X.shape
     N = W.shape[0]
-    rc = lib().hydra_vocab_projection(_dtype_code(X), M, K, N, _dev(X, "X"), _dev(W, "W", X.dtype),
-                                      _dev(Y, "Y", torch.float32), _stream(stream))
+    wsp, wsb = _ws(ws)
+    rc = lib().hydra_vocab_projection(_dtype_code(X), M, K, N, int(k), _dev(X, "X"), _dev(W, "W", X.dtype),
+                                      _dev(Y, "Y", torch.float32), wsp, wsb, _stream(stream))
     return _check("hydra_vocab_projection", rc)
+
+
+def hydra_vocab_topk(M, N, k, ws, lse=None, ids=None, vals=None, stream=None):
+    """Per-row log-sum-exp and sorted top-k from a k > 0 projection's workspace."""
+    wsp, wsb = _ws(ws)
+    rc = lib().hydra_vocab_topk(int(M), int(N), int(k), wsp, wsb, _dev(lse, "lse", torch.float32),
+                                _dev(ids, "ids", torch.int32), _dev(vals, "vals", torch.float32), _stream(stream))
+    return _check("hydra_vocab_topk", rc)
 
 
 def tree_build_workspace_size(B, N, n_keep):

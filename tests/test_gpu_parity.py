@@ -53,6 +53,40 @@ def test_projection_bf16(M, K, N):
     assert err <= 1e-3, err  # bf16 inputs are exact in fp32; only the summation order differs
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("M,K,N,k", [(1, 256, 1000, 10), (13, 4096, 32000, 10), (64, 512, 32000, 1),
+                                     (20, 256, 100, 16), (300, 256, 1000, 3), (5, 256, 70, 4)])
+def test_vocab_topk(dtype, M, K, N, k):
+    """Fused top-k / log-sum-exp of the projection: bit-exact against the CPU
+    on the device logits, and against the oracle's own float64 logits under
+    the 1e-4 margin rule."""
+    from speculative_decoding_hydra_amd import (hydra_vocab_projection, hydra_vocab_projection_workspace_size,
+                                                hydra_vocab_topk)
+
+    print(f"vocab top-k {dtype} M={M} K={K} N={N} k={k}", flush=True)
+    g = torch.Generator().manual_seed(M + K + N + k)
+    dt = torch.float32 if dtype == "fp32" else torch.bfloat16
+    X = torch.randn(M, K, generator=g).to(dt)
+    W = (torch.randn(N, K, generator=g) * 0.05).to(dt)
+    if N <= 100:  # force exact ties: duplicate rows of W
+        W[N // 2:] = W[: N - N // 2]
+    Y = torch.empty(M, N, device="cuda")
+    ws = torch.empty(hydra_vocab_projection_workspace_size(M, N, k), dtype=torch.uint8, device="cuda")
+    lse = torch.empty(M, device="cuda")
+    ids = torch.empty(M, k, dtype=torch.int32, device="cuda")
+    vals = torch.empty(M, k, device="cuda")
+    hydra_vocab_projection(X.cuda(), W.cuda(), Y, k, ws)
+    hydra_vocab_topk(M, N, k, ws, lse, ids, vals)
+    torch.cuda.synchronize()
+    Yd = Y.cpu().double().numpy()
+    ref = HI.as_f64(X) @ HI.as_f64(W).T
+    for m in range(M):
+        assert np.array_equal(ids[m].cpu().numpy(), O.topk_sorted(Yd[m], k)), f"row {m}"
+        assert np.array_equal(vals[m].cpu().double().numpy(), Yd[m][O.topk_sorted(Yd[m], k)])
+        T.check_topk(ref[m], Yd[m], k, ids[m].cpu().numpy(), f"row {m}")
+        assert abs(float(lse[m]) - O.logsumexp(Yd[m])) <= 1e-4 * max(1.0, abs(O.logsumexp(Yd[m])))
+
+
 @pytest.mark.parametrize("M,K,N", [(1, 256, 1000), (9, 256, 1000), (7, 100, 33)])
 def test_projection_f32(M, K, N):
     from speculative_decoding_hydra_amd import hydra_vocab_projection

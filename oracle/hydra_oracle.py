@@ -478,7 +478,7 @@ def sample_inverse_cdf(r, u):
     return int(np.flatnonzero(r > 0)[-1])
 
 
-def rejection_accept(Z, head_z, q_row, tok, parent, u_acc, u_res, T):
+def rejection_accept(Z, head_z, q_row, tok, parent, u_acc, u_res, T, follow=None, trace=None):
     """Stochastic acceptance on a tree (rule S1), for one sequence.
 
     Chain rule [SD, "The acceptance criterion"]: accept a drafted token x with
@@ -497,20 +497,51 @@ def rejection_accept(Z, head_z, q_row, tok, parent, u_acc, u_res, T):
     whose distribution drafted each node's children, u_acc [N] (used when the
     node is tested as a child), u_res [N] (used when a draw happens at it).
     Returns (m, path, out).
+
+    Checking aid: with ``follow = (path, out)`` from another implementation,
+    the walk takes that implementation's decisions instead of its own and, if
+    ``trace`` is a list, appends one record per decision: ("accept", own,
+    taken, margin) with margin = |u q(x) - r(x)| / r(x), or ("sample", own,
+    taken, margin) with margin = distance of u * sum(r) to the cumulative
+    boundary between the two tokens, over sum(r).
     """
     u, path, out = 0, [0], []
+    fpath = None if follow is None else [int(x) for x in follow[0]]
+    fout = None if follow is None else [int(x) for x in follow[1]]
+
+    def draw(r, uu):
+        own = sample_inverse_cdf(r, uu)
+        if fout is None:
+            return own
+        taken = fout[len(out)]
+        if trace is not None:
+            c = np.cumsum(r)
+            thr = uu * c[-1]
+            lo, hi = min(own, taken), max(own, taken)
+            edge = c[lo:hi]  # boundaries separating the two tokens
+            margin = float(np.min(np.abs(edge - thr)) / c[-1]) if hi > lo else np.inf
+            trace.append(("sample", own, taken, margin))
+        return taken
+
     while True:
         p = softmax(np.asarray(Z[u], dtype=np.float64) / T)
         kids = [c for c in range(len(parent)) if parent[c] == u]
         if not kids:
-            out.append(sample_inverse_cdf(p, u_res[u]))
+            out.append(draw(p, u_res[u]))
             break
         q = softmax(np.asarray(head_z[q_row[u]], dtype=np.float64) / T)
         r = p
         moved = False
         for c in kids:
             x = int(tok[c])
-            if u_acc[c] * q[x] < r[x]:
+            own = bool(u_acc[c] * q[x] < r[x])
+            take = own
+            if fpath is not None:
+                take = len(path) < len(fpath) and fpath[len(path)] == c
+                if trace is not None:
+                    margin = abs(u_acc[c] * q[x] - r[x]) / max(r[x], 1e-300)
+                    trace.append(("accept", own, take, margin))
+            if take:
                 out.append(x)
                 path.append(c)
                 u = c
@@ -520,6 +551,6 @@ def rejection_accept(Z, head_z, q_row, tok, parent, u_acc, u_res, T):
             if nr is not None:
                 r = nr
         if not moved:
-            out.append(sample_inverse_cdf(r, u_res[u]))
+            out.append(draw(r, u_res[u]))
             break
     return len(path) - 1, path, out

@@ -5,7 +5,9 @@ Parity is stage-wise: each oracle stage is fed the device's upstream outputs
 near-tie at depth 1 cannot cascade, and the float and integer results of
 every stage are compared with the oracle on the same inputs:
 
-* head hidden state u: oracle from the device's parent tokens;
+* head hidden state u: oracle from the device's parent tokens; in bf16 mode
+  at most one bf16 rounding step (or 1e-3 where h + SiLU(a) cancels to near
+  zero) apart per element, differing on at most 1% of them;
 * head logits z and log-sum-exp: oracle projection of the device's u;
 * top-k tokens: bit-exact, except where the oracle's margin between
   consecutive sorted logits is below 1e-4, where the decision is recomputed
@@ -29,6 +31,13 @@ import hydra_inputs as HI
 from oracle import hydra_oracle as O
 
 MARGIN = 1e-4
+# Rejection walk: a device decision may differ from the float64 oracle only
+# when the oracle's own decision is that close to its boundary (relative):
+# the accept test u q(x) < r(x), or the cumulative mass at the drawn token.
+# float32 probabilities carry ~1e-7 relative error each, so these bounds leave
+# two orders of magnitude of room.
+ACCEPT_EPS = 1e-5
+SAMPLE_EPS = 1e-5
 
 
 def tol(w):
@@ -112,7 +121,20 @@ def check_draft(inp, rnd, seqs=None, rows=None):
                 ptok = int(inp["root_tok"][b]) if p == 0 else int(ctok[b, p])
                 e = HI.as_f64(inp["E"][ptok])
             u = O.head_hidden(h[b], e, W1, b1, True, bf16)
-            err["u"] = max(err["u"], float(np.max(np.abs(u - hidden[b, r]))))
+            if bf16:
+                # u is stored in bf16: a float32-vs-float64 difference in a can
+                # flip one rounding, so compare in units of the bf16 step
+                # (plus an absolute 1e-3 where h + SiLU(a) cancels to near zero)
+                ulp = np.ldexp(1.0, np.frexp(np.maximum(np.abs(u), 1e-30))[1] - 8)
+                diff = np.abs(u - hidden[b, r])
+                bad = diff > np.maximum(ulp, 1e-3)
+                j = int(np.argmax(diff / np.maximum(ulp, 1e-3)))
+                assert not bad.any(), (f"seq {b} row {r}: u[{j}] = {hidden[b, r][j]!r} vs oracle {u[j]!r} "
+                                       f"(bf16 step {ulp[j]:.3g})")
+                err["u_flips"] = err.get("u_flips", 0) + int(np.sum(diff > 0))
+                err["u_elems"] = err.get("u_elems", 0) + u.size
+            else:
+                err["u"] = max(err["u"], float(np.max(np.abs(u - hidden[b, r]))))
             z = O.head_logits(hidden[b, r], W2)
             err["z"] = max(err["z"], float(np.max(np.abs(z - logits[b, r]))))
             err["lse"] = max(err["lse"], abs(O.logsumexp(z) - lse[b, r]))
@@ -131,6 +153,8 @@ def check_draft(inp, rnd, seqs=None, rows=None):
                 ref = clogp[b, plan.parent[c]] + logits[b, r, ctok[b, c]] - O.logsumexp(logits[b, r])
                 err["logp"] = max(err["logp"], abs(ref - clogp[b, c]))
     assert err["u"] <= t, f"head hidden max-abs {err['u']:.3g} > {t}"
+    if bf16:
+        assert err["u_flips"] <= 0.01 * err["u_elems"], f"{err['u_flips']} rounding flips in u"
     assert err["z"] <= t, f"head logits max-abs {err['z']:.3g} > {t}"
     assert err["lse"] <= t and err["logp"] <= t, (err["lse"], err["logp"])
     for b in seqs:
@@ -191,19 +215,25 @@ def check_accept(inp, rnd, seqs=None):
     for b in seqs:
         Z = O.target_logits(O_dev[b: b + 1], Wt)[0]
         e_z = max(e_z, float(np.max(np.abs(Z - Z_dev[b]))))
-        if w.mode == "greedy":
-            m, p, o = O.greedy_accept(Z_dev[b], tok[b], par[b], Dm)
-        else:
-            hz = np_(rnd.head_logits)[b]
-            m, p, o = O.rejection_accept(Z_dev[b], hz, qrow[b], tok[b], par[b], np_(inp["u_acc"])[b],
-                                         np_(inp["u_res"])[b], w.T)
         got_p = [int(x) for x in path[b] if x >= 0]
         got_o = [int(x) for x in out[b] if x >= 0]
+        assert n_acc[b] == len(got_p) - 1 and len(got_o) == len(got_p)
         if w.mode == "greedy":
+            m, p, o = O.greedy_accept(Z_dev[b], tok[b], par[b], Dm)
             assert n_acc[b] == m and got_p == p and got_o == o, f"seq {b}: greedy walk {got_p}/{got_o} vs {p}/{o}"
-        elif not (n_acc[b] == m and got_p == p and got_o == o):
-            amb += 1
-            assert got_p[: len(p)] == p[: len(got_p)] or got_p[:-1] == p[:-1], f"seq {b}: rejection walk diverged"
+        else:
+            # the oracle follows the device's decisions and reports its own;
+            # they may differ only within float32 rounding of the boundary
+            hz = np_(rnd.head_logits)[b]
+            trace = []
+            m, p, o = O.rejection_accept(Z_dev[b], hz, qrow[b], tok[b], par[b], np_(inp["u_acc"])[b],
+                                         np_(inp["u_res"])[b], w.T, follow=(got_p, got_o), trace=trace)
+            assert p == got_p and o == got_o
+            for kind, own, taken, margin in trace:
+                if own != taken:
+                    amb += 1
+                    bound = ACCEPT_EPS if kind == "accept" else SAMPLE_EPS
+                    assert margin < bound, f"seq {b}: {kind} decision {taken} vs oracle {own} (margin {margin:.3g})"
     assert e_z <= t, f"target logits max-abs {e_z:.3g} > {t}"
     return dict(z=e_z, ambiguous=amb)
 

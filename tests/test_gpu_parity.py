@@ -314,3 +314,69 @@ def test_7b_dense256_round():
     inp, rnd, _ = _round("7b_dense256")
     rep = T.oracle_round_checks(inp, rnd)
     print(rep, flush=True)
+
+
+def test_tiny_stochastic_round():
+    """Rejection acceptance at temperature 0.7 on the tiny workload."""
+    inp, rnd, _ = _round("tiny", mode="stochastic", T=0.7)
+    rep = T.oracle_round_checks(inp, rnd)
+    print(rep, flush=True)
+
+
+@pytest.mark.parametrize("seed", [11, 12, 13])
+def test_tiny_stochastic_planted_acceptance(seed):
+    """Planted attention outputs make the target favour the drafted tokens
+    along one branch, so the rejection walk sees accepts as well as
+    rejections, residual updates and the final draw; every decision is
+    checked against the oracle following the device's path."""
+    inp, rnd, dev = _round("tiny", mode="stochastic", T=0.7, seed=seed)
+    g = np.random.default_rng(seed)
+    plan, _ = T.oracle_plan(inp["workload"].tree)
+    Wt = inp["W_t"]
+    tok = rnd.tok.cpu().numpy()
+    o = rnd.attn_out.clone()
+    for b in range(o.shape[0]):
+        u = 0
+        while plan.children(u):
+            c = int(g.choice(plan.children(u)))
+            o[b, u] = (Wt[int(tok[b, c])] * 40.0).view(o.shape[2], o.shape[3]).to(o.device)
+            u = c
+    rnd.attn_out.copy_(o)
+    rnd.accept(dev["u_acc"], dev["u_res"])
+    torch.cuda.synchronize()
+    rep = T.check_accept(inp, rnd)
+    print(rep, "accepted", rnd.n_accepted.tolist(), flush=True)
+
+
+def test_7b_batched16_round():
+    """16 ragged sequences over scattered 16-token pages; sampled sequences
+    checked stage by stage."""
+    inp, rnd, _ = _round("7b_batched16")
+    lens = inp["prefix_len"].tolist()
+    seqs = sorted({0, int(np.argmin(lens)), int(np.argmax(lens)), 15})
+    print("prefix lengths", lens, "checked", seqs, flush=True)
+    rep = T.oracle_round_checks(inp, rnd, seqs=seqs)
+    print(rep, flush=True)
+
+
+def test_70b_gqa_stochastic_round():
+    """70B-shaped GQA layer (64 query heads on 8 KV heads), prefix 16384,
+    rejection acceptance at temperature 0.7; sequences 0 and 3 checked."""
+    inp, rnd, _ = _round("70b_gqa")
+    rep = T.oracle_round_checks(inp, rnd, seqs=[0, 3])
+    print(rep, flush=True)
+
+
+@pytest.mark.parametrize("B,d,b1", [(4, 8192, 10), (4, 4096, 10), (3, 8192, 13), (2, 256, 16), (1, 8192, 16)])
+def test_draft_first_layer_split_and_fused(B, d, b1):
+    """Head hidden states for row counts on both sides of the fused few-row
+    kernel (B * b1 <= 32) and the split-K projection path, d up to 8192."""
+    w = HI.workload("70b_gqa", B=B, d=d, V=1000, n_heads=2, tree=("cartesian", (b1, 1)), Hq=8, Hkv=8, D=32,
+                    L=(64,), mode="greedy", T=1.0)
+    print(f"first layer B={B} d={d} rows/depth2={B * b1}", flush=True)
+    inp = HI.generate(w)
+    rnd, dev = T.round_inputs(inp)
+    T.run_round(rnd, dev)
+    torch.cuda.synchronize()
+    rep = T.check_draft(inp, rnd)
+    print(rep, flush=True)

@@ -443,6 +443,26 @@ def test_rejection_identity_chi_square(monkeypatch):
     assert scipy.stats.chisquare(naive, mix * trials).pvalue > 1e-3
 
 
+def test_rejection_follow_own_decisions_is_identity():
+    """The checking aid: following the walk's own decisions changes nothing
+    and records no disagreement."""
+    rng = np.random.default_rng(17)
+    V = 12
+    plan = H.plan_cartesian([3, 2, 2])
+    _, _, node_row = H.head_rows(plan, True)
+    for _ in range(100):
+        tok = rng.integers(0, V, plan.n)
+        Z = rng.standard_normal((plan.n, V)) * 2
+        hz = rng.standard_normal((int(node_row.max()) + 1, V)) * 2
+        ua, ur = rng.random(plan.n), rng.random(plan.n)
+        m, path, out = H.rejection_accept(Z, hz, node_row, tok, plan.parent, ua, ur, 0.7)
+        trace = []
+        m2, path2, out2 = H.rejection_accept(Z, hz, node_row, tok, plan.parent, ua, ur, 0.7,
+                                             follow=(path, out), trace=trace)
+        assert (m, path, out) == (m2, path2, out2)
+        assert trace and all(own == taken for _, own, taken, _ in trace)
+
+
 def test_rejection_equal_distributions_never_resample():
     rng = np.random.default_rng(15)
     V = 6

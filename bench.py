@@ -30,6 +30,7 @@ sys.path.insert(0, ROOT)
 METRIC = "verified tree-tokens/sec per round + % HBM roofline (64-node tree, 7B-shape)"
 HBM_PEAK_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "vocab_projection_7b_traffic.json")
+CAL_BYTES = 256 << 20
 
 
 def parse():
@@ -38,7 +39,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="7b_sparse64")
-    ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--no-graph", action="store_true", help="eager launches everywhere (for counter runs)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--kernel-reps", type=int, default=20)
     return ap.parse_args()
@@ -202,6 +203,8 @@ def main():
     torch.cuda.synchronize()
     kgraph = None
     try:  # back-to-back launches from a graph, so the events see no launch gaps
+        if args.no_graph:
+            raise RuntimeError("--no-graph")
         s2 = torch.cuda.Stream()
         s2.wait_stream(stream)
         with torch.cuda.stream(s2):
@@ -228,6 +231,13 @@ def main():
     kb.record(stream)
     torch.cuda.synchronize()
     k_ms = ka.elapsed_time(kb) / args.kernel_reps
+
+    # a plain elementwise pass of known size (reads and writes 256 MiB), so that
+    # HBM counters taken over this command can be scaled to bytes
+    cal = torch.ones(CAL_BYTES // 4, device="cuda")
+    torch.neg(cal, out=torch.empty_like(cal))
+    torch.cuda.synchronize()
+    del cal
     esz = X.element_size()
     alg_bytes = w.V * w.d * esz + M * w.d * esz + M * w.V * 4
     achieved = alg_bytes / (k_ms * 1e-3) / 1e9
@@ -256,7 +266,7 @@ def main():
                    "launch": "hip-graph" if graph is not None else "eager"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(),
-                     "kernel": "proj_bf16_kernel<1,256,2,false,true> (vocabulary projection, fused top-k)",
+                     "kernel": "proj_bf16_kernel (vocabulary projection, fused top-k epilogue)",
                      "bytes_per_launch": alg_bytes, "rows": M, "topk": kk, "avg_launch_ms": k_ms},
         "stages_ms": {"draft": stage_ms[0], "build": stage_ms[1], "attention": stage_ms[2],
                       "accept": stage_ms[3]},

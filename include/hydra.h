@@ -164,22 +164,24 @@ int hydra_draft_heads(int dtype, int B, int d, int V, int hydra, int residual,
  * Y[m, n] = sum_k X[m, k] * W[n, k], float32 accumulation and output.
  * X [M, K], W [N, K] (dtype), Y [M, N] float32. bf16 needs K % 256 == 0.
  * With k > 0 the same pass also leaves, in the workspace, per row and per
- * 64-column block of W, the block's top-k logits and (max, sum exp); finish
- * them with hydra_vocab_topk. k = 0: no workspace is needed (ws may be NULL).
- * 0 <= k <= HYDRA_MAX_TOPK <= N. */
+ * 64-column block of W, the block's largest logit (with its id) and
+ * (max, sum exp); finish them with hydra_vocab_topk. k = 0: no workspace is
+ * needed (ws may be NULL). 0 <= k <= HYDRA_MAX_TOPK, k <= N. */
 size_t hydra_vocab_projection_workspace_size(int M, int N, int k);
 
 int hydra_vocab_projection(int dtype, int M, int K, int N, int k, const void* X,
                            const void* W, float* Y, void* ws, size_t ws_bytes,
                            void* stream);
 
-/* Row reductions of a projection made with k > 0, from its workspace:
- * lse[m] = log sum_n exp(Y[m, n]) and the k largest logits of each row,
- * sorted by value descending, ties to the lower id ([HG] "Candidate Tree
- * Construction": each head keeps its top-b_k tokens).
+/* Row reductions of a projection made with k > 0, from its workspace and its
+ * logits Y [M, N] (unchanged since the projection): lse[m] = log sum_n
+ * exp(Y[m, n]) and the k largest logits of each row, sorted by value
+ * descending, ties to the lower id ([HG] "Candidate Tree Construction": each
+ * head keeps its top-b_k tokens). The top k are read from the k blocks with
+ * the largest maxima, which hold them all.
  * lse [M] float32, ids [M, k] int32, vals [M, k] float32 (any may be NULL). */
-int hydra_vocab_topk(int M, int N, int k, const void* ws, size_t ws_bytes, float* lse,
-                     int32_t* ids, float* vals, void* stream);
+int hydra_vocab_topk(int M, int N, int k, const float* Y, const void* ws, size_t ws_bytes,
+                     float* lse, int32_t* ids, float* vals, void* stream);
 
 /* ------------------------------------------------------------------------
  * Stage 2: tree build

@@ -306,7 +306,7 @@ extern "C" int tree_accept(int dtype, int mode, int B, int N, int d, int V, int 
     uint64_t* keys = arena.take<uint64_t>(static_cast<size_t>(M) * nwg);
     float2* ms = arena.take<float2>(static_cast<size_t>(M) * nwg);
     int rc = launch_projection(dtype, M, d, V, xs, W_t, target_logits, RowMap{M, 0, 0}, V, 1, nullptr,
-                               TopkPartials{keys, ms, 1}, stream);
+                               TopkPartials{keys, ms}, stream);
     if (rc != HYDRA_OK) return rc;
     MergeArgs ma{};
     ma.M = M;
@@ -314,6 +314,9 @@ extern "C" int tree_accept(int dtype, int mode, int B, int N, int d, int V, int 
     ma.k = 1;
     ma.keys = keys;
     ma.ms = ms;
+    ma.Y = target_logits;
+    ma.ldy = V;
+    ma.V = V;
     ma.map = RowMap{M, 0, 0};
     ma.amax = amax;
     ma.P = 1;
@@ -323,7 +326,7 @@ extern "C" int tree_accept(int dtype, int mode, int B, int N, int d, int V, int 
     HY_LAUNCH_CHECK("tree_accept: greedy walk");
   } else {
     int rc = launch_projection(dtype, M, d, V, xs, W_t, target_logits, RowMap{M, 0, 0}, V, 1, nullptr,
-                               TopkPartials{nullptr, nullptr, 0}, stream);
+                               TopkPartials{nullptr, nullptr}, stream);
     if (rc != HYDRA_OK) return rc;
     float* rbuf = arena.take<float>(static_cast<size_t>(B) * 2 * V);
     reject_walk<<<B, kWalkThreads, 0, stream>>>(N, V, R, Dmax, 1.0f / temperature, target_logits, head_logits, tok,

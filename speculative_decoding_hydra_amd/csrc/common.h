@@ -245,12 +245,11 @@ struct XSource {
 };
 
 // Optional fused row reduction of a projection: for every row and every
-// workgroup along N, the top-k keys of that workgroup's columns (sorted,
-// topk_key order) and (max, sum exp(z - max)) over them. k = 0 disables it.
+// 64-column block, the block's largest key (topk_key order) and (max, sum
+// exp(z - max)) over its columns. keys == nullptr disables it.
 struct TopkPartials {
-  uint64_t* keys;  // [M][nwg][k]
+  uint64_t* keys;  // [M][nwg]
   float2* ms;      // [M][nwg]
-  int k;
 };
 
 constexpr int kProjRowsPerWG = 64;
@@ -261,14 +260,18 @@ int launch_projection(int dtype, int M, int K, int N, XSource xs, const void* W,
                       hipStream_t stream);
 
 // Finish the fused row reduction: log-sum-exp and sorted top-k of each row,
-// then either the candidate-tree fill (draft heads) or the arg max.
+// then either the candidate-tree fill (draft heads) or the arg max. The top-k
+// is taken from the finished logits Y of the k blocks with the largest
+// maxima (no key outside those blocks can rank among the first k).
 struct MergeArgs {
   int M, nwg, k;
   const uint64_t* keys;
   const float2* ms;
-  RowMap map;           // launch row -> output row (for head_lse)
+  const float* Y;       // logits, row m at Y + map(m) * ldy, V columns
+  int ldy, V;
+  RowMap map;           // launch row -> output row (logits and head_lse)
   float* lse;           // [out rows] or nullptr
-  int32_t* amax;        // [M] arg max (k = 1) or nullptr
+  int32_t* amax;        // [M] arg max or nullptr
   int32_t* topk_ids;    // [M][k] or nullptr
   float* topk_vals;     // [M][k] or nullptr
   // tree fill (draft heads); node_hi <= node_lo disables it

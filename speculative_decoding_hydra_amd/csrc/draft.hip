@@ -59,12 +59,8 @@ struct DraftWs {
 };
 DraftWs draft_ws(int dtype, int B, int d, int V, int hydra_mode, int Dmax, const int32_t* row_first,
                  const int32_t* k_per_depth) {
-  int maxP = 0, maxk = 1;
-  for (int k = 1; k <= Dmax; ++k) {
-    maxP = std::max(maxP, row_first[k] - row_first[k - 1]);
-    if (k_per_depth) maxk = std::max(maxk, static_cast<int>(k_per_depth[k - 1]));
-  }
-  if (!k_per_depth) maxk = HYDRA_MAX_TOPK;
+  int maxP = 0;
+  for (int k = 1; k <= Dmax; ++k) maxP = std::max(maxP, row_first[k] - row_first[k - 1]);
   const size_t M = static_cast<size_t>(B) * maxP;
   const int in_dim = hydra_mode ? 2 * d : d;
   const size_t esz = dtype == HYDRA_F32 ? 4 : 2;
@@ -72,7 +68,7 @@ DraftWs draft_ws(int dtype, int B, int d, int V, int hydra_mode, int Dmax, const
   DraftWs w;
   w.part = align_up(w1_splits(dtype, in_dim, d) * M * d * sizeof(float), 256);
   w.u = align_up(M * d * esz, 256);
-  w.keys = align_up(M * nwg * maxk * sizeof(uint64_t), 256);
+  w.keys = align_up(M * nwg * sizeof(uint64_t), 256);
   w.ms = align_up(M * nwg * sizeof(float2), 256);
   w.total = w.part + w.u + w.keys + w.ms + 256;
   return w;
@@ -124,11 +120,8 @@ extern "C" int hydra_draft_heads(int dtype, int B, int d, int V, int hydra_mode,
   HY_CHECK(ws_bytes >= need && (need == 0 || ws), HYDRA_ERR_WORKSPACE,
            "draft_heads: workspace %zu < required %zu", ws_bytes, need);
 
-  int maxP = 0, maxk = 1;
-  for (int k = 1; k <= Dmax; ++k) {
-    maxP = std::max(maxP, row_first[k] - row_first[k - 1]);
-    maxk = std::max(maxk, static_cast<int>(k_per_depth[k - 1]));
-  }
+  int maxP = 0;
+  for (int k = 1; k <= Dmax; ++k) maxP = std::max(maxP, row_first[k] - row_first[k - 1]);
   const size_t Mmax = static_cast<size_t>(B) * maxP;
   const int in_dim = hydra_mode ? 2 * d : d;
   const int ns = w1_splits(dtype, in_dim, d);
@@ -137,7 +130,7 @@ extern "C" int hydra_draft_heads(int dtype, int B, int d, int V, int hydra_mode,
   Arena arena(ws, ws_bytes);
   float* part = arena.take<float>(ns * Mmax * d);
   char* U = arena.take<char>(Mmax * d * esz);
-  uint64_t* tkeys = arena.take<uint64_t>(Mmax * nwg * maxk);
+  uint64_t* tkeys = arena.take<uint64_t>(Mmax * nwg);
   float2* tms = arena.take<float2>(Mmax * nwg);
 
   for (int k = 1; k <= Dmax; ++k) {
@@ -175,7 +168,7 @@ extern "C" int hydra_draft_heads(int dtype, int B, int d, int V, int hydra_mode,
     } else {
       rc = launch_projection(dtype, M, in_dim, d, xs, W1[k - 1], dtype == HYDRA_F32 ? part : nullptr,
                              RowMap{M, 0, 0}, d, nsk, dtype == HYDRA_F32 ? nullptr : part,
-                             TopkPartials{nullptr, nullptr, 0}, stream);
+                             TopkPartials{nullptr, nullptr}, stream);
       if (rc != HYDRA_OK) return rc;
     }
     // 2. epilogue: u = h + SiLU(sum + b1)
@@ -201,7 +194,7 @@ extern "C" int hydra_draft_heads(int dtype, int B, int d, int V, int hydra_mode,
     xu.mode = 0;
     const int kk = k_per_depth[k - 1];
     rc = launch_projection(dtype, M, d, V, xu, W2[k - 1], head_logits, map, V, 1, nullptr,
-                           TopkPartials{tkeys, tms, kk}, stream);
+                           TopkPartials{tkeys, tms}, stream);
     if (rc != HYDRA_OK) return rc;
     // 4. log-sum-exp, top-k, tree fill
     MergeArgs ma{};
@@ -210,6 +203,9 @@ extern "C" int hydra_draft_heads(int dtype, int B, int d, int V, int hydra_mode,
     ma.k = kk;
     ma.keys = tkeys;
     ma.ms = tms;
+    ma.Y = head_logits;
+    ma.ldy = V;
+    ma.V = V;
     ma.map = map;
     ma.lse = head_lse;
     ma.amax = nullptr;

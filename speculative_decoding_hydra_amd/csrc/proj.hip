@@ -34,7 +34,7 @@ struct ProjArgs {
   TopkPartials tp;
 };
 
-template <int MT, int KC, int PF, int WV, bool SPLIT, bool TOPK, int KCAP = HYDRA_MAX_TOPK>
+template <int MT, int KC, int PF, int WV, bool SPLIT, bool TOPK>
 __global__ __launch_bounds__(64 * WV) void proj_bf16_kernel(ProjArgs a) {
   constexpr int NT = 64 * WV;      // threads
   constexpr int RPW = 16 * WV;     // rows of W per workgroup (one 16-row tile per wave)
@@ -183,33 +183,32 @@ __global__ __launch_bounds__(64 * WV) void proj_bf16_kernel(ProjArgs a) {
     const int mloc = t2 / TPR, sub = t2 % TPR;
     const int m = m_base + mloc;
     const int col0 = static_cast<int>(blockIdx.x) * RPW + blk * kProjRowsPerWG;
-    // a thread holds VPT values, so its list never needs more than VPT entries;
     // rows past M skip the work (a row's TPR threads share one wave)
-    constexpr int KL = VPT < KCAP ? VPT : KCAP;
     if (m < M && col0 < N) {
-      uint64_t l[KL];
-#pragma unroll
-      for (int j = 0; j < KL; ++j) l[j] = 0;
       float mx = -INFINITY;
-#pragma unroll
-      for (int j = 0; j < VPT; ++j) mx = fmaxf(mx, tile[mloc * TROW + blk * kProjRowsPerWG + sub + j * TPR]);
-      float s = 0.f;
+      uint64_t best = 0;
 #pragma unroll
       for (int j = 0; j < VPT; ++j) {
         const int nl = blk * kProjRowsPerWG + sub + j * TPR;
         const float v = tile[mloc * TROW + nl];
+        mx = fmaxf(mx, v);
+        const uint64_t key = v == -INFINITY ? 0 : topk_key(v, static_cast<int>(blockIdx.x) * RPW + nl);
+        best = key > best ? key : best;
+      }
+      float s = 0.f;
+#pragma unroll
+      for (int j = 0; j < VPT; ++j) {
+        const float v = tile[mloc * TROW + blk * kProjRowsPerWG + sub + j * TPR];
         if (v != -INFINITY) s += expf(v - mx);
-        list_insert<KL>(l, topk_key(v, static_cast<int>(blockIdx.x) * RPW + nl));
       }
       // combine the TPR threads of the row (an aligned lane group of one wave)
       group_ms<TPR>(mx, s);
-      const size_t slot = static_cast<size_t>(m) * projection_nwg(N) + col0 / kProjRowsPerWG;
-      for (int j = 0; j < a.tp.k; ++j) {
-        const uint64_t best = group_max_u64<TPR>(l[0]);
-        if (l[0] == best) list_pop<KL>(l);
-        if (sub == 0) a.tp.keys[slot * a.tp.k + j] = best;
+      best = group_max_u64<TPR>(best);
+      if (sub == 0) {
+        const size_t slot = static_cast<size_t>(m) * projection_nwg(N) + col0 / kProjRowsPerWG;
+        a.tp.keys[slot] = best;
+        a.tp.ms[slot] = make_float2(mx, s);
       }
-      if (sub == 0) a.tp.ms[slot] = make_float2(mx, s);
     }
   }
 }
@@ -255,19 +254,12 @@ __global__ __launch_bounds__(64) void logits_partials(int M, int N, const float*
   const float v = n < N ? Y[static_cast<size_t>(map(m)) * ldy + n] : -INFINITY;
   const float mx = wave_max(v);
   const float s = wave_sum(v == -INFINITY ? 0.f : expf(v - mx));
-  uint64_t key = topk_key(v, n);
-  const size_t slot = static_cast<size_t>(m) * gridDim.x + w;
-  for (int j = 0; j < tp.k; ++j) {
-    uint64_t best = key;
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const uint64_t o = shfl_xor_u64(best, off);
-      best = o > best ? o : best;
-    }
-    if (key == best) key = 0;
-    if (lane == 0) tp.keys[slot * tp.k + j] = best;
+  const uint64_t best = wave_max_u64(n < N ? topk_key(v, n) : 0);
+  if (lane == 0) {
+    const size_t slot = static_cast<size_t>(m) * gridDim.x + w;
+    tp.keys[slot] = best;
+    tp.ms[slot] = make_float2(mx, s);
   }
-  if (lane == 0) tp.ms[slot] = make_float2(mx, s);
 }
 
 template <int MT, int PF, bool TOPK>
@@ -280,16 +272,10 @@ void launch_bf16_pf(const ProjArgs& a, int nsplit, hipStream_t stream) {
     proj_bf16_kernel<MT, KC, PF, 4, true, false><<<grid, 256, 0, stream>>>(a);
   } else if constexpr (MT >= 4) {
     dim3 grid((a.N + 127) / 128, 1);
-    if (TOPK && a.tp.k == 1)  // arg max: a one-entry list per thread
-      proj_bf16_kernel<MT, KC, PF, 8, false, TOPK, 1><<<grid, 512, 0, stream>>>(a);
-    else
-      proj_bf16_kernel<MT, KC, PF, 8, false, TOPK><<<grid, 512, 0, stream>>>(a);
+    proj_bf16_kernel<MT, KC, PF, 8, false, TOPK><<<grid, 512, 0, stream>>>(a);
   } else {
     dim3 grid((a.N + 63) / 64, 1);
-    if (TOPK && a.tp.k == 1)
-      proj_bf16_kernel<MT, KC, PF, 4, false, TOPK, 1><<<grid, 256, 0, stream>>>(a);
-    else
-      proj_bf16_kernel<MT, KC, PF, 4, false, TOPK><<<grid, 256, 0, stream>>>(a);
+    proj_bf16_kernel<MT, KC, PF, 4, false, TOPK><<<grid, 256, 0, stream>>>(a);
   }
 }
 
@@ -322,8 +308,8 @@ int launch_bf16_mt(int mc, const ProjArgs& a, int nsplit, hipStream_t stream) {
 int launch_projection(int dtype, int M, int K, int N, XSource xs, const void* W, float* Y, RowMap map,
                       int ldy, int nsplit, float* part, TopkPartials tp, hipStream_t stream) {
   if (M <= 0 || N <= 0) return HYDRA_OK;
-  if (tp.k > HYDRA_MAX_TOPK || (tp.k > 0 && (part || nsplit != 1))) {
-    set_error("projection: fused top-k needs k <= %d and no split-K", HYDRA_MAX_TOPK);
+  if (tp.keys && (part || nsplit != 1)) {
+    set_error("projection: the fused row reduction needs no split-K");
     return HYDRA_ERR_UNSUPPORTED;
   }
   if (dtype == HYDRA_F32) {
@@ -333,7 +319,7 @@ int launch_projection(int dtype, int M, int K, int N, XSource xs, const void* W,
     }
     proj_f32_kernel<<<(N + 3) / 4, 256, 0, stream>>>(M, K, N, xs, static_cast<const float*>(W), Y, map, ldy);
     HY_LAUNCH_CHECK("projection(f32)");
-    if (tp.k > 0) {
+    if (tp.keys) {
       logits_partials<<<dim3(projection_nwg(N), M), 64, 0, stream>>>(M, N, Y, map, ldy, tp);
       HY_LAUNCH_CHECK("projection(f32) partials");
     }
@@ -348,7 +334,7 @@ int launch_projection(int dtype, int M, int K, int N, XSource xs, const void* W,
     const int mc = M - m0 < 256 ? M - m0 : 256;
     a.m_base = m0;
     const int rc =
-        tp.k > 0 ? launch_bf16_mt<true>(mc, a, nsplit, stream) : launch_bf16_mt<false>(mc, a, nsplit, stream);
+        tp.keys ? launch_bf16_mt<true>(mc, a, nsplit, stream) : launch_bf16_mt<false>(mc, a, nsplit, stream);
     if (rc != HYDRA_OK) return rc;
   }
   return HYDRA_OK;
@@ -364,7 +350,7 @@ VocabWs vocab_ws(int M, int N, int k) {
   VocabWs w{0, 0, 0};
   if (M <= 0 || N <= 0 || k <= 0) return w;
   const size_t slots = static_cast<size_t>(M) * hydra::projection_nwg(N);
-  w.keys = hydra::align_up(slots * k * sizeof(uint64_t), 256);
+  w.keys = hydra::align_up(slots * sizeof(uint64_t), 256);
   w.ms = hydra::align_up(slots * sizeof(float2), 256);
   w.total = w.keys + w.ms + 256;
   return w;
@@ -387,12 +373,11 @@ extern "C" int hydra_vocab_projection(int dtype, int M, int K, int N, int k, con
   const VocabWs w = vocab_ws(M, N, k);
   HY_CHECK(ws_bytes >= w.total && (w.total == 0 || ws), HYDRA_ERR_WORKSPACE,
            "vocab_projection: workspace %zu < %zu", ws_bytes, w.total);
-  TopkPartials tp{nullptr, nullptr, 0};
+  TopkPartials tp{nullptr, nullptr};
   if (k > 0) {
     Arena arena(ws, ws_bytes);
     tp.keys = arena.take<uint64_t>(w.keys / sizeof(uint64_t));
     tp.ms = arena.take<float2>(w.ms / sizeof(float2));
-    tp.k = k;
   }
   XSource xs{};
   xs.x = X;
@@ -402,8 +387,8 @@ extern "C" int hydra_vocab_projection(int dtype, int M, int K, int N, int k, con
   return launch_projection(dtype, M, K, N, xs, W, Y, map, N, 1, nullptr, tp, static_cast<hipStream_t>(stream));
 }
 
-extern "C" int hydra_vocab_topk(int M, int N, int k, const void* ws, size_t ws_bytes, float* lse, int32_t* ids,
-                                float* vals, void* stream) {
+extern "C" int hydra_vocab_topk(int M, int N, int k, const float* Y, const void* ws, size_t ws_bytes, float* lse,
+                                int32_t* ids, float* vals, void* stream) {
   using namespace hydra;
   clear_error();
   HY_CHECK(M >= 0 && N > 0 && k >= 1 && k <= HYDRA_MAX_TOPK && k <= N, HYDRA_ERR_INVALID,
@@ -412,6 +397,7 @@ extern "C" int hydra_vocab_topk(int M, int N, int k, const void* ws, size_t ws_b
   HY_CHECK(ws_bytes >= w.total && (w.total == 0 || ws), HYDRA_ERR_WORKSPACE, "vocab_topk: workspace %zu < %zu",
            ws_bytes, w.total);
   if (M == 0) return HYDRA_OK;
+  HY_CHECK(Y, HYDRA_ERR_INVALID, "vocab_topk: null logits");
   Arena arena(const_cast<void*>(ws), ws_bytes);
   MergeArgs ma{};
   ma.M = M;
@@ -419,6 +405,9 @@ extern "C" int hydra_vocab_topk(int M, int N, int k, const void* ws, size_t ws_b
   ma.k = k;
   ma.keys = arena.take<uint64_t>(w.keys / sizeof(uint64_t));
   ma.ms = arena.take<float2>(w.ms / sizeof(float2));
+  ma.Y = Y;
+  ma.ldy = N;
+  ma.V = N;
   ma.map = RowMap{M, 0, 0};
   ma.lse = lse;
   ma.topk_ids = ids;

@@ -4,115 +4,156 @@
 // tokens) and arg max (section "Parallel Verification and Greedy Acceptance
 // Algorithm"). Ties go to the lower token id.
 //
-// The projection epilogue leaves, for every row and every 64-column
-// workgroup, that workgroup's sorted top-k and (max, sum exp(z - max)); the
-// global top-k of a row is the top-k of the union of those lists. One
-// workgroup per row merges them, then fills the candidate tree: every child
-// that takes its token from this row gets entry rank of the list and the
-// cumulative log-probability of its parent plus z[token] - lse.
+// The projection epilogue leaves, for every row and every 64-column block,
+// the block's largest key and (max, sum exp(z - max)). A workgroup finishes a
+// row: it combines the (max, sum) pairs into the log-sum-exp, picks the k
+// blocks with the largest maxima and takes the top k of their 64 k logits.
+// That is exact: a key in any other block is below its block's maximum,
+// which is below k distinct block maxima, so it cannot rank among the first
+// k. Keys are unique (value, then id), so the order is total. Each selection
+// runs as k rounds of a wave-wide max in every wave, then one wave ranks the
+// waves' winners by counting. The workgroup then fills the candidate tree:
+// every child that takes its token from this row gets entry rank of the list
+// and the cumulative log-probability of its parent plus z[token] - lse.
 #include "common.h"
 
 namespace hydra {
 namespace {
 
-constexpr int kMergeThreads = 256;
-constexpr int kMergeWaves = kMergeThreads / 64;
+constexpr int kMergeWaves = 4;
+constexpr int kMergeThreads = kMergeWaves * 64;
 
-// k-way merge of the per-workgroup lists (each sorted, k entries): thread t
-// owns lists t, t + 256, ... (at most L) and holds them whole in registers;
-// k rounds of a block-wide max over the list heads, the owner of the winning
-// head pops it. No loads happen during the rounds.
-template <int KL, int L>
-__global__ __launch_bounds__(kMergeThreads) void topk_kway_kernel(MergeArgs a) {
-  __shared__ uint64_t s_best[2][kMergeWaves];
-  __shared__ float wm[kMergeWaves], wsum[kMergeWaves];
-  __shared__ uint64_t top[KL];
-  __shared__ float s_lse;
+// k rounds of a wave-wide max over the lanes' sorted lists; lane 0 writes
+// the winners to out[0..k)
+template <int LL>
+__device__ __forceinline__ void wave_top_k(uint64_t (&l)[LL], int k, uint64_t* out, int lane) {
+  for (int j = 0; j < k; ++j) {
+    const uint64_t best = wave_max_u64(l[0]);
+    if (l[0] == best && best != 0) list_pop<LL>(l);
+    if (lane == 0) out[j] = best;
+  }
+}
+
+// wave 0: the k largest of the waves' winner lists cand[0 .. kMergeWaves * k)
+// by rank counting (keys are unique, zero entries are padding). With fewer
+// than k nonzero candidates the remaining entries of top are 0.
+__device__ __forceinline__ void rank_top_k(const uint64_t* cand, int k, uint64_t* top, int lane) {
+  const int n = kMergeWaves * k;  // <= 64
+  const uint64_t mine = lane < n ? cand[lane] : 0;
+  int rank = 0;
+  for (int c = 0; c < n; ++c) rank += cand[c] > mine ? 1 : 0;
+  if (lane < k) top[lane] = 0;  // same wave, so these stores land before the ones below
+  if (lane < n && mine != 0 && rank < k) top[rank] = mine;
+}
+
+// KL: list capacity (>= k); LL: per-thread list of block maxima (holds all of
+// a thread's slots when nwg <= 256 * LL, else LL = KL keeps its top KL)
+template <int KL, int LL>
+__global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(MergeArgs a) {
+  __shared__ uint64_t s_cand[kMergeWaves * KL];
+  __shared__ uint64_t s_top[KL];
+  __shared__ float s_m[kMergeWaves], s_s[kMergeWaves];
   const int i = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int k = a.k;
-  const uint64_t* keys = a.keys + static_cast<size_t>(i) * a.nwg * k;
+  const uint64_t* keys = a.keys + static_cast<size_t>(i) * a.nwg;
   const float2* ms = a.ms + static_cast<size_t>(i) * a.nwg;
 
-  uint64_t lst[L][KL];
-  float2 p[L];
-#pragma unroll
-  for (int j = 0; j < L; ++j) {
-    const int w = tid + j * kMergeThreads;
-    const int wc = w < a.nwg ? w : 0;
-    p[j] = ms[wc];
-#pragma unroll
-    for (int e = 0; e < KL; ++e) lst[j][e] = keys[static_cast<size_t>(wc) * k + (e < k ? e : 0)];
-    if (w >= a.nwg) p[j].x = -INFINITY;
-#pragma unroll
-    for (int e = 0; e < KL; ++e)
-      if (w >= a.nwg || e >= k) lst[j][e] = 0;
-  }
+  // 1. (max, sum exp) of the row; per thread its block maxima, sorted
   float m = -INFINITY, s = 0.f;
+  uint64_t l[LL];
 #pragma unroll
-  for (int j = 0; j < L; ++j) {
-    if (p[j].x == -INFINITY) continue;
-    const float nm = fmaxf(m, p[j].x);
-    s = (m == -INFINITY ? 0.f : s * expf(m - nm)) + p[j].y * expf(p[j].x - nm);
-    m = nm;
+  for (int j = 0; j < LL; ++j) l[j] = 0;
+  for (int w0 = 0; w0 < a.nwg; w0 += kMergeThreads * LL) {
+    uint64_t c[LL];
+    float2 p[LL];
+#pragma unroll
+    for (int j = 0; j < LL; ++j) {
+      const int w = w0 + j * kMergeThreads + tid;
+      const int wc = w < a.nwg ? w : 0;
+      c[j] = keys[wc];
+      p[j] = ms[wc];
+      if (w >= a.nwg) {
+        c[j] = 0;
+        p[j].x = -INFINITY;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < LL; ++j) {
+      ms_combine(m, s, p[j].x, p[j].y);
+      list_insert<LL>(l, c[j]);
+    }
   }
   wave_ms(m, s);
   if (lane == 0) {
-    wm[wave] = m;
-    wsum[wave] = s;
+    s_m[wave] = m;
+    s_s[wave] = s;
   }
-  for (int r = 0; r < k; ++r) {
-    uint64_t best = lst[0][0];
+  // 2. the k largest block maxima
+  wave_top_k<LL>(l, k, s_cand + wave * k, lane);
+  __syncthreads();
+  if (wave == 0) rank_top_k(s_cand, k, s_top, lane);
+  __syncthreads();
+
+  // 3. the top k of those blocks' logits (for k = 1 the largest maximum is it)
+  if (KL > 1 && k > 1) {
+    constexpr int BPW = (KL + kMergeWaves - 1) / kMergeWaves;  // blocks per wave
+    const float* y = a.Y + static_cast<size_t>(a.map(i)) * a.ldy;
+    uint64_t l2[BPW];
 #pragma unroll
-    for (int j = 1; j < L; ++j) best = lst[j][0] > best ? lst[j][0] : best;
-    best = wave_max_u64(best);
-    if (lane == 0) s_best[r & 1][wave] = best;
-    __syncthreads();
-    uint64_t g = s_best[r & 1][0];
+    for (int j = 0; j < BPW; ++j) l2[j] = 0;
+    float v[BPW];
+    int col[BPW];
 #pragma unroll
-    for (int w = 1; w < kMergeWaves; ++w) g = s_best[r & 1][w] > g ? s_best[r & 1][w] : g;
-    if (tid == 0) top[r] = g;
-    // keys are unique, so exactly one list head equals the winner
-#pragma unroll
-    for (int j = 0; j < L; ++j) {
-      if (g != 0 && lst[j][0] == g) {
-#pragma unroll
-        for (int e = 0; e < KL - 1; ++e) lst[j][e] = lst[j][e + 1];
-        lst[j][KL - 1] = 0;
-      }
+    for (int j = 0; j < BPW; ++j) {
+      const int e = wave + j * kMergeWaves;
+      const uint64_t t = s_top[e < k ? e : 0];
+      col[j] = (key_id(t) / kProjRowsPerWG) * kProjRowsPerWG + lane;
+      const bool ok = e < k && t != 0 && col[j] >= 0 && col[j] < a.V;
+      v[j] = y[ok ? col[j] : 0];
+      if (!ok) col[j] = -1;
     }
+#pragma unroll
+    for (int j = 0; j < BPW; ++j)
+      if (col[j] >= 0) list_insert<BPW>(l2, topk_key(v[j], col[j]));
+    wave_top_k<BPW>(l2, k, s_cand + wave * k, lane);
+    __syncthreads();
+    if (wave == 0) rank_top_k(s_cand, k, s_top, lane);
+    __syncthreads();
   }
-  __syncthreads();
-  if (tid == 0) {
-    float M = -INFINITY;
-    for (int w = 0; w < kMergeWaves; ++w) M = fmaxf(M, wm[w]);
-    float S = 0.f;
-    for (int w = 0; w < kMergeWaves; ++w)
-      if (wm[w] != -INFINITY) S += wsum[w] * expf(wm[w] - M);
-    s_lse = M + logf(S);
-    if (a.lse) a.lse[a.map(i)] = s_lse;
-    if (a.amax) a.amax[i] = key_id(top[0]);
+
+  if (wave != 0) return;  // one wave writes the row
+  float M = s_m[0];
+#pragma unroll
+  for (int w = 1; w < kMergeWaves; ++w) M = fmaxf(M, s_m[w]);
+  float S = 0.f;
+#pragma unroll
+  for (int w = 0; w < kMergeWaves; ++w)
+    if (s_m[w] != -INFINITY) S += s_s[w] * expf(s_m[w] - M);
+  const float lse = M + logf(S);
+  if (lane == 0) {
+    if (a.lse) a.lse[a.map(i)] = lse;
+    if (a.amax) a.amax[i] = key_id(s_top[0]);
   }
-  if (tid < k) {
-    if (a.topk_ids) a.topk_ids[static_cast<size_t>(i) * k + tid] = key_id(top[tid]);
-    if (a.topk_vals) a.topk_vals[static_cast<size_t>(i) * k + tid] = key_value(top[tid]);
+  if (lane < k) {
+    const uint64_t mine = s_top[lane];
+    if (a.topk_ids) a.topk_ids[static_cast<size_t>(i) * k + lane] = key_id(mine);
+    if (a.topk_vals) a.topk_vals[static_cast<size_t>(i) * k + lane] = key_value(mine);
   }
-  __syncthreads();
   if (a.node_hi <= a.node_lo) return;
-  const float lse = s_lse;
   const int b = i / a.P;
   const int r = a.r0 + i % a.P;
   const size_t base = static_cast<size_t>(b) * a.N;
-  if (r == 0 && tid == 0) {
+  if (r == 0 && lane == 0) {
     a.cand_tok[base] = a.root_tok[b];
     a.cand_logp[base] = 0.f;
   }
-  for (int c = a.node_lo + tid; c < a.node_hi; c += kMergeThreads) {
+  for (int c = a.node_lo + lane; c < a.node_hi; c += 64) {
     const int pp = a.node_parent[c];
     if (pp < 0 || a.node_row[pp] != r) continue;
     const int rk = a.node_rank[c];
     if (rk < 0 || rk >= k) continue;
-    const uint64_t key = top[rk];
+    const uint64_t key = s_top[rk];
     const float plogp = pp == 0 ? 0.f : a.cand_logp[base + pp];
     a.cand_tok[base + c] = key_id(key);
     a.cand_logp[base + c] = plogp + (key_value(key) - lse);
@@ -120,105 +161,13 @@ __global__ __launch_bounds__(kMergeThreads) void topk_kway_kernel(MergeArgs a) {
 }
 
 template <int KL>
-__global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(MergeArgs a) {
-  constexpr int BATCH = 8;  // keys in flight per thread
-  __shared__ uint64_t wtop[kMergeWaves][KL];
-  __shared__ float wm[kMergeWaves], wsum[kMergeWaves];
-  __shared__ uint64_t top[KL];
-  __shared__ float s_lse;
-  const int i = blockIdx.x;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int k = a.k;
-  const uint64_t* keys = a.keys + static_cast<size_t>(i) * a.nwg * k;
-  const float2* ms = a.ms + static_cast<size_t>(i) * a.nwg;
-
-  float m = -INFINITY, s = 0.f;
-  for (int w0 = 0; w0 < a.nwg; w0 += kMergeThreads * BATCH) {
-    float2 p[BATCH];
-#pragma unroll
-    for (int j = 0; j < BATCH; ++j) {
-      const int w = w0 + j * kMergeThreads + tid;
-      p[j] = ms[w < a.nwg ? w : 0];
-      if (w >= a.nwg) p[j].x = -INFINITY;
-    }
-#pragma unroll
-    for (int j = 0; j < BATCH; ++j) {
-      if (p[j].x == -INFINITY) continue;
-      const float nm = fmaxf(m, p[j].x);
-      s = (m == -INFINITY ? 0.f : s * expf(m - nm)) + p[j].y * expf(p[j].x - nm);
-      m = nm;
-    }
-  }
-  uint64_t l[KL];
-#pragma unroll
-  for (int j = 0; j < KL; ++j) l[j] = 0;
-  const int total = a.nwg * k;
-  for (int e0 = 0; e0 < total; e0 += kMergeThreads * BATCH) {
-    uint64_t c[BATCH];
-#pragma unroll
-    for (int j = 0; j < BATCH; ++j) {
-      const int e = e0 + j * kMergeThreads + tid;
-      c[j] = keys[e < total ? e : 0];
-      if (e >= total) c[j] = 0;
-    }
-#pragma unroll
-    for (int j = 0; j < BATCH; ++j) list_insert<KL>(l, c[j]);
-  }
-
-  wave_ms(m, s);
-  for (int j = 0; j < k; ++j) {
-    const uint64_t best = wave_max_u64(l[0]);
-    if (l[0] == best && best != 0) list_pop<KL>(l);
-    if (lane == 0) wtop[wave][j] = best;
-  }
-  if (lane == 0) {
-    wm[wave] = m;
-    wsum[wave] = s;
-  }
-  __syncthreads();
-  if (wave == 0) {
-    int ptr = 0;
-    for (int j = 0; j < k; ++j) {
-      const uint64_t cand = (lane < kMergeWaves && ptr < k) ? wtop[lane][ptr] : 0;
-      const uint64_t best = wave_max_u64(cand);
-      if (lane < kMergeWaves && cand == best && best != 0) ++ptr;
-      if (lane == 0) top[j] = best;
-    }
-    if (lane == 0) {
-      float M = -INFINITY;
-      for (int w = 0; w < kMergeWaves; ++w) M = fmaxf(M, wm[w]);
-      float S = 0.f;
-      for (int w = 0; w < kMergeWaves; ++w)
-        if (wm[w] != -INFINITY) S += wsum[w] * expf(wm[w] - M);
-      s_lse = M + logf(S);
-      if (a.lse) a.lse[a.map(i)] = s_lse;
-      if (a.amax) a.amax[i] = key_id(top[0]);
-    }
-    if (lane < k) {
-      if (a.topk_ids) a.topk_ids[static_cast<size_t>(i) * k + lane] = key_id(top[lane]);
-      if (a.topk_vals) a.topk_vals[static_cast<size_t>(i) * k + lane] = key_value(top[lane]);
-    }
-  }
-  __syncthreads();
-  if (a.node_hi <= a.node_lo) return;
-  const float lse = s_lse;
-  const int b = i / a.P;
-  const int r = a.r0 + i % a.P;
-  const size_t base = static_cast<size_t>(b) * a.N;
-  if (r == 0 && tid == 0) {
-    a.cand_tok[base] = a.root_tok[b];
-    a.cand_logp[base] = 0.f;
-  }
-  for (int c = a.node_lo + tid; c < a.node_hi; c += kMergeThreads) {
-    const int p = a.node_parent[c];
-    if (p < 0 || a.node_row[p] != r) continue;
-    const int rk = a.node_rank[c];
-    if (rk < 0 || rk >= k) continue;
-    const uint64_t key = top[rk];
-    const float plogp = p == 0 ? 0.f : a.cand_logp[base + p];
-    a.cand_tok[base + c] = key_id(key);
-    a.cand_logp[base + c] = plogp + (key_value(key) - lse);
-  }
+void launch_kl(const MergeArgs& a, hipStream_t stream) {
+  if (a.nwg <= 2 * kMergeThreads)
+    topk_merge_kernel<KL, (KL < 2 ? KL : 2)><<<a.M, kMergeThreads, 0, stream>>>(a);
+  else if (a.nwg <= 4 * kMergeThreads)
+    topk_merge_kernel<KL, (KL < 4 ? KL : 4)><<<a.M, kMergeThreads, 0, stream>>>(a);
+  else
+    topk_merge_kernel<KL, KL><<<a.M, kMergeThreads, 0, stream>>>(a);
 }
 
 }  // namespace
@@ -229,17 +178,14 @@ int launch_topk_merge(const MergeArgs& a, hipStream_t stream) {
     set_error("top-k merge: k=%d out of [1, %d]", a.k, HYDRA_MAX_TOPK);
     return HYDRA_ERR_UNSUPPORTED;
   }
-  if (a.nwg <= 2 * kMergeThreads) {
-    if (a.k == 1) topk_kway_kernel<1, 2><<<a.M, kMergeThreads, 0, stream>>>(a);
-    else if (a.k <= 4) topk_kway_kernel<4, 2><<<a.M, kMergeThreads, 0, stream>>>(a);
-    else topk_kway_kernel<HYDRA_MAX_TOPK, 2><<<a.M, kMergeThreads, 0, stream>>>(a);
-  } else if (a.k == 1) {
-    topk_merge_kernel<1><<<a.M, kMergeThreads, 0, stream>>>(a);
-  } else if (a.k <= 4) {
-    topk_merge_kernel<4><<<a.M, kMergeThreads, 0, stream>>>(a);
-  } else {
-    topk_merge_kernel<HYDRA_MAX_TOPK><<<a.M, kMergeThreads, 0, stream>>>(a);
+  if (a.k > 1 && !a.Y) {
+    set_error("top-k merge: k=%d needs the logits", a.k);
+    return HYDRA_ERR_INVALID;
   }
+  if (a.k == 1) launch_kl<1>(a, stream);
+  else if (a.k <= 4) launch_kl<4>(a, stream);
+  else if (a.k <= 8) launch_kl<8>(a, stream);
+  else launch_kl<HYDRA_MAX_TOPK>(a, stream);
   HY_LAUNCH_CHECK("top-k merge");
   return HYDRA_OK;
 }

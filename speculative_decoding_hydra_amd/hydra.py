@@ -220,10 +220,12 @@ def hydra_vocab_projection(X, W, Y, k=0, ws=None, stream=None):
     return _check("hydra_vocab_projection", rc)
 
 
-def hydra_vocab_topk(M, N, k, ws, lse=None, ids=None, vals=None, stream=None):
-    """Per-row log-sum-exp and sorted top-k from a k > 0 projection's workspace."""
+def hydra_vocab_topk(M, N, k, Y, ws, lse=None, ids=None, vals=None, stream=None):
+    """Per-row log-sum-exp and sorted top-k from a k > 0 projection's logits Y
+    and workspace."""
     wsp, wsb = _ws(ws)
-    rc = lib().hydra_vocab_topk(int(M), int(N), int(k), wsp, wsb, _dev(lse, "lse", torch.float32),
+    rc = lib().hydra_vocab_topk(int(M), int(N), int(k), _dev(Y, "Y", torch.float32), wsp, wsb,
+                                _dev(lse, "lse", torch.float32),
                                 _dev(ids, "ids", torch.int32), _dev(vals, "vals", torch.float32), _stream(stream))
     return _check("hydra_vocab_topk", rc)
 

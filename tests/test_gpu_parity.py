@@ -76,7 +76,7 @@ def test_vocab_topk(dtype, M, K, N, k):
     ids = torch.empty(M, k, dtype=torch.int32, device="cuda")
     vals = torch.empty(M, k, device="cuda")
     hydra_vocab_projection(X.cuda(), W.cuda(), Y, k, ws)
-    hydra_vocab_topk(M, N, k, ws, lse, ids, vals)
+    hydra_vocab_topk(M, N, k, Y, ws, lse, ids, vals)
     torch.cuda.synchronize()
     Yd = Y.cpu().double().numpy()
     ref = HI.as_f64(X) @ HI.as_f64(W).T
@@ -85,6 +85,36 @@ def test_vocab_topk(dtype, M, K, N, k):
         assert np.array_equal(vals[m].cpu().double().numpy(), Yd[m][O.topk_sorted(Yd[m], k)])
         T.check_topk(ref[m], Yd[m], k, ids[m].cpu().numpy(), f"row {m}")
         assert abs(float(lse[m]) - O.logsumexp(Yd[m])) <= 1e-4 * max(1.0, abs(O.logsumexp(Yd[m])))
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("groups,k", [(8, 10), (1, 16), (3, 5)])
+def test_vocab_topk_mass_ties(groups, k):
+    """Every column repeats one of `groups` distinct weight rows, so each row of
+    logits holds only `groups` values, each tied across hundreds of ids: the
+    top k must be the lowest ids carrying the largest value, in id order."""
+    from speculative_decoding_hydra_amd import (hydra_vocab_projection, hydra_vocab_projection_workspace_size,
+                                                hydra_vocab_topk)
+
+    M, K, N = 6, 256, 1000
+    print(f"vocab top-k mass ties groups={groups} k={k}", flush=True)
+    g = torch.Generator().manual_seed(groups * 100 + k)
+    X = torch.randn(M, K, generator=g).to(torch.bfloat16)
+    base = (torch.randn(groups, K, generator=g) * 0.05).to(torch.bfloat16)
+    W = base[torch.arange(N) % groups].contiguous()
+    Y = torch.empty(M, N, device="cuda")
+    ws = torch.empty(hydra_vocab_projection_workspace_size(M, N, k), dtype=torch.uint8, device="cuda")
+    ids = torch.empty(M, k, dtype=torch.int32, device="cuda")
+    hydra_vocab_projection(X.cuda(), W.cuda(), Y, k, ws)
+    hydra_vocab_topk(M, N, k, Y, ws, None, ids, None)
+    torch.cuda.synchronize()
+    Yd = Y.cpu().double().numpy()
+    for m in range(M):
+        assert np.array_equal(ids[m].cpu().numpy(), O.topk_sorted(Yd[m], k)), f"row {m}"
+        first = int(np.argmax(Yd[m][:groups]))
+        top_vals = Yd[m][:groups]
+        if np.sum(top_vals == top_vals[first]) == 1:  # one group holds the maximum
+            assert np.array_equal(ids[m].cpu().numpy(), first + groups * np.arange(k)), f"row {m}"
 
 
 @pytest.mark.parametrize("M,K,N", [(1, 256, 1000), (9, 256, 1000), (7, 100, 33)])

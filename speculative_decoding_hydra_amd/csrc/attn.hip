@@ -9,11 +9,14 @@
 // rows share one pass over the KV prefix.
 //
 // gfx950 design (bf16, D = 128):
-//   * grid = (prefix splits + 1) x (query tiles of 64 rows) x (sequence, KV
-//     head). Query rows of a KV head are (node u, query head g) pairs, so GQA
-//     packs the G query heads into the same tile.
-//   * per 64-key tile, K is staged in LDS row-major and V transposed, both
-//     shared by the 4 waves (16 query rows each);
+//   * grid = (prefix splits + 1) x (query tiles) x (sequence, KV head). Query
+//     rows of a KV head are (node u, query head g) pairs, so GQA packs the G
+//     query heads into the same tile. A workgroup of NW waves holds 16 NW
+//     query rows (one 16-row MFMA tile per wave): with up to 256 rows per
+//     workgroup every tree node of a KV head shares each K/V byte it streams.
+//   * per tile of NW * 16 keys, K is staged in LDS row-major and V
+//     transposed, both shared by all waves; the next tile (the next two for
+//     small workgroups) is in flight in registers while one is consumed;
 //   * S^T = K . Q^T on v_mfma_f32_16x16x32_bf16 puts each query in one lane
 //     column, so the online-softmax statistics need only two cross-lane steps
 //     and the probabilities are already laid out as the B operand of
@@ -25,36 +28,68 @@
 //     their log-sum-exps and rounds the output to bf16.
 #include "common.h"
 
+#include <type_traits>
+
 namespace hydra {
 namespace {
 
-constexpr int kKT = 64;  // keys per tile
 constexpr int kMaxSplitPages = 1024;  // page ids one split stages in LDS
 
 __device__ __forceinline__ uint32_t pack2(uint16_t lo, uint16_t hi) {
   return static_cast<uint32_t>(lo) | (static_cast<uint32_t>(hi) << 16);
 }
 
-template <int D>
-__global__ __launch_bounds__(256) void attn_split_mfma(
+// max / sum over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (one query column
+// of an S^T tile): the gfx950 row swaps hand every lane its partner's value
+// in a VALU step
+__device__ __forceinline__ float col_max(float v) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float col_sum(float v) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// The running offset of a row moves only when a tile's maximum exceeds it by
+// more than this (log2 units): probabilities stay below 2^8, and most tiles
+// skip rescaling the accumulators.
+constexpr float kRescaleSlack = 8.f;
+
+// NW waves of RT 16-row query tiles each (16 NW RT query rows); a thread
+// loads KPT keys x 8 dims of K and V, so a tile holds 4 NW KPT keys; PD tiles
+// in flight. With RT = 2 every K and V^T operand read from LDS feeds two
+// MFMAs. The prefix splits stream whole tiles without any mask and finish
+// with at most one masked tile; the tree split masks every score with the
+// ancestor test.
+template <int NW, int RT, int PD, int KPT>
+__global__ __launch_bounds__(NW * 64, 2) void attn_split_mfma(
     int B, int N, int Hq, int Hkv, float scale_log2, const bf16_t* __restrict__ q,
     const bf16_t* __restrict__ k_tree, const bf16_t* __restrict__ v_tree,
     const bf16_t* __restrict__ k_pages, const bf16_t* __restrict__ v_pages, int n_pages,
-    int page_size, const int32_t* __restrict__ block_table, int max_pages,
+    int page_shift, const int32_t* __restrict__ block_table, int max_pages,
     const int32_t* __restrict__ prefix_len, const int32_t* __restrict__ anc,
     const int32_t* __restrict__ depth, int Dmax, int nsplit, int lsplit, int NQ, int NQpad,
     float* __restrict__ opart, float* __restrict__ mpart, float* __restrict__ lpart) {
-  static_assert(D == 128, "tile mapping assumes D = 128");
-  constexpr int KROW = D + 8;    // K row in LDS (bf16), 16-byte pad
-  constexpr int VROW = kKT + 4;  // V^T row in LDS (bf16), 8-byte pad
+  constexpr int D = 128;
+  constexpr int NT = NW * 64;
+  constexpr int QR = NW * RT * 16;   // query rows per workgroup
+  constexpr int TK = NT / 16 * KPT;  // keys per tile
+  constexpr int KROW = D + 8;        // K row in LDS (bf16), 16-byte pad
+  constexpr int VROW = TK + 4;       // V^T row in LDS (bf16), 8-byte pad
   constexpr int DJ = D / 32;
   constexpr int DD = D / 16;
-  __shared__ __align__(16) bf16_t klds[kKT * KROW];
+  static_assert(TK % 64 == 0, "tiles hold whole 64-key steps");
+  __shared__ __align__(16) bf16_t klds[TK * KROW];
   __shared__ __align__(16) bf16_t vlds[D * VROW];
-  __shared__ bool s_ok[kKT];
-  __shared__ int s_dep[kKT];                              // depth of each tree key of the tile
+  __shared__ __align__(16) uint8_t s_ok[TK];              // key of the tile exists (range and page)
+  __shared__ __align__(16) int s_dep[TK];                 // depth of each tree key of the tile
   __shared__ int s_pages[kMaxSplitPages];                 // page ids of this split
-  __shared__ int s_anc[64][HYDRA_MAX_DEPTH + 1];          // ancestor rows of the 64 query rows
+  __shared__ int s_anc[QR][HYDRA_MAX_DEPTH + 1];          // ancestor rows of the workgroup's query rows
 
   const int split = blockIdx.x;
   const bool tree_part = split == nsplit;
@@ -64,186 +99,207 @@ __global__ __launch_bounds__(256) void attn_split_mfma(
   const int G = Hq / Hkv;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, lq = lane & 15;
+  const int page_size = 1 << page_shift;
 
-  const int qi = qtile * 64 + wave * 16 + lq;
-  const bool qvalid = qi < NQ;
-  const int u = qvalid ? qi / G : 0;
-  const int gq = qi % G;
-  bf16x8_t qreg[DJ];
-  {
+  int wrow[RT];  // this lane's query rows inside the workgroup
+  bf16x8_t qreg[RT][DJ];
+#pragma unroll
+  for (int r = 0; r < RT; ++r) {
+    wrow[r] = (wave * RT + r) * 16 + lq;
+    const int qi = qtile * QR + wrow[r];
+    const bool qvalid = qi < NQ;
+    const int u = qvalid ? qi / G : 0;
+    const int gq = qi % G;
     const bf16_t* qp = q + ((static_cast<size_t>(b) * N + u) * Hq + hkv * G + gq) * D + 8 * g;
 #pragma unroll
     for (int j = 0; j < DJ; ++j) {
       const u32x4_t v = qvalid ? *reinterpret_cast<const u32x4_t*>(qp + 32 * j) : u32x4_t{0u, 0u, 0u, 0u};
-      qreg[j] = __builtin_bit_cast(bf16x8_t, v);
+      qreg[r][j] = __builtin_bit_cast(bf16x8_t, v);
     }
   }
 
   int L = prefix_len[b];
-  const int cap = max_pages * page_size;
+  const int cap = max_pages << page_shift;
   L = L < 0 ? 0 : (L > cap ? cap : L);
-  int t_begin, t_end;
-  if (tree_part) {
-    t_begin = 0;
-    t_end = N;
-  } else {
-    t_begin = split * lsplit;
-    t_end = min(L, t_begin + lsplit);
-  }
+  const int t_begin = tree_part ? 0 : split * lsplit;
+  const int t_end = tree_part ? N : min(L, t_begin + lsplit);
+  const int p0 = t_begin >> page_shift;
   const int32_t* dep_b = depth + static_cast<size_t>(b) * N;
-  const int wrow_q = wave * 16 + lq;  // this lane's query row inside the tile
+  int pages_bad = 0;
   if (tree_part) {
-    for (int e = tid; e < 64 * (Dmax + 1); e += 256) {
-      const int r = e / (Dmax + 1), j = e % (Dmax + 1);
-      const int qr = qtile * 64 + r;
-      s_anc[r][j] = qr < NQ ? anc[(static_cast<size_t>(b) * N + qr / G) * (Dmax + 1) + j] : -1;
+    for (int e = tid; e < QR * (Dmax + 1); e += NT) {
+      const int rr = e / (Dmax + 1), j = e % (Dmax + 1);
+      const int qr = qtile * QR + rr;
+      s_anc[rr][j] = qr < NQ ? anc[(static_cast<size_t>(b) * N + qr / G) * (Dmax + 1) + j] : -1;
     }
   } else {
-    const int p0 = t_begin / page_size;
-    const int np = t_end > t_begin ? (t_end - 1) / page_size - p0 + 1 : 0;
-    for (int e = tid; e < np; e += 256) s_pages[e] = block_table[static_cast<size_t>(b) * max_pages + p0 + e];
+    const int np = t_end > t_begin ? ((t_end - 1) >> page_shift) - p0 + 1 : 0;
+    for (int e = tid; e < np; e += NT) {
+      const int pg = block_table[static_cast<size_t>(b) * max_pages + p0 + e];
+      s_pages[e] = pg;
+      pages_bad |= pg < 0 || pg >= n_pages;
+    }
   }
   __syncthreads();
+  // every page of the split valid: whole tiles then need no mask
+  const bool pages_ok = __syncthreads_or(pages_bad) == 0;
 
-  float m_run = -INFINITY, l_run = 0.f;
-  f32x4_t oacc[DD];
+  float m_run[RT], l_run[RT];
+  f32x4_t oacc[RT][DD];
 #pragma unroll
-  for (int dd = 0; dd < DD; ++dd) oacc[dd] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int r = 0; r < RT; ++r) {
+    m_run[r] = -INFINITY;
+    l_run[r] = 0.f;
+#pragma unroll
+    for (int dd = 0; dd < DD; ++dd) oacc[r][dd] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
 
-  // loader mapping: 4 consecutive keys x 8 dims per thread
-  const int tg = tid >> 4;          // key group 0..15
-  const int dc = tid & 15;          // 8-dim chunk 0..15
-  const int tl = 4 * tg;
+  // loader mapping: KPT consecutive keys (one page, page_size >= 16) x 8 dims
+  const int tg = tid >> 4;  // key group 0 .. NT / 16 - 1
+  const int dc = tid & 15;  // 8-dim chunk 0..15
+  const int tl = KPT * tg;
+  const size_t page_stride = static_cast<size_t>(Hkv) << (page_shift + 7);  // Hkv * page_size * D
+  const size_t head_off = (static_cast<size_t>(hkv) << (page_shift + 7)) + dc * 8;
+  const size_t tree_off = (static_cast<size_t>(b) * N * Hkv + hkv) * D + dc * 8;
 
-  u32x4_t kv[4], vv[4];
-  int kvalid = 0;  // keys of this thread's group of 4 that exist (range and page)
-  // Registers of the next tile: 4 keys x 8 dims of K and of V per thread.
+  u32x4_t kv[PD][KPT], vv[PD][KPT];
+  int kvalid[PD];
+  // Registers of a coming tile: KPT keys x 8 dims of K and of V per thread.
   // Loads are unconditional (invalid keys re-read a valid row and are masked
   // through s_ok), so the compiler can keep them in flight across the tile.
-  auto load_tile = [&](int t0) {
+  auto load_tile = [&](auto SLOT, auto WHOLE, int t0) __attribute__((always_inline)) {
+    constexpr int sl = decltype(SLOT)::value;
+    constexpr bool whole = decltype(WHOLE)::value;
     const int tk = t0 + tl;
-    int valid = tk < t_end ? min(4, t_end - tk) : 0;
     const bf16_t* kb;
     const bf16_t* vb;
-    int stride;
+    size_t stride;
+    int valid = KPT;
+    if (!whole) valid = tk < t_end ? min(KPT, t_end - tk) : 0;
     if (tree_part) {
-      const int tc = tk < N ? tk : 0;
-      const size_t off = ((static_cast<size_t>(b) * N + tc) * Hkv + hkv) * D + dc * 8;
+      const int tc = valid > 0 ? tk : 0;
+      const size_t off = tree_off + static_cast<size_t>(tc) * Hkv * D;
       kb = k_tree + off;
       vb = v_tree + off;
-      stride = Hkv * D;
+      stride = static_cast<size_t>(Hkv) * D;
     } else {
-      const int tc = tk < t_end ? tk : t_begin;
-      int pg = s_pages[tc / page_size - t_begin / page_size];
-      if (pg < 0 || pg >= n_pages) {
+      const int tc = valid > 0 ? tk : t_begin;
+      int pg = s_pages[(tc >> page_shift) - p0];
+      if (!whole && (pg < 0 || pg >= n_pages)) {
         pg = 0;
         valid = 0;
       }
-      const size_t off = ((static_cast<size_t>(pg) * Hkv + hkv) * page_size + tc % page_size) * D + dc * 8;
+      const size_t off = pg * page_stride + head_off + (static_cast<size_t>(tc & (page_size - 1)) << 7);
       kb = k_pages + off;
       vb = v_pages + off;
       stride = D;
     }
-    kvalid = valid;
+    kvalid[sl] = valid;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const size_t o = j < valid ? static_cast<size_t>(j) * stride : 0;
-      kv[j] = *reinterpret_cast<const u32x4_t*>(kb + o);
-      vv[j] = *reinterpret_cast<const u32x4_t*>(vb + o);
+    for (int j = 0; j < KPT; ++j) {
+      const size_t o = whole || j < valid ? j * stride : 0;
+      kv[sl][j] = *reinterpret_cast<const u32x4_t*>(kb + o);
+      vv[sl][j] = *reinterpret_cast<const u32x4_t*>(vb + o);
     }
   };
-  if (t_begin < t_end) load_tile(t_begin);
 
-  for (int t0 = t_begin; t0 < t_end; t0 += kKT) {
-    __syncthreads();  // previous tile fully consumed
-    if (dc == 0) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        s_ok[tl + j] = j < kvalid;
-        if (tree_part) s_dep[tl + j] = j < kvalid ? dep_b[t0 + tl + j] : -1;
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) *reinterpret_cast<u32x4_t*>(&klds[(tl + j) * KROW + dc * 8]) = kv[j];
-    {
-      typedef __attribute__((ext_vector_type(8))) uint16_t u16x8;
-      const u16x8 a0 = __builtin_bit_cast(u16x8, vv[0]);
-      const u16x8 a1 = __builtin_bit_cast(u16x8, vv[1]);
-      const u16x8 a2 = __builtin_bit_cast(u16x8, vv[2]);
-      const u16x8 a3 = __builtin_bit_cast(u16x8, vv[3]);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        u32x2_t w;
-        w.x = pack2(a0[e], a1[e]);
-        w.y = pack2(a2[e], a3[e]);
-        *reinterpret_cast<u32x2_t*>(&vlds[(dc * 8 + e) * VROW + tl]) = w;
-      }
-    }
-    __syncthreads();
-    if (t0 + kKT < t_end) load_tile(t0 + kKT);  // next tile in flight during this one
-
-    // S^T tile: lane holds keys 16 tt + 4 g + i for query column lq
-    f32x4_t sacc[4];
+  // one 64-key step of a staged tile: S^T, online softmax, P.V. MASKED reads
+  // key validity (and in the tree split the ancestor test) per score.
+  auto step = [&](auto MASKED, int c0, int t0) __attribute__((always_inline)) {
+    constexpr bool masked = decltype(MASKED)::value;
+    // S^T tiles: lane holds keys c0 + 16 tt + 4 g + i for query column lq
+    f32x4_t sacc[RT][4];
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) {
-      sacc[tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int r = 0; r < RT; ++r) sacc[r][tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int j = 0; j < DJ; ++j) {
-        const u32x4_t a = *reinterpret_cast<const u32x4_t*>(&klds[(16 * tt + lq) * KROW + 32 * j + 8 * g]);
-        sacc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), qreg[j],
-                                                          sacc[tt], 0, 0, 0);
+        const u32x4_t a = *reinterpret_cast<const u32x4_t*>(&klds[(c0 + 16 * tt + lq) * KROW + 32 * j + 8 * g]);
+#pragma unroll
+        for (int r = 0; r < RT; ++r)
+          sacc[r][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), qreg[r][j],
+                                                               sacc[r][tt], 0, 0, 0);
       }
     }
-    float sv[4][4];
-    float mt = -INFINITY;
+    uint32_t okb[RT];  // bit 4 tt + i: score (tt, i) of row tile r is visible
+    if constexpr (masked) {
+      uint32_t base = 0;
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
+      for (int tt = 0; tt < 4; ++tt) {
+        const uint32_t w = *reinterpret_cast<const uint32_t*>(&s_ok[c0 + 16 * tt + 4 * g]);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int t = t0 + 16 * tt + 4 * g + i;
-        bool ok = s_ok[16 * tt + 4 * g + i];
-        if (tree_part) {
-          const int dv = s_dep[16 * tt + 4 * g + i];
-          ok = ok && dv >= 0 && dv <= Dmax && s_anc[wrow_q][dv] == t;
+        for (int i = 0; i < 4; ++i) base |= ((w >> (8 * i)) & 1u) << (4 * tt + i);
+      }
+#pragma unroll
+      for (int r = 0; r < RT; ++r) okb[r] = base;
+      if (tree_part) {
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+          const int4 d4 = *reinterpret_cast<const int4*>(&s_dep[c0 + 16 * tt + 4 * g]);
+          const int dvs[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int dv = dvs[i];
+            const int dvc = dv < 0 ? 0 : (dv > Dmax ? Dmax : dv);
+#pragma unroll
+            for (int r = 0; r < RT; ++r) {
+              const bool vis = dv == dvc && s_anc[wrow[r]][dvc] == t0 + c0 + 16 * tt + 4 * g + i;
+              okb[r] &= vis ? ~0u : ~(1u << (4 * tt + i));
+            }
+          }
         }
-        const float s = ok ? sacc[tt][i] * scale_log2 : -INFINITY;
-        sv[tt][i] = s;
-        mt = fmaxf(mt, s);
       }
     }
-    mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-    const float m_new = fmaxf(m_run, mt);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = exp2f(m_run - m_use);
-    float ps = 0.f;
+    bf16x8_t pb[RT][2];
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt)
+    for (int r = 0; r < RT; ++r) {
+      // raw scores; the scale (> 0) is folded into the exponent below
+      float mt = -INFINITY;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float p = exp2f(sv[tt][i] - m_use);
-        sv[tt][i] = p;
-        ps += p;
+      for (int tt = 0; tt < 4; ++tt) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if constexpr (masked) sacc[r][tt][i] = (okb[r] >> (4 * tt + i)) & 1u ? sacc[r][tt][i] : -INFINITY;
+          mt = fmaxf(mt, sacc[r][tt][i]);
+        }
       }
-    ps += __shfl_xor(ps, 16, 64);
-    ps += __shfl_xor(ps, 32, 64);
-    l_run = l_run * alpha + ps;
-    m_run = m_new;
+      mt = col_max(mt) * scale_log2;
+      const bool grow = mt > m_run[r] + kRescaleSlack;
+      const float m_new = grow ? fmaxf(m_run[r], mt) : m_run[r];
+      if (__any(grow)) {  // wave-uniform: rescale only when an offset moved
+        const float alpha = m_new == m_run[r] ? 1.f : __builtin_amdgcn_exp2f(m_run[r] - m_new);
+        l_run[r] *= alpha;
 #pragma unroll
-    for (int dd = 0; dd < DD; ++dd) oacc[dd] *= alpha;
-
-    // P^T operands: slots 0..3 = keys 32 ks + 4 g + i, slots 4..7 = keys 32 ks + 16 + 4 g + i
+        for (int dd = 0; dd < DD; ++dd) oacc[r][dd] *= alpha;
+        m_run[r] = m_new;
+      }
+      const float neg_m = m_new == -INFINITY ? 0.f : -m_new;
+      float sv[4][4];
+      float ps = 0.f;
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float pe = __builtin_amdgcn_exp2f(fmaf(sacc[r][tt][i], scale_log2, neg_m));
+          sv[tt][i] = pe;
+          ps += pe;
+        }
+      l_run[r] += col_sum(ps);
+      // P^T operands: slots 0..3 = keys 32 ks + 4 g + i, slots 4..7 = keys 32 ks + 16 + 4 g + i
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          pb[r][ks][i] = static_cast<__bf16>(sv[2 * ks][i]);
+          pb[r][ks][4 + i] = static_cast<__bf16>(sv[2 * ks + 1][i]);
+        }
+    }
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      bf16x8_t pb;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        pb[i] = static_cast<__bf16>(sv[2 * ks][i]);
-        pb[4 + i] = static_cast<__bf16>(sv[2 * ks + 1][i]);
-      }
 #pragma unroll
       for (int dd = 0; dd < DD; ++dd) {
-        const bf16_t* vr = &vlds[(16 * dd + lq) * VROW + 32 * ks + 4 * g];
+        const bf16_t* vr = &vlds[(16 * dd + lq) * VROW + c0 + 32 * ks + 4 * g];
         u32x4_t a;
         const u32x2_t lo = *reinterpret_cast<const u32x2_t*>(vr);
         const u32x2_t hi = *reinterpret_cast<const u32x2_t*>(vr + 16);
@@ -251,33 +307,109 @@ __global__ __launch_bounds__(256) void attn_split_mfma(
         a.y = lo.y;
         a.z = hi.x;
         a.w = hi.y;
-        oacc[dd] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), pb, oacc[dd],
-                                                          0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < RT; ++r)
+          oacc[r][dd] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), pb[r][ks],
+                                                               oacc[r][dd], 0, 0, 0);
       }
     }
+  };
+
+  // one tile: stage slot SLOT in LDS (with the validity / depth bytes unless
+  // WHOLE), refill the slot PD tiles ahead, then its 64-key steps
+  auto process = [&](auto SLOT, auto WHOLE, int t0) __attribute__((always_inline)) {
+    constexpr int sl = decltype(SLOT)::value;
+    constexpr bool whole = decltype(WHOLE)::value;
+    __syncthreads();  // previous tile fully consumed
+    if (!whole && dc == 0) {
+#pragma unroll
+      for (int j = 0; j < KPT; ++j) {
+        s_ok[tl + j] = j < kvalid[sl];
+        if (tree_part) s_dep[tl + j] = j < kvalid[sl] ? dep_b[t0 + tl + j] : -1;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) *reinterpret_cast<u32x4_t*>(&klds[(tl + j) * KROW + dc * 8]) = kv[sl][j];
+    {
+      typedef __attribute__((ext_vector_type(8))) uint16_t u16x8;
+      u16x8 a[KPT];
+#pragma unroll
+      for (int j = 0; j < KPT; ++j) a[j] = __builtin_bit_cast(u16x8, vv[sl][j]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        if constexpr (KPT == 4) {
+          u32x2_t w;
+          w.x = pack2(a[0][e], a[1][e]);
+          w.y = pack2(a[2][e], a[3][e]);
+          *reinterpret_cast<u32x2_t*>(&vlds[(dc * 8 + e) * VROW + tl]) = w;
+        } else {
+          *reinterpret_cast<uint32_t*>(&vlds[(dc * 8 + e) * VROW + tl]) = pack2(a[0][e], a[1][e]);
+        }
+      }
+    }
+    __syncthreads();
+    const int tn = t0 + PD * TK;
+    if (tn < t_end) {
+      // the refill is whole too when it lies entirely inside a clean split
+      if (whole && tn + TK <= t_end) load_tile(SLOT, std::true_type{}, tn);
+      else load_tile(SLOT, std::false_type{}, tn);
+    }
+    for (int c = 0; c < TK / 64; ++c) step(std::integral_constant<bool, !whole>{}, 64 * c, t0);
+  };
+
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, PD - 1>;
+  using Whole = std::true_type;
+  using Part = std::false_type;
+  // whole prefix tiles over valid pages run unmasked in a loop of their own
+  // (pairs of them when two are in flight), the rest masked
+  const int ntiles = t_end > t_begin ? (t_end - t_begin + TK - 1) / TK : 0;
+  const int nwhole = tree_part || !pages_ok ? 0 : (t_end - t_begin) / TK / PD * PD;
+  if (ntiles > 0) {
+    if (nwhole > 0) load_tile(S0{}, Whole{}, t_begin);
+    else load_tile(S0{}, Part{}, t_begin);
+  }
+  if (PD > 1 && ntiles > 1) {
+    if (nwhole > 1) load_tile(S1{}, Whole{}, t_begin + TK);
+    else load_tile(S1{}, Part{}, t_begin + TK);
+  }
+  int it = 0;
+  for (; it < nwhole; it += PD) {
+    process(S0{}, Whole{}, t_begin + it * TK);
+    if (PD > 1) process(S1{}, Whole{}, t_begin + (it + 1) * TK);
+  }
+  for (; it < ntiles; it += PD) {
+    process(S0{}, Part{}, t_begin + it * TK);
+    if (PD > 1 && it + 1 < ntiles) process(S1{}, Part{}, t_begin + (it + 1) * TK);
   }
 
-  if (qvalid) {
-    const size_t row = (static_cast<size_t>(split * B + b) * Hkv + hkv) * NQpad + qi;
 #pragma unroll
-    for (int dd = 0; dd < DD; ++dd)
-      *reinterpret_cast<float4*>(opart + row * D + 16 * dd + 4 * g) =
-          make_float4(oacc[dd][0], oacc[dd][1], oacc[dd][2], oacc[dd][3]);
-    if (g == 0) {
-      mpart[row] = m_run;
-      lpart[row] = l_run;
+  for (int r = 0; r < RT; ++r) {
+    const int qi = qtile * QR + wrow[r];
+    if (qi < NQ) {
+      const size_t row = (static_cast<size_t>(split * B + b) * Hkv + hkv) * NQpad + qi;
+#pragma unroll
+      for (int dd = 0; dd < DD; ++dd)
+        *reinterpret_cast<float4*>(opart + row * D + 16 * dd + 4 * g) =
+            make_float4(oacc[r][dd][0], oacc[r][dd][1], oacc[r][dd][2], oacc[r][dd][3]);
+      if (g == 0) {
+        mpart[row] = m_run[r];
+        lpart[row] = l_run[r];
+      }
     }
   }
 }
 
 // Merge the splits of one (sequence, KV head, query row). D / 4 lanes per row,
-// four dims per lane, so a wave merges 64 * 4 / D rows at once.
+// four dims per lane, so a wave merges 64 * 4 / D rows at once; the parts are
+// read in batches of CB so their loads overlap.
 template <class T>
 __global__ __launch_bounds__(256) void attn_combine(int B, int N, int Hq, int Hkv, int D, int nparts,
                                                     int NQ, int NQpad, const float* __restrict__ opart,
                                                     const float* __restrict__ mpart,
                                                     const float* __restrict__ lpart, T* __restrict__ out,
                                                     float* __restrict__ lse) {
+  constexpr int CB = 8;
   const int lpr = D / 4;  // lanes per row
   const int tid = blockIdx.x * 256 + threadIdx.x;
   const int row = tid / lpr;  // over B * Hkv * NQ
@@ -291,19 +423,36 @@ __global__ __launch_bounds__(256) void attn_combine(int B, int N, int Hq, int Hk
   const size_t stride = static_cast<size_t>(B) * Hkv * NQpad;
   const size_t r0 = (static_cast<size_t>(b) * Hkv + hkv) * NQpad + qi;
   float M = -INFINITY;
-  for (int s = 0; s < nparts; ++s) M = fmaxf(M, mpart[r0 + s * stride]);
+  for (int s0 = 0; s0 < nparts; s0 += CB) {
+    float mv[CB];
+#pragma unroll
+    for (int j = 0; j < CB; ++j) mv[j] = s0 + j < nparts ? mpart[r0 + (s0 + j) * stride] : -INFINITY;
+#pragma unroll
+    for (int j = 0; j < CB; ++j) M = fmaxf(M, mv[j]);
+  }
   const float Mu = M == -INFINITY ? 0.f : M;
   float Lsum = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int s = 0; s < nparts; ++s) {
-    const size_t r = r0 + s * stride;
-    const float w = exp2f(mpart[r] - Mu);
-    Lsum += lpart[r] * w;
-    const float4 o = *reinterpret_cast<const float4*>(opart + r * D + 4 * c);
-    acc.x += o.x * w;
-    acc.y += o.y * w;
-    acc.z += o.z * w;
-    acc.w += o.w * w;
+  for (int s0 = 0; s0 < nparts; s0 += CB) {
+    float mv[CB], lv[CB];
+    float4 ov[CB];
+#pragma unroll
+    for (int j = 0; j < CB; ++j) {
+      const int sp = s0 + j < nparts ? s0 + j : s0;  // past the end: re-read a valid part, weight 0
+      const size_t r = r0 + sp * stride;
+      mv[j] = mpart[r];
+      lv[j] = lpart[r];
+      ov[j] = *reinterpret_cast<const float4*>(opart + r * D + 4 * c);
+    }
+#pragma unroll
+    for (int j = 0; j < CB; ++j) {
+      const float w = s0 + j < nparts ? exp2f(mv[j] - Mu) : 0.f;
+      Lsum += lv[j] * w;
+      acc.x += ov[j].x * w;
+      acc.y += ov[j].y * w;
+      acc.z += ov[j].z * w;
+      acc.w += ov[j].w * w;
+    }
   }
   const float inv = Lsum > 0.f ? 1.0f / Lsum : 0.f;
   T* o = out + ((static_cast<size_t>(b) * N + u) * Hq + hq) * D + 4 * c;
@@ -399,25 +548,34 @@ __global__ __launch_bounds__(64) void attn_simple(int B, int N, int Hq, int Hkv,
 }
 
 struct SplitPlan {
-  int nsplit, lsplit, qtiles, NQ, NQpad;
+  int qr, nsplit, lsplit, qtiles, NQ, NQpad;
 };
 
+// Query rows per workgroup from the query rows of a KV head (up to 256 rows
+// share one K/V stream), then prefix splits: enough workgroups to fill the
+// chip, each split at least four tiles long and short enough that ragged
+// batches balance.
 SplitPlan plan_splits(int B, int N, int Hq, int Hkv, int max_prefix_len) {
   SplitPlan p;
   p.NQ = N * (Hq / Hkv);
-  p.qtiles = (p.NQ + 63) / 64;
-  p.NQpad = p.qtiles * 64;
+  p.qr = p.NQ <= 64 ? 64 : (p.NQ <= 128 ? 128 : 256);
+  const int TK = p.qr == 128 ? 128 : 64;  // keys per tile of the chosen kernel
+  p.qtiles = (p.NQ + p.qr - 1) / p.qr;
+  p.NQpad = p.qtiles * p.qr;
   const int base = B * Hkv * p.qtiles;
   const int Lr = max_prefix_len > 0 ? max_prefix_len : 0;
-  int want = (512 + base - 1) / base;            // workgroups for 256 CUs, twice over
-  int maxs = (Lr + 255) / 256;                   // at least 4 key tiles per split
-  int s = want < maxs ? want : maxs;
+  const int target = p.qr == 64 ? 512 : 256;
+  int s = target / base - 1;  // the tree split takes one slot
+  const int maxs = (Lr + 4 * TK - 1) / (4 * TK);
+  if (s > maxs) s = maxs;
+  const int mins = (Lr + 16 * TK - 1) / (16 * TK);
+  if (s < mins) s = mins;
   if (s < 1) s = 1;
   int ls = (Lr + s - 1) / s;
-  ls = (ls + kKT - 1) / kKT * kKT;
+  ls = (ls + TK - 1) / TK * TK;
   const int lcap = (kMaxSplitPages - 1) * 16;  // pages of a split must fit in LDS (page_size >= 16)
-  if (ls > lcap) ls = lcap / kKT * kKT;
-  if (ls < kKT) ls = kKT;
+  if (ls > lcap) ls = lcap / TK * TK;
+  if (ls < TK) ls = TK;
   p.lsplit = ls;
   p.nsplit = Lr > 0 ? (Lr + ls - 1) / ls : 0;
   return p;
@@ -495,12 +653,17 @@ extern "C" int tree_attention_verify(int dtype, int B, int N, int Hq, int Hkv, i
   float* mpart = arena.take<float>(rows);
   float* lpart = arena.take<float>(rows);
   const float scale_log2 = scale * 1.4426950408889634f;
+  const int page_shift = page_size == 16 ? 4 : (page_size == 32 ? 5 : 6);
   dim3 grid(nparts, p.qtiles, B * Hkv);
-  attn_split_mfma<128><<<grid, 256, 0, stream>>>(
-      B, N, Hq, Hkv, scale_log2, static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k_tree),
-      static_cast<const bf16_t*>(v_tree), static_cast<const bf16_t*>(k_pages), static_cast<const bf16_t*>(v_pages),
-      n_pages, page_size, block_table, max_pages, prefix_len, anc, depth, Dmax, p.nsplit, p.lsplit, p.NQ, p.NQpad,
-      opart, mpart, lpart);
+#define HY_ATTN_ARGS                                                                                           \
+  B, N, Hq, Hkv, scale_log2, static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k_tree),               \
+      static_cast<const bf16_t*>(v_tree), static_cast<const bf16_t*>(k_pages), static_cast<const bf16_t*>(v_pages), \
+      n_pages, page_shift, block_table, max_pages, prefix_len, anc, depth, Dmax, p.nsplit, p.lsplit, p.NQ, p.NQpad, \
+      opart, mpart, lpart
+  if (p.qr == 64) attn_split_mfma<4, 1, 2, 4><<<grid, 256, 0, stream>>>(HY_ATTN_ARGS);
+  else if (p.qr == 128) attn_split_mfma<8, 1, 1, 4><<<grid, 512, 0, stream>>>(HY_ATTN_ARGS);
+  else attn_split_mfma<8, 2, 1, 2><<<grid, 512, 0, stream>>>(HY_ATTN_ARGS);
+#undef HY_ATTN_ARGS
   HY_LAUNCH_CHECK("tree_attention(split)");
   const long long cthreads = static_cast<long long>(B) * Hkv * p.NQ * (D / 4);
   attn_combine<bf16_t><<<static_cast<int>((cthreads + 255) / 256), 256, 0, stream>>>(B, N, Hq, Hkv, D, nparts, p.NQ, p.NQpad, opart, mpart,

@@ -233,13 +233,14 @@ struct RowMap {
 
 // Source of the rows of X: contiguous, or the Hydra head input gathered on the
 // fly as [h_b || E[token]] where b = m / P.
+// Mode 2 (feed-forward kernel only): the embedding row E[token] alone.
 struct XSource {
   const void* x;        // contiguous [M, ldx] (mode 0) or h [B, d] (mode 1)
   int ldx;
-  const void* emb;      // mode 1: [V, d]
-  const int32_t* tok;   // mode 1: cand_tok [B, ntree]
-  const int32_t* root_tok;  // mode 1: [B], the token of node 0
-  const int32_t* row_node;  // mode 1: [R]; node whose token conditions row (b, r0 + m % P)
+  const void* emb;      // modes 1, 2: [V, d]
+  const int32_t* tok;   // modes 1, 2: cand_tok [B, ntree]
+  const int32_t* root_tok;  // modes 1, 2: [B], the token of node 0
+  const int32_t* row_node;  // modes 1, 2: [R]; node whose token conditions row (b, r0 + m % P)
   int ntree, P, r0, d, V;
   int mode;
 };
@@ -283,23 +284,33 @@ struct MergeArgs {
   int32_t* cand_tok;
   float* cand_logp;
 };
-int launch_topk_merge(const MergeArgs& a, hipStream_t stream);
 
-// Fused feed-forward layer of the draft heads for few rows (bf16):
-// U[m] = h[m / P] + SiLU(W1 x_m + b1) rounded to bf16 (or SiLU(...) without
-// the residual), also written to hidden[map(m)] when hidden is set.
+// Feed-forward layer of the draft heads for few rows (bf16), for up to
+// HYDRA_MAX_DEPTH heads at once (blockIdx.y selects the head):
+//   epi 0: A[y][m] = X_m . W[y]^T + b1[y]                  (float32)
+//   epi 1: U[y][m] = h[m / P] + SiLU(X_m . W[y]^T + b1[y])  (bf16)
+//   epi 2: U[m]    = h[m / P] + SiLU(X_m . W[0]^T + A[m / P])
+// (without the residual, SiLU(...) alone); U rows are also written to
+// hidden[map[y](m)] when hidden is set. W[y] points at the first used column
+// of a [d, ldw] matrix and K columns are read.
 struct MlpArgs {
-  int M, K, d;
+  int M, K, d, ldw, heads, epi;
   XSource xs;
-  const bf16_t* W1;
-  const bf16_t* b1;
+  const bf16_t* W[HYDRA_MAX_DEPTH];
+  const bf16_t* b1[HYDRA_MAX_DEPTH];
+  float* A;
   const bf16_t* h;
   int P, residual;
   bf16_t* U;
   bf16_t* hidden;
-  RowMap map;
+  RowMap map[HYDRA_MAX_DEPTH];
 };
 bool mlp_fused_supported(int dtype, int M, int K, int d);
 int launch_mlp_fused(const MlpArgs& a, hipStream_t stream);
+
+// Row merge; with ffn (one head, epi 0, M <= 16 rows) the same launch also
+// runs that feed-forward pass in extra workgroups.
+bool merge_ffn_supported(int M, int K, int d);
+int launch_topk_merge(const MergeArgs& a, hipStream_t stream, const MlpArgs* ffn = nullptr);
 
 }  // namespace hydra

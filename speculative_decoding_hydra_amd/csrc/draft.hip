@@ -8,10 +8,14 @@
 // runs once per expanded node at depth k-1, keeping its top-b_k tokens.
 //
 // Per depth k (sequential: Hydra head k needs the tokens of depth k-1):
-//   1. projection W1 over the gathered rows [h_b || E[token]] (split-K),
-//   2. epilogue: sum of the splits + b1, SiLU, residual, rounded to dtype,
-//   3. projection W2 -> head logits,
-//   4. the W2 epilogue leaves per-workgroup top-k and (max, sum exp) partials;
+//   1. W1 over the rows: with few rows (bf16) the h half of every head's W1
+//      runs once up front for all heads, and depth k streams only the
+//      embedding half, adding the h half, b1, SiLU and the residual in its
+//      epilogue (Medusa heads read h alone, so all their layers run in that
+//      first launch); otherwise a split-K projection over the gathered rows
+//      [h_b || E[token]] and a separate epilogue,
+//   2. projection W2 -> head logits,
+//   3. the W2 epilogue leaves per-block maxima and (max, sum exp) partials;
 //      one workgroup per head row merges them into log-sum-exp and top-k and
 //      fills every child that takes its token from that row.
 #include "common.h"
@@ -55,22 +59,24 @@ using namespace hydra;
 
 namespace {
 struct DraftWs {
-  size_t part, u, keys, ms, total;
+  size_t part, u, a, keys, ms, total;
 };
 DraftWs draft_ws(int dtype, int B, int d, int V, int hydra_mode, int Dmax, const int32_t* row_first,
                  const int32_t* k_per_depth) {
   int maxP = 0;
   for (int k = 1; k <= Dmax; ++k) maxP = std::max(maxP, row_first[k] - row_first[k - 1]);
   const size_t M = static_cast<size_t>(B) * maxP;
+  const size_t MU = std::max(M, static_cast<size_t>(B) * Dmax);  // Medusa keeps every head's u
   const int in_dim = hydra_mode ? 2 * d : d;
   const size_t esz = dtype == HYDRA_F32 ? 4 : 2;
   const size_t nwg = projection_nwg(V);
   DraftWs w;
   w.part = align_up(w1_splits(dtype, in_dim, d) * M * d * sizeof(float), 256);
-  w.u = align_up(M * d * esz, 256);
+  w.u = align_up(MU * d * esz, 256);
+  w.a = align_up(static_cast<size_t>(Dmax) * B * d * sizeof(float), 256);
   w.keys = align_up(M * nwg * sizeof(uint64_t), 256);
   w.ms = align_up(M * nwg * sizeof(float2), 256);
-  w.total = w.part + w.u + w.keys + w.ms + 256;
+  w.total = w.part + w.u + w.a + w.keys + w.ms + 256;
   return w;
 }
 }  // namespace
@@ -123,15 +129,54 @@ extern "C" int hydra_draft_heads(int dtype, int B, int d, int V, int hydra_mode,
   int maxP = 0;
   for (int k = 1; k <= Dmax; ++k) maxP = std::max(maxP, row_first[k] - row_first[k - 1]);
   const size_t Mmax = static_cast<size_t>(B) * maxP;
+  const size_t MU = std::max(Mmax, static_cast<size_t>(B) * Dmax);
   const int in_dim = hydra_mode ? 2 * d : d;
   const int ns = w1_splits(dtype, in_dim, d);
   const size_t esz = dtype == HYDRA_F32 ? 4 : 2;
   const int nwg = projection_nwg(V);
   Arena arena(ws, ws_bytes);
   float* part = arena.take<float>(ns * Mmax * d);
-  char* U = arena.take<char>(Mmax * d * esz);
+  char* U = arena.take<char>(MU * d * esz);
+  float* Ah = arena.take<float>(static_cast<size_t>(Dmax) * B * d);
   uint64_t* tkeys = arena.take<uint64_t>(Mmax * nwg);
   float2* tms = arena.take<float2>(Mmax * nwg);
+
+  // Feed-forward layers. Medusa heads read h alone: with few rows all of
+  // them run in one launch up front. Hydra head k >= 2 splits into the h
+  // half, which runs inside the row merge of depth k - 1 (it does not depend
+  // on that merge), and the embedding half, streamed at depth k. Otherwise
+  // (head 1, many rows, float32) the whole layer runs per depth.
+  const bf16_t* hb = static_cast<const bf16_t*>(h);
+  bool split[HYDRA_MAX_DEPTH + 2] = {};
+  if (hydra_mode)
+    for (int k = 2; k <= Dmax; ++k)
+      split[k] = mlp_fused_supported(dtype, B * (row_first[k] - row_first[k - 1]), d, d) &&
+                 merge_ffn_supported(B, d, d);
+  const bool medusa_once = !hydra_mode && mlp_fused_supported(dtype, B, d, d);
+  if (medusa_once) {
+    MlpArgs pre{};
+    pre.M = B;
+    pre.K = d;
+    pre.d = d;
+    pre.ldw = d;
+    pre.heads = Dmax;
+    pre.epi = 1;
+    pre.xs.x = h;
+    pre.xs.ldx = d;
+    pre.xs.mode = 0;
+    pre.h = hb;
+    pre.P = 1;
+    pre.residual = residual;
+    pre.U = reinterpret_cast<bf16_t*>(U);
+    pre.hidden = static_cast<bf16_t*>(head_hidden);
+    for (int k = 1; k <= Dmax; ++k) {
+      pre.W[k - 1] = static_cast<const bf16_t*>(W1[k - 1]);
+      pre.b1[k - 1] = static_cast<const bf16_t*>(b1[k - 1]);
+      pre.map[k - 1] = RowMap{1, R, row_first[k - 1]};
+    }
+    const int rc = launch_mlp_fused(pre, stream);
+    if (rc != HYDRA_OK) return rc;
+  }
 
   for (int k = 1; k <= Dmax; ++k) {
     const int P = row_first[k] - row_first[k - 1];
@@ -152,51 +197,72 @@ extern "C" int hydra_draft_heads(int dtype, int B, int d, int V, int hydra_mode,
     xs.P = P;
     xs.r0 = r0;
     xs.d = d;
-    if (!hydra_mode) {
-      // Medusa: every row of sequence b is h_b, so M = B rows of h
-      xs.mode = 0;
-    }
-    const int nsk = ns;
     int rc;
-    if (mlp_fused_supported(dtype, M, in_dim, d)) {
-      // 1+2 in one kernel: few rows, the waves of a workgroup split K
-      MlpArgs ma{M, in_dim, d, xs, static_cast<const bf16_t*>(W1[k - 1]), static_cast<const bf16_t*>(b1[k - 1]),
-                 static_cast<const bf16_t*>(h), P, residual, reinterpret_cast<bf16_t*>(U),
-                 static_cast<bf16_t*>(head_hidden), map};
-      rc = launch_mlp_fused(ma, stream);
+    const char* Uk = U;  // rows of this depth's u
+    MlpArgs fa{};
+    fa.M = M;
+    fa.d = d;
+    fa.heads = 1;
+    fa.xs = xs;
+    fa.h = hb;
+    fa.P = P;
+    fa.residual = residual;
+    fa.U = reinterpret_cast<bf16_t*>(U);
+    fa.hidden = static_cast<bf16_t*>(head_hidden);
+    fa.map[0] = map;
+    if (medusa_once) {
+      Uk = U + static_cast<size_t>(k - 1) * B * d * esz;  // written by the all-heads launch
+    } else if (split[k]) {
+      // embedding half; the epilogue adds the h half (with b1), SiLU and the residual
+      fa.K = d;
+      fa.ldw = 2 * d;
+      fa.epi = 2;
+      fa.xs.mode = 2;
+      fa.W[0] = static_cast<const bf16_t*>(W1[k - 1]) + d;
+      fa.A = Ah;
+      rc = launch_mlp_fused(fa, stream);
+      if (rc != HYDRA_OK) return rc;
+    } else if (mlp_fused_supported(dtype, M, in_dim, d)) {
+      // the whole layer: few rows, the waves of a workgroup split K
+      if (!hydra_mode) fa.xs.mode = 0;
+      fa.K = in_dim;
+      fa.ldw = in_dim;
+      fa.epi = 1;
+      fa.W[0] = static_cast<const bf16_t*>(W1[k - 1]);
+      fa.b1[0] = static_cast<const bf16_t*>(b1[k - 1]);
+      rc = launch_mlp_fused(fa, stream);
       if (rc != HYDRA_OK) return rc;
     } else {
+      if (!hydra_mode) xs.mode = 0;  // Medusa: every row of sequence b is h_b (P = 1)
       rc = launch_projection(dtype, M, in_dim, d, xs, W1[k - 1], dtype == HYDRA_F32 ? part : nullptr,
-                             RowMap{M, 0, 0}, d, nsk, dtype == HYDRA_F32 ? nullptr : part,
+                             RowMap{M, 0, 0}, d, ns, dtype == HYDRA_F32 ? nullptr : part,
                              TopkPartials{nullptr, nullptr}, stream);
       if (rc != HYDRA_OK) return rc;
-    }
-    // 2. epilogue: u = h + SiLU(sum + b1)
-    if (!mlp_fused_supported(dtype, M, in_dim, d)) {
+      // epilogue: u = h + SiLU(sum + b1)
       const size_t total = static_cast<size_t>(M) * d;
       const int grid = static_cast<int>(std::min<size_t>((total + 255) / 256, 4096));
-      const int nsum = dtype == HYDRA_F32 ? 1 : nsk;
+      const int nsum = dtype == HYDRA_F32 ? 1 : ns;
       if (dtype == HYDRA_F32) {
         head_mlp_epilogue<float><<<grid, 256, 0, stream>>>(
             M, d, nsum, part, static_cast<const float*>(b1[k - 1]), static_cast<const float*>(h), P, residual,
             reinterpret_cast<float*>(U), static_cast<float*>(head_hidden), map);
       } else {
         head_mlp_epilogue<bf16_t><<<grid, 256, 0, stream>>>(
-            M, d, nsum, part, static_cast<const bf16_t*>(b1[k - 1]), static_cast<const bf16_t*>(h), P,
-            residual, reinterpret_cast<bf16_t*>(U), static_cast<bf16_t*>(head_hidden), map);
+            M, d, nsum, part, static_cast<const bf16_t*>(b1[k - 1]), hb, P, residual,
+            reinterpret_cast<bf16_t*>(U), static_cast<bf16_t*>(head_hidden), map);
       }
       HY_LAUNCH_CHECK("draft_heads: mlp epilogue");
     }
-    // 3. W2: head logits
+    // 2. W2: head logits
     XSource xu{};
-    xu.x = U;
+    xu.x = Uk;
     xu.ldx = d;
     xu.mode = 0;
     const int kk = k_per_depth[k - 1];
     rc = launch_projection(dtype, M, d, V, xu, W2[k - 1], head_logits, map, V, 1, nullptr,
                            TopkPartials{tkeys, tms}, stream);
     if (rc != HYDRA_OK) return rc;
-    // 4. log-sum-exp, top-k, tree fill
+    // 3. log-sum-exp, top-k, tree fill
     MergeArgs ma{};
     ma.M = M;
     ma.nwg = nwg;
@@ -220,7 +286,26 @@ extern "C" int hydra_draft_heads(int dtype, int B, int d, int V, int hydra_mode,
     ma.root_tok = root_tok;
     ma.cand_tok = cand_tok;
     ma.cand_logp = cand_logp;
-    rc = launch_topk_merge(ma, stream);
+    if (k < Dmax && split[k + 1]) {
+      // h half of head k + 1 in the same launch: Ah = W1[:, :d] h + b1
+      MlpArgs hf{};
+      hf.M = B;
+      hf.K = d;
+      hf.d = d;
+      hf.ldw = 2 * d;
+      hf.heads = 1;
+      hf.epi = 0;
+      hf.xs.x = h;
+      hf.xs.ldx = d;
+      hf.xs.mode = 0;
+      hf.W[0] = static_cast<const bf16_t*>(W1[k]);
+      hf.b1[0] = static_cast<const bf16_t*>(b1[k]);
+      hf.A = Ah;
+      hf.P = 1;
+      rc = launch_topk_merge(ma, stream, &hf);
+    } else {
+      rc = launch_topk_merge(ma, stream);
+    }
     if (rc != HYDRA_OK) return rc;
   }
   return HYDRA_OK;

@@ -15,7 +15,7 @@
 // waves' winners by counting. The workgroup then fills the candidate tree:
 // every child that takes its token from this row gets entry rank of the list
 // and the cumulative log-probability of its parent plus z[token] - lse.
-#include "common.h"
+#include "ffn.h"
 
 namespace hydra {
 namespace {
@@ -49,11 +49,10 @@ __device__ __forceinline__ void rank_top_k(const uint64_t* cand, int k, uint64_t
 // KL: list capacity (>= k); LL: per-thread list of block maxima (holds all of
 // a thread's slots when nwg <= 256 * LL, else LL = KL keeps its top KL)
 template <int KL, int LL>
-__global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(MergeArgs a) {
+__device__ __forceinline__ void merge_row(const MergeArgs& a, int i) {
   __shared__ uint64_t s_cand[kMergeWaves * KL];
   __shared__ uint64_t s_top[KL];
   __shared__ float s_m[kMergeWaves], s_s[kMergeWaves];
-  const int i = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int k = a.k;
   const uint64_t* keys = a.keys + static_cast<size_t>(i) * a.nwg;
@@ -160,19 +159,48 @@ __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(MergeArgs a) 
   }
 }
 
+template <int KL, int LL>
+__global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(MergeArgs a) {
+  merge_row<KL, LL>(a, blockIdx.x);
+}
+
+// The same rows, plus the h half of the next Hydra head in workgroups
+// M .. M + d / 16: that feed-forward stream does not depend on this merge, so
+// it fills the otherwise idle chip while the merge runs.
+template <int KL, int LL, int PF>
+__global__ __launch_bounds__(kMergeThreads) void topk_merge_ffn_kernel(MergeArgs a, MlpArgs f) {
+  if (static_cast<int>(blockIdx.x) < a.M) {
+    merge_row<KL, LL>(a, blockIdx.x);
+  } else {
+    mlp_tile<1, PF, kMergeWaves>(f, blockIdx.x - a.M, 0);
+  }
+}
+
+template <int KL, int LL>
+void launch_ll(const MergeArgs& a, const MlpArgs* f, hipStream_t stream) {
+  if (!f) {
+    topk_merge_kernel<KL, LL><<<a.M, kMergeThreads, 0, stream>>>(a);
+  } else if ((f->K / kMergeWaves / 32) % 8 == 0) {
+    topk_merge_ffn_kernel<KL, LL, 8><<<a.M + f->d / 16, kMergeThreads, 0, stream>>>(a, *f);
+  } else {
+    topk_merge_ffn_kernel<KL, LL, 1><<<a.M + f->d / 16, kMergeThreads, 0, stream>>>(a, *f);
+  }
+}
+
 template <int KL>
-void launch_kl(const MergeArgs& a, hipStream_t stream) {
-  if (a.nwg <= 2 * kMergeThreads)
-    topk_merge_kernel<KL, (KL < 2 ? KL : 2)><<<a.M, kMergeThreads, 0, stream>>>(a);
-  else if (a.nwg <= 4 * kMergeThreads)
-    topk_merge_kernel<KL, (KL < 4 ? KL : 4)><<<a.M, kMergeThreads, 0, stream>>>(a);
-  else
-    topk_merge_kernel<KL, KL><<<a.M, kMergeThreads, 0, stream>>>(a);
+void launch_kl(const MergeArgs& a, const MlpArgs* f, hipStream_t stream) {
+  if (a.nwg <= 2 * kMergeThreads) launch_ll<KL, (KL < 2 ? KL : 2)>(a, f, stream);
+  else if (a.nwg <= 4 * kMergeThreads) launch_ll<KL, (KL < 4 ? KL : 4)>(a, f, stream);
+  else launch_ll<KL, KL>(a, f, stream);
 }
 
 }  // namespace
 
-int launch_topk_merge(const MergeArgs& a, hipStream_t stream) {
+bool merge_ffn_supported(int M, int K, int d) {
+  return M >= 1 && M <= 16 && K % (kMergeWaves * 32) == 0 && d % 16 == 0;
+}
+
+int launch_topk_merge(const MergeArgs& a, hipStream_t stream, const MlpArgs* ffn) {
   if (a.M <= 0) return HYDRA_OK;
   if (a.k < 1 || a.k > HYDRA_MAX_TOPK) {
     set_error("top-k merge: k=%d out of [1, %d]", a.k, HYDRA_MAX_TOPK);
@@ -182,10 +210,14 @@ int launch_topk_merge(const MergeArgs& a, hipStream_t stream) {
     set_error("top-k merge: k=%d needs the logits", a.k);
     return HYDRA_ERR_INVALID;
   }
-  if (a.k == 1) launch_kl<1>(a, stream);
-  else if (a.k <= 4) launch_kl<4>(a, stream);
-  else if (a.k <= 8) launch_kl<8>(a, stream);
-  else launch_kl<HYDRA_MAX_TOPK>(a, stream);
+  if (ffn && (ffn->heads != 1 || ffn->epi != 0 || !merge_ffn_supported(ffn->M, ffn->K, ffn->d))) {
+    set_error("top-k merge: unsupported feed-forward work (M=%d K=%d)", ffn->M, ffn->K);
+    return HYDRA_ERR_UNSUPPORTED;
+  }
+  if (a.k == 1) launch_kl<1>(a, ffn, stream);
+  else if (a.k <= 4) launch_kl<4>(a, ffn, stream);
+  else if (a.k <= 8) launch_kl<8>(a, ffn, stream);
+  else launch_kl<HYDRA_MAX_TOPK>(a, ffn, stream);
   HY_LAUNCH_CHECK("top-k merge");
   return HYDRA_OK;
 }

@@ -263,8 +263,7 @@ extern "C" size_t tree_accept_workspace_size(int mode, int B, int N, int V) {
   if (B <= 0 || N <= 0 || V <= 0) return 0;
   const size_t rows = static_cast<size_t>(B) * N;
   if (mode == 0)
-    return align_up(rows * sizeof(int32_t), 256) + align_up(rows * projection_nwg(V) * sizeof(uint64_t), 256) +
-           align_up(rows * projection_nwg(V) * sizeof(float2), 256) + 256;
+    return align_up(rows * sizeof(int32_t), 256) + align_up(rows * projection_nwg(V) * sizeof(uint64_t), 256) + 256;
   return align_up(static_cast<size_t>(B) * 2 * V * sizeof(float), 256) + 256;
 }
 
@@ -304,16 +303,15 @@ extern "C" int tree_accept(int dtype, int mode, int B, int N, int d, int V, int 
     int32_t* amax = arena.take<int32_t>(static_cast<size_t>(M));
     const int nwg = projection_nwg(V);
     uint64_t* keys = arena.take<uint64_t>(static_cast<size_t>(M) * nwg);
-    float2* ms = arena.take<float2>(static_cast<size_t>(M) * nwg);
     int rc = launch_projection(dtype, M, d, V, xs, W_t, target_logits, RowMap{M, 0, 0}, V, 1, nullptr,
-                               TopkPartials{keys, ms}, stream);
+                               TopkPartials{keys, nullptr}, stream);
     if (rc != HYDRA_OK) return rc;
     MergeArgs ma{};
     ma.M = M;
     ma.nwg = nwg;
     ma.k = 1;
     ma.keys = keys;
-    ma.ms = ms;
+    ma.ms = nullptr;  // the greedy walk needs the arg max only
     ma.Y = target_logits;
     ma.ldy = V;
     ma.V = V;

@@ -250,7 +250,7 @@ struct XSource {
 // exp(z - max)) over its columns. keys == nullptr disables it.
 struct TopkPartials {
   uint64_t* keys;  // [M][nwg]
-  float2* ms;      // [M][nwg]
+  float2* ms;      // [M][nwg], or nullptr when no log-sum-exp is wanted
 };
 
 constexpr int kProjRowsPerWG = 64;
@@ -267,7 +267,7 @@ int launch_projection(int dtype, int M, int K, int N, XSource xs, const void* W,
 struct MergeArgs {
   int M, nwg, k;
   const uint64_t* keys;
-  const float2* ms;
+  const float2* ms;     // nullptr: no log-sum-exp (lse must be nullptr too)
   const float* Y;       // logits, row m at Y + map(m) * ldy, V columns
   int ldy, V;
   RowMap map;           // launch row -> output row (logits and head_lse)

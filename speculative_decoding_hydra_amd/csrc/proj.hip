@@ -195,19 +195,19 @@ __global__ __launch_bounds__(64 * WV) void proj_bf16_kernel(ProjArgs a) {
         const uint64_t key = v == -INFINITY ? 0 : topk_key(v, static_cast<int>(blockIdx.x) * RPW + nl);
         best = key > best ? key : best;
       }
-      float s = 0.f;
-#pragma unroll
-      for (int j = 0; j < VPT; ++j) {
-        const float v = tile[mloc * TROW + blk * kProjRowsPerWG + sub + j * TPR];
-        if (v != -INFINITY) s += expf(v - mx);
-      }
       // combine the TPR threads of the row (an aligned lane group of one wave)
-      group_ms<TPR>(mx, s);
       best = group_max_u64<TPR>(best);
-      if (sub == 0) {
-        const size_t slot = static_cast<size_t>(m) * projection_nwg(N) + col0 / kProjRowsPerWG;
-        a.tp.keys[slot] = best;
-        a.tp.ms[slot] = make_float2(mx, s);
+      const size_t slot = static_cast<size_t>(m) * projection_nwg(N) + col0 / kProjRowsPerWG;
+      if (sub == 0) a.tp.keys[slot] = best;
+      if (a.tp.ms) {  // (max, sum exp) only when the row's log-sum-exp is wanted
+        float s = 0.f;
+#pragma unroll
+        for (int j = 0; j < VPT; ++j) {
+          const float v = tile[mloc * TROW + blk * kProjRowsPerWG + sub + j * TPR];
+          if (v != -INFINITY) s += expf(v - mx);
+        }
+        group_ms<TPR>(mx, s);
+        if (sub == 0) a.tp.ms[slot] = make_float2(mx, s);
       }
     }
   }
@@ -258,7 +258,7 @@ __global__ __launch_bounds__(64) void logits_partials(int M, int N, const float*
   if (lane == 0) {
     const size_t slot = static_cast<size_t>(m) * gridDim.x + w;
     tp.keys[slot] = best;
-    tp.ms[slot] = make_float2(mx, s);
+    if (tp.ms) tp.ms[slot] = make_float2(mx, s);
   }
 }
 

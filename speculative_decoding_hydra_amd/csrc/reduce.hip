@@ -56,7 +56,8 @@ __device__ __forceinline__ void merge_row(const MergeArgs& a, int i) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int k = a.k;
   const uint64_t* keys = a.keys + static_cast<size_t>(i) * a.nwg;
-  const float2* ms = a.ms + static_cast<size_t>(i) * a.nwg;
+  const bool want_lse = a.ms != nullptr;
+  const float2* ms = a.ms + (want_lse ? static_cast<size_t>(i) * a.nwg : 0);
 
   // 1. (max, sum exp) of the row; per thread its block maxima, sorted
   float m = -INFINITY, s = 0.f;
@@ -71,7 +72,7 @@ __device__ __forceinline__ void merge_row(const MergeArgs& a, int i) {
       const int w = w0 + j * kMergeThreads + tid;
       const int wc = w < a.nwg ? w : 0;
       c[j] = keys[wc];
-      p[j] = ms[wc];
+      p[j] = want_lse ? ms[wc] : make_float2(-INFINITY, 0.f);
       if (w >= a.nwg) {
         c[j] = 0;
         p[j].x = -INFINITY;
@@ -205,6 +206,10 @@ int launch_topk_merge(const MergeArgs& a, hipStream_t stream, const MlpArgs* ffn
   if (a.k < 1 || a.k > HYDRA_MAX_TOPK) {
     set_error("top-k merge: k=%d out of [1, %d]", a.k, HYDRA_MAX_TOPK);
     return HYDRA_ERR_UNSUPPORTED;
+  }
+  if (!a.ms && (a.lse || a.node_hi > a.node_lo)) {
+    set_error("top-k merge: log-sum-exp and tree fill need the (max, sum exp) partials");
+    return HYDRA_ERR_INVALID;
   }
   if (a.k > 1 && !a.Y) {
     set_error("top-k merge: k=%d needs the logits", a.k);

@@ -260,6 +260,13 @@ int launch_projection(int dtype, int M, int K, int N, XSource xs, const void* W,
                       RowMap map, int ldy, int nsplit, float* part, TopkPartials tp,
                       hipStream_t stream);
 
+// Tiled matrix-core projection for many contiguous rows (bf16, K % 64 == 0),
+// same outputs and partials as launch_projection.
+bool gemm_supported(int K);
+int launch_projection_gemm(int M, int K, int N, const bf16_t* X, int ldx, const bf16_t* W, float* Y, RowMap map,
+                           int ldy, TopkPartials tp, hipStream_t stream);
+constexpr int kGemmMinRows = 160;  // from here on the tiled kernel beats the streaming one
+
 // Finish the fused row reduction: log-sum-exp and sorted top-k of each row,
 // then either the candidate-tree fill (draft heads) or the arg max. The top-k
 // is taken from the finished logits Y of the k blocks with the largest

@@ -1,0 +1,229 @@
+// Vocabulary projection for many rows: Y[m, n] = sum_k X[m, k] * W[n, k].
+//
+// With hundreds of rows (the target projection over every tree row of a
+// 16-sequence batch: M = 1024, 268 GFLOP against 262 MB of W) the projection
+// is bound by the matrix cores, not by HBM ("Parallel Verification and Greedy
+// Acceptance Algorithm" in "Hydra Guide: Sequentially-Dependent Speculative
+// AI": the target scores every tree row in one pass). Design for gfx950:
+//   * a workgroup computes a 256 (n) x 256 (m) tile; its 8 waves hold
+//     128 (n) x 64 (m) each in 32 v_mfma_f32_16x16x32_bf16 accumulators, so
+//     every operand read from LDS feeds 4 or 8 MFMAs;
+//   * K advances in chunks of 64: the next chunk of W and X is loaded from
+//     global memory into registers while the current one is multiplied out
+//     of LDS (two LDS stages, one barrier per chunk);
+//   * workgroups are ordered so that the four m tiles of one n tile run on
+//     the same XCD back to back and share that W tile in its L2;
+//   * the epilogue writes Y and, per row and 64-column block, the largest key
+//     and optionally (max, sum exp), the same partials as the streaming
+//     projection leaves for the row merge.
+#include "common.h"
+
+namespace hydra {
+namespace {
+
+constexpr int GBM = 256, GBN = 256, GBK = 64;
+constexpr int GROW = GBK + 8;  // LDS row (bf16): 144 bytes, so 16 rows spread over the banks
+constexpr int GTHREADS = 512;
+
+struct GemmArgs {
+  int M, K, N, ldx, ldy, mtiles, ntiles;
+  const bf16_t* X;
+  const bf16_t* W;
+  float* Y;
+  RowMap map;
+  TopkPartials tp;
+};
+
+// combine a key over the four lanes l, l ^ 16, l ^ 32, l ^ 48
+__device__ __forceinline__ uint64_t col_max_key(uint64_t v) {
+  auto sw = [](uint64_t x, bool half32) {
+    const uint32_t lo = static_cast<uint32_t>(x), hi = static_cast<uint32_t>(x >> 32);
+    if (half32) {
+      auto a = __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
+      auto b = __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+      const uint64_t p = (static_cast<uint64_t>(b[0]) << 32) | a[0];
+      const uint64_t q = (static_cast<uint64_t>(b[1]) << 32) | a[1];
+      return p > q ? p : q;
+    }
+    auto a = __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
+    auto b = __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
+    const uint64_t p = (static_cast<uint64_t>(b[0]) << 32) | a[0];
+    const uint64_t q = (static_cast<uint64_t>(b[1]) << 32) | a[1];
+    return p > q ? p : q;
+  };
+  return sw(sw(v, false), true);
+}
+
+__device__ __forceinline__ void col_ms(float& m, float& s) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+  auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(s), __float_as_uint(s), false, false);
+  // (a[0], b[0]) and (a[1], b[1]) are this lane's pair and its partner's, in some order
+  float m0 = __uint_as_float(a[0]), s0 = __uint_as_float(b[0]);
+  ms_combine(m0, s0, __uint_as_float(a[1]), __uint_as_float(b[1]));
+  auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(m0), __float_as_uint(m0), false, false);
+  auto d = __builtin_amdgcn_permlane32_swap(__float_as_uint(s0), __float_as_uint(s0), false, false);
+  m = __uint_as_float(c[0]);
+  s = __uint_as_float(d[0]);
+  ms_combine(m, s, __uint_as_float(c[1]), __uint_as_float(d[1]));
+}
+
+__global__ __launch_bounds__(GTHREADS, 2) void proj_gemm_kernel(GemmArgs a) {
+  __shared__ __align__(16) bf16_t wl[2][GBN * GROW];
+  __shared__ __align__(16) bf16_t xl[2][GBM * GROW];
+  // XCD-aware order: workgroup b runs on XCD b % 8; slot s = b / 8 there
+  // covers m tile s % mtiles of n tile (s / mtiles) * 8 + b % 8
+  const int bx = blockIdx.x;
+  const int slot = bx >> 3;
+  const int ntile = (slot / a.mtiles) * 8 + (bx & 7);
+  const int mtile = slot % a.mtiles;
+  if (ntile >= a.ntiles) return;  // whole workgroup: no barrier is pending
+  const int n0 = ntile * GBN, m0 = mtile * GBM;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wn = wave & 1, wm = wave >> 1;  // 2 x 4 waves: 128 n x 64 m each
+
+  // global -> register staging: 4 vectors of 16 bytes of W and of X per thread
+  const bf16_t* wsrc[4];
+  const bf16_t* xsrc[4];
+  int soff[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int idx = tid + j * GTHREADS;
+    const int r = idx >> 3, c = (idx & 7) * 8;
+    const int n = n0 + r < a.N ? n0 + r : a.N - 1;  // rows past the end re-read the last row
+    const int m = m0 + r < a.M ? m0 + r : 0;
+    wsrc[j] = a.W + static_cast<size_t>(n) * a.K + c;
+    xsrc[j] = a.X + static_cast<size_t>(m) * a.ldx + c;
+    soff[j] = r * GROW + c;
+  }
+  u32x4_t wreg[4], xreg[4];
+  auto load = [&](int k0) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      wreg[j] = *reinterpret_cast<const u32x4_t*>(wsrc[j] + k0);
+      xreg[j] = *reinterpret_cast<const u32x4_t*>(xsrc[j] + k0);
+    }
+  };
+  auto store = [&](int st) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      *reinterpret_cast<u32x4_t*>(&wl[st][soff[j]]) = wreg[j];
+      *reinterpret_cast<u32x4_t*>(&xl[st][soff[j]]) = xreg[j];
+    }
+  };
+
+  f32x4_t acc[8][4];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  const int nk = a.K / GBK;
+  load(0);
+  store(0);
+  if (nk > 1) load(GBK);
+  __syncthreads();
+  const int arow = (wn * 128 + (lane & 15)) * GROW + (lane >> 4) * 8;
+  const int brow = (wm * 64 + (lane & 15)) * GROW + (lane >> 4) * 8;
+  for (int c = 0; c < nk; ++c) {
+    const int st = c & 1;
+    if (c + 1 < nk) store(st ^ 1);  // chunk c + 1, loaded one chunk ago
+    if (c + 2 < nk) load((c + 2) * GBK);
+#pragma unroll
+    for (int ks = 0; ks < GBK / 32; ++ks) {
+      bf16x8_t bv[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        bv[j] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(&xl[st][brow + j * 16 * GROW + ks * 32]));
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const bf16x8_t av =
+            __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(&wl[st][arow + i * 16 * GROW + ks * 32]));
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv[j], acc[i][j], 0, 0, 0);
+      }
+    }
+    __syncthreads();
+  }
+
+  // D[n][m]: lane holds n = 16 i + 4 (lane / 16) + e, m = 16 j + lane % 16 of the wave tile
+  const int nb = n0 + wn * 128 + (lane >> 4) * 4;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int m = m0 + wm * 64 + j * 16 + (lane & 15);
+    const bool mok = m < a.M;
+    float* dst = a.Y + static_cast<size_t>(a.map(mok ? m : 0)) * a.ldy;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int n = nb + i * 16;
+      if (!mok) continue;
+      if (n + 3 < a.N && (a.ldy & 3) == 0) {
+        *reinterpret_cast<float4*>(dst + n) = make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (n + e < a.N) dst[n + e] = acc[i][j][e];
+      }
+    }
+    if (!a.tp.keys) continue;
+    // two 64-column blocks per wave: i = 0..3 and 4..7
+#pragma unroll
+    for (int bb = 0; bb < 2; ++bb) {
+      float mx = -INFINITY;
+      uint64_t best = 0;
+#pragma unroll
+      for (int i = 4 * bb; i < 4 * bb + 4; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int n = nb + i * 16 + e;
+          const float v = n < a.N ? acc[i][j][e] : -INFINITY;
+          mx = fmaxf(mx, v);
+          const uint64_t key = n < a.N ? topk_key(v, n) : 0;
+          best = key > best ? key : best;
+        }
+      best = col_max_key(best);
+      const int col0 = n0 + wn * 128 + bb * kProjRowsPerWG;
+      const size_t slot_i = static_cast<size_t>(m) * projection_nwg(a.N) + col0 / kProjRowsPerWG;
+      const bool writer = mok && (lane >> 4) == 0 && col0 < a.N;
+      if (writer) a.tp.keys[slot_i] = best;
+      if (a.tp.ms) {
+        float s = 0.f;
+#pragma unroll
+        for (int i = 4 * bb; i < 4 * bb + 4; ++i)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int n = nb + i * 16 + e;
+            if (n < a.N) s += expf(acc[i][j][e] - mx);
+          }
+        col_ms(mx, s);
+        if (writer) a.tp.ms[slot_i] = make_float2(mx, s);
+      }
+    }
+  }
+}
+
+}  // namespace
+
+bool gemm_supported(int K) { return K % GBK == 0; }
+
+int launch_projection_gemm(int M, int K, int N, const bf16_t* X, int ldx, const bf16_t* W, float* Y, RowMap map,
+                           int ldy, TopkPartials tp, hipStream_t stream) {
+  GemmArgs a{};
+  a.M = M;
+  a.K = K;
+  a.N = N;
+  a.ldx = ldx;
+  a.ldy = ldy;
+  a.mtiles = (M + GBM - 1) / GBM;
+  a.ntiles = (N + GBN - 1) / GBN;
+  a.X = X;
+  a.W = W;
+  a.Y = Y;
+  a.map = map;
+  a.tp = tp;
+  const int slots = (a.ntiles + 7) / 8 * a.mtiles;  // per XCD
+  proj_gemm_kernel<<<slots * 8, GTHREADS, 0, stream>>>(a);
+  HY_LAUNCH_CHECK("projection(gemm)");
+  return HYDRA_OK;
+}
+
+}  // namespace hydra

@@ -5,7 +5,7 @@
 // Mechanics": the Hydra layer reads [h || e(x_parent)].)
 //
 // W1 is [d, in] with d = 4096..8192, while the rows are few (one per expanded
-// node, B * P <= 64). Tiling N in 64-row workgroups leaves too few
+// node, B * P <= 32). Tiling N in 64-row workgroups leaves too few
 // workgroups, and split-K over the grid needs a second pass. Here a
 // workgroup owns 16 rows of W1 and its NWV waves split K: each wave streams
 // its K range of the 16 rows (the MFMA A operand) and reads the matching X
@@ -44,14 +44,14 @@ void launch_mt(const MlpArgs& a, hipStream_t stream) {
 template <int NWV>
 void launch_nwv(const MlpArgs& a, hipStream_t stream) {
   if (a.M <= 16) launch_mt<1, NWV>(a, stream);
-  else if (a.M <= 32) launch_mt<2, NWV>(a, stream);
-  else launch_mt<4, NWV>(a, stream);
+  else launch_mt<2, NWV>(a, stream);
 }
 
 }  // namespace
 
 bool mlp_fused_supported(int dtype, int M, int K, int d) {
-  return dtype == HYDRA_BF16 && M >= 1 && M <= 64 && K % (mlp_waves(K) * 32) == 0 && d % 16 == 0;
+  // beyond 32 rows the per-wave row loads outweigh the weight stream
+  return dtype == HYDRA_BF16 && M >= 1 && M <= 32 && K % (mlp_waves(K) * 32) == 0 && d % 16 == 0;
 }
 
 int launch_mlp_fused(const MlpArgs& a, hipStream_t stream) {

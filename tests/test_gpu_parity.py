@@ -397,14 +397,14 @@ def test_70b_gqa_stochastic_round():
     print(rep, flush=True)
 
 
-@pytest.mark.parametrize("B,d,b1,hydra", [(4, 8192, 10, True), (4, 4096, 10, True), (3, 8192, 13, True),
+@pytest.mark.parametrize("B,d,b1,hydra", [(4, 8192, 10, True), (3, 4096, 10, True), (3, 8192, 13, True),
                                            (2, 256, 16, True), (1, 8192, 16, True), (8, 4096, 10, True),
-                                           (5, 8192, 13, True), (3, 4096, 4, False), (1, 8192, 16, False)])
+                                           (2, 4096, 13, True), (3, 4096, 4, False), (1, 8192, 16, False)])
 def test_draft_first_layer_split_and_fused(B, d, b1, hydra):
     """Head hidden states for row counts on both sides of the few-row kernel
-    (B * b1 <= 64: the h half for all heads, then the embedding half per
-    depth; Medusa: every head in one launch) and the split-K projection
-    path, d up to 8192."""
+    (B * b1 <= 32: head 2's h half runs inside the depth-1 row merge and its
+    embedding half at depth 2; Medusa: every head in one launch) and the
+    split-K projection path (more rows), d up to 8192."""
     w = HI.workload("70b_gqa", B=B, d=d, V=1000, n_heads=2, tree=("cartesian", (b1, 1)), Hq=8, Hkv=8, D=32,
                     L=(64,), mode="greedy", T=1.0, hydra=hydra)
     print(f"first layer B={B} d={d} rows/depth2={B * b1} hydra={hydra}", flush=True)

@@ -14,9 +14,10 @@
 // deterministic, then the epilogue runs before the workgroup ends.
 //
 // The Hydra input splits as W1 [h || e] = W1[:, :d] h + W1[:, d:] e. The h
-// half does not depend on the tree, so the draft runs it for every head in
-// one launch (epi 0, blockIdx.y = head) and each depth then streams only the
-// embedding half (epi 2) before its vocabulary projection.
+// half does not depend on the tree, so the row merge of depth k - 1 runs it
+// for head k in extra workgroups of its launch (epi 0) and depth k streams
+// only the embedding half here (epi 2); Medusa heads read h alone and run all
+// at once (several heads per launch, blockIdx.y = head).
 #include "ffn.h"
 
 namespace hydra {

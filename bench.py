@@ -36,8 +36,8 @@ CAL_BYTES = 256 << 20
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="7b_sparse64")
     ap.add_argument("--no-graph", action="store_true", help="eager launches everywhere (for counter runs)")
     ap.add_argument("--no-cpu", action="store_true")
@@ -170,6 +170,21 @@ def main():
     elapsed = time.perf_counter() - t0
     ms = elapsed / args.steps * 1e3
 
+    # per-round distribution: the same rounds again, each between two events
+    rev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    torch.cuda.synchronize()
+    rev[0].record(stream)
+    for i in range(args.steps):
+        if graph is not None:
+            graph.replay()
+        else:
+            run_round(rnd, dev)
+        rev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    per = sorted(rev[i].elapsed_time(rev[i + 1]) for i in range(args.steps))
+    pick = lambda q: per[min(len(per) - 1, int(q * len(per)))]  # noqa: E731
+    round_ms = {"median": pick(0.5), "p10": pick(0.1), "p90": pick(0.9)}
+
     # per-stage times (eager, events on the launch stream)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
     stage_ms = [0.0] * 4
@@ -268,6 +283,7 @@ def main():
                      "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(),
                      "kernel": "proj_bf16_kernel (vocabulary projection, fused top-k epilogue)",
                      "bytes_per_launch": alg_bytes, "rows": M, "topk": kk, "avg_launch_ms": k_ms},
+        "round_ms": round_ms,
         "stages_ms": {"draft": stage_ms[0], "build": stage_ms[1], "attention": stage_ms[2],
                       "accept": stage_ms[3]},
         "cpu_baseline": cpu,

@@ -22,7 +22,11 @@ namespace hydra {
 namespace {
 
 constexpr int GBM = 256, GBN = 256, GBK = 64;
-constexpr int GROW = GBK + 8;  // LDS row (bf16): 144 bytes, so 16 rows spread over the banks
+// LDS rows are GBK bf16 (128 bytes) with the 16-byte chunk c of row r stored
+// at position c ^ (r % 8): the MFMA operand reads (16 rows at one chunk per
+// 16 lanes) then hit distinct banks, which padded rows do not achieve on gfx950
+constexpr int GROW = GBK;
+__device__ __forceinline__ int swz(int r, int c) { return r * GROW + ((c ^ (r & 7)) << 3); }
 constexpr int GTHREADS = 512;
 
 struct GemmArgs {
@@ -93,7 +97,7 @@ __global__ __launch_bounds__(GTHREADS, 2) void proj_gemm_kernel(GemmArgs a) {
     const int m = m0 + r < a.M ? m0 + r : 0;
     wsrc[j] = a.W + static_cast<size_t>(n) * a.K + c;
     xsrc[j] = a.X + static_cast<size_t>(m) * a.ldx + c;
-    soff[j] = r * GROW + c;
+    soff[j] = swz(r, idx & 7);
   }
   u32x4_t wreg[4], xreg[4];
   auto load = [&](int k0) {
@@ -122,8 +126,9 @@ __global__ __launch_bounds__(GTHREADS, 2) void proj_gemm_kernel(GemmArgs a) {
   store(0);
   if (nk > 1) load(GBK);
   __syncthreads();
-  const int arow = (wn * 128 + (lane & 15)) * GROW + (lane >> 4) * 8;
-  const int brow = (wm * 64 + (lane & 15)) * GROW + (lane >> 4) * 8;
+  // operand rows differ by multiples of 16, so the swizzle depends on the lane alone
+  const int arow = swz(wn * 128 + (lane & 15), lane >> 4), brow = swz(wm * 64 + (lane & 15), lane >> 4);
+  const int ks1 = ((4 ^ ((lane >> 4) ^ (lane & 7))) - ((lane >> 4) ^ (lane & 7))) * 8;  // k step 1 minus k step 0
   for (int c = 0; c < nk; ++c) {
     const int st = c & 1;
     if (c + 1 < nk) store(st ^ 1);  // chunk c + 1, loaded one chunk ago
@@ -133,11 +138,11 @@ __global__ __launch_bounds__(GTHREADS, 2) void proj_gemm_kernel(GemmArgs a) {
       bf16x8_t bv[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        bv[j] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(&xl[st][brow + j * 16 * GROW + ks * 32]));
+        bv[j] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(&xl[st][brow + j * 16 * GROW + ks * ks1]));
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const bf16x8_t av =
-            __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(&wl[st][arow + i * 16 * GROW + ks * 32]));
+            __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(&wl[st][arow + i * 16 * GROW + ks * ks1]));
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv[j], acc[i][j], 0, 0, 0);
       }

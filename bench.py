@@ -1,12 +1,14 @@
 """Throughput of one Hydra draft-and-verify round on one MI355X.
 
-python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-graph] [--no-cpu]
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-graph] [--no-cpu] [--no-fold]
 
 A step is one whole round (draft heads -> tree build -> tree-attention verify
 -> accept) over the workload's synthetic batch, with every input resident in
 HBM before timing starts. The default workload is the Vicuna-7B-shaped layer
 with the 64-node sparse tree and a 2048-token prefix (batch 1). The value is
-verified tree rows per second, B * N / t_round.
+verified tree rows per second, B * N / t_round. Hydra heads use their folded
+embedding tables (built once before timing; --no-fold streams W1[:, d:]
+every round instead).
 
 The JSON line also carries
   roofline      the dominant kernel (the head/target vocabulary projection
@@ -42,6 +44,8 @@ def parse():
     ap.add_argument("--no-graph", action="store_true", help="eager launches everywhere (for counter runs)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--kernel-reps", type=int, default=20)
+    ap.add_argument("--no-fold", action="store_true",
+                    help="stream W1[:, d:] every round instead of the folded embedding tables")
     return ap.parse_args()
 
 
@@ -129,7 +133,8 @@ def main():
     w = HI.workload(args.workload)
     log(f"[bench] generating {w.name}")
     inp = HI.generate(w)
-    rnd, dev = round_from_inputs(inp, device="cuda:0", keep_hidden=False)
+    rnd, dev = round_from_inputs(inp, device="cuda:0", keep_hidden=False,
+                                 fold_embedding=False if args.no_fold else None)
     N = rnd.n_keep
     rows = w.B * N
     stream = torch.cuda.current_stream()
@@ -278,7 +283,9 @@ def main():
         "config": {"workload": w.name, "batch": w.B, "tree_rows": N, "hidden": w.d, "vocab": w.V,
                    "heads": w.n_heads, "q_heads": w.Hq, "kv_heads": w.Hkv, "head_dim": w.D,
                    "prefix": list(w.L), "tree": str(w.tree[0]), "acceptance": w.mode,
-                   "launch": "hip-graph" if graph is not None else "eager"},
+                   "launch": "hip-graph" if graph is not None else "eager",
+                   "embedding_half": ("folded table" if rnd.emb_proj is not None else "streamed")
+                   if w.hydra else None},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(),
                      "kernel": "proj_bf16_kernel (vocabulary projection, fused top-k epilogue)",

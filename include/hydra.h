@@ -132,6 +132,13 @@ int hydra_plan_rows(int N, const int32_t* parent, const int32_t* rank,
  * h            [B, d]
  * root_tok     [B] int32, token of the root of each tree
  * emb          [V, d] embedding table (Hydra); ignored (may be NULL) for Medusa
+ * emb_proj     NULL, or (Hydra, bf16) a host array of n_heads device pointers
+ *              to float32 [V, d] tables from hydra_fold_embedding: table k-1
+ *              holds W1_k[:, d:] E^T, the embedding half of head k's layer for
+ *              every token. With them the embedding half is a row lookup
+ *              instead of a pass over W1_k[:, d:] (the same sum, as the layer
+ *              is linear in e), used when d % 1024 == 0 and B <= 16; otherwise
+ *              the tables are ignored.
  * n_heads      entries in W1/b1/W2 (>= Dmax)
  * W1, b1, W2   host arrays of n_heads device pointers: W1_k [d, in] (in = 2d
  *              Hydra, d Medusa), b1_k [d], W2_k [V, d]; head k at index k-1
@@ -151,7 +158,7 @@ size_t hydra_draft_heads_workspace_size(int dtype, int B, int d, int V, int hydr
 
 int hydra_draft_heads(int dtype, int B, int d, int V, int hydra, int residual,
                       const void* h, const int32_t* root_tok, const void* emb,
-                      int n_heads, const void* const* W1, const void* const* b1,
+                      const float* const* emb_proj, int n_heads, const void* const* W1, const void* const* b1,
                       const void* const* W2, int N, int Dmax,
                       const int32_t* node_parent, const int32_t* node_rank,
                       const int32_t* node_row, int R, const int32_t* row_node,
@@ -159,6 +166,17 @@ int hydra_draft_heads(int dtype, int B, int d, int V, int hydra, int residual,
                       const int32_t* k_per_depth, float* head_logits, float* head_lse,
                       void* head_hidden, int32_t* cand_tok, float* cand_logp,
                       void* ws, size_t ws_bytes, void* stream);
+
+/* Folded embedding table of one Hydra head, computed once per weight set:
+ * out[t, n] = sum_j W1[n, d + j] * emb[t, j] for every token t, with W1 the
+ * head's [d, 2d] first-layer weight ([HG] "1. Embedding Conditioning
+ * Mechanics": the layer reads [h || e(x_parent)], so its e half depends on
+ * the token alone). bf16 emb [V, d] and W1, float32 out [V, d] (caller-owned,
+ * V * d * 4 bytes), float32 accumulation; needs d % 64 == 0. Errors:
+ * HYDRA_ERR_UNSUPPORTED for float32 or other d, HYDRA_ERR_INVALID for bad
+ * sizes or NULL pointers. */
+int hydra_fold_embedding(int dtype, int V, int d, const void* emb, const void* W1, float* out,
+                         void* stream);
 
 /* Vocabulary projection used by the heads and the target:
  * Y[m, n] = sum_k X[m, k] * W[n, k], float32 accumulation and output.

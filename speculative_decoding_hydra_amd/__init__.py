@@ -6,7 +6,7 @@ buffers of a round and calls them in order.
 """
 from .hydra import (  # noqa: F401
     DevicePlan, HydraError, PlanRows, TreePlan, hydra_draft_heads, hydra_draft_heads_workspace_size,
-    hydra_plan_cartesian, hydra_plan_rows, hydra_plan_sparse, hydra_vocab_projection,
+    hydra_fold_embedding, hydra_plan_cartesian, hydra_plan_rows, hydra_plan_sparse, hydra_vocab_projection,
     hydra_vocab_projection_workspace_size, hydra_vocab_topk, tree_accept,
     tree_accept_workspace_size, tree_attention_verify, tree_attention_verify_workspace_size, tree_build,
     tree_build_workspace_size,

@@ -261,10 +261,11 @@ int launch_projection(int dtype, int M, int K, int N, XSource xs, const void* W,
                       hipStream_t stream);
 
 // Tiled matrix-core projection for many contiguous rows (bf16, K % 64 == 0),
-// same outputs and partials as launch_projection.
+// same outputs and partials as launch_projection; row n of W starts at
+// W + n * ldw.
 bool gemm_supported(int K);
-int launch_projection_gemm(int M, int K, int N, const bf16_t* X, int ldx, const bf16_t* W, float* Y, RowMap map,
-                           int ldy, TopkPartials tp, hipStream_t stream);
+int launch_projection_gemm(int M, int K, int N, const bf16_t* X, int ldx, const bf16_t* W, int ldw, float* Y,
+                           RowMap map, int ldy, TopkPartials tp, hipStream_t stream);
 constexpr int kGemmMinRows = 160;  // from here on the tiled kernel beats the streaming one
 
 // Finish the fused row reduction: log-sum-exp and sorted top-k of each row,
@@ -290,21 +291,37 @@ struct MergeArgs {
   const int32_t* root_tok;
   int32_t* cand_tok;
   float* cand_logp;
+  // Hydra feed-forward rows of the next depth from the folded embedding
+  // table: every filled child c with node_row[c] >= 0 gets
+  //   u = h[b] + SiLU(Anext[b] + Enext[token of c])  (SiLU(...) alone without
+  // the residual), stored as bf16 in U[b * Pn + node_row[c] - rn] and
+  // hidden[b * R + node_row[c]]. Enext == nullptr disables it; needs d % 1024 == 0.
+  const float* Enext;   // [V][d]
+  const float* Anext;   // [B][d], b1 included
+  const bf16_t* h;      // [B][d]
+  bf16_t* U;
+  bf16_t* hidden;       // or nullptr
+  int d, R, rn, Pn, residual;
+  int ng;               // workgroups per row (set by the launcher)
 };
 
 // Feed-forward layer of the draft heads for few rows (bf16), for up to
-// HYDRA_MAX_DEPTH heads at once (blockIdx.y selects the head):
+// HYDRA_MAX_DEPTH heads at once (blockIdx.y selects the head), with b = m / P:
 //   epi 0: A[y][m] = X_m . W[y]^T + b1[y]                  (float32)
-//   epi 1: U[y][m] = h[m / P] + SiLU(X_m . W[y]^T + b1[y])  (bf16)
-//   epi 2: U[m]    = h[m / P] + SiLU(X_m . W[0]^T + A[m / P])
+//   epi 1: U[y][m] = h[b] + SiLU(X_m . W[y]^T + b1[y])      (bf16)
+//   epi 2: U[m]    = h[b] + SiLU(X_m . W[0]^T + A[b])
+//   epi 3: U[y][m] = h[b] + SiLU(X_m . W[y]^T + b1[y] + Ef[y][etok[b]])
 // (without the residual, SiLU(...) alone); U rows are also written to
 // hidden[map[y](m)] when hidden is set. W[y] points at the first used column
 // of a [d, ldw] matrix and K columns are read.
 struct MlpArgs {
-  int M, K, d, ldw, heads, epi;
+  int M, K, d, ldw, heads;
+  int epi[HYDRA_MAX_DEPTH];
   XSource xs;
   const bf16_t* W[HYDRA_MAX_DEPTH];
   const bf16_t* b1[HYDRA_MAX_DEPTH];
+  const float* Ef[HYDRA_MAX_DEPTH];  // epi 3: folded embedding table [V][d]
+  const int32_t* etok;               // epi 3: token of sequence b (clamped to [0, xs.V))
   float* A;
   const bf16_t* h;
   int P, residual;

@@ -89,7 +89,7 @@ extern "C" size_t hydra_draft_heads_workspace_size(int dtype, int B, int d, int 
 
 extern "C" int hydra_draft_heads(int dtype, int B, int d, int V, int hydra_mode, int residual,
                                  const void* h, const int32_t* root_tok, const void* emb,
-                                 int n_heads, const void* const* W1, const void* const* b1,
+                                 const float* const* emb_proj, int n_heads, const void* const* W1, const void* const* b1,
                                  const void* const* W2, int N, int Dmax,
                                  const int32_t* node_parent, const int32_t* node_rank,
                                  const int32_t* node_row, int R, const int32_t* row_node,
@@ -147,8 +147,50 @@ extern "C" int hydra_draft_heads(int dtype, int B, int d, int V, int hydra_mode,
   // on that merge), and the embedding half, streamed at depth k. Otherwise
   // (head 1, many rows, float32) the whole layer runs per depth.
   const bf16_t* hb = static_cast<const bf16_t*>(h);
+  // Folded embedding tables (Hydra, bf16, B <= 16): the embedding half of
+  // head k's layer, W1[:, d:] e(token), is row `token` of emb_proj[k - 1],
+  // so no depth streams W1[:, d:]. One launch up front runs head 1 (its h
+  // half plus the root token's table row) and the h half of head 2 (slot 1
+  // of Ah); the row merge of depth k then writes the rows of depth k + 1
+  // from the tokens it picks, while its extra workgroups stream the h half of
+  // head k + 2 into slot k + 1.
+  const bool folded = hydra_mode && emb_proj && dtype == HYDRA_BF16 && d % 1024 == 0 &&
+                      mlp_fused_supported(dtype, B, d, d) && merge_ffn_supported(B, d, d);
+  if (folded) {
+    for (int k = 1; k <= Dmax; ++k)
+      HY_CHECK(emb_proj[k - 1], HYDRA_ERR_INVALID, "draft_heads: null folded embedding table of head %d", k);
+    MlpArgs pre{};
+    pre.M = B;
+    pre.K = d;
+    pre.d = d;
+    pre.ldw = 2 * d;
+    pre.heads = Dmax >= 2 ? 2 : 1;
+    pre.xs.x = h;
+    pre.xs.ldx = d;
+    pre.xs.mode = 0;
+    pre.xs.V = V;
+    pre.epi[0] = 3;
+    pre.W[0] = static_cast<const bf16_t*>(W1[0]);
+    pre.b1[0] = static_cast<const bf16_t*>(b1[0]);
+    pre.Ef[0] = emb_proj[0];
+    pre.etok = root_tok;
+    pre.map[0] = RowMap{1, R, 0};
+    if (Dmax >= 2) {
+      pre.epi[1] = 0;
+      pre.W[1] = static_cast<const bf16_t*>(W1[1]);
+      pre.b1[1] = static_cast<const bf16_t*>(b1[1]);
+    }
+    pre.A = Ah;
+    pre.h = hb;
+    pre.P = 1;
+    pre.residual = residual;
+    pre.U = reinterpret_cast<bf16_t*>(U);
+    pre.hidden = static_cast<bf16_t*>(head_hidden);
+    const int rc = launch_mlp_fused(pre, stream);
+    if (rc != HYDRA_OK) return rc;
+  }
   bool split[HYDRA_MAX_DEPTH + 2] = {};
-  if (hydra_mode)
+  if (hydra_mode && !folded)
     for (int k = 2; k <= Dmax; ++k)
       split[k] = mlp_fused_supported(dtype, B * (row_first[k] - row_first[k - 1]), d, d) &&
                  merge_ffn_supported(B, d, d);
@@ -160,7 +202,6 @@ extern "C" int hydra_draft_heads(int dtype, int B, int d, int V, int hydra_mode,
     pre.d = d;
     pre.ldw = d;
     pre.heads = Dmax;
-    pre.epi = 1;
     pre.xs.x = h;
     pre.xs.ldx = d;
     pre.xs.mode = 0;
@@ -170,6 +211,7 @@ extern "C" int hydra_draft_heads(int dtype, int B, int d, int V, int hydra_mode,
     pre.U = reinterpret_cast<bf16_t*>(U);
     pre.hidden = static_cast<bf16_t*>(head_hidden);
     for (int k = 1; k <= Dmax; ++k) {
+      pre.epi[k - 1] = 1;
       pre.W[k - 1] = static_cast<const bf16_t*>(W1[k - 1]);
       pre.b1[k - 1] = static_cast<const bf16_t*>(b1[k - 1]);
       pre.map[k - 1] = RowMap{1, R, row_first[k - 1]};
@@ -212,11 +254,13 @@ extern "C" int hydra_draft_heads(int dtype, int B, int d, int V, int hydra_mode,
     fa.map[0] = map;
     if (medusa_once) {
       Uk = U + static_cast<size_t>(k - 1) * B * d * esz;  // written by the all-heads launch
+    } else if (folded) {
+      // rows written by the launch up front (k = 1) or the previous merge
     } else if (split[k]) {
       // embedding half; the epilogue adds the h half (with b1), SiLU and the residual
       fa.K = d;
       fa.ldw = 2 * d;
-      fa.epi = 2;
+      fa.epi[0] = 2;
       fa.xs.mode = 2;
       fa.W[0] = static_cast<const bf16_t*>(W1[k - 1]) + d;
       fa.A = Ah;
@@ -227,7 +271,7 @@ extern "C" int hydra_draft_heads(int dtype, int B, int d, int V, int hydra_mode,
       if (!hydra_mode) fa.xs.mode = 0;
       fa.K = in_dim;
       fa.ldw = in_dim;
-      fa.epi = 1;
+      fa.epi[0] = 1;
       fa.W[0] = static_cast<const bf16_t*>(W1[k - 1]);
       fa.b1[0] = static_cast<const bf16_t*>(b1[k - 1]);
       rc = launch_mlp_fused(fa, stream);
@@ -286,7 +330,35 @@ extern "C" int hydra_draft_heads(int dtype, int B, int d, int V, int hydra_mode,
     ma.root_tok = root_tok;
     ma.cand_tok = cand_tok;
     ma.cand_logp = cand_logp;
-    if (k < Dmax && split[k + 1]) {
+    if (folded && k < Dmax) {
+      ma.Enext = emb_proj[k];
+      ma.Anext = Ah + static_cast<size_t>(k) * B * d;
+      ma.h = hb;
+      ma.U = reinterpret_cast<bf16_t*>(U);
+      ma.hidden = static_cast<bf16_t*>(head_hidden);
+      ma.d = d;
+      ma.R = R;
+      ma.rn = row_first[k];
+      ma.Pn = row_first[k + 1] - row_first[k];
+      ma.residual = residual;
+    }
+    if (folded && k + 2 <= Dmax) {
+      // h half of head k + 2 in the same launch, into slot k + 1 of Ah
+      MlpArgs hf{};
+      hf.M = B;
+      hf.K = d;
+      hf.d = d;
+      hf.ldw = 2 * d;
+      hf.heads = 1;
+      hf.xs.x = h;
+      hf.xs.ldx = d;
+      hf.xs.mode = 0;
+      hf.W[0] = static_cast<const bf16_t*>(W1[k + 1]);
+      hf.b1[0] = static_cast<const bf16_t*>(b1[k + 1]);
+      hf.A = Ah + static_cast<size_t>(k + 1) * B * d;
+      hf.P = 1;
+      rc = launch_topk_merge(ma, stream, &hf);
+    } else if (!folded && k < Dmax && split[k + 1]) {
       // h half of head k + 1 in the same launch: Ah = W1[:, :d] h + b1
       MlpArgs hf{};
       hf.M = B;
@@ -294,7 +366,6 @@ extern "C" int hydra_draft_heads(int dtype, int B, int d, int V, int hydra_mode,
       hf.d = d;
       hf.ldw = 2 * d;
       hf.heads = 1;
-      hf.epi = 0;
       hf.xs.x = h;
       hf.xs.ldx = d;
       hf.xs.mode = 0;
@@ -309,4 +380,18 @@ extern "C" int hydra_draft_heads(int dtype, int B, int d, int V, int hydra_mode,
     if (rc != HYDRA_OK) return rc;
   }
   return HYDRA_OK;
+}
+
+extern "C" int hydra_fold_embedding(int dtype, int V, int d, const void* emb, const void* W1, float* out,
+                                    void* stream_) {
+  clear_error();
+  HY_CHECK(dtype == HYDRA_BF16, HYDRA_ERR_UNSUPPORTED, "fold_embedding: bf16 only (dtype %d)", dtype);
+  HY_CHECK(V > 0 && d > 0, HYDRA_ERR_INVALID, "fold_embedding: bad sizes V=%d d=%d", V, d);
+  HY_CHECK(emb && W1 && out, HYDRA_ERR_INVALID, "fold_embedding: null pointer");
+  HY_CHECK(gemm_supported(d), HYDRA_ERR_UNSUPPORTED, "fold_embedding: needs d %% 64 == 0 (d=%d)", d);
+  // out[t][n] = sum_j W1[n][d + j] * emb[t][j]: the embedding half of the
+  // Hydra layer for every token, one tiled product
+  return launch_projection_gemm(V, d, d, static_cast<const bf16_t*>(emb), d, static_cast<const bf16_t*>(W1) + d,
+                                2 * d, out, RowMap{V, 0, 0}, d, TopkPartials{nullptr, nullptr},
+                                static_cast<hipStream_t>(stream_));
 }

@@ -78,6 +78,7 @@ __device__ __forceinline__ void mlp_tile(const MlpArgs& a, int tile, int y) {
   if (wave != 0) return;
   // D[n][m]: lane holds n = n0 + 4 * (lane / 16) + i, m = 16 t + lane % 16
   const int nb = n0 + (lane >> 4) * 4;
+  const int epi = a.epi[y];
 #pragma unroll
   for (int t = 0; t < MT; ++t) {
     f32x4_t sum = red[0][t][lane];
@@ -86,7 +87,7 @@ __device__ __forceinline__ void mlp_tile(const MlpArgs& a, int tile, int y) {
     const int m = t * 16 + (lane & 15);
     if (m >= a.M) continue;
     const int b = m / a.P;
-    if (a.epi == 0) {
+    if (epi == 0) {
       float4 o;
       o.x = sum[0] + bf16_to_f32(a.b1[y][nb + 0]);
       o.y = sum[1] + bf16_to_f32(a.b1[y][nb + 1]);
@@ -96,11 +97,20 @@ __device__ __forceinline__ void mlp_tile(const MlpArgs& a, int tile, int y) {
       continue;
     }
     float4 add;
-    if (a.epi == 2) {
+    if (epi == 2) {
       add = *reinterpret_cast<const float4*>(a.A + static_cast<size_t>(b) * a.d + nb);
     } else {
       add = make_float4(bf16_to_f32(a.b1[y][nb + 0]), bf16_to_f32(a.b1[y][nb + 1]), bf16_to_f32(a.b1[y][nb + 2]),
                         bf16_to_f32(a.b1[y][nb + 3]));
+      if (epi == 3) {  // + the folded embedding half W1[:, d:] e(token)
+        int tk = a.etok[b];
+        tk = tk < 0 ? 0 : (tk >= a.xs.V ? a.xs.V - 1 : tk);
+        const float4 e = *reinterpret_cast<const float4*>(a.Ef[y] + static_cast<size_t>(tk) * a.d + nb);
+        add.x += e.x;
+        add.y += e.y;
+        add.z += e.z;
+        add.w += e.w;
+      }
     }
     const float addv[4] = {add.x, add.y, add.z, add.w};
     bf16_t out[4];

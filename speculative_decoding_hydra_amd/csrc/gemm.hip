@@ -30,7 +30,7 @@ __device__ __forceinline__ int swz(int r, int c) { return r * GROW + ((c ^ (r & 
 constexpr int GTHREADS = 512;
 
 struct GemmArgs {
-  int M, K, N, ldx, ldy, mtiles, ntiles;
+  int M, K, N, ldx, ldw, ldy, mtiles, ntiles;
   const bf16_t* X;
   const bf16_t* W;
   float* Y;
@@ -95,7 +95,7 @@ __global__ __launch_bounds__(GTHREADS, 2) void proj_gemm_kernel(GemmArgs a) {
     const int r = idx >> 3, c = (idx & 7) * 8;
     const int n = n0 + r < a.N ? n0 + r : a.N - 1;  // rows past the end re-read the last row
     const int m = m0 + r < a.M ? m0 + r : 0;
-    wsrc[j] = a.W + static_cast<size_t>(n) * a.K + c;
+    wsrc[j] = a.W + static_cast<size_t>(n) * a.ldw + c;
     xsrc[j] = a.X + static_cast<size_t>(m) * a.ldx + c;
     soff[j] = swz(r, idx & 7);
   }
@@ -210,13 +210,14 @@ __global__ __launch_bounds__(GTHREADS, 2) void proj_gemm_kernel(GemmArgs a) {
 
 bool gemm_supported(int K) { return K % GBK == 0; }
 
-int launch_projection_gemm(int M, int K, int N, const bf16_t* X, int ldx, const bf16_t* W, float* Y, RowMap map,
-                           int ldy, TopkPartials tp, hipStream_t stream) {
+int launch_projection_gemm(int M, int K, int N, const bf16_t* X, int ldx, const bf16_t* W, int ldw, float* Y,
+                           RowMap map, int ldy, TopkPartials tp, hipStream_t stream) {
   GemmArgs a{};
   a.M = M;
   a.K = K;
   a.N = N;
   a.ldx = ldx;
+  a.ldw = ldw;
   a.ldy = ldy;
   a.mtiles = (M + GBM - 1) / GBM;
   a.ntiles = (N + GBN - 1) / GBN;

@@ -330,8 +330,8 @@ int launch_projection(int dtype, int M, int K, int N, XSource xs, const void* W,
     return HYDRA_ERR_UNSUPPORTED;
   }
   if (M >= kGemmMinRows && nsplit == 1 && xs.mode == 0 && gemm_supported(K))
-    return launch_projection_gemm(M, K, N, static_cast<const bf16_t*>(xs.x), xs.ldx, static_cast<const bf16_t*>(W), Y,
-                                  map, ldy, tp, stream);
+    return launch_projection_gemm(M, K, N, static_cast<const bf16_t*>(xs.x), xs.ldx, static_cast<const bf16_t*>(W), K,
+                                  Y, map, ldy, tp, stream);
   ProjArgs a{M, K, N, xs, static_cast<const bf16_t*>(W), Y, map, ldy, K / nsplit, 0, part, tp};
   for (int m0 = 0; m0 < M; m0 += 256) {
     const int mc = M - m0 < 256 ? M - m0 : 256;

@@ -46,10 +46,64 @@ __device__ __forceinline__ void rank_top_k(const uint64_t* cand, int k, uint64_t
   if (lane < n && mine != 0 && rank < k) top[rank] = mine;
 }
 
+// Next-depth Hydra feed-forward rows from the folded embedding table:
+// u = h[b] + SiLU(Anext[b] + Enext[token]) for the nu queued children of
+// this row. Workgroup g of the row's ng takes columns [g d / ng, (g + 1) d / ng),
+// 4 per thread and pass; every child's table load of a pass is issued before
+// any is used, so their latencies overlap.
+template <int KL>
+__device__ __forceinline__ void next_rows(const MergeArgs& a, int b, int g, int nu, const int* urow,
+                                          const int* utok) {
+  if (nu == 0) return;
+  const int d = a.d;
+  const int cw = d / a.ng;
+  // entries past nu repeat the last child: every load is unconditional, so
+  // all of them are in flight before the first use
+  int tk[KL];
+#pragma unroll
+  for (int e = 0; e < KL; ++e) {
+    const int t = utok[e < nu ? e : nu - 1];
+    tk[e] = t < 0 ? 0 : (t >= a.V ? a.V - 1 : t);
+  }
+  for (int c0 = g * cw + threadIdx.x * 4; c0 < (g + 1) * cw; c0 += kMergeThreads * 4) {
+    float4 ev[KL];
+#pragma unroll
+    for (int e = 0; e < KL; ++e) ev[e] = *reinterpret_cast<const float4*>(a.Enext + static_cast<size_t>(tk[e]) * d + c0);
+    const float4 ah = *reinterpret_cast<const float4*>(a.Anext + static_cast<size_t>(b) * d + c0);
+    const u32x2_t hv = *reinterpret_cast<const u32x2_t*>(a.h + static_cast<size_t>(b) * d + c0);
+    const float hf[4] = {bf16_to_f32(static_cast<bf16_t>(hv.x & 0xffffu)), bf16_to_f32(static_cast<bf16_t>(hv.x >> 16)),
+                         bf16_to_f32(static_cast<bf16_t>(hv.y & 0xffffu)), bf16_to_f32(static_cast<bf16_t>(hv.y >> 16))};
+    const float af[4] = {ah.x, ah.y, ah.z, ah.w};
+#pragma unroll
+    for (int e = 0; e < KL; ++e) {
+      if (e >= nu) break;
+      const float evf[4] = {ev[e].x, ev[e].y, ev[e].z, ev[e].w};
+      bf16_t out[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float v = af[q] + evf[q];
+        const float act = v / (1.0f + expf(-v));  // SiLU(v) = v * sigmoid(v)
+        out[q] = f32_to_bf16(a.residual ? hf[q] + act : act);
+      }
+      const u32x2_t packed{static_cast<uint32_t>(out[0]) | (static_cast<uint32_t>(out[1]) << 16),
+                           static_cast<uint32_t>(out[2]) | (static_cast<uint32_t>(out[3]) << 16)};
+      const int m = urow[e];
+      *reinterpret_cast<u32x2_t*>(a.U + static_cast<size_t>(m) * d + c0) = packed;
+      if (a.hidden) {
+        const int hr = (m / a.Pn) * a.R + a.rn + m % a.Pn;
+        *reinterpret_cast<u32x2_t*>(a.hidden + static_cast<size_t>(hr) * d + c0) = packed;
+      }
+    }
+  }
+}
+
 // KL: list capacity (>= k); LL: per-thread list of block maxima (holds all of
 // a thread's slots when nwg <= 256 * LL, else LL = KL keeps its top KL)
+// g: which of the row's ng workgroups this is; all select the same top k,
+// workgroup 0 writes the row's results and each writes its share of the
+// next-depth rows.
 template <int KL, int LL>
-__device__ __forceinline__ void merge_row(const MergeArgs& a, int i) {
+__device__ __forceinline__ void merge_row(const MergeArgs& a, int i, int g) {
   __shared__ uint64_t s_cand[kMergeWaves * KL];
   __shared__ uint64_t s_top[KL];
   __shared__ float s_m[kMergeWaves], s_s[kMergeWaves];
@@ -122,47 +176,67 @@ __device__ __forceinline__ void merge_row(const MergeArgs& a, int i) {
     __syncthreads();
   }
 
-  if (wave != 0) return;  // one wave writes the row
-  float M = s_m[0];
-#pragma unroll
-  for (int w = 1; w < kMergeWaves; ++w) M = fmaxf(M, s_m[w]);
-  float S = 0.f;
-#pragma unroll
-  for (int w = 0; w < kMergeWaves; ++w)
-    if (s_m[w] != -INFINITY) S += s_s[w] * expf(s_m[w] - M);
-  const float lse = M + logf(S);
-  if (lane == 0) {
-    if (a.lse) a.lse[a.map(i)] = lse;
-    if (a.amax) a.amax[i] = key_id(s_top[0]);
-  }
-  if (lane < k) {
-    const uint64_t mine = s_top[lane];
-    if (a.topk_ids) a.topk_ids[static_cast<size_t>(i) * k + lane] = key_id(mine);
-    if (a.topk_vals) a.topk_vals[static_cast<size_t>(i) * k + lane] = key_value(mine);
-  }
-  if (a.node_hi <= a.node_lo) return;
+  const bool fold = a.Enext != nullptr;  // uniform over the launch
+  __shared__ int s_nu;
+  __shared__ int s_urow[KL], s_utok[KL];
   const int b = i / a.P;
-  const int r = a.r0 + i % a.P;
-  const size_t base = static_cast<size_t>(b) * a.N;
-  if (r == 0 && lane == 0) {
-    a.cand_tok[base] = a.root_tok[b];
-    a.cand_logp[base] = 0.f;
+  if (wave == 0) {  // one wave writes the row
+    float M = s_m[0];
+#pragma unroll
+    for (int w = 1; w < kMergeWaves; ++w) M = fmaxf(M, s_m[w]);
+    float S = 0.f;
+#pragma unroll
+    for (int w = 0; w < kMergeWaves; ++w)
+      if (s_m[w] != -INFINITY) S += s_s[w] * expf(s_m[w] - M);
+    const float lse = M + logf(S);
+    const bool writer = g == 0;
+    if (lane == 0) {
+      if (writer && a.lse) a.lse[a.map(i)] = lse;
+      if (writer && a.amax) a.amax[i] = key_id(s_top[0]);
+      s_nu = 0;
+    }
+    if (writer && lane < k) {
+      const uint64_t mine = s_top[lane];
+      if (a.topk_ids) a.topk_ids[static_cast<size_t>(i) * k + lane] = key_id(mine);
+      if (a.topk_vals) a.topk_vals[static_cast<size_t>(i) * k + lane] = key_value(mine);
+    }
+    if (a.node_hi > a.node_lo) {
+      const int r = a.r0 + i % a.P;
+      const size_t base = static_cast<size_t>(b) * a.N;
+      if (writer && r == 0 && lane == 0) {
+        a.cand_tok[base] = a.root_tok[b];
+        a.cand_logp[base] = 0.f;
+      }
+      for (int c = a.node_lo + lane; c < a.node_hi; c += 64) {
+        const int pp = a.node_parent[c];
+        if (pp < 0 || a.node_row[pp] != r) continue;
+        const int rk = a.node_rank[c];
+        if (rk < 0 || rk >= k) continue;
+        const uint64_t key = s_top[rk];
+        if (writer) {
+          const float plogp = pp == 0 ? 0.f : a.cand_logp[base + pp];
+          a.cand_tok[base + c] = key_id(key);
+          a.cand_logp[base + c] = plogp + (key_value(key) - lse);
+        }
+        const int nr = fold ? a.node_row[c] - a.rn : -1;
+        if (nr >= 0 && nr < a.Pn) {  // c is expanded at the next depth: queue its feed-forward row
+          const int e = atomicAdd(&s_nu, 1);  // one parent per row, so e < k <= KL
+          if (e < KL) {
+            s_urow[e] = b * a.Pn + nr;
+            s_utok[e] = key_id(key);
+          }
+        }
+      }
+    }
   }
-  for (int c = a.node_lo + lane; c < a.node_hi; c += 64) {
-    const int pp = a.node_parent[c];
-    if (pp < 0 || a.node_row[pp] != r) continue;
-    const int rk = a.node_rank[c];
-    if (rk < 0 || rk >= k) continue;
-    const uint64_t key = s_top[rk];
-    const float plogp = pp == 0 ? 0.f : a.cand_logp[base + pp];
-    a.cand_tok[base + c] = key_id(key);
-    a.cand_logp[base + c] = plogp + (key_value(key) - lse);
-  }
+  if (!fold) return;
+  __syncthreads();
+  next_rows<KL>(a, b, g, s_nu < KL ? s_nu : KL, s_urow, s_utok);
 }
 
 template <int KL, int LL>
 __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(MergeArgs a) {
-  merge_row<KL, LL>(a, blockIdx.x);
+  merge_row<KL, LL>(a, blockIdx.x / a.ng, blockIdx.x % a.ng);
 }
 
 // The same rows, plus the h half of the next Hydra head in workgroups
@@ -170,21 +244,23 @@ __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(MergeArgs a) 
 // it fills the otherwise idle chip while the merge runs.
 template <int KL, int LL, int PF>
 __global__ __launch_bounds__(kMergeThreads) void topk_merge_ffn_kernel(MergeArgs a, MlpArgs f) {
-  if (static_cast<int>(blockIdx.x) < a.M) {
-    merge_row<KL, LL>(a, blockIdx.x);
+  const int nm = a.M * a.ng;
+  if (static_cast<int>(blockIdx.x) < nm) {
+    merge_row<KL, LL>(a, blockIdx.x / a.ng, blockIdx.x % a.ng);
   } else {
-    mlp_tile<1, PF, kMergeWaves>(f, blockIdx.x - a.M, 0);
+    mlp_tile<1, PF, kMergeWaves>(f, blockIdx.x - nm, 0);
   }
 }
 
 template <int KL, int LL>
 void launch_ll(const MergeArgs& a, const MlpArgs* f, hipStream_t stream) {
+  const int nm = a.M * a.ng;
   if (!f) {
-    topk_merge_kernel<KL, LL><<<a.M, kMergeThreads, 0, stream>>>(a);
+    topk_merge_kernel<KL, LL><<<nm, kMergeThreads, 0, stream>>>(a);
   } else if ((f->K / kMergeWaves / 32) % 8 == 0) {
-    topk_merge_ffn_kernel<KL, LL, 8><<<a.M + f->d / 16, kMergeThreads, 0, stream>>>(a, *f);
+    topk_merge_ffn_kernel<KL, LL, 8><<<nm + f->d / 16, kMergeThreads, 0, stream>>>(a, *f);
   } else {
-    topk_merge_ffn_kernel<KL, LL, 1><<<a.M + f->d / 16, kMergeThreads, 0, stream>>>(a, *f);
+    topk_merge_ffn_kernel<KL, LL, 1><<<nm + f->d / 16, kMergeThreads, 0, stream>>>(a, *f);
   }
 }
 
@@ -201,8 +277,11 @@ bool merge_ffn_supported(int M, int K, int d) {
   return M >= 1 && M <= 16 && K % (kMergeWaves * 32) == 0 && d % 16 == 0;
 }
 
-int launch_topk_merge(const MergeArgs& a, hipStream_t stream, const MlpArgs* ffn) {
-  if (a.M <= 0) return HYDRA_OK;
+int launch_topk_merge(const MergeArgs& args, hipStream_t stream, const MlpArgs* ffn) {
+  if (args.M <= 0) return HYDRA_OK;
+  MergeArgs a = args;
+  // next-depth rows: one workgroup per 1024 columns (at most 8) per row
+  a.ng = a.Enext ? std::min(8, std::max(1, a.d / (4 * kMergeThreads))) : 1;
   if (a.k < 1 || a.k > HYDRA_MAX_TOPK) {
     set_error("top-k merge: k=%d out of [1, %d]", a.k, HYDRA_MAX_TOPK);
     return HYDRA_ERR_UNSUPPORTED;
@@ -211,11 +290,15 @@ int launch_topk_merge(const MergeArgs& a, hipStream_t stream, const MlpArgs* ffn
     set_error("top-k merge: log-sum-exp and tree fill need the (max, sum exp) partials");
     return HYDRA_ERR_INVALID;
   }
+  if (a.Enext && (a.d % (4 * kMergeThreads) != 0 || !a.Anext || !a.h || !a.U || a.Pn < 1)) {
+    set_error("top-k merge: next-depth rows need d %% %d == 0 (d=%d) and their buffers", 4 * kMergeThreads, a.d);
+    return HYDRA_ERR_UNSUPPORTED;
+  }
   if (a.k > 1 && !a.Y) {
     set_error("top-k merge: k=%d needs the logits", a.k);
     return HYDRA_ERR_INVALID;
   }
-  if (ffn && (ffn->heads != 1 || ffn->epi != 0 || !merge_ffn_supported(ffn->M, ffn->K, ffn->d))) {
+  if (ffn && (ffn->heads != 1 || ffn->epi[0] != 0 || !merge_ffn_supported(ffn->M, ffn->K, ffn->d))) {
     set_error("top-k merge: unsupported feed-forward work (M=%d K=%d)", ffn->M, ffn->K);
     return HYDRA_ERR_UNSUPPORTED;
   }

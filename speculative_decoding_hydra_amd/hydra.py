@@ -177,8 +177,9 @@ def hydra_draft_heads_workspace_size(dtype_code, B, d, V, hydra, dplan: DevicePl
 
 
 def hydra_draft_heads(h, root_tok, emb, W1, b1, W2, dplan: DevicePlan, head_logits, head_lse,
-                      cand_tok, cand_logp, ws, head_hidden=None, residual=True, stream=None):
-    """Stage 1 (see include/hydra.h). h [B, d]; W1/b1/W2: lists, head k at k-1."""
+                      cand_tok, cand_logp, ws, head_hidden=None, residual=True, emb_proj=None, stream=None):
+    """Stage 1 (see include/hydra.h). h [B, d]; W1/b1/W2: lists, head k at k-1;
+    emb_proj: optional list of folded embedding tables (hydra_fold_embedding)."""
     dt = _dtype_code(h)
     B, d = h.shape
     V = W2[0].shape[0]
@@ -193,16 +194,32 @@ def hydra_draft_heads(h, root_tok, emb, W1, b1, W2, dplan: DevicePlan, head_logi
     rf, rfp = _host_i32(rows.row_first)
     df, dfp = _host_i32(rows.depth_first)
     kp, kpp = _host_i32(rows.k_per_depth)
+    ep = None
+    if emb_proj is not None:
+        if len(emb_proj) != n_heads:
+            raise ValueError("emb_proj needs one table per head")
+        ep = arr(*[_dev(t, "emb_proj", torch.float32) for t in emb_proj])
     wsp, wsb = _ws(ws)
     rc = lib().hydra_draft_heads(
         dt, B, d, V, int(dplan.hydra), int(bool(residual)), _dev(h, "h"), _dev(root_tok, "root_tok", torch.int32),
-        _dev(emb, "emb", h.dtype) if dplan.hydra else None, n_heads, w1, bb, w2, dplan.N, dplan.dmax,
+        _dev(emb, "emb", h.dtype) if dplan.hydra else None, ep, n_heads, w1, bb, w2, dplan.N, dplan.dmax,
         _dev(dplan.parent, "parent"), _dev(dplan.rank, "rank"), _dev(dplan.node_row, "node_row"), dplan.R,
         _dev(dplan.row_node, "row_node"), rfp, dfp, kpp, _dev(head_logits, "head_logits", torch.float32),
         _dev(head_lse, "head_lse", torch.float32), _dev(head_hidden, "head_hidden", h.dtype),
         _dev(cand_tok, "cand_tok", torch.int32), _dev(cand_logp, "cand_logp", torch.float32), wsp, wsb,
         _stream(stream))
     return _check("hydra_draft_heads", rc)
+
+
+def hydra_fold_embedding(emb, W1, out, stream=None):
+    """out[t, n] = sum_j W1[n, d + j] * emb[t, j] (see include/hydra.h):
+    emb [V, d] and W1 [d, 2d] bf16, out [V, d] float32."""
+    V, d = emb.shape
+    if tuple(W1.shape) != (d, 2 * d) or tuple(out.shape) != (V, d):
+        raise ValueError(f"fold_embedding: W1 {tuple(W1.shape)} / out {tuple(out.shape)} do not match emb {(V, d)}")
+    rc = lib().hydra_fold_embedding(_dtype_code(emb), V, d, _dev(emb, "emb"), _dev(W1, "W1", emb.dtype),
+                                    _dev(out, "out", torch.float32), _stream(stream))
+    return _check("hydra_fold_embedding", rc)
 
 
 def hydra_vocab_projection_workspace_size(M, N, k):

@@ -31,10 +31,13 @@ class HydraRound:
 
     weights: dict with emb [V, d] (Hydra), W1/b1/W2 lists, W_t [V, d].
     shape: dict with B, d, V, Hq, Hkv, D, max_prefix_len.
+    fold_embedding: build the folded embedding tables of the Hydra heads
+    (hydra_fold_embedding, V * d * 4 bytes per head) once here and let the
+    draft stage look the embedding half up; None folds for bf16 Hydra heads.
     """
 
     def __init__(self, weights, tree, shape, hydra=True, mode=0, temperature=1.0, residual=True,
-                 keep_hidden=False, device="cuda"):
+                 keep_hidden=False, device="cuda", fold_embedding=None):
         self.w = weights
         plan, n_keep = make_plan(tree)
         self.dplan = H.DevicePlan(plan, hydra, device)
@@ -69,11 +72,19 @@ class HydraRound:
         self.ws_attn = nb(H.tree_attention_verify_workspace_size(code, B, K, Hq, Hkv, D,
                                                                  shape["max_prefix_len"]))
         self.ws_accept = nb(H.tree_accept_workspace_size(self.mode, B, K, V))
+        if fold_embedding is None:
+            fold_embedding = hydra and dt == torch.bfloat16
+        self.emb_proj = None
+        if fold_embedding:
+            self.emb_proj = [z(V, d) for _ in weights["W1"]]
+            for w1, t in zip(weights["W1"], self.emb_proj):
+                H.hydra_fold_embedding(weights["emb"], w1, t)
 
     def draft(self, h, root_tok, stream=None):
         H.hydra_draft_heads(h, root_tok, self.w.get("emb"), self.w["W1"], self.w["b1"], self.w["W2"], self.dplan,
                             self.head_logits, self.head_lse, self.cand_tok, self.cand_logp, self.ws_draft,
-                            head_hidden=self.head_hidden, residual=self.residual, stream=stream)
+                            head_hidden=self.head_hidden, residual=self.residual, emb_proj=self.emb_proj,
+                            stream=stream)
 
     def build(self, stream=None):
         H.tree_build(self.dplan, self.cand_tok, self.cand_logp, self.n_keep, self.tok, self.parent, self.depth,
@@ -99,7 +110,7 @@ class HydraRound:
         self.accept(u_acc, u_res, stream)
 
 
-def round_from_inputs(inp, device="cuda", keep_hidden=True):
+def round_from_inputs(inp, device="cuda", keep_hidden=True, fold_embedding=None):
     """HydraRound plus device copies of a dict of named input tensors.
 
     Keys: workload (sizes, tree, dtype, mode), root_tok, h, E, W1, b1, W2, W_t,
@@ -113,7 +124,7 @@ def round_from_inputs(inp, device="cuda", keep_hidden=True):
     shape = dict(B=w.B, d=w.d, V=w.V, Hq=w.Hq, Hkv=w.Hkv, D=w.D,
                  max_prefix_len=int(inp["prefix_len"].max()))
     rnd = HydraRound(weights, w.tree, shape, hydra=w.hydra, mode=0 if w.mode == "greedy" else 1,
-                     temperature=w.T, keep_hidden=keep_hidden, device=device)
+                     temperature=w.T, keep_hidden=keep_hidden, device=device, fold_embedding=fold_embedding)
     dev = dict(h=to(inp["h"]), root_tok=to(inp["root_tok"]), q=to(inp["q_tree"]), k_tree=to(inp["k_tree"]),
                v_tree=to(inp["v_tree"]), k_pages=to(inp["k_pages"]), v_pages=to(inp["v_pages"]),
                block_table=to(inp["block_table"]), prefix_len=to(inp["prefix_len"]))

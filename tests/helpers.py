@@ -53,10 +53,10 @@ def oracle_plan(tree):
     return O.plan_cartesian(tree[1]), tree[2]
 
 
-def round_inputs(inp, device="cuda", keep_hidden=True):
+def round_inputs(inp, device="cuda", keep_hidden=True, fold_embedding=None):
     from speculative_decoding_hydra_amd import round_from_inputs
 
-    return round_from_inputs(inp, device=device, keep_hidden=keep_hidden)
+    return round_from_inputs(inp, device=device, keep_hidden=keep_hidden, fold_embedding=fold_embedding)
 
 
 def run_round(rnd, dev, stream=None):

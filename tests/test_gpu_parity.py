@@ -398,20 +398,59 @@ def test_70b_gqa_stochastic_round():
     print(rep, flush=True)
 
 
+@pytest.mark.parametrize("fold", [True, False])
 @pytest.mark.parametrize("B,d,b1,hydra", [(4, 8192, 10, True), (3, 4096, 10, True), (3, 8192, 13, True),
                                            (2, 256, 16, True), (1, 8192, 16, True), (8, 4096, 10, True),
                                            (2, 4096, 13, True), (3, 4096, 4, False), (1, 8192, 16, False)])
-def test_draft_first_layer_split_and_fused(B, d, b1, hydra):
+def test_draft_first_layer_split_and_fused(B, d, b1, hydra, fold):
     """Head hidden states for row counts on both sides of the few-row kernel
     (B * b1 <= 32: head 2's h half runs inside the depth-1 row merge and its
     embedding half at depth 2; Medusa: every head in one launch) and the
-    split-K projection path (more rows), d up to 8192."""
+    split-K projection path (more rows), d up to 8192; Hydra with and
+    without the folded embedding tables (used when d % 1024 == 0)."""
+    if fold and not hydra:
+        pytest.skip("Medusa heads read no embedding")
     w = HI.workload("70b_gqa", B=B, d=d, V=1000, n_heads=2, tree=("cartesian", (b1, 1)), Hq=8, Hkv=8, D=32,
                     L=(64,), mode="greedy", T=1.0, hydra=hydra)
-    print(f"first layer B={B} d={d} rows/depth2={B * b1} hydra={hydra}", flush=True)
+    print(f"first layer B={B} d={d} rows/depth2={B * b1} hydra={hydra} fold={fold}", flush=True)
     inp = HI.generate(w)
-    rnd, dev = T.round_inputs(inp)
+    rnd, dev = T.round_inputs(inp, fold_embedding=fold)
     T.run_round(rnd, dev)
     torch.cuda.synchronize()
     rep = T.check_draft(inp, rnd)
     print(rep, flush=True)
+
+
+@pytest.mark.parametrize("fold", [True, False])
+@pytest.mark.parametrize("tree", [("sparse", (10, 4, 2, 1), 64), ("cartesian", (3, 2, 2, 2))])
+def test_draft_four_heads_folded_and_streamed(tree, fold):
+    """Four Hydra heads at d = 4096 (the folded path's next-depth rows are
+    written by each row merge, and the h half of head k + 2 streams inside
+    the merge of depth k), both against the oracle stage by stage."""
+    w = HI.workload("7b_sparse64", B=2, V=3000, tree=tree, L=(64,))
+    print(f"four heads tree={tree} fold={fold}", flush=True)
+    inp = HI.generate(w)
+    rnd, dev = T.round_inputs(inp, fold_embedding=fold)
+    assert (rnd.emb_proj is not None) == fold
+    T.run_round(rnd, dev)
+    torch.cuda.synchronize()
+    rep = T.check_draft(inp, rnd)
+    print(rep, flush=True)
+
+
+@pytest.mark.parametrize("V,d", [(1000, 256), (300, 1024), (2049, 4096)])
+def test_fold_embedding_table(V, d):
+    """hydra_fold_embedding against the float64 product of the same bf16
+    inputs: out[t] = W1[:, d:] E[t]."""
+    from speculative_decoding_hydra_amd import hydra_fold_embedding
+
+    print(f"fold embedding V={V} d={d}", flush=True)
+    g = torch.Generator().manual_seed(V + d)
+    E = torch.randn(V, d, generator=g).to(torch.bfloat16)
+    W1 = (torch.randn(d, 2 * d, generator=g) * 0.02).to(torch.bfloat16)
+    out = torch.full((V, d), float("nan"), device="cuda")
+    hydra_fold_embedding(E.cuda(), W1.cuda(), out)
+    torch.cuda.synchronize()
+    ref = HI.as_f64(E) @ HI.as_f64(W1)[:, d:].T
+    err = float(np.max(np.abs(out.cpu().double().numpy() - ref)))
+    assert err <= 1e-3, err  # bf16 inputs are exact in fp32; only the summation order differs

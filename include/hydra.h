@@ -137,7 +137,7 @@ int hydra_plan_rows(int N, const int32_t* parent, const int32_t* rank,
  *              holds W1_k[:, d:] E^T, the embedding half of head k's layer for
  *              every token. With them the embedding half is a row lookup
  *              instead of a pass over W1_k[:, d:] (the same sum, as the layer
- *              is linear in e), used when d % 1024 == 0 and B <= 16; otherwise
+ *              is linear in e), used when B <= 16; otherwise
  *              the tables are ignored.
  * n_heads      entries in W1/b1/W2 (>= Dmax)
  * W1, b1, W2   host arrays of n_heads device pointers: W1_k [d, in] (in = 2d

@@ -295,7 +295,7 @@ struct MergeArgs {
   // table: every filled child c with node_row[c] >= 0 gets
   //   u = h[b] + SiLU(Anext[b] + Enext[token of c])  (SiLU(...) alone without
   // the residual), stored as bf16 in U[b * Pn + node_row[c] - rn] and
-  // hidden[b * R + node_row[c]]. Enext == nullptr disables it; needs d % 1024 == 0.
+  // hidden[b * R + node_row[c]]. Enext == nullptr disables it; needs d % 256 == 0.
   const float* Enext;   // [V][d]
   const float* Anext;   // [B][d], b1 included
   const bf16_t* h;      // [B][d]

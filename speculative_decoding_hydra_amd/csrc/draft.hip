@@ -154,7 +154,7 @@ extern "C" int hydra_draft_heads(int dtype, int B, int d, int V, int hydra_mode,
   // of Ah); the row merge of depth k then writes the rows of depth k + 1
   // from the tokens it picks, while its extra workgroups stream the h half of
   // head k + 2 into slot k + 1.
-  const bool folded = hydra_mode && emb_proj && dtype == HYDRA_BF16 && d % 1024 == 0 &&
+  const bool folded = hydra_mode && emb_proj && dtype == HYDRA_BF16 && d % 256 == 0 &&
                       mlp_fused_supported(dtype, B, d, d) && merge_ffn_supported(B, d, d);
   if (folded) {
     for (int k = 1; k <= Dmax; ++k)

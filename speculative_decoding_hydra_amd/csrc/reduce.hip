@@ -48,49 +48,53 @@ __device__ __forceinline__ void rank_top_k(const uint64_t* cand, int k, uint64_t
 
 // Next-depth Hydra feed-forward rows from the folded embedding table:
 // u = h[b] + SiLU(Anext[b] + Enext[token]) for the nu queued children of
-// this row. Workgroup g of the row's ng takes columns [g d / ng, (g + 1) d / ng),
-// 4 per thread and pass; every child's table load of a pass is issued before
-// any is used, so their latencies overlap.
+// this row. Workgroup g of the row's ng takes columns [g d / ng, (g + 1) d / ng)
+// in chunks of 256; in a chunk thread t covers the 4 columns 4 (t % 64) of
+// children t / 64, t / 64 + 4, ... so every thread has at most KL / 4 rows,
+// and all of its table loads are in flight before the first is used.
 template <int KL>
 __device__ __forceinline__ void next_rows(const MergeArgs& a, int b, int g, int nu, const int* urow,
                                           const int* utok) {
+  constexpr int IPT = KL < 4 ? 1 : KL / 4;  // rows per thread
   if (nu == 0) return;
   const int d = a.d;
   const int cw = d / a.ng;
-  // entries past nu repeat the last child: every load is unconditional, so
-  // all of them are in flight before the first use
-  int tk[KL];
+  const int e0 = threadIdx.x >> 6;
+  int tk[IPT], m[IPT];
 #pragma unroll
-  for (int e = 0; e < KL; ++e) {
-    const int t = utok[e < nu ? e : nu - 1];
-    tk[e] = t < 0 ? 0 : (t >= a.V ? a.V - 1 : t);
+  for (int j = 0; j < IPT; ++j) {
+    const int e = e0 + 4 * j < nu ? e0 + 4 * j : nu - 1;  // past nu: repeat the last child, never stored
+    const int t = utok[e];
+    tk[j] = t < 0 ? 0 : (t >= a.V ? a.V - 1 : t);
+    m[j] = urow[e];
   }
-  for (int c0 = g * cw + threadIdx.x * 4; c0 < (g + 1) * cw; c0 += kMergeThreads * 4) {
-    float4 ev[KL];
+  for (int c0 = g * cw + (threadIdx.x & 63) * 4; c0 < (g + 1) * cw; c0 += 256) {
+    float4 ev[IPT];
 #pragma unroll
-    for (int e = 0; e < KL; ++e) ev[e] = *reinterpret_cast<const float4*>(a.Enext + static_cast<size_t>(tk[e]) * d + c0);
+    for (int j = 0; j < IPT; ++j) ev[j] = *reinterpret_cast<const float4*>(a.Enext + static_cast<size_t>(tk[j]) * d + c0);
     const float4 ah = *reinterpret_cast<const float4*>(a.Anext + static_cast<size_t>(b) * d + c0);
     const u32x2_t hv = *reinterpret_cast<const u32x2_t*>(a.h + static_cast<size_t>(b) * d + c0);
     const float hf[4] = {bf16_to_f32(static_cast<bf16_t>(hv.x & 0xffffu)), bf16_to_f32(static_cast<bf16_t>(hv.x >> 16)),
                          bf16_to_f32(static_cast<bf16_t>(hv.y & 0xffffu)), bf16_to_f32(static_cast<bf16_t>(hv.y >> 16))};
     const float af[4] = {ah.x, ah.y, ah.z, ah.w};
 #pragma unroll
-    for (int e = 0; e < KL; ++e) {
-      if (e >= nu) break;
-      const float evf[4] = {ev[e].x, ev[e].y, ev[e].z, ev[e].w};
+    for (int j = 0; j < IPT; ++j) {
+      if (e0 + 4 * j >= nu) continue;  // not break: the loop unrolls fully and ev stays in registers
+      const float evf[4] = {ev[j].x, ev[j].y, ev[j].z, ev[j].w};
       bf16_t out[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const float v = af[q] + evf[q];
-        const float act = v / (1.0f + expf(-v));  // SiLU(v) = v * sigmoid(v)
+        // SiLU(v) = v * sigmoid(v) with the hardware exp2 and reciprocal:
+        // a few float32 ulp, far below the bf16 rounding that follows
+        const float act = v * __builtin_amdgcn_rcpf(1.0f + __expf(-v));
         out[q] = f32_to_bf16(a.residual ? hf[q] + act : act);
       }
       const u32x2_t packed{static_cast<uint32_t>(out[0]) | (static_cast<uint32_t>(out[1]) << 16),
                            static_cast<uint32_t>(out[2]) | (static_cast<uint32_t>(out[3]) << 16)};
-      const int m = urow[e];
-      *reinterpret_cast<u32x2_t*>(a.U + static_cast<size_t>(m) * d + c0) = packed;
+      *reinterpret_cast<u32x2_t*>(a.U + static_cast<size_t>(m[j]) * d + c0) = packed;
       if (a.hidden) {
-        const int hr = (m / a.Pn) * a.R + a.rn + m % a.Pn;
+        const int hr = (m[j] / a.Pn) * a.R + a.rn + m[j] % a.Pn;
         *reinterpret_cast<u32x2_t*>(a.hidden + static_cast<size_t>(hr) * d + c0) = packed;
       }
     }
@@ -280,8 +284,14 @@ bool merge_ffn_supported(int M, int K, int d) {
 int launch_topk_merge(const MergeArgs& args, hipStream_t stream, const MlpArgs* ffn) {
   if (args.M <= 0) return HYDRA_OK;
   MergeArgs a = args;
-  // next-depth rows: one workgroup per 1024 columns (at most 8) per row
-  a.ng = a.Enext ? std::min(8, std::max(1, a.d / (4 * kMergeThreads))) : 1;
+  // next-depth rows: up to one workgroup per 256 columns per row, about 512
+  // workgroups in all (each repeats the row's top-k), dividing d / 256
+  a.ng = 1;
+  if (a.Enext && a.d >= 256) {
+    const int q = a.d / 256;
+    a.ng = std::max(1, std::min(q, 512 / a.M));
+    while (q % a.ng) --a.ng;
+  }
   if (a.k < 1 || a.k > HYDRA_MAX_TOPK) {
     set_error("top-k merge: k=%d out of [1, %d]", a.k, HYDRA_MAX_TOPK);
     return HYDRA_ERR_UNSUPPORTED;
@@ -290,8 +300,8 @@ int launch_topk_merge(const MergeArgs& args, hipStream_t stream, const MlpArgs* 
     set_error("top-k merge: log-sum-exp and tree fill need the (max, sum exp) partials");
     return HYDRA_ERR_INVALID;
   }
-  if (a.Enext && (a.d % (4 * kMergeThreads) != 0 || !a.Anext || !a.h || !a.U || a.Pn < 1)) {
-    set_error("top-k merge: next-depth rows need d %% %d == 0 (d=%d) and their buffers", 4 * kMergeThreads, a.d);
+  if (a.Enext && (a.d % (256 * a.ng) != 0 || !a.Anext || !a.h || !a.U || a.Pn < 1)) {
+    set_error("top-k merge: next-depth rows need d %% %d == 0 (d=%d) and their buffers", 256 * a.ng, a.d);
     return HYDRA_ERR_UNSUPPORTED;
   }
   if (a.k > 1 && !a.Y) {

@@ -132,10 +132,11 @@ constexpr int kDppXor2 = 0x4E;         // quad_perm [2,3,0,1]
 constexpr int kDppHalfMirror = 0x141;  // lane j <-> 7 - j within 8
 constexpr int kDppMirror = 0x140;      // lane j <-> 15 - j within 16
 
+// (every lane reads a valid source under these patterns, so the old value,
+// 0 here, is never kept; 0 lets the compiler fuse the move into an integer max)
 template <int CTRL>
 __device__ __forceinline__ uint32_t dpp32(uint32_t v) {
-  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(static_cast<int>(v), static_cast<int>(v), CTRL, 0xF,
-                                                           0xF, false));
+  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), CTRL, 0xF, 0xF, false));
 }
 template <int CTRL>
 __device__ __forceinline__ float dppf(float v) {
@@ -148,15 +149,25 @@ __device__ __forceinline__ uint64_t dpp64(uint64_t v) {
   return (static_cast<uint64_t>(hi) << 32) | lo;
 }
 
-// max of a key over aligned groups of G lanes (G in 1, 2, 4, 8, 16)
+// max of a 32-bit word over aligned groups of G lanes (G in 1, 2, 4, 8, 16)
+template <int G>
+__device__ __forceinline__ uint32_t group_max_u32(uint32_t v) {
+  if constexpr (G >= 2) v = max(v, dpp32<kDppXor1>(v));
+  if constexpr (G >= 4) v = max(v, dpp32<kDppXor2>(v));
+  if constexpr (G >= 8) v = max(v, dpp32<kDppHalfMirror>(v));
+  if constexpr (G >= 16) v = max(v, dpp32<kDppMirror>(v));
+  return v;
+}
+
+// max of a key over aligned groups of G lanes: the value word first, then
+// the id word among the lanes that hold that value (32-bit steps are single
+// DPP-fused VALU operations; a 64-bit compare-and-select is several)
 template <int G>
 __device__ __forceinline__ uint64_t group_max_u64(uint64_t v) {
-  uint64_t o;
-  if constexpr (G >= 2) { o = dpp64<kDppXor1>(v); v = o > v ? o : v; }
-  if constexpr (G >= 4) { o = dpp64<kDppXor2>(v); v = o > v ? o : v; }
-  if constexpr (G >= 8) { o = dpp64<kDppHalfMirror>(v); v = o > v ? o : v; }
-  if constexpr (G >= 16) { o = dpp64<kDppMirror>(v); v = o > v ? o : v; }
-  return v;
+  const uint32_t hi = static_cast<uint32_t>(v >> 32);
+  const uint32_t mh = group_max_u32<G>(hi);
+  const uint32_t ml = group_max_u32<G>(hi == mh ? static_cast<uint32_t>(v) : 0u);
+  return (static_cast<uint64_t>(mh) << 32) | ml;
 }
 
 // (max, sum exp(x - max)) pairs combined over aligned groups of G lanes
@@ -186,20 +197,23 @@ __device__ __forceinline__ void wave_ms(float& m, float& s) {
   s = rs;
 }
 
-// max of a key over the whole wave, returned in every lane
+// max of a 32-bit word over the whole wave, returned in every lane: rows of
+// 16 by DPP, then the row pairs and the two halves by the gfx950 row-swap
+// moves (VALU, no round trip through scalar registers)
+__device__ __forceinline__ uint32_t max_swapped(uint32_t v, bool half32) {
+  const auto a = half32 ? __builtin_amdgcn_permlane32_swap(v, v, false, false)
+                        : __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  return max(a[0], a[1]);
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  return max_swapped(max_swapped(group_max_u32<16>(v), false), true);
+}
+// max of a key over the whole wave (value word, then id word), in every lane
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-  v = group_max_u64<16>(v);
-  uint64_t r = v;
-#pragma unroll
-  for (int row = 1; row < 4; ++row) {
-    const uint32_t lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(v), row * 16);
-    const uint32_t hi = __builtin_amdgcn_readlane(static_cast<uint32_t>(v >> 32), row * 16);
-    const uint64_t o = (static_cast<uint64_t>(hi) << 32) | lo;
-    r = o > r ? o : r;
-  }
-  const uint32_t lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(r), 0);
-  const uint32_t hi = __builtin_amdgcn_readlane(static_cast<uint32_t>(r >> 32), 0);
-  return (static_cast<uint64_t>(hi) << 32) | lo;
+  const uint32_t hi = static_cast<uint32_t>(v >> 32);
+  const uint32_t mh = wave_max_u32(hi);
+  const uint32_t ml = wave_max_u32(hi == mh ? static_cast<uint32_t>(v) : 0u);
+  return (static_cast<uint64_t>(mh) << 32) | ml;
 }
 
 // Insert key x into a descending list of length K held in registers.

@@ -73,6 +73,30 @@ def measured_traffic():
     return t.get("bytes_per_launch") if t.get("proj_hip_sha256_16") == source_hash() else None
 
 
+def round_bytes(w, rnd, prefix_len):
+    """Algorithmic HBM bytes of one round: every weight matrix the round
+    needs streamed once, the paged prefix K/V read once, the tree Q/K/V/O,
+    the logits written, and (folded Hydra heads) one float32 table row per
+    head row instead of W1's embedding half."""
+    d, V, B, esz = w.d, w.V, w.B, 2 if w.dtype == "bf16" else 4
+    R, N, heads = rnd.dplan.R, rnd.n_keep, rnd.dplan.dmax
+    rows_per_head = [int(rnd.dplan.rows.row_first[k + 1] - rnd.dplan.rows.row_first[k]) for k in range(heads)]
+    draft = heads * V * d * esz  # W2
+    if w.hydra:
+        draft += heads * d * d * esz  # W1 h halves
+        if rnd.emb_proj is None:
+            draft += heads * d * d * esz  # W1 embedding halves, streamed
+        else:
+            draft += B * sum(rows_per_head) * d * 4  # one table row per head row
+    else:
+        draft += heads * d * d * esz
+    draft += B * R * V * 4  # head logits
+    prefix = int(prefix_len.sum())
+    attn = prefix * w.Hkv * w.D * esz * 2 + B * N * (2 * w.Hq + 2 * w.Hkv) * w.D * esz
+    target = V * d * esz + B * N * d * esz + B * N * V * 4
+    return draft + attn + target
+
+
 def cpu_baseline(inp, n_rows):
     """The oracle, as it stands, on one full round of the same workload."""
     import numpy as np
@@ -262,6 +286,7 @@ def main():
     alg_bytes = w.V * w.d * esz + M * w.d * esz + M * w.V * 4
     achieved = alg_bytes / (k_ms * 1e-3) / 1e9
 
+    rbytes = round_bytes(w, rnd, inp["prefix_len"])
     cpu = None
     if not args.no_cpu:
         log("[bench] timing the CPU oracle on one round")
@@ -291,6 +316,8 @@ def main():
                      "kernel": "proj_bf16_kernel (vocabulary projection, fused top-k epilogue)",
                      "bytes_per_launch": alg_bytes, "rows": M, "topk": kk, "avg_launch_ms": k_ms},
         "round_ms": round_ms,
+        "round_bytes": rbytes,
+        "round_hbm_frac": rbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "stages_ms": {"draft": stage_ms[0], "build": stage_ms[1], "attention": stage_ms[2],
                       "accept": stage_ms[3]},
         "cpu_baseline": cpu,

@@ -79,8 +79,13 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_split_mfma(
   constexpr int NT = NW * 64;
   constexpr int QR = NW * RT * 16;   // query rows per workgroup
   constexpr int TK = NT / 16 * KPT;  // keys per tile
-  constexpr int KROW = D + 8;        // K row in LDS (bf16), 16-byte pad
-  constexpr int VROW = TK + 4;       // V^T row in LDS (bf16), 8-byte pad
+  // K rows in LDS are 256 bytes with the 16-byte chunk c of key r at position
+  // c ^ 2 (r % 8): the 16-row operand reads then hit distinct banks (padded
+  // rows cost a two-way conflict on gfx950). V^T rows are TK + 4 bf16 with
+  // column groups of 4 XOR-ed by (row / 8) % 16, which spreads the transposing
+  // writes (16 rows 8 apart per instruction) over the banks.
+  constexpr int KROW = D;
+  constexpr int VROW = TK + 4;
   constexpr int DJ = D / 32;
   constexpr int DD = D / 16;
   static_assert(TK % 64 == 0, "tiles hold whole 64-key steps");
@@ -99,6 +104,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_split_mfma(
   const int G = Hq / Hkv;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, lq = lane & 15;
+  const int kx = (lq & 7) << 1;  // K chunk swizzle of this lane's key rows
   const int page_size = 1 << page_shift;
 
   int wrow[RT];  // this lane's query rows inside the workgroup
@@ -215,7 +221,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_split_mfma(
       for (int r = 0; r < RT; ++r) sacc[r][tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int j = 0; j < DJ; ++j) {
-        const u32x4_t a = *reinterpret_cast<const u32x4_t*>(&klds[(c0 + 16 * tt + lq) * KROW + 32 * j + 8 * g]);
+        const u32x4_t a = *reinterpret_cast<const u32x4_t*>(&klds[(c0 + 16 * tt + lq) * KROW + (((4 * j + g) ^ kx) << 3)]);
 #pragma unroll
         for (int r = 0; r < RT; ++r)
           sacc[r][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), qreg[r][j],
@@ -299,10 +305,12 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_split_mfma(
     for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
       for (int dd = 0; dd < DD; ++dd) {
-        const bf16_t* vr = &vlds[(16 * dd + lq) * VROW + c0 + 32 * ks + 4 * g];
+        const int vrow = 16 * dd + lq;
+        const int vx = ((vrow >> 3) & 15) << 2;
+        const int col = c0 + 32 * ks + 4 * g;
         u32x4_t a;
-        const u32x2_t lo = *reinterpret_cast<const u32x2_t*>(vr);
-        const u32x2_t hi = *reinterpret_cast<const u32x2_t*>(vr + 16);
+        const u32x2_t lo = *reinterpret_cast<const u32x2_t*>(&vlds[vrow * VROW + (col ^ vx)]);
+        const u32x2_t hi = *reinterpret_cast<const u32x2_t*>(&vlds[vrow * VROW + ((col + 16) ^ vx)]);
         a.x = lo.x;
         a.y = lo.y;
         a.z = hi.x;
@@ -329,7 +337,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_split_mfma(
       }
     }
 #pragma unroll
-    for (int j = 0; j < KPT; ++j) *reinterpret_cast<u32x4_t*>(&klds[(tl + j) * KROW + dc * 8]) = kv[sl][j];
+    for (int j = 0; j < KPT; ++j)
+      *reinterpret_cast<u32x4_t*>(&klds[(tl + j) * KROW + ((dc ^ (((tl + j) & 7) << 1)) << 3)]) = kv[sl][j];
     {
       typedef __attribute__((ext_vector_type(8))) uint16_t u16x8;
       u16x8 a[KPT];
@@ -341,9 +350,10 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_split_mfma(
           u32x2_t w;
           w.x = pack2(a[0][e], a[1][e]);
           w.y = pack2(a[2][e], a[3][e]);
-          *reinterpret_cast<u32x2_t*>(&vlds[(dc * 8 + e) * VROW + tl]) = w;
+          *reinterpret_cast<u32x2_t*>(&vlds[(dc * 8 + e) * VROW + (tl ^ ((dc & 15) << 2))]) = w;
         } else {
-          *reinterpret_cast<uint32_t*>(&vlds[(dc * 8 + e) * VROW + tl]) = pack2(a[0][e], a[1][e]);
+          *reinterpret_cast<uint32_t*>(&vlds[(dc * 8 + e) * VROW + (tl ^ ((dc & 15) << 2))]) =
+              pack2(a[0][e], a[1][e]);
         }
       }
     }

@@ -15,7 +15,7 @@
 // the bonus token is drawn from the target distribution when every draft is
 // accepted). p and q are the post-temperature distributions ("Common
 // misconceptions").
-#include "common.h"
+#include "walk.h"
 
 namespace hydra {
 namespace {
@@ -26,38 +26,7 @@ __global__ __launch_bounds__(64) void greedy_walk(int N, int Dmax, const int32_t
                                                   const int32_t* __restrict__ parent,
                                                   int32_t* __restrict__ n_accepted, int32_t* __restrict__ path,
                                                   int32_t* __restrict__ out_tok) {
-  __shared__ int s_path[HYDRA_MAX_DEPTH + 1], s_out[HYDRA_MAX_DEPTH + 1];
-  const int b = blockIdx.x, lane = threadIdx.x;
-  if (lane <= Dmax) {
-    s_path[lane] = -1;
-    s_out[lane] = -1;
-  }
-  __syncthreads();
-  const int32_t* tb = tok + static_cast<size_t>(b) * N;
-  const int32_t* pb = parent + static_cast<size_t>(b) * N;
-  int u = 0, m = 0;
-  if (lane == 0) s_path[0] = 0;
-  while (true) {
-    const int y = amax[static_cast<size_t>(b) * N + u];
-    int found = -1;
-    for (int c0 = 0; c0 < N && found < 0; c0 += 64) {
-      const int c = c0 + lane;
-      const bool hit = c < N && pb[c] == u && tb[c] == y;
-      const unsigned long long mask = __ballot(hit);
-      if (mask) found = c0 + __ffsll(static_cast<long long>(mask)) - 1;
-    }
-    if (lane == 0) s_out[m] = y;
-    if (found < 0 || m >= Dmax) break;
-    ++m;
-    u = found;
-    if (lane == 0) s_path[m] = u;
-  }
-  __syncthreads();
-  if (lane <= Dmax) {
-    path[static_cast<size_t>(b) * (Dmax + 1) + lane] = s_path[lane];
-    out_tok[static_cast<size_t>(b) * (Dmax + 1) + lane] = s_out[lane];
-  }
-  if (lane == 0) n_accepted[b] = m;
+  greedy_walk_seq(blockIdx.x, N, Dmax, amax, tok, parent, n_accepted, path, out_tok);
 }
 
 constexpr int kWalkThreads = 1024;
@@ -263,7 +232,8 @@ extern "C" size_t tree_accept_workspace_size(int mode, int B, int N, int V) {
   if (B <= 0 || N <= 0 || V <= 0) return 0;
   const size_t rows = static_cast<size_t>(B) * N;
   if (mode == 0)
-    return align_up(rows * sizeof(int32_t), 256) + align_up(rows * projection_nwg(V) * sizeof(uint64_t), 256) + 256;
+    return align_up(rows * sizeof(int32_t), 256) + align_up(rows * projection_nwg(V) * sizeof(uint64_t), 256) +
+           align_up(static_cast<size_t>(B) * sizeof(int), 256) + 256;
   return align_up(static_cast<size_t>(B) * 2 * V * sizeof(float), 256) + 256;
 }
 
@@ -303,8 +273,12 @@ extern "C" int tree_accept(int dtype, int mode, int B, int N, int d, int V, int 
     int32_t* amax = arena.take<int32_t>(static_cast<size_t>(M));
     const int nwg = projection_nwg(V);
     uint64_t* keys = arena.take<uint64_t>(static_cast<size_t>(M) * nwg);
-    int rc = launch_projection(dtype, M, d, V, xs, W_t, target_logits, RowMap{M, 0, 0}, V, 1, nullptr,
-                               TopkPartials{keys, nullptr}, stream);
+    int* walk_count = arena.take<int>(static_cast<size_t>(B));
+    // with up to 256 sequences the projection clears the walk counters and
+    // the row merge's last workgroup per sequence walks; otherwise a walk kernel
+    const bool fused_walk = B <= 256;
+    TopkPartials tp{keys, nullptr, fused_walk ? walk_count : nullptr, fused_walk ? B : 0};
+    int rc = launch_projection(dtype, M, d, V, xs, W_t, target_logits, RowMap{M, 0, 0}, V, 1, nullptr, tp, stream);
     if (rc != HYDRA_OK) return rc;
     MergeArgs ma{};
     ma.M = M;
@@ -318,10 +292,22 @@ extern "C" int tree_accept(int dtype, int mode, int B, int N, int d, int V, int 
     ma.map = RowMap{M, 0, 0};
     ma.amax = amax;
     ma.P = 1;
+    if (fused_walk) {
+      ma.N = N;
+      ma.walk_count = walk_count;
+      ma.wtok = tok;
+      ma.wparent = parent;
+      ma.wDmax = Dmax;
+      ma.n_accepted = n_accepted;
+      ma.path = path;
+      ma.out_tok = out_tok;
+    }
     rc = launch_topk_merge(ma, stream);
     if (rc != HYDRA_OK) return rc;
-    greedy_walk<<<B, 64, 0, stream>>>(N, Dmax, amax, tok, parent, n_accepted, path, out_tok);
-    HY_LAUNCH_CHECK("tree_accept: greedy walk");
+    if (!fused_walk) {
+      greedy_walk<<<B, 64, 0, stream>>>(N, Dmax, amax, tok, parent, n_accepted, path, out_tok);
+      HY_LAUNCH_CHECK("tree_accept: greedy walk");
+    }
   } else {
     int rc = launch_projection(dtype, M, d, V, xs, W_t, target_logits, RowMap{M, 0, 0}, V, 1, nullptr,
                                TopkPartials{nullptr, nullptr}, stream);

@@ -265,6 +265,8 @@ struct XSource {
 struct TopkPartials {
   uint64_t* keys;  // [M][nwg]
   float2* ms;      // [M][nwg], or nullptr when no log-sum-exp is wanted
+  int* clear;      // optional: the launch also zeroes clear[0 .. nclear) (nclear <= 256)
+  int nclear;
 };
 
 constexpr int kProjRowsPerWG = 64;
@@ -317,6 +319,17 @@ struct MergeArgs {
   bf16_t* hidden;       // or nullptr
   int d, R, rn, Pn, residual;
   int ng;               // workgroups per row (set by the launcher)
+  // greedy walk (k = 1, rows = B sequences x N tree rows, row i of sequence
+  // i / N): the last row of a sequence to finish walks its tree from the arg
+  // maxes. walk_count [B] must be zero when the launch starts (the projection
+  // launch before it clears it).
+  int* walk_count;      // nullptr disables it
+  const int32_t* wtok;
+  const int32_t* wparent;
+  int wDmax;
+  int32_t* n_accepted;
+  int32_t* path;
+  int32_t* out_tok;
 };
 
 // Feed-forward layer of the draft heads for few rows (bf16), for up to

@@ -83,6 +83,7 @@ __global__ __launch_bounds__(GTHREADS, 2) void proj_gemm_kernel(GemmArgs a) {
   if (ntile >= a.ntiles) return;  // whole workgroup: no barrier is pending
   const int n0 = ntile * GBN, m0 = mtile * GBM;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (a.tp.clear && bx == 0 && tid < a.tp.nclear) a.tp.clear[tid] = 0;
   const int wn = wave & 1, wm = wave >> 1;  // 2 x 4 waves: 128 n x 64 m each
 
   // global -> register staging: 4 vectors of 16 bytes of W and of X per thread

@@ -57,6 +57,7 @@ __global__ __launch_bounds__(64 * WV) void proj_bf16_kernel(ProjArgs a) {
   const int k_begin = blockIdx.y * a.kper;
   const int k_end = k_begin + a.kper;
   const int K0 = xs.mode == 0 ? K : xs.d;
+  if (TOPK && a.tp.clear && blockIdx.x == 0 && blockIdx.y == 0 && tid < a.tp.nclear) a.tp.clear[tid] = 0;
 
   static_assert((MP * VPR) % NT == 0, "X chunk splits evenly over the workgroup");
   const int wrow = min(n_base + (lane & 15), N - 1);
@@ -250,6 +251,8 @@ __global__ __launch_bounds__(256) void proj_f32_kernel(int M, int K, int N, XSou
 __global__ __launch_bounds__(64) void logits_partials(int M, int N, const float* __restrict__ Y, RowMap map,
                                                       int ldy, TopkPartials tp) {
   const int m = blockIdx.y, w = blockIdx.x, lane = threadIdx.x;
+  if (tp.clear && m == 0 && w == 0)
+    for (int c = lane; c < tp.nclear; c += 64) tp.clear[c] = 0;
   const int n = w * kProjRowsPerWG + lane;
   const float v = n < N ? Y[static_cast<size_t>(map(m)) * ldy + n] : -INFINITY;
   const float mx = wave_max(v);

@@ -16,6 +16,7 @@
 // every child that takes its token from this row gets entry rank of the list
 // and the cumulative log-probability of its parent plus z[token] - lse.
 #include "ffn.h"
+#include "walk.h"
 
 namespace hydra {
 namespace {
@@ -233,6 +234,23 @@ __device__ __forceinline__ void merge_row(const MergeArgs& a, int i, int g) {
       }
     }
   }
+  if (a.walk_count) {  // uniform over the launch
+    // the last of sequence wb's rows to finish walks its tree: the release
+    // fence publishes this row's arg max before the count, the acquire fence
+    // of the last one makes every row's visible (across the XCDs' L2s)
+    __shared__ int s_last;
+    const int wb = i / a.N;
+    if (tid == 0) {
+      __threadfence();
+      s_last = atomicAdd(&a.walk_count[wb], 1) == a.N - 1;
+    }
+    __syncthreads();
+    if (s_last && wave == 0) {
+      __threadfence();
+      greedy_walk_seq(wb, a.N, a.wDmax, a.amax, a.wtok, a.wparent, a.n_accepted, a.path, a.out_tok);
+    }
+    return;
+  }
   if (!fold) return;
   __syncthreads();
   next_rows<KL>(a, b, g, s_nu < KL ? s_nu : KL, s_urow, s_utok);
@@ -303,6 +321,10 @@ int launch_topk_merge(const MergeArgs& args, hipStream_t stream, const MlpArgs* 
   if (a.Enext && (a.d % (256 * a.ng) != 0 || !a.Anext || !a.h || !a.U || a.Pn < 1)) {
     set_error("top-k merge: next-depth rows need d %% %d == 0 (d=%d) and their buffers", 256 * a.ng, a.d);
     return HYDRA_ERR_UNSUPPORTED;
+  }
+  if (a.walk_count && (a.k != 1 || !a.amax || a.N < 1 || a.Enext)) {
+    set_error("top-k merge: the greedy walk needs k = 1, the arg maxes and no next-depth rows");
+    return HYDRA_ERR_INVALID;
   }
   if (a.k > 1 && !a.Y) {
     set_error("top-k merge: k=%d needs the logits", a.k);

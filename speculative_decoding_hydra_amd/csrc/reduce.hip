@@ -154,13 +154,18 @@ __device__ __forceinline__ void merge_row(const MergeArgs& a, int i, int g) {
   if (wave == 0) rank_top_k(s_cand, k, s_top, lane);
   __syncthreads();
 
-  // 3. the top k of those blocks' logits (for k = 1 the largest maximum is it)
+  // 3. the top k of those blocks' logits (for k = 1 the largest maximum is
+  // it). The k-th largest block maximum T is a lower bound for the k-th
+  // largest logit (the k maxima are k keys >= T), so only keys >= T are
+  // candidates: usually little more than the maxima themselves. They are
+  // collected in LDS and ranked by counting.
   if (KL > 1 && k > 1) {
     constexpr int BPW = (KL + kMergeWaves - 1) / kMergeWaves;  // blocks per wave
+    __shared__ uint64_t s_c[KL * kProjRowsPerWG];
+    __shared__ int s_nc;
     const float* y = a.Y + static_cast<size_t>(a.map(i)) * a.ldy;
-    uint64_t l2[BPW];
-#pragma unroll
-    for (int j = 0; j < BPW; ++j) l2[j] = 0;
+    const uint64_t T = s_top[k - 1];
+    if (tid == 0) s_nc = 0;
     float v[BPW];
     int col[BPW];
 #pragma unroll
@@ -172,12 +177,21 @@ __device__ __forceinline__ void merge_row(const MergeArgs& a, int i, int g) {
       v[j] = y[ok ? col[j] : 0];
       if (!ok) col[j] = -1;
     }
+    __syncthreads();  // s_nc cleared, every read of s_top above done
 #pragma unroll
-    for (int j = 0; j < BPW; ++j)
-      if (col[j] >= 0) list_insert<BPW>(l2, topk_key(v[j], col[j]));
-    wave_top_k<BPW>(l2, k, s_cand + wave * k, lane);
+    for (int j = 0; j < BPW; ++j) {
+      const uint64_t key = col[j] >= 0 ? topk_key(v[j], col[j]) : 0;
+      if (key != 0 && key >= T) s_c[atomicAdd(&s_nc, 1)] = key;
+    }
+    if (tid < k) s_top[tid] = 0;
     __syncthreads();
-    if (wave == 0) rank_top_k(s_cand, k, s_top, lane);
+    const int n = s_nc;
+    for (int c = tid; c < n; c += kMergeThreads) {
+      const uint64_t mine = s_c[c];
+      int rank = 0;
+      for (int o = 0; o < n; ++o) rank += s_c[o] > mine ? 1 : 0;
+      if (rank < k) s_top[rank] = mine;
+    }
     __syncthreads();
   }
 

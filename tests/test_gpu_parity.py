@@ -289,17 +289,24 @@ def test_zero_init_heads_reproduce_lm_head_exactly(dtype, hydra):
     assert all(torch.equal(got[r], base[0]) for r in range(got.shape[0]))
 
 
-def test_greedy_planted_paths():
-    """Target logits forced along a chosen branch give that accepted length."""
+@pytest.mark.parametrize("B,dtype", [(4, "fp32"), (4, "bf16"), (20, "bf16"), (300, "fp32")])
+def test_greedy_planted_paths(B, dtype):
+    """Target logits forced along a chosen branch give that accepted length.
+    Up to 256 sequences the walk runs inside the arg-max merge (its counters
+    cleared by the streaming projection, by the tiled one at 20 x 21 = 420
+    rows, or by the float32 partials pass); 300 sequences take the separate
+    walk kernel."""
     from speculative_decoding_hydra_amd import tree_accept, tree_accept_workspace_size
 
-    g = np.random.default_rng(0)
-    V, d, B = 1000, 256, 4
+    print(f"greedy planted B={B} {dtype}", flush=True)
+    g = np.random.default_rng(B)
+    dt = torch.float32 if dtype == "fp32" else torch.bfloat16
+    V, d = 1000, 256
     plan = O.plan_cartesian([2, 3, 2])
     N = plan.n
     anc = O.ancestors(plan.parent, plan.dmax)
     W = g.standard_normal((V, d)) * 0.02
-    for trial in range(6):
+    for trial in range(6 if B < 100 else 2):
         tok = np.zeros((B, N), dtype=np.int32)
         o = g.standard_normal((B, N, d)) * 0.1
         want = []
@@ -315,8 +322,8 @@ def test_greedy_planted_paths():
                 o[b, a] = W[tok[b, nx]] * 40.0
             o[b, path[-1]] = W[stop] * 40.0
             want.append((len(path) - 1, path, [int(tok[b, c]) for c in path[1:]] + [stop]))
-        ot = torch.tensor(o, dtype=torch.float32).cuda()
-        Wt = torch.tensor(W, dtype=torch.float32).cuda()
+        ot = torch.tensor(o, dtype=torch.float32).to(dt).cuda()
+        Wt = torch.tensor(W, dtype=torch.float32).to(dt).cuda()
         tk = torch.tensor(tok).cuda()
         par = torch.tensor(np.stack([plan.parent] * B).astype(np.int32)).cuda()
         Z = torch.empty(B, N, V, device="cuda")

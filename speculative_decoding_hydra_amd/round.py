@@ -110,7 +110,7 @@ class HydraRound:
         self.accept(u_acc, u_res, stream)
 
 
-def round_from_inputs(inp, device="cuda", keep_hidden=True, fold_embedding=None):
+def round_from_inputs(inp, device="cuda", keep_hidden=True, fold_embedding=None, residual=True):
     """HydraRound plus device copies of a dict of named input tensors.
 
     Keys: workload (sizes, tree, dtype, mode), root_tok, h, E, W1, b1, W2, W_t,
@@ -124,7 +124,8 @@ def round_from_inputs(inp, device="cuda", keep_hidden=True, fold_embedding=None)
     shape = dict(B=w.B, d=w.d, V=w.V, Hq=w.Hq, Hkv=w.Hkv, D=w.D,
                  max_prefix_len=int(inp["prefix_len"].max()))
     rnd = HydraRound(weights, w.tree, shape, hydra=w.hydra, mode=0 if w.mode == "greedy" else 1,
-                     temperature=w.T, keep_hidden=keep_hidden, device=device, fold_embedding=fold_embedding)
+                     temperature=w.T, residual=residual, keep_hidden=keep_hidden, device=device,
+                     fold_embedding=fold_embedding)
     dev = dict(h=to(inp["h"]), root_tok=to(inp["root_tok"]), q=to(inp["q_tree"]), k_tree=to(inp["k_tree"]),
                v_tree=to(inp["v_tree"]), k_pages=to(inp["k_pages"]), v_pages=to(inp["v_pages"]),
                block_table=to(inp["block_table"]), prefix_len=to(inp["prefix_len"]))

@@ -53,10 +53,11 @@ def oracle_plan(tree):
     return O.plan_cartesian(tree[1]), tree[2]
 
 
-def round_inputs(inp, device="cuda", keep_hidden=True, fold_embedding=None):
+def round_inputs(inp, device="cuda", keep_hidden=True, fold_embedding=None, residual=True):
     from speculative_decoding_hydra_amd import round_from_inputs
 
-    return round_from_inputs(inp, device=device, keep_hidden=keep_hidden, fold_embedding=fold_embedding)
+    return round_from_inputs(inp, device=device, keep_hidden=keep_hidden, fold_embedding=fold_embedding,
+                             residual=residual)
 
 
 def run_round(rnd, dev, stream=None):
@@ -120,7 +121,7 @@ def check_draft(inp, rnd, seqs=None, rows=None):
                 p = int(row_node[r])
                 ptok = int(inp["root_tok"][b]) if p == 0 else int(ctok[b, p])
                 e = HI.as_f64(inp["E"][ptok])
-            u = O.head_hidden(h[b], e, W1, b1, True, bf16)
+            u = O.head_hidden(h[b], e, W1, b1, rnd.residual, bf16)
             if bf16:
                 # u is stored in bf16: a float32-vs-float64 difference in a can
                 # flip one rounding, so compare in units of the bf16 step

@@ -428,16 +428,18 @@ def test_draft_first_layer_split_and_fused(B, d, b1, hydra, fold):
     print(rep, flush=True)
 
 
+@pytest.mark.parametrize("residual", [True, False])
 @pytest.mark.parametrize("fold", [True, False])
 @pytest.mark.parametrize("tree", [("sparse", (10, 4, 2, 1), 64), ("cartesian", (3, 2, 2, 2))])
-def test_draft_four_heads_folded_and_streamed(tree, fold):
+def test_draft_four_heads_folded_and_streamed(tree, fold, residual):
     """Four Hydra heads at d = 4096 (the folded path's next-depth rows are
     written by each row merge, and the h half of head k + 2 streams inside
-    the merge of depth k), both against the oracle stage by stage."""
+    the merge of depth k), both against the oracle stage by stage, with and
+    without the residual connection."""
     w = HI.workload("7b_sparse64", B=2, V=3000, tree=tree, L=(64,))
-    print(f"four heads tree={tree} fold={fold}", flush=True)
+    print(f"four heads tree={tree} fold={fold} residual={residual}", flush=True)
     inp = HI.generate(w)
-    rnd, dev = T.round_inputs(inp, fold_embedding=fold)
+    rnd, dev = T.round_inputs(inp, fold_embedding=fold, residual=residual)
     assert (rnd.emb_proj is not None) == fold
     T.run_round(rnd, dev)
     torch.cuda.synchronize()

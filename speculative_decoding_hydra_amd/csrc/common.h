@@ -282,7 +282,7 @@ int launch_projection(int dtype, int M, int K, int N, XSource xs, const void* W,
 bool gemm_supported(int K);
 int launch_projection_gemm(int M, int K, int N, const bf16_t* X, int ldx, const bf16_t* W, int ldw, float* Y,
                            RowMap map, int ldy, TopkPartials tp, hipStream_t stream);
-constexpr int kGemmMinRows = 160;  // from here on the tiled kernel beats the streaming one
+constexpr int kGemmMinRows = 65;  // from here on the tiled kernel beats the streaming one
 
 // Finish the fused row reduction: log-sum-exp and sorted top-k of each row,
 // then either the candidate-tree fill (draft heads) or the arg max. The top-k

@@ -4,10 +4,12 @@
 // 16-sequence batch: M = 1024, 268 GFLOP against 262 MB of W) the projection
 // is bound by the matrix cores, not by HBM ("Parallel Verification and Greedy
 // Acceptance Algorithm" in "Hydra Guide: Sequentially-Dependent Speculative
-// AI": the target scores every tree row in one pass). Design for gfx950:
-//   * a workgroup computes a 256 (n) x 256 (m) tile; its 8 waves hold
-//     128 (n) x 64 (m) each in 32 v_mfma_f32_16x16x32_bf16 accumulators, so
-//     every operand read from LDS feeds 4 or 8 MFMAs;
+// AI": the target scores every tree row in one pass). From 65 rows on it also
+// beats the streaming kernel. Design for gfx950:
+//   * a workgroup computes a BN (n) x 256 (m) tile; its 8 waves hold
+//     BN / 2 (n) x 64 (m) each in v_mfma_f32_16x16x32_bf16 accumulators, so
+//     every operand read from LDS feeds 4 or BN / 32 MFMAs; BN = 256, or 128
+//     when one m tile covers M (twice the workgroups for 65-256 rows);
 //   * K advances in chunks of 64: the next chunk of W and X is loaded from
 //     global memory into registers while the current one is multiplied out
 //     of LDS (two LDS stages, one barrier per chunk);
@@ -21,7 +23,7 @@
 namespace hydra {
 namespace {
 
-constexpr int GBM = 256, GBN = 256, GBK = 64;
+constexpr int GBM = 256, GBK = 64;  // m tile and K chunk; the n tile BN is 256 or 128
 // LDS rows are GBK bf16 (128 bytes) with the 16-byte chunk c of row r stored
 // at position c ^ (r % 8): the MFMA operand reads (16 rows at one chunk per
 // 16 lanes) then hit distinct banks, which padded rows do not achieve on gfx950
@@ -71,8 +73,12 @@ __device__ __forceinline__ void col_ms(float& m, float& s) {
   ms_combine(m, s, __uint_as_float(c[1]), __uint_as_float(d[1]));
 }
 
+template <int BN>
 __global__ __launch_bounds__(GTHREADS, 2) void proj_gemm_kernel(GemmArgs a) {
-  __shared__ __align__(16) bf16_t wl[2][GBN * GROW];
+  constexpr int WN = BN / 2;        // n columns per wave
+  constexpr int NI = WN / 16;       // 16-column MFMA tiles per wave
+  constexpr int WLD = BN / 64;      // 16-byte W vectors per thread and chunk
+  __shared__ __align__(16) bf16_t wl[2][BN * GROW];
   __shared__ __align__(16) bf16_t xl[2][GBM * GROW];
   // XCD-aware order: workgroup b runs on XCD b % 8; slot s = b / 8 there
   // covers m tile s % mtiles of n tile (s / mtiles) * 8 + b % 8
@@ -81,44 +87,47 @@ __global__ __launch_bounds__(GTHREADS, 2) void proj_gemm_kernel(GemmArgs a) {
   const int ntile = (slot / a.mtiles) * 8 + (bx & 7);
   const int mtile = slot % a.mtiles;
   if (ntile >= a.ntiles) return;  // whole workgroup: no barrier is pending
-  const int n0 = ntile * GBN, m0 = mtile * GBM;
+  const int n0 = ntile * BN, m0 = mtile * GBM;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if (a.tp.clear && bx == 0 && tid < a.tp.nclear) a.tp.clear[tid] = 0;
-  const int wn = wave & 1, wm = wave >> 1;  // 2 x 4 waves: 128 n x 64 m each
+  const int wn = wave & 1, wm = wave >> 1;  // 2 x 4 waves: WN n x 64 m each
 
-  // global -> register staging: 4 vectors of 16 bytes of W and of X per thread
-  const bf16_t* wsrc[4];
+  // global -> register staging: WLD vectors of 16 bytes of W and 4 of X per thread
+  const bf16_t* wsrc[WLD];
   const bf16_t* xsrc[4];
-  int soff[4];
+  int woff[WLD], xoff[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int idx = tid + j * GTHREADS;
     const int r = idx >> 3, c = (idx & 7) * 8;
-    const int n = n0 + r < a.N ? n0 + r : a.N - 1;  // rows past the end re-read the last row
     const int m = m0 + r < a.M ? m0 + r : 0;
-    wsrc[j] = a.W + static_cast<size_t>(n) * a.ldw + c;
     xsrc[j] = a.X + static_cast<size_t>(m) * a.ldx + c;
-    soff[j] = swz(r, idx & 7);
+    xoff[j] = swz(r, idx & 7);
+    if (j < WLD) {
+      const int n = n0 + r < a.N ? n0 + r : a.N - 1;  // rows past the end re-read the last row
+      wsrc[j] = a.W + static_cast<size_t>(n) * a.ldw + c;
+      woff[j] = xoff[j];
+    }
   }
-  u32x4_t wreg[4], xreg[4];
+  u32x4_t wreg[WLD], xreg[4];
   auto load = [&](int k0) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      wreg[j] = *reinterpret_cast<const u32x4_t*>(wsrc[j] + k0);
+      if (j < WLD) wreg[j] = *reinterpret_cast<const u32x4_t*>(wsrc[j] + k0);
       xreg[j] = *reinterpret_cast<const u32x4_t*>(xsrc[j] + k0);
     }
   };
   auto store = [&](int st) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      *reinterpret_cast<u32x4_t*>(&wl[st][soff[j]]) = wreg[j];
-      *reinterpret_cast<u32x4_t*>(&xl[st][soff[j]]) = xreg[j];
+      if (j < WLD) *reinterpret_cast<u32x4_t*>(&wl[st][woff[j]]) = wreg[j];
+      *reinterpret_cast<u32x4_t*>(&xl[st][xoff[j]]) = xreg[j];
     }
   };
 
-  f32x4_t acc[8][4];
+  f32x4_t acc[NI][4];
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < NI; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
@@ -128,7 +137,7 @@ __global__ __launch_bounds__(GTHREADS, 2) void proj_gemm_kernel(GemmArgs a) {
   if (nk > 1) load(GBK);
   __syncthreads();
   // operand rows differ by multiples of 16, so the swizzle depends on the lane alone
-  const int arow = swz(wn * 128 + (lane & 15), lane >> 4), brow = swz(wm * 64 + (lane & 15), lane >> 4);
+  const int arow = swz(wn * WN + (lane & 15), lane >> 4), brow = swz(wm * 64 + (lane & 15), lane >> 4);
   const int ks1 = ((4 ^ ((lane >> 4) ^ (lane & 7))) - ((lane >> 4) ^ (lane & 7))) * 8;  // k step 1 minus k step 0
   for (int c = 0; c < nk; ++c) {
     const int st = c & 1;
@@ -141,7 +150,7 @@ __global__ __launch_bounds__(GTHREADS, 2) void proj_gemm_kernel(GemmArgs a) {
       for (int j = 0; j < 4; ++j)
         bv[j] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(&xl[st][brow + j * 16 * GROW + ks * ks1]));
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
+      for (int i = 0; i < NI; ++i) {
         const bf16x8_t av =
             __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(&wl[st][arow + i * 16 * GROW + ks * ks1]));
 #pragma unroll
@@ -152,14 +161,14 @@ __global__ __launch_bounds__(GTHREADS, 2) void proj_gemm_kernel(GemmArgs a) {
   }
 
   // D[n][m]: lane holds n = 16 i + 4 (lane / 16) + e, m = 16 j + lane % 16 of the wave tile
-  const int nb = n0 + wn * 128 + (lane >> 4) * 4;
+  const int nb = n0 + wn * WN + (lane >> 4) * 4;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int m = m0 + wm * 64 + j * 16 + (lane & 15);
     const bool mok = m < a.M;
     float* dst = a.Y + static_cast<size_t>(a.map(mok ? m : 0)) * a.ldy;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < NI; ++i) {
       const int n = nb + i * 16;
       if (!mok) continue;
       if (n + 3 < a.N && (a.ldy & 3) == 0) {
@@ -171,9 +180,9 @@ __global__ __launch_bounds__(GTHREADS, 2) void proj_gemm_kernel(GemmArgs a) {
       }
     }
     if (!a.tp.keys) continue;
-    // two 64-column blocks per wave: i = 0..3 and 4..7
+    // WN / 64 column blocks of 64 per wave: i = 4 bb .. 4 bb + 3
 #pragma unroll
-    for (int bb = 0; bb < 2; ++bb) {
+    for (int bb = 0; bb < WN / 64; ++bb) {
       float mx = -INFINITY;
       uint64_t best = 0;
 #pragma unroll
@@ -187,7 +196,7 @@ __global__ __launch_bounds__(GTHREADS, 2) void proj_gemm_kernel(GemmArgs a) {
           best = key > best ? key : best;
         }
       best = col_max_key(best);
-      const int col0 = n0 + wn * 128 + bb * kProjRowsPerWG;
+      const int col0 = n0 + wn * WN + bb * kProjRowsPerWG;
       const size_t slot_i = static_cast<size_t>(m) * projection_nwg(a.N) + col0 / kProjRowsPerWG;
       const bool writer = mok && (lane >> 4) == 0 && col0 < a.N;
       if (writer) a.tp.keys[slot_i] = best;
@@ -221,14 +230,17 @@ int launch_projection_gemm(int M, int K, int N, const bf16_t* X, int ldx, const 
   a.ldw = ldw;
   a.ldy = ldy;
   a.mtiles = (M + GBM - 1) / GBM;
-  a.ntiles = (N + GBN - 1) / GBN;
+  // one m tile: 128-column n tiles, so twice as many workgroups cover the chip
+  const int bn = a.mtiles == 1 ? 128 : 256;
+  a.ntiles = (N + bn - 1) / bn;
   a.X = X;
   a.W = W;
   a.Y = Y;
   a.map = map;
   a.tp = tp;
   const int slots = (a.ntiles + 7) / 8 * a.mtiles;  // per XCD
-  proj_gemm_kernel<<<slots * 8, GTHREADS, 0, stream>>>(a);
+  if (bn == 128) proj_gemm_kernel<128><<<slots * 8, GTHREADS, 0, stream>>>(a);
+  else proj_gemm_kernel<256><<<slots * 8, GTHREADS, 0, stream>>>(a);
   HY_LAUNCH_CHECK("projection(gemm)");
   return HYDRA_OK;
 }

@@ -36,7 +36,7 @@ def _bf16(x):
 @pytest.mark.parametrize("M,K,N", [(1, 256, 1000), (5, 512, 640), (16, 4096, 4096), (17, 256, 2000),
                                    (33, 1024, 777), (64, 4096, 32000), (100, 512, 1000), (256, 256, 512),
                                    (300, 256, 130), (13, 8192, 4096), (0, 256, 64), (1024, 1024, 3000),
-                                   (420, 2048, 1111)])
+                                   (420, 2048, 1111), (65, 1024, 3001), (200, 2048, 4100)])
 def test_projection_bf16(M, K, N):
     from speculative_decoding_hydra_amd import hydra_vocab_projection
 

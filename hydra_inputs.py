@@ -18,7 +18,8 @@ in this fixed order:
   5. target vocabulary projection W_t [V, d] ~ N(0, 0.02)
   6. prefix lengths L_b (fixed, or uniform in [lo, hi])
   7. per sequence: prefix K [L_b, Hkv, D], then prefix V, ~ N(0, 1)
-  8. page order: identity, or a random permutation of the pool
+  8. page order: identity, or a random permutation of the pool (the pool
+     holds each prefix plus a reserve of free positions after it)
   9. tree Q [B, N, Hq, D], tree K [B, N, Hkv, D], tree V ~ N(0, 1)
  10. uniforms u_acc [B, N], u_res [B, N] in [0, 1)  (stochastic mode only)
 
@@ -111,8 +112,14 @@ def _normal(g, shape, std, dtype):
     return x.to(dtype)
 
 
-def generate(w: Workload, n_tree: int | None = None) -> dict:
-    """Draw every input of one round for workload ``w`` (CPU tensors)."""
+def generate(w: Workload, n_tree: int | None = None, reserve: int | None = None) -> dict:
+    """Draw every input of one round for workload ``w`` (CPU tensors).
+
+    Each sequence's block table maps pages for its prefix plus ``reserve``
+    more positions (default: one round's commit, n_heads + 1 rows), zeroed.
+    """
+    if reserve is None:
+        reserve = w.n_heads + 1
     g = torch.Generator().manual_seed(w.seed)
     dt = w.torch_dtype
     N = w.n_tree if n_tree is None else n_tree
@@ -145,7 +152,7 @@ def generate(w: Workload, n_tree: int | None = None) -> dict:
         kp.append(_normal(g, (L, w.Hkv, w.D), 1.0, dt))
         vp.append(_normal(g, (L, w.Hkv, w.D), 1.0, dt))
     out["k_prefix"], out["v_prefix"] = kp, vp
-    pages_per = [math.ceil(L / PAGE) for L in lens]
+    pages_per = [math.ceil((L + reserve) / PAGE) for L in lens]
     n_pages = max(1, sum(pages_per))
     if w.scattered:
         order = torch.randperm(n_pages, generator=g).to(torch.int32)

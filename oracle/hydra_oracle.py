@@ -33,6 +33,9 @@ Readings of points the pages leave open (each is listed in the design doc):
 * Sparse template: rank paths with ranks below the per-depth fan-out caps,
   ordered by (2**depth * prod(rank + 1), depth, path) ascending; the first
   ``n_nodes - 1`` plus the root.
+* Commit after acceptance: the root and the accepted drafts take cache
+  positions L .. L + m in path order; the bonus token is the next root and
+  the hidden state of the last accepted row the next h.
 * Stochastic acceptance on a tree (rule S1): siblings are tried in rank order;
   after each rejection the target becomes the normalised residual while the
   draft distribution stays the same.
@@ -55,6 +58,7 @@ __all__ = [
     "head_hidden", "head_logits", "draft_heads", "prune_tree", "ancestors",
     "tree_mask", "tree_attention", "target_logits", "argmax_lowest",
     "greedy_accept", "residual", "sample_inverse_cdf", "rejection_accept",
+    "commit_path",
 ]
 
 
@@ -554,3 +558,70 @@ def rejection_accept(Z, head_z, q_row, tok, parent, u_acc, u_res, T, follow=None
             out.append(draw(r, u_res[u]))
             break
     return len(path) - 1, path, out
+
+
+# ---------------------------------------------------------------------------
+# After acceptance: commit of the kept branch into the paged KV cache
+# ---------------------------------------------------------------------------
+
+def commit_path(k_pages, v_pages, block_table, prefix_len, k_tree, v_tree,
+                n_acc, path, out_tok, dmax, hidden=None):
+    """Commit the accepted branch of every sequence to its KV cache.
+
+    [HG, "Production Engineering and Training Best Practices", items "Tree
+    KV-Cache Page Sizing" and "KV-Cache Tree Branch Management"]: the tree's
+    K/V live in statically reserved blocks, and rejected nodes are rolled back
+    without freeing anything. [SD, "The acceptance criterion"]: the next round
+    continues from the last accepted or resampled token and the rejected
+    suffix is dropped from the caches. [MH, "Tree Attention und Akzeptanz"]:
+    the longest accepted branch is kept and its last hidden state feeds the
+    heads next round.
+
+    Reading: the root (row 0, the last known token, not yet cached) and the
+    m accepted drafts path[1..m] go to cache positions L, ..., L + m in path
+    order; nothing else is written, so a rejected node never reaches the
+    cache. The emitted bonus (or resampled) token out_tok[m] is not cached:
+    it is the next round's root, and the hidden state of the last accepted
+    row path[m] is the next round's h. The next prefix length is L + m + 1.
+
+    k_pages, v_pages [n_layers, n_pages, Hkv, page_size, D]; block_table
+    [B, max_pages]; k_tree, v_tree [n_layers, B, N, Hkv, D]; n_acc [B];
+    path, out_tok [B, dmax + 1]; hidden [B, N, d] or None.
+    A position whose page index is past max_pages or whose page id is not in
+    [0, n_pages) is skipped; a sequence with m outside [0, dmax] or a path
+    row outside [0, N) commits nothing and gets next root -1.
+    Returns (k_pages, v_pages, next_len [B], next_root [B], next_h [B, d]
+    or None); the pools are new arrays.
+    """
+    kp = np.array(k_pages, dtype=np.float64, copy=True)
+    vp = np.array(v_pages, dtype=np.float64, copy=True)
+    kt = np.asarray(k_tree, dtype=np.float64)
+    vt = np.asarray(v_tree, dtype=np.float64)
+    n_pages, ps = kp.shape[1], kp.shape[3]
+    B, N = kt.shape[1], kt.shape[2]
+    max_pages = np.asarray(block_table).shape[1]
+    next_len = np.array([int(x) for x in prefix_len], dtype=np.int64)
+    next_root = -np.ones(B, dtype=np.int64)
+    next_h = None
+    if hidden is not None:
+        hid = np.asarray(hidden, dtype=np.float64)
+        next_h = np.zeros((B, hid.shape[2]))
+    for b in range(B):
+        L, m = int(prefix_len[b]), int(n_acc[b])
+        rows = [int(path[b][j]) for j in range(m + 1)] if 0 <= m <= dmax else []
+        if not rows or any(r < 0 or r >= N for r in rows):
+            continue
+        for j, r in enumerate(rows):
+            pos = L + j
+            if pos // ps >= max_pages:
+                continue
+            page = int(block_table[b][pos // ps])
+            if not 0 <= page < n_pages:
+                continue
+            kp[:, page, :, pos % ps, :] = kt[:, b, r]
+            vp[:, page, :, pos % ps, :] = vt[:, b, r]
+        next_len[b] = L + m + 1
+        next_root[b] = int(out_tok[b][m])
+        if hidden is not None:
+            next_h[b] = hid[b, rows[-1]]
+    return kp, vp, next_len, next_root, next_h

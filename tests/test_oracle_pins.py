@@ -501,3 +501,104 @@ def test_expected_yield_monte_carlo(golden):
 def test_oracle_package_exports():
     for name in H.__all__:
         assert hasattr(oracle, name)
+
+
+# -------------------------------------------------------------------- commit
+
+def _paged_pool(rng, lens, reserve, n_layers, Hkv, D, ps):
+    """Prefix K/V [n_layers][b] -> a scattered page pool with room for
+    `reserve` more positions per sequence (test-side placement)."""
+    per = [-(-(L + reserve) // ps) for L in lens]
+    n_pages = sum(per) + 2  # two spare pages nobody maps
+    order = rng.permutation(n_pages)
+    bt = -np.ones((len(lens), max(per)), dtype=np.int64)
+    kpool = rng.standard_normal((n_layers, n_pages, Hkv, ps, D))  # garbage outside the prefixes
+    vpool = rng.standard_normal((n_layers, n_pages, Hkv, ps, D))
+    kpre = [rng.standard_normal((n_layers, L, Hkv, D)) for L in lens]
+    vpre = [rng.standard_normal((n_layers, L, Hkv, D)) for L in lens]
+    nxt = 0
+    for b, L in enumerate(lens):
+        for j in range(per[b]):
+            bt[b, j] = order[nxt]
+            nxt += 1
+        for pos in range(L):
+            kpool[:, bt[b, pos // ps], :, pos % ps] = kpre[b][:, pos]
+            vpool[:, bt[b, pos // ps], :, pos % ps] = vpre[b][:, pos]
+    return kpool, vpool, bt, kpre, vpre
+
+
+def _gather(pool, bt, b, n, ps):
+    """Positions 0..n-1 of sequence b read back through its block table."""
+    return np.stack([pool[:, bt[b, p // ps], :, p % ps] for p in range(n)], axis=1)
+
+
+@pytest.mark.parametrize("tree,ps", [([2, 3], 4), ([1, 1, 1, 1], 4), ([3, 2, 2], 16)])
+def test_commit_turns_the_kept_branch_into_causal_attention(tree, ps):
+    """After the commit, attention of the kept rows over the cache with a
+    plain causal mask equals the tree-masked attention they had in the verify
+    pass (the tree mask hides exactly the nodes off the branch)."""
+    rng = np.random.default_rng(40 + ps + len(tree))
+    plan = H.plan_cartesian(tree)
+    N, Hq, Hkv, D, nl, dmax = plan.n, 4, 2, 8, 2, plan.dmax
+    lens = [5, 7, 16]
+    B = len(lens)
+    kpool, vpool, bt, kpre, vpre = _paged_pool(rng, lens, dmax + 1, nl, Hkv, D, ps)
+    q = rng.standard_normal((B, N, Hq, D))
+    kt, vt = rng.standard_normal((nl, B, N, Hkv, D)), rng.standard_normal((nl, B, N, Hkv, D))
+    anc = np.stack([H.ancestors(plan.parent, dmax)] * B)
+    hidden = rng.standard_normal((B, N, 6))
+    # kept branch of each sequence: root -> a random node (the root alone for b = 0)
+    ends = [0] + [int(rng.integers(1, N)) for _ in range(B - 1)]
+    path = -np.ones((B, dmax + 1), dtype=np.int64)
+    out_tok = -np.ones((B, dmax + 1), dtype=np.int64)
+    n_acc = np.zeros(B, dtype=np.int64)
+    for b, e in enumerate(ends):
+        br = [int(a) for a in anc[b, e] if a >= 0]
+        n_acc[b] = len(br) - 1
+        path[b, : len(br)] = br
+        out_tok[b, : len(br)] = rng.integers(0, 100, len(br))
+    kp2, vp2, nlen, nroot, nh = H.commit_path(kpool, vpool, bt, lens, kt, vt, n_acc, path, out_tok, dmax, hidden)
+    for b in range(B):
+        m, L = int(n_acc[b]), lens[b]
+        assert nlen[b] == L + m + 1 and nroot[b] == out_tok[b, m]
+        assert np.array_equal(nh[b], hidden[b, path[b, m]])
+        br = [int(x) for x in path[b, : m + 1]]
+        for layer in range(nl):
+            o, _ = H.tree_attention(q[b:b + 1], kt[layer, b:b + 1], vt[layer, b:b + 1], [kpre[b][layer]],
+                                    [vpre[b][layer]], anc[b:b + 1])
+            ks = _gather(kp2, bt, b, L + m + 1, ps)[layer]
+            vs = _gather(vp2, bt, b, L + m + 1, ps)[layer]
+            qs = np.concatenate([np.zeros((L, Hq, D)), q[b, br]])
+            ref = _causal_sdpa(torch.from_numpy(qs), torch.from_numpy(ks), torch.from_numpy(vs)).numpy()[L:]
+            assert np.allclose(o[0, br], ref, rtol=1e-10, atol=1e-12)
+
+
+def test_commit_writes_only_the_kept_positions():
+    rng = np.random.default_rng(47)
+    plan = H.plan_cartesian([2, 2])
+    N, Hkv, D, nl, dmax, ps = plan.n, 2, 4, 1, plan.dmax, 4
+    lens = [3, 8, 6, 2]
+    B = len(lens)
+    kpool, vpool, bt, _, _ = _paged_pool(rng, lens, dmax + 1, nl, Hkv, D, ps)
+    kt, vt = rng.standard_normal((nl, B, N, Hkv, D)), rng.standard_normal((nl, B, N, Hkv, D))
+    path = np.array([[0, 2, 6], [0, 1, -1], [0, 1, 3], [0, 2, 5]])
+    out_tok = np.array([[7, 8, 9], [4, 5, -1], [1, 2, 3], [6, 6, 6]])
+    n_acc = np.array([2, 1, 5, 2])   # sequence 2: count past dmax
+    bt = bt.copy()
+    bt[3, (lens[3] + 2) // ps] = -1  # sequence 3: the page of its position L + 2 is unmapped
+    kp2, vp2, nlen, nroot, _ = H.commit_path(kpool, vpool, bt, lens, kt, vt, n_acc, path, out_tok, dmax)
+    expect_k, expect_v = kpool.copy(), vpool.copy()
+    for b in (0, 1, 3):
+        for j in range(int(n_acc[b]) + 1):
+            pos = lens[b] + j
+            if bt[b, pos // ps] < 0:
+                continue
+            expect_k[:, bt[b, pos // ps], :, pos % ps] = kt[:, b, path[b, j]]
+            expect_v[:, bt[b, pos // ps], :, pos % ps] = vt[:, b, path[b, j]]
+    assert np.array_equal(kp2, expect_k) and np.array_equal(vp2, expect_v)
+    assert not np.array_equal(kp2, kpool)
+    assert list(nlen) == [lens[0] + 3, lens[1] + 2, lens[2], lens[3] + 3]
+    assert list(nroot) == [9, 5, -1, 6]
+    # pages no block table maps are untouched
+    spare = sorted(set(range(kpool.shape[1])) - set(int(x) for x in bt.ravel()))
+    assert len(spare) >= 2 and np.array_equal(kp2[:, spare], kpool[:, spare])

@@ -3,7 +3,8 @@
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-graph] [--no-cpu] [--no-fold]
 
 A step is one whole round (draft heads -> tree build -> tree-attention verify
--> accept) over the workload's synthetic batch, with every input resident in
+-> accept -> commit of the kept branch into the KV cache) over the workload's
+synthetic batch, with every input resident in
 HBM before timing starts. The default workload is the Vicuna-7B-shaped layer
 with the 64-node sparse tree and a 2048-token prefix (batch 1). The value is
 verified tree rows per second, B * N / t_round. Hydra heads use their folded
@@ -76,8 +77,9 @@ def measured_traffic():
 def round_bytes(w, rnd, prefix_len):
     """Algorithmic HBM bytes of one round: every weight matrix the round
     needs streamed once, the paged prefix K/V read once, the tree Q/K/V/O,
-    the logits written, and (folded Hydra heads) one float32 table row per
-    head row instead of W1's embedding half."""
+    the logits written, (folded Hydra heads) one float32 table row per head
+    row instead of W1's embedding half, and the commit's K/V rows (read and
+    written) plus the next hidden state."""
     d, V, B, esz = w.d, w.V, w.B, 2 if w.dtype == "bf16" else 4
     R, N, heads = rnd.dplan.R, rnd.n_keep, rnd.dplan.dmax
     rows_per_head = [int(rnd.dplan.rows.row_first[k + 1] - rnd.dplan.rows.row_first[k]) for k in range(heads)]
@@ -94,7 +96,9 @@ def round_bytes(w, rnd, prefix_len):
     prefix = int(prefix_len.sum())
     attn = prefix * w.Hkv * w.D * esz * 2 + B * N * (2 * w.Hq + 2 * w.Hkv) * w.D * esz
     target = V * d * esz + B * N * d * esz + B * N * V * 4
-    return draft + attn + target
+    kept = int(rnd.n_accepted.clamp(min=0).sum()) + B  # root + accepted rows
+    commit = kept * w.Hkv * w.D * esz * 2 * 2 + B * d * esz * 2
+    return draft + attn + target + commit
 
 
 def cpu_baseline(inp, n_rows):
@@ -111,6 +115,8 @@ def cpu_baseline(inp, n_rows):
     kp = [f(x) for x in inp["k_prefix"]]
     vp = [f(x) for x in inp["v_prefix"]]
     q, kt, vt = f(inp["q_tree"]), f(inp["k_tree"]), f(inp["v_tree"])
+    kpool, vpool = f(inp["k_pages"])[None], f(inp["v_pages"])[None]
+    bt, lens = inp["block_table"].numpy(), inp["prefix_len"].numpy()
     kind = w.tree[0]
     plan = O.plan_sparse_template(w.tree[1], w.tree[2]) if kind == "sparse" else O.plan_cartesian(w.tree[1])
     try:
@@ -130,8 +136,14 @@ def cpu_baseline(inp, n_rows):
         anc = np.stack([O.ancestors(t.parent, plan.dmax) for t, _ in trees])
         out, _ = O.tree_attention(q, kt, vt, kp, vp, anc, bf16=w.dtype == "bf16")
         Z = O.target_logits(out, Wt)
+        n_acc = np.zeros(w.B, dtype=np.int64)
+        path = -np.ones((w.B, plan.dmax + 1), dtype=np.int64)
+        toks = -np.ones((w.B, plan.dmax + 1), dtype=np.int64)
         for b, (t, s) in enumerate(trees):
-            O.greedy_accept(Z[b], res["tok"][b][s], t.parent, plan.dmax)
+            m, pth, tk = O.greedy_accept(Z[b], res["tok"][b][s], t.parent, plan.dmax)
+            n_acc[b], path[b, : m + 1], toks[b, : m + 1] = m, pth, tk
+        O.commit_path(kpool, vpool, bt, lens, kt[None], vt[None], n_acc, path, toks, plan.dmax,
+                      out.reshape(w.B, out.shape[1], -1))
         total += time.perf_counter() - t0
         reps += 1
     dt = total / reps
@@ -215,8 +227,8 @@ def main():
     round_ms = {"median": pick(0.5), "p10": pick(0.1), "p90": pick(0.9)}
 
     # per-stage times (eager, events on the launch stream)
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
-    stage_ms = [0.0] * 4
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+    stage_ms = [0.0] * 5
     reps = 10
     for _ in range(reps):
         ev[0].record(stream)
@@ -229,8 +241,11 @@ def main():
         ev[3].record(stream)
         rnd.accept(dev.get("u_acc"), dev.get("u_res"))
         ev[4].record(stream)
+        rnd.commit(dev["k_tree"], dev["v_tree"], dev["k_pages"], dev["v_pages"], dev["block_table"],
+                   dev["prefix_len"])
+        ev[5].record(stream)
         torch.cuda.synchronize()
-        for i in range(4):
+        for i in range(5):
             stage_ms[i] += ev[i].elapsed_time(ev[i + 1]) / reps
 
     # dominant kernel: the [V, d] vocabulary projection of a head (largest row count of the round)
@@ -319,7 +334,7 @@ def main():
         "round_bytes": rbytes,
         "round_hbm_frac": rbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "stages_ms": {"draft": stage_ms[0], "build": stage_ms[1], "attention": stage_ms[2],
-                      "accept": stage_ms[3]},
+                      "accept": stage_ms[3], "commit": stage_ms[4]},
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)

@@ -169,8 +169,9 @@ def generate(w: Workload, n_tree: int | None = None, reserve: int | None = None)
             nxt += 1
             block_table[b, j] = pid
             lo, hi = j * PAGE, min(L, (j + 1) * PAGE)
-            k_pages[pid, :, : hi - lo] = kp[b][lo:hi].transpose(0, 1)
-            v_pages[pid, :, : hi - lo] = vp[b][lo:hi].transpose(0, 1)
+            if hi > lo:  # pages past the prefix stay zero (the reserve)
+                k_pages[pid, :, : hi - lo] = kp[b][lo:hi].transpose(0, 1)
+                v_pages[pid, :, : hi - lo] = vp[b][lo:hi].transpose(0, 1)
     out["block_table"], out["k_pages"], out["v_pages"] = block_table, k_pages, v_pages
     out["page_size"] = PAGE
 

@@ -7,6 +7,7 @@
  *   tree_build             final tree (identity or pruned), ancestor table
  *   tree_attention_verify  tree-masked attention over a paged KV prefix
  *   tree_accept            target vocabulary projection + acceptance walk
+ *   tree_commit            kept branch into the paged KV cache, next root and h
  * plus host-side tree-plan builders, workspace-size queries and status strings.
  *
  * Sources (cited by page title and section):
@@ -314,6 +315,54 @@ int tree_accept(int dtype, int mode, int B, int N, int d, int V, int Dmax,
                 const float* u_res, float* target_logits, int32_t* n_accepted,
                 int32_t* path, int32_t* out_tok, void* ws, size_t ws_bytes,
                 void* stream);
+
+/* ------------------------------------------------------------------------
+ * After acceptance: commit of the kept branch into the paged KV cache
+ *
+ * [HG] "Production Engineering and Training Best Practices" (tree KV-cache
+ * items): tree K/V live in statically reserved blocks and rejected nodes are
+ * rolled back without freeing memory; [SD] "The acceptance criterion": the
+ * next round starts from the last accepted or resampled token; [MH] "Tree
+ * Attention und Akzeptanz": the kept branch's last hidden state feeds the
+ * heads next round. Per sequence b with L = prefix_len[b], m = n_accepted[b]:
+ *   for j = 0..m: cache position L + j of every layer <- K/V of tree row
+ *                 path[b, j] (the root, then the accepted drafts);
+ *   next_prefix_len[b] = L + m + 1;  next_root_tok[b] = out_tok[b, m]
+ *   (the bonus or resampled token, which is not cached);
+ *   next_h[b] = hidden[b, path[b, m]] (when hidden is given).
+ * Rejected rows are never written, and nothing is freed or cleared.
+ *
+ * k_tree, v_tree     [n_layers, B, N, Hkv, D] (dtype), tree rows of the
+ *                    verify pass (tree_attention_verify's k_tree/v_tree
+ *                    stacked over layers)
+ * k_pages, v_pages   in/out [n_layers, n_pages, Hkv, page_size, D] (dtype);
+ *                    one block_table for every layer (tree_attention_verify
+ *                    layout per layer)
+ * block_table        [B, max_pages] int32; the caller maps pages for
+ *                    positions up to L + Dmax (a position whose page index is
+ *                    >= max_pages or whose page id is outside [0, n_pages) is
+ *                    skipped, never written out of bounds)
+ * prefix_len         [B] int32
+ * n_accepted, path, out_tok  [B], [B, Dmax+1], [B, Dmax+1] int32 from
+ *                    tree_accept; a sequence with m outside [0, Dmax] or a
+ *                    path row outside [0, N) commits nothing: its next length
+ *                    is L, its next root -1 and its next_h row is untouched
+ * hidden             [B, N, d] (dtype) per-row hidden state (the attention
+ *                    output o of tree_accept) or NULL; then next_h is NULL
+ * next_prefix_len    out [B] int32 (must not alias prefix_len)
+ * next_root_tok      out [B] int32
+ * next_h             out [B, d] (dtype) or NULL
+ * Buffers of K/V and hidden states are 16-byte aligned; D % 8 == 0 and, with
+ * hidden, d % 8 == 0. No workspace. B = 0 is a no-op.
+ * ---------------------------------------------------------------------- */
+int tree_commit(int dtype, int n_layers, int B, int N, int Hkv, int D, int Dmax,
+                const void* k_tree, const void* v_tree, void* k_pages,
+                void* v_pages, int n_pages, int page_size,
+                const int32_t* block_table, int max_pages,
+                const int32_t* prefix_len, const int32_t* n_accepted,
+                const int32_t* path, const int32_t* out_tok, int d,
+                const void* hidden, int32_t* next_prefix_len,
+                int32_t* next_root_tok, void* next_h, void* stream);
 
 #ifdef __cplusplus
 }

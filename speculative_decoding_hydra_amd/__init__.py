@@ -1,14 +1,15 @@
 """MI355X-native Hydra/Medusa draft-and-verify round (libhydra, HIP for gfx950).
 
-The four stages are the C entry points of include/hydra.h, bound under the same
-names in ``speculative_decoding_hydra_amd.hydra``; ``HydraRound`` allocates the
-buffers of a round and calls them in order.
+The four stages and the commit of the kept branch are the C entry points of
+include/hydra.h, bound under the same names in
+``speculative_decoding_hydra_amd.hydra``; ``HydraRound`` allocates the buffers
+of a round and calls them in order.
 """
 from .hydra import (  # noqa: F401
     DevicePlan, HydraError, PlanRows, TreePlan, hydra_draft_heads, hydra_draft_heads_workspace_size,
     hydra_fold_embedding, hydra_plan_cartesian, hydra_plan_rows, hydra_plan_sparse, hydra_vocab_projection,
     hydra_vocab_projection_workspace_size, hydra_vocab_topk, tree_accept,
     tree_accept_workspace_size, tree_attention_verify, tree_attention_verify_workspace_size, tree_build,
-    tree_build_workspace_size,
+    tree_build_workspace_size, tree_commit,
 )
 from .round import HydraRound, make_plan, round_from_inputs, run_round  # noqa: F401

@@ -311,3 +311,44 @@ def tree_accept(o, W_t, tok, parent, target_logits, n_accepted, path, out_tok, w
         _dev(n_accepted, "n_accepted", torch.int32), _dev(path, "path", torch.int32),
         _dev(out_tok, "out_tok", torch.int32), wsp, wsb, _stream(stream))
     return _check("tree_accept", rc)
+
+
+def tree_commit(k_tree, v_tree, k_pages, v_pages, block_table, prefix_len, n_accepted, path, out_tok,
+                next_prefix_len, next_root_tok, hidden=None, next_h=None, stream=None):
+    """Kept branch into the paged KV cache (see include/hydra.h).
+
+    k_tree/v_tree [B, N, Hkv, D] or [n_layers, B, N, Hkv, D]; k_pages/v_pages
+    [n_pages, Hkv, page, D] or [n_layers, n_pages, Hkv, page, D] (in/out);
+    hidden [B, N, d] and next_h [B, d] optional."""
+    if k_tree.dim() == 4:
+        k_tree, v_tree = k_tree.unsqueeze(0), v_tree.unsqueeze(0)
+    if k_pages.dim() == 4:
+        k_pages, v_pages = k_pages.unsqueeze(0), v_pages.unsqueeze(0)
+    n_layers, B, N, Hkv, D = k_tree.shape
+    if k_pages.shape[0] != n_layers or tuple(k_pages.shape[2:]) != (Hkv, k_pages.shape[3], D):
+        raise ValueError(f"tree_commit: pages {tuple(k_pages.shape)} do not match tree K/V {tuple(k_tree.shape)}")
+    n_pages, page_size = k_pages.shape[1], k_pages.shape[3]
+    max_pages = block_table.shape[1]
+    Dmax = path.shape[1] - 1
+    d = hidden.shape[2] if hidden is not None else 0
+    want = {"v_tree": (v_tree, tuple(k_tree.shape)), "v_pages": (v_pages, tuple(k_pages.shape)),
+            "block_table": (block_table, (B, max_pages)), "prefix_len": (prefix_len, (B,)),
+            "n_accepted": (n_accepted, (B,)), "path": (path, (B, Dmax + 1)), "out_tok": (out_tok, (B, Dmax + 1)),
+            "next_prefix_len": (next_prefix_len, (B,)), "next_root_tok": (next_root_tok, (B,))}
+    if hidden is not None:
+        want["hidden"] = (hidden, (B, N, d))
+        if next_h is not None:
+            want["next_h"] = (next_h, (B, d))
+    for name, (t, shape) in want.items():
+        if tuple(t.shape) != shape:
+            raise ValueError(f"tree_commit: {name} has shape {tuple(t.shape)}, expected {shape}")
+    dt = k_tree.dtype
+    rc = lib().tree_commit(
+        _dtype_code(k_tree), n_layers, B, N, Hkv, D, Dmax, _dev(k_tree, "k_tree"), _dev(v_tree, "v_tree", dt),
+        _dev(k_pages, "k_pages", dt), _dev(v_pages, "v_pages", dt), n_pages, page_size,
+        _dev(block_table, "block_table", torch.int32), max_pages, _dev(prefix_len, "prefix_len", torch.int32),
+        _dev(n_accepted, "n_accepted", torch.int32), _dev(path, "path", torch.int32),
+        _dev(out_tok, "out_tok", torch.int32), d, _dev(hidden, "hidden", dt),
+        _dev(next_prefix_len, "next_prefix_len", torch.int32), _dev(next_root_tok, "next_root_tok", torch.int32),
+        _dev(next_h, "next_h", dt), _stream(stream))
+    return _check("tree_commit", rc)

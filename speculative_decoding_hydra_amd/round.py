@@ -1,4 +1,5 @@
-"""One draft-and-verify round: buffers plus the four library calls in order.
+"""One draft-and-verify round: buffers plus the library calls in order (the
+four stages, then the commit of the kept branch into the KV cache).
 
 Allocation and sequencing only; every step of the round runs in libhydra's
 kernels. Buffers are allocated once per shape so a round can be replayed (or
@@ -66,6 +67,10 @@ class HydraRound:
         self.n_accepted = z(B, dtype=i32)
         self.path = z(B, Dm + 1, dtype=i32)
         self.out_tok = z(B, Dm + 1, dtype=i32)
+        # handed to the next round by the commit
+        self.next_prefix_len = z(B, dtype=i32)
+        self.next_root_tok = z(B, dtype=i32)
+        self.next_h = z(B, Hq * D, dtype=dt)
         nb = lambda n: torch.empty(max(int(n), 1), dtype=torch.uint8, device=device)  # noqa: E731
         self.ws_draft = nb(H.hydra_draft_heads_workspace_size(code, B, d, V, hydra, self.dplan))
         self.ws_build = nb(H.tree_build_workspace_size(B, N, K))
@@ -102,12 +107,21 @@ class HydraRound:
                       temperature=self.T, q_row=self.q_row, head_logits=self.head_logits, u_acc=u_acc,
                       u_res=u_res, stream=stream)
 
+    def commit(self, k_tree, v_tree, k_pages, v_pages, block_table, prefix_len, stream=None):
+        """Root and accepted rows into the paged cache (in place); next
+        prefix lengths, roots and hidden states into next_*."""
+        B, K = self.attn_out.shape[:2]
+        H.tree_commit(k_tree, v_tree, k_pages, v_pages, block_table, prefix_len, self.n_accepted, self.path,
+                      self.out_tok, self.next_prefix_len, self.next_root_tok, hidden=self.attn_out.view(B, K, -1),
+                      next_h=self.next_h, stream=stream)
+
     def run(self, h, root_tok, q, k_tree, v_tree, k_pages, v_pages, block_table, prefix_len, u_acc=None,
             u_res=None, stream=None):
         self.draft(h, root_tok, stream)
         self.build(stream)
         self.attend(q, k_tree, v_tree, k_pages, v_pages, block_table, prefix_len, stream)
         self.accept(u_acc, u_res, stream)
+        self.commit(k_tree, v_tree, k_pages, v_pages, block_table, prefix_len, stream)
 
 
 def round_from_inputs(inp, device="cuda", keep_hidden=True, fold_embedding=None, residual=True):

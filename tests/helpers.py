@@ -256,3 +256,42 @@ def ambiguous_sample(r, u, eps=1e-6):
     c = np.cumsum(np.asarray(r, dtype=np.float64))
     thr = u * c[-1]
     return float(np.min(np.abs(c - thr))) < eps * c[-1] or math.isclose(thr, 0.0)
+
+
+def check_commit(inp, rnd, dev, seqs=None):
+    """Commit after the round, stage-wise: the oracle commits the device's
+    accepted branches (sub-pools of the sampled sequences, bit-exact); on the
+    whole pool, nothing but the committed positions differs from the input."""
+    w = inp["workload"]
+    seqs = range(w.B) if seqs is None else seqs
+    n_acc, path, out = np_(rnd.n_accepted), np_(rnd.path), np_(rnd.out_tok)
+    Dm = rnd.dplan.dmax
+    lens = inp["prefix_len"].numpy()
+    bt = inp["block_table"].numpy()
+    ps = int(inp["page_size"])
+    nlen, nroot, nh = np_(rnd.next_prefix_len), np_(rnd.next_root_tok), rnd.next_h
+    B, K = rnd.attn_out.shape[:2]
+    hid = rnd.attn_out.view(B, K, -1)
+    for b in seqs:
+        pages = [int(p) for p in bt[b] if p >= 0]
+        sub_bt = np.arange(len(pages))[None]
+        sub = lambda pool: HI.as_f64(pool[pages])[None]  # noqa: E731
+        rk, rv, rl, rr, _ = O.commit_path(sub(inp["k_pages"]), sub(inp["v_pages"]), sub_bt, lens[b:b + 1],
+                                          HI.as_f64(inp["k_tree"][b:b + 1])[None],
+                                          HI.as_f64(inp["v_tree"][b:b + 1])[None], n_acc[b:b + 1],
+                                          path[b:b + 1], out[b:b + 1], Dm)
+        assert np.array_equal(np_(dev["k_pages"][pages]), rk[0]), f"seq {b}: committed K pages"
+        assert np.array_equal(np_(dev["v_pages"][pages]), rv[0]), f"seq {b}: committed V pages"
+        assert nlen[b] == rl[0] and nroot[b] == rr[0], f"seq {b}: next length / root"
+        assert torch.equal(nh[b], hid[b, int(path[b, n_acc[b]])]), f"seq {b}: next h"
+    # whole pool: differences only at committed positions
+    for name in ("k_pages", "v_pages"):
+        ne = dev[name] != inp[name].to(dev[name].device)        # [pages, Hkv, slot, D]
+        diff = ne.permute(0, 2, 1, 3).flatten(2).any(dim=2)      # [pages, slot]
+        diff = diff.cpu().numpy().copy()
+        for b in range(w.B):
+            for j in range(int(n_acc[b]) + 1):
+                pos = int(lens[b]) + j
+                diff[bt[b, pos // ps], pos % ps] = False
+        assert not diff.any(), f"{name}: {int(diff.sum())} positions changed outside the committed branches"
+    return dict(accepted=[int(x) for x in n_acc])

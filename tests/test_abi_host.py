@@ -33,7 +33,7 @@ def lib():
 
 def test_header_declares_the_four_stages():
     names = set(header_functions())
-    for fn in ("hydra_draft_heads", "tree_build", "tree_attention_verify", "tree_accept"):
+    for fn in ("hydra_draft_heads", "tree_build", "tree_attention_verify", "tree_accept", "tree_commit"):
         assert fn in names
 
 
@@ -54,7 +54,7 @@ def test_every_declared_symbol_is_exported_and_bound(lib):
 def test_status_strings(lib):
     assert lib.hydra_status_string(0) == b"ok"
     assert lib.hydra_status_string(-3) == b"workspace too small"
-    assert lib.hydra_abi_version() == 3
+    assert lib.hydra_abi_version() == 4
 
 
 @pytest.mark.parametrize("b", [[2, 3], [3, 2, 2], [4, 4, 4, 4], [1, 1, 1, 1, 1], [5, 2], [2, 1, 3]])
@@ -153,3 +153,29 @@ def test_binding_fails_loudly_without_the_library(monkeypatch):
     monkeypatch.setattr(L, "_lib", None)
     with pytest.raises(RuntimeError, match="no fallback"):
         L.lib()
+
+
+def test_tree_commit_rejects_bad_arguments_before_any_launch(lib):
+    """Argument checks of tree_commit run on the host; fake (aligned,
+    non-null) device addresses are never dereferenced on these paths."""
+    p = [4096 * (i + 1) for i in range(16)]
+    I32 = C.POINTER(C.c_int32)
+
+    def call(dtype=1, layers=1, B=2, N=9, Hkv=8, D=32, Dmax=2, prefix=None, nxt=None, hidden=None, next_h=None,
+             k_tree=None, d=0):
+        ip = lambda a: C.cast(C.c_void_p(a), I32)  # noqa: E731
+        return lib.tree_commit(dtype, layers, B, N, Hkv, D, Dmax, k_tree or p[0], p[1], p[2], p[3], 10, 16,
+                               ip(p[4]), 4, ip(prefix or p[5]), ip(p[6]), ip(p[7]), ip(p[8]), d, hidden,
+                               ip(nxt or p[9]), ip(p[10]), next_h, None)
+
+    assert call(B=0) == 0                           # nothing to do
+    assert call(dtype=7) == -1
+    assert call(layers=0) == -1
+    assert call(Dmax=9) == -1
+    assert call(D=12) == -2                         # 16-byte vectors need D % 8 == 0
+    assert call(prefix=p[9], nxt=p[9]) == -1        # next length aliases the input length
+    assert b"alias" in lib.hydra_last_error()
+    assert call(hidden=p[11]) == -1                 # hidden without next_h
+    assert call(hidden=p[11], next_h=p[12], d=12) == -2
+    assert call(k_tree=p[0] + 8) == -1              # misaligned K
+    assert b"aligned" in lib.hydra_last_error()

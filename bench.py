@@ -16,6 +16,8 @@ The JSON line also carries
                 that streams a [V, d] bf16 matrix): algorithmic bytes per
                 launch / average launch duration from HIP events on its stream,
                 against the 8 TB/s HBM peak;
+  commit_32_layers  the commit kernel moving each sequence's deepest kept
+                branch across 32 layers of caches (bytes, time, HBM fraction);
   cpu_baseline  the CPU oracle timed on this host on one full round of the
                 same workload (rank 0, one GPU only).
 """
@@ -99,6 +101,58 @@ def round_bytes(w, rnd, prefix_len):
     kept = int(rnd.n_accepted.clamp(min=0).sum()) + B  # root + accepted rows
     commit = kept * w.Hkv * w.D * esz * 2 * 2 + B * d * esz * 2
     return draft + attn + target + commit
+
+
+def commit_measure(w, rnd, dev, stream, layers=32, reps=20, use_graph=True):
+    """The commit kernel at model depth: the round's own commit moves one
+    layer (and, with random weights, only the root), so this times the
+    commit of each sequence's deepest kept branch across a `layers`-deep
+    stack of caches (synthetic tree K/V, the round's block table)."""
+    import torch
+
+    from speculative_decoding_hydra_amd import tree_commit
+
+    B, K = rnd.attn_out.shape[:2]
+    dt = rnd.dtype
+    n_pages, _, ps, _ = dev["k_pages"].shape
+    kt = torch.randn(layers, B, K, w.Hkv, w.D, device="cuda").to(dt)
+    vt = torch.randn(layers, B, K, w.Hkv, w.D, device="cuda").to(dt)
+    kp = torch.zeros(layers, n_pages, w.Hkv, ps, w.D, dtype=dt, device="cuda")
+    vp = torch.zeros_like(kp)
+    deepest = rnd.depth.argmax(dim=1)
+    n_acc = rnd.depth.gather(1, deepest[:, None])[:, 0].contiguous()
+    path = rnd.anc[torch.arange(B, device="cuda"), deepest].contiguous()
+    out_tok = torch.zeros_like(path)
+    nlen = torch.empty(B, dtype=torch.int32, device="cuda")
+    nroot = torch.empty_like(nlen)
+    hidden = rnd.attn_out.view(B, K, -1)
+    nh = torch.empty(B, hidden.shape[2], dtype=dt, device="cuda")
+    launch = lambda: tree_commit(kt, vt, kp, vp, dev["block_table"], dev["prefix_len"], n_acc, path,  # noqa: E731
+                                 out_tok, nlen, nroot, hidden=hidden, next_h=nh)
+    launch()
+    torch.cuda.synchronize()
+    g = None
+    if use_graph:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(reps):
+                launch()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record(stream)
+    if g is not None:
+        g.replay()
+    else:
+        for _ in range(reps):
+            launch()
+    b.record(stream)
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) / reps * 1e3
+    rows = int(n_acc.sum()) + B
+    esz = kt.element_size()
+    nbytes = layers * rows * w.Hkv * w.D * esz * 2 * 2 + B * hidden.shape[2] * esz * 2
+    return {"layers": layers, "rows_per_layer": rows, "bytes": nbytes, "avg_launch_us": us,
+            "achieved_GBps": nbytes / (us * 1e-6) / 1e9, "frac_of_hbm_peak": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS}
 
 
 def cpu_baseline(inp, n_rows):
@@ -301,6 +355,7 @@ def main():
     alg_bytes = w.V * w.d * esz + M * w.d * esz + M * w.V * 4
     achieved = alg_bytes / (k_ms * 1e-3) / 1e9
 
+    commit = commit_measure(w, rnd, dev, stream, use_graph=not args.no_graph)
     rbytes = round_bytes(w, rnd, inp["prefix_len"])
     cpu = None
     if not args.no_cpu:
@@ -335,6 +390,7 @@ def main():
         "round_hbm_frac": rbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "stages_ms": {"draft": stage_ms[0], "build": stage_ms[1], "attention": stage_ms[2],
                       "accept": stage_ms[3], "commit": stage_ms[4]},
+        "commit_32_layers": commit,
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)

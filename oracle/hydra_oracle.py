@@ -33,6 +33,10 @@ Readings of points the pages leave open (each is listed in the design doc):
 * Sparse template: rank paths with ranks below the per-depth fan-out caps,
   ordered by (2**depth * prod(rank + 1), depth, path) ascending; the first
   ``n_nodes - 1`` plus the root.
+* Typical acceptance: at the parent u, with p = softmax(Z[u] / T), a child
+  passes iff p(x) > min(eps, delta * exp(-H(p))); the kept branch is the
+  deepest node whose whole path passes (smallest breadth-first index among
+  equals), and one token is drawn from p at its end with that node's u_res.
 * Commit after acceptance: the root and the accepted drafts take cache
   positions L .. L + m in path order; the bonus token is the next root and
   the hidden state of the last accepted row the next h.
@@ -41,9 +45,10 @@ Readings of points the pages leave open (each is listed in the design doc):
   draft distribution stays the same.
 
 Parity unpinned: the choice of nodes in the sparse template beyond its
-invariants (it is this build's own construction), and rule S1 on a tree whose
+invariants (it is this build's own construction), rule S1 on a tree whose
 children are deterministic top-k tokens (the pages prove exactness only for a
-drafted chain).
+drafted chain), and the threshold form of typical acceptance (the pages only
+tie it to the entropy; its pins are its limits and closed forms).
 """
 from __future__ import annotations
 
@@ -58,7 +63,7 @@ __all__ = [
     "head_hidden", "head_logits", "draft_heads", "prune_tree", "ancestors",
     "tree_mask", "tree_attention", "target_logits", "argmax_lowest",
     "greedy_accept", "residual", "sample_inverse_cdf", "rejection_accept",
-    "commit_path",
+    "commit_path", "entropy", "typical_passes", "kept_branch", "typical_accept",
 ]
 
 
@@ -557,6 +562,82 @@ def rejection_accept(Z, head_z, q_row, tok, parent, u_acc, u_res, T, follow=None
         if not moved:
             out.append(draw(r, u_res[u]))
             break
+    return len(path) - 1, path, out
+
+
+# ---------------------------------------------------------------------------
+# Typical acceptance (not distribution-exact)
+# ---------------------------------------------------------------------------
+
+def entropy(p):
+    """Shannon entropy in nats, -sum p log p over the tokens with p > 0."""
+    p = np.asarray(p, dtype=np.float64)
+    nz = p[p > 0]
+    return float(-np.sum(nz * np.log(nz)))
+
+
+def typical_passes(Z, tok, parent, T, eps, delta):
+    """Per-node test of typical acceptance [MH, "Tree Attention und
+    Akzeptanz"]: a candidate is kept when its probability under the target
+    exceeds a threshold tied to the entropy of the target's distribution.
+
+    Reading (the pages give no formula): at the parent u, p = softmax(Z[u] / T)
+    and the threshold is tau = min(eps, delta * exp(-H(p))), so a flat
+    distribution (high entropy) lowers the bar and a peaked one raises it up
+    to eps. Node c passes iff p(tok[c]) > tau. The root passes by definition.
+    Returns (passes [N] bool, margin [N]) with margin = |p(x) - tau| / tau,
+    the relative distance of each decision from its boundary (inf at the root).
+    """
+    N = len(parent)
+    passes = np.zeros(N, dtype=bool)
+    margin = np.full(N, np.inf)
+    passes[0] = True
+    cache = {}
+    for c in range(1, N):
+        u = int(parent[c])
+        if u not in cache:
+            p = softmax(np.asarray(Z[u], dtype=np.float64) / T)
+            cache[u] = (p, min(eps, delta * math.exp(-entropy(p))))
+        p, tau = cache[u]
+        px = p[int(tok[c])]
+        passes[c] = px > tau
+        margin[c] = abs(px - tau) / tau if tau > 0 else np.inf
+    return passes, margin
+
+
+def kept_branch(passes, parent):
+    """End node of the kept branch: among the nodes whose whole root path
+    passes, the deepest [MH, "Tree Attention und Akzeptanz": the longest
+    accepted branch is kept]; equally deep ones go to the smallest
+    breadth-first index (the tree's rank order). Parents precede children."""
+    N = len(parent)
+    ok = np.zeros(N, dtype=bool)
+    depth = np.zeros(N, dtype=np.int64)
+    ok[0] = True
+    end = 0
+    for c in range(1, N):
+        u = int(parent[c])
+        depth[c] = depth[u] + 1
+        ok[c] = ok[u] and bool(passes[c])
+        if ok[c] and depth[c] > depth[end]:
+            end = c
+    return end
+
+
+def typical_accept(Z, tok, parent, u_res, T, eps, delta):
+    """Typical acceptance on a tree, for one sequence: the kept branch of
+    ``kept_branch`` over ``typical_passes``, then one token drawn from the
+    target's distribution at the branch's end by inverse CDF with that
+    node's u_res (as the rejection mode's final draw). Returns (m, path, out)
+    like the other walks: m accepted drafts, then the drawn token."""
+    passes, _ = typical_passes(Z, tok, parent, T, eps, delta)
+    end = kept_branch(passes, parent)
+    path = [end]
+    while parent[path[-1]] >= 0:
+        path.append(int(parent[path[-1]]))
+    path.reverse()
+    out = [int(tok[c]) for c in path[1:]]
+    out.append(sample_inverse_cdf(softmax(np.asarray(Z[end], dtype=np.float64) / T), u_res[end]))
     return len(path) - 1, path, out
 
 

@@ -602,3 +602,87 @@ def test_commit_writes_only_the_kept_positions():
     # pages no block table maps are untouched
     spare = sorted(set(range(kpool.shape[1])) - set(int(x) for x in bt.ravel()))
     assert len(spare) >= 2 and np.array_equal(kp2[:, spare], kpool[:, spare])
+
+
+# -------------------------------------------------------- typical acceptance
+
+def test_entropy_matches_scipy_and_closed_forms():
+    rng = np.random.default_rng(50)
+    for _ in range(20):
+        p = rng.dirichlet(np.ones(int(rng.integers(2, 500))) * rng.uniform(0.05, 3))
+        assert math.isclose(H.entropy(p), float(scipy.stats.entropy(p)), rel_tol=1e-12)
+    assert math.isclose(H.entropy(np.full(1000, 1e-3)), math.log(1000), rel_tol=1e-12)
+    assert H.entropy(np.eye(7)[3]) == 0.0
+
+
+def test_typical_uniform_target_bar_scales_with_delta_over_V():
+    """A flat target (entropy log V exactly) puts the bar at min(eps, delta / V):
+    every candidate (probability 1 / V) passes iff delta < 1 (eps above 1 / V)."""
+    plan = H.plan_cartesian([2, 2])
+    V = 50
+    Z = np.zeros((plan.n, V))
+    tok = np.array([0] + list(range(1, plan.n)))
+    for delta, want in ((0.5, True), (0.99, True), (1.01, False), (2.0, False)):
+        passes, _ = H.typical_passes(Z, tok, plan.parent, 1.0, 0.3, delta)
+        assert all(passes[1:] == want), delta
+    passes, _ = H.typical_passes(Z, tok, plan.parent, 1.0, 0.5 / V, 0.5)  # eps below 1 / V binds
+    assert all(passes[1:])
+
+
+def test_typical_limits_nothing_everything_and_greedy():
+    rng = np.random.default_rng(51)
+    V = 60
+    for tree in ([2, 3], [3, 2, 2], [1, 1, 1]):
+        plan = H.plan_cartesian(tree)
+        depth = plan.depth
+        for _ in range(10):
+            Z = rng.standard_normal((plan.n, V)) * 3
+            tok = np.zeros(plan.n, dtype=np.int64)
+            for u in range(plan.n):
+                kids = plan.children(u)
+                tok[kids] = rng.choice(V, len(kids), replace=False)
+            u_res = rng.random(plan.n)
+            # a bar of 1 passes nothing: the root's own draw
+            m, path, out = H.typical_accept(Z, tok, plan.parent, u_res, 0.8, 1.0, 1e9)
+            assert (m, path) == (0, [0])
+            assert out == [H.sample_inverse_cdf(H.softmax(Z[0] / 0.8), u_res[0])]
+            # a bar of 0 passes everything: the first deepest node
+            m, path, _ = H.typical_accept(Z, tok, plan.parent, u_res, 0.8, 0.0, 0.5)
+            end = int(np.flatnonzero(depth == depth.max())[0])
+            assert m == depth.max() and path[-1] == end
+            # temperature -> 0: the target becomes its arg max, which is greedy
+            # acceptance, and the draw at the end is the arg max
+            got = H.typical_accept(Z, tok, plan.parent, u_res, 1e-4, 0.3, 0.09)
+            assert got == H.greedy_accept(Z, tok, plan.parent, plan.dmax)
+            # scaling logits and temperature together changes nothing
+            assert H.typical_accept(Z * 3, tok, plan.parent, u_res, 2.4, 0.3, 0.3) == \
+                H.typical_accept(Z, tok, plan.parent, u_res, 0.8, 0.3, 0.3)
+
+
+def test_typical_bar_is_monotone_in_eps_and_delta():
+    rng = np.random.default_rng(52)
+    plan = H.plan_cartesian([3, 3])
+    V = 40
+    for _ in range(20):
+        Z = rng.standard_normal((plan.n, V)) * 2
+        tok = rng.integers(0, V, plan.n)
+        a, _ = H.typical_passes(Z, tok, plan.parent, 1.0, 0.2, 0.3)
+        b, _ = H.typical_passes(Z, tok, plan.parent, 1.0, 0.1, 0.3)
+        c, _ = H.typical_passes(Z, tok, plan.parent, 1.0, 0.2, 0.1)
+        assert np.all(b >= a) and np.all(c >= a)  # a lower bar keeps a superset
+
+
+def test_kept_branch_is_the_longest_fully_passing_path_by_brute_force():
+    rng = np.random.default_rng(53)
+    for tree in ([2, 3], [3, 2, 2], [2, 2, 2, 2]):
+        plan = H.plan_cartesian(tree)
+        anc = H.ancestors(plan.parent, plan.dmax)
+        for _ in range(30):
+            passes = rng.random(plan.n) < 0.6
+            passes[0] = True
+            best = (0, 0)
+            for u in range(plan.n):
+                chain = [int(a) for a in anc[u] if a >= 0]
+                if all(passes[c] for c in chain):
+                    best = max(best, (len(chain) - 1, -u))
+            assert H.kept_branch(passes, plan.parent) == -best[1]

@@ -21,7 +21,8 @@ in this fixed order:
   8. page order: identity, or a random permutation of the pool (the pool
      holds each prefix plus a reserve of free positions after it)
   9. tree Q [B, N, Hq, D], tree K [B, N, Hkv, D], tree V ~ N(0, 1)
- 10. uniforms u_acc [B, N], u_res [B, N] in [0, 1)  (stochastic mode only)
+ 10. uniforms u_acc [B, N], u_res [B, N] in [0, 1)  (stochastic and typical
+     modes)
 
 Draws are float32; bfloat16 workloads round them to bfloat16 (round to
 nearest even, torch's conversion).
@@ -51,8 +52,10 @@ class Workload:
     Hkv: int
     D: int
     L: tuple              # (L,) fixed or (lo, hi) uniform per sequence
-    mode: str = "greedy"  # "greedy" | "stochastic"
+    mode: str = "greedy"  # "greedy" | "stochastic" | "typical"
     T: float = 1.0
+    eps: float = 0.1      # typical acceptance: threshold min(eps, delta * exp(-H))
+    delta: float = 0.3
     scattered: bool = False
     zero_init: bool = False
     extra: dict = field(default_factory=dict)
@@ -178,7 +181,7 @@ def generate(w: Workload, n_tree: int | None = None, reserve: int | None = None)
     out["q_tree"] = _normal(g, (w.B, N, w.Hq, w.D), 1.0, dt)
     out["k_tree"] = _normal(g, (w.B, N, w.Hkv, w.D), 1.0, dt)
     out["v_tree"] = _normal(g, (w.B, N, w.Hkv, w.D), 1.0, dt)
-    if w.mode == "stochastic":
+    if w.mode in ("stochastic", "typical"):
         out["u_acc"] = torch.rand((w.B, N), generator=g, dtype=torch.float32)
         out["u_res"] = torch.rand((w.B, N), generator=g, dtype=torch.float32)
     return out

@@ -292,6 +292,14 @@ int tree_attention_verify(int dtype, int B, int N, int Hq, int Hkv, int D,
  *     every child is rejected, one token is drawn from r by inverse CDF with
  *     u_res[u] (smallest id whose cumulative mass exceeds u_res * total). If
  *     a residual has no mass the previous r is kept.
+ *   mode 2, typical ([MH] "Tree Attention und Akzeptanz": a candidate is
+ *     kept when its target probability exceeds a threshold tied to the
+ *     entropy; the longest accepted branch is kept; not distribution-exact):
+ *     at parent u, p = softmax(Z[u] / T) and child c passes iff
+ *     p(tok_c) > min(eps, delta * exp(-H(p))) (threshold form: a reading);
+ *     the kept branch ends at the deepest node whose whole path passes (the
+ *     smallest index among equally deep ones), and one token is drawn from
+ *     p at its end by inverse CDF with u_res[end] (as in mode 1).
  * Outputs: n_accepted[b] = m accepted drafts; path[b, 0..m] tree rows from
  * the root, -1 after; out_tok[b, 0..m] the m accepted tokens then the bonus
  * or resampled token, -1 after.
@@ -301,7 +309,9 @@ int tree_attention_verify(int dtype, int B, int N, int Hq, int Hkv, int D,
  * tok, parent       [B, N] int32 from tree_build (children sorted by rank)
  * q_row             [B, N] int32 from tree_build (mode 1)
  * head_logits       [B, R, V] float32 from hydra_draft_heads (mode 1)
- * u_acc, u_res      [B, N] float32 in [0, 1) (mode 1)
+ * u_acc, u_res      [B, N] float32 in [0, 1) (mode 1; mode 2 reads u_res)
+ * temperature       T > 0 (modes 1 and 2)
+ * eps, delta        typical-acceptance threshold parameters, >= 0 (mode 2)
  * target_logits     out [B, N, V] float32
  * n_accepted        out [B] int32
  * path, out_tok     out [B, Dmax+1] int32
@@ -309,9 +319,10 @@ int tree_attention_verify(int dtype, int B, int N, int Hq, int Hkv, int D,
 size_t tree_accept_workspace_size(int mode, int B, int N, int V);
 
 int tree_accept(int dtype, int mode, int B, int N, int d, int V, int Dmax,
-                const void* o, const void* W_t, float temperature,
-                const int32_t* tok, const int32_t* parent, const int32_t* q_row,
-                const float* head_logits, int R, const float* u_acc,
+                const void* o, const void* W_t, float temperature, float eps,
+                float delta, const int32_t* tok, const int32_t* parent,
+                const int32_t* q_row, const float* head_logits, int R,
+                const float* u_acc,
                 const float* u_res, float* target_logits, int32_t* n_accepted,
                 int32_t* path, int32_t* out_tok, void* ws, size_t ws_bytes,
                 void* stream);

@@ -37,8 +37,8 @@ SIGNATURES = {
                                       c_void, c_void, c_void, c_int, c_int, c_void, c_int, c_void, c_int,
                                       c_void, c_void, c_int, c_void, c_void, c_void, c_size, c_void]),
     "tree_accept_workspace_size": (c_size, [c_int, c_int, c_int, c_int]),
-    "tree_accept": (c_int, [c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_void, c_void, c_float,
-                            c_void, c_void, c_void, c_void, c_int, c_void, c_void, c_void, c_void, c_void,
+    "tree_accept": (c_int, [c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_void, c_void, c_float, c_float,
+                            c_float, c_void, c_void, c_void, c_void, c_int, c_void, c_void, c_void, c_void, c_void,
                             c_void, c_void, c_size, c_void]),
     "tree_commit": (c_int, [c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_void, c_void, c_void, c_void,
                             c_int, c_int, c_void, c_int, c_void, c_void, c_void, c_void, c_int, c_void, c_void,

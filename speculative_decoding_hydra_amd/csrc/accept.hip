@@ -15,6 +15,14 @@
 // the bonus token is drawn from the target distribution when every draft is
 // accepted). p and q are the post-temperature distributions ("Common
 // misconceptions").
+//
+// Typical: "Medusa Heads", section "Tree Attention und Akzeptanz": a
+// candidate is kept when its target probability exceeds a threshold tied to
+// the entropy of the target's distribution, and the longest accepted branch
+// is kept (not distribution-exact). Threshold form (a reading):
+// tau = min(eps, delta * exp(-H(p))) at the parent, p = softmax(z / T); the
+// kept branch ends at the deepest node whose whole path passes (smallest
+// breadth-first index among equals) and one token is drawn from p there.
 #include "walk.h"
 
 namespace hydra {
@@ -223,6 +231,145 @@ __global__ __launch_bounds__(kWalkThreads) void reject_walk(
   if (tid == 0) n_accepted[b] = m;
 }
 
+// Typical acceptance, part 1: one workgroup per tree row u with children.
+// Over the row's scaled logits y = z / T it forms, in float64, S = sum
+// exp(y - M) and W = sum exp(y - M) (y - M), so H(p) = log S - W / S; each
+// child c of u passes iff log p(tok[c]) = y_x - M - log S exceeds
+// log tau = min(log eps, log delta - H). Rows without children exit.
+constexpr int kTypThreads = 256;
+
+__global__ __launch_bounds__(kTypThreads) void typical_rows(int N, int V, float invT, float log_eps,
+                                                            float log_delta, const float* __restrict__ Z,
+                                                            const int32_t* __restrict__ tok,
+                                                            const int32_t* __restrict__ parent,
+                                                            int32_t* __restrict__ pass) {
+  __shared__ int s_kid[2];
+  __shared__ float s_m[kTypThreads / 64];
+  __shared__ double s_s[kTypThreads / 64], s_w[kTypThreads / 64];
+  const int b = blockIdx.x / N, u = blockIdx.x % N, tid = threadIdx.x;
+  const int32_t* pb = parent + static_cast<size_t>(b) * N;
+  if (tid == 0) {
+    s_kid[0] = N;
+    s_kid[1] = 0;
+    if (u == 0) pass[static_cast<size_t>(b) * N] = 1;  // the root
+  }
+  __syncthreads();
+  for (int c = tid; c < N; c += kTypThreads)
+    if (pb[c] == u) {
+      atomicMin(&s_kid[0], c);
+      atomicAdd(&s_kid[1], 1);
+    }
+  __syncthreads();
+  const int c0 = s_kid[0], cnt = s_kid[1];
+  if (cnt == 0) return;
+  const float* zu = Z + (static_cast<size_t>(b) * N + u) * V;
+  float mx = -INFINITY;
+  for (int x = tid; x < V; x += kTypThreads) mx = fmaxf(mx, zu[x] * invT);
+  mx = wave_max(mx);
+  const int lane = tid & 63, wave = tid >> 6;
+  if (lane == 0) s_m[wave] = mx;
+  __syncthreads();
+  float M = s_m[0];
+#pragma unroll
+  for (int w = 1; w < kTypThreads / 64; ++w) M = fmaxf(M, s_m[w]);
+  double S = 0.0, W = 0.0;
+  for (int x = tid; x < V; x += kTypThreads) {
+    const double t = static_cast<double>(zu[x] * invT - M);
+    const double e = exp(t);
+    S += e;
+    W += e * t;
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    S += __shfl_xor(S, off, 64);
+    W += __shfl_xor(W, off, 64);
+  }
+  if (lane == 0) {
+    s_s[wave] = S;
+    s_w[wave] = W;
+  }
+  __syncthreads();
+  S = 0.0;
+  W = 0.0;
+#pragma unroll
+  for (int w = 0; w < kTypThreads / 64; ++w) {
+    S += s_s[w];
+    W += s_w[w];
+  }
+  const double logS = log(S);
+  const double H = logS - W / S;
+  const double log_tau = fmin(static_cast<double>(log_eps), static_cast<double>(log_delta) - H);
+  for (int j = tid; j < cnt; j += kTypThreads) {
+    const int c = c0 + j;
+    const int x = tok[static_cast<size_t>(b) * N + c];
+    const bool ok = x >= 0 && x < V &&
+                    static_cast<double>(zu[x < 0 ? 0 : (x >= V ? V - 1 : x)] * invT - M) - logS > log_tau;
+    pass[static_cast<size_t>(b) * N + c] = ok ? 1 : 0;
+  }
+}
+
+// Typical acceptance, part 2: one workgroup per sequence finds the kept
+// branch from the pass flags (parents precede children), then draws the last
+// token from the target at its end by inverse CDF.
+__global__ __launch_bounds__(kWalkThreads) void typical_walk(int N, int V, int Dmax, float invT,
+                                                             const float* __restrict__ Z,
+                                                             const int32_t* __restrict__ tok,
+                                                             const int32_t* __restrict__ parent,
+                                                             const int32_t* __restrict__ pass,
+                                                             const float* __restrict__ u_res,
+                                                             int32_t* __restrict__ n_accepted,
+                                                             int32_t* __restrict__ path, int32_t* __restrict__ out_tok) {
+  __shared__ double red[kWalkWaves];
+  __shared__ float redf[kWalkWaves];
+  __shared__ int s_pick[2];
+  __shared__ int s_end, s_m;
+  __shared__ int s_path[HYDRA_MAX_DEPTH + 1];
+  __shared__ uint8_t s_ok[HYDRA_MAX_VERIFY];
+  __shared__ uint8_t s_depth[HYDRA_MAX_VERIFY];
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const int32_t* pb = parent + static_cast<size_t>(b) * N;
+  if (tid == 0) {  // N <= 256 nodes in breadth-first order: a sequential pass
+    int end = 0, dend = 0;
+    s_ok[0] = 1;
+    s_depth[0] = 0;
+    for (int c = 1; c < N; ++c) {
+      const int u = pb[c];
+      const bool valid = u >= 0 && u < c;
+      const int dc = valid ? s_depth[u] + 1 : 0;
+      s_depth[c] = static_cast<uint8_t>(dc > 255 ? 255 : dc);
+      s_ok[c] = valid && s_ok[u] && dc <= Dmax && pass[static_cast<size_t>(b) * N + c] != 0;
+      if (s_ok[c] && dc > dend) {
+        end = c;
+        dend = dc;
+      }
+    }
+    for (int j = 0; j <= Dmax; ++j) s_path[j] = -1;
+    int v = end;
+    for (int j = dend; j >= 0; --j) {
+      s_path[j] = v;
+      v = pb[v] < 0 ? 0 : pb[v];
+    }
+    s_end = end;
+    s_m = dend;
+  }
+  __syncthreads();
+  const int end = s_end, m = s_m;
+  const float* ze = Z + (static_cast<size_t>(b) * N + end) * V;
+  float mx = -INFINITY;
+  for (int x = tid; x < V; x += kWalkThreads) mx = fmaxf(mx, ze[x] * invT);
+  Target r{ze, invT, block_max_f(mx, redf), nullptr, 0.0};
+  const int x = block_sample(r, V, u_res[static_cast<size_t>(b) * N + end], red, s_pick);
+  if (tid <= Dmax) {
+    const int pc = s_path[tid];
+    path[static_cast<size_t>(b) * (Dmax + 1) + tid] = pc;
+    int o = -1;
+    if (tid < m) o = tok[static_cast<size_t>(b) * N + s_path[tid + 1]];
+    else if (tid == m) o = x;
+    out_tok[static_cast<size_t>(b) * (Dmax + 1) + tid] = o;
+  }
+  if (tid == 0) n_accepted[b] = m;
+}
+
 }  // namespace
 }  // namespace hydra
 
@@ -234,18 +381,20 @@ extern "C" size_t tree_accept_workspace_size(int mode, int B, int N, int V) {
   if (mode == 0)
     return align_up(rows * sizeof(int32_t), 256) + align_up(rows * projection_nwg(V) * sizeof(uint64_t), 256) +
            align_up(static_cast<size_t>(B) * sizeof(int), 256) + 256;
+  if (mode == 2) return align_up(rows * sizeof(int32_t), 256) + 256;
   return align_up(static_cast<size_t>(B) * 2 * V * sizeof(float), 256) + 256;
 }
 
 extern "C" int tree_accept(int dtype, int mode, int B, int N, int d, int V, int Dmax, const void* o,
-                           const void* W_t, float temperature, const int32_t* tok, const int32_t* parent,
+                           const void* W_t, float temperature, float eps, float delta, const int32_t* tok,
+                           const int32_t* parent,
                            const int32_t* q_row, const float* head_logits, int R, const float* u_acc,
                            const float* u_res, float* target_logits, int32_t* n_accepted, int32_t* path,
                            int32_t* out_tok, void* ws, size_t ws_bytes, void* stream_) {
   clear_error();
   hipStream_t stream = static_cast<hipStream_t>(stream_);
   HY_CHECK(dtype == HYDRA_F32 || dtype == HYDRA_BF16, HYDRA_ERR_INVALID, "tree_accept: bad dtype %d", dtype);
-  HY_CHECK(mode == 0 || mode == 1, HYDRA_ERR_INVALID, "tree_accept: mode %d not in {0, 1}", mode);
+  HY_CHECK(mode >= 0 && mode <= 2, HYDRA_ERR_INVALID, "tree_accept: mode %d not in {0, 1, 2}", mode);
   HY_CHECK(B > 0 && N > 0 && d > 0 && V > 0, HYDRA_ERR_INVALID, "tree_accept: bad sizes B=%d N=%d d=%d V=%d", B, N,
            d, V);
   HY_CHECK(N <= HYDRA_MAX_VERIFY, HYDRA_ERR_INVALID, "tree_accept: N=%d > %d", N, HYDRA_MAX_VERIFY);
@@ -258,6 +407,11 @@ extern "C" int tree_accept(int dtype, int mode, int B, int N, int d, int V, int 
     HY_CHECK(q_row && head_logits && u_acc && u_res && R > 0, HYDRA_ERR_INVALID,
              "tree_accept: rejection mode needs q_row, head_logits, R, u_acc and u_res");
     HY_CHECK(temperature > 0.f, HYDRA_ERR_INVALID, "tree_accept: temperature must be > 0");
+  }
+  if (mode == 2) {
+    HY_CHECK(u_res, HYDRA_ERR_INVALID, "tree_accept: typical mode needs u_res");
+    HY_CHECK(temperature > 0.f, HYDRA_ERR_INVALID, "tree_accept: temperature must be > 0");
+    HY_CHECK(eps >= 0.f && delta >= 0.f, HYDRA_ERR_INVALID, "tree_accept: eps and delta must be >= 0");
   }
   const size_t need = tree_accept_workspace_size(mode, B, N, V);
   HY_CHECK(ws_bytes >= need && ws, HYDRA_ERR_WORKSPACE, "tree_accept: workspace %zu < %zu", ws_bytes, need);
@@ -308,6 +462,18 @@ extern "C" int tree_accept(int dtype, int mode, int B, int N, int d, int V, int 
       greedy_walk<<<B, 64, 0, stream>>>(N, Dmax, amax, tok, parent, n_accepted, path, out_tok);
       HY_LAUNCH_CHECK("tree_accept: greedy walk");
     }
+  } else if (mode == 2) {
+    int rc = launch_projection(dtype, M, d, V, xs, W_t, target_logits, RowMap{M, 0, 0}, V, 1, nullptr,
+                               TopkPartials{nullptr, nullptr}, stream);
+    if (rc != HYDRA_OK) return rc;
+    int32_t* pass = arena.take<int32_t>(static_cast<size_t>(M));
+    const float invT = 1.0f / temperature;
+    typical_rows<<<M, kTypThreads, 0, stream>>>(N, V, invT, logf(eps), logf(delta), target_logits, tok, parent,
+                                                pass);
+    HY_LAUNCH_CHECK("tree_accept: typical rows");
+    typical_walk<<<B, kWalkThreads, 0, stream>>>(N, V, Dmax, invT, target_logits, tok, parent, pass, u_res,
+                                                 n_accepted, path, out_tok);
+    HY_LAUNCH_CHECK("tree_accept: typical walk");
   } else {
     int rc = launch_projection(dtype, M, d, V, xs, W_t, target_logits, RowMap{M, 0, 0}, V, 1, nullptr,
                                TopkPartials{nullptr, nullptr}, stream);

@@ -296,8 +296,11 @@ def tree_accept_workspace_size(mode, B, N, V):
 
 
 def tree_accept(o, W_t, tok, parent, target_logits, n_accepted, path, out_tok, ws, mode=0, temperature=1.0,
-                q_row=None, head_logits=None, u_acc=None, u_res=None, stream=None):
-    """Stage 4 (see include/hydra.h). o [B, N, d]."""
+                q_row=None, head_logits=None, u_acc=None, u_res=None, eps=None, delta=None, stream=None):
+    """Stage 4 (see include/hydra.h). o [B, N, d]; mode 0 greedy, 1 rejection,
+    2 typical (needs eps and delta)."""
+    if mode == 2 and (eps is None or delta is None):
+        raise ValueError("tree_accept: typical acceptance needs eps and delta")
     B, N, d = o.shape
     V = W_t.shape[0]
     Dmax = path.shape[1] - 1
@@ -305,7 +308,7 @@ def tree_accept(o, W_t, tok, parent, target_logits, n_accepted, path, out_tok, w
     wsp, wsb = _ws(ws)
     rc = lib().tree_accept(
         _dtype_code(o), int(mode), B, N, d, V, Dmax, _dev(o, "o"), _dev(W_t, "W_t", o.dtype), float(temperature),
-        _dev(tok, "tok", torch.int32), _dev(parent, "parent", torch.int32), _dev(q_row, "q_row", torch.int32),
+        float(eps or 0.0), float(delta or 0.0), _dev(tok, "tok", torch.int32), _dev(parent, "parent", torch.int32), _dev(q_row, "q_row", torch.int32),
         _dev(head_logits, "head_logits", torch.float32), R, _dev(u_acc, "u_acc", torch.float32),
         _dev(u_res, "u_res", torch.float32), _dev(target_logits, "target_logits", torch.float32),
         _dev(n_accepted, "n_accepted", torch.int32), _dev(path, "path", torch.int32),

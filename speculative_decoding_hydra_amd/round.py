@@ -38,12 +38,13 @@ class HydraRound:
     """
 
     def __init__(self, weights, tree, shape, hydra=True, mode=0, temperature=1.0, residual=True,
-                 keep_hidden=False, device="cuda", fold_embedding=None):
+                 keep_hidden=False, device="cuda", fold_embedding=None, eps=None, delta=None):
         self.w = weights
         plan, n_keep = make_plan(tree)
         self.dplan = H.DevicePlan(plan, hydra, device)
         self.n_keep = n_keep
         self.hydra, self.mode, self.T, self.residual = hydra, int(mode), float(temperature), residual
+        self.eps, self.delta = eps, delta  # typical acceptance (mode 2)
         B, d, V = shape["B"], shape["d"], shape["V"]
         Hq, Hkv, D = shape["Hq"], shape["Hkv"], shape["D"]
         self.shape = dict(shape)
@@ -105,7 +106,7 @@ class HydraRound:
         H.tree_accept(self.attn_out.view(B, K, -1), self.w["W_t"], self.tok, self.parent, self.target_logits,
                       self.n_accepted, self.path, self.out_tok, self.ws_accept, mode=self.mode,
                       temperature=self.T, q_row=self.q_row, head_logits=self.head_logits, u_acc=u_acc,
-                      u_res=u_res, stream=stream)
+                      u_res=u_res, eps=self.eps, delta=self.delta, stream=stream)
 
     def commit(self, k_tree, v_tree, k_pages, v_pages, block_table, prefix_len, stream=None):
         """Root and accepted rows into the paged cache (in place); next
@@ -129,7 +130,7 @@ def round_from_inputs(inp, device="cuda", keep_hidden=True, fold_embedding=None,
 
     Keys: workload (sizes, tree, dtype, mode), root_tok, h, E, W1, b1, W2, W_t,
     q_tree, k_tree, v_tree, k_pages, v_pages, block_table, prefix_len and, for
-    the rejection mode, u_acc and u_res. Returns (round, device tensors).
+    the rejection and typical modes, u_acc and u_res. Returns (round, device tensors).
     """
     w = inp["workload"]
     to = lambda t: t.to(device).contiguous()  # noqa: E731
@@ -137,13 +138,13 @@ def round_from_inputs(inp, device="cuda", keep_hidden=True, fold_embedding=None,
                    b1=[to(x) for x in inp["b1"]], W2=[to(x) for x in inp["W2"]], W_t=to(inp["W_t"]))
     shape = dict(B=w.B, d=w.d, V=w.V, Hq=w.Hq, Hkv=w.Hkv, D=w.D,
                  max_prefix_len=int(inp["prefix_len"].max()))
-    rnd = HydraRound(weights, w.tree, shape, hydra=w.hydra, mode=0 if w.mode == "greedy" else 1,
-                     temperature=w.T, residual=residual, keep_hidden=keep_hidden, device=device,
-                     fold_embedding=fold_embedding)
+    mode = {"greedy": 0, "stochastic": 1, "typical": 2}[w.mode]
+    rnd = HydraRound(weights, w.tree, shape, hydra=w.hydra, mode=mode, temperature=w.T, residual=residual, keep_hidden=keep_hidden, device=device,
+                     fold_embedding=fold_embedding, eps=w.eps, delta=w.delta)
     dev = dict(h=to(inp["h"]), root_tok=to(inp["root_tok"]), q=to(inp["q_tree"]), k_tree=to(inp["k_tree"]),
                v_tree=to(inp["v_tree"]), k_pages=to(inp["k_pages"]), v_pages=to(inp["v_pages"]),
                block_table=to(inp["block_table"]), prefix_len=to(inp["prefix_len"]))
-    if w.mode == "stochastic":
+    if w.mode in ("stochastic", "typical"):
         dev["u_acc"], dev["u_res"] = to(inp["u_acc"]), to(inp["u_res"])
     return rnd, dev
 

@@ -222,6 +222,8 @@ def check_accept(inp, rnd, seqs=None):
         if w.mode == "greedy":
             m, p, o = O.greedy_accept(Z_dev[b], tok[b], par[b], Dm)
             assert n_acc[b] == m and got_p == p and got_o == o, f"seq {b}: greedy walk {got_p}/{got_o} vs {p}/{o}"
+        elif w.mode == "typical":
+            amb += check_typical(Z_dev[b], tok[b], par[b], np_(inp["u_res"])[b], w, got_p, got_o, f"seq {b}")
         else:
             # the oracle follows the device's decisions and reports its own;
             # they may differ only within float32 rounding of the boundary
@@ -237,6 +239,36 @@ def check_accept(inp, rnd, seqs=None):
                     assert margin < bound, f"seq {b}: {kind} decision {taken} vs oracle {own} (margin {margin:.3g})"
     assert e_z <= t, f"target logits max-abs {e_z:.3g} > {t}"
     return dict(z=e_z, ambiguous=amb)
+
+
+def check_typical(Z, tok, parent, u_res, w, got_p, got_o, where):
+    """Typical acceptance of one sequence on the device's target logits. A
+    pass decision within ACCEPT_EPS (relative) of its bar may go either way:
+    the device's branch must be the kept branch of one such choice, and its
+    last token the oracle's draw at that branch's end (or within SAMPLE_EPS
+    of a cumulative boundary). Returns the number of ambiguous decisions."""
+    import itertools
+
+    passes, margin = O.typical_passes(Z, tok, parent, w.T, w.eps, w.delta)
+    amb = [int(c) for c in np.flatnonzero(margin < ACCEPT_EPS)]
+    ends = set()
+    for choice in itertools.product([False, True], repeat=len(amb)):
+        f = passes.copy()
+        f[amb] = choice
+        ends.add(O.kept_branch(f, parent))
+    end = got_p[-1]
+    assert end in ends, f"{where}: typical branch ends at {end}, oracle {sorted(ends)} (ambiguous {amb})"
+    chain = [end]
+    while parent[chain[-1]] >= 0:
+        chain.append(int(parent[chain[-1]]))
+    assert got_p == chain[::-1], f"{where}: path {got_p} is not the root path of {end}"
+    assert got_o[:-1] == [int(tok[c]) for c in got_p[1:]], f"{where}: accepted tokens"
+    r = O.softmax(np.asarray(Z[end], dtype=np.float64) / w.T)
+    x = O.sample_inverse_cdf(r, u_res[end])
+    if got_o[-1] != x:
+        assert ambiguous_sample(r, u_res[end], SAMPLE_EPS), f"{where}: drawn {got_o[-1]} vs oracle {x}"
+        return len(amb) + 1
+    return len(amb)
 
 
 def oracle_round_checks(inp, rnd, seqs=None, rows=None):

@@ -615,3 +615,86 @@ def test_two_rounds_through_the_commit(name):
     assert [int(x) for x in rnd2.path[0] if x >= 0] == path2
     assert [int(x) for x in rnd2.out_tok[0] if x >= 0] == toks2
     assert int(rnd2.next_prefix_len[0]) == L + m + 1 + m2 + 1
+
+
+# ------------------------------------------------------ typical acceptance
+
+def test_tiny_typical_round():
+    """Typical acceptance at temperature 0.7 on the tiny workload, then the
+    commit of its branch."""
+    inp, rnd, dev = _round("tiny", mode="typical", T=0.7)
+    rep = T.oracle_round_checks(inp, rnd)
+    rep.update(T.check_commit(inp, rnd, dev))
+    print(rep, flush=True)
+
+
+def test_7b_sparse64_typical_round():
+    """Typical acceptance on the 7B-shaped round: nearly flat random targets
+    put the bar low, so branches several levels deep are accepted."""
+    inp, rnd, dev = _round("7b_sparse64", mode="typical", T=1.0)
+    rep = T.oracle_round_checks(inp, rnd)
+    rep.update(T.check_commit(inp, rnd, dev))
+    print(rep, flush=True)
+
+
+@pytest.mark.parametrize("B,dtype", [(4, "fp32"), (6, "bf16"), (300, "fp32")])
+def test_typical_planted_branches(B, dtype):
+    """Targets planted on two branches of different depth, with two siblings
+    passing at once: the kept branch is the deeper one even where it starts
+    at the lower-ranked sibling, and the stage-wise oracle agrees."""
+    from speculative_decoding_hydra_amd import tree_accept, tree_accept_workspace_size
+
+    print(f"typical planted B={B} {dtype}", flush=True)
+    g = np.random.default_rng(B + 7)
+    dt = torch.float32 if dtype == "fp32" else torch.bfloat16
+    V, d, Tmp = 1000, 256, 1.0
+    w = HI.workload("tiny", mode="typical", T=Tmp)
+    plan = O.plan_cartesian([2, 3, 2])
+    N = plan.n
+    anc = O.ancestors(plan.parent, plan.dmax)
+    depth = plan.depth
+    W = g.standard_normal((V, d)) * 0.02
+    tok = np.zeros((B, N), dtype=np.int32)
+    o = g.standard_normal((B, N, d)) * 0.01
+    want = []
+    for b in range(B):
+        for u in range(N):
+            kids = plan.children(u)
+            tok[b, kids] = g.choice(V, len(kids), replace=False)
+        deep = [u for u in range(N) if depth[u] == plan.dmax]
+        shallow = [u for u in range(N) if depth[u] == plan.dmax - 1 and plan.children(u)]
+        t_deep = int(g.choice(deep))
+        t_sh = int(g.choice([u for u in shallow if anc[u][1] != anc[t_deep][1]]))
+        plant = {}
+        for t in (t_deep, t_sh):
+            path = [int(a) for a in anc[t] if a >= 0]
+            for a, nx in zip(path[:-1], path[1:]):
+                plant.setdefault(a, set()).add(int(tok[b, nx]))
+        for a in range(N):
+            kids = set(int(tok[b, c]) for c in plan.children(a))
+            if a not in plant and kids:  # a peaked target on a token no child carries: every child fails
+                plant[a] = {int(g.choice([t for t in range(V) if t not in kids]))}
+        for a, xs in plant.items():  # the smallest o giving each planted token a logit of 12
+            Wp = W[sorted(xs)]
+            o[b, a] = Wp.T @ np.linalg.solve(Wp @ Wp.T, np.full(len(xs), 12.0))
+        want.append(t_deep)
+    ot = torch.tensor(o, dtype=torch.float32).to(dt).cuda()
+    Wt = torch.tensor(W, dtype=torch.float32).to(dt).cuda()
+    tk = torch.tensor(tok).cuda()
+    par = torch.tensor(np.stack([plan.parent] * B).astype(np.int32)).cuda()
+    u_res = torch.rand(B, N, generator=torch.Generator().manual_seed(B)).cuda()
+    Z = torch.empty(B, N, V, device="cuda")
+    n_acc = torch.empty(B, dtype=torch.int32, device="cuda")
+    path_t = torch.empty(B, plan.dmax + 1, dtype=torch.int32, device="cuda")
+    out_t = torch.empty_like(path_t)
+    ws = torch.empty(tree_accept_workspace_size(2, B, N, V), dtype=torch.uint8, device="cuda")
+    tree_accept(ot, Wt, tk, par, Z, n_acc, path_t, out_t, ws, mode=2, temperature=Tmp, u_res=u_res,
+                eps=w.eps, delta=w.delta)
+    torch.cuda.synchronize()
+    Zc, ur = Z.cpu().double().numpy(), u_res.cpu().double().numpy()
+    for b in range(B):
+        got_p = [int(x) for x in path_t[b] if x >= 0]
+        got_o = [int(x) for x in out_t[b] if x >= 0]
+        assert int(n_acc[b]) == len(got_p) - 1
+        assert got_p[-1] == want[b], f"seq {b}: kept branch ends at {got_p[-1]}, planted {want[b]}"
+        T.check_typical(Zc[b], tok[b], plan.parent, ur[b], w, got_p, got_o, f"seq {b}")

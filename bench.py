@@ -1,6 +1,7 @@
 """Throughput of one Hydra draft-and-verify round on one MI355X.
 
-python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-graph] [--no-cpu] [--no-fold]
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--acceptance MODE] [--no-graph]
+                [--no-cpu] [--no-fold]
 
 A step is one whole round (draft heads -> tree build -> tree-attention verify
 -> accept -> commit of the kept branch into the KV cache) over the workload's
@@ -47,6 +48,8 @@ def parse():
     ap.add_argument("--no-graph", action="store_true", help="eager launches everywhere (for counter runs)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--kernel-reps", type=int, default=20)
+    ap.add_argument("--acceptance", choices=["greedy", "stochastic", "typical"], default=None,
+                    help="override the workload's acceptance mode")
     ap.add_argument("--no-fold", action="store_true",
                     help="stream W1[:, d:] every round instead of the folded embedding tables")
     return ap.parse_args()
@@ -173,6 +176,9 @@ def cpu_baseline(inp, n_rows):
     bt, lens = inp["block_table"].numpy(), inp["prefix_len"].numpy()
     kind = w.tree[0]
     plan = O.plan_sparse_template(w.tree[1], w.tree[2]) if kind == "sparse" else O.plan_cartesian(w.tree[1])
+    node_row = O.head_rows(plan, w.hydra)[2]
+    u_acc = inp["u_acc"].numpy() if "u_acc" in inp else None
+    u_res = inp["u_res"].numpy() if "u_res" in inp else None
     try:
         from threadpoolctl import threadpool_info
 
@@ -194,7 +200,14 @@ def cpu_baseline(inp, n_rows):
         path = -np.ones((w.B, plan.dmax + 1), dtype=np.int64)
         toks = -np.ones((w.B, plan.dmax + 1), dtype=np.int64)
         for b, (t, s) in enumerate(trees):
-            m, pth, tk = O.greedy_accept(Z[b], res["tok"][b][s], t.parent, plan.dmax)
+            tb = res["tok"][b][s]
+            if w.mode == "greedy":
+                m, pth, tk = O.greedy_accept(Z[b], tb, t.parent, plan.dmax)
+            elif w.mode == "typical":
+                m, pth, tk = O.typical_accept(Z[b], tb, t.parent, u_res[b], w.T, w.eps, w.delta)
+            else:
+                m, pth, tk = O.rejection_accept(Z[b], res["z"][b], node_row[s], tb, t.parent, u_acc[b], u_res[b],
+                                                w.T)
             n_acc[b], path[b, : m + 1], toks[b, : m + 1] = m, pth, tk
         O.commit_path(kpool, vpool, bt, lens, kt[None], vt[None], n_acc, path, toks, plan.dmax,
                       out.reshape(w.B, out.shape[1], -1))
@@ -221,6 +234,8 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
     w = HI.workload(args.workload)
+    if args.acceptance and args.acceptance != w.mode:
+        w = HI.workload(args.workload, mode=args.acceptance, T=w.T if w.mode != "greedy" else 1.0)
     log(f"[bench] generating {w.name}")
     inp = HI.generate(w)
     rnd, dev = round_from_inputs(inp, device="cuda:0", keep_hidden=False,

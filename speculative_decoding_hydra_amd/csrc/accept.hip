@@ -232,11 +232,12 @@ __global__ __launch_bounds__(kWalkThreads) void reject_walk(
 }
 
 // Typical acceptance, part 1: one workgroup per tree row u with children.
-// Over the row's scaled logits y = z / T it forms, in float64, S = sum
-// exp(y - M) and W = sum exp(y - M) (y - M), so H(p) = log S - W / S; each
-// child c of u passes iff log p(tok[c]) = y_x - M - log S exceeds
-// log tau = min(log eps, log delta - H). Rows without children exit.
-constexpr int kTypThreads = 256;
+// Over the row's scaled logits y = z / T it forms S = sum exp(y - M) and
+// W = sum exp(y - M) (y - M) (float32 per thread, float64 across threads),
+// so H(p) = log S - W / S; each child c of u passes iff
+// log p(tok[c]) = y_x - M - log S exceeds log tau = min(log eps,
+// log delta - H). Rows without children exit.
+constexpr int kTypThreads = 1024;
 
 __global__ __launch_bounds__(kTypThreads) void typical_rows(int N, int V, float invT, float log_eps,
                                                             float log_delta, const float* __restrict__ Z,
@@ -272,13 +273,14 @@ __global__ __launch_bounds__(kTypThreads) void typical_rows(int N, int V, float 
   float M = s_m[0];
 #pragma unroll
   for (int w = 1; w < kTypThreads / 64; ++w) M = fmaxf(M, s_m[w]);
-  double S = 0.0, W = 0.0;
+  float Sf = 0.f, Wf = 0.f;
   for (int x = tid; x < V; x += kTypThreads) {
-    const double t = static_cast<double>(zu[x] * invT - M);
-    const double e = exp(t);
-    S += e;
-    W += e * t;
+    const float t = zu[x] * invT - M;
+    const float e = exp2f(t * 1.4426950408889634f);
+    Sf += e;
+    Wf += e * t;
   }
+  double S = Sf, W = Wf;
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) {
     S += __shfl_xor(S, off, 64);
@@ -326,18 +328,25 @@ __global__ __launch_bounds__(kWalkThreads) void typical_walk(int N, int V, int D
   __shared__ int s_path[HYDRA_MAX_DEPTH + 1];
   __shared__ uint8_t s_ok[HYDRA_MAX_VERIFY];
   __shared__ uint8_t s_depth[HYDRA_MAX_VERIFY];
+  __shared__ int s_par[HYDRA_MAX_VERIFY];
+  __shared__ uint8_t s_pass[HYDRA_MAX_VERIFY];
   const int b = blockIdx.x, tid = threadIdx.x;
   const int32_t* pb = parent + static_cast<size_t>(b) * N;
-  if (tid == 0) {  // N <= 256 nodes in breadth-first order: a sequential pass
+  for (int c = tid; c < N; c += kWalkThreads) {  // the tree into LDS, all loads at once
+    s_par[c] = pb[c];
+    s_pass[c] = pass[static_cast<size_t>(b) * N + c] != 0;
+  }
+  __syncthreads();
+  if (tid == 0) {  // N <= 256 nodes in breadth-first order: a sequential pass over LDS
     int end = 0, dend = 0;
     s_ok[0] = 1;
     s_depth[0] = 0;
     for (int c = 1; c < N; ++c) {
-      const int u = pb[c];
+      const int u = s_par[c];
       const bool valid = u >= 0 && u < c;
       const int dc = valid ? s_depth[u] + 1 : 0;
       s_depth[c] = static_cast<uint8_t>(dc > 255 ? 255 : dc);
-      s_ok[c] = valid && s_ok[u] && dc <= Dmax && pass[static_cast<size_t>(b) * N + c] != 0;
+      s_ok[c] = valid && s_ok[u] && dc <= Dmax && s_pass[c];
       if (s_ok[c] && dc > dend) {
         end = c;
         dend = dc;
@@ -347,7 +356,7 @@ __global__ __launch_bounds__(kWalkThreads) void typical_walk(int N, int V, int D
     int v = end;
     for (int j = dend; j >= 0; --j) {
       s_path[j] = v;
-      v = pb[v] < 0 ? 0 : pb[v];
+      v = s_par[v] < 0 ? 0 : s_par[v];
     }
     s_end = end;
     s_m = dend;
@@ -370,6 +379,454 @@ __global__ __launch_bounds__(kWalkThreads) void typical_walk(int N, int V, int D
   if (tid == 0) n_accepted[b] = m;
 }
 
+// ---------------------------------------------------------------------------
+// Register-resident rows (V <= EPT * kWalkThreads). The walks above stream a
+// logits row from memory on every pass (maximum, sum, residual, draw), one
+// load per thread at a time, so each pass costs tens of memory round trips.
+// Here a row is loaded once, with all of a thread's loads in flight together:
+// element x = i * kWalkThreads + tid sits in register i of thread tid, so
+// every load is coalesced, and the passes run on registers. The arithmetic is
+// the same as above, value for value.
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// float sum over the wave, the same value in every lane: rows of 16 by DPP,
+// then the row pairs and halves by the gfx950 row swaps (VALU only; every
+// partial is a commutative pair, so all lanes add in the same order)
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+  v += dppf<kDppXor1>(v);
+  v += dppf<kDppXor2>(v);
+  v += dppf<kDppHalfMirror>(v);
+  v += dppf<kDppMirror>(v);
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(c[0]) + __uint_as_float(c[1]);
+}
+
+// block sum: float within each wave (DPP), float64 across the waves
+__device__ __forceinline__ double block_sum_fd(float v, double* red) {
+  v = wave_sum_dpp(v);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  double t = 0.0;
+  for (int w = 0; w < kWalkWaves; ++w) t += red[w];
+  return t;
+}
+
+
+// row `row` of the [rows][V] float matrix z; buffer loads share one lane
+// offset (register i adds i * 4 KB as a scalar offset), so all EPT loads are
+// in flight at once without a 64-bit address per load
+template <int EPT>
+__device__ __forceinline__ void reg_load_scaled(float (&v)[EPT], const float* __restrict__ z, size_t row, int V,
+                                                float invT) {
+  const size_t r = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(row));
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(z + r * V), 0, V * 4, 0x00020000);
+  const int lane_off = static_cast<int>(threadIdx.x) * 4;
+#pragma unroll
+  for (int i = 0; i < EPT; ++i)
+    v[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, lane_off, i * kWalkThreads * 4, 0));
+#pragma unroll
+  for (int i = 0; i < EPT; ++i) {
+    const int x = i * kWalkThreads + static_cast<int>(threadIdx.x);
+    v[i] = x < V ? v[i] * invT : -INFINITY;  // past V the buffer returns 0
+  }
+}
+
+// v <- exp(v - max v) (0 past V); returns the block sum in float64
+template <int EPT>
+__device__ __forceinline__ double reg_exp(float (&v)[EPT], double* red, float* redf) {
+  float mx = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < EPT; ++i) mx = fmaxf(mx, v[i]);
+  const float M = block_max_f(mx, redf);
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < EPT; ++i) {
+    v[i] = v[i] == -INFINITY ? 0.f : exp2f((v[i] - M) * kLog2e);
+    s += v[i];
+  }
+  return block_sum_fd(s, red);
+}
+
+// a[x] and b[x] for one token x < V, broadcast to the whole block
+template <int EPT>
+__device__ __forceinline__ float2 reg_at2(const float (&a)[EPT], const float (&b)[EPT], int x, float2* s_bc) {
+  __syncthreads();
+  if (static_cast<int>(threadIdx.x) == x % kWalkThreads) {
+    float2 t = make_float2(0.f, 0.f);
+#pragma unroll
+    for (int i = 0; i < EPT; ++i)
+      if (i == x / kWalkThreads) t = make_float2(a[i], b[i]);
+    *s_bc = t;
+  }
+  __syncthreads();
+  return *s_bc;
+}
+
+// Inverse-CDF draw over the unnormalised r held in registers: the smallest x
+// with sum_{y <= x} r(y) > u * sum r. Tile i (register i of every thread,
+// ids i * kWalkThreads ...) is located from the tile sums (float per wave,
+// float64 across waves), then one float64 block scan inside it finds x; if
+// rounding between the two leaves no crossing there, the tile's last x with
+// r > 0 is taken. s_pick holds 3 ints.
+template <int EPT>
+__device__ int reg_sample(const float (&r)[EPT], float u, double* s_tile, double* red, int* s_pick) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  __shared__ double s_thr, s_before;
+  __shared__ double s_tsum[EPT];
+  __shared__ int s_it;
+  int lastpos = -1;
+#pragma unroll
+  for (int i = 0; i < EPT; ++i) {
+    const float t = wave_sum_dpp(r[i]);  // locates the tile only; the scan inside it is float64
+    if (lane == 0) s_tile[wave * EPT + i] = t;
+    if (r[i] > 0.f) lastpos = i * kWalkThreads + tid;
+  }
+  if (tid == 0) {
+    s_pick[0] = -1;
+    s_pick[1] = -1;
+    s_pick[2] = -1;
+  }
+  __syncthreads();
+  if (lastpos >= 0) atomicMax(&s_pick[1], lastpos);
+  if (tid < EPT) {
+    double t = 0.0;
+    for (int w = 0; w < kWalkWaves; ++w) t += s_tile[w * EPT + tid];
+    s_tsum[tid] = t;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    double total = 0.0;
+    for (int i = 0; i < EPT; ++i) total += s_tsum[i];
+    const double thr = static_cast<double>(u) * total;
+    double before = 0.0;
+    int it = -1;
+    for (int i = 0; i < EPT; ++i) {
+      if (before + s_tsum[i] > thr) {
+        it = i;
+        break;
+      }
+      before += s_tsum[i];
+    }
+    s_thr = thr;
+    s_before = before;
+    s_it = it;
+  }
+  __syncthreads();
+  const int it = s_it;
+  if (it >= 0) {
+    float val = 0.f;
+#pragma unroll
+    for (int i = 0; i < EPT; ++i)
+      if (i == it) val = r[i];
+    double inc = val;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const double o = __shfl_up(inc, off, 64);
+      if (lane >= off) inc += o;
+    }
+    if (lane == 63) red[wave] = inc;
+    __syncthreads();
+    double woff = s_before;
+    for (int w = 0; w < wave; ++w) woff += red[w];
+    const double incl = woff + inc, excl = incl - val;
+    const double thr = s_thr;
+    if (val > 0.f && excl <= thr && thr < incl) s_pick[0] = it * kWalkThreads + tid;
+    if (val > 0.f) atomicMax(&s_pick[2], it * kWalkThreads + tid);
+  }
+  __syncthreads();
+  // no crossing: u * total beyond the last tile (the last x with r > 0), or
+  // lost to rounding at the tile's end (its last x with r > 0)
+  const int pick = s_pick[0] >= 0 ? s_pick[0] : (s_pick[2] >= 0 ? s_pick[2] : s_pick[1]);
+  __syncthreads();
+  return pick;
+}
+
+// ---------------------------------------------------------------------------
+// Node-parallel acceptance. What the walk does at a node depends only on that
+// node: its target row, the head row that drafted its children, the
+// children's tokens and uniforms, its own residual uniform and its depth (the
+// walk reaches node u having accepted depth(u) drafts). So one workgroup per
+// tree row settles the node's outcome - the child it accepts, or else the
+// token it draws - all rows at once on different CUs, and a small kernel per
+// sequence then follows the accepted children from the root. The result is
+// the walk's, decision for decision, and its latency no longer grows with the
+// accepted length.
+
+// the sequence's parents into LDS (N <= 256), all loads at once
+__device__ __forceinline__ void load_parents(const int32_t* __restrict__ parent, int b, int N, int* s_par) {
+  for (int c = threadIdx.x; c < N; c += blockDim.x) s_par[c] = parent[static_cast<size_t>(b) * N + c];
+  __syncthreads();
+}
+
+// rejection mode: next[b, u] = the child accepted at u (children tried in rank
+// order against the current residual, q unchanged), or -1 with draw[b, u] the
+// inverse-CDF draw from the residual (from p when u has no children or sits
+// at depth Dmax)
+template <int EPT>
+__global__ __launch_bounds__(kWalkThreads) void reject_node_reg(
+    int N, int V, int R, int Dmax, float invT, const float* __restrict__ Z, const float* __restrict__ HZ,
+    const int32_t* __restrict__ tok, const int32_t* __restrict__ parent, const int32_t* __restrict__ q_row,
+    const float* __restrict__ u_acc, const float* __restrict__ u_res, int32_t* __restrict__ next,
+    int32_t* __restrict__ draw) {
+  __shared__ double red[kWalkWaves];
+  __shared__ float redf[kWalkWaves];
+  __shared__ double s_tile[kWalkWaves * EPT];
+  __shared__ int s_pick[3];
+  __shared__ int s_kid[3];
+  __shared__ float2 s_bc;
+  __shared__ int s_par[HYDRA_MAX_VERIFY];
+  const int b = blockIdx.x / N, u = blockIdx.x % N, tid = threadIdx.x;
+  const size_t row = static_cast<size_t>(b) * N + u;
+  load_parents(parent, b, N, s_par);
+  if (tid == 0) {
+    int d = 0, v = u;
+    while (v > 0 && v < N && d <= N) {  // depth of u (a malformed chain stops within N steps)
+      v = s_par[v];
+      ++d;
+    }
+    if (v != 0) d = N + 1;  // not connected to the root: draw at u
+    s_kid[0] = N;
+    s_kid[1] = 0;
+    s_kid[2] = d;
+  }
+  __syncthreads();
+  for (int c = tid; c < N; c += kWalkThreads)
+    if (s_par[c] == u) {
+      atomicMin(&s_kid[0], c);
+      atomicAdd(&s_kid[1], 1);
+    }
+  float r[EPT], q[EPT];
+  reg_load_scaled(r, Z, row, V, invT);
+  double total = reg_exp(r, red, redf);  // its barriers also publish s_kid
+  const int c0 = s_kid[0], cnt = s_kid[1], depth = s_kid[2];
+  int taken = -1;
+  if (cnt > 0 && depth < Dmax) {
+    const int qr = q_row[row];
+    reg_load_scaled(q, HZ, static_cast<size_t>(b) * R + (qr < 0 ? 0 : qr), V, invT);
+    const float qinv = static_cast<float>(1.0 / reg_exp(q, red, redf));
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) q[i] *= qinv;
+    for (int j = 0; j < cnt; ++j) {
+      const int c = c0 + j;
+      int x = tok[static_cast<size_t>(b) * N + c];
+      x = x < 0 ? 0 : (x >= V ? V - 1 : x);
+      const float2 rq = reg_at2(r, q, x, &s_bc);
+      const float rx = static_cast<float>(rq.x / total);
+      if (u_acc[static_cast<size_t>(b) * N + c] * rq.y < rx) {
+        taken = c;
+        break;
+      }
+      // residual norm(max(r - q, 0)), kept unless it has no mass
+      const float rinv = static_cast<float>(1.0 / total);
+      float nsf = 0.f;
+#pragma unroll
+      for (int i = 0; i < EPT; ++i) {
+        float t = fmaxf(r[i] * rinv - q[i], 0.f);
+        asm volatile("" : "+v"(t));  // recomputed below rather than kept: the rows fill the registers
+        nsf += t;
+      }
+      const double ns = block_sum_fd(nsf, red);
+      if (ns > 0.0) {
+#pragma unroll
+        for (int i = 0; i < EPT; ++i) r[i] = fmaxf(r[i] * rinv - q[i], 0.f);
+        total = ns;
+      }
+    }
+  }
+  int x = -1;
+  if (taken < 0) x = reg_sample(r, u_res[row], s_tile, red, s_pick);
+  if (tid == 0) {
+    next[row] = taken;
+    draw[row] = x;
+  }
+}
+
+// typical mode: pass[b, c] for the children of u (see typical_rows) and
+// draw[b, u], the inverse-CDF draw from p at u (used if the kept branch ends
+// there)
+template <int EPT>
+__global__ __launch_bounds__(kWalkThreads) void typical_node_reg(int N, int V, float invT, float log_eps,
+                                                                 float log_delta, const float* __restrict__ Z,
+                                                                 const int32_t* __restrict__ tok,
+                                                                 const int32_t* __restrict__ parent,
+                                                                 const float* __restrict__ u_res,
+                                                                 int32_t* __restrict__ pass,
+                                                                 int32_t* __restrict__ draw) {
+  __shared__ double red[kWalkWaves];
+  __shared__ float redf[kWalkWaves];
+  __shared__ double s_tile[kWalkWaves * EPT];
+  __shared__ double s_w[kWalkWaves];
+  __shared__ int s_pick[3];
+  __shared__ int s_kid[2];
+  const int b = blockIdx.x / N, u = blockIdx.x % N, tid = threadIdx.x;
+  const size_t row = static_cast<size_t>(b) * N + u;
+  if (tid == 0) {
+    s_kid[0] = N;
+    s_kid[1] = 0;
+    if (u == 0) pass[static_cast<size_t>(b) * N] = 1;  // the root
+  }
+  __syncthreads();
+  for (int c = tid; c < N; c += kWalkThreads)
+    if (parent[static_cast<size_t>(b) * N + c] == u) {
+      atomicMin(&s_kid[0], c);
+      atomicAdd(&s_kid[1], 1);
+    }
+  float r[EPT];
+  reg_load_scaled(r, Z, row, V, invT);
+  float mx = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < EPT; ++i) mx = fmaxf(mx, r[i]);
+  const float M = block_max_f(mx, redf);
+  float Sf = 0.f, Wf = 0.f;
+#pragma unroll
+  for (int i = 0; i < EPT; ++i) {
+    const float t = r[i] - M;
+    const float e = r[i] == -INFINITY ? 0.f : exp2f(t * kLog2e);
+    Sf += e;
+    Wf += r[i] == -INFINITY ? 0.f : e * t;
+    r[i] = e;
+  }
+  const double S = block_sum_d(Sf, red);
+  double Wd = Wf;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) Wd += __shfl_xor(Wd, off, 64);
+  if ((tid & 63) == 0) s_w[tid >> 6] = Wd;
+  __syncthreads();
+  double W = 0.0;
+  for (int w = 0; w < kWalkWaves; ++w) W += s_w[w];
+  const int c0 = s_kid[0], cnt = s_kid[1];
+  if (cnt > 0) {
+    const double logS = log(S);
+    const double H = logS - W / S;
+    const double log_tau = fmin(static_cast<double>(log_eps), static_cast<double>(log_delta) - H);
+    const float* zu = Z + row * V;
+    for (int j = tid; j < cnt; j += kWalkThreads) {
+      const int c = c0 + j;
+      const int x = tok[static_cast<size_t>(b) * N + c];
+      const bool ok = x >= 0 && x < V &&
+                      static_cast<double>(zu[x < 0 ? 0 : (x >= V ? V - 1 : x)] * invT - M) - logS > log_tau;
+      pass[static_cast<size_t>(b) * N + c] = ok ? 1 : 0;
+    }
+  }
+  const int x = reg_sample(r, u_res[row], s_tile, red, s_pick);
+  if (tid == 0) draw[row] = x;
+}
+
+// one wave per sequence: follow next[] from the root (rejection mode) and
+// emit the accepted tokens plus the draw where the walk stops
+__global__ __launch_bounds__(64) void reject_pick(int N, int Dmax, const int32_t* __restrict__ tok,
+                                                  const int32_t* __restrict__ next, const int32_t* __restrict__ draw,
+                                                  int32_t* __restrict__ n_accepted, int32_t* __restrict__ path,
+                                                  int32_t* __restrict__ out_tok) {
+  __shared__ int s_next[HYDRA_MAX_VERIFY], s_tok[HYDRA_MAX_VERIFY], s_draw[HYDRA_MAX_VERIFY];
+  const int b = blockIdx.x, lane = threadIdx.x;
+  for (int c = lane; c < N; c += 64) {
+    s_next[c] = next[static_cast<size_t>(b) * N + c];
+    s_tok[c] = tok[static_cast<size_t>(b) * N + c];
+    s_draw[c] = draw[static_cast<size_t>(b) * N + c];
+  }
+  __syncthreads();
+  if (lane == 0) {
+    int u = 0, m = 0;
+    int32_t* pb = path + static_cast<size_t>(b) * (Dmax + 1);
+    int32_t* ob = out_tok + static_cast<size_t>(b) * (Dmax + 1);
+    pb[0] = 0;
+    while (m < Dmax && s_next[u] > u && s_next[u] < N) {  // children follow their parents
+      const int c = s_next[u];
+      ob[m] = s_tok[c];
+      ++m;
+      pb[m] = c;
+      u = c;
+    }
+    ob[m] = s_draw[u];
+    for (int j = m + 1; j <= Dmax; ++j) {
+      pb[j] = -1;
+      ob[j] = -1;
+    }
+    n_accepted[b] = m;
+  }
+}
+
+// one workgroup per sequence: the kept branch of the typical mode from the
+// pass flags, then the accepted tokens and the draw at its end
+__global__ __launch_bounds__(256) void typical_pick(int N, int Dmax, const int32_t* __restrict__ tok,
+                                                    const int32_t* __restrict__ parent,
+                                                    const int32_t* __restrict__ pass,
+                                                    const int32_t* __restrict__ draw,
+                                                    int32_t* __restrict__ n_accepted, int32_t* __restrict__ path,
+                                                    int32_t* __restrict__ out_tok) {
+  __shared__ int s_par[HYDRA_MAX_VERIFY];
+  __shared__ uint8_t s_pass[HYDRA_MAX_VERIFY];
+  __shared__ uint32_t s_keys[4];
+  const int b = blockIdx.x, tid = threadIdx.x;
+  for (int c = tid; c < N; c += 256) {
+    s_par[c] = parent[static_cast<size_t>(b) * N + c];
+    s_pass[c] = pass[static_cast<size_t>(b) * N + c] != 0;
+  }
+  __syncthreads();
+  // every node walks up to the root (at most Dmax steps): it is kept when each
+  // node on the way passes; the kept branch is the largest (depth, -index)
+  uint32_t key = 0;
+  if (tid < N) {
+    int v = tid, dc = 0;
+    bool ok = true;
+    while (v > 0 && ok) {
+      const int pv = s_par[v];
+      ok = pv >= 0 && pv < v && s_pass[v] && dc < Dmax;
+      ++dc;
+      v = pv;
+    }
+    if (ok && v == 0) key = (static_cast<uint32_t>(dc) << 16) | (0xFFFFu - static_cast<uint32_t>(tid));
+  }
+  key = wave_max_u32(key);
+  if ((tid & 63) == 0) s_keys[tid >> 6] = key;
+  __syncthreads();
+  if (tid == 0) {
+    const uint32_t best = max(max(s_keys[0], s_keys[1]), max(s_keys[2], s_keys[3]));
+    const int end = static_cast<int>(0xFFFFu - (best & 0xFFFFu)), m = static_cast<int>(best >> 16);
+    int32_t* pb = path + static_cast<size_t>(b) * (Dmax + 1);
+    int32_t* ob = out_tok + static_cast<size_t>(b) * (Dmax + 1);
+    for (int j = m + 1; j <= Dmax; ++j) {
+      pb[j] = -1;
+      ob[j] = -1;
+    }
+    ob[m] = draw[static_cast<size_t>(b) * N + end];
+    int v = end;
+    for (int j = m; j >= 1; --j) {
+      pb[j] = v;
+      ob[j - 1] = tok[static_cast<size_t>(b) * N + v];
+      v = s_par[v];
+    }
+    pb[0] = 0;
+    n_accepted[b] = m;
+  }
+}
+
+// register tiles per thread for a vocabulary of V, or 0 past 32 (streamed walks)
+int walk_ept(int V) {
+  const int e = (V + kWalkThreads - 1) / kWalkThreads;
+  for (int t = 1; t <= 32; t *= 2)
+    if (e <= t) return t;
+  return 0;
+}
+
+template <typename F>
+void with_ept(int ept, F f) {
+  switch (ept) {
+    case 1: f(std::integral_constant<int, 1>{}); break;
+    case 2: f(std::integral_constant<int, 2>{}); break;
+    case 4: f(std::integral_constant<int, 4>{}); break;
+    case 8: f(std::integral_constant<int, 8>{}); break;
+    case 16: f(std::integral_constant<int, 16>{}); break;
+    default: f(std::integral_constant<int, 32>{}); break;
+  }
+}
+
 }  // namespace
 }  // namespace hydra
 
@@ -381,8 +838,10 @@ extern "C" size_t tree_accept_workspace_size(int mode, int B, int N, int V) {
   if (mode == 0)
     return align_up(rows * sizeof(int32_t), 256) + align_up(rows * projection_nwg(V) * sizeof(uint64_t), 256) +
            align_up(static_cast<size_t>(B) * sizeof(int), 256) + 256;
-  if (mode == 2) return align_up(rows * sizeof(int32_t), 256) + 256;
-  return align_up(static_cast<size_t>(B) * 2 * V * sizeof(float), 256) + 256;
+  // modes 1 and 2: two int32 per row (next child or pass flag, and the draw)
+  const size_t per_row = 2 * align_up(rows * sizeof(int32_t), 256);
+  if (mode == 2) return per_row + 256;
+  return per_row + align_up(static_cast<size_t>(B) * 2 * V * sizeof(float), 256) + 256;
 }
 
 extern "C" int tree_accept(int dtype, int mode, int B, int N, int d, int V, int Dmax, const void* o,
@@ -467,20 +926,43 @@ extern "C" int tree_accept(int dtype, int mode, int B, int N, int d, int V, int 
                                TopkPartials{nullptr, nullptr}, stream);
     if (rc != HYDRA_OK) return rc;
     int32_t* pass = arena.take<int32_t>(static_cast<size_t>(M));
+    int32_t* drawn = arena.take<int32_t>(static_cast<size_t>(M));
     const float invT = 1.0f / temperature;
-    typical_rows<<<M, kTypThreads, 0, stream>>>(N, V, invT, logf(eps), logf(delta), target_logits, tok, parent,
-                                                pass);
-    HY_LAUNCH_CHECK("tree_accept: typical rows");
-    typical_walk<<<B, kWalkThreads, 0, stream>>>(N, V, Dmax, invT, target_logits, tok, parent, pass, u_res,
-                                                 n_accepted, path, out_tok);
-    HY_LAUNCH_CHECK("tree_accept: typical walk");
+    if (const int ept = walk_ept(V)) {
+      with_ept(ept, [&](auto e) {
+        typical_node_reg<decltype(e)::value><<<M, kWalkThreads, 0, stream>>>(
+            N, V, invT, logf(eps), logf(delta), target_logits, tok, parent, u_res, pass, drawn);
+      });
+      HY_LAUNCH_CHECK("tree_accept: typical nodes");
+      typical_pick<<<B, 256, 0, stream>>>(N, Dmax, tok, parent, pass, drawn, n_accepted, path, out_tok);
+      HY_LAUNCH_CHECK("tree_accept: typical pick");
+    } else {
+      typical_rows<<<M, kTypThreads, 0, stream>>>(N, V, invT, logf(eps), logf(delta), target_logits, tok, parent,
+                                                  pass);
+      HY_LAUNCH_CHECK("tree_accept: typical rows");
+      typical_walk<<<B, kWalkThreads, 0, stream>>>(N, V, Dmax, invT, target_logits, tok, parent, pass, u_res,
+                                                   n_accepted, path, out_tok);
+      HY_LAUNCH_CHECK("tree_accept: typical walk");
+    }
   } else {
     int rc = launch_projection(dtype, M, d, V, xs, W_t, target_logits, RowMap{M, 0, 0}, V, 1, nullptr,
                                TopkPartials{nullptr, nullptr}, stream);
     if (rc != HYDRA_OK) return rc;
+    int32_t* nxt = arena.take<int32_t>(static_cast<size_t>(M));
+    int32_t* drawn = arena.take<int32_t>(static_cast<size_t>(M));
     float* rbuf = arena.take<float>(static_cast<size_t>(B) * 2 * V);
-    reject_walk<<<B, kWalkThreads, 0, stream>>>(N, V, R, Dmax, 1.0f / temperature, target_logits, head_logits, tok,
-                                                parent, q_row, u_acc, u_res, rbuf, n_accepted, path, out_tok);
+    const float invT = 1.0f / temperature;
+    if (const int ept = walk_ept(V)) {
+      with_ept(ept, [&](auto e) {
+        reject_node_reg<decltype(e)::value><<<M, kWalkThreads, 0, stream>>>(
+            N, V, R, Dmax, invT, target_logits, head_logits, tok, parent, q_row, u_acc, u_res, nxt, drawn);
+      });
+      HY_LAUNCH_CHECK("tree_accept: rejection nodes");
+      reject_pick<<<B, 64, 0, stream>>>(N, Dmax, tok, nxt, drawn, n_accepted, path, out_tok);
+    } else {
+      reject_walk<<<B, kWalkThreads, 0, stream>>>(N, V, R, Dmax, invT, target_logits, head_logits, tok, parent,
+                                                  q_row, u_acc, u_res, rbuf, n_accepted, path, out_tok);
+    }
     HY_LAUNCH_CHECK("tree_accept: rejection walk");
   }
   return HYDRA_OK;

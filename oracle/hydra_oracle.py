@@ -33,6 +33,8 @@ Readings of points the pages leave open (each is listed in the design doc):
 * Sparse template: rank paths with ranks below the per-depth fan-out caps,
   ordered by (2**depth * prod(rank + 1), depth, path) ascending; the first
   ``n_nodes - 1`` plus the root.
+* Positions: tree row u of sequence b stands at L_b + depth(u); rotary
+  embedding in the LLaMA half-split layout with base theta (10000).
 * Typical acceptance: at the parent u, with p = softmax(Z[u] / T), a child
   passes iff p(x) > min(eps, delta * exp(-H(p))); the kept branch is the
   deepest node whose whole path passes (smallest breadth-first index among
@@ -64,6 +66,7 @@ __all__ = [
     "tree_mask", "tree_attention", "target_logits", "argmax_lowest",
     "greedy_accept", "residual", "sample_inverse_cdf", "rejection_accept",
     "commit_path", "entropy", "typical_passes", "kept_branch", "typical_accept",
+    "tree_positions", "rope",
 ]
 
 
@@ -383,6 +386,37 @@ def tree_mask(parent):
             M[u, v] = 0.0
             v = int(parent[v])
     return M
+
+
+# ---------------------------------------------------------------------------
+# Positions of the tree rows and their rotary embedding
+# ---------------------------------------------------------------------------
+
+def tree_positions(prefix_len, depth):
+    """Position of every tree row: L_b + depth [SD, "Beyond draft models:
+    Medusa": the candidates of one head stand at the same future position;
+    HG, "Parallel Verification and Greedy Acceptance Algorithm": accepting a
+    depth-k node advances to position t + k]. Siblings share a position; the
+    root (depth 0) is at L_b, the first position not in the cache.
+    prefix_len [B], depth [B, N]."""
+    L = np.asarray(prefix_len, dtype=np.int64)
+    return L[:, None] + np.asarray(depth, dtype=np.int64)
+
+
+def rope(x, pos, theta=10000.0):
+    """Rotary position embedding of the rows of x [..., D] at positions pos
+    (broadcast over the leading axes), in the half-split layout of the
+    LLaMA family: dimension i pairs with i + D/2 and rotates by the angle
+    pos * theta^(-2i/D). This is how position ids enter the pages' models
+    (Vicuna, LLaMA-2); the pages only fix the positions themselves."""
+    x = np.asarray(x, dtype=np.float64)
+    D = x.shape[-1]
+    half = D // 2
+    inv = theta ** (-2.0 * np.arange(half) / D)
+    ang = np.asarray(pos, dtype=np.float64)[..., None] * inv
+    c, s = np.cos(ang), np.sin(ang)
+    a, b = x[..., :half], x[..., half:]
+    return np.concatenate([a * c - b * s, b * c + a * s], axis=-1)
 
 
 # ---------------------------------------------------------------------------

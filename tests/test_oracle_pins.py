@@ -686,3 +686,54 @@ def test_kept_branch_is_the_longest_fully_passing_path_by_brute_force():
                 if all(passes[c] for c in chain):
                     best = max(best, (len(chain) - 1, -u))
             assert H.kept_branch(passes, plan.parent) == -best[1]
+
+
+# ------------------------------------------------------- positions and RoPE
+
+def test_rope_is_a_rotation_with_additive_angles():
+    rng = np.random.default_rng(60)
+    x = rng.standard_normal((7, 3, 64))
+    pos = rng.integers(0, 20000, (7, 3))
+    y = H.rope(x, pos)
+    assert np.allclose(np.linalg.norm(y, axis=-1), np.linalg.norm(x, axis=-1), rtol=1e-12)
+    assert np.array_equal(H.rope(x, np.zeros((7, 3))), x)
+    assert np.allclose(H.rope(H.rope(x, pos), pos + 5), H.rope(x, 2 * pos + 5), atol=1e-9)
+    # the same rotation as multiplying (x_i + j x_{i+D/2}) by exp(j pos theta^(-2i/D))
+    z = (x[..., :32] + 1j * x[..., 32:]) * np.exp(1j * pos[..., None] * 10000.0 ** (-np.arange(32) / 32))
+    assert np.allclose(y, np.concatenate([z.real, z.imag], axis=-1), atol=1e-9)
+
+
+def test_rope_scores_depend_on_position_differences_only():
+    rng = np.random.default_rng(61)
+    q, k = rng.standard_normal(128), rng.standard_normal(128)
+    for m, n, s in ((3, 1, 100), (50, 70, 12345), (0, 0, 7)):
+        a = H.rope(q, m) @ H.rope(k, n)
+        b = H.rope(q, m + s) @ H.rope(k, n + s)
+        assert math.isclose(a, b, rel_tol=1e-9, abs_tol=1e-9)
+
+
+@pytest.mark.parametrize("tree", [[2, 3], [3, 2, 2]])
+def test_tree_positions_make_each_branch_a_causal_sequence(tree):
+    """With positions L + depth, tree attention over rotated Q/K equals causal
+    attention over each root-to-leaf branch at consecutive positions L, L+1, ...
+    (positions by breadth-first index would break this for every branch that
+    is not the first)."""
+    rng = np.random.default_rng(62 + len(tree))
+    plan = H.plan_cartesian(tree)
+    N, Hq, Hkv, D, L = plan.n, 4, 2, 16, 9
+    anc = H.ancestors(plan.parent, plan.dmax)[None]
+    q = rng.standard_normal((1, N, Hq, D))
+    kt, vt = rng.standard_normal((1, N, Hkv, D)), rng.standard_normal((1, N, Hkv, D))
+    kp, vp = rng.standard_normal((L, Hkv, D)), rng.standard_normal((L, Hkv, D))
+    pos = H.tree_positions([L], plan.depth[None])
+    assert pos[0, 0] == L and np.array_equal(pos[0], L + plan.depth)
+    kp_rot = H.rope(kp, np.arange(L)[:, None])
+    out, _ = H.tree_attention(H.rope(q, pos[..., None]), H.rope(kt, pos[..., None]), vt, [kp_rot], [vp], anc)
+    for leaf in [u for u in range(N) if not plan.children(u)]:
+        br = [int(a) for a in anc[0, leaf] if a >= 0]
+        cpos = np.arange(L, L + len(br))[:, None]
+        qs = np.concatenate([np.zeros((L, Hq, D)), H.rope(q[0, br], cpos)])
+        ks = np.concatenate([kp_rot, H.rope(kt[0, br], cpos)])
+        vs = np.concatenate([vp, vt[0, br]])
+        ref = _causal_sdpa(torch.from_numpy(qs), torch.from_numpy(ks), torch.from_numpy(vs)).numpy()[L:]
+        assert np.allclose(out[0, br], ref, rtol=1e-10, atol=1e-12)

@@ -3,8 +3,9 @@
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--acceptance MODE] [--no-graph]
                 [--no-cpu] [--no-fold]
 
-A step is one whole round (draft heads -> tree build -> tree-attention verify
--> accept -> commit of the kept branch into the KV cache) over the workload's
+A step is one whole round (draft heads -> tree build -> rotary embedding of
+the tree Q/K rows at positions prefix + depth -> tree-attention verify ->
+accept -> commit of the kept branch into the KV cache) over the workload's
 synthetic batch, with every input resident in
 HBM before timing starts. The default workload is the Vicuna-7B-shaped layer
 with the 64-node sparse tree and a 2048-token prefix (batch 1). The value is
@@ -194,7 +195,9 @@ def cpu_baseline(inp, n_rows):
         else:
             trees = [(plan, np.arange(plan.n)) for _ in range(w.B)]
         anc = np.stack([O.ancestors(t.parent, plan.dmax) for t, _ in trees])
-        out, _ = O.tree_attention(q, kt, vt, kp, vp, anc, bf16=w.dtype == "bf16")
+        pos = O.tree_positions(lens, np.stack([t.depth for t, _ in trees]))[..., None]
+        q_rot, kt_rot = O.rope(q, pos), O.rope(kt, pos)
+        out, _ = O.tree_attention(q_rot, kt_rot, vt, kp, vp, anc, bf16=w.dtype == "bf16")
         Z = O.target_logits(out, Wt)
         n_acc = np.zeros(w.B, dtype=np.int64)
         path = -np.ones((w.B, plan.dmax + 1), dtype=np.int64)
@@ -209,7 +212,7 @@ def cpu_baseline(inp, n_rows):
                 m, pth, tk = O.rejection_accept(Z[b], res["z"][b], node_row[s], tb, t.parent, u_acc[b], u_res[b],
                                                 w.T)
             n_acc[b], path[b, : m + 1], toks[b, : m + 1] = m, pth, tk
-        O.commit_path(kpool, vpool, bt, lens, kt[None], vt[None], n_acc, path, toks, plan.dmax,
+        O.commit_path(kpool, vpool, bt, lens, kt_rot[None], vt[None], n_acc, path, toks, plan.dmax,
                       out.reshape(w.B, out.shape[1], -1))
         total += time.perf_counter() - t0
         reps += 1

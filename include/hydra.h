@@ -6,6 +6,8 @@
  *   hydra_draft_heads      draft heads + per-head top-k, filling the candidate tree
  *   tree_build             final tree (identity or pruned), ancestor table
  *   tree_attention_verify  tree-masked attention over a paged KV prefix
+ *                          (tree_rope first rotates the tree Q/K rows at
+ *                          positions prefix_len + depth)
  *   tree_accept            target vocabulary projection + acceptance walk
  *   tree_commit            kept branch into the paged KV cache, next root and h
  * plus host-side tree-plan builders, workspace-size queries and status strings.
@@ -232,6 +234,33 @@ int tree_build(int B, int N, int Dmax, const int32_t* node_parent,
                const float* cand_logp, int n_keep, int32_t* tok, int32_t* parent,
                int32_t* depth, int32_t* anc, int32_t* q_row, int32_t* src,
                void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Before attention: positions of the tree rows and their rotary embedding
+ *
+ * [SD] "Beyond draft models: Medusa": the candidates of one head stand at the
+ * same future position; [HG] "Parallel Verification and Greedy Acceptance
+ * Algorithm": accepting a depth-k node advances to position t + k. Tree row u
+ * of sequence b stands at pos = prefix_len[b] + depth[b, u] (siblings share
+ * it; the root is at prefix_len[b]), and
+ *   out[b, u, h, i]       = x_i cos(a) - x_{i+D/2} sin(a)
+ *   out[b, u, h, i + D/2] = x_{i+D/2} cos(a) + x_i sin(a),
+ *   a = pos * theta^(-2i/D), i < D/2
+ * (the half-split layout of the LLaMA family), computed in float64 and
+ * rounded once to the storage type. Apply it to the tree Q and K rows (not V)
+ * before tree_attention_verify; the cached prefix K rows were rotated at
+ * their own positions when they were written (tree_commit copies rotated
+ * rows, whose positions L + depth are the cache positions they land on).
+ *
+ * x, out        [B, N, H, D] (dtype); out may equal x (in place)
+ * depth         [B, N] int32 from tree_build
+ * prefix_len    [B] int32
+ * theta         rotary base (> 1; 10000 in the LLaMA family)
+ * Limits: D even. B = 0 is a no-op. No workspace.
+ * ---------------------------------------------------------------------- */
+int tree_rope(int dtype, int B, int N, int H, int D, const void* x, void* out,
+              const int32_t* depth, const int32_t* prefix_len, float theta,
+              void* stream);
 
 /* ------------------------------------------------------------------------
  * Stage 3: tree-masked attention verify (one attention layer's share)

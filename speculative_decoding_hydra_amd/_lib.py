@@ -32,6 +32,7 @@ SIGNATURES = {
     "tree_build_workspace_size": (c_size, [c_int, c_int, c_int]),
     "tree_build": (c_int, [c_int, c_int, c_int, c_void, c_void, c_void, c_void, c_void, c_void, c_int,
                            c_void, c_void, c_void, c_void, c_void, c_void, c_void, c_size, c_void]),
+    "tree_rope": (c_int, [c_int, c_int, c_int, c_int, c_int, c_void, c_void, c_void, c_void, c_float, c_void]),
     "tree_attention_verify_workspace_size": (c_size, [c_int, c_int, c_int, c_int, c_int, c_int, c_int]),
     "tree_attention_verify": (c_int, [c_int, c_int, c_int, c_int, c_int, c_int, c_float, c_void, c_void,
                                       c_void, c_void, c_void, c_int, c_int, c_void, c_int, c_void, c_int,

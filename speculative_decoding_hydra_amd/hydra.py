@@ -266,6 +266,21 @@ def tree_build(dplan: DevicePlan, cand_tok, cand_logp, n_keep, tok, parent, dept
     return _check("tree_build", rc)
 
 
+def tree_rope(x, depth, prefix_len, out=None, theta=10000.0, stream=None):
+    """Rotary embedding of the tree rows x [B, N, H, D] at positions
+    prefix_len + depth (see include/hydra.h); out defaults to x (in place)."""
+    B, N, H, D = x.shape
+    if out is None:
+        out = x
+    if tuple(out.shape) != tuple(x.shape) or tuple(depth.shape) != (B, N) or tuple(prefix_len.shape) != (B,):
+        raise ValueError(f"tree_rope: shapes x {tuple(x.shape)}, out {tuple(out.shape)}, depth "
+                         f"{tuple(depth.shape)}, prefix_len {tuple(prefix_len.shape)}")
+    rc = lib().tree_rope(_dtype_code(x), B, N, H, D, _dev(x, "x"), _dev(out, "out", x.dtype),
+                         _dev(depth, "depth", torch.int32), _dev(prefix_len, "prefix_len", torch.int32), float(theta),
+                         _stream(stream))
+    return _check("tree_rope", rc)
+
+
 def tree_attention_verify_workspace_size(dtype_code, B, N, Hq, Hkv, D, max_prefix_len):
     return int(lib().tree_attention_verify_workspace_size(dtype_code, B, N, Hq, Hkv, D, max_prefix_len))
 

@@ -35,10 +35,12 @@ class HydraRound:
     fold_embedding: build the folded embedding tables of the Hydra heads
     (hydra_fold_embedding, V * d * 4 bytes per head) once here and let the
     draft stage look the embedding half up; None folds for bf16 Hydra heads.
+    rope_theta: rotate the tree Q/K rows at positions prefix_len + depth
+    (tree_rope) before attention; None gives the rows to attention as they are.
     """
 
     def __init__(self, weights, tree, shape, hydra=True, mode=0, temperature=1.0, residual=True,
-                 keep_hidden=False, device="cuda", fold_embedding=None, eps=None, delta=None):
+                 keep_hidden=False, device="cuda", fold_embedding=None, eps=None, delta=None, rope_theta=10000.0):
         self.w = weights
         plan, n_keep = make_plan(tree)
         self.dplan = H.DevicePlan(plan, hydra, device)
@@ -63,6 +65,9 @@ class HydraRound:
         self.q_row, self.src = z(B, K, dtype=i32), z(B, K, dtype=i32)
         self.anc = z(B, K, Dm + 1, dtype=i32)
         self.attn_out = z(B, K, Hq, D, dtype=dt)
+        self.rope_theta = rope_theta
+        self.q_rot = z(B, K, Hq, D, dtype=dt) if rope_theta else None
+        self.k_rot = z(B, K, Hkv, D, dtype=dt) if rope_theta else None
         self.attn_lse = z(B, K, Hq)
         self.target_logits = z(B, K, V)
         self.n_accepted = z(B, dtype=i32)
@@ -97,6 +102,10 @@ class HydraRound:
                      self.anc, self.q_row, self.src, self.ws_build, stream=stream)
 
     def attend(self, q, k_tree, v_tree, k_pages, v_pages, block_table, prefix_len, stream=None):
+        if self.rope_theta:
+            H.tree_rope(q, self.depth, prefix_len, out=self.q_rot, theta=self.rope_theta, stream=stream)
+            H.tree_rope(k_tree, self.depth, prefix_len, out=self.k_rot, theta=self.rope_theta, stream=stream)
+            q, k_tree = self.q_rot, self.k_rot
         H.tree_attention_verify(q, k_tree, v_tree, k_pages, v_pages, block_table, prefix_len,
                                 self.shape["max_prefix_len"], self.anc, self.depth, self.attn_out, self.attn_lse,
                                 self.ws_attn, stream=stream)
@@ -112,6 +121,8 @@ class HydraRound:
         """Root and accepted rows into the paged cache (in place); next
         prefix lengths, roots and hidden states into next_*."""
         B, K = self.attn_out.shape[:2]
+        if self.rope_theta:
+            k_tree = self.k_rot  # the cache holds rotated keys
         H.tree_commit(k_tree, v_tree, k_pages, v_pages, block_table, prefix_len, self.n_accepted, self.path,
                       self.out_tok, self.next_prefix_len, self.next_root_tok, hidden=self.attn_out.view(B, K, -1),
                       next_h=self.next_h, stream=stream)

@@ -191,8 +191,15 @@ def check_attention(inp, rnd, seqs=None):
     sub = lambda x: HI.as_f64(x[seqs])  # noqa: E731
     kp = [HI.as_f64(inp["k_prefix"][b]) for b in seqs]
     vp = [HI.as_f64(inp["v_prefix"][b]) for b in seqs]
-    out, lse = O.tree_attention(sub(inp["q_tree"]), sub(inp["k_tree"]), sub(inp["v_tree"]), kp, vp, anc,
-                                bf16=w.dtype == "bf16")
+    q, k = sub(inp["q_tree"]), sub(inp["k_tree"])
+    if rnd.rope_theta:  # rows rotated at prefix_len + depth (the device's tree)
+        pos = O.tree_positions(inp["prefix_len"].numpy()[seqs], np_(rnd.depth)[seqs])[..., None]
+        q, k = O.rope(q, pos, rnd.rope_theta), O.rope(k, pos, rnd.rope_theta)
+        t_rot = 1e-6 if w.dtype == "fp32" else 2e-2
+        for name, mine, dev_rot in (("q", q, rnd.q_rot), ("k", k, rnd.k_rot)):
+            e = float(np.max(np.abs(mine - np_(dev_rot)[seqs])))
+            assert e <= t_rot, f"rotated {name} max-abs {e:.3g}"
+    out, lse = O.tree_attention(q, k, sub(inp["v_tree"]), kp, vp, anc, bf16=w.dtype == "bf16")
     got = np_(rnd.attn_out)[seqs]
     e_o = float(np.max(np.abs(out - got)))
     e_l = float(np.max(np.abs(lse - np_(rnd.attn_lse)[seqs])))
@@ -308,8 +315,9 @@ def check_commit(inp, rnd, dev, seqs=None):
         pages = [int(p) for p in bt[b] if p >= 0]
         sub_bt = np.arange(len(pages))[None]
         sub = lambda pool: HI.as_f64(pool[pages])[None]  # noqa: E731
+        ksrc = rnd.k_rot if rnd.rope_theta else inp["k_tree"]  # the keys the round committed
         rk, rv, rl, rr, _ = O.commit_path(sub(inp["k_pages"]), sub(inp["v_pages"]), sub_bt, lens[b:b + 1],
-                                          HI.as_f64(inp["k_tree"][b:b + 1])[None],
+                                          np_(ksrc[b:b + 1])[None],
                                           HI.as_f64(inp["v_tree"][b:b + 1])[None], n_acc[b:b + 1],
                                           path[b:b + 1], out[b:b + 1], Dm)
         assert np.array_equal(np_(dev["k_pages"][pages]), rk[0]), f"seq {b}: committed K pages"

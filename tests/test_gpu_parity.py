@@ -262,7 +262,8 @@ def test_tiny_round_end_to_end(name):
         assert res["margin"][0, r] > T.MARGIN, "near tie: seed would need the margin rule"
     assert np.array_equal(res["tok"], rnd.cand_tok.cpu().numpy())
     anc = O.ancestors(plan.parent, plan.dmax)[None]
-    out, _ = O.tree_attention(f(inp["q_tree"]), f(inp["k_tree"]), f(inp["v_tree"]),
+    pos = O.tree_positions(inp["prefix_len"].numpy(), plan.depth[None])[..., None]
+    out, _ = O.tree_attention(O.rope(f(inp["q_tree"]), pos), O.rope(f(inp["k_tree"]), pos), f(inp["v_tree"]),
                               [f(x) for x in inp["k_prefix"]], [f(x) for x in inp["v_prefix"]], anc)
     Z = O.target_logits(out, f(inp["W_t"]))[0]
     m, path, toks = O.greedy_accept(Z, res["tok"][0], plan.parent, plan.dmax)
@@ -553,7 +554,7 @@ def test_tree_commit(dtype, B, N, Hkv, D, layers, page, dmax):
         assert rroot[3] == -1 and rroot[4] == -1  # the invalid sequences committed nothing
 
 
-def _oracle_round(w, inp, plan, h, root, q, kt, vt, kpre, vpre, dev_logits):
+def _oracle_round(w, inp, plan, h, root, q, kt, vt, kpre, vpre, dev_logits, L):
     """The oracle's own greedy round (float32 workloads, B = 1). Its top-k
     decisions are the device's whenever every margin exceeds twice the
     largest difference between the two sides' head logits, so that is
@@ -565,10 +566,12 @@ def _oracle_round(w, inp, plan, h, root, q, kt, vt, kpre, vpre, dev_logits):
     assert err <= 1e-4, f"head logits max-abs {err:.3g}"
     assert np.all(res["margin"] > 2 * err), f"top-k margin {res['margin'].min():.3g} within 2 x {err:.3g}"
     anc = O.ancestors(plan.parent, plan.dmax)[None]
+    pos = O.tree_positions([L], plan.depth[None])[..., None]  # rows rotated at L + depth
+    q, kt = O.rope(q, pos), O.rope(kt, pos)
     out, _ = O.tree_attention(q, kt, vt, kpre, vpre, anc)
     Z = O.target_logits(out, f(inp["W_t"]))[0]
     m, path, toks = O.greedy_accept(Z, res["tok"][0], plan.parent, plan.dmax)
-    return res, out, m, path, toks
+    return res, out, m, path, toks, kt
 
 
 @pytest.mark.parametrize("name", ["tiny", "tiny_medusa"])
@@ -594,21 +597,23 @@ def test_two_rounds_through_the_commit(name):
 
     f = HI.as_f64
     L = int(inp["prefix_len"][0])
-    res, out, m, path, toks = _oracle_round(w, inp, plan, f(inp["h"]), inp["root_tok"].numpy(), f(inp["q_tree"]),
-                                            f(inp["k_tree"]), f(inp["v_tree"]), [f(inp["k_prefix"][0])],
-                                            [f(inp["v_prefix"][0])], rnd.head_logits)
+    res, out, m, path, toks, kt_rot = _oracle_round(w, inp, plan, f(inp["h"]), inp["root_tok"].numpy(),
+                                                    f(inp["q_tree"]), f(inp["k_tree"]), f(inp["v_tree"]),
+                                                    [f(inp["k_prefix"][0])], [f(inp["v_prefix"][0])],
+                                                    rnd.head_logits, L)
     assert [int(x) for x in rnd.path[0] if x >= 0] == path and int(rnd.n_accepted[0]) == m
     bt = inp["block_table"].numpy()
     pad = lambda a: np.concatenate([a, -np.ones(plan.dmax + 1 - len(a), dtype=np.int64)])[None]  # noqa: E731
     kp, vp, nlen, nroot, nh = O.commit_path(f(inp["k_pages"])[None], f(inp["v_pages"])[None], bt, [L],
-                                            f(inp["k_tree"])[None], f(inp["v_tree"])[None], [m], pad(path),
+                                            kt_rot[None], f(inp["v_tree"])[None], [m], pad(path),
                                             pad(toks), plan.dmax, out.reshape(1, plan.n, -1))
     assert int(rnd.next_prefix_len[0]) == nlen[0] == L + m + 1 and int(rnd.next_root_tok[0]) == nroot[0]
     assert np.max(np.abs(rnd.next_h.cpu().double().numpy() - nh)) <= 1e-4
     ps = int(inp["page_size"])
     gather = lambda pool: np.stack([pool[0, bt[0, p // ps], :, p % ps] for p in range(nlen[0])])  # noqa: E731
-    res2, out2, m2, path2, toks2 = _oracle_round(w, inp, plan, nh, nroot, f(fresh["q_tree"]), f(fresh["k_tree"]),
-                                                 f(fresh["v_tree"]), [gather(kp)], [gather(vp)], rnd2.head_logits)
+    res2, out2, m2, path2, toks2, _ = _oracle_round(w, inp, plan, nh, nroot, f(fresh["q_tree"]),
+                                                    f(fresh["k_tree"]), f(fresh["v_tree"]), [gather(kp)],
+                                                    [gather(vp)], rnd2.head_logits, int(nlen[0]))
     assert np.array_equal(res2["tok"], rnd2.cand_tok.cpu().numpy())
     assert np.max(np.abs(out2 - rnd2.attn_out.cpu().double().numpy())) <= 1e-4
     assert int(rnd2.n_accepted[0]) == m2
@@ -698,3 +703,33 @@ def test_typical_planted_branches(B, dtype):
         assert int(n_acc[b]) == len(got_p) - 1
         assert got_p[-1] == want[b], f"seq {b}: kept branch ends at {got_p[-1]}, planted {want[b]}"
         T.check_typical(Zc[b], tok[b], plan.parent, ur[b], w, got_p, got_o, f"seq {b}")
+
+
+# ---------------------------------------------------------- positions / RoPE
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("B,N,H,D,lens,inplace", [(1, 9, 8, 32, [128], False), (3, 64, 32, 128, [0, 2049, 16384], False),
+                                                  (2, 37, 8, 64, [5, 700], True), (1, 1, 1, 2, [3], True)])
+def test_tree_rope(dtype, B, N, H, D, lens, inplace):
+    """Rotated rows against the oracle at positions prefix_len + depth:
+    float32 within 1e-6, bfloat16 within one rounding step of the oracle's
+    value rounded to bfloat16."""
+    from speculative_decoding_hydra_amd import tree_rope
+
+    print(f"rope {dtype} B={B} N={N} H={H} D={D} L={lens} inplace={inplace}", flush=True)
+    g = torch.Generator().manual_seed(B * 100 + N + D)
+    dt = torch.float32 if dtype == "fp32" else torch.bfloat16
+    x = torch.randn(B, N, H, D, generator=g).to(dt)
+    depth = torch.randint(0, 9, (B, N), generator=g, dtype=torch.int32)
+    L = torch.tensor(lens, dtype=torch.int32)
+    xd = x.cuda()
+    out = xd if inplace else torch.full_like(xd, float("nan"))
+    tree_rope(xd, depth.cuda(), L.cuda(), out=out)
+    torch.cuda.synchronize()
+    ref = O.rope(HI.as_f64(x), O.tree_positions(L.numpy(), depth.numpy())[..., None])
+    got = out.cpu().double().numpy()
+    if dtype == "fp32":
+        assert np.max(np.abs(got - ref)) <= 1e-6
+    else:
+        step = np.ldexp(1.0, np.frexp(np.maximum(np.abs(ref), 1e-30))[1] - 8)
+        assert np.all(np.abs(got - ref) <= step), float(np.max(np.abs(got - ref) / step))

@@ -35,6 +35,9 @@ Readings of points the pages leave open (each is listed in the design doc):
   ``n_nodes - 1`` plus the root.
 * Positions: tree row u of sequence b stands at L_b + depth(u); rotary
   embedding in the LLaMA half-split layout with base theta (10000).
+* Decoder layer of the verify pass: the LLaMA pre-norm layer (RMSNorm,
+  rotated Q/K, tree attention, output projection, residual, RMSNorm, SwiGLU
+  feed-forward, residual) over every tree row at once.
 * Typical acceptance: at the parent u, with p = softmax(Z[u] / T), a child
   passes iff p(x) > min(eps, delta * exp(-H(p))); the kept branch is the
   deepest node whose whole path passes (smallest breadth-first index among
@@ -66,7 +69,7 @@ __all__ = [
     "tree_mask", "tree_attention", "target_logits", "argmax_lowest",
     "greedy_accept", "residual", "sample_inverse_cdf", "rejection_accept",
     "commit_path", "entropy", "typical_passes", "kept_branch", "typical_accept",
-    "tree_positions", "rope",
+    "tree_positions", "rope", "rms_norm", "decoder_layer",
 ]
 
 
@@ -461,6 +464,53 @@ def tree_attention(q, k_tree, v_tree, k_prefix, v_prefix, anc, bf16=False):
     if bf16:
         out = round_bf16(out)
     return out, lse
+
+
+# ---------------------------------------------------------------------------
+# One decoder layer of the target over the tree rows (verification pass)
+# ---------------------------------------------------------------------------
+
+def rms_norm(x, g, eps):
+    """x / sqrt(mean(x^2) + eps) * g over the last axis."""
+    x = np.asarray(x, dtype=np.float64)
+    return x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps) * np.asarray(g, dtype=np.float64)
+
+
+def decoder_layer(x, w, k_prefix, v_prefix, anc, depth, prefix_len, Hq, Hkv, D, eps, theta=10000.0,
+                  bf16=False):
+    """The target's decoder layer over every tree row, all rows in one pass
+    [SD, "Draft, then verify": the target scores all candidates in one
+    forward pass; HG, "Tree Attention Matrix with Topology-Aware Causal
+    Masking": each row sees the prefix and its ancestors].
+
+    Reading (the pages name the models, Vicuna / LLaMA, not their layer):
+    the LLaMA pre-norm layer,
+      a = rms(x) g1;  q, k, v = a Wq^T, a Wk^T, a Wv^T;  q, k rotated at L + depth;
+      o = tree attention;  x1 = x + o Wo^T;
+      b = rms(x1) g2;  x2 = x1 + (silu(b Wg^T) * (b Wu^T)) Wd^T.
+    x [B, N, d]; w: dict of g1, Wq [Hq D, d], Wk/Wv [Hkv D, d], Wo [d, Hq D],
+    g2, Wg/Wu [F, d], Wd [d, F]; k_prefix/v_prefix: per sequence [L_b, Hkv, D]
+    (already rotated keys). With bf16, the tensors the device stores in
+    bfloat16 (a, q, k, v, o, x1, b, the gated product, x2) are rounded there.
+    Returns (x2, k_rot, v) with k_rot, v [B, N, Hkv, D] (the rows a commit
+    copies into this layer's cache).
+    """
+    r = round_bf16 if bf16 else (lambda t: t)
+    f = lambda t: np.asarray(t, dtype=np.float64)  # noqa: E731
+    x = f(x)
+    B, N, d = x.shape
+    a = r(rms_norm(x, w["g1"], eps))
+    q = r(a @ f(w["Wq"]).T).reshape(B, N, Hq, D)
+    k = r(a @ f(w["Wk"]).T).reshape(B, N, Hkv, D)
+    v = r(a @ f(w["Wv"]).T).reshape(B, N, Hkv, D)
+    pos = tree_positions(prefix_len, depth)[..., None]
+    q, k = r(rope(q, pos, theta)), r(rope(k, pos, theta))
+    o, _ = tree_attention(q, k, v, k_prefix, v_prefix, anc, bf16=bf16)
+    x1 = r(x + o.reshape(B, N, Hq * D) @ f(w["Wo"]).T)
+    b = r(rms_norm(x1, w["g2"], eps))
+    g = r(silu(b @ f(w["Wg"]).T) * (b @ f(w["Wu"]).T))
+    x2 = r(x1 + g @ f(w["Wd"]).T)
+    return x2, k, v
 
 
 # ---------------------------------------------------------------------------

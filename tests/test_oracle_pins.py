@@ -737,3 +737,68 @@ def test_tree_positions_make_each_branch_a_causal_sequence(tree):
         vs = np.concatenate([vp, vt[0, br]])
         ref = _causal_sdpa(torch.from_numpy(qs), torch.from_numpy(ks), torch.from_numpy(vs)).numpy()[L:]
         assert np.allclose(out[0, br], ref, rtol=1e-10, atol=1e-12)
+
+
+# -------------------------------------------------------- decoder layer
+
+def _llama_layer(d, F, Hq, Hkv, D, eps, theta, w):
+    from transformers import LlamaConfig
+    from transformers.models.llama.modeling_llama import LlamaDecoderLayer, LlamaRotaryEmbedding
+
+    cfg = LlamaConfig(hidden_size=d, intermediate_size=F, num_attention_heads=Hq, num_key_value_heads=Hkv,
+                      head_dim=D, rms_norm_eps=eps, rope_theta=theta, num_hidden_layers=1, vocab_size=16)
+    cfg._attn_implementation = "eager"
+    layer = LlamaDecoderLayer(cfg, layer_idx=0).double().eval()
+    t = lambda a: torch.from_numpy(np.asarray(a, dtype=np.float64))  # noqa: E731
+    with torch.no_grad():
+        layer.input_layernorm.weight.copy_(t(w["g1"]))
+        layer.post_attention_layernorm.weight.copy_(t(w["g2"]))
+        for name, key in (("q_proj", "Wq"), ("k_proj", "Wk"), ("v_proj", "Wv"), ("o_proj", "Wo")):
+            getattr(layer.self_attn, name).weight.copy_(t(w[key]))
+        for name, key in (("gate_proj", "Wg"), ("up_proj", "Wu"), ("down_proj", "Wd")):
+            getattr(layer.mlp, name).weight.copy_(t(w[key]))
+    return cfg, layer, LlamaRotaryEmbedding(cfg)
+
+
+@pytest.mark.parametrize("tree,Hq,Hkv", [([2, 3], 4, 2), ([3, 2, 2], 4, 4)])
+def test_decoder_layer_matches_transformers_llama_layer(tree, Hq, Hkv):
+    """The oracle's decoder layer against transformers' LlamaDecoderLayer in
+    float64, run per sequence with the prefix in its cache, position ids
+    L + depth and an additive mask that opens the prefix and each row's
+    ancestors (its rotary tables and its RMSNorm are float32: positions stay
+    small and the tolerance is 1e-5)."""
+    from transformers import DynamicCache
+
+    rng = np.random.default_rng(70 + len(tree) + Hkv)
+    plan = H.plan_cartesian(tree)
+    N, D, F, eps, theta = plan.n, 8, 48, 1e-6, 10000.0
+    d = Hq * D
+    lens = [5, 11]
+    B = len(lens)
+    w = dict(g1=1 + 0.1 * rng.standard_normal(d), g2=1 + 0.1 * rng.standard_normal(d),
+             Wq=0.2 * rng.standard_normal((Hq * D, d)), Wk=0.2 * rng.standard_normal((Hkv * D, d)),
+             Wv=0.2 * rng.standard_normal((Hkv * D, d)), Wo=0.2 * rng.standard_normal((d, Hq * D)),
+             Wg=0.2 * rng.standard_normal((F, d)), Wu=0.2 * rng.standard_normal((F, d)),
+             Wd=0.2 * rng.standard_normal((d, F)))
+    x = rng.standard_normal((B, N, d))
+    kp = [rng.standard_normal((L, Hkv, D)) for L in lens]
+    vp = [rng.standard_normal((L, Hkv, D)) for L in lens]
+    anc = np.stack([H.ancestors(plan.parent, plan.dmax)] * B)
+    depth = np.stack([plan.depth] * B)
+    got, k_rot, v = H.decoder_layer(x, w, kp, vp, anc, depth, lens, Hq, Hkv, D, eps, theta)
+    cfg, layer, rot = _llama_layer(d, F, Hq, Hkv, D, eps, theta, w)
+    vis = H.tree_mask(plan.parent)  # 0 / -inf over the tree rows
+    for b, L in enumerate(lens):
+        cache = DynamicCache()
+        cache.update(torch.from_numpy(kp[b]).transpose(0, 1)[None], torch.from_numpy(vp[b]).transpose(0, 1)[None], 0)
+        mask = np.concatenate([np.zeros((N, L)), np.where(np.isfinite(vis), 0.0, np.finfo(np.float64).min)], axis=1)
+        hs = torch.from_numpy(x[b])[None]
+        pos_ids = torch.from_numpy(L + plan.depth)[None]
+        with torch.no_grad():
+            out = layer(hs, attention_mask=torch.from_numpy(mask)[None, None], position_ids=pos_ids,
+                        past_key_values=cache, use_cache=True, position_embeddings=rot(hs, pos_ids))
+        out = out[0] if isinstance(out, tuple) else out
+        assert np.allclose(got[b], out[0].numpy(), rtol=1e-5, atol=1e-5)
+        # the cache now holds the layer's rotated tree keys and values after the prefix
+        ck, cv = cache.layers[0].keys[0].transpose(0, 1).numpy(), cache.layers[0].values[0].transpose(0, 1).numpy()
+        assert np.allclose(ck[L:], k_rot[b], rtol=1e-5, atol=1e-5) and np.allclose(cv[L:], v[b], rtol=1e-5, atol=1e-5)

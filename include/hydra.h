@@ -7,7 +7,8 @@
  *   tree_build             final tree (identity or pruned), ancestor table
  *   tree_attention_verify  tree-masked attention over a paged KV prefix
  *                          (tree_rope first rotates the tree Q/K rows at
- *                          positions prefix_len + depth)
+ *                          positions prefix_len + depth; tree_decoder_layer
+ *                          runs a whole target layer over the tree rows)
  *   tree_accept            target vocabulary projection + acceptance walk
  *   tree_commit            kept branch into the paged KV cache, next root and h
  * plus host-side tree-plan builders, workspace-size queries and status strings.
@@ -302,6 +303,50 @@ int tree_attention_verify(int dtype, int B, int N, int Hq, int Hkv, int D,
                           const int32_t* anc, const int32_t* depth, int Dmax,
                           void* out, float* lse, void* ws, size_t ws_bytes,
                           void* stream);
+
+/* ------------------------------------------------------------------------
+ * The target's decoder layer over the tree rows (the verification pass)
+ *
+ * [SD] "Draft, then verify": the target scores every candidate in one
+ * forward pass; [HG] "Tree Attention Matrix with Topology-Aware Causal
+ * Masking": each row sees the prefix and its ancestors. One LLaMA pre-norm
+ * layer (the pages' model family; the layer form is a reading):
+ *   a = rms(x) g1;  [q | k | v] = a Wqkv^T;  q, k rotated at prefix_len + depth
+ *   (as tree_rope);  o = tree-masked attention over this layer's paged prefix
+ *   (as tree_attention_verify, scale 1/sqrt(D));  x1 = x + o Wo^T;
+ *   b = rms(x1) g2;  [gate | up] = b Wgu^T;  x_out = x1 + (silu(gate) * up) Wd^T,
+ * with rms(y) = y / sqrt(mean(y^2) + eps). a, q, k, v, o, x1, b, the gated
+ * product and x_out are stored in dtype; products accumulate in float32.
+ *
+ * x              [B, N, d] (dtype) hidden states of the tree rows
+ * ln1, ln2       [d] (dtype) norm gains
+ * Wqkv           [(Hq + 2 Hkv) D, d] (dtype): Wq rows, then Wk, then Wv
+ * Wo             [d, Hq D] (dtype)
+ * Wgu            [2 F, d] (dtype): gate rows, then up rows
+ * Wd             [d, F] (dtype)
+ * k_pages ...    this layer's paged prefix, block table, lengths (as
+ *                tree_attention_verify)
+ * anc, depth     from tree_build
+ * x_out          out [B, N, d] (dtype), must not alias x
+ * k_tree, v_tree out [B, N, Hkv, D] (dtype): this layer's rotated keys and
+ *                values of the tree rows (tree_commit's inputs for this layer)
+ * Limits: those of tree_attention_verify; bf16 needs d, Hq D and F multiples
+ * of 256. Workspace: tree_decoder_layer_workspace_size.
+ * ---------------------------------------------------------------------- */
+size_t tree_decoder_layer_workspace_size(int dtype, int B, int N, int d, int Hq,
+                                         int Hkv, int D, int F,
+                                         int max_prefix_len);
+
+int tree_decoder_layer(int dtype, int B, int N, int d, int Hq, int Hkv, int D,
+                       int F, const void* x, const void* ln1, const void* Wqkv,
+                       const void* Wo, const void* ln2, const void* Wgu,
+                       const void* Wd, float eps, float theta,
+                       const void* k_pages, const void* v_pages, int n_pages,
+                       int page_size, const int32_t* block_table, int max_pages,
+                       const int32_t* prefix_len, int max_prefix_len,
+                       const int32_t* anc, const int32_t* depth, int Dmax,
+                       void* x_out, void* k_tree, void* v_tree, void* ws,
+                       size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
  * Stage 4: acceptance

@@ -37,6 +37,11 @@ SIGNATURES = {
     "tree_attention_verify": (c_int, [c_int, c_int, c_int, c_int, c_int, c_int, c_float, c_void, c_void,
                                       c_void, c_void, c_void, c_int, c_int, c_void, c_int, c_void, c_int,
                                       c_void, c_void, c_int, c_void, c_void, c_void, c_size, c_void]),
+    "tree_decoder_layer_workspace_size": (c_size, [c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_int]),
+    "tree_decoder_layer": (c_int, [c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_void, c_void, c_void,
+                                   c_void, c_void, c_void, c_void, c_float, c_float, c_void, c_void, c_int, c_int,
+                                   c_void, c_int, c_void, c_int, c_void, c_void, c_int, c_void, c_void, c_void,
+                                   c_void, c_size, c_void]),
     "tree_accept_workspace_size": (c_size, [c_int, c_int, c_int, c_int]),
     "tree_accept": (c_int, [c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_void, c_void, c_float, c_float,
                             c_float, c_void, c_void, c_void, c_void, c_int, c_void, c_void, c_void, c_void, c_void,

@@ -1,0 +1,278 @@
+// One decoder layer of the target over every tree row (the verification pass).
+//
+// "Speculative Decoding", section "Draft, then verify": the target scores
+// all candidates in one forward pass; "Hydra Guide: Sequentially-Dependent
+// Speculative AI", section "Tree Attention Matrix with Topology-Aware Causal
+// Masking": each row sees the prefix and its own ancestors. The layer is the
+// LLaMA pre-norm block of the pages' models (Vicuna, LLaMA-2):
+//   a = rms(x) g1;  q, k, v = a Wq^T, a Wk^T, a Wv^T;  q, k rotated at L + depth;
+//   o = tree attention;  x1 = x + o Wo^T;
+//   b = rms(x1) g2;  x2 = x1 + (silu(b Wg^T) * (b Wu^T)) Wd^T.
+//
+// At decode shapes the rows are few (64 per sequence) and the layer streams
+// its weights once (404 MB at the 7B shape), so every product is the
+// bandwidth-bound projection kernel (one launch for Q, K and V together, one
+// for the gate and up rows together); the elementwise and row-wise steps
+// between them (norms, rotation, SwiGLU, residuals) are small kernels over
+// M x d values. Activations are stored in the layer's dtype at the same
+// points as the reference arithmetic: a, q, k, v (before and after the
+// rotation), o, x1, b, the gated product and x2.
+#include "common.h"
+
+extern "C" size_t tree_attention_verify_workspace_size(int dtype, int B, int N, int Hq, int Hkv, int D,
+                                                       int max_prefix_len);
+extern "C" int tree_attention_verify(int dtype, int B, int N, int Hq, int Hkv, int D, float scale, const void* q,
+                                     const void* k_tree, const void* v_tree, const void* k_pages,
+                                     const void* v_pages, int n_pages, int page_size, const int32_t* block_table,
+                                     int max_pages, const int32_t* prefix_len, int max_prefix_len,
+                                     const int32_t* anc, const int32_t* depth, int Dmax, void* out, float* lse,
+                                     void* ws, size_t ws_bytes, void* stream);
+
+namespace hydra {
+namespace {
+
+template <typename T>
+__device__ __forceinline__ float ld(const T* p, size_t i);
+template <>
+__device__ __forceinline__ float ld<float>(const float* p, size_t i) {
+  return p[i];
+}
+template <>
+__device__ __forceinline__ float ld<bf16_t>(const bf16_t* p, size_t i) {
+  return bf16_to_f32(p[i]);
+}
+template <typename T>
+__device__ __forceinline__ T cv(float v);
+template <>
+__device__ __forceinline__ float cv<float>(float v) {
+  return v;
+}
+template <>
+__device__ __forceinline__ bf16_t cv<bf16_t>(float v) {
+  return f32_to_bf16(v);
+}
+
+// v rounded to T and back
+template <typename T>
+__device__ __forceinline__ float rt(float v);
+template <>
+__device__ __forceinline__ float rt<float>(float v) {
+  return v;
+}
+template <>
+__device__ __forceinline__ float rt<bf16_t>(float v) {
+  return bf16_to_f32(f32_to_bf16(v));
+}
+
+constexpr int kNormThreads = 256;
+
+// One workgroup per row. With add: x1 = T(x + add) is stored first and
+// normalised; without: x itself. out = T(x1 / sqrt(mean(x1^2) + eps) * g).
+template <typename T>
+__global__ __launch_bounds__(kNormThreads) void rmsnorm_rows(int d, float eps, const T* __restrict__ x,
+                                                             const float* __restrict__ add, T* __restrict__ x1,
+                                                             const T* __restrict__ g, T* __restrict__ out) {
+  __shared__ float red[kNormThreads / 64];
+  const size_t row = blockIdx.x;
+  const T* xr = x + row * d;
+  float ss = 0.f;
+  for (int i = threadIdx.x; i < d; i += kNormThreads) {
+    float v = ld<T>(xr, i);
+    if (add) {
+      v = rt<T>(v + add[row * d + i]);
+      x1[row * d + i] = cv<T>(v);
+    }
+    ss += v * v;
+  }
+  ss = wave_sum(ss);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  float tot = 0.f;
+#pragma unroll
+  for (int w = 0; w < kNormThreads / 64; ++w) tot += red[w];
+  const float inv = rsqrtf(tot / d + eps);
+  for (int i = threadIdx.x; i < d; i += kNormThreads) {
+    const float v = add ? ld<T>(x1, row * d + i) : ld<T>(xr, i);
+    out[row * d + i] = cv<T>(v * inv * ld<T>(g, i));
+  }
+}
+
+// Q, K, V out of the fused projection [M][(Hq + 2 Hkv) D] (float32): each
+// value rounded to T, Q and K rotated at prefix_len + depth (float64 angles)
+// and rounded again. One thread per (row, head, pair).
+template <typename T>
+__global__ __launch_bounds__(256) void qkv_rope(long long pairs, int N, int Hq, int Hkv, int D, double log_theta,
+                                                const float* __restrict__ qkv, const int32_t* __restrict__ depth,
+                                                const int32_t* __restrict__ prefix_len, T* __restrict__ q,
+                                                T* __restrict__ k, T* __restrict__ v) {
+  const long long t = static_cast<long long>(blockIdx.x) * 256 + threadIdx.x;
+  if (t >= pairs) return;
+  const int half = D / 2, H = Hq + 2 * Hkv;
+  const int i = static_cast<int>(t % half);
+  const long long rh = t / half;
+  const int h = static_cast<int>(rh % H);
+  const long long m = rh / H;  // row = b * N + u
+  const float* src = qkv + static_cast<size_t>(m) * H * D + static_cast<size_t>(h) * D;
+  const double a = rt<T>(src[i]), b = rt<T>(src[i + half]);
+  if (h >= Hq + Hkv) {  // V: no rotation
+    T* dst = v + (static_cast<size_t>(m) * Hkv + (h - Hq - Hkv)) * D;
+    dst[i] = cv<T>(static_cast<float>(a));
+    dst[i + half] = cv<T>(static_cast<float>(b));
+    return;
+  }
+  const int bseq = static_cast<int>(m / N);
+  const double pos = static_cast<double>(prefix_len[bseq]) + static_cast<double>(depth[m]);
+  double s, c;
+  sincos(pos * exp(-2.0 * i / D * log_theta), &s, &c);
+  T* dst = h < Hq ? q + (static_cast<size_t>(m) * Hq + h) * D : k + (static_cast<size_t>(m) * Hkv + (h - Hq)) * D;
+  dst[i] = cv<T>(static_cast<float>(a * c - b * s));
+  dst[i + half] = cv<T>(static_cast<float>(b * c + a * s));
+}
+
+// g = T(silu(gate) * up) from the fused projection [M][2F] (gate columns first)
+template <typename T>
+__global__ __launch_bounds__(256) void swiglu_rows(long long n, int F, const float* __restrict__ gu,
+                                                   T* __restrict__ g) {
+  const long long t = static_cast<long long>(blockIdx.x) * 256 + threadIdx.x;
+  if (t >= n) return;
+  const long long m = t / F;
+  const int j = static_cast<int>(t % F);
+  const float gate = gu[static_cast<size_t>(m) * 2 * F + j], up = gu[static_cast<size_t>(m) * 2 * F + F + j];
+  g[t] = cv<T>(gate / (1.0f + expf(-gate)) * up);
+}
+
+// out = T(x + add)
+template <typename T>
+__global__ __launch_bounds__(256) void residual_add(long long n, const T* __restrict__ x,
+                                                    const float* __restrict__ add, T* __restrict__ out) {
+  const long long t = static_cast<long long>(blockIdx.x) * 256 + threadIdx.x;
+  if (t < n) out[t] = cv<T>(ld<T>(x, t) + add[t]);
+}
+
+struct LayerWs {
+  size_t a, acc, q, o, x1, g, attn, total;
+};
+
+LayerWs layer_ws(int dtype, int B, int N, int d, int Hq, int Hkv, int D, int F, int max_prefix_len) {
+  LayerWs w{};
+  const size_t M = static_cast<size_t>(B) * N, esz = dtype == HYDRA_F32 ? 4 : 2;
+  const size_t accn = std::max({M * (Hq + 2 * Hkv) * D, M * 2 * F, M * static_cast<size_t>(d)});
+  w.a = align_up(M * d * esz, 256);
+  w.acc = align_up(accn * 4, 256);
+  w.q = align_up(M * Hq * D * esz, 256);
+  w.o = w.q;
+  w.x1 = w.a;
+  w.g = align_up(M * F * esz, 256);
+  w.attn = align_up(tree_attention_verify_workspace_size(dtype, B, N, Hq, Hkv, D, max_prefix_len), 256);
+  w.total = w.a + w.acc + w.q + w.o + w.x1 + w.g + w.attn + 256 * 8;
+  return w;
+}
+
+template <typename T>
+int run_layer(int dtype, int B, int N, int d, int Hq, int Hkv, int D, int F, const T* x, const T* ln1,
+              const T* Wqkv, const T* Wo, const T* ln2, const T* Wgu, const T* Wd, float eps, float theta,
+              const void* k_pages, const void* v_pages, int n_pages, int page_size, const int32_t* block_table,
+              int max_pages, const int32_t* prefix_len, int max_prefix_len, const int32_t* anc,
+              const int32_t* depth, int Dmax, T* x_out, T* k_tree, T* v_tree, void* ws, size_t ws_bytes,
+              hipStream_t stream) {
+  const LayerWs w = layer_ws(dtype, B, N, d, Hq, Hkv, D, F, max_prefix_len);
+  Arena arena(ws, ws_bytes);
+  T* a = arena.take<T>(w.a / sizeof(T));
+  float* acc = arena.take<float>(w.acc / 4);
+  T* q = arena.take<T>(w.q / sizeof(T));
+  T* o = arena.take<T>(w.o / sizeof(T));
+  T* x1 = arena.take<T>(w.x1 / sizeof(T));
+  T* g = arena.take<T>(w.g / sizeof(T));
+  void* attn_ws = arena.take<char>(w.attn);
+  const int M = B * N;
+  auto proj = [&](int K, int Nout, const T* X, const T* W) {
+    XSource xs{};
+    xs.x = X;
+    xs.ldx = K;
+    xs.mode = 0;
+    return launch_projection(dtype, M, K, Nout, xs, W, acc, RowMap{M, 0, 0}, Nout, 1, nullptr,
+                             TopkPartials{nullptr, nullptr}, stream);
+  };
+  auto blocks = [](long long n) { return static_cast<unsigned>((n + 255) / 256); };
+  // a = rms(x) g1
+  rmsnorm_rows<T><<<M, kNormThreads, 0, stream>>>(d, eps, x, nullptr, nullptr, ln1, a);
+  HY_LAUNCH_CHECK("decoder layer: norm 1");
+  // q, k, v (one product), rotated
+  int rc = proj(d, (Hq + 2 * Hkv) * D, a, Wqkv);
+  if (rc != HYDRA_OK) return rc;
+  const long long pairs = static_cast<long long>(M) * (Hq + 2 * Hkv) * (D / 2);
+  qkv_rope<T><<<blocks(pairs), 256, 0, stream>>>(pairs, N, Hq, Hkv, D, log(static_cast<double>(theta)), acc, depth,
+                                                  prefix_len, q, k_tree, v_tree);
+  HY_LAUNCH_CHECK("decoder layer: q/k/v");
+  rc = tree_attention_verify(dtype, B, N, Hq, Hkv, D, 1.0f / sqrtf(static_cast<float>(D)), q, k_tree, v_tree,
+                             k_pages, v_pages, n_pages, page_size, block_table, max_pages, prefix_len,
+                             max_prefix_len, anc, depth, Dmax, o, nullptr, attn_ws, w.attn, stream);
+  if (rc != HYDRA_OK) return rc;
+  // x1 = x + o Wo^T;  b = rms(x1) g2 (into a)
+  rc = proj(Hq * D, d, o, Wo);
+  if (rc != HYDRA_OK) return rc;
+  rmsnorm_rows<T><<<M, kNormThreads, 0, stream>>>(d, eps, x, acc, x1, ln2, a);
+  HY_LAUNCH_CHECK("decoder layer: norm 2");
+  // g = silu(b Wg^T) * (b Wu^T);  x2 = x1 + g Wd^T
+  rc = proj(d, 2 * F, a, Wgu);
+  if (rc != HYDRA_OK) return rc;
+  const long long gn = static_cast<long long>(M) * F;
+  swiglu_rows<T><<<blocks(gn), 256, 0, stream>>>(gn, F, acc, g);
+  HY_LAUNCH_CHECK("decoder layer: swiglu");
+  rc = proj(F, d, g, Wd);
+  if (rc != HYDRA_OK) return rc;
+  const long long xn = static_cast<long long>(M) * d;
+  residual_add<T><<<blocks(xn), 256, 0, stream>>>(xn, x1, acc, x_out);
+  HY_LAUNCH_CHECK("decoder layer: residual");
+  return HYDRA_OK;
+}
+
+}  // namespace
+}  // namespace hydra
+
+extern "C" size_t tree_decoder_layer_workspace_size(int dtype, int B, int N, int d, int Hq, int Hkv, int D, int F,
+                                                    int max_prefix_len) {
+  if (B <= 0 || N <= 0 || d <= 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || F <= 0) return 0;
+  return hydra::layer_ws(dtype, B, N, d, Hq, Hkv, D, F, max_prefix_len).total;
+}
+
+extern "C" int tree_decoder_layer(int dtype, int B, int N, int d, int Hq, int Hkv, int D, int F, const void* x,
+                                  const void* ln1, const void* Wqkv, const void* Wo, const void* ln2,
+                                  const void* Wgu, const void* Wd, float eps, float theta, const void* k_pages,
+                                  const void* v_pages, int n_pages, int page_size, const int32_t* block_table,
+                                  int max_pages, const int32_t* prefix_len, int max_prefix_len, const int32_t* anc,
+                                  const int32_t* depth, int Dmax, void* x_out, void* k_tree, void* v_tree, void* ws,
+                                  size_t ws_bytes, void* stream_) {
+  using namespace hydra;
+  clear_error();
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+  HY_CHECK(dtype == HYDRA_F32 || dtype == HYDRA_BF16, HYDRA_ERR_INVALID, "decoder_layer: bad dtype %d", dtype);
+  HY_CHECK(B >= 0 && N >= 1 && d >= 1 && Hq >= 1 && Hkv >= 1 && D >= 2 && D % 2 == 0 && F >= 1 && Hq % Hkv == 0,
+           HYDRA_ERR_INVALID, "decoder_layer: bad sizes B=%d N=%d d=%d Hq=%d Hkv=%d D=%d F=%d", B, N, d, Hq, Hkv, D,
+           F);
+  HY_CHECK(eps > 0.f && theta > 1.f, HYDRA_ERR_INVALID, "decoder_layer: eps must be > 0 and theta > 1");
+  if (B == 0) return HYDRA_OK;
+  HY_CHECK(x && ln1 && Wqkv && Wo && ln2 && Wgu && Wd && k_pages && v_pages && block_table && prefix_len && anc &&
+               depth && x_out && k_tree && v_tree,
+           HYDRA_ERR_INVALID, "decoder_layer: null pointer");
+  HY_CHECK(x_out != x, HYDRA_ERR_INVALID, "decoder_layer: x_out must not alias x");
+  HY_CHECK(dtype == HYDRA_F32 || (d % 256 == 0 && (Hq * D) % 256 == 0 && F % 256 == 0), HYDRA_ERR_UNSUPPORTED,
+           "decoder_layer: bf16 needs d, Hq*D and F multiples of 256 (d=%d Hq*D=%d F=%d)", d, Hq * D, F);
+  const size_t need = tree_decoder_layer_workspace_size(dtype, B, N, d, Hq, Hkv, D, F, max_prefix_len);
+  HY_CHECK(ws && ws_bytes >= need, HYDRA_ERR_WORKSPACE, "decoder_layer: workspace %zu < %zu", ws_bytes, need);
+  if (dtype == HYDRA_F32)
+    return run_layer<float>(dtype, B, N, d, Hq, Hkv, D, F, static_cast<const float*>(x),
+                            static_cast<const float*>(ln1), static_cast<const float*>(Wqkv),
+                            static_cast<const float*>(Wo), static_cast<const float*>(ln2),
+                            static_cast<const float*>(Wgu), static_cast<const float*>(Wd), eps, theta, k_pages,
+                            v_pages, n_pages, page_size, block_table, max_pages, prefix_len, max_prefix_len, anc,
+                            depth, Dmax, static_cast<float*>(x_out), static_cast<float*>(k_tree),
+                            static_cast<float*>(v_tree), ws, ws_bytes, stream);
+  return run_layer<bf16_t>(dtype, B, N, d, Hq, Hkv, D, F, static_cast<const bf16_t*>(x),
+                           static_cast<const bf16_t*>(ln1), static_cast<const bf16_t*>(Wqkv),
+                           static_cast<const bf16_t*>(Wo), static_cast<const bf16_t*>(ln2),
+                           static_cast<const bf16_t*>(Wgu), static_cast<const bf16_t*>(Wd), eps, theta, k_pages,
+                           v_pages, n_pages, page_size, block_table, max_pages, prefix_len, max_prefix_len, anc,
+                           depth, Dmax, static_cast<bf16_t*>(x_out), static_cast<bf16_t*>(k_tree),
+                           static_cast<bf16_t*>(v_tree), ws, ws_bytes, stream);
+}

@@ -306,6 +306,42 @@ def tree_attention_verify(q, k_tree, v_tree, k_pages, v_pages, block_table, pref
     return _check("tree_attention_verify", rc)
 
 
+def tree_decoder_layer_workspace_size(dtype_code, B, N, d, Hq, Hkv, D, F, max_prefix_len):
+    return int(lib().tree_decoder_layer_workspace_size(dtype_code, B, N, d, Hq, Hkv, D, F, max_prefix_len))
+
+
+def tree_decoder_layer(x, w, Hq, Hkv, k_pages, v_pages, block_table, prefix_len, max_prefix_len, anc, depth,
+                       x_out, k_tree, v_tree, ws, eps=1e-6, theta=10000.0, stream=None):
+    """The target's decoder layer over the tree rows (see include/hydra.h).
+    x [B, N, d]; w: dict of ln1 [d], Wqkv [(Hq + 2 Hkv) D, d], Wo [d, Hq D],
+    ln2 [d], Wgu [2F, d], Wd [d, F]; pages [n_pages, Hkv, page, D]."""
+    B, N, d = x.shape
+    D = k_tree.shape[3]
+    F = w["Wd"].shape[1]
+    n_pages, _, page_size, _ = k_pages.shape
+    shapes = {"Wqkv": ((Hq + 2 * Hkv) * D, d), "Wo": (d, Hq * D), "ln1": (d,), "ln2": (d,), "Wgu": (2 * F, d),
+              "Wd": (d, F)}
+    for name, shape in shapes.items():
+        if tuple(w[name].shape) != shape:
+            raise ValueError(f"tree_decoder_layer: {name} has shape {tuple(w[name].shape)}, expected {shape}")
+    for name, t, shape in (("x_out", x_out, (B, N, d)), ("k_tree", k_tree, (B, N, Hkv, D)),
+                           ("v_tree", v_tree, (B, N, Hkv, D)), ("anc", anc, (B, N, anc.shape[2])),
+                           ("depth", depth, (B, N)), ("prefix_len", prefix_len, (B,))):
+        if tuple(t.shape) != shape:
+            raise ValueError(f"tree_decoder_layer: {name} has shape {tuple(t.shape)}, expected {shape}")
+    dt = x.dtype
+    wsp, wsb = _ws(ws)
+    rc = lib().tree_decoder_layer(
+        _dtype_code(x), B, N, d, Hq, Hkv, D, F, _dev(x, "x"), _dev(w["ln1"], "ln1", dt), _dev(w["Wqkv"], "Wqkv", dt),
+        _dev(w["Wo"], "Wo", dt), _dev(w["ln2"], "ln2", dt), _dev(w["Wgu"], "Wgu", dt), _dev(w["Wd"], "Wd", dt),
+        float(eps), float(theta), _dev(k_pages, "k_pages", dt), _dev(v_pages, "v_pages", dt), n_pages, page_size,
+        _dev(block_table, "block_table", torch.int32), block_table.shape[1],
+        _dev(prefix_len, "prefix_len", torch.int32), int(max_prefix_len), _dev(anc, "anc", torch.int32),
+        _dev(depth, "depth", torch.int32), anc.shape[2] - 1, _dev(x_out, "x_out", dt), _dev(k_tree, "k_tree", dt),
+        _dev(v_tree, "v_tree", dt), wsp, wsb, _stream(stream))
+    return _check("tree_decoder_layer", rc)
+
+
 def tree_accept_workspace_size(mode, B, N, V):
     return int(lib().tree_accept_workspace_size(mode, B, N, V))
 

@@ -36,7 +36,8 @@ def _bf16(x):
 @pytest.mark.parametrize("M,K,N", [(1, 256, 1000), (5, 512, 640), (16, 4096, 4096), (17, 256, 2000),
                                    (33, 1024, 777), (64, 4096, 32000), (100, 512, 1000), (256, 256, 512),
                                    (300, 256, 130), (13, 8192, 4096), (0, 256, 64), (1024, 1024, 3000),
-                                   (420, 2048, 1111), (65, 1024, 3001), (200, 2048, 4100)])
+                                   (420, 2048, 1111), (65, 1024, 3001), (200, 2048, 4100), (64, 11008, 4096),
+                                   (13, 11008, 1000), (18, 768, 640), (64, 4096, 22016)])
 def test_projection_bf16(M, K, N):
     from speculative_decoding_hydra_amd import hydra_vocab_projection
 
@@ -733,3 +734,79 @@ def test_tree_rope(dtype, B, N, H, D, lens, inplace):
     else:
         step = np.ldexp(1.0, np.frexp(np.maximum(np.abs(ref), 1e-30))[1] - 8)
         assert np.all(np.abs(got - ref) <= step), float(np.max(np.abs(got - ref) / step))
+
+
+# ------------------------------------------------ the target's decoder layer
+
+def _layer_weights(g, d, Hq, Hkv, D, F, dt):
+    n = lambda *s: (torch.randn(*s, generator=g) * 0.02).to(dt)  # noqa: E731
+    return dict(ln1=(1 + 0.1 * torch.randn(d, generator=g)).to(dt), Wqkv=n((Hq + 2 * Hkv) * D, d), Wo=n(d, Hq * D),
+                ln2=(1 + 0.1 * torch.randn(d, generator=g)).to(dt), Wgu=n(2 * F, d), Wd=n(d, F))
+
+
+def _oracle_weights(w, Hq, Hkv, D, F):
+    f = HI.as_f64
+    wqkv, wgu = f(w["Wqkv"]), f(w["Wgu"])
+    return dict(g1=f(w["ln1"]), g2=f(w["ln2"]), Wq=wqkv[: Hq * D], Wk=wqkv[Hq * D:(Hq + Hkv) * D],
+                Wv=wqkv[(Hq + Hkv) * D:], Wo=f(w["Wo"]), Wg=wgu[:F], Wu=wgu[F:], Wd=f(w["Wd"]))
+
+
+def _close(got, ref, dtype, what, stream=False):
+    """float32: 1e-4. bfloat16: 2e-2 plus two rounding steps of the value's
+    scale; for the residual stream (stream=True) the scale is at least the
+    row's RMS, since x_out is the rounded sum of two rounded operands of that
+    size and keeps their rounding errors where they cancel to a small value."""
+    if dtype == "fp32":
+        e = float(np.max(np.abs(got - ref)))
+        assert e <= 1e-4, f"{what}: max-abs {e:.3g}"
+        return
+    scale = np.abs(ref)
+    if stream:
+        scale = np.maximum(scale, np.sqrt(np.mean(ref * ref, axis=-1, keepdims=True)))
+    step = np.ldexp(1.0, np.frexp(np.maximum(scale, 1e-30))[1] - 8)
+    bad = np.abs(got - ref) > 2e-2 + 2 * step
+    assert not bad.any(), f"{what}: {int(bad.sum())} values off, worst {float(np.max(np.abs(got - ref))):.3g}"
+
+
+@pytest.mark.parametrize("dtype,B,tree,d,Hq,Hkv,D,F,lens,layers", [
+    ("fp32", 2, ("cartesian", [2, 3]), 256, 8, 2, 32, 512, [5, 40], 2),
+    ("bf16", 2, ("cartesian", [2, 3]), 256, 8, 2, 32, 512, [5, 40], 2),
+    ("bf16", 3, ("cartesian", [3, 2, 2]), 512, 4, 4, 128, 1024, [0, 17, 300], 1),
+    ("bf16", 1, ("sparse", (10, 4, 2, 1), 64), 4096, 32, 32, 128, 11008, [2048], 1),
+])
+def test_tree_decoder_layer(dtype, B, tree, d, Hq, Hkv, D, F, lens, layers):
+    """Decoder layers over the tree rows (each with its own weights and paged
+    prefix, the second reading the first's output) against the oracle's;
+    also the rotated keys and values each layer hands to the commit."""
+    from speculative_decoding_hydra_amd import tree_decoder_layer, tree_decoder_layer_workspace_size
+
+    print(f"decoder layer {dtype} B={B} tree={tree} d={d} Hq={Hq} Hkv={Hkv} D={D} F={F} L={lens} x{layers}",
+          flush=True)
+    plan = T.oracle_plan(tree)[0]
+    N = plan.n
+    g = torch.Generator().manual_seed(d + N + B)
+    dt = torch.float32 if dtype == "fp32" else torch.bfloat16
+    anc = np.stack([O.ancestors(plan.parent, plan.dmax)] * B).astype(np.int32)
+    depth = np.stack([plan.depth] * B).astype(np.int32)
+    x = torch.randn(B, N, d, generator=g).to(dt)
+    dev = lambda t: (torch.from_numpy(t) if isinstance(t, np.ndarray) else t).cuda().contiguous()  # noqa: E731
+    xs_dev, xs_ref = dev(x), HI.as_f64(x)
+    for layer in range(layers):
+        w = _layer_weights(g, d, Hq, Hkv, D, F, dt)
+        c = _attn_case(B, N, Hq, Hkv, D, lens, dtype, seed=100 * layer + d, tree=plan.parent)
+        out = torch.empty(B, N, d, dtype=dt, device="cuda")
+        kt = torch.empty(B, N, Hkv, D, dtype=dt, device="cuda")
+        vt = torch.empty_like(kt)
+        code = 0 if dtype == "fp32" else 1
+        ws = torch.empty(tree_decoder_layer_workspace_size(code, B, N, d, Hq, Hkv, D, F, max(lens)),
+                         dtype=torch.uint8, device="cuda")
+        tree_decoder_layer(xs_dev, {k: dev(v) for k, v in w.items()}, Hq, Hkv, dev(c["kpool"]), dev(c["vpool"]),
+                           dev(c["bt"]), dev(c["lens"]), max(lens), dev(anc), dev(depth), out, kt, vt, ws)
+        torch.cuda.synchronize()
+        ref, rk, rv = O.decoder_layer(xs_ref, _oracle_weights(w, Hq, Hkv, D, F), [HI.as_f64(t) for t in c["kp"]],
+                                      [HI.as_f64(t) for t in c["vp"]], anc, depth, lens, Hq, Hkv, D, 1e-6,
+                                      bf16=dtype == "bf16")
+        _close(kt.cpu().double().numpy(), rk, dtype, f"layer {layer} keys")
+        _close(vt.cpu().double().numpy(), rv, dtype, f"layer {layer} values")
+        _close(out.cpu().double().numpy(), ref, dtype, f"layer {layer} output", stream=True)
+        xs_dev, xs_ref = out, ref  # each side's next layer reads its own output

@@ -18,6 +18,8 @@ The JSON line also carries
                 that streams a [V, d] bf16 matrix): algorithmic bytes per
                 launch / average launch duration from HIP events on its stream,
                 against the 8 TB/s HBM peak;
+  decoder_layer one target decoder layer over every tree row at the workload's
+                shape (tree_decoder_layer; bytes, time, HBM fraction);
   commit_32_layers  the commit kernel moving each sequence's deepest kept
                 branch across 32 layers of caches (bytes, time, HBM fraction);
   cpu_baseline  the CPU oracle timed on this host on one full round of the
@@ -156,6 +158,67 @@ def commit_measure(w, rnd, dev, stream, layers=32, reps=20, use_graph=True):
     esz = kt.element_size()
     nbytes = layers * rows * w.Hkv * w.D * esz * 2 * 2 + B * hidden.shape[2] * esz * 2
     return {"layers": layers, "rows_per_layer": rows, "bytes": nbytes, "avg_launch_us": us,
+            "achieved_GBps": nbytes / (us * 1e-6) / 1e9, "frac_of_hbm_peak": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS}
+
+
+FFN_DIM = {4096: 11008, 8192: 28672}  # the LLaMA-family feed-forward widths of the two model shapes
+
+
+def layer_measure(w, rnd, dev, stream, reps=10, use_graph=True):
+    """One target decoder layer over every tree row of the round
+    (tree_decoder_layer) at the workload's shape, cycling two weight sets so
+    the last-level cache cannot serve repeats; random weights, the round's
+    paged prefix, tree and positions."""
+    import torch
+
+    from speculative_decoding_hydra_amd import tree_decoder_layer, tree_decoder_layer_workspace_size
+
+    B, K = rnd.attn_out.shape[:2]
+    d, Hq, Hkv, D = w.d, w.Hq, w.Hkv, w.D
+    F = FFN_DIM.get(d, 4 * d)
+    dt = rnd.dtype
+    g = torch.Generator(device="cuda").manual_seed(7)
+    n = lambda *s: (torch.randn(*s, device="cuda", generator=g) * 0.02).to(dt)  # noqa: E731
+    ones = torch.ones(d, device="cuda", dtype=dt)
+    sets = [dict(ln1=ones, Wqkv=n((Hq + 2 * Hkv) * D, d), Wo=n(d, Hq * D), ln2=ones, Wgu=n(2 * F, d), Wd=n(d, F))
+            for _ in range(2)]
+    x = torch.randn(B, K, d, device="cuda", generator=g).to(dt)
+    out = torch.empty_like(x)
+    kt = torch.empty(B, K, Hkv, D, device="cuda", dtype=dt)
+    vt = torch.empty_like(kt)
+    mpl = int(rnd.shape["max_prefix_len"])
+    code = 0 if dt == torch.float32 else 1
+    ws = torch.empty(tree_decoder_layer_workspace_size(code, B, K, d, Hq, Hkv, D, F, mpl), dtype=torch.uint8,
+                     device="cuda")
+    launch = lambda i: tree_decoder_layer(x, sets[i % 2], Hq, Hkv, dev["k_pages"], dev["v_pages"],  # noqa: E731
+                                          dev["block_table"], dev["prefix_len"], mpl, rnd.anc, rnd.depth, out, kt,
+                                          vt, ws)
+    launch(0)
+    launch(1)
+    torch.cuda.synchronize()
+    gr = None
+    if use_graph:
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            for i in range(reps):
+                launch(i)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record(stream)
+    if gr is not None:
+        gr.replay()
+    else:
+        for i in range(reps):
+            launch(i)
+    b.record(stream)
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) / reps * 1e3
+    esz = x.element_size()
+    weights = ((Hq + 2 * Hkv) * D * d + d * Hq * D + 3 * F * d) * esz
+    prefix = int(dev["prefix_len"].sum()) * Hkv * D * esz * 2
+    acts = B * K * (2 * d + 2 * Hkv * D) * esz
+    nbytes = weights + prefix + acts
+    return {"d": d, "ffn": F, "rows": B * K, "bytes": nbytes, "weight_bytes": weights, "avg_launch_us": us,
             "achieved_GBps": nbytes / (us * 1e-6) / 1e9, "frac_of_hbm_peak": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS}
 
 
@@ -374,6 +437,7 @@ def main():
     achieved = alg_bytes / (k_ms * 1e-3) / 1e9
 
     commit = commit_measure(w, rnd, dev, stream, use_graph=not args.no_graph)
+    layer = layer_measure(w, rnd, dev, stream, use_graph=not args.no_graph)
     rbytes = round_bytes(w, rnd, inp["prefix_len"])
     cpu = None
     if not args.no_cpu:
@@ -409,6 +473,7 @@ def main():
         "stages_ms": {"draft": stage_ms[0], "build": stage_ms[1], "attention": stage_ms[2],
                       "accept": stage_ms[3], "commit": stage_ms[4]},
         "commit_32_layers": commit,
+        "decoder_layer": layer,
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)

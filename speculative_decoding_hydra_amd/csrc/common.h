@@ -283,6 +283,17 @@ bool gemm_supported(int K);
 int launch_projection_gemm(int M, int K, int N, const bf16_t* X, int ldx, const bf16_t* W, int ldw, float* Y,
                            RowMap map, int ldy, TopkPartials tp, hipStream_t stream);
 constexpr int kGemmMinRows = 65;  // from here on the tiled kernel beats the streaming one
+// Split K for products with few output tiles: workgroups (blockIdx.y = s)
+// take K range [s kper, min((s + 1) kper, K)) and write part + s * M * N
+// (row-major [M][N]); kper % 64 == 0. The caller sums the nsplit partials.
+int launch_projection_gemm_split(int M, int K, int N, const bf16_t* X, const bf16_t* W, float* part, int nsplit,
+                                 int kper, hipStream_t stream);
+int gemm_workgroups(int M, int N);
+// Y or its split-K partials for the decoder layer's products: picks the
+// kernel by M and a split of K that gives the chip enough workgroups; writes
+// nsplit partials part[s][M][N] (float32) and returns nsplit (>= 1).
+int launch_projection_parts(int dtype, int M, int K, int N, const void* X, const void* W, float* part,
+                            size_t part_floats, int* nsplit, hipStream_t stream);
 
 // Finish the fused row reduction: log-sum-exp and sorted top-k of each row,
 // then either the candidate-tree fill (draft heads) or the arg max. The top-k

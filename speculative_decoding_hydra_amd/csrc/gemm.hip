@@ -33,6 +33,8 @@ constexpr int GTHREADS = 512;
 
 struct GemmArgs {
   int M, K, N, ldx, ldw, ldy, mtiles, ntiles;
+  int kper;         // split K: workgroups with blockIdx.y = s take K range [s kper, (s + 1) kper)
+  size_t ystride;   // ... and write Y + s * ystride
   const bf16_t* X;
   const bf16_t* W;
   float* Y;
@@ -90,6 +92,8 @@ __global__ __launch_bounds__(GTHREADS, 2) void proj_gemm_kernel(GemmArgs a) {
   const int n0 = ntile * BN, m0 = mtile * GBM;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if (a.tp.clear && bx == 0 && tid < a.tp.nclear) a.tp.clear[tid] = 0;
+  const int kb = static_cast<int>(blockIdx.y) * a.kper;
+  const int klen = a.K - kb < a.kper ? a.K - kb : a.kper;
   const int wn = wave & 1, wm = wave >> 1;  // 2 x 4 waves: WN n x 64 m each
 
   // global -> register staging: WLD vectors of 16 bytes of W and 4 of X per thread
@@ -101,11 +105,11 @@ __global__ __launch_bounds__(GTHREADS, 2) void proj_gemm_kernel(GemmArgs a) {
     const int idx = tid + j * GTHREADS;
     const int r = idx >> 3, c = (idx & 7) * 8;
     const int m = m0 + r < a.M ? m0 + r : 0;
-    xsrc[j] = a.X + static_cast<size_t>(m) * a.ldx + c;
+    xsrc[j] = a.X + static_cast<size_t>(m) * a.ldx + kb + c;
     xoff[j] = swz(r, idx & 7);
     if (j < WLD) {
       const int n = n0 + r < a.N ? n0 + r : a.N - 1;  // rows past the end re-read the last row
-      wsrc[j] = a.W + static_cast<size_t>(n) * a.ldw + c;
+      wsrc[j] = a.W + static_cast<size_t>(n) * a.ldw + kb + c;
       woff[j] = xoff[j];
     }
   }
@@ -131,7 +135,7 @@ __global__ __launch_bounds__(GTHREADS, 2) void proj_gemm_kernel(GemmArgs a) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  const int nk = a.K / GBK;
+  const int nk = klen / GBK;
   load(0);
   store(0);
   if (nk > 1) load(GBK);
@@ -166,7 +170,7 @@ __global__ __launch_bounds__(GTHREADS, 2) void proj_gemm_kernel(GemmArgs a) {
   for (int j = 0; j < 4; ++j) {
     const int m = m0 + wm * 64 + j * 16 + (lane & 15);
     const bool mok = m < a.M;
-    float* dst = a.Y + static_cast<size_t>(a.map(mok ? m : 0)) * a.ldy;
+    float* dst = a.Y + blockIdx.y * a.ystride + static_cast<size_t>(a.map(mok ? m : 0)) * a.ldy;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int n = nb + i * 16;
@@ -238,11 +242,45 @@ int launch_projection_gemm(int M, int K, int N, const bf16_t* X, int ldx, const 
   a.Y = Y;
   a.map = map;
   a.tp = tp;
+  a.kper = K;
+  a.ystride = 0;
   const int slots = (a.ntiles + 7) / 8 * a.mtiles;  // per XCD
   if (bn == 128) proj_gemm_kernel<128><<<slots * 8, GTHREADS, 0, stream>>>(a);
   else proj_gemm_kernel<256><<<slots * 8, GTHREADS, 0, stream>>>(a);
   HY_LAUNCH_CHECK("projection(gemm)");
   return HYDRA_OK;
+}
+
+int launch_projection_gemm_split(int M, int K, int N, const bf16_t* X, const bf16_t* W, float* part, int nsplit,
+                                 int kper, hipStream_t stream) {
+  GemmArgs a{};
+  a.M = M;
+  a.K = K;
+  a.N = N;
+  a.ldx = K;
+  a.ldw = K;
+  a.ldy = N;
+  a.mtiles = (M + GBM - 1) / GBM;
+  const int bn = a.mtiles == 1 ? 128 : 256;
+  a.ntiles = (N + bn - 1) / bn;
+  a.X = X;
+  a.W = W;
+  a.Y = part;
+  a.map = RowMap{M, 0, 0};
+  a.tp = TopkPartials{nullptr, nullptr};
+  a.kper = kper;
+  a.ystride = static_cast<size_t>(M) * N;
+  const int slots = (a.ntiles + 7) / 8 * a.mtiles;
+  const dim3 grid(slots * 8, nsplit);
+  if (bn == 128) proj_gemm_kernel<128><<<grid, GTHREADS, 0, stream>>>(a);
+  else proj_gemm_kernel<256><<<grid, GTHREADS, 0, stream>>>(a);
+  HY_LAUNCH_CHECK("projection(gemm, split K)");
+  return HYDRA_OK;
+}
+
+int gemm_workgroups(int M, int N) {
+  const int mt = (M + GBM - 1) / GBM, bn = mt == 1 ? 128 : 256;
+  return mt * ((N + bn - 1) / bn);
 }
 
 }  // namespace hydra

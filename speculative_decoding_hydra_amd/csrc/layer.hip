@@ -64,14 +64,33 @@ __device__ __forceinline__ float rt<bf16_t>(float v) {
   return bf16_to_f32(f32_to_bf16(v));
 }
 
+// sum of the ns split-K partials of element i (stride floats apart)
+__device__ __forceinline__ float psum(const float* __restrict__ p, int ns, size_t stride, size_t i) {
+  float v = p[i];
+  for (int s = 1; s < ns; ++s) v += p[s * stride + i];
+  return v;
+}
+__device__ __forceinline__ float4 psum4(const float* __restrict__ p, int ns, size_t stride, size_t i) {
+  float4 v = *reinterpret_cast<const float4*>(p + i);
+  for (int s = 1; s < ns; ++s) {
+    const float4 t = *reinterpret_cast<const float4*>(p + s * stride + i);
+    v.x += t.x;
+    v.y += t.y;
+    v.z += t.z;
+    v.w += t.w;
+  }
+  return v;
+}
+
 constexpr int kNormThreads = 256;
 
 // One workgroup per row. With add: x1 = T(x + add) is stored first and
 // normalised; without: x itself. out = T(x1 / sqrt(mean(x1^2) + eps) * g).
 template <typename T>
 __global__ __launch_bounds__(kNormThreads) void rmsnorm_rows(int d, float eps, const T* __restrict__ x,
-                                                             const float* __restrict__ add, T* __restrict__ x1,
-                                                             const T* __restrict__ g, T* __restrict__ out) {
+                                                             const float* __restrict__ add, int ns, size_t stride,
+                                                             T* __restrict__ x1, const T* __restrict__ g,
+                                                             T* __restrict__ out) {
   __shared__ float red[kNormThreads / 64];
   const size_t row = blockIdx.x;
   const T* xr = x + row * d;
@@ -79,7 +98,7 @@ __global__ __launch_bounds__(kNormThreads) void rmsnorm_rows(int d, float eps, c
   for (int i = threadIdx.x; i < d; i += kNormThreads) {
     float v = ld<T>(xr, i);
     if (add) {
-      v = rt<T>(v + add[row * d + i]);
+      v = rt<T>(v + psum(add, ns, stride, row * d + i));
       x1[row * d + i] = cv<T>(v);
     }
     ss += v * v;
@@ -97,12 +116,90 @@ __global__ __launch_bounds__(kNormThreads) void rmsnorm_rows(int d, float eps, c
   }
 }
 
+// bf16 rows with d % 8 == 0 and d <= 8 * kNormThreads * VPT: every thread
+// keeps its (up to VPT) 8-value chunks in registers between the two passes,
+// with 16-byte loads and stores; same arithmetic as rmsnorm_rows
+template <int VPT>
+__global__ __launch_bounds__(kNormThreads) void rmsnorm_rows_bf16(int d, float eps, const bf16_t* __restrict__ x,
+                                                                  const float* __restrict__ add, int ns,
+                                                                  size_t stride, bf16_t* __restrict__ x1,
+                                                                  const bf16_t* __restrict__ g,
+                                                                  bf16_t* __restrict__ out) {
+  __shared__ float red[kNormThreads / 64];
+  const size_t row = blockIdx.x;
+  const int nch = d / 8;
+  float v[VPT][8];
+  float ss = 0.f;
+#pragma unroll
+  for (int j = 0; j < VPT; ++j) {
+    const int c = threadIdx.x + j * kNormThreads;
+    if (c >= nch) continue;
+    const u32x4_t raw = *reinterpret_cast<const u32x4_t*>(x + row * d + c * 8);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[j][2 * e] = bf16_to_f32(static_cast<bf16_t>(raw[e] & 0xffffu));
+      v[j][2 * e + 1] = bf16_to_f32(static_cast<bf16_t>(raw[e] >> 16));
+    }
+    if (add) {
+      const float4 a0 = psum4(add, ns, stride, row * d + c * 8);
+      const float4 a1 = psum4(add, ns, stride, row * d + c * 8 + 4);
+      const float av[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+      u32x4_t packed;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[j][e] = rt<bf16_t>(v[j][e] + av[e]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        packed[e] = static_cast<uint32_t>(f32_to_bf16(v[j][2 * e])) |
+                    (static_cast<uint32_t>(f32_to_bf16(v[j][2 * e + 1])) << 16);
+      *reinterpret_cast<u32x4_t*>(x1 + row * d + c * 8) = packed;
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ss += v[j][e] * v[j][e];
+  }
+  ss = wave_sum(ss);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  float tot = 0.f;
+#pragma unroll
+  for (int w = 0; w < kNormThreads / 64; ++w) tot += red[w];
+  const float inv = rsqrtf(tot / d + eps);
+#pragma unroll
+  for (int j = 0; j < VPT; ++j) {
+    const int c = threadIdx.x + j * kNormThreads;
+    if (c >= nch) continue;
+    const u32x4_t graw = *reinterpret_cast<const u32x4_t*>(g + c * 8);
+    u32x4_t packed;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float g0 = bf16_to_f32(static_cast<bf16_t>(graw[e] & 0xffffu));
+      const float g1 = bf16_to_f32(static_cast<bf16_t>(graw[e] >> 16));
+      packed[e] = static_cast<uint32_t>(f32_to_bf16(v[j][2 * e] * inv * g0)) |
+                  (static_cast<uint32_t>(f32_to_bf16(v[j][2 * e + 1] * inv * g1)) << 16);
+    }
+    *reinterpret_cast<u32x4_t*>(out + row * d + c * 8) = packed;
+  }
+}
+
+template <typename T>
+void launch_norm(int M, int d, float eps, const T* x, const float* add, int ns, T* x1, const T* g, T* out,
+                 hipStream_t stream) {
+  const size_t stride = static_cast<size_t>(M) * d;
+  if constexpr (std::is_same<T, bf16_t>::value) {
+    if (d % 8 == 0 && d <= 8 * kNormThreads * 4) {
+      rmsnorm_rows_bf16<4><<<M, kNormThreads, 0, stream>>>(d, eps, x, add, ns, stride, x1, g, out);
+      return;
+    }
+  }
+  rmsnorm_rows<T><<<M, kNormThreads, 0, stream>>>(d, eps, x, add, ns, stride, x1, g, out);
+}
+
 // Q, K, V out of the fused projection [M][(Hq + 2 Hkv) D] (float32): each
 // value rounded to T, Q and K rotated at prefix_len + depth (float64 angles)
 // and rounded again. One thread per (row, head, pair).
 template <typename T>
 __global__ __launch_bounds__(256) void qkv_rope(long long pairs, int N, int Hq, int Hkv, int D, double log_theta,
-                                                const float* __restrict__ qkv, const int32_t* __restrict__ depth,
+                                                const float* __restrict__ qkv, int ns, size_t stride,
+                                                const int32_t* __restrict__ depth,
                                                 const int32_t* __restrict__ prefix_len, T* __restrict__ q,
                                                 T* __restrict__ k, T* __restrict__ v) {
   const long long t = static_cast<long long>(blockIdx.x) * 256 + threadIdx.x;
@@ -112,8 +209,8 @@ __global__ __launch_bounds__(256) void qkv_rope(long long pairs, int N, int Hq, 
   const long long rh = t / half;
   const int h = static_cast<int>(rh % H);
   const long long m = rh / H;  // row = b * N + u
-  const float* src = qkv + static_cast<size_t>(m) * H * D + static_cast<size_t>(h) * D;
-  const double a = rt<T>(src[i]), b = rt<T>(src[i + half]);
+  const size_t src = static_cast<size_t>(m) * H * D + static_cast<size_t>(h) * D;
+  const double a = rt<T>(psum(qkv, ns, stride, src + i)), b = rt<T>(psum(qkv, ns, stride, src + i + half));
   if (h >= Hq + Hkv) {  // V: no rotation
     T* dst = v + (static_cast<size_t>(m) * Hkv + (h - Hq - Hkv)) * D;
     dst[i] = cv<T>(static_cast<float>(a));
@@ -131,22 +228,24 @@ __global__ __launch_bounds__(256) void qkv_rope(long long pairs, int N, int Hq, 
 
 // g = T(silu(gate) * up) from the fused projection [M][2F] (gate columns first)
 template <typename T>
-__global__ __launch_bounds__(256) void swiglu_rows(long long n, int F, const float* __restrict__ gu,
-                                                   T* __restrict__ g) {
+__global__ __launch_bounds__(256) void swiglu_rows(long long n, int F, const float* __restrict__ gu, int ns,
+                                                   size_t stride, T* __restrict__ g) {
   const long long t = static_cast<long long>(blockIdx.x) * 256 + threadIdx.x;
   if (t >= n) return;
   const long long m = t / F;
   const int j = static_cast<int>(t % F);
-  const float gate = gu[static_cast<size_t>(m) * 2 * F + j], up = gu[static_cast<size_t>(m) * 2 * F + F + j];
+  const float gate = psum(gu, ns, stride, static_cast<size_t>(m) * 2 * F + j);
+  const float up = psum(gu, ns, stride, static_cast<size_t>(m) * 2 * F + F + j);
   g[t] = cv<T>(gate / (1.0f + expf(-gate)) * up);
 }
 
 // out = T(x + add)
 template <typename T>
 __global__ __launch_bounds__(256) void residual_add(long long n, const T* __restrict__ x,
-                                                    const float* __restrict__ add, T* __restrict__ out) {
+                                                    const float* __restrict__ add, int ns,
+                                                    T* __restrict__ out) {
   const long long t = static_cast<long long>(blockIdx.x) * 256 + threadIdx.x;
-  if (t < n) out[t] = cv<T>(ld<T>(x, t) + add[t]);
+  if (t < n) out[t] = cv<T>(ld<T>(x, t) + psum(add, ns, static_cast<size_t>(n), t));
 }
 
 struct LayerWs {
@@ -156,7 +255,8 @@ struct LayerWs {
 LayerWs layer_ws(int dtype, int B, int N, int d, int Hq, int Hkv, int D, int F, int max_prefix_len) {
   LayerWs w{};
   const size_t M = static_cast<size_t>(B) * N, esz = dtype == HYDRA_F32 ? 4 : 2;
-  const size_t accn = std::max({M * (Hq + 2 * Hkv) * D, M * 2 * F, M * static_cast<size_t>(d)});
+  // split-K partials: up to 8 for the d-wide products (few output tiles)
+  const size_t accn = std::max({M * (Hq + 2 * Hkv) * D * 2, M * 2 * F * 2, 8 * M * static_cast<size_t>(d)});
   w.a = align_up(M * d * esz, 256);
   w.acc = align_up(accn * 4, 256);
   w.q = align_up(M * Hq * D * esz, 256);
@@ -185,24 +285,21 @@ int run_layer(int dtype, int B, int N, int d, int Hq, int Hkv, int D, int F, con
   T* g = arena.take<T>(w.g / sizeof(T));
   void* attn_ws = arena.take<char>(w.attn);
   const int M = B * N;
+  int ns = 1;  // split-K partials of the last product
   auto proj = [&](int K, int Nout, const T* X, const T* W) {
-    XSource xs{};
-    xs.x = X;
-    xs.ldx = K;
-    xs.mode = 0;
-    return launch_projection(dtype, M, K, Nout, xs, W, acc, RowMap{M, 0, 0}, Nout, 1, nullptr,
-                             TopkPartials{nullptr, nullptr}, stream);
+    return launch_projection_parts(dtype, M, K, Nout, X, W, acc, w.acc / 4, &ns, stream);
   };
   auto blocks = [](long long n) { return static_cast<unsigned>((n + 255) / 256); };
   // a = rms(x) g1
-  rmsnorm_rows<T><<<M, kNormThreads, 0, stream>>>(d, eps, x, nullptr, nullptr, ln1, a);
+  launch_norm<T>(M, d, eps, x, nullptr, 1, nullptr, ln1, a, stream);
   HY_LAUNCH_CHECK("decoder layer: norm 1");
   // q, k, v (one product), rotated
   int rc = proj(d, (Hq + 2 * Hkv) * D, a, Wqkv);
   if (rc != HYDRA_OK) return rc;
   const long long pairs = static_cast<long long>(M) * (Hq + 2 * Hkv) * (D / 2);
-  qkv_rope<T><<<blocks(pairs), 256, 0, stream>>>(pairs, N, Hq, Hkv, D, log(static_cast<double>(theta)), acc, depth,
-                                                  prefix_len, q, k_tree, v_tree);
+  qkv_rope<T><<<blocks(pairs), 256, 0, stream>>>(pairs, N, Hq, Hkv, D, log(static_cast<double>(theta)), acc, ns,
+                                                  static_cast<size_t>(M) * (Hq + 2 * Hkv) * D, depth, prefix_len, q,
+                                                  k_tree, v_tree);
   HY_LAUNCH_CHECK("decoder layer: q/k/v");
   rc = tree_attention_verify(dtype, B, N, Hq, Hkv, D, 1.0f / sqrtf(static_cast<float>(D)), q, k_tree, v_tree,
                              k_pages, v_pages, n_pages, page_size, block_table, max_pages, prefix_len,
@@ -211,18 +308,18 @@ int run_layer(int dtype, int B, int N, int d, int Hq, int Hkv, int D, int F, con
   // x1 = x + o Wo^T;  b = rms(x1) g2 (into a)
   rc = proj(Hq * D, d, o, Wo);
   if (rc != HYDRA_OK) return rc;
-  rmsnorm_rows<T><<<M, kNormThreads, 0, stream>>>(d, eps, x, acc, x1, ln2, a);
+  launch_norm<T>(M, d, eps, x, acc, ns, x1, ln2, a, stream);
   HY_LAUNCH_CHECK("decoder layer: norm 2");
   // g = silu(b Wg^T) * (b Wu^T);  x2 = x1 + g Wd^T
   rc = proj(d, 2 * F, a, Wgu);
   if (rc != HYDRA_OK) return rc;
   const long long gn = static_cast<long long>(M) * F;
-  swiglu_rows<T><<<blocks(gn), 256, 0, stream>>>(gn, F, acc, g);
+  swiglu_rows<T><<<blocks(gn), 256, 0, stream>>>(gn, F, acc, ns, static_cast<size_t>(M) * 2 * F, g);
   HY_LAUNCH_CHECK("decoder layer: swiglu");
   rc = proj(F, d, g, Wd);
   if (rc != HYDRA_OK) return rc;
   const long long xn = static_cast<long long>(M) * d;
-  residual_add<T><<<blocks(xn), 256, 0, stream>>>(xn, x1, acc, x_out);
+  residual_add<T><<<blocks(xn), 256, 0, stream>>>(xn, x1, acc, ns, x_out);
   HY_LAUNCH_CHECK("decoder layer: residual");
   return HYDRA_OK;
 }

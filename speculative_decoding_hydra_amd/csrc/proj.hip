@@ -34,7 +34,9 @@ struct ProjArgs {
   TopkPartials tp;
 };
 
-template <int MT, int KC, int PF, int WV, bool SPLIT, bool TOPK>
+// REM: the K range need not be a multiple of PF * KC (a multiple of KC is
+// enough); the chunks past its end are skipped and their loads clamped
+template <int MT, int KC, int PF, int WV, bool SPLIT, bool TOPK, bool REM = false>
 __global__ __launch_bounds__(64 * WV) void proj_bf16_kernel(ProjArgs a) {
   constexpr int NT = 64 * WV;      // threads
   constexpr int RPW = 16 * WV;     // rows of W per workgroup (one 16-row tile per wave)
@@ -55,7 +57,7 @@ __global__ __launch_bounds__(64 * WV) void proj_bf16_kernel(ProjArgs a) {
   const int wave = tid >> 6;
   const int n_base = blockIdx.x * RPW + wave * 16;
   const int k_begin = blockIdx.y * a.kper;
-  const int k_end = k_begin + a.kper;
+  const int k_end = REM && k_begin + a.kper > a.K ? a.K : k_begin + a.kper;  // REM: the last split may be short
   const int K0 = xs.mode == 0 ? K : xs.d;
   if (TOPK && a.tp.clear && blockIdx.x == 0 && blockIdx.y == 0 && tid < a.tp.nclear) a.tp.clear[tid] = 0;
 
@@ -95,12 +97,14 @@ __global__ __launch_bounds__(64 * WV) void proj_bf16_kernel(ProjArgs a) {
   }
 
   // prologue: PF chunks of W in flight, the first X chunk in registers
-  // (the launcher guarantees PF * KC divides the K range of the workgroup)
+  // (the launcher guarantees PF * KC divides the K range of the workgroup,
+  // or REM)
 #pragma unroll
-  for (int p = 0; p < PF; ++p)
+  for (int p = 0; p < PF; ++p) {
+    const int kp = REM && k_begin + p * KC > k_end - KC ? k_end - KC : k_begin + p * KC;
 #pragma unroll
-    for (int s = 0; s < STEPS; ++s)
-      wbuf[p][s] = *reinterpret_cast<const u32x4_t*>(wp + k_begin + p * KC + s * 32);
+    for (int s = 0; s < STEPS; ++s) wbuf[p][s] = *reinterpret_cast<const u32x4_t*>(wp + kp + s * 32);
+  }
 #pragma unroll
   for (int v = 0; v < XV; ++v)
     xbuf[v] = *reinterpret_cast<const u32x4_t*>((k_begin < K0 ? xp0[v] : xp1[v]) + k_begin);
@@ -110,6 +114,7 @@ __global__ __launch_bounds__(64 * WV) void proj_bf16_kernel(ProjArgs a) {
 #pragma unroll
     for (int p = 0; p < PF; ++p) {
       const int kc = kc0 + p * KC;
+      if (REM && kc >= k_end) continue;  // uniform over the workgroup
       __syncthreads();
 #pragma unroll
       for (int v = 0; v < XV; ++v) *reinterpret_cast<u32x4_t*>(&xlds[xo[v]]) = xbuf[v];
@@ -265,20 +270,20 @@ __global__ __launch_bounds__(64) void logits_partials(int M, int N, const float*
   }
 }
 
-template <int MT, int PF, bool TOPK>
+template <int MT, int PF, bool TOPK, bool REM = false>
 void launch_bf16_pf(const ProjArgs& a, int nsplit, hipStream_t stream) {
   constexpr int KC = MT <= 4 ? 256 : (MT <= 8 ? 128 : 64);
   // split-K launches (partials) and direct launches are separate instances;
   // with 4+ row tiles, 8-wave workgroups share each staged X chunk twice as far
   if (a.part) {
     dim3 grid((a.N + 63) / 64, nsplit);
-    proj_bf16_kernel<MT, KC, PF, 4, true, false><<<grid, 256, 0, stream>>>(a);
+    proj_bf16_kernel<MT, KC, PF, 4, true, false, REM><<<grid, 256, 0, stream>>>(a);
   } else if constexpr (MT >= 4) {
     dim3 grid((a.N + 127) / 128, 1);
-    proj_bf16_kernel<MT, KC, PF, 8, false, TOPK><<<grid, 512, 0, stream>>>(a);
+    proj_bf16_kernel<MT, KC, PF, 8, false, TOPK, REM><<<grid, 512, 0, stream>>>(a);
   } else {
     dim3 grid((a.N + 63) / 64, 1);
-    proj_bf16_kernel<MT, KC, PF, 4, false, TOPK><<<grid, 256, 0, stream>>>(a);
+    proj_bf16_kernel<MT, KC, PF, 4, false, TOPK, REM><<<grid, 256, 0, stream>>>(a);
   }
 }
 
@@ -286,8 +291,13 @@ template <int MT, bool TOPK>
 int launch_bf16(const ProjArgs& a, int nsplit, hipStream_t stream) {
   constexpr int KC = MT <= 4 ? 256 : (MT <= 8 ? 128 : 64);
   constexpr int PF = MT <= 4 ? 2 : (MT <= 8 ? 4 : 8);
-  if (a.kper % (PF * KC) == 0) {
+  const bool ragged = a.K % a.kper != 0;  // split K with a shorter last range
+  if (!ragged && a.kper % (PF * KC) == 0) {
     launch_bf16_pf<MT, PF, TOPK>(a, nsplit, stream);
+  } else if (a.kper > PF * KC) {
+    launch_bf16_pf<MT, PF, TOPK, true>(a, nsplit, stream);  // e.g. K = 11008: 43 chunks of 256
+  } else if (ragged) {
+    launch_bf16_pf<MT, 1, TOPK, true>(a, nsplit, stream);
   } else {
     launch_bf16_pf<MT, 1, TOPK>(a, nsplit, stream);  // K range of 256 .. PF*KC-256
   }
@@ -341,6 +351,50 @@ int launch_projection(int dtype, int M, int K, int N, XSource xs, const void* W,
     a.m_base = m0;
     const int rc =
         tp.keys ? launch_bf16_mt<true>(mc, a, nsplit, stream) : launch_bf16_mt<false>(mc, a, nsplit, stream);
+    if (rc != HYDRA_OK) return rc;
+  }
+  return HYDRA_OK;
+}
+
+int launch_projection_parts(int dtype, int M, int K, int N, const void* X, const void* W, float* part,
+                            size_t part_floats, int* nsplit, hipStream_t stream) {
+  *nsplit = 1;
+  XSource xs{};
+  xs.x = X;
+  xs.ldx = K;
+  xs.mode = 0;
+  if (M <= 0 || N <= 0) return HYDRA_OK;
+  const size_t mn = static_cast<size_t>(M) * N;
+  const int cap = static_cast<int>(std::min<size_t>(16, std::max<size_t>(1, part_floats / mn)));
+  if (dtype == HYDRA_F32 || K % 256 != 0)
+    return launch_projection(dtype, M, K, N, xs, W, part, RowMap{M, 0, 0}, N, 1, nullptr,
+                             TopkPartials{nullptr, nullptr}, stream);
+  if (M >= kGemmMinRows && gemm_supported(K)) {
+    // about one workgroup per CU, each K range at least 512 long
+    const int wg = gemm_workgroups(M, N);
+    int ns = std::max(1, std::min({cap, 8, (256 + wg - 1) / wg, K / 512}));
+    const int kper = (K / 64 + ns - 1) / ns * 64;
+    ns = (K + kper - 1) / kper;
+    *nsplit = ns;
+    return launch_projection_gemm_split(M, K, N, static_cast<const bf16_t*>(X), static_cast<const bf16_t*>(W), part,
+                                        ns, kper, stream);
+  }
+  // streaming kernel: 64 output columns per workgroup and split; about 512
+  // workgroups, each K range a multiple of 256
+  const int wg = (N + 63) / 64 * ((M + 255) / 256);
+  int ns = std::max(1, std::min({cap, 16, (512 + wg - 1) / wg, K / 256}));
+  const int kper = (K / 256 + ns - 1) / ns * 256;
+  ns = (K + kper - 1) / kper;
+  *nsplit = ns;
+  if (ns == 1)
+    return launch_projection(dtype, M, K, N, xs, W, part, RowMap{M, 0, 0}, N, 1, nullptr,
+                             TopkPartials{nullptr, nullptr}, stream);
+  ProjArgs a{M, K, N, xs, static_cast<const bf16_t*>(W), nullptr, RowMap{M, 0, 0}, N, kper, 0, part,
+             TopkPartials{nullptr, nullptr}};
+  for (int m0 = 0; m0 < M; m0 += 256) {
+    const int mc = M - m0 < 256 ? M - m0 : 256;
+    a.m_base = m0;
+    const int rc = launch_bf16_mt<false>(mc, a, ns, stream);
     if (rc != HYDRA_OK) return rc;
   }
   return HYDRA_OK;

@@ -35,6 +35,8 @@ Readings of points the pages leave open (each is listed in the design doc):
   ``n_nodes - 1`` plus the root.
 * Positions: tree row u of sequence b stands at L_b + depth(u); rotary
   embedding in the LLaMA half-split layout with base theta (10000).
+* Two-layer heads of the [HG] sketch: head 1 LayerNorm(SiLU(Wa h + ba)), later
+  heads LayerNorm(Wb SiLU(Wa [h || e(parent)] + ba) + bb), LayerNorm eps 1e-5.
 * Decoder layer of the verify pass: the LLaMA pre-norm layer (RMSNorm,
   rotated Q/K, tree attention, output projection, residual, RMSNorm, SwiGLU
   feed-forward, residual) over every tree row at once.
@@ -69,7 +71,7 @@ __all__ = [
     "tree_mask", "tree_attention", "target_logits", "argmax_lowest",
     "greedy_accept", "residual", "sample_inverse_cdf", "rejection_accept",
     "commit_path", "entropy", "typical_passes", "kept_branch", "typical_accept",
-    "tree_positions", "rope", "rms_norm", "decoder_layer",
+    "tree_positions", "rope", "rms_norm", "decoder_layer", "layer_norm", "sketch_hidden",
 ]
 
 
@@ -269,6 +271,31 @@ def head_hidden(h, e, W1, b1, residual=True, bf16=False):
     return round_bf16(u) if bf16 else u
 
 
+def layer_norm(x, g, b, eps=1e-5):
+    """(x - mean) / sqrt(var + eps) * g + b over the last axis (biased var)."""
+    x = np.asarray(x, dtype=np.float64)
+    mu = np.mean(x, axis=-1, keepdims=True)
+    var = np.mean((x - mu) ** 2, axis=-1, keepdims=True)
+    return (x - mu) / np.sqrt(var + eps) * np.asarray(g, dtype=np.float64) + np.asarray(b, dtype=np.float64)
+
+
+def sketch_hidden(h, e, head, bf16=False):
+    """Hidden state of one row of the two-layer head of the [HG] sketch
+    ("Python code block" of the implementation section: HydraHeadLayer and
+    HydraDraftEngine). Head 1 reads h alone: LayerNorm(SiLU(Wa h + ba)).
+    Later heads read [h || e(parent)]: LayerNorm(Wb SiLU(Wa [h || e] + ba) + bb),
+    Wa [H, 2d] (H = 1024 in the sketch), Wb [d, H]; every Linear has a bias
+    and the LayerNorm a gain and a bias. With bf16 the two stored tensors (the
+    SiLU output and u) are rounded."""
+    r = round_bf16 if bf16 else (lambda t: t)
+    f = lambda t: np.asarray(t, dtype=np.float64)  # noqa: E731
+    x = f(h) if e is None else np.concatenate([f(h), f(e)])
+    a = r(silu(f(head["Wa"]) @ x + f(head["ba"])))
+    if "Wb" in head:
+        a = f(head["Wb"]) @ a + f(head["bb"])
+    return r(layer_norm(a, head["ln_g"], head["ln_b"]))
+
+
 def head_logits(u, W2):
     """Vocabulary projection of a head, z = W2 u (W2 has no bias)."""
     return np.asarray(W2, dtype=np.float64) @ np.asarray(u, dtype=np.float64)
@@ -279,9 +306,10 @@ def draft_heads(h, root_tok, E, heads, plan: TreePlan, hydra=True,
     """All draft heads of one round, filling the candidate tree.
 
     h [B, d], root_tok [B], E [V, d] (Hydra only), heads = list of (W1, b1, W2)
-    with head k at index k-1. Node c at depth k takes entry rank[c] of the
-    top-k list of the row that expanded its parent; its cumulative score adds
-    that token's log-softmax to the parent's.
+    with head k at index k-1, or of dicts for the sketch's two-layer heads
+    (Wa, ba, [Wb, bb,] ln_g, ln_b, W2; see sketch_hidden). Node c at depth k
+    takes entry rank[c] of the top-k list of the row that expanded its parent;
+    its cumulative score adds that token's log-softmax to the parent's.
 
     ``forced_tok`` [B, N] (stage-wise checking): when given, conditioning
     tokens and cumulative scores follow these tokens instead of the oracle's
@@ -292,7 +320,7 @@ def draft_heads(h, root_tok, E, heads, plan: TreePlan, hydra=True,
     row_node, row_depth, node_row = head_rows(plan, hydra)
     R = len(row_node)
     d = h.shape[1]
-    V = heads[0][2].shape[0]
+    V = (heads[0]["W2"] if isinstance(heads[0], dict) else heads[0][2]).shape[0]
     tok = -np.ones((B, N), dtype=np.int64)
     logp = np.zeros((B, N), dtype=np.float64)
     u_all = np.zeros((B, R, d))
@@ -307,7 +335,11 @@ def draft_heads(h, root_tok, E, heads, plan: TreePlan, hydra=True,
         tok[b, 0] = root_tok[b]
         follow = tok if forced_tok is None else np.asarray(forced_tok)
         for k in range(1, plan.dmax + 1):
-            W1, b1, W2 = heads[k - 1]
+            sketch = isinstance(heads[k - 1], dict)
+            if sketch:
+                W2 = heads[k - 1]["W2"]
+            else:
+                W1, b1, W2 = heads[k - 1]
             for r in np.flatnonzero(row_depth == k):
                 if hydra:
                     p = row_node[r]
@@ -315,7 +347,10 @@ def draft_heads(h, root_tok, E, heads, plan: TreePlan, hydra=True,
                     e = np.asarray(E[ptok], dtype=np.float64)
                 else:
                     e = None
-                u = head_hidden(h[b], e, W1, b1, residual, bf16)
+                if sketch:
+                    u = sketch_hidden(h[b], e if k > 1 else None, heads[k - 1], bf16)
+                else:
+                    u = head_hidden(h[b], e, W1, b1, residual, bf16)
                 z = head_logits(u, W2)
                 lse = logsumexp(z)
                 u_all[b, r], z_all[b, r], lse_all[b, r] = u, z, lse

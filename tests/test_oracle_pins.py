@@ -123,6 +123,105 @@ def test_head_bf16_rounds_hidden_state():
     assert np.array_equal(u, ref)
 
 
+def _sketch_modules(d, V, n_heads, hidden, seed):
+    """Heads built as torch modules after the two-layer sketch: head 1 is
+    Linear(d, d), SiLU, LayerNorm(d), Linear(d, V); later heads fuse
+    [h || e(parent)] with Linear(2d, hidden), SiLU, Linear(hidden, d),
+    LayerNorm(d) and project with Linear(d, V). Returns the modules and the
+    same weights as the oracle's dicts."""
+    torch.manual_seed(seed)
+    mods, dicts = [], []
+    for k in range(1, n_heads + 1):
+        if k == 1:
+            lin_a, ln = torch.nn.Linear(d, d), torch.nn.LayerNorm(d)
+            body = torch.nn.Sequential(lin_a, torch.nn.SiLU(), ln)
+            w = {}
+        else:
+            lin_a, lin_b, ln = torch.nn.Linear(2 * d, hidden), torch.nn.Linear(hidden, d), torch.nn.LayerNorm(d)
+            body = torch.nn.Sequential(lin_a, torch.nn.SiLU(), lin_b, ln)
+            w = {"Wb": lin_b.weight, "bb": lin_b.bias}
+        with torch.no_grad():  # the default LayerNorm is the identity affine map
+            ln.weight.uniform_(0.5, 1.5)
+            ln.bias.uniform_(-0.5, 0.5)
+        head = torch.nn.Linear(d, V, bias=False)
+        body, head = body.double(), head.double()
+        mods.append((body, head))
+        w.update(Wa=lin_a.weight, ba=lin_a.bias, ln_g=ln.weight, ln_b=ln.bias, W2=head.weight)
+        dicts.append({n: t.detach().double().numpy().copy() for n, t in w.items()})
+    return mods, dicts
+
+
+def test_layer_norm_matches_torch():
+    rng = np.random.default_rng(11)
+    x, g, b = rng.standard_normal((3, 40)) * 4 + 2, rng.standard_normal(40), rng.standard_normal(40)
+    ref = torch.nn.functional.layer_norm(torch.from_numpy(x), (40,), torch.from_numpy(g), torch.from_numpy(b), 1e-5)
+    assert np.allclose(H.layer_norm(x, g, b), ref.numpy(), rtol=1e-12, atol=1e-12)
+    # a constant row has no spread: only the bias survives
+    assert np.allclose(H.layer_norm(np.full(8, 3.0), np.ones(8), np.arange(8.0)), np.arange(8.0))
+
+
+def test_sketch_heads_match_torch_modules():
+    rng = np.random.default_rng(12)
+    d, V, hidden = 24, 61, 40
+    mods, dicts = _sketch_modules(d, V, 3, hidden, seed=3)
+    h, e = rng.standard_normal(d), rng.standard_normal(d)
+    for k, ((body, head), w) in enumerate(zip(mods, dicts), start=1):
+        x = torch.from_numpy(h if k == 1 else np.concatenate([h, e]))
+        ref = head(body(x)).detach().numpy()
+        got = H.head_logits(H.sketch_hidden(h, None if k == 1 else e, w), w["W2"])
+        assert np.allclose(got, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_sketch_tree_matches_brute_force_expansion():
+    # Expand every candidate as the sketch describes, head by head: softmax of
+    # the head's logits, its top-k tokens, cumulative probability as the
+    # product along the branch. The oracle's tree must hold the same branches
+    # with the same probabilities (exp of its cumulative log-softmax).
+    rng = np.random.default_rng(13)
+    d, V, hidden, branching = 16, 50, 32, [3, 2, 2]
+    mods, dicts = _sketch_modules(d, V, 3, hidden, seed=4)
+    E = rng.standard_normal((V, d))
+    h = rng.standard_normal((1, d))
+    ht = torch.from_numpy(h[0])
+    want = {}
+    frontier = [((), 1.0)]
+    for k, ((body, head), kk) in enumerate(zip(mods, branching), start=1):
+        nxt = []
+        for path, prob in frontier:
+            x = ht if k == 1 else torch.cat([ht, torch.from_numpy(E[path[-1]])])
+            p = torch.softmax(head(body(x)), dim=-1).detach().numpy()
+            for t in np.argsort(-p, kind="stable")[:kk]:
+                nxt.append((path + (int(t),), prob * p[t]))
+        want.update(nxt)
+        frontier = nxt
+    plan = H.plan_cartesian(branching)
+    res = H.draft_heads(h, [0], E, dicts, plan, hydra=True)
+    got = {}
+    for c in range(1, plan.n):
+        path, u = [], c
+        while u:
+            path.append(int(res["tok"][0, u]))
+            u = plan.parent[u]
+        got[tuple(reversed(path))] = math.exp(res["logp"][0, c])
+    assert got.keys() == want.keys()
+    for key in want:
+        assert got[key] == pytest.approx(want[key], rel=1e-10)
+
+
+def test_sketch_bf16_rounds_both_stored_tensors():
+    rng = np.random.default_rng(14)
+    d, hidden = 16, 24
+    w = {"Wa": rng.standard_normal((hidden, 2 * d)), "ba": rng.standard_normal(hidden),
+         "Wb": rng.standard_normal((d, hidden)), "bb": rng.standard_normal(d),
+         "ln_g": rng.standard_normal(d), "ln_b": rng.standard_normal(d)}
+    h, e = rng.standard_normal(d), rng.standard_normal(d)
+    bf = lambda t: torch.from_numpy(t).float().to(torch.bfloat16).double().numpy()  # noqa: E731
+    a = bf(H.silu(w["Wa"] @ np.concatenate([h, e]) + w["ba"]))
+    ref = bf(H.layer_norm(w["Wb"] @ a + w["bb"], w["ln_g"], w["ln_b"]))
+    assert np.array_equal(H.sketch_hidden(h, e, w, bf16=True), ref)
+    assert not np.array_equal(H.sketch_hidden(h, e, w, bf16=False), ref)
+
+
 # -------------------------------------------------------------------- trees
 
 def test_cartesian_counts(golden):

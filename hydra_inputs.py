@@ -23,6 +23,9 @@ in this fixed order:
   9. tree Q [B, N, Hq, D], tree K [B, N, Hkv, D], tree V ~ N(0, 1)
  10. uniforms u_acc [B, N], u_res [B, N] in [0, 1)  (stochastic and typical
      modes)
+ 11. two-layer heads only, per head k: Wa [d, d] (k = 1) or [H, 2d], ba, then
+     (k > 1) Wb [d, H], bb, all ~ N(0, 0.02); LayerNorm gain 1 + N(0, 0.1) and
+     bias N(0, 0.1) [d]; W2 [V, d] ~ N(0, 0.02)  (H = head_hidden, 1024)
 
 Draws are float32; bfloat16 workloads round them to bfloat16 (round to
 nearest even, torch's conversion).
@@ -58,6 +61,8 @@ class Workload:
     delta: float = 0.3
     scattered: bool = False
     zero_init: bool = False
+    head: str = "mlp"     # "mlp" (one SiLU layer) | "sketch" (two-layer LayerNorm heads)
+    head_hidden: int = 1024
     extra: dict = field(default_factory=dict)
 
     @property
@@ -98,6 +103,10 @@ WORKLOADS = {
     "7b_batched16": Workload("7b_batched16", 3, B=16, tree=_SPARSE, L=(512, 4096),
                              scattered=True, **_7B),
     # 70B-shaped GQA layer, stochastic acceptance at temperature 0.7
+    # the two-layer LayerNorm heads of the Hydra guide's sketch (hidden 1024)
+    "tiny_sketch": Workload("tiny_sketch", 5, "fp32", 1, 256, 1000, 3, True, ("cartesian", (2, 3)),
+                            8, 8, 32, (128,), head="sketch"),
+    "7b_sketch": Workload("7b_sketch", 6, B=1, tree=_SPARSE, L=(2048,), head="sketch", **_7B),
     "70b_gqa": Workload("70b_gqa", 4, "bf16", 4, 8192, 32000, 4, True, _SPARSE,
                         64, 8, 128, (16384,), mode="stochastic", T=0.7),
 }
@@ -184,6 +193,22 @@ def generate(w: Workload, n_tree: int | None = None, reserve: int | None = None)
     if w.mode in ("stochastic", "typical"):
         out["u_acc"] = torch.rand((w.B, N), generator=g, dtype=torch.float32)
         out["u_res"] = torch.rand((w.B, N), generator=g, dtype=torch.float32)
+    if w.head == "sketch":
+        # drawn last so the other inputs of a seed do not move; LayerNorm gain
+        # near 1 and bias near 0 (not exactly, so both take part)
+        heads = []
+        for k in range(1, w.n_heads + 1):
+            width = w.d if k == 1 else w.head_hidden
+            hd = {"Wa": _normal(g, (width, w.d if k == 1 else 2 * w.d), 0.02, dt),
+                  "ba": _normal(g, (width,), 0.02, dt)}
+            if k > 1:
+                hd["Wb"] = _normal(g, (w.d, w.head_hidden), 0.02, dt)
+                hd["bb"] = _normal(g, (w.d,), 0.02, dt)
+            hd["ln_g"] = (1.0 + _normal(g, (w.d,), 0.1, torch.float32)).to(dt)
+            hd["ln_b"] = _normal(g, (w.d,), 0.1, dt)
+            hd["W2"] = _normal(g, (w.V, w.d), 0.02, dt)
+            heads.append(hd)
+        out["heads"] = heads
     return out
 
 

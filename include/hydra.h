@@ -4,6 +4,8 @@
  *
  * A round has four stages, one entry point each:
  *   hydra_draft_heads      draft heads + per-head top-k, filling the candidate tree
+ *                          (hydra_draft_heads_sketch: the same with two-layer
+ *                          LayerNorm heads)
  *   tree_build             final tree (identity or pruned), ancestor table
  *   tree_attention_verify  tree-masked attention over a paged KV prefix
  *                          (tree_rope first rotates the tree Q/K rows at
@@ -170,6 +172,43 @@ int hydra_draft_heads(int dtype, int B, int d, int V, int hydra, int residual,
                       const int32_t* k_per_depth, float* head_logits, float* head_lse,
                       void* head_hidden, int32_t* cand_tok, float* cand_logp,
                       void* ws, size_t ws_bytes, void* stream);
+
+/* Stage 1 with the two-layer heads of [HG] "End-to-End Implementation" (its
+ * HydraHeadLayer and HydraDraftEngine modules). Same tree expansion, outputs
+ * and plan arguments as hydra_draft_heads (Hydra mode); only u differs:
+ *   head 1:   u = LN_1(T(SiLU(Wa_1 h_b + ba_1)))
+ *   head k>1: a = T(SiLU(Wa_k [h_b || E[token of row_node[r]]] + ba_k))
+ *             u = LN_k(Wb_k a + bb_k)
+ *   LN_k(x) = (x - mean) / sqrt(var + ln_eps) * ln_g_k + ln_b_k over the d
+ *   values of a row (biased variance); T() rounds to dtype (the identity for
+ *   float32); u is stored in dtype.
+ * then z = W2_k u and everything after it as in hydra_draft_heads.
+ *
+ * hidden_dim   H, the width of a (1024 in the source)
+ * Wa, ba       host arrays of n_heads device pointers: Wa_1 [d, d], ba_1 [d];
+ *              Wa_k [H, 2d], ba_k [H] for k > 1
+ * Wb, bb       host arrays of n_heads device pointers: Wb_k [d, H], bb_k [d]
+ *              for k > 1 (entry 0 is not read and may be NULL)
+ * ln_g, ln_b   host arrays of n_heads device pointers, [d] each
+ * W2           host array of n_heads device pointers, W2_k [V, d]
+ * ln_eps       LayerNorm epsilon (> 0; 1e-5 in the source)
+ * Plan arguments as in hydra_draft_heads; head 1 must have one row (R's first
+ * row, the root). Supported: d, H <= 8192; bf16 needs d % 256 == 0 and
+ * H % 256 == 0. Errors as in hydra_draft_heads. */
+size_t hydra_draft_heads_sketch_workspace_size(int dtype, int B, int d, int V, int hidden_dim,
+                                               int Dmax, const int32_t* row_first);
+
+int hydra_draft_heads_sketch(int dtype, int B, int d, int V, int hidden_dim, const void* h,
+                             const int32_t* root_tok, const void* emb, int n_heads,
+                             const void* const* Wa, const void* const* ba, const void* const* Wb,
+                             const void* const* bb, const void* const* ln_g, const void* const* ln_b,
+                             const void* const* W2, float ln_eps, int N, int Dmax,
+                             const int32_t* node_parent, const int32_t* node_rank,
+                             const int32_t* node_row, int R, const int32_t* row_node,
+                             const int32_t* row_first, const int32_t* depth_first,
+                             const int32_t* k_per_depth, float* head_logits, float* head_lse,
+                             void* head_hidden, int32_t* cand_tok, float* cand_logp,
+                             void* ws, size_t ws_bytes, void* stream);
 
 /* Folded embedding table of one Hydra head, computed once per weight set:
  * out[t, n] = sum_j W1[n, d + j] * emb[t, j] for every token t, with W1 the

@@ -211,6 +211,44 @@ def hydra_draft_heads(h, root_tok, emb, W1, b1, W2, dplan: DevicePlan, head_logi
     return _check("hydra_draft_heads", rc)
 
 
+def hydra_draft_heads_sketch_workspace_size(dtype_code, B, d, V, hidden_dim, dplan: DevicePlan):
+    rf, rfp = _host_i32(dplan.rows.row_first)
+    return int(lib().hydra_draft_heads_sketch_workspace_size(dtype_code, B, d, V, hidden_dim, dplan.dmax, rfp))
+
+
+def hydra_draft_heads_sketch(h, root_tok, emb, heads, dplan: DevicePlan, head_logits, head_lse, cand_tok,
+                             cand_logp, ws, head_hidden=None, ln_eps=1e-5, stream=None):
+    """Stage 1 with two-layer LayerNorm heads (see include/hydra.h). heads: one
+    dict per head (head k at k-1) with Wa, ba, ln_g, ln_b, W2 and, for k > 1,
+    Wb, bb."""
+    if not dplan.hydra:
+        raise ValueError("two-layer heads read [h || e(parent)]: the plan must be a Hydra plan")
+    dt = _dtype_code(h)
+    B, d = h.shape
+    n_heads = len(heads)
+    V = heads[0]["W2"].shape[0]
+    hidden_dim = heads[1]["Wa"].shape[0] if n_heads > 1 else d
+    arr = C.c_void_p * n_heads
+
+    def col(name, first=True):
+        return arr(*[_dev(w[name], name, h.dtype) if (first or k > 0) else None for k, w in enumerate(heads)])
+
+    rows = dplan.rows
+    rf, rfp = _host_i32(rows.row_first)
+    df, dfp = _host_i32(rows.depth_first)
+    kp, kpp = _host_i32(rows.k_per_depth)
+    wsp, wsb = _ws(ws)
+    rc = lib().hydra_draft_heads_sketch(
+        dt, B, d, V, hidden_dim, _dev(h, "h"), _dev(root_tok, "root_tok", torch.int32), _dev(emb, "emb", h.dtype),
+        n_heads, col("Wa"), col("ba"), col("Wb", False), col("bb", False), col("ln_g"), col("ln_b"), col("W2"),
+        float(ln_eps), dplan.N, dplan.dmax, _dev(dplan.parent, "parent"), _dev(dplan.rank, "rank"),
+        _dev(dplan.node_row, "node_row"), dplan.R, _dev(dplan.row_node, "row_node"), rfp, dfp, kpp,
+        _dev(head_logits, "head_logits", torch.float32), _dev(head_lse, "head_lse", torch.float32),
+        _dev(head_hidden, "head_hidden", h.dtype), _dev(cand_tok, "cand_tok", torch.int32),
+        _dev(cand_logp, "cand_logp", torch.float32), wsp, wsb, _stream(stream))
+    return _check("hydra_draft_heads_sketch", rc)
+
+
 def hydra_fold_embedding(emb, W1, out, stream=None):
     """out[t, n] = sum_j W1[n, d + j] * emb[t, j] (see include/hydra.h):
     emb [V, d] and W1 [d, 2d] bf16, out [V, d] float32."""

@@ -30,7 +30,9 @@ def make_plan(tree):
 class HydraRound:
     """Buffers and calls for one round of B sequences.
 
-    weights: dict with emb [V, d] (Hydra), W1/b1/W2 lists, W_t [V, d].
+    weights: dict with emb [V, d] (Hydra), W1/b1/W2 lists, W_t [V, d]; or,
+    for the two-layer LayerNorm heads (hydra_draft_heads_sketch), ``heads``:
+    one dict per head (Wa, ba, [Wb, bb,] ln_g, ln_b, W2) instead of W1/b1/W2.
     shape: dict with B, d, V, Hq, Hkv, D, max_prefix_len.
     fold_embedding: build the folded embedding tables of the Hydra heads
     (hydra_fold_embedding, V * d * 4 bytes per head) once here and let the
@@ -78,13 +80,18 @@ class HydraRound:
         self.next_root_tok = z(B, dtype=i32)
         self.next_h = z(B, Hq * D, dtype=dt)
         nb = lambda n: torch.empty(max(int(n), 1), dtype=torch.uint8, device=device)  # noqa: E731
-        self.ws_draft = nb(H.hydra_draft_heads_workspace_size(code, B, d, V, hydra, self.dplan))
+        self.sketch = weights.get("heads") is not None
+        if self.sketch:
+            hid = weights["heads"][1]["Wa"].shape[0] if len(weights["heads"]) > 1 else d
+            self.ws_draft = nb(H.hydra_draft_heads_sketch_workspace_size(code, B, d, V, hid, self.dplan))
+        else:
+            self.ws_draft = nb(H.hydra_draft_heads_workspace_size(code, B, d, V, hydra, self.dplan))
         self.ws_build = nb(H.tree_build_workspace_size(B, N, K))
         self.ws_attn = nb(H.tree_attention_verify_workspace_size(code, B, K, Hq, Hkv, D,
                                                                  shape["max_prefix_len"]))
         self.ws_accept = nb(H.tree_accept_workspace_size(self.mode, B, K, V))
         if fold_embedding is None:
-            fold_embedding = hydra and dt == torch.bfloat16
+            fold_embedding = hydra and dt == torch.bfloat16 and not self.sketch
         self.emb_proj = None
         if fold_embedding:
             self.emb_proj = [z(V, d) for _ in weights["W1"]]
@@ -92,6 +99,11 @@ class HydraRound:
                 H.hydra_fold_embedding(weights["emb"], w1, t)
 
     def draft(self, h, root_tok, stream=None):
+        if self.sketch:
+            H.hydra_draft_heads_sketch(h, root_tok, self.w["emb"], self.w["heads"], self.dplan, self.head_logits,
+                                       self.head_lse, self.cand_tok, self.cand_logp, self.ws_draft,
+                                       head_hidden=self.head_hidden, stream=stream)
+            return
         H.hydra_draft_heads(h, root_tok, self.w.get("emb"), self.w["W1"], self.w["b1"], self.w["W2"], self.dplan,
                             self.head_logits, self.head_lse, self.cand_tok, self.cand_logp, self.ws_draft,
                             head_hidden=self.head_hidden, residual=self.residual, emb_proj=self.emb_proj,
@@ -139,14 +151,18 @@ class HydraRound:
 def round_from_inputs(inp, device="cuda", keep_hidden=True, fold_embedding=None, residual=True):
     """HydraRound plus device copies of a dict of named input tensors.
 
-    Keys: workload (sizes, tree, dtype, mode), root_tok, h, E, W1, b1, W2, W_t,
+    Keys: workload (sizes, tree, dtype, mode), root_tok, h, E, W1, b1, W2 (or
+    heads, for two-layer heads), W_t,
     q_tree, k_tree, v_tree, k_pages, v_pages, block_table, prefix_len and, for
     the rejection and typical modes, u_acc and u_res. Returns (round, device tensors).
     """
     w = inp["workload"]
     to = lambda t: t.to(device).contiguous()  # noqa: E731
-    weights = dict(emb=to(inp["E"]) if w.hydra else None, W1=[to(x) for x in inp["W1"]],
-                   b1=[to(x) for x in inp["b1"]], W2=[to(x) for x in inp["W2"]], W_t=to(inp["W_t"]))
+    weights = dict(emb=to(inp["E"]) if w.hydra else None, W_t=to(inp["W_t"]))
+    if w.head == "sketch":
+        weights["heads"] = [{n: to(t) for n, t in hd.items()} for hd in inp["heads"]]
+    else:
+        weights.update(W1=[to(x) for x in inp["W1"]], b1=[to(x) for x in inp["b1"]], W2=[to(x) for x in inp["W2"]])
     shape = dict(B=w.B, d=w.d, V=w.V, Hq=w.Hq, Hkv=w.Hkv, D=w.D,
                  max_prefix_len=int(inp["prefix_len"].max()))
     mode = {"greedy": 0, "stochastic": 1, "typical": 2}[w.mode]

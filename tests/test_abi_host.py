@@ -54,7 +54,7 @@ def test_every_declared_symbol_is_exported_and_bound(lib):
 def test_status_strings(lib):
     assert lib.hydra_status_string(0) == b"ok"
     assert lib.hydra_status_string(-3) == b"workspace too small"
-    assert lib.hydra_abi_version() == 7
+    assert lib.hydra_abi_version() == 8
 
 
 @pytest.mark.parametrize("b", [[2, 3], [3, 2, 2], [4, 4, 4, 4], [1, 1, 1, 1, 1], [5, 2], [2, 1, 3]])
@@ -179,3 +179,42 @@ def test_tree_commit_rejects_bad_arguments_before_any_launch(lib):
     assert call(hidden=p[11], next_h=p[12], d=12) == -2
     assert call(k_tree=p[0] + 8) == -1              # misaligned K
     assert b"aligned" in lib.hydra_last_error()
+
+
+def test_draft_heads_sketch_rejects_bad_arguments_before_any_launch(lib):
+    """Argument checks of hydra_draft_heads_sketch run on the host; the fake
+    device addresses are never dereferenced on these paths."""
+    import speculative_decoding_hydra_amd as S
+
+    plan = S.hydra_plan_cartesian([2, 3])
+    rows = S.hydra_plan_rows(plan, True)
+    I32 = C.POINTER(C.c_int32)
+    host = lambda a: (C.c_int32 * len(a))(*[int(x) for x in a])  # noqa: E731
+    rf, df, kp = host(rows.row_first), host(rows.depth_first), host(rows.k_per_depth)
+    p = [4096 * (i + 1) for i in range(32)]
+    arr = C.c_void_p * 2
+
+    def call(dtype=1, d=256, hid=1024, eps=1e-5, n_heads=2, Wb=None, ws_bytes=1 << 30):
+        Wb = arr(None, p[20]) if Wb is None else Wb
+        heads = [arr(p[10 + 2 * i], p[11 + 2 * i]) for i in range(5)]
+        ip = lambda a: C.cast(C.c_void_p(a), I32)  # noqa: E731
+        return lib.hydra_draft_heads_sketch(
+            dtype, 1, d, 1000, hid, p[0], ip(p[1]), p[2], n_heads, heads[0], heads[1], Wb, heads[2], heads[3],
+            heads[4], arr(p[21], p[22]), eps, plan.n, 2, p[3], p[4], p[5], len(rows.row_node), p[6],
+            C.cast(rf, I32), C.cast(df, I32), C.cast(kp, I32), p[7], p[8], None, p[9], p[23], p[24], ws_bytes, None)
+
+    assert call(dtype=7) == -1
+    assert call(d=300) == -2                        # bf16 needs d % 256 == 0
+    assert call(hid=1000) == -2                     # ... and H % 256 == 0
+    assert call(dtype=0, hid=9000) == -2            # rows held in LDS: H <= 8192
+    assert call(eps=0.0) == -1
+    assert call(n_heads=1) == -1                    # two depths, one head
+    assert call(Wb=arr(p[20], None)) == -1          # head 2 has no second layer
+    assert b"head 2" in lib.hydra_last_error()
+    assert call(ws_bytes=16) == -3
+    assert S.hydra_draft_heads_sketch_workspace_size(1, 1, 256, 1000, 1024, _Plan(rows)) >= 6 * 1024 * 4
+
+
+class _Plan:
+    def __init__(self, rows):
+        self.rows, self.dmax = rows, 2

@@ -242,7 +242,7 @@ def _round(name, **over):
     return _cache[key]
 
 
-@pytest.mark.parametrize("name", ["tiny", "tiny_medusa"])
+@pytest.mark.parametrize("name", ["tiny", "tiny_medusa", "tiny_sketch"])
 def test_tiny_round_stagewise(name):
     inp, rnd, dev = _round(name)
     rep = T.oracle_round_checks(inp, rnd)
@@ -250,14 +250,17 @@ def test_tiny_round_stagewise(name):
     print(rep, flush=True)
 
 
-@pytest.mark.parametrize("name", ["tiny", "tiny_medusa"])
+@pytest.mark.parametrize("name", ["tiny", "tiny_medusa", "tiny_sketch"])
 def test_tiny_round_end_to_end(name):
     """Float32 workload: the oracle's own round from the inputs alone."""
     inp, rnd, _ = _round(name)
     w = inp["workload"]
     plan, _ = T.oracle_plan(w.tree)
     f = HI.as_f64
-    heads = [(f(a), f(b), f(c)) for a, b, c in zip(inp["W1"], inp["b1"], inp["W2"])]
+    if w.head == "sketch":
+        heads = [{n: f(t) for n, t in hd.items()} for hd in inp["heads"]]
+    else:
+        heads = [(f(a), f(b), f(c)) for a, b, c in zip(inp["W1"], inp["b1"], inp["W2"])]
     res = O.draft_heads(f(inp["h"]), inp["root_tok"].numpy(), f(inp["E"]), heads, plan, hydra=w.hydra)
     for r in range(res["z"].shape[1]):
         assert res["margin"][0, r] > T.MARGIN, "near tie: seed would need the margin rule"
@@ -452,6 +455,38 @@ def test_draft_four_heads_folded_and_streamed(tree, fold, residual):
     T.run_round(rnd, dev)
     torch.cuda.synchronize()
     rep = T.check_draft(inp, rnd)
+    print(rep, flush=True)
+
+
+@pytest.mark.parametrize("B,d,hid,V,tree", [
+    (1, 4096, 1024, 32000, ("sparse", (10, 4, 2, 1), 64)),   # the 7B sketch shape
+    (3, 256, 512, 1000, ("cartesian", (4, 3, 2))),
+    (2, 8192, 1024, 2000, ("cartesian", (10, 2))),           # 70B width, 20 rows at depth 2
+    (20, 512, 768, 1000, ("sparse", (10, 4, 2, 1), 64)),     # 200 rows at depth 2: tiled second layer
+    (1, 256, 256, 777, ("cartesian", (16, 1, 1))),           # ragged vocabulary, 16-wide first depth
+])
+def test_sketch_heads_stagewise(B, d, hid, V, tree):
+    """Two-layer LayerNorm heads in bf16 against the oracle stage by stage:
+    u within one bf16 step, logits, log-sum-exp and top-k under the margin
+    rule, at row counts on both sides of the tiled-product threshold."""
+    w = HI.workload("7b_sketch", B=B, d=d, V=V, head_hidden=hid, tree=tree, n_heads=len(tree[1]), Hq=8, Hkv=8,
+                    D=32, L=(64,))
+    print(f"sketch heads B={B} d={d} H={hid} V={V} tree={tree}", flush=True)
+    inp = HI.generate(w)
+    rnd, dev = T.round_inputs(inp)
+    assert rnd.sketch and rnd.emb_proj is None
+    T.run_round(rnd, dev)
+    torch.cuda.synchronize()
+    rep = T.check_draft(inp, rnd)
+    print(rep, flush=True)
+
+
+def test_sketch_7b_round():
+    """Whole round with the sketch heads at the 7B shape: stage-wise checks
+    on every stage plus the commit."""
+    inp, rnd, dev = _round("7b_sketch")
+    rep = T.oracle_round_checks(inp, rnd)
+    rep.update(T.check_commit(inp, rnd, dev))
     print(rep, flush=True)
 
 

@@ -86,13 +86,17 @@ def round_bytes(w, rnd, prefix_len):
     """Algorithmic HBM bytes of one round: every weight matrix the round
     needs streamed once, the paged prefix K/V read once, the tree Q/K/V/O,
     the logits written, (folded Hydra heads) one float32 table row per head
-    row instead of W1's embedding half, and the commit's K/V rows (read and
-    written) plus the next hidden state."""
+    row instead of W1's embedding half (two-layer heads: their Wa and Wb),
+    and the commit's K/V rows (read and written) plus the next hidden
+    state."""
     d, V, B, esz = w.d, w.V, w.B, 2 if w.dtype == "bf16" else 4
     R, N, heads = rnd.dplan.R, rnd.n_keep, rnd.dplan.dmax
     rows_per_head = [int(rnd.dplan.rows.row_first[k + 1] - rnd.dplan.rows.row_first[k]) for k in range(heads)]
     draft = heads * V * d * esz  # W2
-    if w.hydra:
+    if getattr(rnd, "sketch", False):
+        hid = w.head_hidden
+        draft += d * d * esz + (heads - 1) * 3 * d * hid * esz  # head 1's Wa; later heads' Wa and Wb
+    elif w.hydra:
         draft += heads * d * d * esz  # W1 h halves
         if rnd.emb_proj is None:
             draft += heads * d * d * esz  # W1 embedding halves, streamed
@@ -231,7 +235,10 @@ def cpu_baseline(inp, n_rows):
 
     w = inp["workload"]
     f = HI.as_f64
-    heads = [(f(a), f(b), f(c)) for a, b, c in zip(inp["W1"], inp["b1"], inp["W2"])]
+    if w.head == "sketch":
+        heads = [{n: f(t) for n, t in hd.items()} for hd in inp["heads"]]
+    else:
+        heads = [(f(a), f(b), f(c)) for a, b, c in zip(inp["W1"], inp["b1"], inp["W2"])]
     E, Wt, h = f(inp["E"]), f(inp["W_t"]), f(inp["h"])
     kp = [f(x) for x in inp["k_prefix"]]
     vp = [f(x) for x in inp["v_prefix"]]
@@ -390,7 +397,8 @@ def main():
     X = torch.randn(M, w.d, device="cuda").to(rnd.dtype)
     Y = torch.empty(M, w.V, device="cuda")
     kws = torch.empty(hydra_vocab_projection_workspace_size(M, w.V, kk), dtype=torch.uint8, device="cuda")
-    W2 = rnd.w["W2"][0]
+    W2s = [hd["W2"] for hd in rnd.w["heads"]] if rnd.sketch else rnd.w["W2"]
+    W2 = W2s[0]
     proj = lambda Wm: hydra_vocab_projection(X, Wm, Y, kk, kws)  # noqa: E731
     for _ in range(3):
         proj(W2)
@@ -408,7 +416,7 @@ def main():
         kgraph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(kgraph):
             for i in range(args.kernel_reps):
-                proj(rnd.w["W2"][i % len(rnd.w["W2"])])
+                proj(W2s[i % len(W2s)])
         kgraph.replay()
         torch.cuda.synchronize()
     except Exception as e:  # noqa: BLE001
@@ -421,7 +429,7 @@ def main():
         kgraph.replay()
     else:
         for i in range(args.kernel_reps):
-            proj(rnd.w["W2"][i % len(rnd.w["W2"])])
+            proj(W2s[i % len(W2s)])
     kb.record(stream)
     torch.cuda.synchronize()
     k_ms = ka.elapsed_time(kb) / args.kernel_reps

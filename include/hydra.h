@@ -180,7 +180,7 @@ int hydra_draft_heads(int dtype, int B, int d, int V, int hydra, int residual,
  *   head k>1: a = T(SiLU(Wa_k [h_b || E[token of row_node[r]]] + ba_k))
  *             u = LN_k(Wb_k a + bb_k)
  *   LN_k(x) = (x - mean) / sqrt(var + ln_eps) * ln_g_k + ln_b_k over the d
- *   values of a row (biased variance); T() rounds to dtype (the identity for
+ *   values of a row (biased variance). T() rounds to dtype (the identity for
  *   float32); u is stored in dtype.
  * then z = W2_k u and everything after it as in hydra_draft_heads.
  *
@@ -193,7 +193,7 @@ int hydra_draft_heads(int dtype, int B, int d, int V, int hydra, int residual,
  * W2           host array of n_heads device pointers, W2_k [V, d]
  * ln_eps       LayerNorm epsilon (> 0; 1e-5 in the source)
  * Plan arguments as in hydra_draft_heads; head 1 must have one row (R's first
- * row, the root). Supported: d, H <= 8192; bf16 needs d % 256 == 0 and
+ * row, the root). Supported: d, H <= 8192, multiples of 4; bf16 needs d % 256 == 0 and
  * H % 256 == 0. Errors as in hydra_draft_heads. */
 size_t hydra_draft_heads_sketch_workspace_size(int dtype, int B, int d, int V, int hidden_dim,
                                                int Dmax, const int32_t* row_first);

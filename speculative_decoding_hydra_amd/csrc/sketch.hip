@@ -11,7 +11,8 @@
 // Per depth k the rows are few (one per expanded node), so each Linear is a
 // weight stream: the split-K projection kernels write float32 partials and a
 // row kernel finishes them (partials + bias, SiLU, LayerNorm), one workgroup
-// per row holding the row in LDS between the statistics and the output. The
+// per row (1024 threads, 16-byte loads of every partial at once) holding the
+// row in LDS between the statistics and the output. The
 // vocabulary projection and the merge (log-sum-exp, top-k, tree fill) are the
 // one-layer path's.
 #include "common.h"
@@ -19,7 +20,7 @@
 namespace hydra {
 namespace {
 
-constexpr int kSketchThreads = 256;
+constexpr int kSketchThreads = 1024;
 constexpr int kSketchMaxWidth = 8192;  // row held in LDS: 32 KB of float32
 
 __device__ __forceinline__ double block_sum_d(double v, double* red) {
@@ -45,10 +46,26 @@ __device__ __forceinline__ float round_to<bf16_t>(float v) {
   return bf16_to_f32(f32_to_bf16(v));
 }
 
-// Row m of width W: v = sum of the ns partials (stride floats apart) + bias;
-// with act, v = T(SiLU(v)); with g, v = (v - mean) / sqrt(var + eps) * g + beta
-// over the row (biased variance). T(v) goes to out[m] and, with hidden, to
-// hidden[map(m)].
+template <class T>
+__device__ __forceinline__ float finish(float v, const T* bias, int j, int act) {
+  v += load_f(bias, j);
+  return act ? round_to<T>(v / (1.0f + expf(-v))) : v;
+}
+
+template <class T>
+__device__ __forceinline__ void store4(T* p, size_t i, float4 v) {
+  store_f(p, i, v.x);
+  store_f(p, i + 1, v.y);
+  store_f(p, i + 2, v.z);
+  store_f(p, i + 3, v.w);
+}
+
+// Row m of width W (W % 4 == 0): v = sum of the ns partials (stride floats
+// apart) + bias; with act, v = T(SiLU(v)); with g, v = (v - mean) /
+// sqrt(var + eps) * g + beta over the row (biased variance). T(v) goes to
+// out[m] and, with hidden, to hidden[map(m)]. Rows are few (one per expanded
+// node), so a workgroup of 1024 threads takes a row: every thread issues the
+// 16-byte loads of its columns from all partials at once.
 template <class T>
 __global__ __launch_bounds__(kSketchThreads) void sketch_rows(int W, int ns, size_t stride,
                                                               const float* __restrict__ part,
@@ -56,38 +73,53 @@ __global__ __launch_bounds__(kSketchThreads) void sketch_rows(int W, int ns, siz
                                                               const T* __restrict__ g, const T* __restrict__ beta,
                                                               float eps, T* __restrict__ out,
                                                               T* __restrict__ hidden, RowMap map) {
-  extern __shared__ float row[];
+  extern __shared__ float4 row[];
   __shared__ double red[kSketchThreads / 64];
   const int m = blockIdx.x;
+  const int W4 = W / 4;
   const size_t base = static_cast<size_t>(m) * W;
   float s = 0.f;
-  for (int j = threadIdx.x; j < W; j += kSketchThreads) {
-    float v = part[base + j];
-    for (int t = 1; t < ns; ++t) v += part[t * stride + base + j];
-    v += load_f(bias, j);
-    if (act) v = round_to<T>(v / (1.0f + expf(-v)));
-    row[j] = v;  // each thread reads back only its own columns
-    s += v;
+  for (int c = threadIdx.x; c < W4; c += kSketchThreads) {
+    float4 v = *reinterpret_cast<const float4*>(part + base + 4 * c);
+    for (int t = 1; t < ns; ++t) {
+      const float4 q = *reinterpret_cast<const float4*>(part + t * stride + base + 4 * c);
+      v.x += q.x;
+      v.y += q.y;
+      v.z += q.z;
+      v.w += q.w;
+    }
+    v.x = finish(v.x, bias, 4 * c, act);
+    v.y = finish(v.y, bias, 4 * c + 1, act);
+    v.z = finish(v.z, bias, 4 * c + 2, act);
+    v.w = finish(v.w, bias, 4 * c + 3, act);
+    row[c] = v;  // each thread reads back only its own columns
+    s += (v.x + v.y) + (v.z + v.w);
   }
   T* hrow = hidden ? hidden + static_cast<size_t>(map(m)) * W : nullptr;
   if (!g) {
-    for (int j = threadIdx.x; j < W; j += kSketchThreads) {
-      store_f(out, base + j, row[j]);
-      if (hrow) store_f(hrow, j, row[j]);
+    for (int c = threadIdx.x; c < W4; c += kSketchThreads) {
+      store4(out, base + 4 * c, row[c]);
+      if (hrow) store4(hrow, 4 * c, row[c]);
     }
     return;
   }
   const float mean = static_cast<float>(block_sum_d(s, red) / W);
   float q = 0.f;
-  for (int j = threadIdx.x; j < W; j += kSketchThreads) {
-    const float c = row[j] - mean;
-    q += c * c;
+  for (int c = threadIdx.x; c < W4; c += kSketchThreads) {
+    const float4 v = row[c];
+    q += (v.x - mean) * (v.x - mean) + (v.y - mean) * (v.y - mean) + (v.z - mean) * (v.z - mean) +
+         (v.w - mean) * (v.w - mean);
   }
   const float rstd = static_cast<float>(1.0 / sqrt(block_sum_d(q, red) / W + eps));
-  for (int j = threadIdx.x; j < W; j += kSketchThreads) {
-    const float y = (row[j] - mean) * rstd * load_f(g, j) + load_f(beta, j);
-    store_f(out, base + j, y);
-    if (hrow) store_f(hrow, j, y);
+  for (int c = threadIdx.x; c < W4; c += kSketchThreads) {
+    const float4 v = row[c];
+    const int j = 4 * c;
+    const float4 y = make_float4((v.x - mean) * rstd * load_f(g, j) + load_f(beta, j),
+                                 (v.y - mean) * rstd * load_f(g, j + 1) + load_f(beta, j + 1),
+                                 (v.z - mean) * rstd * load_f(g, j + 2) + load_f(beta, j + 2),
+                                 (v.w - mean) * rstd * load_f(g, j + 3) + load_f(beta, j + 3));
+    store4(out, base + j, y);
+    if (hrow) store4(hrow, j, y);
   }
 }
 
@@ -168,6 +200,8 @@ extern "C" int hydra_draft_heads_sketch(int dtype, int B, int d, int V, int hidd
            "draft_heads_sketch: bad sizes B=%d d=%d V=%d hidden=%d", B, d, V, hid);
   HY_CHECK(d <= kSketchMaxWidth && hid <= kSketchMaxWidth, HYDRA_ERR_UNSUPPORTED,
            "draft_heads_sketch: d=%d and hidden=%d must be <= %d", d, hid, kSketchMaxWidth);
+  HY_CHECK(d % 4 == 0 && hid % 4 == 0, HYDRA_ERR_UNSUPPORTED,
+           "draft_heads_sketch: d and hidden must be multiples of 4 (d=%d hidden=%d)", d, hid);
   HY_CHECK(dtype == HYDRA_F32 || (d % 256 == 0 && hid % 256 == 0), HYDRA_ERR_UNSUPPORTED,
            "draft_heads_sketch: bf16 needs d and hidden multiples of 256 (d=%d hidden=%d)", d, hid);
   HY_CHECK(ln_eps > 0.f, HYDRA_ERR_INVALID, "draft_heads_sketch: LayerNorm eps must be > 0");

@@ -35,6 +35,12 @@ Readings of points the pages leave open (each is listed in the design doc):
   ``n_nodes - 1`` plus the root.
 * Positions: tree row u of sequence b stands at L_b + depth(u); rotary
   embedding in the LLaMA half-split layout with base theta (10000).
+* Full-path conditioning ([HG] "2. Generalizing to Arbitrary Tree Depths":
+  head k reads h and the embeddings of every token before its position): the
+  one-layer head with x = [h || e(t_0) || ... || e(t_{k-1})], t_j the token
+  of the depth-j node on the path from the root to the expanded node (t_0 the
+  root's, so head 1 reads [h || e(root)] as with parent-only conditioning);
+  W1 of head k is [d, (k + 1) d].
 * Two-layer heads of the [HG] sketch: head 1 LayerNorm(SiLU(Wa h + ba)), later
   heads LayerNorm(Wb SiLU(Wa [h || e(parent)] + ba) + bb), LayerNorm eps 1e-5.
 * Decoder layer of the verify pass: the LLaMA pre-norm layer (RMSNorm,
@@ -71,7 +77,7 @@ __all__ = [
     "tree_mask", "tree_attention", "target_logits", "argmax_lowest",
     "greedy_accept", "residual", "sample_inverse_cdf", "rejection_accept",
     "commit_path", "entropy", "typical_passes", "kept_branch", "typical_accept",
-    "tree_positions", "rope", "rms_norm", "decoder_layer", "layer_norm", "sketch_hidden",
+    "tree_positions", "rope", "rms_norm", "decoder_layer", "layer_norm", "sketch_hidden", "path_tokens",
 ]
 
 
@@ -301,8 +307,18 @@ def head_logits(u, W2):
     return np.asarray(W2, dtype=np.float64) @ np.asarray(u, dtype=np.float64)
 
 
+def path_tokens(plan: TreePlan, tok_b, root_tok_b, node):
+    """Tokens t_0 .. t_depth(node) on the path from the root to ``node``."""
+    path = []
+    while node != 0:
+        path.append(int(tok_b[node]))
+        node = int(plan.parent[node])
+    path.append(int(root_tok_b))
+    return path[::-1]
+
+
 def draft_heads(h, root_tok, E, heads, plan: TreePlan, hydra=True,
-                residual=True, bf16=False, forced_tok=None):
+                residual=True, bf16=False, forced_tok=None, full_path=False):
     """All draft heads of one round, filling the candidate tree.
 
     h [B, d], root_tok [B], E [V, d] (Hydra only), heads = list of (W1, b1, W2)
@@ -310,6 +326,10 @@ def draft_heads(h, root_tok, E, heads, plan: TreePlan, hydra=True,
     (Wa, ba, [Wb, bb,] ln_g, ln_b, W2; see sketch_hidden). Node c at depth k
     takes entry rank[c] of the top-k list of the row that expanded its parent;
     its cumulative score adds that token's log-softmax to the parent's.
+
+    ``full_path``: Hydra heads read the embeddings of the whole path from the
+    root to the expanded node instead of its token alone (W1 of head k is
+    [d, (k + 1) d]).
 
     ``forced_tok`` [B, N] (stage-wise checking): when given, conditioning
     tokens and cumulative scores follow these tokens instead of the oracle's
@@ -343,8 +363,12 @@ def draft_heads(h, root_tok, E, heads, plan: TreePlan, hydra=True,
             for r in np.flatnonzero(row_depth == k):
                 if hydra:
                     p = row_node[r]
-                    ptok = int(root_tok[b]) if p == 0 else int(follow[b, p])
-                    e = np.asarray(E[ptok], dtype=np.float64)
+                    if full_path:
+                        toks = path_tokens(plan, follow[b], root_tok[b], p)
+                        e = np.concatenate([np.asarray(E[t], dtype=np.float64) for t in toks])
+                    else:
+                        ptok = int(root_tok[b]) if p == 0 else int(follow[b, p])
+                        e = np.asarray(E[ptok], dtype=np.float64)
                 else:
                     e = None
                 if sketch:

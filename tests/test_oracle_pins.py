@@ -222,6 +222,53 @@ def test_sketch_bf16_rounds_both_stored_tensors():
     assert not np.array_equal(H.sketch_hidden(h, e, w, bf16=False), ref)
 
 
+def test_full_path_reduces_to_parent_only_when_earlier_blocks_vanish():
+    # with W1_k = [W_h, 0, ..., 0, W_e] the full-path head reads only h and
+    # the parent's embedding: the parent-only head with [W_h, W_e]
+    rng = np.random.default_rng(21)
+    d, V = 8, 40
+    plan = H.plan_cartesian([3, 2, 2])
+    E, h = rng.standard_normal((V, d)), rng.standard_normal((2, d))
+    parent_only, full = [], []
+    for k in range(1, 4):
+        Wh, We = rng.standard_normal((d, d)) * 0.5, rng.standard_normal((d, d)) * 0.5
+        b1, W2 = rng.standard_normal(d) * 0.1, rng.standard_normal((V, d))
+        parent_only.append((np.hstack([Wh, We]), b1, W2))
+        full.append((np.hstack([Wh] + [np.zeros((d, d))] * (k - 1) + [We]), b1, W2))
+    a = H.draft_heads(h, [3, 7], E, parent_only, plan)
+    b = H.draft_heads(h, [3, 7], E, full, plan, full_path=True)
+    assert np.array_equal(a["tok"], b["tok"])
+    assert np.allclose(a["logp"], b["logp"], rtol=0, atol=1e-12)
+
+
+def test_full_path_block_j_reads_the_depth_j_token():
+    # only block j of head 3's input weights is nonzero: every depth-3 row's
+    # hidden state is h + SiLU(W E[t_j] + b1) for the depth-j token of its
+    # own path, found here by walking parent links by hand
+    rng = np.random.default_rng(22)
+    d, V = 6, 30
+    plan = H.plan_cartesian([2, 2, 2])
+    E, h = rng.standard_normal((V, d)), rng.standard_normal((1, d))
+    base = [(rng.standard_normal((d, (k + 1) * d)), rng.standard_normal(d), rng.standard_normal((V, d)))
+            for k in range(1, 4)]
+    row_node, row_depth, _ = H.head_rows(plan, True)
+    for j in range(3):
+        W = rng.standard_normal((d, d))
+        W1 = np.zeros((d, 4 * d))
+        W1[:, (j + 1) * d:(j + 2) * d] = W
+        heads = base[:2] + [(W1, base[2][1], base[2][2])]
+        res = H.draft_heads(h, [5], E, heads, plan, full_path=True)
+        for r in np.flatnonzero(row_depth == 3):
+            node, chain = int(row_node[r]), []
+            while node:
+                chain.append(int(res["tok"][0, node]))
+                node = int(plan.parent[node])
+            chain.append(5)
+            t_j = chain[::-1][j]
+            want = h[0] + torch.nn.functional.silu(torch.from_numpy(W @ E[t_j] + base[2][1])).numpy()
+            assert np.allclose(res["u"][0, r], want, rtol=1e-12, atol=1e-12)
+
+
 # -------------------------------------------------------------------- trees
 
 def test_cartesian_counts(golden):

@@ -96,6 +96,8 @@ def round_bytes(w, rnd, prefix_len):
     if getattr(rnd, "sketch", False):
         hid = w.head_hidden
         draft += d * d * esz + (heads - 1) * 3 * d * hid * esz  # head 1's Wa; later heads' Wa and Wb
+    elif w.hydra and w.cond == "path":
+        draft += sum((k + 1) * d * d for k in range(1, heads + 1)) * esz  # W1 over [h, path embeddings]
     elif w.hydra:
         draft += heads * d * d * esz  # W1 h halves
         if rnd.emb_proj is None:
@@ -259,7 +261,8 @@ def cpu_baseline(inp, n_rows):
     reps, total = 0, 0.0
     while reps < 5 and total < 10.0:  # a bounded sample: whole rounds, about 10 s
         t0 = time.perf_counter()
-        res = O.draft_heads(h, inp["root_tok"].numpy(), E, heads, plan, hydra=w.hydra, bf16=w.dtype == "bf16")
+        res = O.draft_heads(h, inp["root_tok"].numpy(), E, heads, plan, hydra=w.hydra, bf16=w.dtype == "bf16",
+                            full_path=w.cond == "path")
         if kind == "dense":
             trees = [O.prune_tree(plan, res["logp"][b], w.tree[2]) for b in range(w.B)]
         else:

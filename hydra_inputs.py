@@ -14,7 +14,8 @@ in this fixed order:
   2. h [B, d] ~ N(0, 1)
   3. embedding table E [V, d] ~ N(0, 1)
   4. per head k = 1..n_heads: W1 [d, in] ~ N(0, 0.02), b1 [d] ~ N(0, 0.02),
-     W2 [V, d] ~ N(0, 0.02)      (in = 2 d for Hydra, d for Medusa)
+     W2 [V, d] ~ N(0, 0.02)      (in = 2 d for Hydra, d for Medusa, (k + 1) d
+     for full-path conditioning)
   5. target vocabulary projection W_t [V, d] ~ N(0, 0.02)
   6. prefix lengths L_b (fixed, or uniform in [lo, hi])
   7. per sequence: prefix K [L_b, Hkv, D], then prefix V, ~ N(0, 1)
@@ -63,6 +64,7 @@ class Workload:
     zero_init: bool = False
     head: str = "mlp"     # "mlp" (one SiLU layer) | "sketch" (two-layer LayerNorm heads)
     head_hidden: int = 1024
+    cond: str = "parent"  # Hydra conditioning: "parent" token or the whole "path" from the root
     extra: dict = field(default_factory=dict)
 
     @property
@@ -107,6 +109,10 @@ WORKLOADS = {
     "tiny_sketch": Workload("tiny_sketch", 5, "fp32", 1, 256, 1000, 3, True, ("cartesian", (2, 3)),
                             8, 8, 32, (128,), head="sketch"),
     "7b_sketch": Workload("7b_sketch", 6, B=1, tree=_SPARSE, L=(2048,), head="sketch", **_7B),
+    # full-path conditioning: head k reads h and the embeddings of its whole path
+    "tiny_path": Workload("tiny_path", 7, "fp32", 1, 256, 1000, 3, True, ("cartesian", (2, 3)),
+                          8, 8, 32, (128,), cond="path"),
+    "7b_path": Workload("7b_path", 8, B=1, tree=_SPARSE, L=(2048,), cond="path", **_7B),
     "70b_gqa": Workload("70b_gqa", 4, "bf16", 4, 8192, 32000, 4, True, _SPARSE,
                         64, 8, 128, (16384,), mode="stochastic", T=0.7),
 }
@@ -141,7 +147,9 @@ def generate(w: Workload, n_tree: int | None = None, reserve: int | None = None)
     out["E"] = _normal(g, (w.V, w.d), 1.0, dt)
     in_dim = 2 * w.d if w.hydra else w.d
     W1, b1, W2 = [], [], []
-    for _ in range(w.n_heads):
+    for k in range(1, w.n_heads + 1):
+        if w.cond == "path":
+            in_dim = (k + 1) * w.d
         W1.append(_normal(g, (w.d, in_dim), 0.02, dt))
         b1.append(_normal(g, (w.d,), 0.02, dt))
         W2.append(_normal(g, (w.V, w.d), 0.02, dt))

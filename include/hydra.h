@@ -133,7 +133,11 @@ int hydra_plan_rows(int N, const int32_t* parent, const int32_t* rank,
  *
  * dtype        HYDRA_F32 or HYDRA_BF16 (h, emb, W1, b1, W2, head_hidden)
  * B, d, V      sequences, hidden size, vocabulary size
- * hydra        1: [h || e(parent)] input of width 2d; 0: Medusa, input h
+ * hydra        1: [h || e(parent)] input of width 2d; 0: Medusa, input h;
+ *              2: full path ([HG] "2. Generalizing to Arbitrary Tree Depths"):
+ *              head k reads [h || E[t_0] || ... || E[t_{k-1}]] of width
+ *              (k + 1) d, t_j the token of the depth-j node on the path from
+ *              the root to the expanded node (emb_proj is not used)
  * residual     1: u = h + SiLU(a); 0: u = SiLU(a)
  * h            [B, d]
  * root_tok     [B] int32, token of the root of each tree
@@ -147,7 +151,8 @@ int hydra_plan_rows(int N, const int32_t* parent, const int32_t* rank,
  *              the tables are ignored.
  * n_heads      entries in W1/b1/W2 (>= Dmax)
  * W1, b1, W2   host arrays of n_heads device pointers: W1_k [d, in] (in = 2d
- *              Hydra, d Medusa), b1_k [d], W2_k [V, d]; head k at index k-1
+ *              Hydra, d Medusa, (k + 1) d full path), b1_k [d], W2_k [V, d];
+ *              head k at index k-1
  * N, Dmax      plan nodes, plan depth
  * node_parent, node_rank, node_row   device int32 [N] (plan and hydra_plan_rows)
  * R, row_node  rows per sequence; device int32 [R]

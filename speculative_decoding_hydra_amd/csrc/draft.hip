@@ -44,6 +44,37 @@ __global__ __launch_bounds__(256) void head_mlp_epilogue(int M, int d, int nspli
   }
 }
 
+// Full-path input of the depth-k rows ([HG] "2. Generalizing to Arbitrary
+// Tree Depths"): x = [h_b || E[t_0] || ... || E[t_{k-1}]], t_j the token of
+// the depth-j node on the path from the root to the expanded node. One
+// workgroup per row: one lane walks the parent links, then the row is copied
+// into a contiguous [M, (k + 1) d] buffer for the split-K projection.
+template <class T>
+__global__ __launch_bounds__(256) void gather_path(int d, int k, int P, int r0, int N, int V, const T* __restrict__ h,
+                                                   const T* __restrict__ emb, const int32_t* __restrict__ row_node,
+                                                   const int32_t* __restrict__ parent,
+                                                   const int32_t* __restrict__ root_tok,
+                                                   const int32_t* __restrict__ tok, T* __restrict__ X) {
+  __shared__ int toks[HYDRA_MAX_DEPTH + 1];
+  const int m = blockIdx.x;
+  const int b = m / P;
+  if (threadIdx.x == 0) {
+    int a = row_node[r0 + m % P];  // depth k - 1
+    for (int j = k - 1; j >= 0; --j) {
+      int t = a <= 0 ? root_tok[b] : tok[static_cast<size_t>(b) * N + a];
+      toks[j] = t < 0 ? 0 : (t >= V ? V - 1 : t);
+      a = a <= 0 ? 0 : parent[a];
+    }
+  }
+  __syncthreads();
+  const int width = (k + 1) * d;
+  T* xr = X + static_cast<size_t>(m) * width;
+  for (int i = threadIdx.x; i < width; i += 256) {
+    const int seg = i / d, c = i - seg * d;
+    xr[i] = seg == 0 ? h[static_cast<size_t>(b) * d + c] : emb[static_cast<size_t>(toks[seg - 1]) * d + c];
+  }
+}
+
 int w1_splits(int dtype, int in_dim, int d) {
   if (dtype == HYDRA_F32) return 1;
   // enough workgroups for 256 CUs: d / 64 row tiles times the splits
@@ -59,7 +90,7 @@ using namespace hydra;
 
 namespace {
 struct DraftWs {
-  size_t part, u, a, keys, ms, total;
+  size_t part, u, a, keys, ms, x, total;
 };
 DraftWs draft_ws(int dtype, int B, int d, int V, int hydra_mode, int Dmax, const int32_t* row_first,
                  const int32_t* k_per_depth) {
@@ -71,12 +102,14 @@ DraftWs draft_ws(int dtype, int B, int d, int V, int hydra_mode, int Dmax, const
   const size_t esz = dtype == HYDRA_F32 ? 4 : 2;
   const size_t nwg = projection_nwg(V);
   DraftWs w;
-  w.part = align_up(w1_splits(dtype, in_dim, d) * M * d * sizeof(float), 256);
+  // full path (mode 2): up to 16 split-K partials and the gathered rows
+  w.part = align_up((hydra_mode == 2 ? 16 : w1_splits(dtype, in_dim, d)) * M * d * sizeof(float), 256);
+  w.x = hydra_mode == 2 ? align_up(M * (Dmax + 1) * d * esz, 256) : 0;
   w.u = align_up(MU * d * esz, 256);
   w.a = align_up(static_cast<size_t>(Dmax) * B * d * sizeof(float), 256);
   w.keys = align_up(M * nwg * sizeof(uint64_t), 256);
   w.ms = align_up(M * nwg * sizeof(float2), 256);
-  w.total = w.part + w.u + w.a + w.keys + w.ms + 256;
+  w.total = w.part + w.u + w.a + w.keys + w.ms + w.x + 256;
   return w;
 }
 }  // namespace
@@ -102,12 +135,15 @@ extern "C" int hydra_draft_heads(int dtype, int B, int d, int V, int hydra_mode,
   HY_CHECK(dtype == HYDRA_F32 || dtype == HYDRA_BF16, HYDRA_ERR_INVALID, "draft_heads: bad dtype %d", dtype);
   HY_CHECK(B > 0 && d > 0 && V > 0, HYDRA_ERR_INVALID, "draft_heads: bad sizes B=%d d=%d V=%d", B, d, V);
   HY_CHECK(Dmax >= 1 && Dmax <= HYDRA_MAX_DEPTH, HYDRA_ERR_INVALID, "draft_heads: Dmax=%d out of [1, %d]", Dmax, HYDRA_MAX_DEPTH);
+  HY_CHECK(hydra_mode >= 0 && hydra_mode <= 2, HYDRA_ERR_INVALID, "draft_heads: hydra mode %d", hydra_mode);
   HY_CHECK(n_heads >= Dmax, HYDRA_ERR_INVALID, "draft_heads: n_heads=%d < Dmax=%d", n_heads, Dmax);
   HY_CHECK(N >= 2 && N <= HYDRA_MAX_TREE, HYDRA_ERR_INVALID, "draft_heads: N=%d out of [2, %d]", N, HYDRA_MAX_TREE);
   HY_CHECK(h && root_tok && W1 && b1 && W2 && node_parent && node_rank && node_row && row_first &&
                depth_first && k_per_depth && head_logits && head_lse && cand_tok && cand_logp,
            HYDRA_ERR_INVALID, "draft_heads: null pointer");
   HY_CHECK(!hydra_mode || (emb && row_node), HYDRA_ERR_INVALID, "draft_heads: Hydra mode needs emb and row_node");
+  HY_CHECK(hydra_mode != 2 || (dtype == HYDRA_F32 || d % 256 == 0), HYDRA_ERR_UNSUPPORTED,
+           "draft_heads: full-path bf16 needs d %% 256 == 0");
   HY_CHECK(dtype == HYDRA_F32 || d % 256 == 0, HYDRA_ERR_UNSUPPORTED, "draft_heads: bf16 needs d %% 256 == 0 (d=%d)", d);
   HY_CHECK(row_first[0] == 0 && row_first[Dmax] == R, HYDRA_ERR_INVALID, "draft_heads: row_first must span [0, R=%d)", R);
   HY_CHECK(depth_first[0] == 0 && depth_first[1] == 1 && depth_first[Dmax + 1] == N, HYDRA_ERR_INVALID,
@@ -134,12 +170,14 @@ extern "C" int hydra_draft_heads(int dtype, int B, int d, int V, int hydra_mode,
   const int ns = w1_splits(dtype, in_dim, d);
   const size_t esz = dtype == HYDRA_F32 ? 4 : 2;
   const int nwg = projection_nwg(V);
+  const DraftWs wl = draft_ws(dtype, B, d, V, hydra_mode, Dmax, row_first, k_per_depth);
   Arena arena(ws, ws_bytes);
-  float* part = arena.take<float>(ns * Mmax * d);
+  float* part = arena.take<float>(wl.part / sizeof(float));
   char* U = arena.take<char>(MU * d * esz);
   float* Ah = arena.take<float>(static_cast<size_t>(Dmax) * B * d);
   uint64_t* tkeys = arena.take<uint64_t>(Mmax * nwg);
   float2* tms = arena.take<float2>(Mmax * nwg);
+  char* Xp = hydra_mode == 2 ? arena.take<char>(wl.x) : nullptr;
 
   // Feed-forward layers. Medusa heads read h alone: with few rows all of
   // them run in one launch up front. Hydra head k >= 2 splits into the h
@@ -154,7 +192,7 @@ extern "C" int hydra_draft_heads(int dtype, int B, int d, int V, int hydra_mode,
   // of Ah); the row merge of depth k then writes the rows of depth k + 1
   // from the tokens it picks, while its extra workgroups stream the h half of
   // head k + 2 into slot k + 1.
-  const bool folded = hydra_mode && emb_proj && dtype == HYDRA_BF16 && d % 256 == 0 &&
+  const bool folded = hydra_mode == 1 && emb_proj && dtype == HYDRA_BF16 && d % 256 == 0 &&
                       mlp_fused_supported(dtype, B, d, d) && merge_ffn_supported(B, d, d);
   if (folded) {
     for (int k = 1; k <= Dmax; ++k)
@@ -190,7 +228,7 @@ extern "C" int hydra_draft_heads(int dtype, int B, int d, int V, int hydra_mode,
     if (rc != HYDRA_OK) return rc;
   }
   bool split[HYDRA_MAX_DEPTH + 2] = {};
-  if (hydra_mode && !folded)
+  if (hydra_mode == 1 && !folded)
     for (int k = 2; k <= Dmax; ++k)
       split[k] = mlp_fused_supported(dtype, B * (row_first[k] - row_first[k - 1]), d, d) &&
                  merge_ffn_supported(B, d, d);
@@ -252,7 +290,32 @@ extern "C" int hydra_draft_heads(int dtype, int B, int d, int V, int hydra_mode,
     fa.U = reinterpret_cast<bf16_t*>(U);
     fa.hidden = static_cast<bf16_t*>(head_hidden);
     fa.map[0] = map;
-    if (medusa_once) {
+    if (hydra_mode == 2) {
+      // full path: gather [h || E[t_0] || ... || E[t_{k-1}]], split-K W1, epilogue
+      const int width = (k + 1) * d;
+      if (dtype == HYDRA_F32)
+        gather_path<float><<<M, 256, 0, stream>>>(d, k, P, r0, N, V, static_cast<const float*>(h),
+                                                  static_cast<const float*>(emb), row_node, node_parent, root_tok,
+                                                  cand_tok, reinterpret_cast<float*>(Xp));
+      else
+        gather_path<bf16_t><<<M, 256, 0, stream>>>(d, k, P, r0, N, V, hb, static_cast<const bf16_t*>(emb), row_node,
+                                                   node_parent, root_tok, cand_tok, reinterpret_cast<bf16_t*>(Xp));
+      HY_LAUNCH_CHECK("draft_heads: path gather");
+      int nsp = 1;
+      rc = launch_projection_parts(dtype, M, width, d, Xp, W1[k - 1], part, wl.part / sizeof(float), &nsp, stream);
+      if (rc != HYDRA_OK) return rc;
+      const size_t total = static_cast<size_t>(M) * d;
+      const int grid = static_cast<int>(std::min<size_t>((total + 255) / 256, 4096));
+      if (dtype == HYDRA_F32)
+        head_mlp_epilogue<float><<<grid, 256, 0, stream>>>(
+            M, d, nsp, part, static_cast<const float*>(b1[k - 1]), static_cast<const float*>(h), P, residual,
+            reinterpret_cast<float*>(U), static_cast<float*>(head_hidden), map);
+      else
+        head_mlp_epilogue<bf16_t><<<grid, 256, 0, stream>>>(M, d, nsp, part, static_cast<const bf16_t*>(b1[k - 1]),
+                                                            hb, P, residual, reinterpret_cast<bf16_t*>(U),
+                                                            static_cast<bf16_t*>(head_hidden), map);
+      HY_LAUNCH_CHECK("draft_heads: mlp epilogue");
+    } else if (medusa_once) {
       Uk = U + static_cast<size_t>(k - 1) * B * d * esz;  // written by the all-heads launch
     } else if (folded) {
       // rows written by the launch up front (k = 1) or the previous merge

@@ -177,9 +177,13 @@ def hydra_draft_heads_workspace_size(dtype_code, B, d, V, hydra, dplan: DevicePl
 
 
 def hydra_draft_heads(h, root_tok, emb, W1, b1, W2, dplan: DevicePlan, head_logits, head_lse,
-                      cand_tok, cand_logp, ws, head_hidden=None, residual=True, emb_proj=None, stream=None):
+                      cand_tok, cand_logp, ws, head_hidden=None, residual=True, emb_proj=None, full_path=False,
+                      stream=None):
     """Stage 1 (see include/hydra.h). h [B, d]; W1/b1/W2: lists, head k at k-1;
-    emb_proj: optional list of folded embedding tables (hydra_fold_embedding)."""
+    emb_proj: optional list of folded embedding tables (hydra_fold_embedding);
+    full_path: Hydra heads read every path token's embedding (W1_k [d, (k+1) d])."""
+    if full_path and not dplan.hydra:
+        raise ValueError("full-path conditioning needs a Hydra plan")
     dt = _dtype_code(h)
     B, d = h.shape
     V = W2[0].shape[0]
@@ -196,12 +200,14 @@ def hydra_draft_heads(h, root_tok, emb, W1, b1, W2, dplan: DevicePlan, head_logi
     kp, kpp = _host_i32(rows.k_per_depth)
     ep = None
     if emb_proj is not None:
+        if full_path:
+            raise ValueError("full-path heads take no folded tables")
         if len(emb_proj) != n_heads:
             raise ValueError("emb_proj needs one table per head")
         ep = arr(*[_dev(t, "emb_proj", torch.float32) for t in emb_proj])
     wsp, wsb = _ws(ws)
     rc = lib().hydra_draft_heads(
-        dt, B, d, V, int(dplan.hydra), int(bool(residual)), _dev(h, "h"), _dev(root_tok, "root_tok", torch.int32),
+        dt, B, d, V, 2 if full_path else int(dplan.hydra), int(bool(residual)), _dev(h, "h"), _dev(root_tok, "root_tok", torch.int32),
         _dev(emb, "emb", h.dtype) if dplan.hydra else None, ep, n_heads, w1, bb, w2, dplan.N, dplan.dmax,
         _dev(dplan.parent, "parent"), _dev(dplan.rank, "rank"), _dev(dplan.node_row, "node_row"), dplan.R,
         _dev(dplan.row_node, "row_node"), rfp, dfp, kpp, _dev(head_logits, "head_logits", torch.float32),

@@ -37,12 +37,15 @@ class HydraRound:
     fold_embedding: build the folded embedding tables of the Hydra heads
     (hydra_fold_embedding, V * d * 4 bytes per head) once here and let the
     draft stage look the embedding half up; None folds for bf16 Hydra heads.
+    full_path: Hydra heads read the embeddings of the whole path from the
+    root (W1 of head k is [d, (k + 1) d]); never folded.
     rope_theta: rotate the tree Q/K rows at positions prefix_len + depth
     (tree_rope) before attention; None gives the rows to attention as they are.
     """
 
     def __init__(self, weights, tree, shape, hydra=True, mode=0, temperature=1.0, residual=True,
-                 keep_hidden=False, device="cuda", fold_embedding=None, eps=None, delta=None, rope_theta=10000.0):
+                 keep_hidden=False, device="cuda", fold_embedding=None, eps=None, delta=None, rope_theta=10000.0,
+                 full_path=False):
         self.w = weights
         plan, n_keep = make_plan(tree)
         self.dplan = H.DevicePlan(plan, hydra, device)
@@ -81,17 +84,19 @@ class HydraRound:
         self.next_h = z(B, Hq * D, dtype=dt)
         nb = lambda n: torch.empty(max(int(n), 1), dtype=torch.uint8, device=device)  # noqa: E731
         self.sketch = weights.get("heads") is not None
+        self.full_path = bool(full_path)
         if self.sketch:
             hid = weights["heads"][1]["Wa"].shape[0] if len(weights["heads"]) > 1 else d
             self.ws_draft = nb(H.hydra_draft_heads_sketch_workspace_size(code, B, d, V, hid, self.dplan))
         else:
-            self.ws_draft = nb(H.hydra_draft_heads_workspace_size(code, B, d, V, hydra, self.dplan))
+            self.ws_draft = nb(H.hydra_draft_heads_workspace_size(code, B, d, V, 2 if full_path else hydra,
+                                                                  self.dplan))
         self.ws_build = nb(H.tree_build_workspace_size(B, N, K))
         self.ws_attn = nb(H.tree_attention_verify_workspace_size(code, B, K, Hq, Hkv, D,
                                                                  shape["max_prefix_len"]))
         self.ws_accept = nb(H.tree_accept_workspace_size(self.mode, B, K, V))
         if fold_embedding is None:
-            fold_embedding = hydra and dt == torch.bfloat16 and not self.sketch
+            fold_embedding = hydra and dt == torch.bfloat16 and not self.sketch and not self.full_path
         self.emb_proj = None
         if fold_embedding:
             self.emb_proj = [z(V, d) for _ in weights["W1"]]
@@ -107,7 +112,7 @@ class HydraRound:
         H.hydra_draft_heads(h, root_tok, self.w.get("emb"), self.w["W1"], self.w["b1"], self.w["W2"], self.dplan,
                             self.head_logits, self.head_lse, self.cand_tok, self.cand_logp, self.ws_draft,
                             head_hidden=self.head_hidden, residual=self.residual, emb_proj=self.emb_proj,
-                            stream=stream)
+                            full_path=self.full_path, stream=stream)
 
     def build(self, stream=None):
         H.tree_build(self.dplan, self.cand_tok, self.cand_logp, self.n_keep, self.tok, self.parent, self.depth,
@@ -167,7 +172,7 @@ def round_from_inputs(inp, device="cuda", keep_hidden=True, fold_embedding=None,
                  max_prefix_len=int(inp["prefix_len"].max()))
     mode = {"greedy": 0, "stochastic": 1, "typical": 2}[w.mode]
     rnd = HydraRound(weights, w.tree, shape, hydra=w.hydra, mode=mode, temperature=w.T, residual=residual, keep_hidden=keep_hidden, device=device,
-                     fold_embedding=fold_embedding, eps=w.eps, delta=w.delta)
+                     fold_embedding=fold_embedding, eps=w.eps, delta=w.delta, full_path=w.cond == "path")
     dev = dict(h=to(inp["h"]), root_tok=to(inp["root_tok"]), q=to(inp["q_tree"]), k_tree=to(inp["k_tree"]),
                v_tree=to(inp["v_tree"]), k_pages=to(inp["k_pages"]), v_pages=to(inp["v_pages"]),
                block_table=to(inp["block_table"]), prefix_len=to(inp["prefix_len"]))

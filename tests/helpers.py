@@ -148,8 +148,12 @@ def check_draft(inp, rnd, seqs=None, rows=None):
             e = None
             if w.hydra:
                 p = int(row_node[r])
-                ptok = int(inp["root_tok"][b]) if p == 0 else int(ctok[b, p])
-                e = HI.as_f64(inp["E"][ptok])
+                if getattr(w, "cond", "parent") == "path":
+                    toks = O.path_tokens(plan, ctok[b], int(inp["root_tok"][b]), p)
+                    e = np.concatenate([HI.as_f64(inp["E"][t]) for t in toks])
+                else:
+                    ptok = int(inp["root_tok"][b]) if p == 0 else int(ctok[b, p])
+                    e = HI.as_f64(inp["E"][ptok])
             if sketch:
                 u = O.sketch_hidden(h[b], e if k > 1 else None, W1, bf16)
             else:

@@ -46,32 +46,35 @@ __global__ __launch_bounds__(256) void head_mlp_epilogue(int M, int d, int nspli
 
 // Full-path input of the depth-k rows ([HG] "2. Generalizing to Arbitrary
 // Tree Depths"): x = [h_b || E[t_0] || ... || E[t_{k-1}]], t_j the token of
-// the depth-j node on the path from the root to the expanded node. One
-// workgroup per row: one lane walks the parent links, then the row is copied
-// into a contiguous [M, (k + 1) d] buffer for the split-K projection.
+// the depth-j node on the path from the root to the expanded node, copied
+// into a contiguous [M, (k + 1) d] buffer for the split-K projection. One
+// workgroup per (segment, row): segment j > 0 climbs k - j parent links from
+// the expanded node (depth k - 1) to its depth-(j - 1) ancestor and copies
+// that token's embedding row, 16 bytes per lane when rows allow it.
 template <class T>
 __global__ __launch_bounds__(256) void gather_path(int d, int k, int P, int r0, int N, int V, const T* __restrict__ h,
                                                    const T* __restrict__ emb, const int32_t* __restrict__ row_node,
                                                    const int32_t* __restrict__ parent,
                                                    const int32_t* __restrict__ root_tok,
                                                    const int32_t* __restrict__ tok, T* __restrict__ X) {
-  __shared__ int toks[HYDRA_MAX_DEPTH + 1];
-  const int m = blockIdx.x;
+  const int seg = blockIdx.x, m = blockIdx.y;
   const int b = m / P;
-  if (threadIdx.x == 0) {
-    int a = row_node[r0 + m % P];  // depth k - 1
-    for (int j = k - 1; j >= 0; --j) {
-      int t = a <= 0 ? root_tok[b] : tok[static_cast<size_t>(b) * N + a];
-      toks[j] = t < 0 ? 0 : (t >= V ? V - 1 : t);
-      a = a <= 0 ? 0 : parent[a];
-    }
+  const T* src = h + static_cast<size_t>(b) * d;
+  if (seg > 0) {
+    int a = row_node[r0 + m % P];
+    for (int s = 0; s < k - seg && a > 0; ++s) a = parent[a];
+    int t = a <= 0 ? root_tok[b] : tok[static_cast<size_t>(b) * N + a];
+    t = t < 0 ? 0 : (t >= V ? V - 1 : t);
+    src = emb + static_cast<size_t>(t) * d;
   }
-  __syncthreads();
-  const int width = (k + 1) * d;
-  T* xr = X + static_cast<size_t>(m) * width;
-  for (int i = threadIdx.x; i < width; i += 256) {
-    const int seg = i / d, c = i - seg * d;
-    xr[i] = seg == 0 ? h[static_cast<size_t>(b) * d + c] : emb[static_cast<size_t>(toks[seg - 1]) * d + c];
+  T* dst = X + (static_cast<size_t>(m) * (k + 1) + seg) * d;
+  constexpr int kVec = 16 / sizeof(T);
+  if (d % kVec == 0) {
+    const u32x4_t* s4 = reinterpret_cast<const u32x4_t*>(src);
+    u32x4_t* d4 = reinterpret_cast<u32x4_t*>(dst);
+    for (int i = threadIdx.x; i < d / kVec; i += 256) d4[i] = s4[i];
+  } else {
+    for (int i = threadIdx.x; i < d; i += 256) dst[i] = src[i];
   }
 }
 
@@ -294,12 +297,13 @@ extern "C" int hydra_draft_heads(int dtype, int B, int d, int V, int hydra_mode,
       // full path: gather [h || E[t_0] || ... || E[t_{k-1}]], split-K W1, epilogue
       const int width = (k + 1) * d;
       if (dtype == HYDRA_F32)
-        gather_path<float><<<M, 256, 0, stream>>>(d, k, P, r0, N, V, static_cast<const float*>(h),
-                                                  static_cast<const float*>(emb), row_node, node_parent, root_tok,
-                                                  cand_tok, reinterpret_cast<float*>(Xp));
+        gather_path<float><<<dim3(k + 1, M), 256, 0, stream>>>(
+            d, k, P, r0, N, V, static_cast<const float*>(h), static_cast<const float*>(emb), row_node, node_parent,
+            root_tok, cand_tok, reinterpret_cast<float*>(Xp));
       else
-        gather_path<bf16_t><<<M, 256, 0, stream>>>(d, k, P, r0, N, V, hb, static_cast<const bf16_t*>(emb), row_node,
-                                                   node_parent, root_tok, cand_tok, reinterpret_cast<bf16_t*>(Xp));
+        gather_path<bf16_t><<<dim3(k + 1, M), 256, 0, stream>>>(d, k, P, r0, N, V, hb, static_cast<const bf16_t*>(emb),
+                                                                row_node, node_parent, root_tok, cand_tok,
+                                                                reinterpret_cast<bf16_t*>(Xp));
       HY_LAUNCH_CHECK("draft_heads: path gather");
       int nsp = 1;
       rc = launch_projection_parts(dtype, M, width, d, Xp, W1[k - 1], part, wl.part / sizeof(float), &nsp, stream);

@@ -41,6 +41,14 @@ Readings of points the pages leave open (each is listed in the design doc):
   of the depth-j node on the path from the root to the expanded node (t_0 the
   root's, so head 1 reads [h || e(root)] as with parent-only conditioning);
   W1 of head k is [d, (k + 1) d].
+* Hydra++ self-attention fusion ([HG] "3. Hydra++": one causal
+  self-attention layer over the candidate token embeddings): one layer
+  shared by all heads, single head, no biases, scale 1/sqrt(d). At an
+  expanded node with path tokens t_0 .. t_{k-1}, x_j = e(t_j), the query is
+  Wq x_{k-1}, keys Wk x_j, values Wv x_j (j <= k - 1: causal), and
+  c = x_{k-1} + Wo sum_j softmax_j(q . K_j / sqrt(d)) V_j replaces e(parent)
+  in the one-layer head. In bf16 the attention output and c are rounded
+  (stored), q, K and V are not.
 * Two-layer heads of the [HG] sketch: head 1 LayerNorm(SiLU(Wa h + ba)), later
   heads LayerNorm(Wb SiLU(Wa [h || e(parent)] + ba) + bb), LayerNorm eps 1e-5.
 * Decoder layer of the verify pass: the LLaMA pre-norm layer (RMSNorm,
@@ -77,7 +85,7 @@ __all__ = [
     "tree_mask", "tree_attention", "target_logits", "argmax_lowest",
     "greedy_accept", "residual", "sample_inverse_cdf", "rejection_accept",
     "commit_path", "entropy", "typical_passes", "kept_branch", "typical_accept",
-    "tree_positions", "rope", "rms_norm", "decoder_layer", "layer_norm", "sketch_hidden", "path_tokens",
+    "tree_positions", "rope", "rms_norm", "decoder_layer", "layer_norm", "sketch_hidden", "path_tokens", "path_attention",
 ]
 
 
@@ -317,8 +325,24 @@ def path_tokens(plan: TreePlan, tok_b, root_tok_b, node):
     return path[::-1]
 
 
+def path_attention(X, attn, bf16=False):
+    """Hydra++ fusion of the path embeddings X [k, d] (root first): the
+    causal self-attention output at the last position plus the residual,
+    c = x_{k-1} + Wo softmax(q K^T / sqrt(d)) V with q = Wq x_{k-1}."""
+    X = np.asarray(X, dtype=np.float64)
+    f = lambda n: np.asarray(attn[n], dtype=np.float64)  # noqa: E731
+    r = round_bf16 if bf16 else (lambda t: t)
+    q = f("Wq") @ X[-1]
+    K = X @ f("Wk").T
+    Vv = X @ f("Wv").T
+    s = K @ q / math.sqrt(X.shape[1])
+    p = np.exp(s - np.max(s))
+    a = r(p @ Vv / np.sum(p))
+    return r(X[-1] + f("Wo") @ a)
+
+
 def draft_heads(h, root_tok, E, heads, plan: TreePlan, hydra=True,
-                residual=True, bf16=False, forced_tok=None, full_path=False):
+                residual=True, bf16=False, forced_tok=None, full_path=False, attn=None):
     """All draft heads of one round, filling the candidate tree.
 
     h [B, d], root_tok [B], E [V, d] (Hydra only), heads = list of (W1, b1, W2)
@@ -330,6 +354,10 @@ def draft_heads(h, root_tok, E, heads, plan: TreePlan, hydra=True,
     ``full_path``: Hydra heads read the embeddings of the whole path from the
     root to the expanded node instead of its token alone (W1 of head k is
     [d, (k + 1) d]).
+
+    ``attn``: Hydra++ fusion (dict of Wq, Wk, Wv, Wo, [d, d] each): the
+    head reads [h || path_attention(embeddings of the path)] instead of
+    [h || e(parent)].
 
     ``forced_tok`` [B, N] (stage-wise checking): when given, conditioning
     tokens and cumulative scores follow these tokens instead of the oracle's
@@ -363,7 +391,10 @@ def draft_heads(h, root_tok, E, heads, plan: TreePlan, hydra=True,
             for r in np.flatnonzero(row_depth == k):
                 if hydra:
                     p = row_node[r]
-                    if full_path:
+                    if attn is not None:
+                        toks = path_tokens(plan, follow[b], root_tok[b], p)
+                        e = path_attention(np.stack([np.asarray(E[t], dtype=np.float64) for t in toks]), attn, bf16)
+                    elif full_path:
                         toks = path_tokens(plan, follow[b], root_tok[b], p)
                         e = np.concatenate([np.asarray(E[t], dtype=np.float64) for t in toks])
                     else:

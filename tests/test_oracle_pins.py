@@ -269,6 +269,55 @@ def test_full_path_block_j_reads_the_depth_j_token():
             assert np.allclose(res["u"][0, r], want, rtol=1e-12, atol=1e-12)
 
 
+def _attn_weights(rng, d, scale=0.3):
+    return {n: rng.standard_normal((d, d)) * scale for n in ("Wq", "Wk", "Wv", "Wo")}
+
+
+def test_path_attention_matches_torch_causal_attention():
+    # the fusion is one causal self-attention layer over the path embeddings,
+    # read at the last position, plus the residual: torch's SDPA with a
+    # causal mask over the whole sequence gives the same last row
+    rng = np.random.default_rng(31)
+    d = 16
+    for k in (1, 2, 5):
+        X = rng.standard_normal((k, d))
+        w = _attn_weights(rng, d)
+        t = lambda a: torch.from_numpy(a)[None, None]  # noqa: E731
+        out = torch.nn.functional.scaled_dot_product_attention(t(X @ w["Wq"].T), t(X @ w["Wk"].T),
+                                                               t(X @ w["Wv"].T), is_causal=True)[0, 0]
+        want = X[-1] + w["Wo"] @ out[-1].numpy()
+        assert np.allclose(H.path_attention(X, w), want, rtol=1e-12, atol=1e-12)
+
+
+def test_path_attention_special_cases():
+    rng = np.random.default_rng(32)
+    d = 8
+    X = rng.standard_normal((4, d))
+    w = _attn_weights(rng, d)
+    # one position: the softmax is 1 and c = x + Wo Wv x
+    assert np.allclose(H.path_attention(X[:1], w), X[0] + w["Wo"] @ w["Wv"] @ X[0], atol=1e-12)
+    # zero query: uniform weights, c = x_last + Wo mean(V)
+    wz = dict(w, Wq=np.zeros((d, d)))
+    assert np.allclose(H.path_attention(X, wz), X[-1] + w["Wo"] @ (w["Wv"] @ X.mean(axis=0)), atol=1e-12)
+
+
+def test_hydra_pp_with_zero_output_projection_is_parent_only():
+    # Wo = 0 leaves c = e(parent): the Hydra++ heads become the parent-only heads
+    rng = np.random.default_rng(33)
+    d, V = 8, 40
+    plan = H.plan_cartesian([3, 2, 2])
+    E, h = rng.standard_normal((V, d)), rng.standard_normal((2, d))
+    heads = [(rng.standard_normal((d, 2 * d)) * 0.5, rng.standard_normal(d) * 0.1, rng.standard_normal((V, d)))
+             for _ in range(3)]
+    w = dict(_attn_weights(rng, d), Wo=np.zeros((d, d)))
+    a = H.draft_heads(h, [3, 7], E, heads, plan)
+    b = H.draft_heads(h, [3, 7], E, heads, plan, attn=w)
+    assert np.array_equal(a["tok"], b["tok"])
+    assert np.allclose(a["logp"], b["logp"], rtol=0, atol=1e-12)
+    c = H.draft_heads(h, [3, 7], E, heads, plan, attn=_attn_weights(rng, d))
+    assert not np.allclose(a["u"], c["u"])
+
+
 # -------------------------------------------------------------------- trees
 
 def test_cartesian_counts(golden):

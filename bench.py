@@ -96,6 +96,8 @@ def round_bytes(w, rnd, prefix_len):
     if getattr(rnd, "sketch", False):
         hid = w.head_hidden
         draft += d * d * esz + (heads - 1) * 3 * d * hid * esz  # head 1's Wa; later heads' Wa and Wb
+    elif w.hydra and w.cond == "attn":
+        draft += heads * 2 * d * d * esz + 4 * heads * d * d * esz  # W1, and Wqkv + Wo once per depth
     elif w.hydra and w.cond == "path":
         draft += sum((k + 1) * d * d for k in range(1, heads + 1)) * esz  # W1 over [h, path embeddings]
     elif w.hydra:
@@ -241,6 +243,10 @@ def cpu_baseline(inp, n_rows):
         heads = [{n: f(t) for n, t in hd.items()} for hd in inp["heads"]]
     else:
         heads = [(f(a), f(b), f(c)) for a, b, c in zip(inp["W1"], inp["b1"], inp["W2"])]
+    attn = None
+    if w.cond == "attn":
+        Wqkv = f(inp["attn"]["Wqkv"])
+        attn = {"Wq": Wqkv[:w.d], "Wk": Wqkv[w.d:2 * w.d], "Wv": Wqkv[2 * w.d:], "Wo": f(inp["attn"]["Wo"])}
     E, Wt, h = f(inp["E"]), f(inp["W_t"]), f(inp["h"])
     kp = [f(x) for x in inp["k_prefix"]]
     vp = [f(x) for x in inp["v_prefix"]]
@@ -262,7 +268,7 @@ def cpu_baseline(inp, n_rows):
     while reps < 5 and total < 10.0:  # a bounded sample: whole rounds, about 10 s
         t0 = time.perf_counter()
         res = O.draft_heads(h, inp["root_tok"].numpy(), E, heads, plan, hydra=w.hydra, bf16=w.dtype == "bf16",
-                            full_path=w.cond == "path")
+                            full_path=w.cond == "path", attn=attn)
         if kind == "dense":
             trees = [O.prune_tree(plan, res["logp"][b], w.tree[2]) for b in range(w.B)]
         else:

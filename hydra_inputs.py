@@ -27,6 +27,7 @@ in this fixed order:
  11. two-layer heads only, per head k: Wa [d, d] (k = 1) or [H, 2d], ba, then
      (k > 1) Wb [d, H], bb, all ~ N(0, 0.02); LayerNorm gain 1 + N(0, 0.1) and
      bias N(0, 0.1) [d]; W2 [V, d] ~ N(0, 0.02)  (H = head_hidden, 1024)
+ 12. Hydra++ fusion only: Wqkv [3d, d], then Wo [d, d], ~ N(0, 0.02)
 
 Draws are float32; bfloat16 workloads round them to bfloat16 (round to
 nearest even, torch's conversion).
@@ -64,7 +65,7 @@ class Workload:
     zero_init: bool = False
     head: str = "mlp"     # "mlp" (one SiLU layer) | "sketch" (two-layer LayerNorm heads)
     head_hidden: int = 1024
-    cond: str = "parent"  # Hydra conditioning: "parent" token or the whole "path" from the root
+    cond: str = "parent"  # Hydra conditioning: "parent" token, the whole "path", or Hydra++ "attn" fusion
     extra: dict = field(default_factory=dict)
 
     @property
@@ -113,6 +114,10 @@ WORKLOADS = {
     "tiny_path": Workload("tiny_path", 7, "fp32", 1, 256, 1000, 3, True, ("cartesian", (2, 3)),
                           8, 8, 32, (128,), cond="path"),
     "7b_path": Workload("7b_path", 8, B=1, tree=_SPARSE, L=(2048,), cond="path", **_7B),
+    # Hydra++ self-attention fusion over the path embeddings
+    "tiny_attn": Workload("tiny_attn", 9, "fp32", 1, 256, 1000, 3, True, ("cartesian", (2, 3)),
+                          8, 8, 32, (128,), cond="attn"),
+    "7b_attn": Workload("7b_attn", 10, B=1, tree=_SPARSE, L=(2048,), cond="attn", **_7B),
     "70b_gqa": Workload("70b_gqa", 4, "bf16", 4, 8192, 32000, 4, True, _SPARSE,
                         64, 8, 128, (16384,), mode="stochastic", T=0.7),
 }
@@ -217,6 +222,8 @@ def generate(w: Workload, n_tree: int | None = None, reserve: int | None = None)
             hd["W2"] = _normal(g, (w.V, w.d), 0.02, dt)
             heads.append(hd)
         out["heads"] = heads
+    if w.cond == "attn":
+        out["attn"] = {"Wqkv": _normal(g, (3 * w.d, w.d), 0.02, dt), "Wo": _normal(g, (w.d, w.d), 0.02, dt)}
     return out
 
 

@@ -5,7 +5,8 @@
  * A round has four stages, one entry point each:
  *   hydra_draft_heads      draft heads + per-head top-k, filling the candidate tree
  *                          (hydra_draft_heads_sketch: the same with two-layer
- *                          LayerNorm heads)
+ *                          LayerNorm heads; hydra_draft_heads_attn: with
+ *                          Hydra++ self-attention fusion)
  *   tree_build             final tree (identity or pruned), ancestor table
  *   tree_attention_verify  tree-masked attention over a paged KV prefix
  *                          (tree_rope first rotates the tree Q/K rows at
@@ -214,6 +215,38 @@ int hydra_draft_heads_sketch(int dtype, int B, int d, int V, int hidden_dim, con
                              const int32_t* k_per_depth, float* head_logits, float* head_lse,
                              void* head_hidden, int32_t* cand_tok, float* cand_logp,
                              void* ws, size_t ws_bytes, void* stream);
+
+/* Stage 1 with Hydra++ self-attention fusion ([HG] "3. Hydra++: Enhanced
+ * Architectures and Knowledge Distillation": one causal self-attention layer
+ * over the candidate token embeddings). One layer shared by all heads, one
+ * attention head, no biases: at the node a head row expands, with path
+ * tokens t_0 .. t_{k-1} (root first) and x_j = emb[t_j],
+ *   q = Wq x_{k-1},  K_j = Wk x_j,  V_j = Wv x_j   (j <= k - 1, float32)
+ *   a = sum_j softmax_j(q . K_j / sqrt(d)) V_j     (stored in dtype)
+ *   c = x_{k-1} + Wo a                             (stored in dtype)
+ * and the one-layer Hydra head reads [h || c] in place of [h || e(parent)]:
+ * u = h + SiLU(W1_k [h || c] + b1_k) (residual = 1), z = W2_k u; the tree
+ * expansion, outputs and plan arguments are those of hydra_draft_heads
+ * (Hydra mode). Each node's K/V is computed once, when its own row runs,
+ * and kept in the workspace for its descendants.
+ *
+ * Wqkv     [3d, d] (dtype): rows of Wq, then Wk, then Wv
+ * Wo       [d, d] (dtype)
+ * W1, b1, W2, residual and the rest as in hydra_draft_heads (W1_k [d, 2d]).
+ * Supported: d <= 8192; bf16 needs d % 256 == 0. Errors as in
+ * hydra_draft_heads. */
+size_t hydra_draft_heads_attn_workspace_size(int dtype, int B, int d, int V, int N, int Dmax,
+                                             const int32_t* row_first);
+
+int hydra_draft_heads_attn(int dtype, int B, int d, int V, int residual, const void* h,
+                           const int32_t* root_tok, const void* emb, const void* Wqkv, const void* Wo,
+                           int n_heads, const void* const* W1, const void* const* b1,
+                           const void* const* W2, int N, int Dmax, const int32_t* node_parent,
+                           const int32_t* node_rank, const int32_t* node_row, int R,
+                           const int32_t* row_node, const int32_t* row_first, const int32_t* depth_first,
+                           const int32_t* k_per_depth, float* head_logits, float* head_lse,
+                           void* head_hidden, int32_t* cand_tok, float* cand_logp, void* ws,
+                           size_t ws_bytes, void* stream);
 
 /* Folded embedding table of one Hydra head, computed once per weight set:
  * out[t, n] = sum_j W1[n, d + j] * emb[t, j] for every token t, with W1 the

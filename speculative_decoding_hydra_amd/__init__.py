@@ -6,7 +6,8 @@ include/hydra.h, bound under the same names in
 of a round and calls them in order.
 """
 from .hydra import (  # noqa: F401
-    DevicePlan, HydraError, PlanRows, TreePlan, hydra_draft_heads, hydra_draft_heads_sketch,
+    DevicePlan, HydraError, PlanRows, TreePlan, hydra_draft_heads, hydra_draft_heads_attn,
+    hydra_draft_heads_attn_workspace_size, hydra_draft_heads_sketch,
     hydra_draft_heads_sketch_workspace_size, hydra_draft_heads_workspace_size,
     hydra_fold_embedding, hydra_plan_cartesian, hydra_plan_rows, hydra_plan_sparse, hydra_vocab_projection,
     hydra_vocab_projection_workspace_size, hydra_vocab_topk, tree_accept,

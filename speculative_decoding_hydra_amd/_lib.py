@@ -29,6 +29,11 @@ SIGNATURES = {
                                  + [C.POINTER(c_void)] * 7
                                  + [c_float, c_int, c_int, c_void, c_void, c_void, c_int, c_void, i32p, i32p, i32p,
                                     c_void, c_void, c_void, c_void, c_void, c_void, c_size, c_void]),
+    "hydra_draft_heads_attn_workspace_size": (c_size, [c_int, c_int, c_int, c_int, c_int, c_int, i32p]),
+    "hydra_draft_heads_attn": (c_int, [c_int, c_int, c_int, c_int, c_int, c_void, c_void, c_void, c_void, c_void,
+                                       c_int, C.POINTER(c_void), C.POINTER(c_void), C.POINTER(c_void), c_int, c_int,
+                                       c_void, c_void, c_void, c_int, c_void, i32p, i32p, i32p, c_void, c_void,
+                                       c_void, c_void, c_void, c_void, c_size, c_void]),
     "hydra_fold_embedding": (c_int, [c_int, c_int, c_int, c_void, c_void, c_void, c_void]),
     "hydra_vocab_projection_workspace_size": (c_size, [c_int, c_int, c_int]),
     "hydra_vocab_projection": (c_int, [c_int, c_int, c_int, c_int, c_int, c_void, c_void, c_void, c_void, c_size,

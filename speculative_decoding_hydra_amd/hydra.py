@@ -255,6 +255,43 @@ def hydra_draft_heads_sketch(h, root_tok, emb, heads, dplan: DevicePlan, head_lo
     return _check("hydra_draft_heads_sketch", rc)
 
 
+def hydra_draft_heads_attn_workspace_size(dtype_code, B, d, V, dplan: DevicePlan):
+    rf, rfp = _host_i32(dplan.rows.row_first)
+    return int(lib().hydra_draft_heads_attn_workspace_size(dtype_code, B, d, V, dplan.N, dplan.dmax, rfp))
+
+
+def hydra_draft_heads_attn(h, root_tok, emb, Wqkv, Wo, W1, b1, W2, dplan: DevicePlan, head_logits, head_lse,
+                           cand_tok, cand_logp, ws, head_hidden=None, residual=True, stream=None):
+    """Stage 1 with Hydra++ self-attention fusion (see include/hydra.h).
+    Wqkv [3d, d] (Wq, Wk, Wv rows), Wo [d, d]; W1/b1/W2 as hydra_draft_heads."""
+    if not dplan.hydra:
+        raise ValueError("self-attention fusion reads the candidate embeddings: the plan must be a Hydra plan")
+    dt = _dtype_code(h)
+    B, d = h.shape
+    V = W2[0].shape[0]
+    n_heads = len(W2)
+    if not (len(W1) == len(b1) == n_heads):
+        raise ValueError("W1, b1 and W2 need one entry per head")
+    arr = C.c_void_p * n_heads
+    w1 = arr(*[_dev(w, "W1", h.dtype) for w in W1])
+    bb = arr(*[_dev(w, "b1", h.dtype) for w in b1])
+    w2 = arr(*[_dev(w, "W2", h.dtype) for w in W2])
+    rows = dplan.rows
+    rf, rfp = _host_i32(rows.row_first)
+    df, dfp = _host_i32(rows.depth_first)
+    kp, kpp = _host_i32(rows.k_per_depth)
+    wsp, wsb = _ws(ws)
+    rc = lib().hydra_draft_heads_attn(
+        dt, B, d, V, int(bool(residual)), _dev(h, "h"), _dev(root_tok, "root_tok", torch.int32),
+        _dev(emb, "emb", h.dtype), _dev(Wqkv, "Wqkv", h.dtype), _dev(Wo, "Wo", h.dtype), n_heads, w1, bb, w2,
+        dplan.N, dplan.dmax, _dev(dplan.parent, "parent"), _dev(dplan.rank, "rank"), _dev(dplan.node_row, "node_row"),
+        dplan.R, _dev(dplan.row_node, "row_node"), rfp, dfp, kpp, _dev(head_logits, "head_logits", torch.float32),
+        _dev(head_lse, "head_lse", torch.float32), _dev(head_hidden, "head_hidden", h.dtype),
+        _dev(cand_tok, "cand_tok", torch.int32), _dev(cand_logp, "cand_logp", torch.float32), wsp, wsb,
+        _stream(stream))
+    return _check("hydra_draft_heads_attn", rc)
+
+
 def hydra_fold_embedding(emb, W1, out, stream=None):
     """out[t, n] = sum_j W1[n, d + j] * emb[t, j] (see include/hydra.h):
     emb [V, d] and W1 [d, 2d] bf16, out [V, d] float32."""

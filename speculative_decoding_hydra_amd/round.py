@@ -32,7 +32,10 @@ class HydraRound:
 
     weights: dict with emb [V, d] (Hydra), W1/b1/W2 lists, W_t [V, d]; or,
     for the two-layer LayerNorm heads (hydra_draft_heads_sketch), ``heads``:
-    one dict per head (Wa, ba, [Wb, bb,] ln_g, ln_b, W2) instead of W1/b1/W2.
+    one dict per head (Wa, ba, [Wb, bb,] ln_g, ln_b, W2) instead of W1/b1/W2;
+    with ``attn`` (dict of Wqkv [3d, d] and Wo [d, d]) the Hydra heads read
+    Hydra++ self-attention fusion of the path embeddings
+    (hydra_draft_heads_attn).
     shape: dict with B, d, V, Hq, Hkv, D, max_prefix_len.
     fold_embedding: build the folded embedding tables of the Hydra heads
     (hydra_fold_embedding, V * d * 4 bytes per head) once here and let the
@@ -85,7 +88,10 @@ class HydraRound:
         nb = lambda n: torch.empty(max(int(n), 1), dtype=torch.uint8, device=device)  # noqa: E731
         self.sketch = weights.get("heads") is not None
         self.full_path = bool(full_path)
-        if self.sketch:
+        self.attn = weights.get("attn")
+        if self.attn is not None:
+            self.ws_draft = nb(H.hydra_draft_heads_attn_workspace_size(code, B, d, V, self.dplan))
+        elif self.sketch:
             hid = weights["heads"][1]["Wa"].shape[0] if len(weights["heads"]) > 1 else d
             self.ws_draft = nb(H.hydra_draft_heads_sketch_workspace_size(code, B, d, V, hid, self.dplan))
         else:
@@ -97,6 +103,7 @@ class HydraRound:
         self.ws_accept = nb(H.tree_accept_workspace_size(self.mode, B, K, V))
         if fold_embedding is None:
             fold_embedding = hydra and dt == torch.bfloat16 and not self.sketch and not self.full_path
+            fold_embedding = fold_embedding and self.attn is None
         self.emb_proj = None
         if fold_embedding:
             self.emb_proj = [z(V, d) for _ in weights["W1"]]
@@ -104,6 +111,12 @@ class HydraRound:
                 H.hydra_fold_embedding(weights["emb"], w1, t)
 
     def draft(self, h, root_tok, stream=None):
+        if self.attn is not None:
+            H.hydra_draft_heads_attn(h, root_tok, self.w["emb"], self.attn["Wqkv"], self.attn["Wo"], self.w["W1"],
+                                     self.w["b1"], self.w["W2"], self.dplan, self.head_logits, self.head_lse,
+                                     self.cand_tok, self.cand_logp, self.ws_draft, head_hidden=self.head_hidden,
+                                     residual=self.residual, stream=stream)
+            return
         if self.sketch:
             H.hydra_draft_heads_sketch(h, root_tok, self.w["emb"], self.w["heads"], self.dplan, self.head_logits,
                                        self.head_lse, self.cand_tok, self.cand_logp, self.ws_draft,
@@ -164,6 +177,8 @@ def round_from_inputs(inp, device="cuda", keep_hidden=True, fold_embedding=None,
     w = inp["workload"]
     to = lambda t: t.to(device).contiguous()  # noqa: E731
     weights = dict(emb=to(inp["E"]) if w.hydra else None, W_t=to(inp["W_t"]))
+    if w.cond == "attn":
+        weights["attn"] = {n: to(t) for n, t in inp["attn"].items()}
     if w.head == "sketch":
         weights["heads"] = [{n: to(t) for n, t in hd.items()} for hd in inp["heads"]]
     else:

@@ -106,6 +106,47 @@ def sketch_u_slack(x, head):
     return rstd * np.abs(head["ln_g"]) * shift
 
 
+def _bf16_step(v):
+    return np.ldexp(1.0, np.frexp(np.maximum(np.abs(v), 1e-30))[1] - 8)
+
+
+def attn_u_slack(X, attn, W1):
+    """Extra slack on a bf16 Hydra++ head's u. The attention output a and
+    c = x + Wo a are rounded before use, so a one-step flip of a_l (where
+    device and oracle fall on two sides of a rounding midpoint) moves c_i by
+    Wo_il step_l, and a flip of c_i moves W1's sum by W1_ji step_i. A value
+    perturbed with standard deviation sigma, at a uniform place in its
+    rounding cell, flips with probability about 0.8 sigma / step; flips are
+    independent with random signs, so each stage's perturbation has variance
+    sum (weight * step)^2 * P(flip), and the slack is four standard
+    deviations of W1's sum (times 1.1 >= |SiLU'|). The float32 error of a
+    K-term sum has standard deviation about 2^-24 sqrt(K / 2) sqrt(sum terms^2)."""
+    X = np.asarray(X)
+    d = X.shape[1]
+    u32 = 2.0 ** -24 * math.sqrt(d / 2)
+    q, K, Vv = attn["Wq"] @ X[-1], X @ attn["Wk"].T, X @ attn["Wv"].T
+    sc = K @ q / math.sqrt(d)
+    p = np.exp(sc - sc.max())
+    p /= p.sum()
+    a = p @ Vv
+    sd_a = u32 * np.sqrt((attn["Wv"] ** 2) @ (X ** 2).max(axis=0))
+    step_a = _bf16_step(a)
+    pf_a = np.minimum(1.0, 0.8 * sd_a / step_a)
+    ar = O.round_bf16(a)
+    c = X[-1] + attn["Wo"] @ ar
+    var_c = (attn["Wo"] ** 2) @ (step_a ** 2 * pf_a) + (u32 ** 2) * ((attn["Wo"] ** 2) @ (ar ** 2))
+    step_c = _bf16_step(c)
+    pf_c = np.minimum(1.0, 0.8 * np.sqrt(var_c) / step_c)
+    return 1.1 * 4.0 * np.sqrt((W1[:, d:] ** 2) @ (step_c ** 2 * pf_c))
+
+
+def oracle_attn(inp):
+    """The Hydra++ fusion weights of an input dict, as the oracle takes them."""
+    Wqkv = HI.as_f64(inp["attn"]["Wqkv"])
+    d = Wqkv.shape[1]
+    return {"Wq": Wqkv[:d], "Wk": Wqkv[d:2 * d], "Wv": Wqkv[2 * d:], "Wo": HI.as_f64(inp["attn"]["Wo"])}
+
+
 def check_draft(inp, rnd, seqs=None, rows=None):
     """Stage 1, stage-wise. Returns max errors."""
     w = inp["workload"]
@@ -132,6 +173,7 @@ def check_draft(inp, rnd, seqs=None, rows=None):
     rows = range(len(row_node)) if rows is None else rows
     err = dict(u=0.0, z=0.0, lse=0.0, logp=0.0, flips=0)
     sketch = getattr(w, "head", "mlp") == "sketch"
+    attn_w = oracle_attn(inp) if getattr(w, "cond", "parent") == "attn" else None
     W1c, W2c = {}, {}
     for r in rows:
         k = int(row_depth[r])
@@ -148,7 +190,10 @@ def check_draft(inp, rnd, seqs=None, rows=None):
             e = None
             if w.hydra:
                 p = int(row_node[r])
-                if getattr(w, "cond", "parent") == "path":
+                if getattr(w, "cond", "parent") == "attn":
+                    toks = O.path_tokens(plan, ctok[b], int(inp["root_tok"][b]), p)
+                    e = O.path_attention(np.stack([HI.as_f64(inp["E"][t]) for t in toks]), attn_w, bf16)
+                elif getattr(w, "cond", "parent") == "path":
                     toks = O.path_tokens(plan, ctok[b], int(inp["root_tok"][b]), p)
                     e = np.concatenate([HI.as_f64(inp["E"][t]) for t in toks])
                 else:
@@ -168,6 +213,12 @@ def check_draft(inp, rnd, seqs=None, rows=None):
                 if sketch:
                     x = h[b] if k == 1 else np.concatenate([h[b], e])
                     lim = lim + sketch_u_slack(x, W1)
+                elif attn_w is not None:
+                    extra = attn_u_slack(np.stack([HI.as_f64(inp["E"][t]) for t in toks]), attn_w, W1)
+                    lim = lim + extra
+                    # expected flips of u under the same model (sigma = extra / 4.4)
+                    err["u_flips_model"] = err.get("u_flips_model", 0.0) + float(
+                        np.sum(np.minimum(1.0, 0.8 * (extra / 4.4) / ulp)))
                 bad = diff > lim
                 j = int(np.argmax(diff / lim))
                 assert not bad.any(), (f"seq {b} row {r}: u[{j}] = {hidden[b, r][j]!r} vs oracle {u[j]!r} "
@@ -198,8 +249,12 @@ def check_draft(inp, rnd, seqs=None, rows=None):
         # two-layer heads round twice: a flip in the SiLU output moves Wb a by
         # ~1e-4 relative, enough to move about 1 in 40 of that row's u across
         # a bf16 rounding boundary (one step, which the check above bounds)
-        allowed = 0.05 if sketch else 0.01
-        assert err["u_flips"] <= allowed * err["u_elems"], f"{err['u_flips']} rounding flips in u"
+        # (Hydra++ fusion rounds a and c first: the same effect through W1)
+        # Hydra++: at d = 8192 the flips of c flip several percent of u; allow
+        # twice the model's expectation on top of the one-layer 1%
+        model = min(2 * err.get("u_flips_model", 0.0), 0.15 * err["u_elems"])
+        allowed = 0.05 * err["u_elems"] if sketch else 0.01 * err["u_elems"] + model
+        assert err["u_flips"] <= allowed, f"{err['u_flips']} rounding flips in u (allowed {allowed:.0f})"
     assert err["z"] <= t, f"head logits max-abs {err['z']:.3g} > {t}"
     assert err["lse"] <= t and err["logp"] <= t, (err["lse"], err["logp"])
     for b in seqs:

@@ -242,7 +242,7 @@ def _round(name, **over):
     return _cache[key]
 
 
-@pytest.mark.parametrize("name", ["tiny", "tiny_medusa", "tiny_sketch", "tiny_path"])
+@pytest.mark.parametrize("name", ["tiny", "tiny_medusa", "tiny_sketch", "tiny_path", "tiny_attn"])
 def test_tiny_round_stagewise(name):
     inp, rnd, dev = _round(name)
     rep = T.oracle_round_checks(inp, rnd)
@@ -250,7 +250,7 @@ def test_tiny_round_stagewise(name):
     print(rep, flush=True)
 
 
-@pytest.mark.parametrize("name", ["tiny", "tiny_medusa", "tiny_sketch", "tiny_path"])
+@pytest.mark.parametrize("name", ["tiny", "tiny_medusa", "tiny_sketch", "tiny_path", "tiny_attn"])
 def test_tiny_round_end_to_end(name):
     """Float32 workload: the oracle's own round from the inputs alone."""
     inp, rnd, _ = _round(name)
@@ -262,7 +262,7 @@ def test_tiny_round_end_to_end(name):
     else:
         heads = [(f(a), f(b), f(c)) for a, b, c in zip(inp["W1"], inp["b1"], inp["W2"])]
     res = O.draft_heads(f(inp["h"]), inp["root_tok"].numpy(), f(inp["E"]), heads, plan, hydra=w.hydra,
-                        full_path=w.cond == "path")
+                        full_path=w.cond == "path", attn=T.oracle_attn(inp) if w.cond == "attn" else None)
     for r in range(res["z"].shape[1]):
         assert res["margin"][0, r] > T.MARGIN, "near tie: seed would need the margin rule"
     assert np.array_equal(res["tok"], rnd.cand_tok.cpu().numpy())
@@ -499,6 +499,36 @@ def test_full_path_heads_stagewise(B, d, V, tree):
     T.run_round(rnd, dev)
     torch.cuda.synchronize()
     rep = T.check_draft(inp, rnd)
+    print(rep, flush=True)
+
+
+@pytest.mark.parametrize("B,d,V,tree", [
+    (3, 256, 1000, ("cartesian", (4, 3, 2))),
+    (2, 8192, 2000, ("cartesian", (10, 2))),            # 70B width: 8 columns per thread in the path attention
+    (20, 512, 1000, ("sparse", (10, 4, 2, 1), 64)),     # 200 rows at depth 2: tiled products
+    (1, 256, 777, ("cartesian", (2, 2, 2, 2, 2, 2, 1, 1))),  # eight heads: the deepest path, ragged vocabulary
+])
+def test_hydra_pp_heads_stagewise(B, d, V, tree):
+    """Hydra++ self-attention fusion in bf16 against the oracle stage by
+    stage: each row attends over its own path's embeddings, keys and values
+    of the ancestors coming from the rows of earlier depths."""
+    w = HI.workload("7b_attn", B=B, d=d, V=V, tree=tree, n_heads=len(tree[1]), Hq=8, Hkv=8, D=32, L=(64,))
+    print(f"Hydra++ heads B={B} d={d} V={V} tree={tree}", flush=True)
+    inp = HI.generate(w)
+    rnd, dev = T.round_inputs(inp)
+    assert rnd.attn is not None and rnd.emb_proj is None
+    T.run_round(rnd, dev)
+    torch.cuda.synchronize()
+    rep = T.check_draft(inp, rnd)
+    print(rep, flush=True)
+
+
+def test_hydra_pp_7b_round():
+    """Whole round with Hydra++ heads at the 7B shape, every stage plus the
+    commit."""
+    inp, rnd, dev = _round("7b_attn")
+    rep = T.oracle_round_checks(inp, rnd)
+    rep.update(T.check_commit(inp, rnd, dev))
     print(rep, flush=True)
 
 

@@ -16,9 +16,10 @@
 // float32 cache for its descendants. Per depth k:
 //   1. gather x_{k-1} = E[token] of each row's node,
 //   2. one split-K product with [Wq; Wk; Wv] ([3d, d]),
-//   3. path_attend: one workgroup per row sums the partials, stores the
-//      node's K/V, scores the path (k dot products of length d) and writes
-//      the attention output a (rounded to the storage type),
+//   3. path_scores / path_values: workgroups of 256 columns of a row sum the
+//      partials, store the node's K/V and leave their share of the k dot
+//      products; then each takes the row's softmax over the path and writes
+//      its columns of the attention output a (rounded to the storage type),
 //   4. Wo a, then c = x_{k-1} + Wo a written next to h as [h || c],
 //   5. W1 over [h || c] and the head epilogue, then W2 and the merge of the
 //      one-layer path.
@@ -27,8 +28,7 @@
 namespace hydra {
 namespace {
 
-constexpr int kAttnThreads = 1024;
-constexpr int kAttnPer = 8;  // columns per thread: d <= 8192
+constexpr int kMaxWidth = 8192;  // d
 
 template <class T>
 __global__ __launch_bounds__(256) void gather_rows(int d, int P, int r0, int N, int V, const T* __restrict__ emb,
@@ -56,90 +56,96 @@ __device__ __forceinline__ float sum_parts(const float* __restrict__ p, int ns, 
   return v;
 }
 
-// One row (expanded node at depth k - 1) per workgroup. qkv partials are
-// [ns][M][3d]; Kc, Vc are [B, N, d] float32 node caches.
-template <class T>
-__global__ __launch_bounds__(kAttnThreads) void path_attend(int d, int k, int P, int r0, int N, int ns, size_t stride,
-                                                            const float* __restrict__ qkv,
-                                                            const int32_t* __restrict__ row_node,
-                                                            const int32_t* __restrict__ parent, float* __restrict__ Kc,
-                                                            float* __restrict__ Vc, T* __restrict__ A) {
+constexpr int kChunk = 256;  // columns per workgroup of the path attention
+
+// The path attention in two launches over (column chunk, row) workgroups, so
+// that a row's 3d partial sums and k cached keys and values are read by d/256
+// CUs instead of one.
+// Scores: sums the [Wq; Wk; Wv] partials ([ns][M][3d]) of this chunk, stores
+// the node's K and V in the [B, N, d] float32 caches, and leaves this
+// chunk's share of q . K_j for every path position in S[m][chunk][j]; the
+// chunk-0 workgroup also leaves the path (root first) in path[m][j].
+__global__ __launch_bounds__(kChunk) void path_scores(int d, int k, int P, int r0, int N, int ns, size_t stride,
+                                                      const float* __restrict__ qkv,
+                                                      const int32_t* __restrict__ row_node,
+                                                      const int32_t* __restrict__ parent, float* __restrict__ Kc,
+                                                      float* __restrict__ Vc, float* __restrict__ S,
+                                                      int32_t* __restrict__ path) {
   __shared__ int anc[HYDRA_MAX_DEPTH + 1];
-  __shared__ float red[kAttnThreads / 64][HYDRA_MAX_DEPTH + 1];
-  const int m = blockIdx.x, b = m / P;
+  __shared__ float red[kChunk / 64][HYDRA_MAX_DEPTH + 1];
+  const int chunk = blockIdx.x, m = blockIdx.y, b = m / P;
+  const int nchunk = gridDim.x;
   const int node = row_node[r0 + m % P];
-  if (threadIdx.x == 0) {  // the path, root first: anc[k - 1] = node
+  if (threadIdx.x == 0) {
     int a = node;
     for (int j = k - 1; j >= 0; --j) {
       anc[j] = a;
       a = a > 0 ? parent[a] : 0;
     }
   }
+  const int c = chunk * kChunk + threadIdx.x;
+  const bool on = c < d;
   const size_t row = static_cast<size_t>(m) * 3 * d;
-  float q[kAttnPer], kv[kAttnPer], vv[kAttnPer];
-  const size_t nb = (static_cast<size_t>(b) * N + node) * d;
-#pragma unroll
-  for (int i = 0; i < kAttnPer; ++i) {
-    const int c = threadIdx.x + i * kAttnThreads;
-    q[i] = kv[i] = vv[i] = 0.f;
-    if (c < d) {
-      q[i] = sum_parts(qkv, ns, stride, row + c);
-      kv[i] = sum_parts(qkv, ns, stride, row + d + c);
-      vv[i] = sum_parts(qkv, ns, stride, row + 2 * d + c);
-      Kc[nb + c] = kv[i];
-      Vc[nb + c] = vv[i];
-    }
+  float q = 0.f, kv = 0.f;
+  if (on) {
+    q = sum_parts(qkv, ns, stride, row + c);
+    kv = sum_parts(qkv, ns, stride, row + d + c);
+    const float vv = sum_parts(qkv, ns, stride, row + 2 * d + c);
+    const size_t nb = (static_cast<size_t>(b) * N + node) * d;
+    Kc[nb + c] = kv;
+    Vc[nb + c] = vv;
   }
   __syncthreads();
-  // scores: this thread's share of q . K_j for every path position (loops
-  // over j are unrolled to the maximum depth so the arrays stay in registers)
-  float sc[HYDRA_MAX_DEPTH + 1];
+  if (chunk == 0 && threadIdx.x < k) path[m * (HYDRA_MAX_DEPTH + 1) + threadIdx.x] = anc[threadIdx.x];
 #pragma unroll
   for (int j = 0; j <= HYDRA_MAX_DEPTH; ++j) {
-    sc[j] = 0.f;
     if (j < k) {  // uniform over the workgroup
-      const float* kj = Kc + (static_cast<size_t>(b) * N + anc[j]) * d;
-      float s = 0.f;
-#pragma unroll
-      for (int i = 0; i < kAttnPer; ++i) {
-        const int c = threadIdx.x + i * kAttnThreads;
-        if (c < d) s += q[i] * (j == k - 1 ? kv[i] : kj[c]);  // the node's own key from registers
-      }
-      s = wave_sum(s);
-      if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6][j] = s;
+      float t = 0.f;
+      if (on) t = q * (j == k - 1 ? kv : Kc[(static_cast<size_t>(b) * N + anc[j]) * d + c]);
+      t = wave_sum(t);
+      if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6][j] = t;
     }
   }
   __syncthreads();
-  float mx = -INFINITY;
-  const float scale = 1.0f / sqrtf(static_cast<float>(d));
+  if (threadIdx.x < k) {
+    float t = 0.f;
 #pragma unroll
-  for (int j = 0; j <= HYDRA_MAX_DEPTH; ++j) {
+    for (int w = 0; w < kChunk / 64; ++w) t += red[w][threadIdx.x];
+    S[(static_cast<size_t>(m) * nchunk + chunk) * (HYDRA_MAX_DEPTH + 1) + threadIdx.x] = t;
+  }
+}
+
+// Values: the scores of the row (chunk shares summed in a fixed order, in
+// float64), softmax over the path, and a = sum_j p_j V_j for this chunk.
+template <class T>
+__global__ __launch_bounds__(kChunk) void path_values(int d, int k, int N, int P, const float* __restrict__ S,
+                                                      const int32_t* __restrict__ path,
+                                                      const float* __restrict__ Vc, T* __restrict__ A) {
+  __shared__ float p[HYDRA_MAX_DEPTH + 1];
+  const int chunk = blockIdx.x, m = blockIdx.y, b = m / P;
+  const int nchunk = gridDim.x;
+  if (threadIdx.x < 64) {  // one wave: lane j < k sums position j's shares
+    const int j = threadIdx.x;
+    float sc = -INFINITY;
     if (j < k) {
       double t = 0.0;
-      for (int w = 0; w < kAttnThreads / 64; ++w) t += red[w][j];
-      sc[j] = static_cast<float>(t) * scale;
-      mx = fmaxf(mx, sc[j]);
+      for (int ch = 0; ch < nchunk; ++ch) t += S[(static_cast<size_t>(m) * nchunk + ch) * (HYDRA_MAX_DEPTH + 1) + j];
+      sc = static_cast<float>(t) / sqrtf(static_cast<float>(d));
     }
+    const float mx = wave_max(sc);
+    const float e = j < k ? expf(sc - mx) : 0.f;
+    const float den = wave_sum(e);
+    if (j < k) p[j] = e / den;
   }
-  float den = 0.f;
+  __syncthreads();
+  const int c = chunk * kChunk + threadIdx.x;
+  if (c >= d) return;
+  const int32_t* pr = path + m * (HYDRA_MAX_DEPTH + 1);
+  float a = 0.f;
 #pragma unroll
-  for (int j = 0; j <= HYDRA_MAX_DEPTH; ++j) {
-    if (j < k) {
-      sc[j] = expf(sc[j] - mx);
-      den += sc[j];
-    }
-  }
-  const float inv = 1.0f / den;
-#pragma unroll
-  for (int i = 0; i < kAttnPer; ++i) {
-    const int c = threadIdx.x + i * kAttnThreads;
-    if (c >= d) continue;
-    float a = 0.f;
-#pragma unroll
-    for (int j = 0; j <= HYDRA_MAX_DEPTH; ++j)
-      if (j < k) a += sc[j] * (j == k - 1 ? vv[i] : Vc[(static_cast<size_t>(b) * N + anc[j]) * d + c]);
-    store_f(A, static_cast<size_t>(m) * d + c, a * inv);
-  }
+  for (int j = 0; j <= HYDRA_MAX_DEPTH; ++j)
+    if (j < k) a += p[j] * Vc[(static_cast<size_t>(b) * N + pr[j]) * d + c];
+  store_f(A, static_cast<size_t>(m) * d + c, a);
 }
 
 // [h_b || c] with c = T(x + sum of the Wo partials), x the gathered e row
@@ -173,7 +179,7 @@ __global__ __launch_bounds__(256) void head_epilogue(int M, int d, int P, int ns
 }
 
 struct AttnWs {
-  size_t part, x, a, x2, u, kc, vc, keys, ms, total;
+  size_t part, x, a, x2, u, kc, vc, sc, path, keys, ms, total;
 };
 AttnWs attn_ws(int dtype, int B, int d, int V, int N, int Dmax, const int32_t* row_first) {
   int maxP = 0;
@@ -189,10 +195,18 @@ AttnWs attn_ws(int dtype, int B, int d, int V, int N, int Dmax, const int32_t* r
   w.u = align_up(M * d * esz, 256);
   w.kc = align_up(static_cast<size_t>(B) * N * d * sizeof(float), 256);
   w.vc = w.kc;
+  w.sc = align_up(M * ((d + kChunk - 1) / kChunk) * (HYDRA_MAX_DEPTH + 1) * sizeof(float), 256);
+  w.path = align_up(M * (HYDRA_MAX_DEPTH + 1) * sizeof(int32_t), 256);
   w.keys = align_up(M * nwg * sizeof(uint64_t), 256);
   w.ms = align_up(M * nwg * sizeof(float2), 256);
-  w.total = w.part + w.x + w.a + w.x2 + w.u + w.kc + w.vc + w.keys + w.ms + 256;
+  w.total = w.part + w.x + w.a + w.x2 + w.u + w.kc + w.vc + w.sc + w.path + w.keys + w.ms + 256;
   return w;
+}
+
+bool M_ok(int B, int Dmax, const int32_t* row_first) {
+  for (int k = 1; k <= Dmax; ++k)
+    if (static_cast<long long>(B) * (row_first[k] - row_first[k - 1]) > 65535) return false;
+  return true;
 }
 
 int grid_for(size_t total) { return static_cast<int>(std::min<size_t>((total + 255) / 256, 4096)); }
@@ -221,8 +235,7 @@ extern "C" int hydra_draft_heads_attn(int dtype, int B, int d, int V, int residu
   hipStream_t stream = static_cast<hipStream_t>(stream_);
   HY_CHECK(dtype == HYDRA_F32 || dtype == HYDRA_BF16, HYDRA_ERR_INVALID, "draft_heads_attn: bad dtype %d", dtype);
   HY_CHECK(B > 0 && d > 0 && V > 0, HYDRA_ERR_INVALID, "draft_heads_attn: bad sizes B=%d d=%d V=%d", B, d, V);
-  HY_CHECK(d <= kAttnThreads * kAttnPer, HYDRA_ERR_UNSUPPORTED, "draft_heads_attn: d=%d > %d", d,
-           kAttnThreads * kAttnPer);
+  HY_CHECK(d <= kMaxWidth, HYDRA_ERR_UNSUPPORTED, "draft_heads_attn: d=%d > %d", d, kMaxWidth);
   HY_CHECK(dtype == HYDRA_F32 || d % 256 == 0, HYDRA_ERR_UNSUPPORTED, "draft_heads_attn: bf16 needs d %% 256 == 0");
   HY_CHECK(Dmax >= 1 && Dmax <= HYDRA_MAX_DEPTH, HYDRA_ERR_INVALID, "draft_heads_attn: Dmax=%d out of [1, %d]", Dmax,
            HYDRA_MAX_DEPTH);
@@ -245,6 +258,7 @@ extern "C" int hydra_draft_heads_attn(int dtype, int B, int d, int V, int residu
              HYDRA_MAX_TOPK);
     HY_CHECK(W1[k - 1] && b1[k - 1] && W2[k - 1], HYDRA_ERR_INVALID, "draft_heads_attn: null weight of head %d", k);
   }
+  HY_CHECK(M_ok(B, Dmax, row_first), HYDRA_ERR_UNSUPPORTED, "draft_heads_attn: more than 65535 rows at one depth");
   const size_t need = hydra_draft_heads_attn_workspace_size(dtype, B, d, V, N, Dmax, row_first);
   HY_CHECK(ws && ws_bytes >= need, HYDRA_ERR_WORKSPACE, "draft_heads_attn: workspace %zu < required %zu", ws_bytes,
            need);
@@ -258,6 +272,8 @@ extern "C" int hydra_draft_heads_attn(int dtype, int B, int d, int V, int residu
   char* U = arena.take<char>(wl.u);
   float* Kc = arena.take<float>(wl.kc / sizeof(float));
   float* Vc = arena.take<float>(wl.vc / sizeof(float));
+  float* Sc = arena.take<float>(wl.sc / sizeof(float));
+  int32_t* pathb = arena.take<int32_t>(wl.path / sizeof(int32_t));
   uint64_t* tkeys = arena.take<uint64_t>(wl.keys / sizeof(uint64_t));
   float2* tms = arena.take<float2>(wl.ms / sizeof(float2));
   const size_t pf = wl.part / sizeof(float);
@@ -281,13 +297,14 @@ extern "C" int hydra_draft_heads_attn(int dtype, int B, int d, int V, int residu
     if (rc != HYDRA_OK) return rc;
     // 3. causal attention over the path
     const size_t stride = static_cast<size_t>(M) * 3 * d;
+    const dim3 grid((d + kChunk - 1) / kChunk, M);
+    path_scores<<<grid, kChunk, 0, stream>>>(d, k, P, r0, N, ns, stride, part, row_node, node_parent, Kc, Vc, Sc, pathb);
+    HY_LAUNCH_CHECK("draft_heads_attn: path scores");
     if (f32)
-      path_attend<float><<<M, kAttnThreads, 0, stream>>>(d, k, P, r0, N, ns, stride, part, row_node, node_parent, Kc,
-                                                         Vc, reinterpret_cast<float*>(Ab));
+      path_values<float><<<grid, kChunk, 0, stream>>>(d, k, N, P, Sc, pathb, Vc, reinterpret_cast<float*>(Ab));
     else
-      path_attend<bf16_t><<<M, kAttnThreads, 0, stream>>>(d, k, P, r0, N, ns, stride, part, row_node, node_parent, Kc,
-                                                          Vc, reinterpret_cast<bf16_t*>(Ab));
-    HY_LAUNCH_CHECK("draft_heads_attn: path attention");
+      path_values<bf16_t><<<grid, kChunk, 0, stream>>>(d, k, N, P, Sc, pathb, Vc, reinterpret_cast<bf16_t*>(Ab));
+    HY_LAUNCH_CHECK("draft_heads_attn: path values");
     // 4. c = x + Wo a, next to h
     rc = launch_projection_parts(dtype, M, d, d, Ab, Wo, part, pf, &ns, stream);
     if (rc != HYDRA_OK) return rc;

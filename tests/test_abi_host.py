@@ -218,3 +218,45 @@ def test_draft_heads_sketch_rejects_bad_arguments_before_any_launch(lib):
 class _Plan:
     def __init__(self, rows):
         self.rows, self.dmax = rows, 2
+
+
+def test_draft_heads_attn_and_modes_reject_bad_arguments_before_any_launch(lib):
+    """Host-side checks of hydra_draft_heads_attn and of hydra_draft_heads'
+    hydra mode (2 = full path); fake device addresses are never touched."""
+    import speculative_decoding_hydra_amd as S
+
+    plan = S.hydra_plan_cartesian([2, 3])
+    rows = S.hydra_plan_rows(plan, True)
+    I32 = C.POINTER(C.c_int32)
+    host = lambda a: (C.c_int32 * len(a))(*[int(x) for x in a])  # noqa: E731
+    rf, df, kp = host(rows.row_first), host(rows.depth_first), host(rows.k_per_depth)
+    p = [4096 * (i + 1) for i in range(40)]
+    arr = C.c_void_p * 2
+    ip = lambda a: C.cast(C.c_void_p(a), I32)  # noqa: E731
+    plan_args = (plan.n, 2, p[3], p[4], p[5], len(rows.row_node), p[6], C.cast(rf, I32), C.cast(df, I32),
+                 C.cast(kp, I32))
+
+    def attn(dtype=1, d=256, Wo=None, ws_bytes=1 << 30):
+        return lib.hydra_draft_heads_attn(dtype, 1, d, 1000, 1, p[0], ip(p[1]), p[2], p[30], Wo or p[31], 2,
+                                          arr(p[10], p[11]), arr(p[12], p[13]), arr(p[14], p[15]), *plan_args,
+                                          p[7], p[8], None, p[9], p[23], p[24], ws_bytes, None)
+
+    assert attn(dtype=5) == -1
+    assert attn(d=300) == -2                        # bf16 needs d % 256 == 0
+    assert attn(dtype=0, d=9000) == -2              # d <= 8192
+    assert attn(ws_bytes=16) == -3
+    assert S.hydra_draft_heads_attn_workspace_size(1, 1, 256, 1000, _Plan2(rows, plan.n)) >= 2 * 6 * 256 * 4
+
+    def heads(mode, d=256):
+        return lib.hydra_draft_heads(1, 1, d, 1000, mode, 1, p[0], ip(p[1]), p[2], None, 2, arr(p[10], p[11]),
+                                     arr(p[12], p[13]), arr(p[14], p[15]), *plan_args, p[7], p[8], None, p[9],
+                                     p[23], p[24], 1 << 30, None)
+
+    assert heads(3) == -1                           # modes are 0, 1, 2
+    assert b"hydra mode" in lib.hydra_last_error()
+    assert heads(2, d=300) == -2                    # full path in bf16 needs d % 256 == 0
+
+
+class _Plan2:
+    def __init__(self, rows, n):
+        self.rows, self.dmax, self.N = rows, 2, n

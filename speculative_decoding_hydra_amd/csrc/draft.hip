@@ -160,6 +160,8 @@ extern "C" int hydra_draft_heads(int dtype, int B, int d, int V, int hydra_mode,
     HY_CHECK(W1[k - 1] && b1[k - 1] && W2[k - 1], HYDRA_ERR_INVALID, "draft_heads: null weight of head %d", k);
     HY_CHECK(hydra_mode || row_first[k] - row_first[k - 1] == 1, HYDRA_ERR_INVALID,
              "draft_heads: Medusa mode has one row per depth");
+    HY_CHECK(hydra_mode != 2 || static_cast<long long>(B) * (row_first[k] - row_first[k - 1]) <= 65535,
+             HYDRA_ERR_UNSUPPORTED, "draft_heads: full path takes at most 65535 rows per depth");
   }
   const size_t need = hydra_draft_heads_workspace_size(dtype, B, d, V, hydra_mode, Dmax, row_first);
   HY_CHECK(ws_bytes >= need && (need == 0 || ws), HYDRA_ERR_WORKSPACE,

@@ -340,6 +340,13 @@ int tree_rope(int dtype, int B, int N, int H, int D, const void* x, void* out,
               const int32_t* depth, const int32_t* prefix_len, float theta,
               void* stream);
 
+/* tree_rope of the tree Q rows [B, N, Hq, D] and K rows [B, N, Hkv, D] in one
+ * launch, each value exactly as tree_rope computes it (q_out may equal q and
+ * k_out may equal k). Same limits and errors as tree_rope. */
+int tree_rope_qk(int dtype, int B, int N, int Hq, int Hkv, int D, const void* q, void* q_out,
+                 const void* k, void* k_out, const int32_t* depth, const int32_t* prefix_len, float theta,
+                 void* stream);
+
 /* ------------------------------------------------------------------------
  * Stage 3: tree-masked attention verify (one attention layer's share)
  *

@@ -43,6 +43,8 @@ SIGNATURES = {
     "tree_build": (c_int, [c_int, c_int, c_int, c_void, c_void, c_void, c_void, c_void, c_void, c_int,
                            c_void, c_void, c_void, c_void, c_void, c_void, c_void, c_size, c_void]),
     "tree_rope": (c_int, [c_int, c_int, c_int, c_int, c_int, c_void, c_void, c_void, c_void, c_float, c_void]),
+    "tree_rope_qk": (c_int, [c_int, c_int, c_int, c_int, c_int, c_int, c_void, c_void, c_void, c_void, c_void,
+                             c_void, c_float, c_void]),
     "tree_attention_verify_workspace_size": (c_size, [c_int, c_int, c_int, c_int, c_int, c_int, c_int]),
     "tree_attention_verify": (c_int, [c_int, c_int, c_int, c_int, c_int, c_int, c_float, c_void, c_void,
                                       c_void, c_void, c_void, c_int, c_int, c_void, c_int, c_void, c_int,

@@ -41,11 +41,9 @@ __device__ __forceinline__ bf16_t from_d<bf16_t>(double v) {
 }
 
 template <typename T>
-__global__ __launch_bounds__(256) void rope_kernel(long long pairs, int N, int H, int D, const T* x,
-                                                   T* out, const int32_t* __restrict__ depth,
-                                                   const int32_t* __restrict__ prefix_len, double log_theta) {
-  const long long t = static_cast<long long>(blockIdx.x) * 256 + threadIdx.x;
-  if (t >= pairs) return;
+__device__ __forceinline__ void rope_pair(long long t, int N, int H, int D, const T* x, T* out,
+                                          const int32_t* __restrict__ depth, const int32_t* __restrict__ prefix_len,
+                                          double log_theta) {
   const int half = D / 2;
   const int i = static_cast<int>(t % half);
   const long long row = t / half;  // (b, u, h)
@@ -59,6 +57,28 @@ __global__ __launch_bounds__(256) void rope_kernel(long long pairs, int N, int H
   const double a = to_d<T>(x[base + i]), v = to_d<T>(x[base + i + half]);
   out[base + i] = from_d<T>(a * c - v * s);
   out[base + i + half] = from_d<T>(v * c + a * s);
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void rope_kernel(long long pairs, int N, int H, int D, const T* x,
+                                                   T* out, const int32_t* __restrict__ depth,
+                                                   const int32_t* __restrict__ prefix_len, double log_theta) {
+  const long long t = static_cast<long long>(blockIdx.x) * 256 + threadIdx.x;
+  if (t < pairs) rope_pair<T>(t, N, H, D, x, out, depth, prefix_len, log_theta);
+}
+
+// Q and K of the tree rows in one launch: the first qpairs threads rotate Q
+// (Hq heads), the rest K (Hkv heads), each exactly as rope_kernel does
+template <typename T>
+__global__ __launch_bounds__(256) void rope_qk_kernel(long long qpairs, long long pairs, int N, int Hq, int Hkv,
+                                                      int D, const T* q, T* q_out, const T* k, T* k_out,
+                                                      const int32_t* __restrict__ depth,
+                                                      const int32_t* __restrict__ prefix_len, double log_theta) {
+  const long long t = static_cast<long long>(blockIdx.x) * 256 + threadIdx.x;
+  if (t < qpairs)
+    rope_pair<T>(t, N, Hq, D, q, q_out, depth, prefix_len, log_theta);
+  else if (t < pairs)
+    rope_pair<T>(t - qpairs, N, Hkv, D, k, k_out, depth, prefix_len, log_theta);
 }
 
 }  // namespace
@@ -86,5 +106,34 @@ extern "C" int tree_rope(int dtype, int B, int N, int H, int D, const void* x, v
     rope_kernel<bf16_t><<<static_cast<unsigned>(blocks), 256, 0, s>>>(
         pairs, N, H, D, static_cast<const bf16_t*>(x), static_cast<bf16_t*>(out), depth, prefix_len, lt);
   HY_LAUNCH_CHECK("tree_rope");
+  return HYDRA_OK;
+}
+
+extern "C" int tree_rope_qk(int dtype, int B, int N, int Hq, int Hkv, int D, const void* q, void* q_out,
+                            const void* k, void* k_out, const int32_t* depth, const int32_t* prefix_len, float theta,
+                            void* stream) {
+  using namespace hydra;
+  clear_error();
+  HY_CHECK(dtype == HYDRA_F32 || dtype == HYDRA_BF16, HYDRA_ERR_INVALID, "tree_rope_qk: bad dtype %d", dtype);
+  HY_CHECK(B >= 0 && N >= 1 && Hq >= 1 && Hkv >= 1 && D >= 2 && D % 2 == 0, HYDRA_ERR_INVALID,
+           "tree_rope_qk: bad sizes B=%d N=%d Hq=%d Hkv=%d D=%d (D even)", B, N, Hq, Hkv, D);
+  HY_CHECK(theta > 1.f, HYDRA_ERR_INVALID, "tree_rope_qk: theta must be > 1 (got %g)", static_cast<double>(theta));
+  if (B == 0) return HYDRA_OK;
+  HY_CHECK(q && q_out && k && k_out && depth && prefix_len, HYDRA_ERR_INVALID, "tree_rope_qk: null pointer");
+  const long long qpairs = static_cast<long long>(B) * N * Hq * (D / 2);
+  const long long pairs = qpairs + static_cast<long long>(B) * N * Hkv * (D / 2);
+  const long long blocks = (pairs + 255) / 256;
+  HY_CHECK(blocks <= 0x7fffffffll, HYDRA_ERR_UNSUPPORTED, "tree_rope_qk: %lld pairs is too many", pairs);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const double lt = log(static_cast<double>(theta));
+  if (dtype == HYDRA_F32)
+    rope_qk_kernel<float><<<static_cast<unsigned>(blocks), 256, 0, s>>>(
+        qpairs, pairs, N, Hq, Hkv, D, static_cast<const float*>(q), static_cast<float*>(q_out),
+        static_cast<const float*>(k), static_cast<float*>(k_out), depth, prefix_len, lt);
+  else
+    rope_qk_kernel<bf16_t><<<static_cast<unsigned>(blocks), 256, 0, s>>>(
+        qpairs, pairs, N, Hq, Hkv, D, static_cast<const bf16_t*>(q), static_cast<bf16_t*>(q_out),
+        static_cast<const bf16_t*>(k), static_cast<bf16_t*>(k_out), depth, prefix_len, lt);
+  HY_LAUNCH_CHECK("tree_rope_qk");
   return HYDRA_OK;
 }

@@ -362,6 +362,22 @@ def tree_rope(x, depth, prefix_len, out=None, theta=10000.0, stream=None):
     return _check("tree_rope", rc)
 
 
+def tree_rope_qk(q, k, depth, prefix_len, q_out=None, k_out=None, theta=10000.0, stream=None):
+    """tree_rope of the tree Q [B, N, Hq, D] and K [B, N, Hkv, D] rows in one
+    launch (see include/hydra.h); the outputs default to the inputs."""
+    B, N, Hq, D = q.shape
+    Hkv = k.shape[2]
+    q_out = q if q_out is None else q_out
+    k_out = k if k_out is None else k_out
+    if (tuple(k.shape) != (B, N, Hkv, D) or tuple(q_out.shape) != tuple(q.shape)
+            or tuple(k_out.shape) != tuple(k.shape) or tuple(depth.shape) != (B, N) or tuple(prefix_len.shape) != (B,)):
+        raise ValueError(f"tree_rope_qk: shapes q {tuple(q.shape)}, k {tuple(k.shape)}, depth {tuple(depth.shape)}")
+    rc = lib().tree_rope_qk(_dtype_code(q), B, N, Hq, Hkv, D, _dev(q, "q"), _dev(q_out, "q_out", q.dtype),
+                            _dev(k, "k", q.dtype), _dev(k_out, "k_out", q.dtype), _dev(depth, "depth", torch.int32),
+                            _dev(prefix_len, "prefix_len", torch.int32), float(theta), _stream(stream))
+    return _check("tree_rope_qk", rc)
+
+
 def tree_attention_verify_workspace_size(dtype_code, B, N, Hq, Hkv, D, max_prefix_len):
     return int(lib().tree_attention_verify_workspace_size(dtype_code, B, N, Hq, Hkv, D, max_prefix_len))
 

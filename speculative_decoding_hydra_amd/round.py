@@ -133,8 +133,8 @@ class HydraRound:
 
     def attend(self, q, k_tree, v_tree, k_pages, v_pages, block_table, prefix_len, stream=None):
         if self.rope_theta:
-            H.tree_rope(q, self.depth, prefix_len, out=self.q_rot, theta=self.rope_theta, stream=stream)
-            H.tree_rope(k_tree, self.depth, prefix_len, out=self.k_rot, theta=self.rope_theta, stream=stream)
+            H.tree_rope_qk(q, k_tree, self.depth, prefix_len, q_out=self.q_rot, k_out=self.k_rot,
+                           theta=self.rope_theta, stream=stream)
             q, k_tree = self.q_rot, self.k_rot
         H.tree_attention_verify(q, k_tree, v_tree, k_pages, v_pages, block_table, prefix_len,
                                 self.shape["max_prefix_len"], self.anc, self.depth, self.attn_out, self.attn_lse,

@@ -831,6 +831,33 @@ def test_tree_rope(dtype, B, N, H, D, lens, inplace):
         assert np.all(np.abs(got - ref) <= step), float(np.max(np.abs(got - ref) / step))
 
 
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("B,N,Hq,Hkv,D,lens", [(1, 64, 32, 32, 128, [2048]), (3, 21, 64, 8, 128, [0, 17, 16384]),
+                                               (2, 5, 4, 2, 32, [3, 100])])
+def test_tree_rope_qk_equals_two_rotations(dtype, B, N, Hq, Hkv, D, lens):
+    """The one-launch Q/K rotation gives tree_rope's values bit for bit
+    (tree_rope itself is checked against the oracle above), also in place."""
+    from speculative_decoding_hydra_amd import tree_rope, tree_rope_qk
+
+    print(f"rope qk {dtype} B={B} N={N} Hq={Hq} Hkv={Hkv} D={D}", flush=True)
+    g = torch.Generator().manual_seed(B * 7 + N + Hq)
+    dt = torch.float32 if dtype == "fp32" else torch.bfloat16
+    q = torch.randn(B, N, Hq, D, generator=g).to(dt).cuda()
+    k = torch.randn(B, N, Hkv, D, generator=g).to(dt).cuda()
+    depth = torch.randint(0, 9, (B, N), generator=g, dtype=torch.int32).cuda()
+    L = torch.tensor(lens, dtype=torch.int32).cuda()
+    qr, kr = torch.full_like(q, float("nan")), torch.full_like(k, float("nan"))
+    tree_rope(q, depth, L, out=qr)
+    tree_rope(k, depth, L, out=kr)
+    qo, ko = torch.full_like(q, float("nan")), torch.full_like(k, float("nan"))
+    tree_rope_qk(q, k, depth, L, q_out=qo, k_out=ko)
+    torch.cuda.synchronize()
+    assert torch.equal(qo, qr) and torch.equal(ko, kr)
+    tree_rope_qk(q, k, depth, L)  # in place
+    torch.cuda.synchronize()
+    assert torch.equal(q, qr) and torch.equal(k, kr)
+
+
 # ------------------------------------------------ the target's decoder layer
 
 def _layer_weights(g, d, Hq, Hkv, D, F, dt):

@@ -9,7 +9,7 @@
  *                          Hydra++ self-attention fusion)
  *   tree_build             final tree (identity or pruned), ancestor table
  *   tree_attention_verify  tree-masked attention over a paged KV prefix
- *                          (tree_rope first rotates the tree Q/K rows at
+ *                          (tree_rope / tree_rope_qk first rotate the tree Q/K rows at
  *                          positions prefix_len + depth; tree_decoder_layer
  *                          runs a whole target layer over the tree rows)
  *   tree_accept            target vocabulary projection + acceptance walk

@@ -260,3 +260,19 @@ def test_draft_heads_attn_and_modes_reject_bad_arguments_before_any_launch(lib):
 class _Plan2:
     def __init__(self, rows, n):
         self.rows, self.dmax, self.N = rows, 2, n
+
+
+def test_tree_rope_qk_rejects_bad_arguments_before_any_launch(lib):
+    I32 = C.POINTER(C.c_int32)
+    ip = lambda a: C.cast(C.c_void_p(a), I32)  # noqa: E731
+    p = [4096 * (i + 1) for i in range(8)]
+
+    def call(dtype=1, B=1, D=128, theta=10000.0, k=None):
+        return lib.tree_rope_qk(dtype, B, 4, 8, 2, D, p[0], p[1], p[2] if k is None else k, p[3], ip(p[4]),
+                                ip(p[5]), theta, None)
+
+    assert call(B=0) == 0
+    assert call(dtype=3) == -1
+    assert call(D=7) == -1
+    assert call(theta=1.0) == -1
+    assert call(k=0) == -1                          # null K

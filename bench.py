@@ -305,7 +305,7 @@ def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (each sequence "
-              "batch shards across GPUs with no exchange; see DESIGN.md). Run with --gpus 1.", file=sys.stderr)
+              "batch shards across GPUs with no exchange). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
     import torch
 

@@ -18,7 +18,7 @@ nearest even) at exactly the two points where the device path stores a
 bfloat16 tensor: the head hidden state ``u`` and the attention output ``O``.
 Logits, log-sum-exps and cumulative log-probabilities stay float64.
 
-Readings of points the pages leave open (each is listed in the design doc):
+Readings of points the pages leave open:
 
 * Hydra head form: one layer, ``u = h + SiLU(W1 [h || e(parent)] + b1)``; the
   residual on ``h`` is the Medusa block with its input widened.

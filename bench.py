@@ -304,7 +304,7 @@ def cpu_baseline(inp, n_rows):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path (each sequence "
+        print("bench.py measures one GPU only: the library has no multi-GPU path (each sequence "
               "batch shards across GPUs with no exchange). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
     import torch

@@ -66,7 +66,7 @@ Readings of points the pages leave open:
   draft distribution stays the same.
 
 Parity unpinned: the choice of nodes in the sparse template beyond its
-invariants (it is this build's own construction), rule S1 on a tree whose
+invariants (a construction of this oracle's own), rule S1 on a tree whose
 children are deterministic top-k tokens (the pages prove exactness only for a
 drafted chain), and the threshold form of typical acceptance (the pages only
 tie it to the entropy; its pins are its limits and closed forms).

@@ -858,6 +858,45 @@ def test_tree_rope_qk_equals_two_rotations(dtype, B, N, Hq, Hkv, D, lens):
     assert torch.equal(q, qr) and torch.equal(k, kr)
 
 
+@pytest.mark.parametrize("over", [dict(), dict(head="sketch", head_hidden=256), dict(cond="path"), dict(cond="attn"),
+                                  dict(mode="stochastic", T=0.7), dict(mode="typical")],
+                         ids=["folded", "sketch", "path", "attn", "stochastic", "typical"])
+def test_round_graph_replays_match_eager(over):
+    """The whole round captured in a HIP graph (as bench.py times it) and
+    replayed three times, with eager work and synchronisations between the
+    replays: every replay reproduces the eager round bit for bit (the kernels
+    are deterministic and nothing in the round is a memset or an allocation),
+    and the commit writes the same cache contents again."""
+    w = HI.workload("7b_sparse64", B=2, d=512, V=3000, Hq=8, Hkv=8, D=128, L=(256,), **over)
+    print(f"graph replay {over}", flush=True)
+    inp = HI.generate(w)
+    rnd, dev = T.round_inputs(inp)
+    outs = lambda: [t.clone() for t in (rnd.cand_tok, rnd.cand_logp, rnd.head_logits, rnd.head_lse, rnd.tok,  # noqa: E731
+                                        rnd.anc, rnd.attn_out, rnd.target_logits, rnd.n_accepted, rnd.path,
+                                        rnd.out_tok, rnd.next_prefix_len, rnd.next_root_tok, rnd.next_h)]
+    T.run_round(rnd, dev)
+    torch.cuda.synchronize()
+    ref, kp, vp = outs(), dev["k_pages"].clone(), dev["v_pages"].clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        T.run_round(rnd, dev)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        T.run_round(rnd, dev)
+    for rep in range(3):
+        for t in (rnd.cand_tok, rnd.cand_logp, rnd.head_logits, rnd.target_logits, rnd.n_accepted, rnd.out_tok):
+            t.fill_(-7)  # eager work between the replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for i, (a, b) in enumerate(zip(ref, outs())):
+            assert torch.equal(a, b), f"replay {rep}: output {i} differs from the eager round"
+        assert torch.equal(dev["k_pages"], kp) and torch.equal(dev["v_pages"], vp)
+
+
 # ------------------------------------------------ the target's decoder layer
 
 def _layer_weights(g, d, Hq, Hkv, D, F, dt):

@@ -451,6 +451,10 @@ def tree_accept(o, W_t, tok, parent, target_logits, n_accepted, path, out_tok, w
         raise ValueError("tree_accept: typical acceptance needs eps and delta")
     B, N, d = o.shape
     V = W_t.shape[0]
+    if W_t.dim() != 2 or W_t.shape[1] != d:
+        raise ValueError(f"tree_accept: W_t {tuple(W_t.shape)} does not take rows of width {d} (o {tuple(o.shape)})")
+    if tuple(target_logits.shape) != (B, N, V):
+        raise ValueError(f"tree_accept: target_logits {tuple(target_logits.shape)}, expected {(B, N, V)}")
     Dmax = path.shape[1] - 1
     R = head_logits.shape[1] if head_logits is not None else 0
     wsp, wsb = _ws(ws)

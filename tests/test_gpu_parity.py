@@ -434,7 +434,7 @@ def test_draft_first_layer_split_and_fused(B, d, b1, hydra, fold):
     print(f"first layer B={B} d={d} rows/depth2={B * b1} hydra={hydra} fold={fold}", flush=True)
     inp = HI.generate(w)
     rnd, dev = T.round_inputs(inp, fold_embedding=fold)
-    T.run_round(rnd, dev)
+    rnd.draft(dev["h"], dev["root_tok"])  # the draft stage alone (the layer sizes differ from d)
     torch.cuda.synchronize()
     rep = T.check_draft(inp, rnd)
     print(rep, flush=True)
@@ -453,7 +453,7 @@ def test_draft_four_heads_folded_and_streamed(tree, fold, residual):
     inp = HI.generate(w)
     rnd, dev = T.round_inputs(inp, fold_embedding=fold, residual=residual)
     assert (rnd.emb_proj is not None) == fold
-    T.run_round(rnd, dev)
+    rnd.draft(dev["h"], dev["root_tok"])  # the draft stage alone (the layer sizes differ from d)
     torch.cuda.synchronize()
     rep = T.check_draft(inp, rnd)
     print(rep, flush=True)
@@ -476,7 +476,7 @@ def test_sketch_heads_stagewise(B, d, hid, V, tree):
     inp = HI.generate(w)
     rnd, dev = T.round_inputs(inp)
     assert rnd.sketch and rnd.emb_proj is None
-    T.run_round(rnd, dev)
+    rnd.draft(dev["h"], dev["root_tok"])  # the draft stage alone (the layer sizes differ from d)
     torch.cuda.synchronize()
     rep = T.check_draft(inp, rnd)
     print(rep, flush=True)
@@ -496,7 +496,7 @@ def test_full_path_heads_stagewise(B, d, V, tree):
     inp = HI.generate(w)
     rnd, dev = T.round_inputs(inp)
     assert rnd.full_path and rnd.emb_proj is None
-    T.run_round(rnd, dev)
+    rnd.draft(dev["h"], dev["root_tok"])  # the draft stage alone (the layer sizes differ from d)
     torch.cuda.synchronize()
     rep = T.check_draft(inp, rnd)
     print(rep, flush=True)
@@ -517,7 +517,7 @@ def test_hydra_pp_heads_stagewise(B, d, V, tree):
     inp = HI.generate(w)
     rnd, dev = T.round_inputs(inp)
     assert rnd.attn is not None and rnd.emb_proj is None
-    T.run_round(rnd, dev)
+    rnd.draft(dev["h"], dev["root_tok"])  # the draft stage alone (the layer sizes differ from d)
     torch.cuda.synchronize()
     rep = T.check_draft(inp, rnd)
     print(rep, flush=True)
@@ -867,7 +867,7 @@ def test_round_graph_replays_match_eager(over):
     replays: every replay reproduces the eager round bit for bit (the kernels
     are deterministic and nothing in the round is a memset or an allocation),
     and the commit writes the same cache contents again."""
-    w = HI.workload("7b_sparse64", B=2, d=512, V=3000, Hq=8, Hkv=8, D=128, L=(256,), **over)
+    w = HI.workload("7b_sparse64", B=2, d=512, V=3000, Hq=4, Hkv=4, D=128, L=(256,), **over)
     print(f"graph replay {over}", flush=True)
     inp = HI.generate(w)
     rnd, dev = T.round_inputs(inp)

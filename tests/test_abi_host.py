@@ -276,3 +276,17 @@ def test_tree_rope_qk_rejects_bad_arguments_before_any_launch(lib):
     assert call(D=7) == -1
     assert call(theta=1.0) == -1
     assert call(k=0) == -1                          # null K
+
+
+def test_tree_accept_binding_rejects_mismatched_target_weights():
+    """The target projection reads W_t rows as wide as the attention output:
+    the binding refuses a W_t of another width before touching any pointer."""
+    import torch
+
+    import speculative_decoding_hydra_amd as S
+
+    o = torch.zeros(1, 4, 8)
+    with pytest.raises(ValueError, match="W_t"):
+        S.tree_accept(o, torch.zeros(10, 16), None, None, torch.zeros(1, 4, 10), None, torch.zeros(1, 3), None, None)
+    with pytest.raises(ValueError, match="target_logits"):
+        S.tree_accept(o, torch.zeros(10, 8), None, None, torch.zeros(1, 4, 9), None, torch.zeros(1, 3), None, None)

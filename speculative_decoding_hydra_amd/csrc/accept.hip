@@ -176,7 +176,7 @@ __global__ __launch_bounds__(kWalkThreads) void reject_walk(
     }
     // q at u: the head row that drafted u's children
     const int qr = q_row[static_cast<size_t>(b) * N + u];
-    const float* hz = HZ + (static_cast<size_t>(b) * R + (qr < 0 ? 0 : qr)) * V;
+    const float* hz = HZ + (static_cast<size_t>(b) * R + (qr < 0 ? 0 : (qr >= R ? R - 1 : qr))) * V;
     float qm = -INFINITY;
     for (int x = tid; x < V; x += kWalkThreads) qm = fmaxf(qm, hz[x] * invT);
     qm = block_max_f(qm, redf);
@@ -607,7 +607,7 @@ __global__ __launch_bounds__(kWalkThreads) void reject_node_reg(
   int taken = -1;
   if (cnt > 0 && depth < Dmax) {
     const int qr = q_row[row];
-    reg_load_scaled(q, HZ, static_cast<size_t>(b) * R + (qr < 0 ? 0 : qr), V, invT);
+    reg_load_scaled(q, HZ, static_cast<size_t>(b) * R + (qr < 0 ? 0 : (qr >= R ? R - 1 : qr)), V, invT);
     const float qinv = static_cast<float>(1.0 / reg_exp(q, red, redf));
 #pragma unroll
     for (int i = 0; i < EPT; ++i) q[i] *= qinv;

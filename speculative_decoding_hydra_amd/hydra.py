@@ -56,6 +56,19 @@ def _dev(t, name, dtype=None):
     return t.data_ptr()
 
 
+def _shapes(fn, **want):
+    """Raise ValueError unless every given tensor (None skipped) has its
+    expected shape: the C entry points see pointers only, so this is where a
+    mismatched tensor is refused before any kernel could read past it."""
+    for name, (t, shape) in want.items():
+        if t is None:
+            continue
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{fn}: {name}: expected a tensor")
+        if tuple(t.shape) != tuple(int(x) for x in shape):
+            raise ValueError(f"{fn}: {name} has shape {tuple(t.shape)}, expected {tuple(int(x) for x in shape)}")
+
+
 def _host_i32(a):
     a = np.ascontiguousarray(np.asarray(a, dtype=np.int32))
     return a, a.ctypes.data_as(C.POINTER(C.c_int32))
@@ -171,6 +184,21 @@ class DevicePlan:
 
 # ------------------------------------------------------------------ stages
 
+def _draft_shapes(fn, h, root_tok, emb, W2, dplan, head_logits, head_lse, cand_tok, cand_logp, head_hidden):
+    """Shapes shared by the three draft-stage bindings."""
+    if h.dim() != 2:
+        raise ValueError(f"{fn}: h must be [B, d], got {tuple(h.shape)}")
+    B, d = h.shape
+    V = W2[0].shape[0]
+    if len(W2) < dplan.dmax:
+        raise ValueError(f"{fn}: the tree is {dplan.dmax} deep but there are {len(W2)} heads")
+    _shapes(fn, root_tok=(root_tok, (B,)), emb=(emb, (V, d)), head_logits=(head_logits, (B, dplan.R, V)),
+            head_lse=(head_lse, (B, dplan.R)), cand_tok=(cand_tok, (B, dplan.N)), cand_logp=(cand_logp, (B, dplan.N)),
+            head_hidden=(head_hidden, (B, dplan.R, d)))
+    for k, w in enumerate(W2):
+        _shapes(fn, **{f"W2[{k}]": (w, (V, d))})
+
+
 def hydra_draft_heads_workspace_size(dtype_code, B, d, V, hydra, dplan: DevicePlan):
     rf, rfp = _host_i32(dplan.rows.row_first)
     return int(lib().hydra_draft_heads_workspace_size(dtype_code, B, d, V, int(hydra), dplan.dmax, rfp))
@@ -190,6 +218,11 @@ def hydra_draft_heads(h, root_tok, emb, W1, b1, W2, dplan: DevicePlan, head_logi
     n_heads = len(W2)
     if not (len(W1) == len(b1) == n_heads):
         raise ValueError("W1, b1 and W2 need one entry per head")
+    _draft_shapes("hydra_draft_heads", h, root_tok, emb if dplan.hydra else None, W2, dplan, head_logits, head_lse,
+                  cand_tok, cand_logp, head_hidden)
+    for k in range(n_heads):
+        in_k = (k + 2) * d if full_path else (2 * d if dplan.hydra else d)
+        _shapes("hydra_draft_heads", **{f"W1[{k}]": (W1[k], (d, in_k)), f"b1[{k}]": (b1[k], (d,))})
     arr = C.c_void_p * n_heads
     w1 = arr(*[_dev(w, "W1", h.dtype) for w in W1])
     bb = arr(*[_dev(w, "b1", h.dtype) for w in b1])
@@ -204,6 +237,8 @@ def hydra_draft_heads(h, root_tok, emb, W1, b1, W2, dplan: DevicePlan, head_logi
             raise ValueError("full-path heads take no folded tables")
         if len(emb_proj) != n_heads:
             raise ValueError("emb_proj needs one table per head")
+        for k, t in enumerate(emb_proj):
+            _shapes("hydra_draft_heads", **{f"emb_proj[{k}]": (t, (V, d))})
         ep = arr(*[_dev(t, "emb_proj", torch.float32) for t in emb_proj])
     wsp, wsb = _ws(ws)
     rc = lib().hydra_draft_heads(
@@ -234,6 +269,14 @@ def hydra_draft_heads_sketch(h, root_tok, emb, heads, dplan: DevicePlan, head_lo
     n_heads = len(heads)
     V = heads[0]["W2"].shape[0]
     hidden_dim = heads[1]["Wa"].shape[0] if n_heads > 1 else d
+    _draft_shapes("hydra_draft_heads_sketch", h, root_tok, emb, [w["W2"] for w in heads], dplan, head_logits,
+                  head_lse, cand_tok, cand_logp, head_hidden)
+    for k, w in enumerate(heads):
+        want = {"Wa": (d, d) if k == 0 else (hidden_dim, 2 * d), "ba": (d,) if k == 0 else (hidden_dim,),
+                "ln_g": (d,), "ln_b": (d,)}
+        if k > 0:
+            want.update(Wb=(d, hidden_dim), bb=(d,))
+        _shapes("hydra_draft_heads_sketch", **{f"heads[{k}].{n}": (w[n], sh) for n, sh in want.items()})
     arr = C.c_void_p * n_heads
 
     def col(name, first=True):
@@ -272,6 +315,11 @@ def hydra_draft_heads_attn(h, root_tok, emb, Wqkv, Wo, W1, b1, W2, dplan: Device
     n_heads = len(W2)
     if not (len(W1) == len(b1) == n_heads):
         raise ValueError("W1, b1 and W2 need one entry per head")
+    _draft_shapes("hydra_draft_heads_attn", h, root_tok, emb, W2, dplan, head_logits, head_lse, cand_tok, cand_logp,
+                  head_hidden)
+    _shapes("hydra_draft_heads_attn", Wqkv=(Wqkv, (3 * d, d)), Wo=(Wo, (d, d)))
+    for k in range(n_heads):
+        _shapes("hydra_draft_heads_attn", **{f"W1[{k}]": (W1[k], (d, 2 * d)), f"b1[{k}]": (b1[k], (d,))})
     arr = C.c_void_p * n_heads
     w1 = arr(*[_dev(w, "W1", h.dtype) for w in W1])
     bb = arr(*[_dev(w, "b1", h.dtype) for w in b1])
@@ -312,6 +360,7 @@ def hydra_vocab_projection(X, W, Y, k=0, ws=None, stream=None):
     top-k partials in ws (finish with hydra_vocab_topk)."""
     M, K = X.shape
     N = W.shape[0]
+    _shapes("hydra_vocab_projection", W=(W, (N, K)), Y=(Y, (M, N)))
     wsp, wsb = _ws(ws)
     rc = lib().hydra_vocab_projection(_dtype_code(X), M, K, N, int(k), _dev(X, "X"), _dev(W, "W", X.dtype),
                                       _dev(Y, "Y", torch.float32), wsp, wsb, _stream(stream))
@@ -321,6 +370,7 @@ def hydra_vocab_projection(X, W, Y, k=0, ws=None, stream=None):
 def hydra_vocab_topk(M, N, k, Y, ws, lse=None, ids=None, vals=None, stream=None):
     """Per-row log-sum-exp and sorted top-k from a k > 0 projection's logits Y
     and workspace."""
+    _shapes("hydra_vocab_topk", Y=(Y, (M, N)), lse=(lse, (M,)), ids=(ids, (M, k)), vals=(vals, (M, k)))
     wsp, wsb = _ws(ws)
     rc = lib().hydra_vocab_topk(int(M), int(N), int(k), _dev(Y, "Y", torch.float32), wsp, wsb,
                                 _dev(lse, "lse", torch.float32),
@@ -336,6 +386,10 @@ def tree_build(dplan: DevicePlan, cand_tok, cand_logp, n_keep, tok, parent, dept
                ws=None, stream=None):
     """Stage 2 (see include/hydra.h)."""
     B = cand_tok.shape[0]
+    K = int(n_keep)
+    _shapes("tree_build", cand_tok=(cand_tok, (B, dplan.N)), cand_logp=(cand_logp, (B, dplan.N)), tok=(tok, (B, K)),
+            parent=(parent, (B, K)), depth=(depth, (B, K)), anc=(anc, (B, K, dplan.dmax + 1)), q_row=(q_row, (B, K)),
+            src=(src, (B, K)))
     wsp, wsb = _ws(ws)
     rc = lib().tree_build(B, dplan.N, dplan.dmax, _dev(dplan.parent, "parent"), _dev(dplan.rank, "rank"),
                           _dev(dplan.depth, "depth"), _dev(dplan.node_row, "node_row"),
@@ -387,9 +441,16 @@ def tree_attention_verify(q, k_tree, v_tree, k_pages, v_pages, block_table, pref
     """Stage 3 (see include/hydra.h). q [B, N, Hq, D]; pages [n_pages, Hkv, page, D]."""
     B, N, Hq, D = q.shape
     Hkv = k_tree.shape[2]
+    if k_pages.dim() != 4 or anc.dim() != 3 or block_table.dim() != 2:
+        raise ValueError("tree_attention_verify: pages [n_pages, Hkv, page, D], anc [B, N, Dmax + 1] and "
+                         "block_table [B, max_pages] expected")
     n_pages, _, page_size, _ = k_pages.shape
     max_pages = block_table.shape[1]
     Dmax = anc.shape[2] - 1
+    _shapes("tree_attention_verify", k_tree=(k_tree, (B, N, Hkv, D)), v_tree=(v_tree, (B, N, Hkv, D)),
+            k_pages=(k_pages, (n_pages, Hkv, page_size, D)), v_pages=(v_pages, (n_pages, Hkv, page_size, D)),
+            block_table=(block_table, (B, max_pages)), prefix_len=(prefix_len, (B,)), anc=(anc, (B, N, Dmax + 1)),
+            depth=(depth, (B, N)), out=(out, (B, N, Hq, D)), lse=(lse, (B, N, Hq)))
     if scale is None:
         scale = 1.0 / float(D) ** 0.5
     wsp, wsb = _ws(ws)
@@ -457,6 +518,9 @@ def tree_accept(o, W_t, tok, parent, target_logits, n_accepted, path, out_tok, w
         raise ValueError(f"tree_accept: target_logits {tuple(target_logits.shape)}, expected {(B, N, V)}")
     Dmax = path.shape[1] - 1
     R = head_logits.shape[1] if head_logits is not None else 0
+    _shapes("tree_accept", tok=(tok, (B, N)), parent=(parent, (B, N)), q_row=(q_row, (B, N)),
+            head_logits=(head_logits, (B, R, V)), u_acc=(u_acc, (B, N)), u_res=(u_res, (B, N)),
+            n_accepted=(n_accepted, (B,)), path=(path, (B, Dmax + 1)), out_tok=(out_tok, (B, Dmax + 1)))
     wsp, wsb = _ws(ws)
     rc = lib().tree_accept(
         _dtype_code(o), int(mode), B, N, d, V, Dmax, _dev(o, "o"), _dev(W_t, "W_t", o.dtype), float(temperature),

@@ -15,7 +15,11 @@ every stage are compared with the oracle on the same inputs:
 * tree: oracle prune / ancestors from the device's cumulative scores;
 * attention output: oracle from the device's ancestor table;
 * target logits: oracle projection of the device's attention output;
-* acceptance: oracle walk on the device's logits.
+* target arg max of every row: the device's equals the oracle's, except
+  where the oracle's top-1 margin is below 1e-4 (recomputed from the device
+  logits);
+* acceptance: oracle walk on the device's logits (greedy: and on the
+  oracle's own logits, unless a visited row was recomputed).
 
 Tolerances (max-abs): 1e-4 in float32 mode and 2e-2 for bfloat16 inputs
 with float32 accumulation.
@@ -319,15 +323,32 @@ def check_accept(inp, rnd, seqs=None):
     Dm = rnd.dplan.dmax
     e_z = 0.0
     amb = 0
+    recomputed = 0
     for b in seqs:
         Z = O.target_logits(O_dev[b: b + 1], Wt)[0]
         e_z = max(e_z, float(np.max(np.abs(Z - Z_dev[b]))))
+        # every row's arg max: the device's (over its own logits, as its walk
+        # takes it) equals the oracle's unless the oracle's top-1 margin is
+        # below 1e-4, where the decision is recomputed from the device logits
+        for u in range(Z.shape[0]):
+            mine, dev_y = O.argmax_lowest(Z[u]), O.argmax_lowest(Z_dev[b, u])
+            if mine != dev_y:
+                margin = O.topk_margin(Z[u], 1)
+                assert margin < MARGIN, (f"seq {b} row {u}: device arg max {dev_y} != oracle {mine} "
+                                         f"(margin {margin:.3g})")
+                recomputed += 1
         got_p = [int(x) for x in path[b] if x >= 0]
         got_o = [int(x) for x in out[b] if x >= 0]
         assert n_acc[b] == len(got_p) - 1 and len(got_o) == len(got_p)
         if w.mode == "greedy":
             m, p, o = O.greedy_accept(Z_dev[b], tok[b], par[b], Dm)
             assert n_acc[b] == m and got_p == p and got_o == o, f"seq {b}: greedy walk {got_p}/{got_o} vs {p}/{o}"
+            # and on the oracle's own logits, the same walk unless a row it
+            # visits was recomputed above
+            m2, p2, o2 = O.greedy_accept(Z, tok[b], par[b], Dm)
+            if (p2, o2) != (p, o):
+                near = [u for u in set(p) | set(p2) if O.topk_margin(Z[u], 1) < MARGIN]
+                assert near, f"seq {b}: walk on the oracle's logits {p2}/{o2} vs device {p}/{o}"
         elif w.mode == "typical":
             amb += check_typical(Z_dev[b], tok[b], par[b], np_(inp["u_res"])[b], w, got_p, got_o, f"seq {b}")
         else:
@@ -344,7 +365,7 @@ def check_accept(inp, rnd, seqs=None):
                     bound = ACCEPT_EPS if kind == "accept" else SAMPLE_EPS
                     assert margin < bound, f"seq {b}: {kind} decision {taken} vs oracle {own} (margin {margin:.3g})"
     assert e_z <= t, f"target logits max-abs {e_z:.3g} > {t}"
-    return dict(z=e_z, ambiguous=amb)
+    return dict(z=e_z, ambiguous=amb, argmax_recomputed=recomputed)
 
 
 def check_typical(Z, tok, parent, u_res, w, got_p, got_o, where):

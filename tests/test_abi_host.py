@@ -290,3 +290,81 @@ def test_tree_accept_binding_rejects_mismatched_target_weights():
         S.tree_accept(o, torch.zeros(10, 16), None, None, torch.zeros(1, 4, 10), None, torch.zeros(1, 3), None, None)
     with pytest.raises(ValueError, match="target_logits"):
         S.tree_accept(o, torch.zeros(10, 8), None, None, torch.zeros(1, 4, 9), None, torch.zeros(1, 3), None, None)
+
+
+def _refuses(fn, good, bad):
+    """fn(**good) gets past every shape check (it stops at the first CPU
+    tensor, which is not a device pointer); each entry of bad, swapped in
+    alone, is refused by name before any pointer is taken."""
+    for name, t in bad.items():
+        args = dict(good)
+        key = name.split("[")[0]
+        if "[" in name:  # one entry of a per-head list
+            j = int(name.split("[")[1].rstrip("]"))
+            args[key] = list(args[key])
+            args[key][j] = t
+        else:
+            args[key] = t
+        with pytest.raises(ValueError, match=re.escape(name) + " has shape"):
+            fn(**args)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        fn(**good)
+
+
+def test_bindings_refuse_every_mismatched_shape():
+    """The C entry points see pointers only: every tensor argument of every
+    stage binding is checked against the shape the kernels index it with."""
+    import torch
+
+    import speculative_decoding_hydra_amd as S
+    from speculative_decoding_hydra_amd import hydra as Hy
+
+    f = lambda *s: torch.zeros(*s)  # noqa: E731
+    i = lambda *s: torch.zeros(*s, dtype=torch.int32)  # noqa: E731
+    B, d, V, heads = 2, 16, 40, 2
+    dplan = Hy.DevicePlan(Hy.hydra_plan_cartesian([2, 3]), True, "cpu")
+    N, R, Dm = dplan.N, dplan.R, dplan.dmax
+    draft = dict(h=f(B, d), root_tok=i(B), emb=f(V, d), W1=[f(d, 2 * d)] * heads, b1=[f(d)] * heads,
+                 W2=[f(V, d)] * heads, dplan=dplan, head_logits=f(B, R, V), head_lse=f(B, R), cand_tok=i(B, N),
+                 cand_logp=f(B, N), ws=None, head_hidden=f(B, R, d))
+    _refuses(S.hydra_draft_heads, draft,
+             {"root_tok": i(B + 1), "emb": f(V, d + 1), "head_logits": f(B, R + 1, V), "head_lse": f(B, R, 2),
+              "cand_tok": i(B, N - 1), "cand_logp": f(B + 1, N), "head_hidden": f(B, R, d - 1),
+              "W1[1]": f(d, d), "b1[0]": f(d + 1), "W2[1]": f(V - 1, d)})
+    sketch = {k: v for k, v in draft.items() if k not in ("W1", "b1", "W2")}
+    hid = 8
+    sketch["heads"] = [dict(Wa=f(d, d), ba=f(d), ln_g=f(d), ln_b=f(d), W2=f(V, d)),
+                       dict(Wa=f(hid, 2 * d), ba=f(hid), Wb=f(d, hid), bb=f(d), ln_g=f(d), ln_b=f(d), W2=f(V, d))]
+    for k, name, bad in [(1, "Wb", f(d, hid + 1)), (0, "Wa", f(d, 2 * d)), (1, "ln_g", f(d - 1))]:
+        hs = [dict(x) for x in sketch["heads"]]
+        hs[k][name] = bad
+        with pytest.raises(ValueError, match=re.escape(f"heads[{k}].{name} has shape")):
+            S.hydra_draft_heads_sketch(**{**sketch, "heads": hs})
+    attn = dict(draft, Wqkv=f(3 * d, d), Wo=f(d, d))
+    attn.pop("emb")
+    attn = {"h": attn.pop("h"), "root_tok": attn.pop("root_tok"), "emb": f(V, d), **attn}
+    _refuses(S.hydra_draft_heads_attn, attn, {"Wqkv": f(2 * d, d), "Wo": f(d, 2 * d), "cand_tok": i(B, N + 1)})
+
+    K = N
+    build = dict(dplan=dplan, cand_tok=i(B, N), cand_logp=f(B, N), n_keep=K, tok=i(B, K), parent=i(B, K),
+                 depth=i(B, K), anc=i(B, K, Dm + 1), q_row=i(B, K), src=i(B, K))
+    _refuses(S.tree_build, build, {"cand_logp": f(B, N + 1), "anc": i(B, K, Dm), "src": i(B, K - 1),
+                                   "q_row": i(B + 1, K)})
+
+    Hq, Hkv, D, P, ps, mp = 4, 2, 32, 6, 16, 3
+    att = dict(q=f(B, N, Hq, D), k_tree=f(B, N, Hkv, D), v_tree=f(B, N, Hkv, D), k_pages=f(P, Hkv, ps, D),
+               v_pages=f(P, Hkv, ps, D), block_table=i(B, mp), prefix_len=i(B), max_prefix_len=40,
+               anc=i(B, N, Dm + 1), depth=i(B, N), out=f(B, N, Hq, D), lse=f(B, N, Hq))
+    _refuses(S.tree_attention_verify, att,
+             {"k_tree": f(B, N + 1, Hkv, D), "v_tree": f(B, N - 1, Hkv, D), "v_pages": f(P + 1, Hkv, ps, D),
+              "prefix_len": i(B + 1), "depth": i(B, N + 1), "out": f(B, N, Hkv, D), "lse": f(B, N, Hq, 1)})
+
+    acc = dict(o=f(B, N, d), W_t=f(V, d), tok=i(B, N), parent=i(B, N), target_logits=f(B, N, V), n_accepted=i(B),
+               path=i(B, Dm + 1), out_tok=i(B, Dm + 1), ws=None, mode=1, q_row=i(B, N), head_logits=f(B, R, V),
+               u_acc=f(B, N), u_res=f(B, N))
+    _refuses(S.tree_accept, acc,
+             {"tok": i(B, N + 1), "parent": i(B - 1, N), "q_row": i(B, N - 1), "head_logits": f(B, R, V + 1),
+              "u_acc": f(B, 1), "u_res": f(1, N), "n_accepted": i(B + 1), "out_tok": i(B, Dm)})
+
+    proj = dict(X=f(5, d), W=f(V, d), Y=f(5, V))
+    _refuses(S.hydra_vocab_projection, proj, {"W": f(V, d + 1), "Y": f(5, V + 1)})

@@ -396,6 +396,89 @@ def test_tiny_stochastic_planted_acceptance(seed):
     print(rep, "accepted", rnd.n_accepted.tolist(), flush=True)
 
 
+@pytest.mark.parametrize("B,dtype", [(3, "bf16"), (2, "fp32")])
+def test_rejection_planted_large_vocabulary(B, dtype):
+    """Rule S1 over a 32000-token vocabulary (the register-resident node
+    kernel holds 32 logits per thread). Planted attention outputs make the
+    target put almost all its mass on one drafted token per node of a chosen
+    branch, two to four deep; at one node the favoured child is the second
+    in rank order, so the first is rejected, the residual norm(max(p - q, 0))
+    is formed and the second is accepted from it. The device must take the
+    planted branch, and every decision is checked against the oracle
+    following the device's path."""
+    from speculative_decoding_hydra_amd import tree_accept, tree_accept_workspace_size
+
+    print(f"rejection planted V=32000 B={B} {dtype}", flush=True)
+    g = np.random.default_rng(40 + B)
+    dt = torch.float32 if dtype == "fp32" else torch.bfloat16
+    V, d, Tm = 32000, 256, 0.7
+    plan = O.plan_sparse_template((4, 3, 2, 1), 30)
+    N = plan.n
+    _, _, node_row = O.head_rows(plan, True)
+    R = int(node_row.max()) + 1
+    W = HI.as_f64(_bf16(torch.tensor(g.standard_normal((V, d)) * 0.02, dtype=torch.float32)))
+    tok = np.zeros((B, N), dtype=np.int32)
+    o = g.standard_normal((B, N, d)) * 0.01
+    hz = (g.standard_normal((B, R, V)) * 2.0).astype(np.float32)
+    u_acc = g.random((B, N)).astype(np.float32)
+    u_res = g.random((B, N)).astype(np.float32)
+    want = []
+    for b in range(B):
+        for u in range(N):
+            kids = plan.children(u)
+            tok[b, kids] = g.choice(V, len(kids), replace=False)
+        depth_t = int(g.integers(2, plan.dmax + 1))
+        r1_step = int(g.integers(0, depth_t))  # the step that takes a rank-1 child
+        path = [0]
+        for step in range(depth_t):
+            kids = plan.children(path[-1])
+            if not kids:
+                break
+            pick = [c for c in kids if plan.rank[c] == 1] if step == r1_step else kids
+            pick = pick or kids
+            if step + 1 < depth_t:
+                pick = [c for c in pick if plan.children(c)] or pick
+            path.append(int(g.choice(pick)))
+        for a, nx in zip(path[:-1], path[1:]):
+            o[b, a] = W[tok[b, nx]] * 400.0
+        want.append(path)
+    assert any(plan.rank[nx] == 1 for p in want for nx in p[1:]), "no rejected first sibling planted"
+    ot = torch.tensor(o, dtype=torch.float32).to(dt).cuda()
+    Wt = torch.tensor(W, dtype=torch.float32).to(dt).cuda()
+    tk = torch.tensor(tok).cuda()
+    par = torch.tensor(np.stack([plan.parent] * B).astype(np.int32)).cuda()
+    qrow = torch.tensor(np.stack([node_row] * B).astype(np.int32)).cuda()
+    Z = torch.empty(B, N, V, device="cuda")
+    n_acc = torch.empty(B, dtype=torch.int32, device="cuda")
+    path_t = torch.empty(B, plan.dmax + 1, dtype=torch.int32, device="cuda")
+    out_t = torch.empty_like(path_t)
+    ws = torch.empty(tree_accept_workspace_size(1, B, N, V), dtype=torch.uint8, device="cuda")
+    tree_accept(ot, Wt, tk, par, Z, n_acc, path_t, out_t, ws, mode=1, temperature=Tm, q_row=qrow,
+                head_logits=torch.tensor(hz).cuda(), u_acc=torch.tensor(u_acc).cuda(),
+                u_res=torch.tensor(u_res).cuda())
+    torch.cuda.synchronize()
+    Zd = Z.cpu().double().numpy()
+    Zo = O.target_logits(HI.as_f64(ot.cpu()), W)
+    assert float(np.max(np.abs(Zo - Zd))) <= (1e-4 if dtype == "fp32" else 2e-2)
+    depths, rejections = [], 0
+    for b in range(B):
+        got_p = [int(x) for x in path_t[b] if x >= 0]
+        got_o = [int(x) for x in out_t[b] if x >= 0]
+        assert int(n_acc[b]) == len(got_p) - 1
+        assert got_p[: len(want[b])] == want[b], f"seq {b}: device path {got_p}, planted {want[b]}"
+        trace = []
+        m, p, ot_ = O.rejection_accept(Zd[b], hz[b].astype(np.float64), node_row, tok[b], plan.parent, u_acc[b],
+                                       u_res[b], Tm, follow=(got_p, got_o), trace=trace)
+        assert p == got_p and ot_ == got_o
+        for kind, own, taken, margin in trace:
+            if own != taken:
+                bound = T.ACCEPT_EPS if kind == "accept" else T.SAMPLE_EPS
+                assert margin < bound, f"seq {b}: {kind} decision {taken} vs oracle {own} (margin {margin:.3g})"
+        rejections += sum(1 for e in trace if e[0] == "accept" and not e[2])
+        depths.append(len(got_p) - 1)
+    assert min(depths) >= 2 and rejections > 0, (depths, rejections)
+
+
 def test_7b_batched16_round():
     """16 ragged sequences over scattered 16-token pages; sampled sequences
     checked stage by stage."""

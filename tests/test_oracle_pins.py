@@ -67,6 +67,59 @@ def test_inverse_cdf_matches_searchsorted():
         assert H.sample_inverse_cdf(r, u) == ref
 
 
+def _margin_brute_force(z, k):
+    """Smallest |a - b| over all pairs of the k + 1 largest values of z (the
+    k + 1 largest taken by repeatedly removing a maximum)."""
+    rest = [float(x) for x in z]
+    top = []
+    for _ in range(min(k + 1, len(rest))):
+        i = max(range(len(rest)), key=lambda j: rest[j])
+        top.append(rest.pop(i))
+    if len(top) < 2:
+        return math.inf
+    return min(abs(a - b) for i, a in enumerate(top) for b in top[i + 1:])
+
+
+def test_topk_margin_matches_brute_force_over_pairs():
+    rng = np.random.default_rng(4)
+    for _ in range(300):
+        n = int(rng.integers(1, 40))
+        z = np.round(rng.standard_normal(n) * 3, int(rng.integers(0, 4)))  # rounding makes ties
+        k = int(rng.integers(1, n + 2))
+        assert H.topk_margin(z, k) == _margin_brute_force(z, k)
+    # the k / k + 1 boundary counts: the first k values are far apart, the
+    # (k + 1)-th sits just below the k-th; a margin over the first k alone
+    # would call this decision safe
+    z = np.array([9.0, 5.0, 1.0, 1.0 - 3e-5, -4.0])
+    assert H.topk_margin(z, 3) == pytest.approx(3e-5)
+    first_k_only = float(np.min(-np.diff(np.sort(z)[::-1][:3])))
+    assert first_k_only == 4.0 and H.topk_margin(z, 3) < 1e-4
+
+
+def test_topk_margin_bounds_the_perturbation_that_changes_top_k():
+    """Below half the margin no perturbation changes the sorted top-k ids;
+    just above it, moving the two closest of the k + 1 largest values
+    towards each other does."""
+    rng = np.random.default_rng(5)
+    for _ in range(200):
+        n = int(rng.integers(3, 30))
+        z = rng.standard_normal(n)
+        k = int(rng.integers(1, n))
+        m = H.topk_margin(z, k)
+        base = H.topk_sorted(z, k)
+        for _ in range(5):
+            dz = rng.uniform(-1, 1, n) * 0.49 * m
+            assert np.array_equal(H.topk_sorted(z + dz, k), base)
+        order = np.argsort(-z, kind="stable")[: k + 1]
+        gaps = z[order[:-1]] - z[order[1:]]
+        j = int(np.argmin(gaps))
+        hi, lo = order[j], order[j + 1]
+        dz = np.zeros(n)
+        dz[hi] -= 0.51 * m
+        dz[lo] += 0.51 * m
+        assert not np.array_equal(H.topk_sorted(z + dz, k), base)
+
+
 # ------------------------------------------------------------------- heads
 
 def test_medusa_zero_init_reproduces_lm_head(golden):
@@ -506,6 +559,33 @@ def test_tree_attention_equals_causal_attention_per_branch(L, tree):
 
 
 # --------------------------------------------------------------- acceptance
+
+def test_target_logits_sum_over_query_heads():
+    """Z[b, u] = sum over query heads hq of W_t[:, hq D:(hq + 1) D] O[b, u, hq]
+    (the attention output is laid out head-major in the hidden vector), by
+    explicit loops and by torch's F.linear on the flattened rows. A D-major
+    flatten, or W_t used untransposed (a square W_t lets that run), fails."""
+    rng = np.random.default_rng(21)
+    for (B, N, Hq, D, V) in [(2, 5, 3, 4, 11), (1, 3, 2, 6, 12)]:  # the second has V = Hq D
+        O_ = rng.standard_normal((B, N, Hq, D))
+        Wt = rng.standard_normal((V, Hq * D))
+        Z = H.target_logits(O_, Wt)
+        ref = np.zeros((B, N, V))
+        for b in range(B):
+            for u in range(N):
+                for hq in range(Hq):
+                    for v in range(V):
+                        ref[b, u, v] += sum(Wt[v, hq * D + j] * O_[b, u, hq, j] for j in range(D))
+        assert Z.shape == (B, N, V)
+        assert np.allclose(Z, ref, rtol=1e-12, atol=1e-12)
+        lin = torch.nn.functional.linear(torch.from_numpy(O_.reshape(B, N, Hq * D)), torch.from_numpy(Wt)).numpy()
+        assert np.allclose(Z, lin, rtol=1e-12, atol=1e-12)
+        d_major = O_.transpose(0, 1, 3, 2).reshape(B, N, -1) @ Wt.T
+        assert not np.allclose(d_major, ref, atol=1e-6)
+        if V == Hq * D:
+            untransposed = O_.reshape(B, N, -1) @ Wt
+            assert not np.allclose(untransposed, ref, atol=1e-6)
+
 
 def _planted_Z(rng, plan, tok, path, stop_tok, V):
     Z = rng.standard_normal((plan.n, V))

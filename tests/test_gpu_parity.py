@@ -428,7 +428,7 @@ def test_rejection_planted_large_vocabulary(B, dtype):
             kids = plan.children(u)
             tok[b, kids] = g.choice(V, len(kids), replace=False)
         depth_t = int(g.integers(2, plan.dmax + 1))
-        r1_step = int(g.integers(0, depth_t))  # the step that takes a rank-1 child
+        r1_step = int(g.integers(0, 2))  # the step that takes a rank-1 child (nodes above depth 2 all have two or more)
         path = [0]
         for step in range(depth_t):
             kids = plan.children(path[-1])

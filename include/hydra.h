@@ -485,6 +485,26 @@ int tree_accept(int dtype, int mode, int B, int N, int d, int V, int Dmax,
                 int32_t* path, int32_t* out_tok, void* ws, size_t ws_bytes,
                 void* stream);
 
+/* tree_accept without a workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc). Same arguments, outputs and kernels as tree_accept; the
+ * scratch comes from a 32 MiB array the library holds on each GPU it runs on
+ * (until the process ends) instead of ws. Calls whose
+ * tree_accept_workspace_size(mode, B, N, V) exceeds 32 MiB return
+ * HYDRA_ERR_WORKSPACE before anything is enqueued. The first call with a
+ * device current looks up that device's array address (hipGetSymbolAddress);
+ * make it outside graph capture. All calls on one GPU share its array: calls
+ * that overlap in time on the same GPU (concurrent streams) race. Allocates
+ * nothing. */
+int tree_accept_noalloc(int dtype, int mode, int B, int N, int d, int V, int Dmax,
+                        const void* o, const void* W_t, float temperature,
+                        float eps, float delta, const int32_t* tok,
+                        const int32_t* parent, const int32_t* q_row,
+                        const float* head_logits, int R, const float* u_acc,
+                        const float* u_res, float* target_logits,
+                        int32_t* n_accepted, int32_t* path, int32_t* out_tok,
+                        void* stream);
+
 /* ------------------------------------------------------------------------
  * After acceptance: commit of the kept branch into the paged KV cache
  *

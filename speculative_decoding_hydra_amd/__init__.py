@@ -10,7 +10,7 @@ from .hydra import (  # noqa: F401
     hydra_draft_heads_attn_workspace_size, hydra_draft_heads_sketch,
     hydra_draft_heads_sketch_workspace_size, hydra_draft_heads_workspace_size,
     hydra_fold_embedding, hydra_plan_cartesian, hydra_plan_rows, hydra_plan_sparse, hydra_vocab_projection,
-    hydra_vocab_projection_workspace_size, hydra_vocab_topk, tree_accept,
+    hydra_vocab_projection_workspace_size, hydra_vocab_topk, tree_accept, tree_accept_noalloc,
     tree_accept_workspace_size, tree_attention_verify, tree_attention_verify_workspace_size, tree_build,
     tree_build_workspace_size, tree_commit, tree_decoder_layer, tree_decoder_layer_workspace_size, tree_rope,
     tree_rope_qk,

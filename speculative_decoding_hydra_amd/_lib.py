@@ -58,6 +58,9 @@ SIGNATURES = {
     "tree_accept": (c_int, [c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_void, c_void, c_float, c_float,
                             c_float, c_void, c_void, c_void, c_void, c_int, c_void, c_void, c_void, c_void, c_void,
                             c_void, c_void, c_size, c_void]),
+    "tree_accept_noalloc": (c_int, [c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_void, c_void, c_float,
+                                    c_float, c_float, c_void, c_void, c_void, c_void, c_int, c_void, c_void, c_void,
+                                    c_void, c_void, c_void, c_void]),
     "tree_commit": (c_int, [c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_void, c_void, c_void, c_void,
                             c_int, c_int, c_void, c_int, c_void, c_void, c_void, c_void, c_int, c_void, c_void,
                             c_void, c_void, c_void]),

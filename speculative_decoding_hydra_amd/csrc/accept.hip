@@ -25,6 +25,8 @@
 // breadth-first index among equals) and one token is drawn from p there.
 #include "walk.h"
 
+#include <mutex>
+
 namespace hydra {
 namespace {
 
@@ -966,4 +968,73 @@ extern "C" int tree_accept(int dtype, int mode, int B, int N, int d, int V, int 
     HY_LAUNCH_CHECK("tree_accept: rejection walk");
   }
   return HYDRA_OK;
+}
+
+// ------------------------------------------------------------------------
+// Allocation-free variant: the scratch tree_accept takes from a caller
+// workspace lives instead in this module's static device array, one copy per
+// GPU. Its device address is taken once per device (hipGetSymbolAddress, with
+// that device current) and kept; host code never passes the array's own name
+// to a kernel. Every call on a GPU shares that GPU's array and leaves its
+// contents behind; nothing in it has to start at zero (the walk counters are
+// cleared by the projection launch of the same call), and calls that overlap
+// on one GPU race.
+
+namespace hydra {
+namespace {
+
+constexpr size_t kNoAllocScratchBytes = static_cast<size_t>(32) << 20;  // 32 MiB
+constexpr int kNoAllocMaxDevices = 64;
+
+}  // namespace
+}  // namespace hydra
+
+static __device__ __align__(256) uint8_t scratch[hydra::kNoAllocScratchBytes];
+
+namespace hydra {
+namespace {
+
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kNoAllocMaxDevices] = {};
+
+// Device address of the current device's scratch array, looked up on the
+// first call made with that device current.
+int scratch_of_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  HY_CHECK(e == hipSuccess && dev >= 0 && dev < kNoAllocMaxDevices, HYDRA_ERR_HIP,
+           "tree_accept_noalloc: no usable current device (%s, device %d)", hipGetErrorString(e), dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    HY_CHECK(e == hipSuccess && p, HYDRA_ERR_HIP, "tree_accept_noalloc: hipGetSymbolAddress failed on device %d (%s)",
+             dev, hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return HYDRA_OK;
+}
+
+}  // namespace
+}  // namespace hydra
+
+extern "C" int tree_accept_noalloc(int dtype, int mode, int B, int N, int d, int V, int Dmax, const void* o,
+                                   const void* W_t, float temperature, float eps, float delta, const int32_t* tok,
+                                   const int32_t* parent, const int32_t* q_row, const float* head_logits, int R,
+                                   const float* u_acc, const float* u_res, float* target_logits,
+                                   int32_t* n_accepted, int32_t* path, int32_t* out_tok, void* stream) {
+  clear_error();
+  HY_CHECK(B > 0 && N > 0 && V > 0, HYDRA_ERR_INVALID, "tree_accept_noalloc: bad sizes B=%d N=%d V=%d", B, N, V);
+  const size_t need = tree_accept_workspace_size(mode, B, N, V);
+  HY_CHECK(need <= kNoAllocScratchBytes, HYDRA_ERR_WORKSPACE,
+           "tree_accept_noalloc: this call needs %zu bytes of scratch, more than the %zu the library holds per "
+           "device (use tree_accept with a workspace)",
+           need, kNoAllocScratchBytes);
+  void* ws = nullptr;
+  const int rc = scratch_of_current_device(&ws);
+  if (rc != HYDRA_OK) return rc;
+  return tree_accept(dtype, mode, B, N, d, V, Dmax, o, W_t, temperature, eps, delta, tok, parent, q_row,
+                     head_logits, R, u_acc, u_res, target_logits, n_accepted, path, out_tok, ws,
+                     kNoAllocScratchBytes, stream);
 }

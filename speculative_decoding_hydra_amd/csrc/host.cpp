@@ -82,7 +82,7 @@ extern "C" const char* hydra_status_string(int code) {
 
 extern "C" const char* hydra_last_error(void) { return g_last_error.c_str(); }
 
-extern "C" int hydra_abi_version(void) { return 8; }
+extern "C" int hydra_abi_version(void) { return 9; }
 
 extern "C" int hydra_plan_cartesian(const int32_t* b, int K, int max_nodes, int32_t* parent, int32_t* rank,
                                     int32_t* depth) {

@@ -532,6 +532,32 @@ def tree_accept(o, W_t, tok, parent, target_logits, n_accepted, path, out_tok, w
     return _check("tree_accept", rc)
 
 
+def tree_accept_noalloc(o, W_t, tok, parent, target_logits, n_accepted, path, out_tok, mode=0, temperature=1.0,
+                        q_row=None, head_logits=None, u_acc=None, u_res=None, eps=None, delta=None, stream=None):
+    """tree_accept with the library's per-GPU scratch instead of a workspace
+    (see include/hydra.h): for callers that cannot allocate."""
+    if mode == 2 and (eps is None or delta is None):
+        raise ValueError("tree_accept_noalloc: typical acceptance needs eps and delta")
+    B, N, d = o.shape
+    V = W_t.shape[0]
+    if W_t.dim() != 2 or W_t.shape[1] != d:
+        raise ValueError(f"tree_accept_noalloc: W_t {tuple(W_t.shape)} does not take rows of width {d}")
+    Dmax = path.shape[1] - 1
+    R = head_logits.shape[1] if head_logits is not None else 0
+    _shapes("tree_accept_noalloc", target_logits=(target_logits, (B, N, V)), tok=(tok, (B, N)),
+            parent=(parent, (B, N)), q_row=(q_row, (B, N)), head_logits=(head_logits, (B, R, V)),
+            u_acc=(u_acc, (B, N)), u_res=(u_res, (B, N)), n_accepted=(n_accepted, (B,)), path=(path, (B, Dmax + 1)),
+            out_tok=(out_tok, (B, Dmax + 1)))
+    rc = lib().tree_accept_noalloc(
+        _dtype_code(o), int(mode), B, N, d, V, Dmax, _dev(o, "o"), _dev(W_t, "W_t", o.dtype), float(temperature),
+        float(eps or 0.0), float(delta or 0.0), _dev(tok, "tok", torch.int32), _dev(parent, "parent", torch.int32),
+        _dev(q_row, "q_row", torch.int32), _dev(head_logits, "head_logits", torch.float32), R,
+        _dev(u_acc, "u_acc", torch.float32), _dev(u_res, "u_res", torch.float32),
+        _dev(target_logits, "target_logits", torch.float32), _dev(n_accepted, "n_accepted", torch.int32),
+        _dev(path, "path", torch.int32), _dev(out_tok, "out_tok", torch.int32), _stream(stream))
+    return _check("tree_accept_noalloc", rc)
+
+
 def tree_commit(k_tree, v_tree, k_pages, v_pages, block_table, prefix_len, n_accepted, path, out_tok,
                 next_prefix_len, next_root_tok, hidden=None, next_h=None, stream=None):
     """Kept branch into the paged KV cache (see include/hydra.h).

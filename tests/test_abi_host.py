@@ -54,7 +54,7 @@ def test_every_declared_symbol_is_exported_and_bound(lib):
 def test_status_strings(lib):
     assert lib.hydra_status_string(0) == b"ok"
     assert lib.hydra_status_string(-3) == b"workspace too small"
-    assert lib.hydra_abi_version() == 8
+    assert lib.hydra_abi_version() == 9
 
 
 @pytest.mark.parametrize("b", [[2, 3], [3, 2, 2], [4, 4, 4, 4], [1, 1, 1, 1, 1], [5, 2], [2, 1, 3]])

@@ -363,10 +363,13 @@ int tree_rope_qk(int dtype, int B, int N, int Hq, int Hkv, int D, const void* q,
  *                    sequence b lives in page block_table[b, p / page_size],
  *                    slot p % page_size
  * block_table        [B, max_pages] int32 page ids
- * prefix_len         [B] int32, each <= max_prefix_len and
- *                    <= max_pages * page_size; page ids must be < n_pages
- *                    (out-of-range ids and positions contribute nothing)
- * max_prefix_len     host bound on prefix_len (plans the split of the prefix)
+ * prefix_len         [B] int32; each sequence attends to its whole prefix,
+ *                    clamped to max_pages * page_size; page ids must be
+ *                    < n_pages (out-of-range ids contribute nothing)
+ * max_prefix_len     the longest prefix the caller expects: it sizes the
+ *                    split plan and the workspace only (each sequence cuts
+ *                    its own prefix into the planned number of ranges), so a
+ *                    longer prefix_len is still attended in full
  * anc                [B, N, Dmax+1] int32 from tree_build
  * depth              [B, N] int32 from tree_build
  * out                out [B, N, Hq, D] (dtype)

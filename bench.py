@@ -1,7 +1,7 @@
 """Throughput of one Hydra draft-and-verify round on one MI355X.
 
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--acceptance MODE] [--no-graph]
-                [--no-cpu] [--no-fold]
+                [--no-cpu] [--no-fold] [--no-configs]
 
 A step is one whole round (draft heads -> tree build -> rotary embedding of
 the tree Q/K rows at positions prefix + depth -> tree-attention verify ->
@@ -22,6 +22,12 @@ The JSON line also carries
                 shape (tree_decoder_layer; bytes, time, HBM fraction);
   commit_32_layers  the commit kernel moving each sequence's deepest kept
                 branch across 32 layers of caches (bytes, time, HBM fraction);
+  configs       the same round on the other workloads (7B dense 256-row
+                tree at prefix 8192, the 64-node tree at prefix 8192, 16
+                ragged sequences, the 70B GQA layer with rejection
+                acceptance) and the headline round with W1's embedding half
+                streamed: ms, verified rows/s and round HBM fraction each
+                (their inputs are drawn on the device; --no-configs skips);
   cpu_baseline  the CPU oracle timed on this host on one full round of the
                 same workload (rank 0, one GPU only).
 """
@@ -55,6 +61,7 @@ def parse():
                     help="override the workload's acceptance mode")
     ap.add_argument("--no-fold", action="store_true",
                     help="stream W1[:, d:] every round instead of the folded embedding tables")
+    ap.add_argument("--no-configs", action="store_true", help="skip the other workloads' rounds")
     return ap.parse_args()
 
 
@@ -230,6 +237,92 @@ def layer_measure(w, rnd, dev, stream, reps=10, use_graph=True):
             "achieved_GBps": nbytes / (us * 1e-6) / 1e9, "frac_of_hbm_peak": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS}
 
 
+def time_round(rnd, dev, steps, warmup, use_graph=True):
+    """Mean ms per round over `steps` graph-replayed rounds (after `warmup`),
+    the graph (or None) and the per-round event distribution."""
+    import torch
+
+    from speculative_decoding_hydra_amd import run_round
+
+    stream = torch.cuda.current_stream()
+    for _ in range(max(1, warmup)):
+        run_round(rnd, dev)
+    torch.cuda.synchronize()
+    graph = None
+    if use_graph:
+        try:
+            s = torch.cuda.Stream()
+            s.wait_stream(stream)
+            with torch.cuda.stream(s):
+                run_round(rnd, dev)
+            stream.wait_stream(s)
+            torch.cuda.synchronize()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                run_round(rnd, dev)
+            torch.cuda.synchronize()
+            for _ in range(max(1, warmup)):
+                graph.replay()
+            torch.cuda.synchronize()
+        except Exception as e:  # noqa: BLE001
+            log(f"[bench] graph capture unavailable ({e}); timing eager launches")
+            graph = None
+    step = graph.replay if graph is not None else (lambda: run_round(rnd, dev))
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) / steps * 1e3
+    rev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    rev[0].record(stream)
+    for i in range(steps):
+        step()
+        rev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    per = sorted(rev[i].elapsed_time(rev[i + 1]) for i in range(steps))
+    pick = lambda q: per[min(len(per) - 1, int(q * len(per)))]  # noqa: E731
+    return ms, graph, {"median": pick(0.5), "p10": pick(0.1), "p90": pick(0.9)}
+
+
+# the other workloads of the same round, each on its own synthetic inputs
+# (drawn on the device); the first uses the headline's inputs with the
+# embedding half of W1 streamed every round instead of the folded tables
+CONFIGS = ["7b_sparse64:streamed", "7b_dense256", "7b_sparse64_L8192", "7b_batched16", "70b_gqa"]
+
+
+def configs_measure(head_inp, steps, warmup, use_graph=True):
+    import torch
+
+    import hydra_inputs as HI
+    from speculative_decoding_hydra_amd import round_from_inputs
+
+    out = {}
+    for spec in CONFIGS:
+        name, _, variant = spec.partition(":")
+        t0 = time.perf_counter()
+        w = HI.workload(name)
+        inp = head_inp if variant == "streamed" else HI.generate(w, device="cuda")
+        rnd, dev = round_from_inputs(inp, device="cuda:0", keep_hidden=False,
+                                     fold_embedding=False if variant == "streamed" else None)
+        ms, graph, dist = time_round(rnd, dev, steps, warmup, use_graph)
+        rows = w.B * rnd.n_keep
+        rb = round_bytes(w, rnd, inp["prefix_len"].cpu())
+        out[spec] = {"ms_per_round": ms, "round_ms": dist, "tokens_per_s": rows / (ms * 1e-3), "tree_rows": rows,
+                     "round_bytes": rb, "round_hbm_frac": rb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                     "acceptance": w.mode, "embedding_half": ("folded table" if rnd.emb_proj is not None
+                                                              else "streamed") if w.hydra else None,
+                     "launch": "hip-graph" if graph is not None else "eager"}
+        log(f"[bench] {spec}: {ms:.4f} ms/round ({time.perf_counter() - t0:.1f} s)")
+        del graph, rnd, dev
+        if inp is not head_inp:
+            del inp
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(inp, n_rows):
     """The oracle, as it stands, on one full round of the same workload."""
     import numpy as np
@@ -311,7 +404,7 @@ def main():
 
     import hydra_inputs as HI
     from speculative_decoding_hydra_amd import (hydra_vocab_projection, hydra_vocab_projection_workspace_size,
-                                                 round_from_inputs, run_round)
+                                                 round_from_inputs)
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
@@ -325,57 +418,8 @@ def main():
     N = rnd.n_keep
     rows = w.B * N
     stream = torch.cuda.current_stream()
-
-    for _ in range(max(1, args.warmup)):
-        run_round(rnd, dev)
-    torch.cuda.synchronize()
-
-    graph = None
-    if not args.no_graph:
-        try:
-            s = torch.cuda.Stream()
-            s.wait_stream(stream)
-            with torch.cuda.stream(s):
-                run_round(rnd, dev)
-            stream.wait_stream(s)
-            torch.cuda.synchronize()
-            graph = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(graph):
-                run_round(rnd, dev)
-            torch.cuda.synchronize()
-            for _ in range(max(1, args.warmup)):
-                graph.replay()
-            torch.cuda.synchronize()
-        except Exception as e:  # noqa: BLE001
-            log(f"[bench] graph capture unavailable ({e}); timing eager launches")
-            graph = None
-
-    log(f"[bench] timing {args.steps} rounds ({'graph' if graph else 'eager'})")
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        if graph is not None:
-            graph.replay()
-        else:
-            run_round(rnd, dev)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    ms = elapsed / args.steps * 1e3
-
-    # per-round distribution: the same rounds again, each between two events
-    rev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
-    torch.cuda.synchronize()
-    rev[0].record(stream)
-    for i in range(args.steps):
-        if graph is not None:
-            graph.replay()
-        else:
-            run_round(rnd, dev)
-        rev[i + 1].record(stream)
-    torch.cuda.synchronize()
-    per = sorted(rev[i].elapsed_time(rev[i + 1]) for i in range(args.steps))
-    pick = lambda q: per[min(len(per) - 1, int(q * len(per)))]  # noqa: E731
-    round_ms = {"median": pick(0.5), "p10": pick(0.1), "p90": pick(0.9)}
+    ms, graph, round_ms = time_round(rnd, dev, args.steps, args.warmup, use_graph=not args.no_graph)
+    log(f"[bench] {w.name}: {ms:.4f} ms/round ({'graph' if graph else 'eager'})")
 
     # per-stage times (eager, events on the launch stream)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
@@ -456,6 +500,9 @@ def main():
     commit = commit_measure(w, rnd, dev, stream, use_graph=not args.no_graph)
     layer = layer_measure(w, rnd, dev, stream, use_graph=not args.no_graph)
     rbytes = round_bytes(w, rnd, inp["prefix_len"])
+    configs = None
+    if not args.no_configs and args.workload == "7b_sparse64" and not args.no_fold:
+        configs = configs_measure(inp, args.steps, args.warmup, use_graph=not args.no_graph)
     cpu = None
     if not args.no_cpu:
         log("[bench] timing the CPU oracle on one round")
@@ -482,7 +529,8 @@ def main():
                    if w.hydra else None},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(),
-                     "kernel": "proj_bf16_kernel (vocabulary projection, fused top-k epilogue)",
+                     "kernel": ("proj_bf16_kernel (streaming vocabulary projection, fused top-k epilogue)"
+                                if M < 65 else "proj_gemm_kernel (tiled vocabulary projection, fused top-k epilogue)"),
                      "bytes_per_launch": alg_bytes, "rows": M, "topk": kk, "avg_launch_ms": k_ms},
         "round_ms": round_ms,
         "round_bytes": rbytes,
@@ -491,6 +539,7 @@ def main():
                       "accept": stage_ms[3], "commit": stage_ms[4]},
         "commit_32_layers": commit,
         "decoder_layer": layer,
+        "configs": configs,
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)

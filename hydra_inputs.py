@@ -30,7 +30,10 @@ in this fixed order:
  12. Hydra++ fusion only: Wqkv [3d, d], then Wo [d, d], ~ N(0, 0.02)
 
 Draws are float32; bfloat16 workloads round them to bfloat16 (round to
-nearest even, torch's conversion).
+nearest even, torch's conversion). ``generate(w, device="cuda")`` makes the
+same draws in the same order from a generator on that device (same shapes,
+distributions and seed, different numbers): the benchmark's extra workloads
+use it to skip the host-side draws; parity tests use the host default.
 """
 from __future__ import annotations
 
@@ -129,25 +132,27 @@ def workload(name: str, **overrides) -> Workload:
 
 
 def _normal(g, shape, std, dtype):
-    x = torch.randn(shape, generator=g, dtype=torch.float32)
+    x = torch.randn(shape, generator=g, dtype=torch.float32, device=g.device)
     if std != 1.0:
         x.mul_(std)
     return x.to(dtype)
 
 
-def generate(w: Workload, n_tree: int | None = None, reserve: int | None = None) -> dict:
-    """Draw every input of one round for workload ``w`` (CPU tensors).
+def generate(w: Workload, n_tree: int | None = None, reserve: int | None = None, device=None) -> dict:
+    """Draw every input of one round for workload ``w`` (CPU tensors, or on
+    ``device`` from a generator there).
 
     Each sequence's block table maps pages for its prefix plus ``reserve``
     more positions (default: one round's commit, n_heads + 1 rows), zeroed.
     """
     if reserve is None:
         reserve = w.n_heads + 1
-    g = torch.Generator().manual_seed(w.seed)
+    g = torch.Generator(device=device or "cpu").manual_seed(w.seed)
+    on = g.device
     dt = w.torch_dtype
     N = w.n_tree if n_tree is None else n_tree
     out = {"workload": w, "N": N}
-    out["root_tok"] = torch.randint(0, w.V, (w.B,), generator=g, dtype=torch.int64).to(torch.int32)
+    out["root_tok"] = torch.randint(0, w.V, (w.B,), generator=g, dtype=torch.int64, device=on).to(torch.int32)
     out["h"] = _normal(g, (w.B, w.d), 1.0, dt)
     out["E"] = _normal(g, (w.V, w.d), 1.0, dt)
     in_dim = 2 * w.d if w.hydra else w.d
@@ -170,8 +175,8 @@ def generate(w: Workload, n_tree: int | None = None, reserve: int | None = None)
     if len(w.L) == 1:
         lens = [w.L[0]] * w.B
     else:
-        lens = torch.randint(w.L[0], w.L[1] + 1, (w.B,), generator=g).tolist()
-    out["prefix_len"] = torch.tensor(lens, dtype=torch.int32)
+        lens = torch.randint(w.L[0], w.L[1] + 1, (w.B,), generator=g, device=on).tolist()
+    out["prefix_len"] = torch.tensor(lens, dtype=torch.int32, device=on)
     kp, vp = [], []
     for L in lens:
         kp.append(_normal(g, (L, w.Hkv, w.D), 1.0, dt))
@@ -180,13 +185,13 @@ def generate(w: Workload, n_tree: int | None = None, reserve: int | None = None)
     pages_per = [math.ceil((L + reserve) / PAGE) for L in lens]
     n_pages = max(1, sum(pages_per))
     if w.scattered:
-        order = torch.randperm(n_pages, generator=g).to(torch.int32)
+        order = torch.randperm(n_pages, generator=g, device=on).to(torch.int32).cpu()
     else:
         order = torch.arange(n_pages, dtype=torch.int32)
     max_pages = max(1, max(pages_per))
     block_table = torch.full((w.B, max_pages), -1, dtype=torch.int32)
-    k_pages = torch.zeros((n_pages, w.Hkv, PAGE, w.D), dtype=dt)
-    v_pages = torch.zeros((n_pages, w.Hkv, PAGE, w.D), dtype=dt)
+    k_pages = torch.zeros((n_pages, w.Hkv, PAGE, w.D), dtype=dt, device=on)
+    v_pages = torch.zeros((n_pages, w.Hkv, PAGE, w.D), dtype=dt, device=on)
     nxt = 0
     for b, L in enumerate(lens):
         for j in range(pages_per[b]):
@@ -197,15 +202,15 @@ def generate(w: Workload, n_tree: int | None = None, reserve: int | None = None)
             if hi > lo:  # pages past the prefix stay zero (the reserve)
                 k_pages[pid, :, : hi - lo] = kp[b][lo:hi].transpose(0, 1)
                 v_pages[pid, :, : hi - lo] = vp[b][lo:hi].transpose(0, 1)
-    out["block_table"], out["k_pages"], out["v_pages"] = block_table, k_pages, v_pages
+    out["block_table"], out["k_pages"], out["v_pages"] = block_table.to(on), k_pages, v_pages
     out["page_size"] = PAGE
 
     out["q_tree"] = _normal(g, (w.B, N, w.Hq, w.D), 1.0, dt)
     out["k_tree"] = _normal(g, (w.B, N, w.Hkv, w.D), 1.0, dt)
     out["v_tree"] = _normal(g, (w.B, N, w.Hkv, w.D), 1.0, dt)
     if w.mode in ("stochastic", "typical"):
-        out["u_acc"] = torch.rand((w.B, N), generator=g, dtype=torch.float32)
-        out["u_res"] = torch.rand((w.B, N), generator=g, dtype=torch.float32)
+        out["u_acc"] = torch.rand((w.B, N), generator=g, dtype=torch.float32, device=on)
+        out["u_res"] = torch.rand((w.B, N), generator=g, dtype=torch.float32, device=on)
     if w.head == "sketch":
         # drawn last so the other inputs of a seed do not move; LayerNorm gain
         # near 1 and bias near 0 (not exactly, so both take part)

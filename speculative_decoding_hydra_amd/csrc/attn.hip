@@ -8,10 +8,17 @@
 // verifying k rows costs about as much as a prompt of length k, so all tree
 // rows share one pass over the KV prefix.
 //
-// gfx950 design (bf16, D = 128):
-//   * the query rows of a KV head are (node u, query head g) pairs, so GQA
-//     packs the G query heads into the same tile; every wave owns 64 of them
-//     as two 32-column tiles of v_mfma_f32_32x32x16_bf16;
+// gfx950 design (bf16, D = 128). The query rows of a KV head are (node u,
+// query head g) pairs, so GQA packs the G query heads into the same tile.
+// Two kernels, chosen by the query rows per KV head:
+//   * up to 64 (the MHA trees of 64 nodes): attn_split_mfma, a small
+//     streaming kernel (K/V through registers into LDS, 16x16x32 MFMAs, the
+//     tree rows as one extra split) of which two workgroups share a CU; it
+//     hides the prefix stream's latency better at these few rows;
+//   * more (256-row trees, GQA): attn_tile_mfma, below.
+// attn_tile_mfma:
+//   * every wave owns 32 query rows as one 32-column tile of
+//     v_mfma_f32_32x32x16_bf16;
 //   * the keys of a (sequence, KV head) are cut into splits; a split takes a
 //     range of the paged prefix and a share of the tree keys, so no split is
 //     tree-only; one workgroup (4 waves) per split and query tile;
@@ -26,10 +33,11 @@
 //     layout of O^T = V^T . P^T; V^T comes from the row-major V tile through
 //     gfx950's transposing LDS read (ds_read_b64_tr_b16), with the keys of a
 //     16-key step permuted identically on both operands;
-//   * with 64 query rows or fewer the four waves split the keys and merge
-//     their states in LDS; with more they split the queries and share every
-//     K/V tile; the two 256-row query tiles of one split run on the same XCD
-//     (workgroup ids 8 apart), so the second one reads the tiles from L2;
+//   * eight waves per workgroup split the queries and share every K/V tile
+//     (up to 256 rows), or split the keys into groups that merge their
+//     states in LDS at the end (128 rows: two groups); the query tiles of one
+//     split run on the same XCD (workgroup ids 8 apart), so all but the first
+//     read the tiles from L2;
 //   * the tree keys are masked by the ancestor table (v visible to u iff
 //     anc[u][depth v] == v), no dense mask;
 //   * splits write unnormalised partials; a combine kernel merges them with
@@ -538,6 +546,395 @@ __global__ __launch_bounds__(64 * WQ * WK, 1) void attn_tile_mfma(AttnArgs a) {
   }
 }
 
+constexpr int kMaxSplitPages = 1024;  // page ids a split of the streaming kernel stages in LDS
+
+__device__ __forceinline__ uint32_t pack2(uint16_t lo, uint16_t hi) {
+  return static_cast<uint32_t>(lo) | (static_cast<uint32_t>(hi) << 16);
+}
+
+// max / sum over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (one query column
+// of a 16 x 16 S^T tile): the gfx950 row swaps hand every lane its partner's
+// value in a VALU step
+__device__ __forceinline__ float col_max(float v) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float col_sum(float v) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// Streaming kernel for up to 64 query rows per KV head (the 64-node MHA
+// trees): NW waves of RT 16-row query tiles each (16 NW RT query rows); a
+// thread loads KPT keys x 8 dims of K and V into registers, so a tile holds
+// 4 NW KPT keys, and PD tiles are in flight; 16x16x32 MFMAs on S^T = K Q^T
+// and O^T = V^T P^T with V transposed into LDS as it is stored; the tree rows
+// are one extra split of their own, masked by the ancestor table. Small
+// (about 40 KB of LDS) so that two workgroups share a CU and the tree split
+// overlaps the prefix splits.
+template <int NW, int RT, int PD, int KPT>
+__global__ __launch_bounds__(NW * 64, 2) void attn_split_mfma(
+    int B, int N, int Hq, int Hkv, float scale_log2, const bf16_t* __restrict__ q,
+    const bf16_t* __restrict__ k_tree, const bf16_t* __restrict__ v_tree,
+    const bf16_t* __restrict__ k_pages, const bf16_t* __restrict__ v_pages, int n_pages,
+    int page_shift, const int32_t* __restrict__ block_table, int max_pages,
+    const int32_t* __restrict__ prefix_len, const int32_t* __restrict__ anc,
+    const int32_t* __restrict__ depth, int Dmax, int nsplit, int NQ, int NQpad,
+    float* __restrict__ opart, float* __restrict__ mpart, float* __restrict__ lpart) {
+  constexpr int D = 128;
+  constexpr int NT = NW * 64;
+  constexpr int QR = NW * RT * 16;   // query rows per workgroup
+  constexpr int TK = NT / 16 * KPT;  // keys per tile
+  // K rows in LDS are 256 bytes with the 16-byte chunk c of key r at position
+  // c ^ 2 (r % 8): the 16-row operand reads then hit distinct banks (padded
+  // rows cost a two-way conflict on gfx950). V^T rows are TK + 4 bf16 with
+  // column groups of 4 XOR-ed by (row / 8) % 16, which spreads the transposing
+  // writes (16 rows 8 apart per instruction) over the banks.
+  constexpr int KROW = D;
+  constexpr int VROW = TK + 4;
+  constexpr int DJ = D / 32;
+  constexpr int DD = D / 16;
+  static_assert(TK % 64 == 0, "tiles hold whole 64-key steps");
+  __shared__ __align__(16) bf16_t klds[TK * KROW];
+  __shared__ __align__(16) bf16_t vlds[D * VROW];
+  __shared__ __align__(16) uint8_t s_ok[TK];              // key of the tile exists (range and page)
+  __shared__ __align__(16) int s_dep[TK];                 // depth of each tree key of the tile
+  __shared__ int s_pages[kMaxSplitPages];                 // page ids of this split
+  __shared__ int s_anc[QR][HYDRA_MAX_DEPTH + 1];          // ancestor rows of the workgroup's query rows
+
+  const int split = blockIdx.x;
+  const bool tree_part = split == nsplit;
+  const int qtile = blockIdx.y;
+  const int b = blockIdx.z / Hkv;
+  const int hkv = blockIdx.z % Hkv;
+  const int G = Hq / Hkv;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, lq = lane & 15;
+  const int kx = (lq & 7) << 1;  // K chunk swizzle of this lane's key rows
+  const int page_size = 1 << page_shift;
+
+  int wrow[RT];  // this lane's query rows inside the workgroup
+  bf16x8_t qreg[RT][DJ];
+#pragma unroll
+  for (int r = 0; r < RT; ++r) {
+    wrow[r] = (wave * RT + r) * 16 + lq;
+    const int qi = qtile * QR + wrow[r];
+    const bool qvalid = qi < NQ;
+    const int u = qvalid ? qi / G : 0;
+    const int gq = qi % G;
+    const bf16_t* qp = q + ((static_cast<size_t>(b) * N + u) * Hq + hkv * G + gq) * D + 8 * g;
+#pragma unroll
+    for (int j = 0; j < DJ; ++j) {
+      const u32x4_t v = qvalid ? *reinterpret_cast<const u32x4_t*>(qp + 32 * j) : u32x4_t{0u, 0u, 0u, 0u};
+      qreg[r][j] = __builtin_bit_cast(bf16x8_t, v);
+    }
+  }
+
+  // this split's share of the sequence's own prefix (the split count is
+  // planned, the range length follows the sequence), in windows whose page
+  // ids fit the LDS staging area
+  int L = prefix_len[b];
+  const int cap = max_pages << page_shift;
+  L = L < 0 ? 0 : (L > cap ? cap : L);
+  const int lsp = nsplit > 0 ? ((L + nsplit - 1) / nsplit + TK - 1) / TK * TK : 0;
+  const int s_begin = tree_part ? 0 : min(L, split * lsp);
+  const int s_end = tree_part ? N : min(L, s_begin + lsp);
+  constexpr int kWinKeys = (kMaxSplitPages - 1) * 16 / TK * TK;
+  const int32_t* dep_b = depth + static_cast<size_t>(b) * N;
+  if (tree_part) {
+    for (int e = tid; e < QR * (Dmax + 1); e += NT) {
+      const int rr = e / (Dmax + 1), j = e % (Dmax + 1);
+      const int qr = qtile * QR + rr;
+      s_anc[rr][j] = qr < NQ ? anc[(static_cast<size_t>(b) * N + qr / G) * (Dmax + 1) + j] : -1;
+    }
+  }
+
+  float m_run[RT], l_run[RT];
+  f32x4_t oacc[RT][DD];
+#pragma unroll
+  for (int r = 0; r < RT; ++r) {
+    m_run[r] = -INFINITY;
+    l_run[r] = 0.f;
+#pragma unroll
+    for (int dd = 0; dd < DD; ++dd) oacc[r][dd] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+
+  for (int wb = s_begin;; wb += kWinKeys) {
+  const int t_begin = wb;
+  const int t_end = tree_part ? s_end : min(s_end, wb + kWinKeys);
+  const int p0 = t_begin >> page_shift;
+  if (wb > s_begin) __syncthreads();  // the previous window's tiles are consumed
+  int pages_bad = 0;
+  if (!tree_part) {
+    const int np = t_end > t_begin ? ((t_end - 1) >> page_shift) - p0 + 1 : 0;
+    for (int e = tid; e < np; e += NT) {
+      const int pg = block_table[static_cast<size_t>(b) * max_pages + p0 + e];
+      s_pages[e] = pg;
+      pages_bad |= pg < 0 || pg >= n_pages;
+    }
+  }
+  // every page of the window valid: whole tiles then need no mask (the
+  // barrier also publishes the ancestor rows)
+  const bool pages_ok = __syncthreads_or(pages_bad) == 0;
+
+  // loader mapping: KPT consecutive keys (one page, page_size >= 16) x 8 dims
+  const int tg = tid >> 4;  // key group 0 .. NT / 16 - 1
+  const int dc = tid & 15;  // 8-dim chunk 0..15
+  const int tl = KPT * tg;
+  const size_t page_stride = static_cast<size_t>(Hkv) << (page_shift + 7);  // Hkv * page_size * D
+  const size_t head_off = (static_cast<size_t>(hkv) << (page_shift + 7)) + dc * 8;
+  const size_t tree_off = (static_cast<size_t>(b) * N * Hkv + hkv) * D + dc * 8;
+
+  u32x4_t kv[PD][KPT], vv[PD][KPT];
+  int kvalid[PD];
+  // Registers of a coming tile: KPT keys x 8 dims of K and of V per thread.
+  // Loads are unconditional (invalid keys re-read a valid row and are masked
+  // through s_ok), so the compiler can keep them in flight across the tile.
+  auto load_tile = [&](auto SLOT, auto WHOLE, int t0) __attribute__((always_inline)) {
+    constexpr int sl = decltype(SLOT)::value;
+    constexpr bool whole = decltype(WHOLE)::value;
+    const int tk = t0 + tl;
+    const bf16_t* kb;
+    const bf16_t* vb;
+    size_t stride;
+    int valid = KPT;
+    if (!whole) valid = tk < t_end ? min(KPT, t_end - tk) : 0;
+    if (tree_part) {
+      const int tc = valid > 0 ? tk : 0;
+      const size_t off = tree_off + static_cast<size_t>(tc) * Hkv * D;
+      kb = k_tree + off;
+      vb = v_tree + off;
+      stride = static_cast<size_t>(Hkv) * D;
+    } else {
+      const int tc = valid > 0 ? tk : t_begin;
+      int pg = s_pages[(tc >> page_shift) - p0];
+      if (!whole && (pg < 0 || pg >= n_pages)) {
+        pg = 0;
+        valid = 0;
+      }
+      const size_t off = pg * page_stride + head_off + (static_cast<size_t>(tc & (page_size - 1)) << 7);
+      kb = k_pages + off;
+      vb = v_pages + off;
+      stride = D;
+    }
+    kvalid[sl] = valid;
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      const size_t o = whole || j < valid ? j * stride : 0;
+      kv[sl][j] = *reinterpret_cast<const u32x4_t*>(kb + o);
+      vv[sl][j] = *reinterpret_cast<const u32x4_t*>(vb + o);
+    }
+  };
+
+  // one 64-key step of a staged tile: S^T, online softmax, P.V. MASKED reads
+  // key validity (and in the tree split the ancestor test) per score.
+  auto step = [&](auto MASKED, int c0, int t0) __attribute__((always_inline)) {
+    constexpr bool masked = decltype(MASKED)::value;
+    // S^T tiles: lane holds keys c0 + 16 tt + 4 g + i for query column lq
+    f32x4_t sacc[RT][4];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+#pragma unroll
+      for (int r = 0; r < RT; ++r) sacc[r][tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < DJ; ++j) {
+        const u32x4_t a = *reinterpret_cast<const u32x4_t*>(&klds[(c0 + 16 * tt + lq) * KROW + (((4 * j + g) ^ kx) << 3)]);
+#pragma unroll
+        for (int r = 0; r < RT; ++r)
+          sacc[r][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), qreg[r][j],
+                                                               sacc[r][tt], 0, 0, 0);
+      }
+    }
+    uint32_t okb[RT];  // bit 4 tt + i: score (tt, i) of row tile r is visible
+    if constexpr (masked) {
+      uint32_t base = 0;
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
+        const uint32_t w = *reinterpret_cast<const uint32_t*>(&s_ok[c0 + 16 * tt + 4 * g]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) base |= ((w >> (8 * i)) & 1u) << (4 * tt + i);
+      }
+#pragma unroll
+      for (int r = 0; r < RT; ++r) okb[r] = base;
+      if (tree_part) {
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+          const int4 d4 = *reinterpret_cast<const int4*>(&s_dep[c0 + 16 * tt + 4 * g]);
+          const int dvs[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int dv = dvs[i];
+            const int dvc = dv < 0 ? 0 : (dv > Dmax ? Dmax : dv);
+#pragma unroll
+            for (int r = 0; r < RT; ++r) {
+              const bool vis = dv == dvc && s_anc[wrow[r]][dvc] == t0 + c0 + 16 * tt + 4 * g + i;
+              okb[r] &= vis ? ~0u : ~(1u << (4 * tt + i));
+            }
+          }
+        }
+      }
+    }
+    bf16x8_t pb[RT][2];
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+      // raw scores; the scale (> 0) is folded into the exponent below
+      float mt = -INFINITY;
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if constexpr (masked) sacc[r][tt][i] = (okb[r] >> (4 * tt + i)) & 1u ? sacc[r][tt][i] : -INFINITY;
+          mt = fmaxf(mt, sacc[r][tt][i]);
+        }
+      }
+      mt = col_max(mt) * scale_log2;
+      const bool grow = mt > m_run[r] + kRescaleSlack;
+      const float m_new = grow ? fmaxf(m_run[r], mt) : m_run[r];
+      if (__any(grow)) {  // wave-uniform: rescale only when an offset moved
+        const float alpha = m_new == m_run[r] ? 1.f : __builtin_amdgcn_exp2f(m_run[r] - m_new);
+        l_run[r] *= alpha;
+#pragma unroll
+        for (int dd = 0; dd < DD; ++dd) oacc[r][dd] *= alpha;
+        m_run[r] = m_new;
+      }
+      const float neg_m = m_new == -INFINITY ? 0.f : -m_new;
+      float sv[4][4];
+      float ps = 0.f;
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float pe = __builtin_amdgcn_exp2f(fmaf(sacc[r][tt][i], scale_log2, neg_m));
+          sv[tt][i] = pe;
+          ps += pe;
+        }
+      l_run[r] += col_sum(ps);
+      // P^T operands: slots 0..3 = keys 32 ks + 4 g + i, slots 4..7 = keys 32 ks + 16 + 4 g + i
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          pb[r][ks][i] = static_cast<__bf16>(sv[2 * ks][i]);
+          pb[r][ks][4 + i] = static_cast<__bf16>(sv[2 * ks + 1][i]);
+        }
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+      for (int dd = 0; dd < DD; ++dd) {
+        const int vrow = 16 * dd + lq;
+        const int vx = ((vrow >> 3) & 15) << 2;
+        const int col = c0 + 32 * ks + 4 * g;
+        u32x4_t a;
+        const u32x2_t lo = *reinterpret_cast<const u32x2_t*>(&vlds[vrow * VROW + (col ^ vx)]);
+        const u32x2_t hi = *reinterpret_cast<const u32x2_t*>(&vlds[vrow * VROW + ((col + 16) ^ vx)]);
+        a.x = lo.x;
+        a.y = lo.y;
+        a.z = hi.x;
+        a.w = hi.y;
+#pragma unroll
+        for (int r = 0; r < RT; ++r)
+          oacc[r][dd] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), pb[r][ks],
+                                                               oacc[r][dd], 0, 0, 0);
+      }
+    }
+  };
+
+  // one tile: stage slot SLOT in LDS (with the validity / depth bytes unless
+  // WHOLE), refill the slot PD tiles ahead, then its 64-key steps
+  auto process = [&](auto SLOT, auto WHOLE, int t0) __attribute__((always_inline)) {
+    constexpr int sl = decltype(SLOT)::value;
+    constexpr bool whole = decltype(WHOLE)::value;
+    __syncthreads();  // previous tile fully consumed
+    if (!whole && dc == 0) {
+#pragma unroll
+      for (int j = 0; j < KPT; ++j) {
+        s_ok[tl + j] = j < kvalid[sl];
+        if (tree_part) s_dep[tl + j] = j < kvalid[sl] ? dep_b[t0 + tl + j] : -1;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < KPT; ++j)
+      *reinterpret_cast<u32x4_t*>(&klds[(tl + j) * KROW + ((dc ^ (((tl + j) & 7) << 1)) << 3)]) = kv[sl][j];
+    {
+      typedef __attribute__((ext_vector_type(8))) uint16_t u16x8;
+      u16x8 a[KPT];
+#pragma unroll
+      for (int j = 0; j < KPT; ++j) a[j] = __builtin_bit_cast(u16x8, vv[sl][j]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        if constexpr (KPT == 4) {
+          u32x2_t w;
+          w.x = pack2(a[0][e], a[1][e]);
+          w.y = pack2(a[2][e], a[3][e]);
+          *reinterpret_cast<u32x2_t*>(&vlds[(dc * 8 + e) * VROW + (tl ^ ((dc & 15) << 2))]) = w;
+        } else {
+          *reinterpret_cast<uint32_t*>(&vlds[(dc * 8 + e) * VROW + (tl ^ ((dc & 15) << 2))]) =
+              pack2(a[0][e], a[1][e]);
+        }
+      }
+    }
+    __syncthreads();
+    const int tn = t0 + PD * TK;
+    if (tn < t_end) {
+      // the refill is whole too when it lies entirely inside a clean split
+      if (whole && tn + TK <= t_end) load_tile(SLOT, std::true_type{}, tn);
+      else load_tile(SLOT, std::false_type{}, tn);
+    }
+    for (int c = 0; c < TK / 64; ++c) step(std::integral_constant<bool, !whole>{}, 64 * c, t0);
+  };
+
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, PD - 1>;
+  using Whole = std::true_type;
+  using Part = std::false_type;
+  // whole prefix tiles over valid pages run unmasked in a loop of their own
+  // (pairs of them when two are in flight), the rest masked
+  const int ntiles = t_end > t_begin ? (t_end - t_begin + TK - 1) / TK : 0;
+  const int nwhole = tree_part || !pages_ok ? 0 : (t_end - t_begin) / TK / PD * PD;
+  if (ntiles > 0) {
+    if (nwhole > 0) load_tile(S0{}, Whole{}, t_begin);
+    else load_tile(S0{}, Part{}, t_begin);
+  }
+  if (PD > 1 && ntiles > 1) {
+    if (nwhole > 1) load_tile(S1{}, Whole{}, t_begin + TK);
+    else load_tile(S1{}, Part{}, t_begin + TK);
+  }
+  int it = 0;
+  for (; it < nwhole; it += PD) {
+    process(S0{}, Whole{}, t_begin + it * TK);
+    if (PD > 1) process(S1{}, Whole{}, t_begin + (it + 1) * TK);
+  }
+  for (; it < ntiles; it += PD) {
+    process(S0{}, Part{}, t_begin + it * TK);
+    if (PD > 1 && it + 1 < ntiles) process(S1{}, Part{}, t_begin + (it + 1) * TK);
+  }
+
+  if (tree_part || t_end >= s_end) break;
+  }
+
+#pragma unroll
+  for (int r = 0; r < RT; ++r) {
+    const int qi = qtile * QR + wrow[r];
+    if (qi < NQ) {
+      const size_t row = (static_cast<size_t>(split * B + b) * Hkv + hkv) * NQpad + qi;
+#pragma unroll
+      for (int dd = 0; dd < DD; ++dd)
+        *reinterpret_cast<float4*>(opart + row * D + 16 * dd + 4 * g) =
+            make_float4(oacc[r][dd][0], oacc[r][dd][1], oacc[r][dd][2], oacc[r][dd][3]);
+      if (g == 0) {
+        mpart[row] = m_run[r];
+        lpart[row] = l_run[r];
+      }
+    }
+  }
+}
+
+
 // Merge the splits of one (sequence, KV head, query row). D / 4 lanes per row,
 // four dims per lane, so a wave merges 64 * 4 / D rows at once; the parts are
 // read in batches of CB so their loads overlap.
@@ -724,7 +1121,35 @@ TilePlan plan_tiles(int B, int N, int Hq, int Hkv, int max_prefix_len) {
   return p;
 }
 
+// Streaming kernel plan (up to 64 query rows per KV head): about 512
+// workgroups, each split at least four 64-key tiles (and at most 16) of the
+// planned prefix, at least one split so that prefixes beyond the plan are
+// still covered; the tree rows are the extra split.
+struct SplitPlan {
+  int nsplit, NQ, NQpad;
+};
+SplitPlan plan_splits(int B, int N, int Hq, int Hkv, int max_prefix_len) {
+  constexpr int TK = 64;
+  SplitPlan p;
+  p.NQ = N * (Hq / Hkv);
+  p.NQpad = 64;
+  const int base = B * Hkv;
+  const int Lr = max_prefix_len > 0 ? max_prefix_len : 0;
+  int s = 512 / base - 1;  // the tree split takes one slot
+  const int maxs = (Lr + 4 * TK - 1) / (4 * TK);
+  if (s > maxs) s = maxs;
+  const int mins = (Lr + 16 * TK - 1) / (16 * TK);
+  if (s < mins) s = mins;
+  if (s < 1) s = 1;
+  int ls = (Lr + s - 1) / s;
+  ls = (ls + TK - 1) / TK * TK;
+  if (ls < TK) ls = TK;
+  p.nsplit = Lr > 0 ? (Lr + ls - 1) / ls : 1;
+  return p;
+}
+
 bool use_mfma(int dtype, int D) { return dtype == HYDRA_BF16 && D == 128; }
+bool use_streaming(int N, int Hq, int Hkv) { return N * (Hq / Hkv) <= 64; }
 
 }  // namespace
 }  // namespace hydra
@@ -734,8 +1159,14 @@ using namespace hydra;
 extern "C" size_t tree_attention_verify_workspace_size(int dtype, int B, int N, int Hq, int Hkv, int D,
                                                        int max_prefix_len) {
   if (!use_mfma(dtype, D) || B <= 0 || N <= 0 || Hkv <= 0 || Hq <= 0 || Hq % Hkv) return 0;
-  const TilePlan p = plan_tiles(B, N, Hq, Hkv, max_prefix_len);
-  const size_t rows = static_cast<size_t>(p.S) * B * Hkv * p.NQpad;
+  size_t rows;
+  if (use_streaming(N, Hq, Hkv)) {
+    const SplitPlan p = plan_splits(B, N, Hq, Hkv, max_prefix_len);
+    rows = static_cast<size_t>(p.nsplit + 1) * B * Hkv * p.NQpad;
+  } else {
+    const TilePlan p = plan_tiles(B, N, Hq, Hkv, max_prefix_len);
+    rows = static_cast<size_t>(p.S) * B * Hkv * p.NQpad;
+  }
   return align_up(rows * D * sizeof(float), 256) + 2 * align_up(rows * sizeof(float), 256) + 256;
 }
 
@@ -787,19 +1218,40 @@ extern "C" int tree_attention_verify(int dtype, int B, int N, int Hq, int Hkv, i
     return HYDRA_OK;
   }
 
+  Arena arena(ws, ws_bytes);
+  const float scale_log2 = scale * 1.4426950408889634f;
+  const int page_shift = page_size == 16 ? 4 : (page_size == 32 ? 5 : 6);
+  if (use_streaming(N, Hq, Hkv)) {
+    const SplitPlan p = plan_splits(B, N, Hq, Hkv, max_prefix_len);
+    const int nparts = p.nsplit + 1;
+    const size_t rows = static_cast<size_t>(nparts) * B * Hkv * p.NQpad;
+    float* opart = arena.take<float>(rows * D);
+    float* mpart = arena.take<float>(rows);
+    float* lpart = arena.take<float>(rows);
+    attn_split_mfma<4, 1, 2, 4><<<dim3(nparts, 1, B * Hkv), 256, 0, stream>>>(
+        B, N, Hq, Hkv, scale_log2, static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k_tree),
+        static_cast<const bf16_t*>(v_tree), static_cast<const bf16_t*>(k_pages), static_cast<const bf16_t*>(v_pages),
+        n_pages, page_shift, block_table, max_pages, prefix_len, anc, depth, Dmax, p.nsplit, p.NQ, p.NQpad, opart,
+        mpart, lpart);
+    HY_LAUNCH_CHECK("tree_attention(split)");
+    const long long cthreads = static_cast<long long>(B) * Hkv * p.NQ * (D / 4);
+    attn_combine<bf16_t><<<static_cast<int>((cthreads + 255) / 256), 256, 0, stream>>>(
+        B, N, Hq, Hkv, D, nparts, p.NQ, p.NQpad, opart, mpart, lpart, static_cast<bf16_t*>(out), lse);
+    HY_LAUNCH_CHECK("tree_attention(combine)");
+    return HYDRA_OK;
+  }
   const TilePlan p = plan_tiles(B, N, Hq, Hkv, max_prefix_len);
   const size_t rows = static_cast<size_t>(p.S) * B * Hkv * p.NQpad;
-  Arena arena(ws, ws_bytes);
   AttnArgs a;
   a.B = B, a.N = N, a.Hq = Hq, a.Hkv = Hkv, a.G = Hq / Hkv, a.Dmax = Dmax;
-  a.scale_log2 = scale * 1.4426950408889634f;
+  a.scale_log2 = scale_log2;
   a.q = static_cast<const bf16_t*>(q);
   a.k_tree = static_cast<const bf16_t*>(k_tree);
   a.v_tree = static_cast<const bf16_t*>(v_tree);
   a.k_pages = static_cast<const bf16_t*>(k_pages);
   a.v_pages = static_cast<const bf16_t*>(v_pages);
   a.n_pages = n_pages, a.max_pages = max_pages;
-  a.page_shift = page_size == 16 ? 4 : (page_size == 32 ? 5 : 6);
+  a.page_shift = page_shift;
   a.block_table = block_table, a.prefix_len = prefix_len, a.anc = anc, a.depth = depth;
   a.S = p.S, a.QT = p.QT, a.NQ = p.NQ, a.NQpad = p.NQpad;
   a.nchunks = B * Hkv * p.S;

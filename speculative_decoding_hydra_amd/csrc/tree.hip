@@ -30,6 +30,7 @@ __global__ __launch_bounds__(kBuildThreads) void tree_build_kernel(
   __shared__ int s_new[HYDRA_MAX_TREE];
   __shared__ int s_src[HYDRA_MAX_VERIFY];
   __shared__ int s_par[HYDRA_MAX_VERIFY];
+  __shared__ int s_wave[kBuildThreads / 64];
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
   const int32_t* ct = cand_tok + static_cast<size_t>(b) * N;
@@ -43,28 +44,47 @@ __global__ __launch_bounds__(kBuildThreads) void tree_build_kernel(
   if (n_keep >= N) {
     for (int i = tid; i < N; i += kBuildThreads) s_new[i] = i;
   } else {
-    for (int i = tid; i < N; i += kBuildThreads) {
-      int keep = 1;
-      if (i > 0) {
+    // rank of candidate i among 1..N-1 by (log-prob desc, depth asc, index
+    // asc): kRankSplit adjacent threads count the candidates ahead of it,
+    // each over every kRankSplit-th entry of the list
+    constexpr int kRankSplit = 4;
+    static_assert(64 % kRankSplit == 0, "a candidate's threads share a wave");
+    for (int base = 0; base < N; base += kBuildThreads / kRankSplit) {
+      const int i = base + tid / kRankSplit, part = tid % kRankSplit;
+      int ahead = 0;
+      if (i < N && i > 0) {
         const float li = s_lp[i];
         const int di = s_dep[i];
-        int ahead = 0;
-        for (int j = 1; j < N; ++j) {
+        for (int j = 1 + part; j < N; j += kRankSplit) {
           const float lj = s_lp[j];
           const int dj = s_dep[j];
           ahead += (lj > li) || (lj == li && (dj < di || (dj == di && j < i)));
         }
-        keep = ahead < n_keep - 1;
       }
-      s_new[i] = keep;
+      // the kRankSplit partial counts of a candidate sit in adjacent lanes
+#pragma unroll
+      for (int o = 1; o < kRankSplit; o <<= 1) ahead += __shfl_xor(ahead, o);
+      if (i < N && part == 0) s_new[i] = i == 0 || ahead < n_keep - 1;
     }
     __syncthreads();
-    if (tid == 0) {
-      int c = 0;
-      for (int i = 0; i < N; ++i) s_new[i] = s_new[i] ? c++ : -1;
+    // stable compaction: new index = number of kept candidates before i
+    // (wave ballot, per-wave counts, then their prefix)
+    const int lane = tid & 63, wave = tid >> 6;
+    int total = 0;
+    for (int base = 0; base < N; base += kBuildThreads) {
+      const int i = base + tid;
+      const bool keep = i < N && s_new[i] != 0;
+      const uint64_t ballot = __ballot(keep);
+      if (lane == 0) s_wave[wave] = __popcll(ballot);
+      __syncthreads();
+      int before = total;
+      for (int w = 0; w < wave; ++w) before += s_wave[w];
+      for (int w = 0; w < kBuildThreads / 64; ++w) total += s_wave[w];
+      before += __popcll(ballot & ((uint64_t(1) << lane) - 1));
+      __syncthreads();
+      if (i < N) s_new[i] = keep ? before : -1;
     }
   }
-  __syncthreads();
   const int nk = n_keep < N ? n_keep : N;
   for (int i = tid; i < N; i += kBuildThreads) {
     const int ni = s_new[i];

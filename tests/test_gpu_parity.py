@@ -1054,3 +1054,31 @@ def test_tree_decoder_layer(dtype, B, tree, d, Hq, Hkv, D, F, lens, layers):
         _close(vt.cpu().double().numpy(), rv, dtype, f"layer {layer} values")
         _close(out.cpu().double().numpy(), ref, dtype, f"layer {layer} output", stream=True)
         xs_dev, xs_ref = out, ref  # each side's next layer reads its own output
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_tree_attention_prefix_beyond_the_plan(dtype):
+    """max_prefix_len only sizes the split plan: prefixes longer than it (a
+    round object reused after its commit grew the cache) are attended in
+    full, on both paths."""
+    from speculative_decoding_hydra_amd import tree_attention_verify, tree_attention_verify_workspace_size
+
+    B, N, Hq, Hkv, D, lens = 2, 64, 8, 2, (128 if dtype == "bf16" else 64), [2100, 700]
+    print(f"attention beyond the plan {dtype} lens={lens} planned 600", flush=True)
+    c = _attn_case(B, N, Hq, Hkv, D, lens, dtype, seed=99)
+    dev = lambda t: t.cuda().contiguous()  # noqa: E731
+    out = torch.full((B, N, Hq, D), float("nan"), dtype=c["dt"], device="cuda")
+    lse = torch.empty(B, N, Hq, device="cuda")
+    code = 0 if dtype == "fp32" else 1
+    ws = torch.empty(max(1, tree_attention_verify_workspace_size(code, B, N, Hq, Hkv, D, 600)), dtype=torch.uint8,
+                     device="cuda")
+    tree_attention_verify(dev(c["q"]), dev(c["kt"]), dev(c["vt"]), dev(c["kpool"]), dev(c["vpool"]), dev(c["bt"]),
+                          dev(c["lens"]), 600, dev(torch.from_numpy(c["anc"])), dev(torch.from_numpy(c["dep"])),
+                          out, lse, ws)
+    torch.cuda.synchronize()
+    f = HI.as_f64
+    ref, ref_lse = O.tree_attention(f(c["q"]), f(c["kt"]), f(c["vt"]), [f(x) for x in c["kp"]],
+                                    [f(x) for x in c["vp"]], c["anc"], bf16=dtype == "bf16")
+    t = 1e-4 if dtype == "fp32" else 2e-2
+    assert float(np.max(np.abs(out.cpu().double().numpy() - ref))) <= t
+    assert float(np.max(np.abs(lse.cpu().double().numpy() - ref_lse))) <= t

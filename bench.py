@@ -22,6 +22,10 @@ The JSON line also carries
                 shape (tree_decoder_layer; bytes, time, HBM fraction);
   commit_32_layers  the commit kernel moving each sequence's deepest kept
                 branch across 32 layers of caches (bytes, time, HBM fraction);
+  mfma          the tiled projection at an MFMA-bound shape (1024 rows x
+                32000 x 4096, arg-max epilogue): flops / launch time against
+                the 2.5 PFLOP/s dense bf16 peak, with the rocprofv3 MFMA
+                counters committed for it (null when gemm.hip changed since);
   configs       the same round on the other workloads (7B dense 256-row
                 tree at prefix 8192, the 64-node tree at prefix 8192, 16
                 ragged sequences, the 70B GQA layer with rejection
@@ -45,6 +49,8 @@ sys.path.insert(0, ROOT)
 METRIC = "verified tree-tokens/sec per round + % HBM roofline (64-node tree, 7B-shape)"
 HBM_PEAK_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "vocab_projection_7b_traffic.json")
+MFMA_FILE = os.path.join(ROOT, "profiles", "tiled_projection_1024_mfma.json")
+MFMA_PEAK_TFLOPS = 2500.0  # dense bf16
 CAL_BYTES = 256 << 20
 
 
@@ -62,6 +68,8 @@ def parse():
     ap.add_argument("--no-fold", action="store_true",
                     help="stream W1[:, d:] every round instead of the folded embedding tables")
     ap.add_argument("--no-configs", action="store_true", help="skip the other workloads' rounds")
+    ap.add_argument("--mfma-only", action="store_true",
+                    help="only the tiled projection at 1024 rows (for counter runs); prints its object")
     return ap.parse_args()
 
 
@@ -76,6 +84,73 @@ def source_hash():
     with open(os.path.join(ROOT, "speculative_decoding_hydra_amd", "csrc", "proj.hip"), "rb") as f:
         h.update(f.read())
     return h.hexdigest()[:16]
+
+
+def file_hash(name):
+    import hashlib
+
+    with open(os.path.join(ROOT, "speculative_decoding_hydra_amd", "csrc", name), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_mfma():
+    """MFMA counters of the tiled projection at 1024 rows from a committed
+    rocprofv3 run, or None when missing or the kernel changed since."""
+    try:
+        with open(MFMA_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    return t.get("counters") if t.get("gemm_hip_sha256_16") == file_hash("gemm.hip") else None
+
+
+def mfma_measure(W2s, M=1024, reps=10, use_graph=True):
+    """The tiled projection at an MFMA-bound row count (M rows of one
+    sequence batch x every tree row: 1024 x 32000 x 4096, the 16-sequence
+    target projection), with the arg-max epilogue of the target projection,
+    cycling the heads' W2 copies so the last-level cache cannot serve
+    repeats: flops / average launch time against the dense bf16 peak."""
+    import torch
+
+    from speculative_decoding_hydra_amd import hydra_vocab_projection, hydra_vocab_projection_workspace_size
+
+    N, K = W2s[0].shape
+    X = torch.randn(M, K, device="cuda").to(W2s[0].dtype)
+    Y = torch.empty(M, N, device="cuda")
+    ws = torch.empty(hydra_vocab_projection_workspace_size(M, N, 1), dtype=torch.uint8, device="cuda")
+    proj = lambda W: hydra_vocab_projection(X, W, Y, 1, ws)  # noqa: E731
+    for W in W2s:
+        proj(W)
+    torch.cuda.synchronize()
+    g = None
+    if use_graph:
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            proj(W2s[0])
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(reps):
+                proj(W2s[i % len(W2s)])
+        g.replay()
+        torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    if g is not None:
+        g.replay()
+    else:
+        for i in range(reps):
+            proj(W2s[i % len(W2s)])
+    b.record()
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) / reps * 1e3
+    flops = 2.0 * M * N * K
+    tf = flops / (us * 1e-6) / 1e12
+    return {"kernel": "proj_gemm_kernel (tiled vocabulary projection, arg-max epilogue)", "rows": M, "cols": N,
+            "depth": K, "flops": flops, "avg_launch_us": us, "achieved_TFLOPs": tf, "peak_TFLOPs": MFMA_PEAK_TFLOPS,
+            "frac": tf / MFMA_PEAK_TFLOPS, "counters": measured_mfma()}
 
 
 def measured_traffic():
@@ -408,6 +483,11 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
+    if args.mfma_only:
+        g = torch.Generator(device="cuda").manual_seed(1)
+        W2s = [(torch.randn(32000, 4096, device="cuda", generator=g) * 0.02).to(torch.bfloat16) for _ in range(4)]
+        print(json.dumps(mfma_measure(W2s, use_graph=not args.no_graph)), flush=True)
+        return
     w = HI.workload(args.workload)
     if args.acceptance and args.acceptance != w.mode:
         w = HI.workload(args.workload, mode=args.acceptance, T=w.T if w.mode != "greedy" else 1.0)
@@ -497,6 +577,7 @@ def main():
     alg_bytes = w.V * w.d * esz + M * w.d * esz + M * w.V * 4
     achieved = alg_bytes / (k_ms * 1e-3) / 1e9
 
+    mfma = mfma_measure(W2s, use_graph=not args.no_graph) if w.d == 4096 and rnd.dtype == torch.bfloat16 else None
     commit = commit_measure(w, rnd, dev, stream, use_graph=not args.no_graph)
     layer = layer_measure(w, rnd, dev, stream, use_graph=not args.no_graph)
     rbytes = round_bytes(w, rnd, inp["prefix_len"])
@@ -532,6 +613,7 @@ def main():
                      "kernel": ("proj_bf16_kernel (streaming vocabulary projection, fused top-k epilogue)"
                                 if M < 65 else "proj_gemm_kernel (tiled vocabulary projection, fused top-k epilogue)"),
                      "bytes_per_launch": alg_bytes, "rows": M, "topk": kk, "avg_launch_ms": k_ms},
+        "mfma": mfma,
         "round_ms": round_ms,
         "round_bytes": rbytes,
         "round_hbm_frac": rbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,

@@ -69,6 +69,8 @@ class Workload:
     head: str = "mlp"     # "mlp" (one SiLU layer) | "sketch" (two-layer LayerNorm heads)
     head_hidden: int = 1024
     cond: str = "parent"  # Hydra conditioning: "parent" token, the whole "path", or Hydra++ "attn" fusion
+    layers: int = 0       # 0: one attention layer over given tree Q/K/V; n: the target's n decoder layers
+    ffn: int = 0          # the decoder layers' feed-forward width
     extra: dict = field(default_factory=dict)
 
     @property
@@ -123,6 +125,12 @@ WORKLOADS = {
     "7b_attn": Workload("7b_attn", 10, B=1, tree=_SPARSE, L=(2048,), cond="attn", **_7B),
     "70b_gqa": Workload("70b_gqa", 4, "bf16", 4, 8192, 32000, 4, True, _SPARSE,
                         64, 8, 128, (16384,), mode="stochastic", T=0.7),
+    # the verification pass through the target's decoder layers (embeddings of
+    # the tree tokens, n LLaMA layers over per-layer paged prefixes, final
+    # norm) instead of one attention layer over given Q/K/V
+    "tiny_layers": Workload("tiny_layers", 11, "fp32", 2, 256, 1000, 3, True, ("cartesian", (2, 3)),
+                            8, 4, 32, (40, 130), layers=3, ffn=512),
+    "7b_layers": Workload("7b_layers", 12, B=1, tree=_SPARSE, L=(2048,), layers=32, ffn=11008, **_7B),
 }
 
 
@@ -229,6 +237,33 @@ def generate(w: Workload, n_tree: int | None = None, reserve: int | None = None,
         out["heads"] = heads
     if w.cond == "attn":
         out["attn"] = {"Wqkv": _normal(g, (3 * w.d, w.d), 0.02, dt), "Wo": _normal(g, (w.d, w.d), 0.02, dt)}
+    if w.layers:
+        # the target's layers, layer-stacked; norm gains near 1. Layer 0's
+        # prefix is the one drawn above; each further layer draws its own
+        # into pools that share the block table
+        n, F, HD = w.layers, w.ffn, (w.Hq + 2 * w.Hkv) * w.D
+        gain = lambda *shape: (1.0 + _normal(g, shape, 0.1, torch.float32)).to(dt)  # noqa: E731
+        out["target"] = {"ln1": gain(n, w.d), "Wqkv": _normal(g, (n, HD, w.d), 0.02, dt),
+                         "Wo": _normal(g, (n, w.d, w.Hq * w.D), 0.02, dt), "ln2": gain(n, w.d),
+                         "Wgu": _normal(g, (n, 2 * F, w.d), 0.02, dt), "Wd": _normal(g, (n, w.d, F), 0.02, dt)}
+        out["ln_f"] = gain(w.d)
+        kpl, vpl = [kp], [vp]
+        kps = torch.zeros((n,) + tuple(k_pages.shape), dtype=dt, device=on)
+        vps = torch.zeros_like(kps)
+        kps[0], vps[0] = k_pages, v_pages
+        for layer in range(1, n):
+            kl = [_normal(g, (L, w.Hkv, w.D), 1.0, dt) for L in lens]
+            vl = [_normal(g, (L, w.Hkv, w.D), 1.0, dt) for L in lens]
+            for b, L in enumerate(lens):
+                for j in range(pages_per[b]):
+                    pid, lo, hi = int(block_table[b, j]), j * PAGE, min(L, (j + 1) * PAGE)
+                    if hi > lo:
+                        kps[layer, pid, :, : hi - lo] = kl[b][lo:hi].transpose(0, 1)
+                        vps[layer, pid, :, : hi - lo] = vl[b][lo:hi].transpose(0, 1)
+            kpl.append(kl)
+            vpl.append(vl)
+        out["k_prefix_layers"], out["v_prefix_layers"] = kpl, vpl
+        out["k_pages"], out["v_pages"] = kps, vps
     return out
 
 

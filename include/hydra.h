@@ -11,7 +11,9 @@
  *   tree_attention_verify  tree-masked attention over a paged KV prefix
  *                          (tree_rope / tree_rope_qk first rotate the tree Q/K rows at
  *                          positions prefix_len + depth; tree_decoder_layer
- *                          runs a whole target layer over the tree rows)
+ *                          runs a whole target layer over the tree rows and
+ *                          tree_verify_layers the target's whole forward pass:
+ *                          embeddings, every layer, final norm)
  *   tree_accept            target vocabulary projection + acceptance walk
  *   tree_commit            kept branch into the paged KV cache, next root and h
  * plus host-side tree-plan builders, workspace-size queries and status strings.
@@ -433,6 +435,52 @@ int tree_decoder_layer(int dtype, int B, int N, int d, int Hq, int Hkv, int D,
                        const int32_t* prefix_len, int max_prefix_len,
                        const int32_t* anc, const int32_t* depth, int Dmax,
                        void* x_out, void* k_tree, void* v_tree, void* ws,
+                       size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * The target's forward pass over the tree rows: every layer
+ *
+ * [SD] "Draft, then verify": one forward pass of the target scores every
+ * candidate; [HG] "Tree Attention Matrix with Topology-Aware Causal
+ * Masking": every layer's attention is tree-masked. The rows' input is the
+ * embedding of their own token (the root row's is the root token); then
+ * n_layers decoder layers as tree_decoder_layer, each over its own weights
+ * and paged prefix; then the final norm h = rms(x) ln_f (stored in dtype).
+ * h is what tree_accept takes as o (Z = W_t h) and tree_commit as hidden;
+ * k_tree / v_tree are tree_commit's layer-stacked inputs.
+ *
+ * tok            [B, N] tree tokens (tree_build's tok); a token outside
+ *                [0, V) reads a row of zeros
+ * emb            [V, d] (dtype) token embeddings
+ * ln1, ln2       [n_layers, d] (dtype)
+ * Wqkv           [n_layers, (Hq + 2 Hkv) D, d] (dtype)
+ * Wo             [n_layers, d, Hq D] (dtype)
+ * Wgu            [n_layers, 2 F, d] (dtype)
+ * Wd             [n_layers, d, F] (dtype)
+ * ln_f           [d] (dtype) final norm gain
+ * k_pages ...    [n_layers, n_pages, Hkv, page_size, D] (dtype), one block
+ *                table and prefix length per sequence shared by the layers
+ * h_out          out [B, N, d] (dtype)
+ * k_tree, v_tree out [n_layers, B, N, Hkv, D] (dtype): every layer's rotated
+ *                keys and values of the tree rows
+ * Limits: those of tree_decoder_layer; emb and h_out 16-byte aligned.
+ * Workspace: tree_verify_layers_workspace_size (two hidden-state buffers
+ * plus one layer's). Errors as tree_decoder_layer.
+ * ---------------------------------------------------------------------- */
+size_t tree_verify_layers_workspace_size(int dtype, int B, int N, int d, int Hq,
+                                         int Hkv, int D, int F,
+                                         int max_prefix_len);
+
+int tree_verify_layers(int dtype, int n_layers, int B, int N, int d, int Hq,
+                       int Hkv, int D, int F, int V, const int32_t* tok,
+                       const void* emb, const void* ln1, const void* Wqkv,
+                       const void* Wo, const void* ln2, const void* Wgu,
+                       const void* Wd, const void* ln_f, float eps, float theta,
+                       const void* k_pages, const void* v_pages, int n_pages,
+                       int page_size, const int32_t* block_table, int max_pages,
+                       const int32_t* prefix_len, int max_prefix_len,
+                       const int32_t* anc, const int32_t* depth, int Dmax,
+                       void* h_out, void* k_tree, void* v_tree, void* ws,
                        size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------

@@ -603,6 +603,34 @@ def decoder_layer(x, w, k_prefix, v_prefix, anc, depth, prefix_len, Hq, Hkv, D, 
     return x2, k, v
 
 
+def verify_layers(tok, E, layers, g_f, k_prefix, v_prefix, anc, depth, prefix_len, Hq, Hkv, D, eps,
+                  theta=10000.0, bf16=False):
+    """The target's whole forward pass over the tree rows [SD, "Draft, then
+    verify": one forward pass of the target scores every candidate; HG,
+    "Tree Attention Matrix with Topology-Aware Causal Masking": the tree mask
+    applies in every layer's attention].
+
+    Each row's input is the embedding of its own token (a token outside the
+    table reads zeros); the decoder layers follow in order, each with its own
+    weights and its own cached prefix; the final RMSNorm (gain g_f) gives the
+    hidden state h that the target's vocabulary projection reads.
+    tok [B, N]; E [V, d]; layers: list of decoder_layer weight dicts;
+    k_prefix/v_prefix: per layer, per sequence [L_b, Hkv, D].
+    Returns (h [B, N, d], k_rot [n, B, N, Hkv, D], v [n, B, N, Hkv, D]).
+    """
+    r = round_bf16 if bf16 else (lambda t: t)
+    E = np.asarray(E, dtype=np.float64)
+    tok = np.asarray(tok, dtype=np.int64)
+    ok = (tok >= 0) & (tok < E.shape[0])
+    x = np.where(ok[..., None], E[np.where(ok, tok, 0)], 0.0)
+    ks, vs = [], []
+    for w, kp, vp in zip(layers, k_prefix, v_prefix):
+        x, k, v = decoder_layer(x, w, kp, vp, anc, depth, prefix_len, Hq, Hkv, D, eps, theta, bf16=bf16)
+        ks.append(k)
+        vs.append(v)
+    return r(rms_norm(x, g_f, eps)), np.stack(ks), np.stack(vs)
+
+
 # ---------------------------------------------------------------------------
 # Stage 4: target projection and acceptance
 # ---------------------------------------------------------------------------

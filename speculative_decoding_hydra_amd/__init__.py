@@ -13,6 +13,6 @@ from .hydra import (  # noqa: F401
     hydra_vocab_projection_workspace_size, hydra_vocab_topk, tree_accept, tree_accept_noalloc,
     tree_accept_workspace_size, tree_attention_verify, tree_attention_verify_workspace_size, tree_build,
     tree_build_workspace_size, tree_commit, tree_decoder_layer, tree_decoder_layer_workspace_size, tree_rope,
-    tree_rope_qk,
+    tree_rope_qk, tree_verify_layers, tree_verify_layers_workspace_size,
 )
 from .round import HydraRound, make_plan, round_from_inputs, run_round  # noqa: F401

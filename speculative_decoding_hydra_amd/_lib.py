@@ -54,6 +54,10 @@ SIGNATURES = {
                                    c_void, c_void, c_void, c_void, c_float, c_float, c_void, c_void, c_int, c_int,
                                    c_void, c_int, c_void, c_int, c_void, c_void, c_int, c_void, c_void, c_void,
                                    c_void, c_size, c_void]),
+    "tree_verify_layers_workspace_size": (c_size, [c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_int]),
+    "tree_verify_layers": (c_int, [c_int] * 10 + [c_void] * 9 + [c_float, c_float, c_void, c_void, c_int, c_int,
+                                                                c_void, c_int, c_void, c_int, c_void, c_void, c_int,
+                                                                c_void, c_void, c_void, c_void, c_size, c_void]),
     "tree_accept_workspace_size": (c_size, [c_int, c_int, c_int, c_int]),
     "tree_accept": (c_int, [c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_void, c_void, c_float, c_float,
                             c_float, c_void, c_void, c_void, c_void, c_int, c_void, c_void, c_void, c_void, c_void,

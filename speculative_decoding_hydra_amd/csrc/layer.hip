@@ -324,6 +324,76 @@ int run_layer(int dtype, int B, int N, int d, int Hq, int Hkv, int D, int F, con
   return HYDRA_OK;
 }
 
+// out[r] = emb[tok[r]]: the tree rows' input to the first layer; a token
+// outside [0, V) gives a row of zeros. 16-byte copies when d allows.
+template <typename T>
+__global__ __launch_bounds__(256) void embed_rows(int d, int V, const int32_t* __restrict__ tok,
+                                                  const T* __restrict__ emb, T* __restrict__ out) {
+  const size_t row = blockIdx.x;
+  const int t = tok[row];
+  const bool ok = t >= 0 && t < V;
+  const T* src = emb + static_cast<size_t>(ok ? t : 0) * d;
+  T* dst = out + row * d;
+  constexpr int per = 16 / sizeof(T);
+  if (d % per == 0) {
+    for (int c = threadIdx.x; c < d / per; c += 256) {
+      const u32x4_t v = ok ? *reinterpret_cast<const u32x4_t*>(src + c * per) : u32x4_t{0u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x4_t*>(dst + c * per) = v;
+    }
+  } else {
+    for (int i = threadIdx.x; i < d; i += 256) dst[i] = ok ? src[i] : cv<T>(0.f);
+  }
+}
+
+struct VerifyWs {
+  LayerWs layer;
+  size_t x, total;
+};
+
+VerifyWs verify_ws(int dtype, int B, int N, int d, int Hq, int Hkv, int D, int F, int max_prefix_len) {
+  VerifyWs w{};
+  w.layer = layer_ws(dtype, B, N, d, Hq, Hkv, D, F, max_prefix_len);
+  w.x = align_up(static_cast<size_t>(B) * N * d * (dtype == HYDRA_F32 ? 4 : 2), 256);
+  w.total = w.layer.total + 2 * w.x + 256;
+  return w;
+}
+
+// embeddings -> n_layers decoder layers (layer-stacked weights, pools and
+// tree K/V) -> final norm; the hidden states ping-pong between two buffers
+template <typename T>
+int run_verify(int dtype, int n_layers, int B, int N, int d, int Hq, int Hkv, int D, int F, int V,
+               const int32_t* tok, const T* emb, const T* ln1, const T* Wqkv, const T* Wo, const T* ln2,
+               const T* Wgu, const T* Wd, const T* ln_f, float eps, float theta, const T* k_pages,
+               const T* v_pages, int n_pages, int page_size, const int32_t* block_table, int max_pages,
+               const int32_t* prefix_len, int max_prefix_len, const int32_t* anc, const int32_t* depth, int Dmax,
+               T* h_out, T* k_tree, T* v_tree, void* ws, size_t ws_bytes, hipStream_t stream) {
+  const VerifyWs w = verify_ws(dtype, B, N, d, Hq, Hkv, D, F, max_prefix_len);
+  Arena arena(ws, ws_bytes);
+  T* cur = arena.take<T>(w.x / sizeof(T));
+  T* nxt = arena.take<T>(w.x / sizeof(T));
+  void* lws = arena.take<char>(w.layer.total);
+  const size_t M = static_cast<size_t>(B) * N;
+  embed_rows<T><<<static_cast<unsigned>(M), 256, 0, stream>>>(d, V, tok, emb, cur);
+  HY_LAUNCH_CHECK("verify layers: embeddings");
+  const size_t sqkv = static_cast<size_t>(Hq + 2 * Hkv) * D * d, so = static_cast<size_t>(d) * Hq * D;
+  const size_t sgu = 2 * static_cast<size_t>(F) * d, sd = static_cast<size_t>(d) * F;
+  const size_t skv = M * Hkv * D, spool = static_cast<size_t>(n_pages) * Hkv * page_size * D;
+  for (int l = 0; l < n_layers; ++l) {
+    const int rc = run_layer<T>(dtype, B, N, d, Hq, Hkv, D, F, cur, ln1 + l * static_cast<size_t>(d),
+                                Wqkv + l * sqkv, Wo + l * so, ln2 + l * static_cast<size_t>(d), Wgu + l * sgu,
+                                Wd + l * sd, eps, theta, k_pages + l * spool, v_pages + l * spool, n_pages,
+                                page_size, block_table, max_pages, prefix_len, max_prefix_len, anc, depth, Dmax, nxt,
+                                k_tree + l * skv, v_tree + l * skv, lws, w.layer.total, stream);
+    if (rc != HYDRA_OK) return rc;
+    T* t = cur;
+    cur = nxt;
+    nxt = t;
+  }
+  launch_norm<T>(static_cast<int>(M), d, eps, cur, nullptr, 1, nullptr, ln_f, h_out, stream);
+  HY_LAUNCH_CHECK("verify layers: final norm");
+  return HYDRA_OK;
+}
+
 }  // namespace
 }  // namespace hydra
 
@@ -372,4 +442,54 @@ extern "C" int tree_decoder_layer(int dtype, int B, int N, int d, int Hq, int Hk
                            v_pages, n_pages, page_size, block_table, max_pages, prefix_len, max_prefix_len, anc,
                            depth, Dmax, static_cast<bf16_t*>(x_out), static_cast<bf16_t*>(k_tree),
                            static_cast<bf16_t*>(v_tree), ws, ws_bytes, stream);
+}
+
+extern "C" size_t tree_verify_layers_workspace_size(int dtype, int B, int N, int d, int Hq, int Hkv, int D, int F,
+                                                    int max_prefix_len) {
+  if (B <= 0 || N <= 0 || d <= 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || F <= 0) return 0;
+  return hydra::verify_ws(dtype, B, N, d, Hq, Hkv, D, F, max_prefix_len).total;
+}
+
+extern "C" int tree_verify_layers(int dtype, int n_layers, int B, int N, int d, int Hq, int Hkv, int D, int F, int V,
+                                  const int32_t* tok, const void* emb, const void* ln1, const void* Wqkv,
+                                  const void* Wo, const void* ln2, const void* Wgu, const void* Wd,
+                                  const void* ln_f, float eps, float theta, const void* k_pages,
+                                  const void* v_pages, int n_pages, int page_size, const int32_t* block_table,
+                                  int max_pages, const int32_t* prefix_len, int max_prefix_len, const int32_t* anc,
+                                  const int32_t* depth, int Dmax, void* h_out, void* k_tree, void* v_tree, void* ws,
+                                  size_t ws_bytes, void* stream_) {
+  using namespace hydra;
+  clear_error();
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+  HY_CHECK(dtype == HYDRA_F32 || dtype == HYDRA_BF16, HYDRA_ERR_INVALID, "verify_layers: bad dtype %d", dtype);
+  HY_CHECK(n_layers >= 1 && B >= 0 && N >= 1 && d >= 1 && Hq >= 1 && Hkv >= 1 && D >= 2 && D % 2 == 0 && F >= 1 &&
+               Hq % Hkv == 0 && V >= 1,
+           HYDRA_ERR_INVALID, "verify_layers: bad sizes layers=%d B=%d N=%d d=%d Hq=%d Hkv=%d D=%d F=%d V=%d",
+           n_layers, B, N, d, Hq, Hkv, D, F, V);
+  HY_CHECK(eps > 0.f && theta > 1.f, HYDRA_ERR_INVALID, "verify_layers: eps must be > 0 and theta > 1");
+  if (B == 0) return HYDRA_OK;
+  HY_CHECK(tok && emb && ln1 && Wqkv && Wo && ln2 && Wgu && Wd && ln_f && k_pages && v_pages && block_table &&
+               prefix_len && anc && depth && h_out && k_tree && v_tree,
+           HYDRA_ERR_INVALID, "verify_layers: null pointer");
+  HY_CHECK(dtype == HYDRA_F32 || (d % 256 == 0 && (Hq * D) % 256 == 0 && F % 256 == 0), HYDRA_ERR_UNSUPPORTED,
+           "verify_layers: bf16 needs d, Hq*D and F multiples of 256 (d=%d Hq*D=%d F=%d)", d, Hq * D, F);
+  const size_t need = tree_verify_layers_workspace_size(dtype, B, N, d, Hq, Hkv, D, F, max_prefix_len);
+  HY_CHECK(ws && ws_bytes >= need, HYDRA_ERR_WORKSPACE, "verify_layers: workspace %zu < %zu", ws_bytes, need);
+  if (dtype == HYDRA_F32)
+    return run_verify<float>(
+        dtype, n_layers, B, N, d, Hq, Hkv, D, F, V, tok, static_cast<const float*>(emb),
+        static_cast<const float*>(ln1), static_cast<const float*>(Wqkv), static_cast<const float*>(Wo),
+        static_cast<const float*>(ln2), static_cast<const float*>(Wgu), static_cast<const float*>(Wd),
+        static_cast<const float*>(ln_f), eps, theta, static_cast<const float*>(k_pages),
+        static_cast<const float*>(v_pages), n_pages, page_size, block_table, max_pages, prefix_len, max_prefix_len,
+        anc, depth, Dmax, static_cast<float*>(h_out), static_cast<float*>(k_tree), static_cast<float*>(v_tree), ws,
+        ws_bytes, stream);
+  return run_verify<bf16_t>(
+      dtype, n_layers, B, N, d, Hq, Hkv, D, F, V, tok, static_cast<const bf16_t*>(emb),
+      static_cast<const bf16_t*>(ln1), static_cast<const bf16_t*>(Wqkv), static_cast<const bf16_t*>(Wo),
+      static_cast<const bf16_t*>(ln2), static_cast<const bf16_t*>(Wgu), static_cast<const bf16_t*>(Wd),
+      static_cast<const bf16_t*>(ln_f), eps, theta, static_cast<const bf16_t*>(k_pages),
+      static_cast<const bf16_t*>(v_pages), n_pages, page_size, block_table, max_pages, prefix_len, max_prefix_len, anc,
+      depth, Dmax, static_cast<bf16_t*>(h_out), static_cast<bf16_t*>(k_tree), static_cast<bf16_t*>(v_tree), ws,
+      ws_bytes, stream);
 }

@@ -500,6 +500,44 @@ def tree_decoder_layer(x, w, Hq, Hkv, k_pages, v_pages, block_table, prefix_len,
     return _check("tree_decoder_layer", rc)
 
 
+def tree_verify_layers_workspace_size(dtype_code, B, N, d, Hq, Hkv, D, F, max_prefix_len):
+    return int(lib().tree_verify_layers_workspace_size(dtype_code, B, N, d, Hq, Hkv, D, F, max_prefix_len))
+
+
+def tree_verify_layers(tok, emb, w, ln_f, Hq, Hkv, k_pages, v_pages, block_table, prefix_len, max_prefix_len, anc,
+                       depth, h_out, k_tree, v_tree, ws, eps=1e-6, theta=10000.0, stream=None):
+    """The target's forward pass over the tree rows (see include/hydra.h):
+    embeddings of tok, every decoder layer, final norm. w: dict of
+    layer-stacked ln1 [n, d], Wqkv [n, (Hq + 2 Hkv) D, d], Wo [n, d, Hq D],
+    ln2 [n, d], Wgu [n, 2F, d], Wd [n, d, F]; pages [n, n_pages, Hkv, page, D];
+    k_tree, v_tree [n, B, N, Hkv, D]; h_out [B, N, d]."""
+    B, N = tok.shape
+    V, d = emb.shape
+    n = w["Wqkv"].shape[0]
+    D = k_tree.shape[4]
+    F = w["Wd"].shape[2]
+    n_pages, page_size = k_pages.shape[1], k_pages.shape[3]
+    dt = emb.dtype
+    _shapes("tree_verify_layers", ln1=(w["ln1"], (n, d)), Wqkv=(w["Wqkv"], (n, (Hq + 2 * Hkv) * D, d)),
+            Wo=(w["Wo"], (n, d, Hq * D)), ln2=(w["ln2"], (n, d)), Wgu=(w["Wgu"], (n, 2 * F, d)),
+            Wd=(w["Wd"], (n, d, F)), ln_f=(ln_f, (d,)), k_pages=(k_pages, (n, n_pages, Hkv, page_size, D)),
+            v_pages=(v_pages, (n, n_pages, Hkv, page_size, D)), h_out=(h_out, (B, N, d)),
+            k_tree=(k_tree, (n, B, N, Hkv, D)), v_tree=(v_tree, (n, B, N, Hkv, D)),
+            anc=(anc, (B, N, anc.shape[2])), depth=(depth, (B, N)), prefix_len=(prefix_len, (B,)),
+            block_table=(block_table, (B, block_table.shape[1])))
+    wsp, wsb = _ws(ws)
+    rc = lib().tree_verify_layers(
+        _dtype_code(emb), n, B, N, d, Hq, Hkv, D, F, V, _dev(tok, "tok", torch.int32), _dev(emb, "emb"),
+        _dev(w["ln1"], "ln1", dt), _dev(w["Wqkv"], "Wqkv", dt), _dev(w["Wo"], "Wo", dt), _dev(w["ln2"], "ln2", dt),
+        _dev(w["Wgu"], "Wgu", dt), _dev(w["Wd"], "Wd", dt), _dev(ln_f, "ln_f", dt), float(eps), float(theta),
+        _dev(k_pages, "k_pages", dt), _dev(v_pages, "v_pages", dt), n_pages, page_size,
+        _dev(block_table, "block_table", torch.int32), block_table.shape[1],
+        _dev(prefix_len, "prefix_len", torch.int32), int(max_prefix_len), _dev(anc, "anc", torch.int32),
+        _dev(depth, "depth", torch.int32), anc.shape[2] - 1, _dev(h_out, "h_out", dt), _dev(k_tree, "k_tree", dt),
+        _dev(v_tree, "v_tree", dt), wsp, wsb, _stream(stream))
+    return _check("tree_verify_layers", rc)
+
+
 def tree_accept_workspace_size(mode, B, N, V):
     return int(lib().tree_accept_workspace_size(mode, B, N, V))
 

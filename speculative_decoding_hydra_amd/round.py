@@ -44,6 +44,11 @@ class HydraRound:
     root (W1 of head k is [d, (k + 1) d]); never folded.
     rope_theta: rotate the tree Q/K rows at positions prefix_len + depth
     (tree_rope) before attention; None gives the rows to attention as they are.
+    With ``target`` in weights (layer-stacked ln1, Wqkv, Wo, ln2, Wgu, Wd, the
+    final norm gain ln_f and the embedding table emb) the verification runs
+    the target's decoder layers over the tree tokens (tree_verify_layers)
+    instead of one attention layer over given Q/K/V; the pools are then
+    layer-stacked and the commit writes every layer's K/V.
     """
 
     def __init__(self, weights, tree, shape, hydra=True, mode=0, temperature=1.0, residual=True,
@@ -78,6 +83,13 @@ class HydraRound:
         self.k_rot = z(B, K, Hkv, D, dtype=dt) if rope_theta else None
         self.attn_lse = z(B, K, Hq)
         self.target_logits = z(B, K, V)
+        self.target = weights.get("target")
+        self.hidden = self.k_layers = self.v_layers = None
+        if self.target is not None:
+            n_layers, F = self.target["Wqkv"].shape[0], self.target["Wd"].shape[2]
+            self.hidden = z(B, K, d, dtype=dt)
+            self.k_layers = z(n_layers, B, K, Hkv, D, dtype=dt)
+            self.v_layers = z(n_layers, B, K, Hkv, D, dtype=dt)
         self.n_accepted = z(B, dtype=i32)
         self.path = z(B, Dm + 1, dtype=i32)
         self.out_tok = z(B, Dm + 1, dtype=i32)
@@ -101,6 +113,9 @@ class HydraRound:
         self.ws_attn = nb(H.tree_attention_verify_workspace_size(code, B, K, Hq, Hkv, D,
                                                                  shape["max_prefix_len"]))
         self.ws_accept = nb(H.tree_accept_workspace_size(self.mode, B, K, V))
+        if self.target is not None:
+            self.ws_verify = nb(H.tree_verify_layers_workspace_size(code, B, K, d, Hq, Hkv, D, F,
+                                                                    shape["max_prefix_len"]))
         if fold_embedding is None:
             fold_embedding = hydra and dt == torch.bfloat16 and not self.sketch and not self.full_path
             fold_embedding = fold_embedding and self.attn is None
@@ -140,9 +155,26 @@ class HydraRound:
                                 self.shape["max_prefix_len"], self.anc, self.depth, self.attn_out, self.attn_lse,
                                 self.ws_attn, stream=stream)
 
-    def accept(self, u_acc=None, u_res=None, stream=None):
+    def verify(self, k_pages, v_pages, block_table, prefix_len, stream=None):
+        """The target's forward pass over the tree tokens: every layer's
+        rotated K/V into k_layers / v_layers, the final hidden states into
+        hidden."""
+        t = self.target
+        H.tree_verify_layers(self.tok, t["emb"], t, t["ln_f"], self.shape["Hq"], self.shape["Hkv"], k_pages,
+                             v_pages, block_table, prefix_len, self.shape["max_prefix_len"], self.anc, self.depth,
+                             self.hidden, self.k_layers, self.v_layers, self.ws_verify, eps=t.get("eps", 1e-6),
+                             theta=self.rope_theta or 10000.0, stream=stream)
+
+    def rows(self):
+        """[B, N, d] hidden states of the tree rows that the target projection
+        reads: the final layer's output, or the attention output."""
+        if self.target is not None:
+            return self.hidden
         B, K = self.attn_out.shape[:2]
-        H.tree_accept(self.attn_out.view(B, K, -1), self.w["W_t"], self.tok, self.parent, self.target_logits,
+        return self.attn_out.view(B, K, -1)
+
+    def accept(self, u_acc=None, u_res=None, stream=None):
+        H.tree_accept(self.rows(), self.w["W_t"], self.tok, self.parent, self.target_logits,
                       self.n_accepted, self.path, self.out_tok, self.ws_accept, mode=self.mode,
                       temperature=self.T, q_row=self.q_row, head_logits=self.head_logits, u_acc=u_acc,
                       u_res=u_res, eps=self.eps, delta=self.delta, stream=stream)
@@ -150,18 +182,22 @@ class HydraRound:
     def commit(self, k_tree, v_tree, k_pages, v_pages, block_table, prefix_len, stream=None):
         """Root and accepted rows into the paged cache (in place); next
         prefix lengths, roots and hidden states into next_*."""
-        B, K = self.attn_out.shape[:2]
-        if self.rope_theta:
+        if self.target is not None:
+            k_tree, v_tree = self.k_layers, self.v_layers
+        elif self.rope_theta:
             k_tree = self.k_rot  # the cache holds rotated keys
         H.tree_commit(k_tree, v_tree, k_pages, v_pages, block_table, prefix_len, self.n_accepted, self.path,
-                      self.out_tok, self.next_prefix_len, self.next_root_tok, hidden=self.attn_out.view(B, K, -1),
+                      self.out_tok, self.next_prefix_len, self.next_root_tok, hidden=self.rows(),
                       next_h=self.next_h, stream=stream)
 
     def run(self, h, root_tok, q, k_tree, v_tree, k_pages, v_pages, block_table, prefix_len, u_acc=None,
             u_res=None, stream=None):
         self.draft(h, root_tok, stream)
         self.build(stream)
-        self.attend(q, k_tree, v_tree, k_pages, v_pages, block_table, prefix_len, stream)
+        if self.target is not None:
+            self.verify(k_pages, v_pages, block_table, prefix_len, stream)
+        else:
+            self.attend(q, k_tree, v_tree, k_pages, v_pages, block_table, prefix_len, stream)
         self.accept(u_acc, u_res, stream)
         self.commit(k_tree, v_tree, k_pages, v_pages, block_table, prefix_len, stream)
 
@@ -171,14 +207,18 @@ def round_from_inputs(inp, device="cuda", keep_hidden=True, fold_embedding=None,
 
     Keys: workload (sizes, tree, dtype, mode), root_tok, h, E, W1, b1, W2 (or
     heads, for two-layer heads), W_t,
-    q_tree, k_tree, v_tree, k_pages, v_pages, block_table, prefix_len and, for
-    the rejection and typical modes, u_acc and u_res. Returns (round, device tensors).
+    q_tree, k_tree, v_tree (or, with the target's layers, target and ln_f),
+    k_pages, v_pages, block_table, prefix_len and, for the rejection and
+    typical modes, u_acc and u_res. Returns (round, device tensors).
     """
     w = inp["workload"]
     to = lambda t: t.to(device).contiguous()  # noqa: E731
     weights = dict(emb=to(inp["E"]) if w.hydra else None, W_t=to(inp["W_t"]))
     if w.cond == "attn":
         weights["attn"] = {n: to(t) for n, t in inp["attn"].items()}
+    if w.layers:
+        weights["target"] = dict({n: to(t) for n, t in inp["target"].items()}, ln_f=to(inp["ln_f"]),
+                                 emb=to(inp["E"]))
     if w.head == "sketch":
         weights["heads"] = [{n: to(t) for n, t in hd.items()} for hd in inp["heads"]]
     else:
@@ -188,9 +228,10 @@ def round_from_inputs(inp, device="cuda", keep_hidden=True, fold_embedding=None,
     mode = {"greedy": 0, "stochastic": 1, "typical": 2}[w.mode]
     rnd = HydraRound(weights, w.tree, shape, hydra=w.hydra, mode=mode, temperature=w.T, residual=residual, keep_hidden=keep_hidden, device=device,
                      fold_embedding=fold_embedding, eps=w.eps, delta=w.delta, full_path=w.cond == "path")
-    dev = dict(h=to(inp["h"]), root_tok=to(inp["root_tok"]), q=to(inp["q_tree"]), k_tree=to(inp["k_tree"]),
-               v_tree=to(inp["v_tree"]), k_pages=to(inp["k_pages"]), v_pages=to(inp["v_pages"]),
+    dev = dict(h=to(inp["h"]), root_tok=to(inp["root_tok"]), k_pages=to(inp["k_pages"]), v_pages=to(inp["v_pages"]),
                block_table=to(inp["block_table"]), prefix_len=to(inp["prefix_len"]))
+    if not w.layers:  # the target's layers make their own Q/K/V
+        dev.update(q=to(inp["q_tree"]), k_tree=to(inp["k_tree"]), v_tree=to(inp["v_tree"]))
     if w.mode in ("stochastic", "typical"):
         dev["u_acc"], dev["u_res"] = to(inp["u_acc"]), to(inp["u_res"])
     return rnd, dev
@@ -198,5 +239,5 @@ def round_from_inputs(inp, device="cuda", keep_hidden=True, fold_embedding=None,
 
 def run_round(rnd, dev, stream=None):
     """One round on the device tensors returned by round_from_inputs."""
-    rnd.run(dev["h"], dev["root_tok"], dev["q"], dev["k_tree"], dev["v_tree"], dev["k_pages"], dev["v_pages"],
-            dev["block_table"], dev["prefix_len"], dev.get("u_acc"), dev.get("u_res"), stream=stream)
+    rnd.run(dev["h"], dev["root_tok"], dev.get("q"), dev.get("k_tree"), dev.get("v_tree"), dev["k_pages"],
+            dev["v_pages"], dev["block_table"], dev["prefix_len"], dev.get("u_acc"), dev.get("u_res"), stream=stream)

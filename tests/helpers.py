@@ -286,7 +286,60 @@ def check_build(inp, rnd, seqs=None):
         assert np.array_equal(qrow[b], node_row[s])
 
 
+def close_stream(got, ref, dtype, what, layers=1):
+    """float32: 1e-4 per layer. bfloat16: per layer 2e-2 plus two rounding
+    steps of the value's scale, the scale at least the row's RMS: every
+    layer rounds its stored tensors once more and hands what it inherited on
+    through the residual sum, so the bound grows with the number of layers
+    the value went through."""
+    if dtype == "fp32":
+        e = float(np.max(np.abs(got - ref)))
+        assert e <= 1e-4 * layers, f"{what}: max-abs {e:.3g}"
+        return e
+    scale = np.maximum(np.abs(ref), np.sqrt(np.mean(ref * ref, axis=-1, keepdims=True)))
+    step = np.ldexp(1.0, np.frexp(np.maximum(scale, 1e-30))[1] - 8)
+    bad = np.abs(got - ref) > layers * (2e-2 + 2 * step)
+    assert not bad.any(), f"{what}: {int(bad.sum())} values off, worst {float(np.max(np.abs(got - ref))):.3g}"
+    return float(np.max(np.abs(got - ref)))
+
+
+def target_layers_f64(inp):
+    """The oracle's per-layer weight dicts from the layer-stacked inputs."""
+    w, t, f = inp["workload"], inp["target"], HI.as_f64
+    qd, kd, F = w.Hq * w.D, w.Hkv * w.D, w.ffn
+    out = []
+    for layer in range(w.layers):
+        wqkv, wgu = f(t["Wqkv"][layer]), f(t["Wgu"][layer])
+        out.append(dict(g1=f(t["ln1"][layer]), g2=f(t["ln2"][layer]), Wq=wqkv[:qd], Wk=wqkv[qd:qd + kd],
+                        Wv=wqkv[qd + kd:], Wo=f(t["Wo"][layer]), Wg=wgu[:F], Wu=wgu[F:], Wd=f(t["Wd"][layer])))
+    return out
+
+
+def check_verify(inp, rnd, seqs=None):
+    """The target's forward pass over the device's tree (its tokens, ancestor
+    table and depths) against the oracle's: embeddings, the chain of decoder
+    layers over each layer's prefix, final norm; every layer's rotated K/V."""
+    w = inp["workload"]
+    seqs = list(range(w.B)) if seqs is None else list(seqs)
+    f = HI.as_f64
+    kp = [[f(inp["k_prefix_layers"][layer][b]) for b in seqs] for layer in range(w.layers)]
+    vp = [[f(inp["v_prefix_layers"][layer][b]) for b in seqs] for layer in range(w.layers)]
+    h, k, v = O.verify_layers(np_(rnd.tok)[seqs], f(inp["E"]), target_layers_f64(inp), f(inp["ln_f"]), kp, vp,
+                              np_(rnd.anc)[seqs], np_(rnd.depth)[seqs], inp["prefix_len"].numpy()[seqs], w.Hq, w.Hkv,
+                              w.D, 1e-6, theta=rnd.rope_theta or 10000.0, bf16=w.dtype == "bf16")
+    rep = {}
+    for layer in range(w.layers):
+        rep[f"k{layer}"] = close_stream(np_(rnd.k_layers[layer])[seqs], k[layer], w.dtype, f"layer {layer} keys",
+                                        layer + 1)
+        rep[f"v{layer}"] = close_stream(np_(rnd.v_layers[layer])[seqs], v[layer], w.dtype, f"layer {layer} values",
+                                        layer + 1)
+    rep["h"] = close_stream(np_(rnd.hidden)[seqs], h, w.dtype, "final hidden states", w.layers)
+    return rep
+
+
 def check_attention(inp, rnd, seqs=None):
+    if rnd.target is not None:
+        return check_verify(inp, rnd, seqs)
     w = inp["workload"]
     t = tol(w)
     seqs = list(range(w.B)) if seqs is None else list(seqs)
@@ -315,7 +368,7 @@ def check_accept(inp, rnd, seqs=None):
     w = inp["workload"]
     t = tol(w)
     seqs = range(w.B) if seqs is None else seqs
-    O_dev = np_(rnd.attn_out)
+    O_dev = np_(rnd.rows())
     Z_dev = np_(rnd.target_logits)
     Wt = HI.as_f64(inp["W_t"])
     tok, par, qrow = np_(rnd.tok), np_(rnd.parent), np_(rnd.q_row)
@@ -429,24 +482,31 @@ def check_commit(inp, rnd, dev, seqs=None):
     bt = inp["block_table"].numpy()
     ps = int(inp["page_size"])
     nlen, nroot, nh = np_(rnd.next_prefix_len), np_(rnd.next_root_tok), rnd.next_h
-    B, K = rnd.attn_out.shape[:2]
-    hid = rnd.attn_out.view(B, K, -1)
+    hid = rnd.rows()
+    layered = rnd.target is not None  # pools and tree K/V stacked over the target's layers
     for b in seqs:
         pages = [int(p) for p in bt[b] if p >= 0]
         sub_bt = np.arange(len(pages))[None]
-        sub = lambda pool: HI.as_f64(pool[pages])[None]  # noqa: E731
-        ksrc = rnd.k_rot if rnd.rope_theta else inp["k_tree"]  # the keys the round committed
-        rk, rv, rl, rr, _ = O.commit_path(sub(inp["k_pages"]), sub(inp["v_pages"]), sub_bt, lens[b:b + 1],
-                                          np_(ksrc[b:b + 1])[None],
-                                          HI.as_f64(inp["v_tree"][b:b + 1])[None], n_acc[b:b + 1],
-                                          path[b:b + 1], out[b:b + 1], Dm)
-        assert np.array_equal(np_(dev["k_pages"][pages]), rk[0]), f"seq {b}: committed K pages"
-        assert np.array_equal(np_(dev["v_pages"][pages]), rv[0]), f"seq {b}: committed V pages"
+        if layered:
+            sub = lambda pool: HI.as_f64(pool[:, pages])  # noqa: E731
+            ksrc, vsrc = np_(rnd.k_layers[:, b:b + 1]), np_(rnd.v_layers[:, b:b + 1])
+        else:
+            sub = lambda pool: HI.as_f64(pool[pages])[None]  # noqa: E731
+            ksrc = np_((rnd.k_rot if rnd.rope_theta else inp["k_tree"])[b:b + 1])[None]  # the keys committed
+            vsrc = HI.as_f64(inp["v_tree"][b:b + 1])[None]
+        rk, rv, rl, rr, _ = O.commit_path(sub(inp["k_pages"]), sub(inp["v_pages"]), sub_bt, lens[b:b + 1], ksrc,
+                                          vsrc, n_acc[b:b + 1], path[b:b + 1], out[b:b + 1], Dm)
+        got_k = np_(dev["k_pages"][:, pages]) if layered else np_(dev["k_pages"][pages])[None]
+        got_v = np_(dev["v_pages"][:, pages]) if layered else np_(dev["v_pages"][pages])[None]
+        assert np.array_equal(got_k, rk), f"seq {b}: committed K pages"
+        assert np.array_equal(got_v, rv), f"seq {b}: committed V pages"
         assert nlen[b] == rl[0] and nroot[b] == rr[0], f"seq {b}: next length / root"
         assert torch.equal(nh[b], hid[b, int(path[b, n_acc[b]])]), f"seq {b}: next h"
     # whole pool: differences only at committed positions
     for name in ("k_pages", "v_pages"):
-        ne = dev[name] != inp[name].to(dev[name].device)        # [pages, Hkv, slot, D]
+        ne = dev[name] != inp[name].to(dev[name].device)        # [(layers,) pages, Hkv, slot, D]
+        if layered:
+            ne = ne.any(dim=0)
         diff = ne.permute(0, 2, 1, 3).flatten(2).any(dim=2)      # [pages, slot]
         diff = diff.cpu().numpy().copy()
         for b in range(w.B):

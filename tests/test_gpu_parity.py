@@ -1056,6 +1056,28 @@ def test_tree_decoder_layer(dtype, B, tree, d, Hq, Hkv, D, F, lens, layers):
         xs_dev, xs_ref = out, ref  # each side's next layer reads its own output
 
 
+@pytest.mark.parametrize("name,over", [("tiny_layers", {}), ("tiny_layers", {"dtype": "bf16"}),
+                                       ("tiny_layers", {"mode": "stochastic", "T": 0.8, "layers": 2}),
+                                       ("7b_layers", {"layers": 2})])
+def test_round_through_the_target_layers(name, over):
+    """A whole round whose verification runs the target's decoder layers over
+    the tree tokens (tree_verify_layers): the device's final hidden states and
+    every layer's rotated K/V against the oracle's chain of layers on the
+    device's tree, acceptance on those hidden states, and the commit of every
+    layer's K/V of the kept branch (bit-exact)."""
+    w = HI.workload(name, **over)
+    print(f"round through the target's layers {w.name} {w.dtype} layers={w.layers} B={w.B} mode={w.mode}",
+          flush=True)
+    inp = HI.generate(w)
+    rnd, dev = T.round_inputs(inp, device="cuda")
+    T.run_round(rnd, dev)
+    torch.cuda.synchronize()
+    seqs = [0] if w.d >= 4096 else None
+    rep = T.oracle_round_checks(inp, rnd, seqs=seqs, rows=[0, 1] if seqs else None)
+    rep.update(T.check_commit(inp, rnd, dev, seqs=seqs))
+    print("  ", {k: v for k, v in rep.items() if not isinstance(v, list)}, flush=True)
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
 def test_tree_attention_prefix_beyond_the_plan(dtype):
     """max_prefix_len only sizes the split plan: prefixes longer than it (a

@@ -1077,3 +1077,109 @@ def test_decoder_layer_matches_transformers_llama_layer(tree, Hq, Hkv):
         # the cache now holds the layer's rotated tree keys and values after the prefix
         ck, cv = cache.layers[0].keys[0].transpose(0, 1).numpy(), cache.layers[0].values[0].transpose(0, 1).numpy()
         assert np.allclose(ck[L:], k_rot[b], rtol=1e-5, atol=1e-5) and np.allclose(cv[L:], v[b], rtol=1e-5, atol=1e-5)
+
+
+# -------------------------------------------------------- the target's forward pass
+
+def _layer_dict(rng, d, F, Hq, Hkv, D):
+    return dict(g1=1 + 0.1 * rng.standard_normal(d), g2=1 + 0.1 * rng.standard_normal(d),
+                Wq=0.2 * rng.standard_normal((Hq * D, d)), Wk=0.2 * rng.standard_normal((Hkv * D, d)),
+                Wv=0.2 * rng.standard_normal((Hkv * D, d)), Wo=0.2 * rng.standard_normal((d, Hq * D)),
+                Wg=0.2 * rng.standard_normal((F, d)), Wu=0.2 * rng.standard_normal((F, d)),
+                Wd=0.2 * rng.standard_normal((d, F)))
+
+
+def test_verify_layers_matches_transformers_llama_model_on_a_chain():
+    """On a chain-shaped tree with nothing cached, tree attention is causal
+    attention at positions 0..N-1, so the oracle's forward pass (embeddings,
+    layers, final norm) must equal transformers' LlamaModel on the same ids in
+    float64, hidden states and every layer's cached keys and values alike."""
+    from transformers import LlamaConfig, LlamaModel
+
+    rng = np.random.default_rng(81)
+    n_layers, Hq, Hkv, D, F, V, eps, theta = 3, 4, 2, 8, 40, 50, 1e-6, 10000.0
+    d = Hq * D
+    plan = H.plan_cartesian([1, 1, 1, 1, 1])  # root and five drafts in a line
+    assert list(plan.parent) == [-1, 0, 1, 2, 3, 4]
+    B, N = 2, plan.n
+    tok = rng.integers(0, V, (B, N))
+    E = rng.standard_normal((V, d))
+    layers = [_layer_dict(rng, d, F, Hq, Hkv, D) for _ in range(n_layers)]
+    g_f = 1 + 0.1 * rng.standard_normal(d)
+    empty = [np.zeros((0, Hkv, D))] * B
+    anc = np.stack([H.ancestors(plan.parent, plan.dmax)] * B)
+    depth = np.stack([plan.depth] * B)
+    h, k, v = H.verify_layers(tok, E, layers, g_f, [empty] * n_layers, [empty] * n_layers, anc, depth, [0] * B,
+                              Hq, Hkv, D, eps, theta)
+    cfg = LlamaConfig(hidden_size=d, intermediate_size=F, num_attention_heads=Hq, num_key_value_heads=Hkv,
+                      head_dim=D, rms_norm_eps=eps, rope_theta=theta, num_hidden_layers=n_layers, vocab_size=V)
+    cfg._attn_implementation = "eager"
+    model = LlamaModel(cfg).double().eval()
+    t = lambda a: torch.from_numpy(np.asarray(a, dtype=np.float64))  # noqa: E731
+    with torch.no_grad():
+        model.embed_tokens.weight.copy_(t(E))
+        model.norm.weight.copy_(t(g_f))
+        for layer, w in zip(model.layers, layers):
+            layer.input_layernorm.weight.copy_(t(w["g1"]))
+            layer.post_attention_layernorm.weight.copy_(t(w["g2"]))
+            for name, key in (("q_proj", "Wq"), ("k_proj", "Wk"), ("v_proj", "Wv"), ("o_proj", "Wo")):
+                getattr(layer.self_attn, name).weight.copy_(t(w[key]))
+            for name, key in (("gate_proj", "Wg"), ("up_proj", "Wu"), ("down_proj", "Wd")):
+                getattr(layer.mlp, name).weight.copy_(t(w[key]))
+        out = model(input_ids=torch.from_numpy(tok), use_cache=True)
+    assert np.allclose(h, out.last_hidden_state.numpy(), rtol=1e-5, atol=1e-5)
+    for l in range(n_layers):
+        ck = out.past_key_values.layers[l].keys.transpose(1, 2).numpy()
+        cv = out.past_key_values.layers[l].values.transpose(1, 2).numpy()
+        assert np.allclose(k[l], ck, rtol=1e-5, atol=1e-5) and np.allclose(v[l], cv, rtol=1e-5, atol=1e-5)
+
+
+def test_verify_layers_on_a_tree_with_cached_prefixes_matches_transformers_modules():
+    """A branching tree over per-layer cached prefixes of different lengths:
+    the forward pass equals transformers' own pieces chained by hand (the
+    embedding lookup, LlamaDecoderLayer per layer with that layer's prefix
+    in its cache, position ids L + depth and the tree mask, LlamaRMSNorm); a
+    token outside the table gives its row a zero input."""
+    from transformers import DynamicCache
+    from transformers.models.llama.modeling_llama import LlamaRMSNorm
+
+    rng = np.random.default_rng(82)
+    n_layers, Hq, Hkv, D, F, V, eps, theta = 2, 4, 2, 8, 40, 30, 1e-6, 10000.0
+    d = Hq * D
+    plan = H.plan_cartesian([2, 3])
+    N, lens = plan.n, [4, 9]
+    B = len(lens)
+    tok = rng.integers(0, V, (B, N))
+    tok[1, 2] = V + 5  # outside the table
+    E = rng.standard_normal((V, d))
+    layers = [_layer_dict(rng, d, F, Hq, Hkv, D) for _ in range(n_layers)]
+    g_f = 1 + 0.1 * rng.standard_normal(d)
+    kp = [[rng.standard_normal((L, Hkv, D)) for L in lens] for _ in range(n_layers)]
+    vp = [[rng.standard_normal((L, Hkv, D)) for L in lens] for _ in range(n_layers)]
+    anc = np.stack([H.ancestors(plan.parent, plan.dmax)] * B)
+    depth = np.stack([plan.depth] * B)
+    h, k, v = H.verify_layers(tok, E, layers, g_f, kp, vp, anc, depth, lens, Hq, Hkv, D, eps, theta)
+    mods = [_llama_layer(d, F, Hq, Hkv, D, eps, theta, w) for w in layers]
+    norm = LlamaRMSNorm(d, eps=eps).double()
+    with torch.no_grad():
+        norm.weight.copy_(torch.from_numpy(g_f))
+    vis = H.tree_mask(plan.parent)
+    Et = torch.from_numpy(np.concatenate([E, np.zeros((1, d))]))  # the zero row stands in for the bad token
+    for b, L in enumerate(lens):
+        ids = torch.from_numpy(np.where(tok[b] < V, tok[b], V))
+        hs = torch.nn.functional.embedding(ids, Et)[None]
+        mask = np.concatenate([np.zeros((N, L)), np.where(np.isfinite(vis), 0.0, np.finfo(np.float64).min)], axis=1)
+        pos_ids = torch.from_numpy(L + plan.depth)[None]
+        for l, (cfg, layer, rot) in enumerate(mods):
+            cache = DynamicCache()
+            cache.update(torch.from_numpy(kp[l][b]).transpose(0, 1)[None],
+                         torch.from_numpy(vp[l][b]).transpose(0, 1)[None], 0)
+            with torch.no_grad():
+                hs = layer(hs, attention_mask=torch.from_numpy(mask)[None, None], position_ids=pos_ids,
+                           past_key_values=cache, use_cache=True, position_embeddings=rot(hs, pos_ids))
+            hs = hs[0] if isinstance(hs, tuple) else hs
+            ck = cache.layers[0].keys[0].transpose(0, 1).numpy()
+            assert np.allclose(ck[L:], k[l, b], rtol=1e-5, atol=1e-5)
+        with torch.no_grad():
+            ref = norm(hs)[0].numpy()
+        assert np.allclose(h[b], ref, rtol=1e-5, atol=1e-5)

@@ -29,8 +29,10 @@ The JSON line also carries
   configs       the same round on the other workloads (7B dense 256-row
                 tree at prefix 8192, the 64-node tree at prefix 8192, 16
                 ragged sequences, the 70B GQA layer with rejection
-                acceptance) and the headline round with W1's embedding half
-                streamed: ms, verified rows/s and round HBM fraction each
+                acceptance, the 7B round verified through all 32 of the
+                target's decoder layers) and the headline round with W1's
+                embedding half streamed: ms, verified rows/s and round HBM
+                fraction each
                 (their inputs are drawn on the device; --no-configs skips);
   cpu_baseline  the CPU oracle timed on this host on one full round of the
                 same workload (rank 0, one GPU only).
@@ -196,6 +198,14 @@ def round_bytes(w, rnd, prefix_len):
     target = V * d * esz + B * N * d * esz + B * N * V * 4
     kept = int(rnd.n_accepted.clamp(min=0).sum()) + B  # root + accepted rows
     commit = kept * w.Hkv * w.D * esz * 2 * 2 + B * d * esz * 2
+    if w.layers:
+        # the target's layers: each streams its weights and reads its prefix
+        # K/V once; the rows' activations in and out; embedding rows read and
+        # final hidden states written; the commit moves every layer's K/V
+        weights = ((w.Hq + 2 * w.Hkv) * w.D * d + d * w.Hq * w.D + 3 * w.ffn * d + 2 * d) * esz
+        acts = B * N * (2 * d + 2 * w.Hkv * w.D) * esz
+        attn = w.layers * (weights + prefix * w.Hkv * w.D * esz * 2 + acts) + 2 * B * N * d * esz
+        commit = w.layers * kept * w.Hkv * w.D * esz * 2 * 2 + B * d * esz * 2
     return draft + attn + target + commit
 
 
@@ -364,7 +374,7 @@ def time_round(rnd, dev, steps, warmup, use_graph=True):
 # the other workloads of the same round, each on its own synthetic inputs
 # (drawn on the device); the first uses the headline's inputs with the
 # embedding half of W1 streamed every round instead of the folded tables
-CONFIGS = ["7b_sparse64:streamed", "7b_dense256", "7b_sparse64_L8192", "7b_batched16", "70b_gqa"]
+CONFIGS = ["7b_sparse64:streamed", "7b_dense256", "7b_sparse64_L8192", "7b_batched16", "70b_gqa", "7b_layers"]
 
 
 def configs_measure(head_inp, steps, warmup, use_graph=True):
@@ -388,7 +398,8 @@ def configs_measure(head_inp, steps, warmup, use_graph=True):
                      "round_bytes": rb, "round_hbm_frac": rb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                      "acceptance": w.mode, "embedding_half": ("folded table" if rnd.emb_proj is not None
                                                               else "streamed") if w.hydra else None,
-                     "launch": "hip-graph" if graph is not None else "eager"}
+                     "launch": "hip-graph" if graph is not None else "eager",
+                     "target_layers": w.layers or None}
         log(f"[bench] {spec}: {ms:.4f} ms/round ({time.perf_counter() - t0:.1f} s)")
         del graph, rnd, dev
         if inp is not head_inp:

@@ -31,8 +31,9 @@ The JSON line also carries
                 ragged sequences, the 70B GQA layer with rejection
                 acceptance, the 7B round verified through all 32 of the
                 target's decoder layers) and the headline round with W1's
-                embedding half streamed: ms, verified rows/s and round HBM
-                fraction each
+                embedding half streamed, and with its vocabulary weights
+                row-major rather than packed: ms, verified rows/s and round
+                HBM fraction each
                 (their inputs are drawn on the device; --no-configs skips);
   cpu_baseline  the CPU oracle timed on this host on one full round of the
                 same workload (rank 0, one GPU only).
@@ -150,8 +151,11 @@ def mfma_measure(W2s, M=1024, reps=10, use_graph=True):
     us = a.elapsed_time(b) / reps * 1e3
     flops = 2.0 * M * N * K
     tf = flops / (us * 1e-6) / 1e12
+    from speculative_decoding_hydra_amd import PackedWeight
+
     return {"kernel": "proj_gemm_kernel (tiled vocabulary projection, arg-max epilogue)", "rows": M, "cols": N,
-            "depth": K, "flops": flops, "avg_launch_us": us, "achieved_TFLOPs": tf, "peak_TFLOPs": MFMA_PEAK_TFLOPS,
+            "depth": K, "weight_layout": "packed" if isinstance(W2s[0], PackedWeight) else "row-major",
+            "flops": flops, "avg_launch_us": us, "achieved_TFLOPs": tf, "peak_TFLOPs": MFMA_PEAK_TFLOPS,
             "frac": tf / MFMA_PEAK_TFLOPS, "counters": measured_mfma()}
 
 
@@ -374,7 +378,8 @@ def time_round(rnd, dev, steps, warmup, use_graph=True):
 # the other workloads of the same round, each on its own synthetic inputs
 # (drawn on the device); the first uses the headline's inputs with the
 # embedding half of W1 streamed every round instead of the folded tables
-CONFIGS = ["7b_sparse64:streamed", "7b_dense256", "7b_sparse64_L8192", "7b_batched16", "70b_gqa", "7b_layers"]
+CONFIGS = ["7b_sparse64:streamed", "7b_sparse64:row-major", "7b_dense256", "7b_sparse64_L8192", "7b_batched16",
+           "70b_gqa", "7b_layers"]
 
 
 def configs_measure(head_inp, steps, warmup, use_graph=True):
@@ -388,9 +393,10 @@ def configs_measure(head_inp, steps, warmup, use_graph=True):
         name, _, variant = spec.partition(":")
         t0 = time.perf_counter()
         w = HI.workload(name)
-        inp = head_inp if variant == "streamed" else HI.generate(w, device="cuda")
+        inp = head_inp if variant in ("streamed", "row-major") else HI.generate(w, device="cuda")
         rnd, dev = round_from_inputs(inp, device="cuda:0", keep_hidden=False,
-                                     fold_embedding=False if variant == "streamed" else None)
+                                     fold_embedding=False if variant == "streamed" else None,
+                                     pack_vocab=False if variant == "row-major" else None)
         ms, graph, dist = time_round(rnd, dev, steps, warmup, use_graph)
         rows = w.B * rnd.n_keep
         rb = round_bytes(w, rnd, inp["prefix_len"].cpu())
@@ -398,6 +404,7 @@ def configs_measure(head_inp, steps, warmup, use_graph=True):
                      "round_bytes": rb, "round_hbm_frac": rb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                      "acceptance": w.mode, "embedding_half": ("folded table" if rnd.emb_proj is not None
                                                               else "streamed") if w.hydra else None,
+                     "vocab_weights": "packed" if rnd.pack_vocab else "row-major",
                      "launch": "hip-graph" if graph is not None else "eager",
                      "target_layers": w.layers or None}
         log(f"[bench] {spec}: {ms:.4f} ms/round ({time.perf_counter() - t0:.1f} s)")
@@ -496,7 +503,10 @@ def main():
     torch.cuda.set_device(0)
     if args.mfma_only:
         g = torch.Generator(device="cuda").manual_seed(1)
-        W2s = [(torch.randn(32000, 4096, device="cuda", generator=g) * 0.02).to(torch.bfloat16) for _ in range(4)]
+        from speculative_decoding_hydra_amd import hydra_pack_weight
+
+        W2s = [hydra_pack_weight((torch.randn(32000, 4096, device="cuda", generator=g) * 0.02).to(torch.bfloat16))
+               for _ in range(4)]  # packed, as the rounds hold their vocabulary weights
         print(json.dumps(mfma_measure(W2s, use_graph=not args.no_graph)), flush=True)
         return
     w = HI.workload(args.workload)
@@ -541,7 +551,7 @@ def main():
     X = torch.randn(M, w.d, device="cuda").to(rnd.dtype)
     Y = torch.empty(M, w.V, device="cuda")
     kws = torch.empty(hydra_vocab_projection_workspace_size(M, w.V, kk), dtype=torch.uint8, device="cuda")
-    W2s = [hd["W2"] for hd in rnd.w["heads"]] if rnd.sketch else rnd.w["W2"]
+    W2s = [hd["W2"] for hd in rnd.heads] if rnd.sketch else rnd.W2  # as the round holds them (packed or not)
     W2 = W2s[0]
     proj = lambda Wm: hydra_vocab_projection(X, Wm, Y, kk, kws)  # noqa: E731
     for _ in range(3):
@@ -618,12 +628,14 @@ def main():
                    "prefix": list(w.L), "tree": str(w.tree[0]), "acceptance": w.mode,
                    "launch": "hip-graph" if graph is not None else "eager",
                    "embedding_half": ("folded table" if rnd.emb_proj is not None else "streamed")
-                   if w.hydra else None},
+                   if w.hydra else None,
+                   "vocab_weights": "packed" if rnd.pack_vocab else "row-major"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(),
                      "kernel": ("proj_bf16_kernel (streaming vocabulary projection, fused top-k epilogue)"
                                 if M < 65 else "proj_gemm_kernel (tiled vocabulary projection, fused top-k epilogue)"),
-                     "bytes_per_launch": alg_bytes, "rows": M, "topk": kk, "avg_launch_ms": k_ms},
+                     "bytes_per_launch": alg_bytes, "rows": M, "topk": kk, "avg_launch_ms": k_ms,
+                     "weight_layout": "packed" if rnd.pack_vocab else "row-major"},
         "mfma": mfma,
         "round_ms": round_ms,
         "round_bytes": rbytes,

@@ -39,6 +39,10 @@
  *     activation and weight tensors: HYDRA_F32 (float) or HYDRA_BF16
  *     (bfloat16 bits in uint16). Logits, log-sum-exps and cumulative
  *     log-probabilities are always float32; token ids and indices int32.
+ *     With HYDRA_BF16, OR-ing HYDRA_VOCAB_PACKED into dtype says that the
+ *     vocabulary projection weights of the call (the heads' W2, W_t, the W
+ *     of hydra_vocab_projection) are in the packed layout of
+ *     hydra_pack_weight; every other tensor keeps its row-major layout.
  *   - Entry points are stateless and reentrant; calls that share a workspace
  *     must be ordered on one stream.
  */
@@ -60,6 +64,7 @@ extern "C" {
 
 #define HYDRA_F32 0
 #define HYDRA_BF16 1
+#define HYDRA_VOCAB_PACKED 0x100 /* dtype flag: vocabulary weights packed */
 
 #define HYDRA_MAX_DEPTH 8     /* deepest tree (number of draft heads used) */
 #define HYDRA_MAX_TOPK 16     /* widest fan-out of one node */
@@ -115,6 +120,30 @@ int hydra_plan_rows(int N, const int32_t* parent, const int32_t* rank,
                     const int32_t* depth, int hydra, int32_t* node_row,
                     int32_t* row_node, int32_t* row_first, int32_t* depth_first,
                     int32_t* k_per_depth);
+
+/* ------------------------------------------------------------------------
+ * Packed weight layout for the streaming projections
+ *
+ * The vocabulary projections stream W once per call and are bound by HBM
+ * reads. Row-major, the chip's concurrent reads of a K chunk are 512-byte
+ * pieces 2K bytes apart (one per row); packed, every 16-row tile's chunk
+ * of 256 columns is 8 KB in one place and chunk c of all tiles lies in one
+ * contiguous range, so the reads of a chunk sweep contiguous memory (same
+ * arithmetic, a layout of the same values). Layout: tiles of 16 rows (the
+ * last one padded with zero rows), chunk-major: chunk c of tile t is 4096
+ * bf16 at (c * ceil(N / 16) + t) * 4096; inside it, 32-column step s at
+ * + 512 s, 8-column group g at + 128 g, row r at + 8 r (8 values of row
+ * 16 t + r, columns 256 c + 32 s + 8 g ..).
+ *
+ * hydra_packed_weight_size: bytes of the packed copy of a bf16 W [N, K]
+ * (0 when K % 256 != 0 or a size is not positive).
+ * hydra_pack_weight: writes it; W and packed 16-byte aligned, not aliasing.
+ * Errors: HYDRA_ERR_INVALID (sizes, null or aliasing pointers),
+ * HYDRA_ERR_UNSUPPORTED (K % 256 != 0). No workspace.
+ * ---------------------------------------------------------------------- */
+size_t hydra_packed_weight_size(int N, int K);
+
+int hydra_pack_weight(int N, int K, const void* W, void* packed, void* stream);
 
 /* ------------------------------------------------------------------------
  * Stage 1: draft heads

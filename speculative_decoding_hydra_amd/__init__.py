@@ -6,10 +6,10 @@ include/hydra.h, bound under the same names in
 of a round and calls them in order.
 """
 from .hydra import (  # noqa: F401
-    DevicePlan, HydraError, PlanRows, TreePlan, hydra_draft_heads, hydra_draft_heads_attn,
+    DevicePlan, HydraError, PackedWeight, PlanRows, TreePlan, hydra_draft_heads, hydra_draft_heads_attn,
     hydra_draft_heads_attn_workspace_size, hydra_draft_heads_sketch,
     hydra_draft_heads_sketch_workspace_size, hydra_draft_heads_workspace_size,
-    hydra_fold_embedding, hydra_plan_cartesian, hydra_plan_rows, hydra_plan_sparse, hydra_vocab_projection,
+    hydra_fold_embedding, hydra_pack_weight, hydra_packed_weight_size, hydra_plan_cartesian, hydra_plan_rows, hydra_plan_sparse, hydra_vocab_projection,
     hydra_vocab_projection_workspace_size, hydra_vocab_topk, tree_accept, tree_accept_noalloc,
     tree_accept_workspace_size, tree_attention_verify, tree_attention_verify_workspace_size, tree_build,
     tree_build_workspace_size, tree_commit, tree_decoder_layer, tree_decoder_layer_workspace_size, tree_rope,

@@ -38,6 +38,8 @@ SIGNATURES = {
     "hydra_vocab_projection_workspace_size": (c_size, [c_int, c_int, c_int]),
     "hydra_vocab_projection": (c_int, [c_int, c_int, c_int, c_int, c_int, c_void, c_void, c_void, c_void, c_size,
                                        c_void]),
+    "hydra_packed_weight_size": (c_size, [c_int, c_int]),
+    "hydra_pack_weight": (c_int, [c_int, c_int, c_void, c_void, c_void]),
     "hydra_vocab_topk": (c_int, [c_int, c_int, c_int, c_void, c_void, c_size, c_void, c_void, c_void, c_void]),
     "tree_build_workspace_size": (c_size, [c_int, c_int, c_int]),
     "tree_build": (c_int, [c_int, c_int, c_int, c_void, c_void, c_void, c_void, c_void, c_void, c_int,

@@ -854,7 +854,10 @@ extern "C" int tree_accept(int dtype, int mode, int B, int N, int d, int V, int 
                            int32_t* out_tok, void* ws, size_t ws_bytes, void* stream_) {
   clear_error();
   hipStream_t stream = static_cast<hipStream_t>(stream_);
+  const int vpack = dtype & HYDRA_VOCAB_PACKED;  // packed vocabulary weights (hydra_pack_weight)
+  dtype &= ~HYDRA_VOCAB_PACKED;
   HY_CHECK(dtype == HYDRA_F32 || dtype == HYDRA_BF16, HYDRA_ERR_INVALID, "tree_accept: bad dtype %d", dtype);
+  HY_CHECK(!vpack || dtype == HYDRA_BF16, HYDRA_ERR_UNSUPPORTED, "tree_accept: packed vocabulary weights are bf16");
   HY_CHECK(mode >= 0 && mode <= 2, HYDRA_ERR_INVALID, "tree_accept: mode %d not in {0, 1, 2}", mode);
   HY_CHECK(B > 0 && N > 0 && d > 0 && V > 0, HYDRA_ERR_INVALID, "tree_accept: bad sizes B=%d N=%d d=%d V=%d", B, N,
            d, V);
@@ -893,7 +896,7 @@ extern "C" int tree_accept(int dtype, int mode, int B, int N, int d, int V, int 
     // the row merge's last workgroup per sequence walks; otherwise a walk kernel
     const bool fused_walk = B <= 256;
     TopkPartials tp{keys, nullptr, fused_walk ? walk_count : nullptr, fused_walk ? B : 0};
-    int rc = launch_projection(dtype, M, d, V, xs, W_t, target_logits, RowMap{M, 0, 0}, V, 1, nullptr, tp, stream);
+    int rc = launch_projection(dtype | vpack, M, d, V, xs, W_t, target_logits, RowMap{M, 0, 0}, V, 1, nullptr, tp, stream);
     if (rc != HYDRA_OK) return rc;
     MergeArgs ma{};
     ma.M = M;
@@ -924,7 +927,7 @@ extern "C" int tree_accept(int dtype, int mode, int B, int N, int d, int V, int 
       HY_LAUNCH_CHECK("tree_accept: greedy walk");
     }
   } else if (mode == 2) {
-    int rc = launch_projection(dtype, M, d, V, xs, W_t, target_logits, RowMap{M, 0, 0}, V, 1, nullptr,
+    int rc = launch_projection(dtype | vpack, M, d, V, xs, W_t, target_logits, RowMap{M, 0, 0}, V, 1, nullptr,
                                TopkPartials{nullptr, nullptr}, stream);
     if (rc != HYDRA_OK) return rc;
     int32_t* pass = arena.take<int32_t>(static_cast<size_t>(M));
@@ -947,7 +950,7 @@ extern "C" int tree_accept(int dtype, int mode, int B, int N, int d, int V, int 
       HY_LAUNCH_CHECK("tree_accept: typical walk");
     }
   } else {
-    int rc = launch_projection(dtype, M, d, V, xs, W_t, target_logits, RowMap{M, 0, 0}, V, 1, nullptr,
+    int rc = launch_projection(dtype | vpack, M, d, V, xs, W_t, target_logits, RowMap{M, 0, 0}, V, 1, nullptr,
                                TopkPartials{nullptr, nullptr}, stream);
     if (rc != HYDRA_OK) return rc;
     int32_t* nxt = arena.take<int32_t>(static_cast<size_t>(M));

@@ -269,6 +269,20 @@ struct TopkPartials {
   int nclear;
 };
 
+// Packed weight layout (hydra_pack_weight): W [N][K] bf16 as 16-row tiles
+// and 256-column chunks, chunk-major: chunk c of tile t is 8 KB at
+// (c * ntiles + t) * 4096 elements; inside it, 32-column step s, then
+// 8-column group g, then row r (16 bytes each), which is the operand order
+// of v_mfma_f32_16x16x32_bf16 (lane 16 g + r holds row r, columns 8 g ..).
+// Rows past N in the last tile are zeros. Element offset of the 16-byte
+// piece holding row n, columns k .. k + 7 (k % 8 == 0):
+constexpr int kPackChunk = 256;
+__host__ __device__ inline size_t packed_piece(int n, int k, int N) {
+  const size_t ntiles = static_cast<size_t>((N + 15) / 16);
+  return ((static_cast<size_t>(k >> 8) * ntiles + (n >> 4)) * 8 + ((k & 255) >> 5)) * 512 +
+         static_cast<size_t>(((k & 31) >> 3) * 16 + (n & 15)) * 8;
+}
+
 constexpr int kProjRowsPerWG = 64;
 __host__ __device__ inline int projection_nwg(int N) { return (N + kProjRowsPerWG - 1) / kProjRowsPerWG; }
 
@@ -278,7 +292,7 @@ int launch_projection(int dtype, int M, int K, int N, XSource xs, const void* W,
 
 // Tiled matrix-core projection for many contiguous rows (bf16, K % 64 == 0),
 // same outputs and partials as launch_projection; row n of W starts at
-// W + n * ldw.
+// W + n * ldw, or ldw < 0: W is in the packed layout (K % 256 == 0).
 bool gemm_supported(int K);
 int launch_projection_gemm(int M, int K, int N, const bf16_t* X, int ldx, const bf16_t* W, int ldw, float* Y,
                            RowMap map, int ldy, TopkPartials tp, hipStream_t stream);

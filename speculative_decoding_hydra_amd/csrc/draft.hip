@@ -120,7 +120,7 @@ DraftWs draft_ws(int dtype, int B, int d, int V, int hydra_mode, int Dmax, const
 extern "C" size_t hydra_draft_heads_workspace_size(int dtype, int B, int d, int V, int hydra_mode,
                                                    int Dmax, const int32_t* row_first) {
   if (B <= 0 || d <= 0 || V <= 0 || Dmax <= 0 || Dmax > HYDRA_MAX_DEPTH || !row_first) return 0;
-  return draft_ws(dtype, B, d, V, hydra_mode, Dmax, row_first, nullptr).total;
+  return draft_ws(dtype & ~HYDRA_VOCAB_PACKED, B, d, V, hydra_mode, Dmax, row_first, nullptr).total;
 }
 
 extern "C" int hydra_draft_heads(int dtype, int B, int d, int V, int hydra_mode, int residual,
@@ -135,7 +135,10 @@ extern "C" int hydra_draft_heads(int dtype, int B, int d, int V, int hydra_mode,
                                  float* cand_logp, void* ws, size_t ws_bytes, void* stream_) {
   clear_error();
   hipStream_t stream = static_cast<hipStream_t>(stream_);
+  const int vpack = dtype & HYDRA_VOCAB_PACKED;  // packed vocabulary weights (hydra_pack_weight)
+  dtype &= ~HYDRA_VOCAB_PACKED;
   HY_CHECK(dtype == HYDRA_F32 || dtype == HYDRA_BF16, HYDRA_ERR_INVALID, "draft_heads: bad dtype %d", dtype);
+  HY_CHECK(!vpack || dtype == HYDRA_BF16, HYDRA_ERR_UNSUPPORTED, "draft_heads: packed vocabulary weights are bf16");
   HY_CHECK(B > 0 && d > 0 && V > 0, HYDRA_ERR_INVALID, "draft_heads: bad sizes B=%d d=%d V=%d", B, d, V);
   HY_CHECK(Dmax >= 1 && Dmax <= HYDRA_MAX_DEPTH, HYDRA_ERR_INVALID, "draft_heads: Dmax=%d out of [1, %d]", Dmax, HYDRA_MAX_DEPTH);
   HY_CHECK(hydra_mode >= 0 && hydra_mode <= 2, HYDRA_ERR_INVALID, "draft_heads: hydra mode %d", hydra_mode);
@@ -372,7 +375,7 @@ extern "C" int hydra_draft_heads(int dtype, int B, int d, int V, int hydra_mode,
     xu.ldx = d;
     xu.mode = 0;
     const int kk = k_per_depth[k - 1];
-    rc = launch_projection(dtype, M, d, V, xu, W2[k - 1], head_logits, map, V, 1, nullptr,
+    rc = launch_projection(dtype | vpack, M, d, V, xu, W2[k - 1], head_logits, map, V, 1, nullptr,
                            TopkPartials{tkeys, tms}, stream);
     if (rc != HYDRA_OK) return rc;
     // 3. log-sum-exp, top-k, tree fill

@@ -96,10 +96,11 @@ __global__ __launch_bounds__(GTHREADS, 2) void proj_gemm_kernel(GemmArgs a) {
   const int klen = a.K - kb < a.kper ? a.K - kb : a.kper;
   const int wn = wave & 1, wm = wave >> 1;  // 2 x 4 waves: WN n x 64 m each
 
-  // global -> register staging: WLD vectors of 16 bytes of W and 4 of X per thread
+  // global -> register staging: WLD vectors of 16 bytes of W and 4 of X per
+  // thread; packed W (ldw < 0) is addressed piece by piece
   const bf16_t* wsrc[WLD];
   const bf16_t* xsrc[4];
-  int woff[WLD], xoff[4];
+  int woff[WLD], xoff[4], wrn[WLD], wk[WLD];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int idx = tid + j * GTHREADS;
@@ -109,7 +110,9 @@ __global__ __launch_bounds__(GTHREADS, 2) void proj_gemm_kernel(GemmArgs a) {
     xoff[j] = swz(r, idx & 7);
     if (j < WLD) {
       const int n = n0 + r < a.N ? n0 + r : a.N - 1;  // rows past the end re-read the last row
-      wsrc[j] = a.W + static_cast<size_t>(n) * a.ldw + kb + c;
+      wsrc[j] = a.ldw < 0 ? a.W : a.W + static_cast<size_t>(n) * a.ldw + kb + c;
+      wrn[j] = n;
+      wk[j] = kb + c;
       woff[j] = xoff[j];
     }
   }
@@ -117,7 +120,9 @@ __global__ __launch_bounds__(GTHREADS, 2) void proj_gemm_kernel(GemmArgs a) {
   auto load = [&](int k0) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      if (j < WLD) wreg[j] = *reinterpret_cast<const u32x4_t*>(wsrc[j] + k0);
+      if (j < WLD)
+        wreg[j] = *reinterpret_cast<const u32x4_t*>(a.ldw < 0 ? wsrc[j] + packed_piece(wrn[j], wk[j] + k0, a.N)
+                                                              : wsrc[j] + k0);
       xreg[j] = *reinterpret_cast<const u32x4_t*>(xsrc[j] + k0);
     }
   };

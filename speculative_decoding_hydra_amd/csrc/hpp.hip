@@ -219,7 +219,7 @@ using namespace hydra;
 extern "C" size_t hydra_draft_heads_attn_workspace_size(int dtype, int B, int d, int V, int N, int Dmax,
                                                         const int32_t* row_first) {
   if (B <= 0 || d <= 0 || V <= 0 || N <= 0 || Dmax <= 0 || Dmax > HYDRA_MAX_DEPTH || !row_first) return 0;
-  return attn_ws(dtype, B, d, V, N, Dmax, row_first).total;
+  return attn_ws(dtype & ~HYDRA_VOCAB_PACKED, B, d, V, N, Dmax, row_first).total;
 }
 
 extern "C" int hydra_draft_heads_attn(int dtype, int B, int d, int V, int residual, const void* h,
@@ -233,7 +233,10 @@ extern "C" int hydra_draft_heads_attn(int dtype, int B, int d, int V, int residu
                                       size_t ws_bytes, void* stream_) {
   clear_error();
   hipStream_t stream = static_cast<hipStream_t>(stream_);
+  const int vpack = dtype & HYDRA_VOCAB_PACKED;  // packed vocabulary weights (hydra_pack_weight)
+  dtype &= ~HYDRA_VOCAB_PACKED;
   HY_CHECK(dtype == HYDRA_F32 || dtype == HYDRA_BF16, HYDRA_ERR_INVALID, "draft_heads_attn: bad dtype %d", dtype);
+  HY_CHECK(!vpack || dtype == HYDRA_BF16, HYDRA_ERR_UNSUPPORTED, "draft_heads_attn: packed vocabulary weights are bf16");
   HY_CHECK(B > 0 && d > 0 && V > 0, HYDRA_ERR_INVALID, "draft_heads_attn: bad sizes B=%d d=%d V=%d", B, d, V);
   HY_CHECK(d <= kMaxWidth, HYDRA_ERR_UNSUPPORTED, "draft_heads_attn: d=%d > %d", d, kMaxWidth);
   HY_CHECK(dtype == HYDRA_F32 || d % 256 == 0, HYDRA_ERR_UNSUPPORTED, "draft_heads_attn: bf16 needs d %% 256 == 0");
@@ -333,7 +336,7 @@ extern "C" int hydra_draft_heads_attn(int dtype, int B, int d, int V, int residu
     xu.x = U;
     xu.ldx = d;
     xu.mode = 0;
-    rc = launch_projection(dtype, M, d, V, xu, W2[k - 1], head_logits, map, V, 1, nullptr, TopkPartials{tkeys, tms},
+    rc = launch_projection(dtype | vpack, M, d, V, xu, W2[k - 1], head_logits, map, V, 1, nullptr, TopkPartials{tkeys, tms},
                            stream);
     if (rc != HYDRA_OK) return rc;
     MergeArgs ma{};

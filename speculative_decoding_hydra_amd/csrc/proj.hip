@@ -32,6 +32,7 @@ struct ProjArgs {
   int ldy, kper, m_base;
   float* part;
   TopkPartials tp;
+  int wpacked;  // W in the packed layout (packed_piece) rather than row-major [N][K]
 };
 
 // REM: the K range need not be a multiple of PF * KC (a multiple of KC is
@@ -62,8 +63,20 @@ __global__ __launch_bounds__(64 * WV) void proj_bf16_kernel(ProjArgs a) {
   if (TOPK && a.tp.clear && blockIdx.x == 0 && blockIdx.y == 0 && tid < a.tp.nclear) a.tp.clear[tid] = 0;
 
   static_assert((MP * VPR) % NT == 0, "X chunk splits evenly over the workgroup");
-  const int wrow = min(n_base + (lane & 15), N - 1);
-  const bf16_t* wp = a.W + static_cast<size_t>(wrow) * K + (lane >> 4) * 8;
+  // this lane's 16 bytes of W at column k (a multiple of 32) lie at
+  // wp + (k / 256) * wcs + (k % 256 / 32) * wss: row-major, wp is the row
+  // (rows past N re-read row N - 1) and the strides are 256 and 32 columns;
+  // packed, wp is the lane's piece in the first 256-column chunk of its tile
+  // (tile rows past N are zeros) and the strides are a chunk of all tiles and
+  // one 1 KB step
+  // packed weights reach this kernel with at most 64 rows (from 65 rows on,
+  // contiguous X goes to the tiled kernel), so larger tiles leave it out
+  const bool packed = MT <= 4 && a.wpacked != 0;
+  const bf16_t* wp = packed ? a.W + static_cast<size_t>(n_base / 16) * kPackChunk * 16 + lane * 8
+                            : a.W + static_cast<size_t>(min(n_base + (lane & 15), N - 1)) * K + (lane >> 4) * 8;
+  const size_t wcs = packed ? static_cast<size_t>((N + 15) / 16) * kPackChunk * 16 : kPackChunk;
+  const int wss = packed ? 512 : 32;
+  auto wat = [wp, wcs, wss](int k) { return wp + (static_cast<size_t>(k >> 8) * wcs + ((k & 255) >> 5) * wss); };
 
   f32x4_t acc[MT];
 #pragma unroll
@@ -103,7 +116,7 @@ __global__ __launch_bounds__(64 * WV) void proj_bf16_kernel(ProjArgs a) {
   for (int p = 0; p < PF; ++p) {
     const int kp = REM && k_begin + p * KC > k_end - KC ? k_end - KC : k_begin + p * KC;
 #pragma unroll
-    for (int s = 0; s < STEPS; ++s) wbuf[p][s] = *reinterpret_cast<const u32x4_t*>(wp + kp + s * 32);
+    for (int s = 0; s < STEPS; ++s) wbuf[p][s] = *reinterpret_cast<const u32x4_t*>(wat(kp + s * 32));
   }
 #pragma unroll
   for (int v = 0; v < XV; ++v)
@@ -138,7 +151,7 @@ __global__ __launch_bounds__(64 * WV) void proj_bf16_kernel(ProjArgs a) {
             bq[(s + 1) & 1][t] = *reinterpret_cast<const u32x4_t*>(xrow + t * 16 * LDS_ROW + (s + 1) * 32);
         }
         const bf16x8_t av = __builtin_bit_cast(bf16x8_t, wbuf[p][s]);
-        wbuf[p][s] = *reinterpret_cast<const u32x4_t*>(wp + kn + s * 32);
+        wbuf[p][s] = *reinterpret_cast<const u32x4_t*>(wat(kn + s * 32));
 #pragma unroll
         for (int t = 0; t < MT; ++t)
           acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8_t, bq[s & 1][t]), acc[t],
@@ -320,7 +333,13 @@ int launch_bf16_mt(int mc, const ProjArgs& a, int nsplit, hipStream_t stream) {
 // part[split][m][n] instead of Y. M is processed in chunks of up to 256 rows.
 int launch_projection(int dtype, int M, int K, int N, XSource xs, const void* W, float* Y, RowMap map,
                       int ldy, int nsplit, float* part, TopkPartials tp, hipStream_t stream) {
+  const int wpacked = (dtype & HYDRA_VOCAB_PACKED) != 0;
+  dtype &= ~HYDRA_VOCAB_PACKED;
   if (M <= 0 || N <= 0) return HYDRA_OK;
+  if (wpacked && (dtype != HYDRA_BF16 || K % kPackChunk != 0)) {
+    set_error("projection: packed weights are bf16 with K %% %d == 0 (K=%d)", kPackChunk, K);
+    return HYDRA_ERR_UNSUPPORTED;
+  }
   if (tp.keys && (part || nsplit != 1)) {
     set_error("projection: the fused row reduction needs no split-K");
     return HYDRA_ERR_UNSUPPORTED;
@@ -343,9 +362,13 @@ int launch_projection(int dtype, int M, int K, int N, XSource xs, const void* W,
     return HYDRA_ERR_UNSUPPORTED;
   }
   if (M >= kGemmMinRows && nsplit == 1 && xs.mode == 0 && gemm_supported(K))
-    return launch_projection_gemm(M, K, N, static_cast<const bf16_t*>(xs.x), xs.ldx, static_cast<const bf16_t*>(W), K,
-                                  Y, map, ldy, tp, stream);
-  ProjArgs a{M, K, N, xs, static_cast<const bf16_t*>(W), Y, map, ldy, K / nsplit, 0, part, tp};
+    return launch_projection_gemm(M, K, N, static_cast<const bf16_t*>(xs.x), xs.ldx, static_cast<const bf16_t*>(W),
+                                  wpacked ? -1 : K, Y, map, ldy, tp, stream);
+  if (wpacked && (M > 64 || xs.mode != 0 || nsplit != 1)) {
+    set_error("projection: packed weights take contiguous rows without split K (M=%d)", M);
+    return HYDRA_ERR_UNSUPPORTED;
+  }
+  ProjArgs a{M, K, N, xs, static_cast<const bf16_t*>(W), Y, map, ldy, K / nsplit, 0, part, tp, wpacked};
   for (int m0 = 0; m0 < M; m0 += 256) {
     const int mc = M - m0 < 256 ? M - m0 : 256;
     a.m_base = m0;
@@ -392,7 +415,7 @@ int launch_projection_parts(int dtype, int M, int K, int N, const void* X, const
     return launch_projection(dtype, M, K, N, xs, W, part, RowMap{M, 0, 0}, N, 1, nullptr,
                              TopkPartials{nullptr, nullptr}, stream);
   ProjArgs a{M, K, N, xs, static_cast<const bf16_t*>(W), nullptr, RowMap{M, 0, 0}, N, kper, 0, part,
-             TopkPartials{nullptr, nullptr}};
+             TopkPartials{nullptr, nullptr}, 0};
   for (int m0 = 0; m0 < M; m0 += 256) {
     const int mc = M - m0 < 256 ? M - m0 : 256;
     a.m_base = m0;
@@ -403,6 +426,47 @@ int launch_projection_parts(int dtype, int M, int K, int N, const void* X, const
 }
 
 }  // namespace hydra
+
+namespace hydra {
+namespace {
+
+// one thread per 16-byte piece of the packed layout, in output order: reads
+// row n, columns k .. k + 7 of W (zeros for rows past N)
+__global__ __launch_bounds__(256) void pack_weight_kernel(int N, int K, const bf16_t* __restrict__ W,
+                                                          bf16_t* __restrict__ out, size_t pieces) {
+  const size_t p = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (p >= pieces) return;
+  const size_t ntiles = static_cast<size_t>((N + 15) / 16);
+  const int r = static_cast<int>(p & 15), g = static_cast<int>((p >> 4) & 3), s = static_cast<int>((p >> 6) & 7);
+  const size_t ct = p >> 9;  // chunk * ntiles + tile
+  const int t = static_cast<int>(ct % ntiles), c = static_cast<int>(ct / ntiles);
+  const int n = t * 16 + r, k = c * kPackChunk + s * 32 + g * 8;
+  u32x4_t v{0u, 0u, 0u, 0u};
+  if (n < N) v = *reinterpret_cast<const u32x4_t*>(W + static_cast<size_t>(n) * K + k);
+  *reinterpret_cast<u32x4_t*>(out + p * 8) = v;
+}
+
+}  // namespace
+}  // namespace hydra
+
+extern "C" size_t hydra_packed_weight_size(int N, int K) {
+  if (N <= 0 || K <= 0 || K % hydra::kPackChunk != 0) return 0;
+  return static_cast<size_t>((N + 15) / 16) * 16 * K * 2;
+}
+
+extern "C" int hydra_pack_weight(int N, int K, const void* W, void* packed, void* stream) {
+  using namespace hydra;
+  clear_error();
+  HY_CHECK(N > 0 && K > 0, HYDRA_ERR_INVALID, "pack_weight: bad sizes N=%d K=%d", N, K);
+  HY_CHECK(K % kPackChunk == 0, HYDRA_ERR_UNSUPPORTED, "pack_weight: needs K %% %d == 0 (K=%d)", kPackChunk, K);
+  HY_CHECK(W && packed, HYDRA_ERR_INVALID, "pack_weight: null pointer");
+  HY_CHECK(W != packed, HYDRA_ERR_INVALID, "pack_weight: packed must not alias W");
+  const size_t pieces = hydra_packed_weight_size(N, K) / 16;
+  pack_weight_kernel<<<static_cast<unsigned>((pieces + 255) / 256), 256, 0, static_cast<hipStream_t>(stream)>>>(
+      N, K, static_cast<const bf16_t*>(W), static_cast<bf16_t*>(packed), pieces);
+  HY_LAUNCH_CHECK("pack_weight");
+  return HYDRA_OK;
+}
 
 namespace {
 struct VocabWs {
@@ -425,7 +489,10 @@ extern "C" int hydra_vocab_projection(int dtype, int M, int K, int N, int k, con
                                       float* Y, void* ws, size_t ws_bytes, void* stream) {
   using namespace hydra;
   clear_error();
+  const int vpack = dtype & HYDRA_VOCAB_PACKED;  // packed vocabulary weights (hydra_pack_weight)
+  dtype &= ~HYDRA_VOCAB_PACKED;
   HY_CHECK(dtype == HYDRA_F32 || dtype == HYDRA_BF16, HYDRA_ERR_INVALID, "vocab_projection: bad dtype %d", dtype);
+  HY_CHECK(!vpack || dtype == HYDRA_BF16, HYDRA_ERR_UNSUPPORTED, "vocab_projection: packed vocabulary weights are bf16");
   HY_CHECK(M >= 0 && K > 0 && N > 0, HYDRA_ERR_INVALID, "vocab_projection: bad sizes M=%d K=%d N=%d", M, K, N);
   HY_CHECK(k >= 0 && k <= HYDRA_MAX_TOPK && k <= N, HYDRA_ERR_INVALID, "vocab_projection: k=%d out of [0, %d]", k,
            HYDRA_MAX_TOPK);
@@ -446,7 +513,7 @@ extern "C" int hydra_vocab_projection(int dtype, int M, int K, int N, int k, con
   xs.ldx = K;
   xs.mode = 0;
   RowMap map{M > 0 ? M : 1, 0, 0};
-  return launch_projection(dtype, M, K, N, xs, W, Y, map, N, 1, nullptr, tp, static_cast<hipStream_t>(stream));
+  return launch_projection(dtype | vpack, M, K, N, xs, W, Y, map, N, 1, nullptr, tp, static_cast<hipStream_t>(stream));
 }
 
 extern "C" int hydra_vocab_topk(int M, int N, int k, const float* Y, const void* ws, size_t ws_bytes, float* lse,

@@ -178,7 +178,7 @@ using namespace hydra;
 extern "C" size_t hydra_draft_heads_sketch_workspace_size(int dtype, int B, int d, int V, int hidden_dim, int Dmax,
                                                           const int32_t* row_first) {
   if (B <= 0 || d <= 0 || V <= 0 || hidden_dim <= 0 || Dmax <= 0 || Dmax > HYDRA_MAX_DEPTH || !row_first) return 0;
-  return sketch_ws(dtype, B, d, V, hidden_dim, Dmax, row_first).total;
+  return sketch_ws(dtype & ~HYDRA_VOCAB_PACKED, B, d, V, hidden_dim, Dmax, row_first).total;
 }
 
 extern "C" int hydra_draft_heads_sketch(int dtype, int B, int d, int V, int hidden_dim, const void* h,
@@ -195,7 +195,10 @@ extern "C" int hydra_draft_heads_sketch(int dtype, int B, int d, int V, int hidd
   clear_error();
   hipStream_t stream = static_cast<hipStream_t>(stream_);
   const int hid = hidden_dim;
+  const int vpack = dtype & HYDRA_VOCAB_PACKED;  // packed vocabulary weights (hydra_pack_weight)
+  dtype &= ~HYDRA_VOCAB_PACKED;
   HY_CHECK(dtype == HYDRA_F32 || dtype == HYDRA_BF16, HYDRA_ERR_INVALID, "draft_heads_sketch: bad dtype %d", dtype);
+  HY_CHECK(!vpack || dtype == HYDRA_BF16, HYDRA_ERR_UNSUPPORTED, "draft_heads_sketch: packed vocabulary weights are bf16");
   HY_CHECK(B > 0 && d > 0 && V > 0 && hid > 0, HYDRA_ERR_INVALID,
            "draft_heads_sketch: bad sizes B=%d d=%d V=%d hidden=%d", B, d, V, hid);
   HY_CHECK(d <= kSketchMaxWidth && hid <= kSketchMaxWidth, HYDRA_ERR_UNSUPPORTED,
@@ -290,7 +293,7 @@ extern "C" int hydra_draft_heads_sketch(int dtype, int B, int d, int V, int hidd
     xu.x = U;
     xu.ldx = d;
     xu.mode = 0;
-    rc = launch_projection(dtype, M, d, V, xu, W2[k - 1], head_logits, map, V, 1, nullptr,
+    rc = launch_projection(dtype | vpack, M, d, V, xu, W2[k - 1], head_logits, map, V, 1, nullptr,
                            TopkPartials{tkeys, tms}, stream);
     if (rc != HYDRA_OK) return rc;
     MergeArgs ma{};

@@ -16,6 +16,7 @@ import torch
 from ._lib import lib
 
 HYDRA_F32, HYDRA_BF16 = 0, 1
+HYDRA_VOCAB_PACKED = 0x100  # dtype flag: the call's vocabulary weights are packed (hydra_pack_weight)
 MAX_DEPTH, MAX_TOPK, MAX_TREE, MAX_VERIFY = 8, 16, 1024, 256
 
 
@@ -41,10 +42,61 @@ def _dtype_code(t):
     raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
 
 
+class PackedWeight:
+    """A bfloat16 weight W [N, K] in the packed layout that hydra_pack_weight
+    writes (see include/hydra.h). Accepted wherever a call takes vocabulary
+    projection weights (the heads' W2, W_t, the W of hydra_vocab_projection);
+    the binding then sets HYDRA_VOCAB_PACKED in the call's dtype."""
+
+    dtype = torch.bfloat16
+
+    def __init__(self, data, N, K):
+        self.data, self.N, self.K = data, int(N), int(K)
+
+    @property
+    def shape(self):
+        return torch.Size((self.N, self.K))
+
+    def dim(self):
+        return 2
+
+
+def hydra_packed_weight_size(N, K):
+    return int(lib().hydra_packed_weight_size(int(N), int(K)))
+
+
+def hydra_pack_weight(W, stream=None):
+    """The packed copy of a bfloat16 W [N, K] (K % 256 == 0) as a PackedWeight."""
+    if W.dim() != 2:
+        raise ValueError(f"hydra_pack_weight: W must be 2-D, got {tuple(W.shape)}")
+    N, K = W.shape
+    size = hydra_packed_weight_size(N, K)
+    if size == 0:
+        raise ValueError(f"hydra_pack_weight: needs K % 256 == 0 and positive sizes (N={N}, K={K})")
+    out = torch.empty(size // 2, dtype=torch.bfloat16, device=W.device)
+    _check("hydra_pack_weight", lib().hydra_pack_weight(N, K, _dev(W, "W", torch.bfloat16), out.data_ptr(),
+                                                       _stream(stream)))
+    return PackedWeight(out, N, K)
+
+
+def _vocab_flag(fn, weights):
+    """HYDRA_VOCAB_PACKED when every given vocabulary weight is packed, 0 when
+    none is; a mix is refused."""
+    packed = [isinstance(w, PackedWeight) for w in weights]
+    if any(packed) and not all(packed):
+        raise ValueError(f"{fn}: either every vocabulary weight is packed or none is")
+    return HYDRA_VOCAB_PACKED if packed and all(packed) else 0
+
+
 def _dev(t, name, dtype=None):
-    """Device pointer of a contiguous GPU tensor (None -> NULL)."""
+    """Device pointer of a contiguous GPU tensor or of a packed weight's data
+    (None -> NULL)."""
     if t is None:
         return None
+    if isinstance(t, PackedWeight):
+        if dtype is not None and dtype != torch.bfloat16:
+            raise TypeError(f"{name}: packed weights are bfloat16, the call works in {dtype}")
+        t = t.data
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name}: expected a tensor")
     if not t.is_cuda:
@@ -63,7 +115,7 @@ def _shapes(fn, **want):
     for name, (t, shape) in want.items():
         if t is None:
             continue
-        if not isinstance(t, torch.Tensor):
+        if not isinstance(t, (torch.Tensor, PackedWeight)):
             raise TypeError(f"{fn}: {name}: expected a tensor")
         if tuple(t.shape) != tuple(int(x) for x in shape):
             raise ValueError(f"{fn}: {name} has shape {tuple(t.shape)}, expected {tuple(int(x) for x in shape)}")
@@ -227,6 +279,7 @@ def hydra_draft_heads(h, root_tok, emb, W1, b1, W2, dplan: DevicePlan, head_logi
     w1 = arr(*[_dev(w, "W1", h.dtype) for w in W1])
     bb = arr(*[_dev(w, "b1", h.dtype) for w in b1])
     w2 = arr(*[_dev(w, "W2", h.dtype) for w in W2])
+    dt |= _vocab_flag("draft heads", W2)
     rows = dplan.rows
     rf, rfp = _host_i32(rows.row_first)
     df, dfp = _host_i32(rows.depth_first)
@@ -282,6 +335,8 @@ def hydra_draft_heads_sketch(h, root_tok, emb, heads, dplan: DevicePlan, head_lo
     def col(name, first=True):
         return arr(*[_dev(w[name], name, h.dtype) if (first or k > 0) else None for k, w in enumerate(heads)])
 
+    dt |= _vocab_flag("hydra_draft_heads_sketch", [w["W2"] for w in heads])
+
     rows = dplan.rows
     rf, rfp = _host_i32(rows.row_first)
     df, dfp = _host_i32(rows.depth_first)
@@ -324,6 +379,7 @@ def hydra_draft_heads_attn(h, root_tok, emb, Wqkv, Wo, W1, b1, W2, dplan: Device
     w1 = arr(*[_dev(w, "W1", h.dtype) for w in W1])
     bb = arr(*[_dev(w, "b1", h.dtype) for w in b1])
     w2 = arr(*[_dev(w, "W2", h.dtype) for w in W2])
+    dt |= _vocab_flag("draft heads", W2)
     rows = dplan.rows
     rf, rfp = _host_i32(rows.row_first)
     df, dfp = _host_i32(rows.depth_first)
@@ -362,7 +418,8 @@ def hydra_vocab_projection(X, W, Y, k=0, ws=None, stream=None):
     N = W.shape[0]
     _shapes("hydra_vocab_projection", W=(W, (N, K)), Y=(Y, (M, N)))
     wsp, wsb = _ws(ws)
-    rc = lib().hydra_vocab_projection(_dtype_code(X), M, K, N, int(k), _dev(X, "X"), _dev(W, "W", X.dtype),
+    rc = lib().hydra_vocab_projection(_dtype_code(X) | _vocab_flag("hydra_vocab_projection", [W]), M, K, N, int(k),
+                                      _dev(X, "X"), _dev(W, "W", X.dtype),
                                       _dev(Y, "Y", torch.float32), wsp, wsb, _stream(stream))
     return _check("hydra_vocab_projection", rc)
 
@@ -561,7 +618,8 @@ def tree_accept(o, W_t, tok, parent, target_logits, n_accepted, path, out_tok, w
             n_accepted=(n_accepted, (B,)), path=(path, (B, Dmax + 1)), out_tok=(out_tok, (B, Dmax + 1)))
     wsp, wsb = _ws(ws)
     rc = lib().tree_accept(
-        _dtype_code(o), int(mode), B, N, d, V, Dmax, _dev(o, "o"), _dev(W_t, "W_t", o.dtype), float(temperature),
+        _dtype_code(o) | _vocab_flag("tree_accept", [W_t]), int(mode), B, N, d, V, Dmax, _dev(o, "o"),
+        _dev(W_t, "W_t", o.dtype), float(temperature),
         float(eps or 0.0), float(delta or 0.0), _dev(tok, "tok", torch.int32), _dev(parent, "parent", torch.int32), _dev(q_row, "q_row", torch.int32),
         _dev(head_logits, "head_logits", torch.float32), R, _dev(u_acc, "u_acc", torch.float32),
         _dev(u_res, "u_res", torch.float32), _dev(target_logits, "target_logits", torch.float32),
@@ -587,7 +645,8 @@ def tree_accept_noalloc(o, W_t, tok, parent, target_logits, n_accepted, path, ou
             u_acc=(u_acc, (B, N)), u_res=(u_res, (B, N)), n_accepted=(n_accepted, (B,)), path=(path, (B, Dmax + 1)),
             out_tok=(out_tok, (B, Dmax + 1)))
     rc = lib().tree_accept_noalloc(
-        _dtype_code(o), int(mode), B, N, d, V, Dmax, _dev(o, "o"), _dev(W_t, "W_t", o.dtype), float(temperature),
+        _dtype_code(o) | _vocab_flag("tree_accept", [W_t]), int(mode), B, N, d, V, Dmax, _dev(o, "o"),
+        _dev(W_t, "W_t", o.dtype), float(temperature),
         float(eps or 0.0), float(delta or 0.0), _dev(tok, "tok", torch.int32), _dev(parent, "parent", torch.int32),
         _dev(q_row, "q_row", torch.int32), _dev(head_logits, "head_logits", torch.float32), R,
         _dev(u_acc, "u_acc", torch.float32), _dev(u_res, "u_res", torch.float32),

@@ -42,6 +42,9 @@ class HydraRound:
     draft stage look the embedding half up; None folds for bf16 Hydra heads.
     full_path: Hydra heads read the embeddings of the whole path from the
     root (W1 of head k is [d, (k + 1) d]); never folded.
+    pack_vocab: keep the vocabulary projection weights (the heads' W2 and
+    W_t) in the packed layout (hydra_pack_weight, one copy each made here);
+    None packs them for bf16 with d % 256 == 0.
     rope_theta: rotate the tree Q/K rows at positions prefix_len + depth
     (tree_rope) before attention; None gives the rows to attention as they are.
     With ``target`` in weights (layer-stacked ln1, Wqkv, Wo, ln2, Wgu, Wd, the
@@ -53,7 +56,7 @@ class HydraRound:
 
     def __init__(self, weights, tree, shape, hydra=True, mode=0, temperature=1.0, residual=True,
                  keep_hidden=False, device="cuda", fold_embedding=None, eps=None, delta=None, rope_theta=10000.0,
-                 full_path=False):
+                 full_path=False, pack_vocab=None):
         self.w = weights
         plan, n_keep = make_plan(tree)
         self.dplan = H.DevicePlan(plan, hydra, device)
@@ -119,6 +122,15 @@ class HydraRound:
         if fold_embedding is None:
             fold_embedding = hydra and dt == torch.bfloat16 and not self.sketch and not self.full_path
             fold_embedding = fold_embedding and self.attn is None
+        if pack_vocab is None:
+            pack_vocab = dt == torch.bfloat16 and d % 256 == 0
+        self.pack_vocab = bool(pack_vocab)
+        pk = H.hydra_pack_weight if self.pack_vocab else (lambda W: W)  # noqa: E731
+        self.W_t = pk(weights["W_t"])
+        if self.sketch:
+            self.heads = [dict(hd, W2=pk(hd["W2"])) for hd in weights["heads"]]
+        else:
+            self.W2 = [pk(W) for W in weights["W2"]]
         self.emb_proj = None
         if fold_embedding:
             self.emb_proj = [z(V, d) for _ in weights["W1"]]
@@ -128,16 +140,16 @@ class HydraRound:
     def draft(self, h, root_tok, stream=None):
         if self.attn is not None:
             H.hydra_draft_heads_attn(h, root_tok, self.w["emb"], self.attn["Wqkv"], self.attn["Wo"], self.w["W1"],
-                                     self.w["b1"], self.w["W2"], self.dplan, self.head_logits, self.head_lse,
+                                     self.w["b1"], self.W2, self.dplan, self.head_logits, self.head_lse,
                                      self.cand_tok, self.cand_logp, self.ws_draft, head_hidden=self.head_hidden,
                                      residual=self.residual, stream=stream)
             return
         if self.sketch:
-            H.hydra_draft_heads_sketch(h, root_tok, self.w["emb"], self.w["heads"], self.dplan, self.head_logits,
+            H.hydra_draft_heads_sketch(h, root_tok, self.w["emb"], self.heads, self.dplan, self.head_logits,
                                        self.head_lse, self.cand_tok, self.cand_logp, self.ws_draft,
                                        head_hidden=self.head_hidden, stream=stream)
             return
-        H.hydra_draft_heads(h, root_tok, self.w.get("emb"), self.w["W1"], self.w["b1"], self.w["W2"], self.dplan,
+        H.hydra_draft_heads(h, root_tok, self.w.get("emb"), self.w["W1"], self.w["b1"], self.W2, self.dplan,
                             self.head_logits, self.head_lse, self.cand_tok, self.cand_logp, self.ws_draft,
                             head_hidden=self.head_hidden, residual=self.residual, emb_proj=self.emb_proj,
                             full_path=self.full_path, stream=stream)
@@ -174,7 +186,7 @@ class HydraRound:
         return self.attn_out.view(B, K, -1)
 
     def accept(self, u_acc=None, u_res=None, stream=None):
-        H.tree_accept(self.rows(), self.w["W_t"], self.tok, self.parent, self.target_logits,
+        H.tree_accept(self.rows(), self.W_t, self.tok, self.parent, self.target_logits,
                       self.n_accepted, self.path, self.out_tok, self.ws_accept, mode=self.mode,
                       temperature=self.T, q_row=self.q_row, head_logits=self.head_logits, u_acc=u_acc,
                       u_res=u_res, eps=self.eps, delta=self.delta, stream=stream)
@@ -202,7 +214,7 @@ class HydraRound:
         self.commit(k_tree, v_tree, k_pages, v_pages, block_table, prefix_len, stream)
 
 
-def round_from_inputs(inp, device="cuda", keep_hidden=True, fold_embedding=None, residual=True):
+def round_from_inputs(inp, device="cuda", keep_hidden=True, fold_embedding=None, residual=True, pack_vocab=None):
     """HydraRound plus device copies of a dict of named input tensors.
 
     Keys: workload (sizes, tree, dtype, mode), root_tok, h, E, W1, b1, W2 (or
@@ -227,7 +239,8 @@ def round_from_inputs(inp, device="cuda", keep_hidden=True, fold_embedding=None,
                  max_prefix_len=int(inp["prefix_len"].max()))
     mode = {"greedy": 0, "stochastic": 1, "typical": 2}[w.mode]
     rnd = HydraRound(weights, w.tree, shape, hydra=w.hydra, mode=mode, temperature=w.T, residual=residual, keep_hidden=keep_hidden, device=device,
-                     fold_embedding=fold_embedding, eps=w.eps, delta=w.delta, full_path=w.cond == "path")
+                     fold_embedding=fold_embedding, eps=w.eps, delta=w.delta, full_path=w.cond == "path",
+                     pack_vocab=pack_vocab)
     dev = dict(h=to(inp["h"]), root_tok=to(inp["root_tok"]), k_pages=to(inp["k_pages"]), v_pages=to(inp["v_pages"]),
                block_table=to(inp["block_table"]), prefix_len=to(inp["prefix_len"]))
     if not w.layers:  # the target's layers make their own Q/K/V

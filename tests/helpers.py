@@ -57,11 +57,11 @@ def oracle_plan(tree):
     return O.plan_cartesian(tree[1]), tree[2]
 
 
-def round_inputs(inp, device="cuda", keep_hidden=True, fold_embedding=None, residual=True):
+def round_inputs(inp, device="cuda", keep_hidden=True, fold_embedding=None, residual=True, pack_vocab=None):
     from speculative_decoding_hydra_amd import round_from_inputs
 
     return round_from_inputs(inp, device=device, keep_hidden=keep_hidden, fold_embedding=fold_embedding,
-                             residual=residual)
+                             residual=residual, pack_vocab=pack_vocab)
 
 
 def run_round(rnd, dev, stream=None):

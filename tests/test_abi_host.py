@@ -368,3 +368,26 @@ def test_bindings_refuse_every_mismatched_shape():
 
     proj = dict(X=f(5, d), W=f(V, d), Y=f(5, V))
     _refuses(S.hydra_vocab_projection, proj, {"W": f(V, d + 1), "Y": f(5, V + 1)})
+
+
+def test_packed_weight_size_and_the_mixing_rule(lib):
+    """The packed copy of W [N, K] holds ceil(N / 16) tiles of 16 rows (K a
+    multiple of 256, else 0); a call's vocabulary weights are all packed or
+    all row-major."""
+    import torch
+
+    from speculative_decoding_hydra_amd import PackedWeight, hydra_packed_weight_size
+    from speculative_decoding_hydra_amd.hydra import HYDRA_VOCAB_PACKED, _vocab_flag
+
+    assert hydra_packed_weight_size(32000, 4096) == 32000 * 4096 * 2
+    assert hydra_packed_weight_size(1000, 256) == 1008 * 256 * 2
+    assert hydra_packed_weight_size(17, 512) == 32 * 512 * 2
+    for N, K in ((100, 300), (0, 256), (16, 0), (-1, 256)):
+        assert hydra_packed_weight_size(N, K) == 0
+    pw = PackedWeight(torch.zeros(8), 16, 256)
+    assert tuple(pw.shape) == (16, 256) and pw.dim() == 2
+    row = torch.zeros(16, 256, dtype=torch.bfloat16)
+    assert _vocab_flag("t", [pw, pw]) == HYDRA_VOCAB_PACKED
+    assert _vocab_flag("t", [row, row]) == 0
+    with pytest.raises(ValueError):
+        _vocab_flag("t", [pw, row])

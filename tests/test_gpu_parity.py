@@ -55,6 +55,50 @@ def test_projection_bf16(M, K, N):
     assert err <= 1e-3, err  # bf16 inputs are exact in fp32; only the summation order differs
 
 
+@pytest.mark.parametrize("M,K,N,k", [(1, 256, 1000, 10), (13, 4096, 32000, 10), (64, 4096, 32000, 1),
+                                     (17, 512, 1000, 0), (33, 256, 777, 3), (100, 512, 1000, 5),
+                                     (300, 256, 130, 0), (1024, 1024, 3000, 1), (5, 256, 70, 4)])
+def test_projection_packed_weights_match_row_major(M, K, N, k):
+    """The packed weight layout is a layout of the same values and the
+    kernels keep their K order, so the logits (streaming kernel up to 64
+    rows, tiled kernel from 65) and the fused top-k partials are bit-identical
+    to those of the row-major weights; the packed copy itself holds every
+    value of W at the offset the layout defines, and zeros past row N."""
+    from speculative_decoding_hydra_amd import (hydra_pack_weight, hydra_vocab_projection,
+                                                hydra_vocab_projection_workspace_size, hydra_vocab_topk)
+
+    print(f"packed weights M={M} K={K} N={N} k={k}", flush=True)
+    g = torch.Generator().manual_seed(M + 3 * K + N + k)
+    X = _bf16(torch.randn(M, K, generator=g)).cuda()
+    W = _bf16(torch.randn(N, K, generator=g) * 0.05).cuda()
+    Wp = hydra_pack_weight(W)
+    torch.cuda.synchronize()
+    # the layout, spelled out: tile t, chunk c, step s, group g, row r
+    T = (N + 15) // 16
+    ref_pack = torch.zeros(T * 16, K, dtype=torch.bfloat16)
+    ref_pack[:N] = W.cpu()
+    ref_pack = ref_pack.view(T, 16, K // 256, 8, 4, 8).permute(2, 0, 3, 4, 1, 5).reshape(-1)
+    assert torch.equal(Wp.data.cpu(), ref_pack)
+    outs = []
+    for Wm in (W, Wp):
+        Y = torch.empty(M, N, device="cuda")
+        ws = torch.empty(max(1, hydra_vocab_projection_workspace_size(M, N, k)), dtype=torch.uint8, device="cuda")
+        hydra_vocab_projection(X, Wm, Y, k, ws if k else None)
+        res = [Y]
+        if k:
+            lse = torch.empty(M, device="cuda")
+            ids = torch.empty(M, k, dtype=torch.int32, device="cuda")
+            vals = torch.empty(M, k, device="cuda")
+            hydra_vocab_topk(M, N, k, Y, ws, lse, ids, vals)
+            res += [lse, ids, vals]
+        torch.cuda.synchronize()
+        outs.append([t.cpu() for t in res])
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
+    ref = HI.as_f64(X) @ HI.as_f64(W).T
+    assert float(np.max(np.abs(outs[1][0].double().numpy() - ref))) <= 1e-3
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
 @pytest.mark.parametrize("M,K,N,k", [(1, 256, 1000, 10), (13, 4096, 32000, 10), (64, 512, 32000, 1),
                                      (20, 256, 100, 16), (300, 256, 1000, 3), (5, 256, 70, 4)])
@@ -227,13 +271,13 @@ def test_tree_attention(dtype, B, N, Hq, Hkv, D, lens):
 _cache = {}
 
 
-def _round(name, **over):
-    key = (name, tuple(sorted(over.items())))
+def _round(name, pack_vocab=None, **over):
+    key = (name, pack_vocab, tuple(sorted(over.items())))
     if key not in _cache:
         w = HI.workload(name, **over)
-        print(f"round {name} {over}: generating", flush=True)
+        print(f"round {name} {over} pack_vocab={pack_vocab}: generating", flush=True)
         inp = HI.generate(w)
-        rnd, dev = T.round_inputs(inp)
+        rnd, dev = T.round_inputs(inp, pack_vocab=pack_vocab)
         print(f"round {name}: running on the device", flush=True)
         T.run_round(rnd, dev)
         torch.cuda.synchronize()
@@ -349,8 +393,12 @@ def test_greedy_planted_paths(B, dtype):
             assert [int(x) for x in out_t[b] if x >= 0] == toks
 
 
-def test_7b_sparse64_round():
-    inp, rnd, dev = _round("7b_sparse64")
+@pytest.mark.parametrize("pack_vocab", [None, False])
+def test_7b_sparse64_round(pack_vocab):
+    """The headline round; by default its bf16 vocabulary weights are packed,
+    and once more with them row-major."""
+    inp, rnd, dev = _round("7b_sparse64", pack_vocab=pack_vocab)
+    assert rnd.pack_vocab == (pack_vocab is None)
     rep = T.oracle_round_checks(inp, rnd)
     rep.update(T.check_commit(inp, rnd, dev))
     print(rep, flush=True)

@@ -286,6 +286,10 @@ def layer_measure(w, rnd, dev, stream, reps=10, use_graph=True):
     ones = torch.ones(d, device="cuda", dtype=dt)
     sets = [dict(ln1=ones, Wqkv=n((Hq + 2 * Hkv) * D, d), Wo=n(d, Hq * D), ln2=ones, Wgu=n(2 * F, d), Wd=n(d, F))
             for _ in range(2)]
+    if rnd.pack_vocab:  # the layout the rounds keep their weights in
+        from speculative_decoding_hydra_amd import hydra_pack_weight
+
+        sets = [dict(s, **{k: hydra_pack_weight(s[k]) for k in ("Wqkv", "Wo", "Wgu", "Wd")}) for s in sets]
     x = torch.randn(B, K, d, device="cuda", generator=g).to(dt)
     out = torch.empty_like(x)
     kt = torch.empty(B, K, Hkv, D, device="cuda", dtype=dt)
@@ -322,7 +326,8 @@ def layer_measure(w, rnd, dev, stream, reps=10, use_graph=True):
     prefix = int(dev["prefix_len"].sum()) * Hkv * D * esz * 2
     acts = B * K * (2 * d + 2 * Hkv * D) * esz
     nbytes = weights + prefix + acts
-    return {"d": d, "ffn": F, "rows": B * K, "bytes": nbytes, "weight_bytes": weights, "avg_launch_us": us,
+    return {"d": d, "ffn": F, "rows": B * K, "weight_layout": "packed" if rnd.pack_vocab else "row-major",
+            "bytes": nbytes, "weight_bytes": weights, "avg_launch_us": us,
             "achieved_GBps": nbytes / (us * 1e-6) / 1e9, "frac_of_hbm_peak": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS}
 
 

@@ -43,6 +43,9 @@
  *     vocabulary projection weights of the call (the heads' W2, W_t, the W
  *     of hydra_vocab_projection) are in the packed layout of
  *     hydra_pack_weight; every other tensor keeps its row-major layout.
+ *     HYDRA_LAYER_PACKED (tree_decoder_layer, tree_verify_layers) says the
+ *     same of the decoder layers' Wqkv, Wo, Wgu and Wd (each layer's matrix
+ *     packed on its own; the norm gains stay plain).
  *   - Entry points are stateless and reentrant; calls that share a workspace
  *     must be ordered on one stream.
  */
@@ -65,6 +68,7 @@ extern "C" {
 #define HYDRA_F32 0
 #define HYDRA_BF16 1
 #define HYDRA_VOCAB_PACKED 0x100 /* dtype flag: vocabulary weights packed */
+#define HYDRA_LAYER_PACKED 0x200 /* dtype flag: decoder layer weights packed */
 
 #define HYDRA_MAX_DEPTH 8     /* deepest tree (number of draft heads used) */
 #define HYDRA_MAX_TOPK 16     /* widest fan-out of one node */

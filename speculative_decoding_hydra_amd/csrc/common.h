@@ -300,7 +300,7 @@ constexpr int kGemmMinRows = 65;  // from here on the tiled kernel beats the str
 // Split K for products with few output tiles: workgroups (blockIdx.y = s)
 // take K range [s kper, min((s + 1) kper, K)) and write part + s * M * N
 // (row-major [M][N]); kper % 64 == 0. The caller sums the nsplit partials.
-int launch_projection_gemm_split(int M, int K, int N, const bf16_t* X, const bf16_t* W, float* part, int nsplit,
+int launch_projection_gemm_split(int M, int K, int N, const bf16_t* X, const bf16_t* W, int ldw, float* part, int nsplit,
                                  int kper, hipStream_t stream);
 int gemm_workgroups(int M, int N);
 // Y or its split-K partials for the decoder layer's products: picks the

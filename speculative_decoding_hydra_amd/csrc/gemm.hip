@@ -256,14 +256,14 @@ int launch_projection_gemm(int M, int K, int N, const bf16_t* X, int ldx, const 
   return HYDRA_OK;
 }
 
-int launch_projection_gemm_split(int M, int K, int N, const bf16_t* X, const bf16_t* W, float* part, int nsplit,
+int launch_projection_gemm_split(int M, int K, int N, const bf16_t* X, const bf16_t* W, int ldw, float* part, int nsplit,
                                  int kper, hipStream_t stream) {
   GemmArgs a{};
   a.M = M;
   a.K = K;
   a.N = N;
   a.ldx = K;
-  a.ldw = K;
+  a.ldw = ldw;  // < 0: packed
   a.ldy = N;
   a.mtiles = (M + GBM - 1) / GBM;
   const int bn = a.mtiles == 1 ? 128 : 256;

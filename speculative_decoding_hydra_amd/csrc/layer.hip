@@ -268,8 +268,9 @@ LayerWs layer_ws(int dtype, int B, int N, int d, int Hq, int Hkv, int D, int F, 
   return w;
 }
 
+// wflag: HYDRA_LAYER_PACKED when Wqkv, Wo, Wgu and Wd are packed
 template <typename T>
-int run_layer(int dtype, int B, int N, int d, int Hq, int Hkv, int D, int F, const T* x, const T* ln1,
+int run_layer(int dtype, int wflag, int B, int N, int d, int Hq, int Hkv, int D, int F, const T* x, const T* ln1,
               const T* Wqkv, const T* Wo, const T* ln2, const T* Wgu, const T* Wd, float eps, float theta,
               const void* k_pages, const void* v_pages, int n_pages, int page_size, const int32_t* block_table,
               int max_pages, const int32_t* prefix_len, int max_prefix_len, const int32_t* anc,
@@ -287,7 +288,7 @@ int run_layer(int dtype, int B, int N, int d, int Hq, int Hkv, int D, int F, con
   const int M = B * N;
   int ns = 1;  // split-K partials of the last product
   auto proj = [&](int K, int Nout, const T* X, const T* W) {
-    return launch_projection_parts(dtype, M, K, Nout, X, W, acc, w.acc / 4, &ns, stream);
+    return launch_projection_parts(dtype | wflag, M, K, Nout, X, W, acc, w.acc / 4, &ns, stream);
   };
   auto blocks = [](long long n) { return static_cast<unsigned>((n + 255) / 256); };
   // a = rms(x) g1
@@ -361,7 +362,7 @@ VerifyWs verify_ws(int dtype, int B, int N, int d, int Hq, int Hkv, int D, int F
 // embeddings -> n_layers decoder layers (layer-stacked weights, pools and
 // tree K/V) -> final norm; the hidden states ping-pong between two buffers
 template <typename T>
-int run_verify(int dtype, int n_layers, int B, int N, int d, int Hq, int Hkv, int D, int F, int V,
+int run_verify(int dtype, int wflag, int n_layers, int B, int N, int d, int Hq, int Hkv, int D, int F, int V,
                const int32_t* tok, const T* emb, const T* ln1, const T* Wqkv, const T* Wo, const T* ln2,
                const T* Wgu, const T* Wd, const T* ln_f, float eps, float theta, const T* k_pages,
                const T* v_pages, int n_pages, int page_size, const int32_t* block_table, int max_pages,
@@ -379,7 +380,7 @@ int run_verify(int dtype, int n_layers, int B, int N, int d, int Hq, int Hkv, in
   const size_t sgu = 2 * static_cast<size_t>(F) * d, sd = static_cast<size_t>(d) * F;
   const size_t skv = M * Hkv * D, spool = static_cast<size_t>(n_pages) * Hkv * page_size * D;
   for (int l = 0; l < n_layers; ++l) {
-    const int rc = run_layer<T>(dtype, B, N, d, Hq, Hkv, D, F, cur, ln1 + l * static_cast<size_t>(d),
+    const int rc = run_layer<T>(dtype, wflag, B, N, d, Hq, Hkv, D, F, cur, ln1 + l * static_cast<size_t>(d),
                                 Wqkv + l * sqkv, Wo + l * so, ln2 + l * static_cast<size_t>(d), Wgu + l * sgu,
                                 Wd + l * sd, eps, theta, k_pages + l * spool, v_pages + l * spool, n_pages,
                                 page_size, block_table, max_pages, prefix_len, max_prefix_len, anc, depth, Dmax, nxt,
@@ -400,7 +401,7 @@ int run_verify(int dtype, int n_layers, int B, int N, int d, int Hq, int Hkv, in
 extern "C" size_t tree_decoder_layer_workspace_size(int dtype, int B, int N, int d, int Hq, int Hkv, int D, int F,
                                                     int max_prefix_len) {
   if (B <= 0 || N <= 0 || d <= 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || F <= 0) return 0;
-  return hydra::layer_ws(dtype, B, N, d, Hq, Hkv, D, F, max_prefix_len).total;
+  return hydra::layer_ws(dtype & ~HYDRA_LAYER_PACKED, B, N, d, Hq, Hkv, D, F, max_prefix_len).total;
 }
 
 extern "C" int tree_decoder_layer(int dtype, int B, int N, int d, int Hq, int Hkv, int D, int F, const void* x,
@@ -413,7 +414,10 @@ extern "C" int tree_decoder_layer(int dtype, int B, int N, int d, int Hq, int Hk
   using namespace hydra;
   clear_error();
   hipStream_t stream = static_cast<hipStream_t>(stream_);
+  const int wflag = dtype & HYDRA_LAYER_PACKED;  // packed layer weights (hydra_pack_weight)
+  dtype &= ~HYDRA_LAYER_PACKED;
   HY_CHECK(dtype == HYDRA_F32 || dtype == HYDRA_BF16, HYDRA_ERR_INVALID, "decoder_layer: bad dtype %d", dtype);
+  HY_CHECK(!wflag || dtype == HYDRA_BF16, HYDRA_ERR_UNSUPPORTED, "decoder_layer: packed weights are bf16");
   HY_CHECK(B >= 0 && N >= 1 && d >= 1 && Hq >= 1 && Hkv >= 1 && D >= 2 && D % 2 == 0 && F >= 1 && Hq % Hkv == 0,
            HYDRA_ERR_INVALID, "decoder_layer: bad sizes B=%d N=%d d=%d Hq=%d Hkv=%d D=%d F=%d", B, N, d, Hq, Hkv, D,
            F);
@@ -428,14 +432,14 @@ extern "C" int tree_decoder_layer(int dtype, int B, int N, int d, int Hq, int Hk
   const size_t need = tree_decoder_layer_workspace_size(dtype, B, N, d, Hq, Hkv, D, F, max_prefix_len);
   HY_CHECK(ws && ws_bytes >= need, HYDRA_ERR_WORKSPACE, "decoder_layer: workspace %zu < %zu", ws_bytes, need);
   if (dtype == HYDRA_F32)
-    return run_layer<float>(dtype, B, N, d, Hq, Hkv, D, F, static_cast<const float*>(x),
+    return run_layer<float>(dtype, wflag, B, N, d, Hq, Hkv, D, F, static_cast<const float*>(x),
                             static_cast<const float*>(ln1), static_cast<const float*>(Wqkv),
                             static_cast<const float*>(Wo), static_cast<const float*>(ln2),
                             static_cast<const float*>(Wgu), static_cast<const float*>(Wd), eps, theta, k_pages,
                             v_pages, n_pages, page_size, block_table, max_pages, prefix_len, max_prefix_len, anc,
                             depth, Dmax, static_cast<float*>(x_out), static_cast<float*>(k_tree),
                             static_cast<float*>(v_tree), ws, ws_bytes, stream);
-  return run_layer<bf16_t>(dtype, B, N, d, Hq, Hkv, D, F, static_cast<const bf16_t*>(x),
+  return run_layer<bf16_t>(dtype, wflag, B, N, d, Hq, Hkv, D, F, static_cast<const bf16_t*>(x),
                            static_cast<const bf16_t*>(ln1), static_cast<const bf16_t*>(Wqkv),
                            static_cast<const bf16_t*>(Wo), static_cast<const bf16_t*>(ln2),
                            static_cast<const bf16_t*>(Wgu), static_cast<const bf16_t*>(Wd), eps, theta, k_pages,
@@ -447,7 +451,7 @@ extern "C" int tree_decoder_layer(int dtype, int B, int N, int d, int Hq, int Hk
 extern "C" size_t tree_verify_layers_workspace_size(int dtype, int B, int N, int d, int Hq, int Hkv, int D, int F,
                                                     int max_prefix_len) {
   if (B <= 0 || N <= 0 || d <= 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || F <= 0) return 0;
-  return hydra::verify_ws(dtype, B, N, d, Hq, Hkv, D, F, max_prefix_len).total;
+  return hydra::verify_ws(dtype & ~HYDRA_LAYER_PACKED, B, N, d, Hq, Hkv, D, F, max_prefix_len).total;
 }
 
 extern "C" int tree_verify_layers(int dtype, int n_layers, int B, int N, int d, int Hq, int Hkv, int D, int F, int V,
@@ -461,7 +465,10 @@ extern "C" int tree_verify_layers(int dtype, int n_layers, int B, int N, int d, 
   using namespace hydra;
   clear_error();
   hipStream_t stream = static_cast<hipStream_t>(stream_);
+  const int wflag = dtype & HYDRA_LAYER_PACKED;  // packed layer weights (hydra_pack_weight, layer by layer)
+  dtype &= ~HYDRA_LAYER_PACKED;
   HY_CHECK(dtype == HYDRA_F32 || dtype == HYDRA_BF16, HYDRA_ERR_INVALID, "verify_layers: bad dtype %d", dtype);
+  HY_CHECK(!wflag || dtype == HYDRA_BF16, HYDRA_ERR_UNSUPPORTED, "verify_layers: packed weights are bf16");
   HY_CHECK(n_layers >= 1 && B >= 0 && N >= 1 && d >= 1 && Hq >= 1 && Hkv >= 1 && D >= 2 && D % 2 == 0 && F >= 1 &&
                Hq % Hkv == 0 && V >= 1,
            HYDRA_ERR_INVALID, "verify_layers: bad sizes layers=%d B=%d N=%d d=%d Hq=%d Hkv=%d D=%d F=%d V=%d",
@@ -477,7 +484,7 @@ extern "C" int tree_verify_layers(int dtype, int n_layers, int B, int N, int d, 
   HY_CHECK(ws && ws_bytes >= need, HYDRA_ERR_WORKSPACE, "verify_layers: workspace %zu < %zu", ws_bytes, need);
   if (dtype == HYDRA_F32)
     return run_verify<float>(
-        dtype, n_layers, B, N, d, Hq, Hkv, D, F, V, tok, static_cast<const float*>(emb),
+        dtype, wflag, n_layers, B, N, d, Hq, Hkv, D, F, V, tok, static_cast<const float*>(emb),
         static_cast<const float*>(ln1), static_cast<const float*>(Wqkv), static_cast<const float*>(Wo),
         static_cast<const float*>(ln2), static_cast<const float*>(Wgu), static_cast<const float*>(Wd),
         static_cast<const float*>(ln_f), eps, theta, static_cast<const float*>(k_pages),
@@ -485,7 +492,7 @@ extern "C" int tree_verify_layers(int dtype, int n_layers, int B, int N, int d, 
         anc, depth, Dmax, static_cast<float*>(h_out), static_cast<float*>(k_tree), static_cast<float*>(v_tree), ws,
         ws_bytes, stream);
   return run_verify<bf16_t>(
-      dtype, n_layers, B, N, d, Hq, Hkv, D, F, V, tok, static_cast<const bf16_t*>(emb),
+      dtype, wflag, n_layers, B, N, d, Hq, Hkv, D, F, V, tok, static_cast<const bf16_t*>(emb),
       static_cast<const bf16_t*>(ln1), static_cast<const bf16_t*>(Wqkv), static_cast<const bf16_t*>(Wo),
       static_cast<const bf16_t*>(ln2), static_cast<const bf16_t*>(Wgu), static_cast<const bf16_t*>(Wd),
       static_cast<const bf16_t*>(ln_f), eps, theta, static_cast<const bf16_t*>(k_pages),

@@ -382,6 +382,12 @@ int launch_projection(int dtype, int M, int K, int N, XSource xs, const void* W,
 int launch_projection_parts(int dtype, int M, int K, int N, const void* X, const void* W, float* part,
                             size_t part_floats, int* nsplit, hipStream_t stream) {
   *nsplit = 1;
+  const int wpacked = (dtype & HYDRA_LAYER_PACKED) != 0;  // W in the packed layout
+  dtype &= ~HYDRA_LAYER_PACKED;
+  if (wpacked && (dtype != HYDRA_BF16 || K % kPackChunk != 0)) {
+    set_error("projection: packed weights are bf16 with K %% %d == 0 (K=%d)", kPackChunk, K);
+    return HYDRA_ERR_UNSUPPORTED;
+  }
   XSource xs{};
   xs.x = X;
   xs.ldx = K;
@@ -399,7 +405,8 @@ int launch_projection_parts(int dtype, int M, int K, int N, const void* X, const
     const int kper = (K / 64 + ns - 1) / ns * 64;
     ns = (K + kper - 1) / kper;
     *nsplit = ns;
-    return launch_projection_gemm_split(M, K, N, static_cast<const bf16_t*>(X), static_cast<const bf16_t*>(W), part,
+    return launch_projection_gemm_split(M, K, N, static_cast<const bf16_t*>(X), static_cast<const bf16_t*>(W),
+                                        wpacked ? -1 : K, part,
                                         ns, kper, stream);
   }
   // streaming kernel: 64 output columns per workgroup and split; about one
@@ -412,10 +419,10 @@ int launch_projection_parts(int dtype, int M, int K, int N, const void* X, const
   ns = (K + kper - 1) / kper;
   *nsplit = ns;
   if (ns == 1)
-    return launch_projection(dtype, M, K, N, xs, W, part, RowMap{M, 0, 0}, N, 1, nullptr,
-                             TopkPartials{nullptr, nullptr}, stream);
+    return launch_projection(dtype | (wpacked ? HYDRA_VOCAB_PACKED : 0), M, K, N, xs, W, part, RowMap{M, 0, 0}, N,
+                             1, nullptr, TopkPartials{nullptr, nullptr}, stream);
   ProjArgs a{M, K, N, xs, static_cast<const bf16_t*>(W), nullptr, RowMap{M, 0, 0}, N, kper, 0, part,
-             TopkPartials{nullptr, nullptr}, 0};
+             TopkPartials{nullptr, nullptr}, wpacked};
   for (int m0 = 0; m0 < M; m0 += 256) {
     const int mc = M - m0 < 256 ? M - m0 : 256;
     a.m_base = m0;

@@ -17,6 +17,7 @@ from ._lib import lib
 
 HYDRA_F32, HYDRA_BF16 = 0, 1
 HYDRA_VOCAB_PACKED = 0x100  # dtype flag: the call's vocabulary weights are packed (hydra_pack_weight)
+HYDRA_LAYER_PACKED = 0x200  # dtype flag: the decoder layers' weights are packed
 MAX_DEPTH, MAX_TOPK, MAX_TREE, MAX_VERIFY = 8, 16, 1024, 256
 
 
@@ -43,22 +44,27 @@ def _dtype_code(t):
 
 
 class PackedWeight:
-    """A bfloat16 weight W [N, K] in the packed layout that hydra_pack_weight
-    writes (see include/hydra.h). Accepted wherever a call takes vocabulary
-    projection weights (the heads' W2, W_t, the W of hydra_vocab_projection);
-    the binding then sets HYDRA_VOCAB_PACKED in the call's dtype."""
+    """A bfloat16 weight W [N, K] (or a layer stack [n, N, K], each layer
+    packed on its own) in the packed layout that hydra_pack_weight writes
+    (see include/hydra.h). Accepted wherever a call takes vocabulary
+    projection weights (the heads' W2, W_t, the W of hydra_vocab_projection)
+    or decoder layer weights (Wqkv, Wo, Wgu, Wd); the binding then sets
+    HYDRA_VOCAB_PACKED or HYDRA_LAYER_PACKED in the call's dtype."""
 
     dtype = torch.bfloat16
 
-    def __init__(self, data, N, K):
+    def __init__(self, data, N, K, layers=None):
         self.data, self.N, self.K = data, int(N), int(K)
+        self.layers = None if layers is None else int(layers)
 
     @property
     def shape(self):
-        return torch.Size((self.N, self.K))
+        if self.layers is None:
+            return torch.Size((self.N, self.K))
+        return torch.Size((self.layers, self.N, self.K))
 
     def dim(self):
-        return 2
+        return 2 if self.layers is None else 3
 
 
 def hydra_packed_weight_size(N, K):
@@ -66,26 +72,33 @@ def hydra_packed_weight_size(N, K):
 
 
 def hydra_pack_weight(W, stream=None):
-    """The packed copy of a bfloat16 W [N, K] (K % 256 == 0) as a PackedWeight."""
-    if W.dim() != 2:
-        raise ValueError(f"hydra_pack_weight: W must be 2-D, got {tuple(W.shape)}")
-    N, K = W.shape
+    """The packed copy of a bfloat16 W [N, K] (K % 256 == 0) as a
+    PackedWeight; a layer stack [n, N, K] (N % 16 == 0, so that each layer's
+    packed matrix keeps the row-major stride) is packed layer by layer."""
+    if W.dim() not in (2, 3):
+        raise ValueError(f"hydra_pack_weight: W must be [N, K] or [layers, N, K], got {tuple(W.shape)}")
+    N, K = W.shape[-2:]
     size = hydra_packed_weight_size(N, K)
     if size == 0:
         raise ValueError(f"hydra_pack_weight: needs K % 256 == 0 and positive sizes (N={N}, K={K})")
-    out = torch.empty(size // 2, dtype=torch.bfloat16, device=W.device)
-    _check("hydra_pack_weight", lib().hydra_pack_weight(N, K, _dev(W, "W", torch.bfloat16), out.data_ptr(),
-                                                       _stream(stream)))
-    return PackedWeight(out, N, K)
+    if W.dim() == 3 and N % 16 != 0:
+        raise ValueError(f"hydra_pack_weight: a layer stack needs N % 16 == 0 (N={N})")
+    n = W.shape[0] if W.dim() == 3 else 1
+    out = torch.empty(n * size // 2, dtype=torch.bfloat16, device=W.device)
+    Wc = W.reshape(n, N, K)
+    for layer in range(n):
+        _check("hydra_pack_weight", lib().hydra_pack_weight(N, K, _dev(Wc[layer], "W", torch.bfloat16),
+                                                           out.data_ptr() + layer * size, _stream(stream)))
+    return PackedWeight(out, N, K, layers=n if W.dim() == 3 else None)
 
 
-def _vocab_flag(fn, weights):
-    """HYDRA_VOCAB_PACKED when every given vocabulary weight is packed, 0 when
-    none is; a mix is refused."""
+def _vocab_flag(fn, weights, flag=HYDRA_VOCAB_PACKED):
+    """flag when every given weight is packed, 0 when none is; a mix is
+    refused."""
     packed = [isinstance(w, PackedWeight) for w in weights]
     if any(packed) and not all(packed):
-        raise ValueError(f"{fn}: either every vocabulary weight is packed or none is")
-    return HYDRA_VOCAB_PACKED if packed and all(packed) else 0
+        raise ValueError(f"{fn}: either every vocabulary or layer weight is packed or none is")
+    return flag if packed and all(packed) else 0
 
 
 def _dev(t, name, dtype=None):
@@ -547,7 +560,8 @@ def tree_decoder_layer(x, w, Hq, Hkv, k_pages, v_pages, block_table, prefix_len,
     dt = x.dtype
     wsp, wsb = _ws(ws)
     rc = lib().tree_decoder_layer(
-        _dtype_code(x), B, N, d, Hq, Hkv, D, F, _dev(x, "x"), _dev(w["ln1"], "ln1", dt), _dev(w["Wqkv"], "Wqkv", dt),
+        _dtype_code(x) | _vocab_flag("tree_decoder_layer", [w[n] for n in ("Wqkv", "Wo", "Wgu", "Wd")],
+                                     HYDRA_LAYER_PACKED), B, N, d, Hq, Hkv, D, F, _dev(x, "x"), _dev(w["ln1"], "ln1", dt), _dev(w["Wqkv"], "Wqkv", dt),
         _dev(w["Wo"], "Wo", dt), _dev(w["ln2"], "ln2", dt), _dev(w["Wgu"], "Wgu", dt), _dev(w["Wd"], "Wd", dt),
         float(eps), float(theta), _dev(k_pages, "k_pages", dt), _dev(v_pages, "v_pages", dt), n_pages, page_size,
         _dev(block_table, "block_table", torch.int32), block_table.shape[1],
@@ -584,7 +598,8 @@ def tree_verify_layers(tok, emb, w, ln_f, Hq, Hkv, k_pages, v_pages, block_table
             block_table=(block_table, (B, block_table.shape[1])))
     wsp, wsb = _ws(ws)
     rc = lib().tree_verify_layers(
-        _dtype_code(emb), n, B, N, d, Hq, Hkv, D, F, V, _dev(tok, "tok", torch.int32), _dev(emb, "emb"),
+        _dtype_code(emb) | _vocab_flag("tree_verify_layers", [w[n] for n in ("Wqkv", "Wo", "Wgu", "Wd")],
+                                       HYDRA_LAYER_PACKED), n, B, N, d, Hq, Hkv, D, F, V, _dev(tok, "tok", torch.int32), _dev(emb, "emb"),
         _dev(w["ln1"], "ln1", dt), _dev(w["Wqkv"], "Wqkv", dt), _dev(w["Wo"], "Wo", dt), _dev(w["ln2"], "ln2", dt),
         _dev(w["Wgu"], "Wgu", dt), _dev(w["Wd"], "Wd", dt), _dev(ln_f, "ln_f", dt), float(eps), float(theta),
         _dev(k_pages, "k_pages", dt), _dev(v_pages, "v_pages", dt), n_pages, page_size,

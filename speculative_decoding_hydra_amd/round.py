@@ -43,8 +43,9 @@ class HydraRound:
     full_path: Hydra heads read the embeddings of the whole path from the
     root (W1 of head k is [d, (k + 1) d]); never folded.
     pack_vocab: keep the vocabulary projection weights (the heads' W2 and
-    W_t) in the packed layout (hydra_pack_weight, one copy each made here);
-    None packs them for bf16 with d % 256 == 0.
+    W_t) and the target layers' weights in the packed layout
+    (hydra_pack_weight, one copy each made here); None packs them for bf16
+    with d % 256 == 0.
     rope_theta: rotate the tree Q/K rows at positions prefix_len + depth
     (tree_rope) before attention; None gives the rows to attention as they are.
     With ``target`` in weights (layer-stacked ln1, Wqkv, Wo, ln2, Wgu, Wd, the
@@ -127,6 +128,10 @@ class HydraRound:
         self.pack_vocab = bool(pack_vocab)
         pk = H.hydra_pack_weight if self.pack_vocab else (lambda W: W)  # noqa: E731
         self.W_t = pk(weights["W_t"])
+        if self.target is not None and self.pack_vocab:
+            # the decoder layers' products stream their weights the same way
+            self.target = dict(self.target, **{n: H.hydra_pack_weight(self.target[n])
+                                               for n in ("Wqkv", "Wo", "Wgu", "Wd")})
         if self.sketch:
             self.heads = [dict(hd, W2=pk(hd["W2"])) for hd in weights["heads"]]
         else:

@@ -1104,6 +1104,45 @@ def test_tree_decoder_layer(dtype, B, tree, d, Hq, Hkv, D, F, lens, layers):
         xs_dev, xs_ref = out, ref  # each side's next layer reads its own output
 
 
+@pytest.mark.parametrize("B,tree,d,Hq,Hkv,D,F,lens", [
+    (3, ("cartesian", [3, 2, 2]), 512, 4, 4, 128, 1024, [0, 17, 300]),
+    (1, ("sparse", (10, 4, 2, 1), 64), 4096, 32, 32, 128, 11008, [2048]),
+    (2, ("cartesian", [10, 4, 2]), 256, 8, 2, 32, 512, [5, 40]),  # 2 x 131 rows: the tiled split products
+])
+def test_tree_decoder_layer_packed_weights_match_row_major(B, tree, d, Hq, Hkv, D, F, lens):
+    """The layer with its four weight matrices packed (HYDRA_LAYER_PACKED)
+    gives bit for bit the outputs of the row-major weights: same values,
+    same kernels, same K order."""
+    from speculative_decoding_hydra_amd import (hydra_pack_weight, tree_decoder_layer,
+                                                tree_decoder_layer_workspace_size)
+
+    print(f"decoder layer packed B={B} tree={tree} d={d} F={F}", flush=True)
+    plan = T.oracle_plan(tree)[0]
+    N = plan.n
+    g = torch.Generator().manual_seed(d + N + B + 1)
+    dt = torch.bfloat16
+    anc = torch.from_numpy(np.stack([O.ancestors(plan.parent, plan.dmax)] * B).astype(np.int32)).cuda()
+    depth = torch.from_numpy(np.stack([plan.depth] * B).astype(np.int32)).cuda()
+    x = torch.randn(B, N, d, generator=g).to(dt).cuda()
+    w = {k: v.cuda() for k, v in _layer_weights(g, d, Hq, Hkv, D, F, dt).items()}
+    wp = dict(w, **{k: hydra_pack_weight(w[k]) for k in ("Wqkv", "Wo", "Wgu", "Wd")})
+    c = _attn_case(B, N, Hq, Hkv, D, lens, "bf16", seed=d + 7, tree=plan.parent)
+    dev = lambda t: (torch.from_numpy(t) if isinstance(t, np.ndarray) else t).cuda().contiguous()  # noqa: E731
+    ws = torch.empty(tree_decoder_layer_workspace_size(1, B, N, d, Hq, Hkv, D, F, max(lens)), dtype=torch.uint8,
+                     device="cuda")
+    outs = []
+    for weights in (w, wp):
+        out = torch.empty(B, N, d, dtype=dt, device="cuda")
+        kt = torch.empty(B, N, Hkv, D, dtype=dt, device="cuda")
+        vt = torch.empty_like(kt)
+        tree_decoder_layer(x, weights, Hq, Hkv, dev(c["kpool"]), dev(c["vpool"]), dev(c["bt"]), dev(c["lens"]),
+                           max(lens), anc, depth, out, kt, vt, ws)
+        torch.cuda.synchronize()
+        outs.append((out.cpu(), kt.cpu(), vt.cpu()))
+    for a_, b_ in zip(*outs):
+        assert torch.equal(a_, b_)
+
+
 @pytest.mark.parametrize("name,over", [("tiny_layers", {}), ("tiny_layers", {"dtype": "bf16"}),
                                        ("tiny_layers", {"mode": "stochastic", "T": 0.8, "layers": 2}),
                                        ("7b_layers", {"layers": 2})])

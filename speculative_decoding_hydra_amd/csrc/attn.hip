@@ -888,30 +888,33 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_split_mfma(
     for (int c = 0; c < TK / 64; ++c) step(std::integral_constant<bool, !whole>{}, 64 * c, t0);
   };
 
-  using S0 = std::integral_constant<int, 0>;
-  using S1 = std::integral_constant<int, PD - 1>;
   using Whole = std::true_type;
   using Part = std::false_type;
   // whole prefix tiles over valid pages run unmasked in a loop of their own
-  // (pairs of them when two are in flight), the rest masked
+  // (PD at a time, one per register slot), the rest masked; tile i lives in
+  // slot i % PD and its slot's refill fetches tile i + PD
   const int ntiles = t_end > t_begin ? (t_end - t_begin + TK - 1) / TK : 0;
   const int nwhole = tree_part || !pages_ok ? 0 : (t_end - t_begin) / TK / PD * PD;
-  if (ntiles > 0) {
-    if (nwhole > 0) load_tile(S0{}, Whole{}, t_begin);
-    else load_tile(S0{}, Part{}, t_begin);
-  }
-  if (PD > 1 && ntiles > 1) {
-    if (nwhole > 1) load_tile(S1{}, Whole{}, t_begin + TK);
-    else load_tile(S1{}, Part{}, t_begin + TK);
-  }
+  auto prologue = [&](auto SLOT) __attribute__((always_inline)) {
+    constexpr int sl = decltype(SLOT)::value;
+    if (sl < ntiles) {
+      if (sl < nwhole) load_tile(SLOT, Whole{}, t_begin + sl * TK);
+      else load_tile(SLOT, Part{}, t_begin + sl * TK);
+    }
+  };
+  static_for<0, PD>(prologue);
   int it = 0;
   for (; it < nwhole; it += PD) {
-    process(S0{}, Whole{}, t_begin + it * TK);
-    if (PD > 1) process(S1{}, Whole{}, t_begin + (it + 1) * TK);
+    auto whole_step = [&](auto SLOT) __attribute__((always_inline)) {
+      process(SLOT, Whole{}, t_begin + (it + decltype(SLOT)::value) * TK);
+    };
+    static_for<0, PD>(whole_step);
   }
   for (; it < ntiles; it += PD) {
-    process(S0{}, Part{}, t_begin + it * TK);
-    if (PD > 1 && it + 1 < ntiles) process(S1{}, Part{}, t_begin + (it + 1) * TK);
+    auto part_step = [&](auto SLOT) __attribute__((always_inline)) {
+      if (it + decltype(SLOT)::value < ntiles) process(SLOT, Part{}, t_begin + (it + decltype(SLOT)::value) * TK);
+    };
+    static_for<0, PD>(part_step);
   }
 
   if (tree_part || t_end >= s_end) break;

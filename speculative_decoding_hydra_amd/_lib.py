@@ -5,7 +5,9 @@ import ctypes as C
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libhydra.so")
+# HYDRA_LIB selects another build of the same sources (the sanitized one of
+# build.py --sanitize, for host-side checks)
+LIB_PATH = os.environ.get("HYDRA_LIB") or os.path.join(_HERE, "libhydra.so")
 
 c_int, c_float, c_size, c_void = C.c_int, C.c_float, C.c_size_t, C.c_void_p
 i32p = C.POINTER(C.c_int32)

@@ -309,6 +309,14 @@ int gemm_workgroups(int M, int N);
 int launch_projection_parts(int dtype, int M, int K, int N, const void* X, const void* W, float* part,
                             size_t part_floats, int* nsplit, hipStream_t stream);
 
+// The decoder layer's gated feed-forward input g[m][j] = silu(gate) * up in
+// one launch: W [2F][K] holds the gate rows, then the up rows (bf16, packed
+// with HYDRA_LAYER_PACKED in dtype); X [M][K] contiguous; g_out [M][F] bf16.
+// Same arithmetic as a product followed by the elementwise step.
+bool projection_glu_supported(int dtype, int M, int K, int F);
+int launch_projection_glu(int dtype, int M, int K, int F, const void* X, const void* W, bf16_t* g_out,
+                          hipStream_t stream);
+
 // Finish the fused row reduction: log-sum-exp and sorted top-k of each row,
 // then either the candidate-tree fill (draft heads) or the arg max. The top-k
 // is taken from the finished logits Y of the k blocks with the largest

@@ -268,31 +268,69 @@ LayerWs layer_ws(int dtype, int B, int N, int d, int Hq, int Hkv, int D, int F, 
   return w;
 }
 
-// wflag: HYDRA_LAYER_PACKED when Wqkv, Wo, Wgu and Wd are packed
+// The layer's scratch, carved from its workspace in one fixed order (the
+// forward pass reads x1 and acc of the layer before after it returns)
+template <typename T>
+struct LayerBufs {
+  T* a;
+  float* acc;
+  T* q;
+  T* o;
+  T* x1;
+  T* g;
+  void* attn;
+};
+
+template <typename T>
+LayerBufs<T> layer_bufs(const LayerWs& w, void* ws, size_t ws_bytes) {
+  Arena arena(ws, ws_bytes);
+  LayerBufs<T> b;
+  b.a = arena.take<T>(w.a / sizeof(T));
+  b.acc = arena.take<float>(w.acc / 4);
+  b.q = arena.take<T>(w.q / sizeof(T));
+  b.o = arena.take<T>(w.o / sizeof(T));
+  b.x1 = arena.take<T>(w.x1 / sizeof(T));
+  b.g = arena.take<T>(w.g / sizeof(T));
+  b.attn = arena.take<char>(w.attn);
+  return b;
+}
+
+// wflag: HYDRA_LAYER_PACKED when Wqkv, Wo, Wgu and Wd are packed.
+// Chaining (the forward pass through several layers): with in_ns > 0 the
+// layer's input is not materialised yet; it is x1 + the in_ns down-product
+// partials of the layer before (both still in this workspace), and the first
+// norm adds them, stores the sum to x_store and normalises it in one launch.
+// With out_ns the layer leaves its own residual the same way (x1 and the
+// partials in the workspace, their count in *out_ns) instead of writing x_out.
 template <typename T>
 int run_layer(int dtype, int wflag, int B, int N, int d, int Hq, int Hkv, int D, int F, const T* x, const T* ln1,
               const T* Wqkv, const T* Wo, const T* ln2, const T* Wgu, const T* Wd, float eps, float theta,
               const void* k_pages, const void* v_pages, int n_pages, int page_size, const int32_t* block_table,
               int max_pages, const int32_t* prefix_len, int max_prefix_len, const int32_t* anc,
               const int32_t* depth, int Dmax, T* x_out, T* k_tree, T* v_tree, void* ws, size_t ws_bytes,
-              hipStream_t stream) {
+              hipStream_t stream, int in_ns = 0, T* x_store = nullptr, int* out_ns = nullptr) {
   const LayerWs w = layer_ws(dtype, B, N, d, Hq, Hkv, D, F, max_prefix_len);
-  Arena arena(ws, ws_bytes);
-  T* a = arena.take<T>(w.a / sizeof(T));
-  float* acc = arena.take<float>(w.acc / 4);
-  T* q = arena.take<T>(w.q / sizeof(T));
-  T* o = arena.take<T>(w.o / sizeof(T));
-  T* x1 = arena.take<T>(w.x1 / sizeof(T));
-  T* g = arena.take<T>(w.g / sizeof(T));
-  void* attn_ws = arena.take<char>(w.attn);
+  const LayerBufs<T> buf = layer_bufs<T>(w, ws, ws_bytes);
+  T* a = buf.a;
+  float* acc = buf.acc;
+  T* q = buf.q;
+  T* o = buf.o;
+  T* x1 = buf.x1;
+  T* g = buf.g;
   const int M = B * N;
   int ns = 1;  // split-K partials of the last product
   auto proj = [&](int K, int Nout, const T* X, const T* W) {
     return launch_projection_parts(dtype | wflag, M, K, Nout, X, W, acc, w.acc / 4, &ns, stream);
   };
   auto blocks = [](long long n) { return static_cast<unsigned>((n + 255) / 256); };
-  // a = rms(x) g1
-  launch_norm<T>(M, d, eps, x, nullptr, 1, nullptr, ln1, a, stream);
+  // a = rms(x) g1 (chained: x = x1 + partials of the layer before, stored first)
+  const T* xin = x;
+  if (in_ns > 0) {
+    launch_norm<T>(M, d, eps, x1, acc, in_ns, x_store, ln1, a, stream);
+    xin = x_store;
+  } else {
+    launch_norm<T>(M, d, eps, x, nullptr, 1, nullptr, ln1, a, stream);
+  }
   HY_LAUNCH_CHECK("decoder layer: norm 1");
   // q, k, v (one product), rotated
   int rc = proj(d, (Hq + 2 * Hkv) * D, a, Wqkv);
@@ -304,21 +342,31 @@ int run_layer(int dtype, int wflag, int B, int N, int d, int Hq, int Hkv, int D,
   HY_LAUNCH_CHECK("decoder layer: q/k/v");
   rc = tree_attention_verify(dtype, B, N, Hq, Hkv, D, 1.0f / sqrtf(static_cast<float>(D)), q, k_tree, v_tree,
                              k_pages, v_pages, n_pages, page_size, block_table, max_pages, prefix_len,
-                             max_prefix_len, anc, depth, Dmax, o, nullptr, attn_ws, w.attn, stream);
+                             max_prefix_len, anc, depth, Dmax, o, nullptr, buf.attn, w.attn, stream);
   if (rc != HYDRA_OK) return rc;
   // x1 = x + o Wo^T;  b = rms(x1) g2 (into a)
   rc = proj(Hq * D, d, o, Wo);
   if (rc != HYDRA_OK) return rc;
-  launch_norm<T>(M, d, eps, x, acc, ns, x1, ln2, a, stream);
+  launch_norm<T>(M, d, eps, xin, acc, ns, x1, ln2, a, stream);
   HY_LAUNCH_CHECK("decoder layer: norm 2");
-  // g = silu(b Wg^T) * (b Wu^T);  x2 = x1 + g Wd^T
-  rc = proj(d, 2 * F, a, Wgu);
-  if (rc != HYDRA_OK) return rc;
-  const long long gn = static_cast<long long>(M) * F;
-  swiglu_rows<T><<<blocks(gn), 256, 0, stream>>>(gn, F, acc, ns, static_cast<size_t>(M) * 2 * F, g);
-  HY_LAUNCH_CHECK("decoder layer: swiglu");
+  // g = silu(b Wg^T) * (b Wu^T): one gated launch (bf16, up to 64 rows), else
+  // the product's partials and an elementwise pass;  x2 = x1 + g Wd^T
+  if (projection_glu_supported(dtype | wflag, M, d, F)) {
+    rc = launch_projection_glu(dtype | wflag, M, d, F, a, Wgu, reinterpret_cast<bf16_t*>(g), stream);
+    if (rc != HYDRA_OK) return rc;
+  } else {
+    rc = proj(d, 2 * F, a, Wgu);
+    if (rc != HYDRA_OK) return rc;
+    const long long gn = static_cast<long long>(M) * F;
+    swiglu_rows<T><<<blocks(gn), 256, 0, stream>>>(gn, F, acc, ns, static_cast<size_t>(M) * 2 * F, g);
+    HY_LAUNCH_CHECK("decoder layer: swiglu");
+  }
   rc = proj(F, d, g, Wd);
   if (rc != HYDRA_OK) return rc;
+  if (out_ns) {
+    *out_ns = ns;  // the next norm adds x1 and these partials
+    return HYDRA_OK;
+  }
   const long long xn = static_cast<long long>(M) * d;
   residual_add<T><<<blocks(xn), 256, 0, stream>>>(xn, x1, acc, ns, x_out);
   HY_LAUNCH_CHECK("decoder layer: residual");
@@ -379,18 +427,21 @@ int run_verify(int dtype, int wflag, int n_layers, int B, int N, int d, int Hq, 
   const size_t sqkv = static_cast<size_t>(Hq + 2 * Hkv) * D * d, so = static_cast<size_t>(d) * Hq * D;
   const size_t sgu = 2 * static_cast<size_t>(F) * d, sd = static_cast<size_t>(d) * F;
   const size_t skv = M * Hkv * D, spool = static_cast<size_t>(n_pages) * Hkv * page_size * D;
+  // each layer leaves its residual in the workspace (x1 + down partials);
+  // the next layer's first norm, and at the end the final norm, adds it and
+  // stores the sum, so no launch of its own materialises a layer's output
+  int ns = 0;
   for (int l = 0; l < n_layers; ++l) {
     const int rc = run_layer<T>(dtype, wflag, B, N, d, Hq, Hkv, D, F, cur, ln1 + l * static_cast<size_t>(d),
                                 Wqkv + l * sqkv, Wo + l * so, ln2 + l * static_cast<size_t>(d), Wgu + l * sgu,
                                 Wd + l * sd, eps, theta, k_pages + l * spool, v_pages + l * spool, n_pages,
-                                page_size, block_table, max_pages, prefix_len, max_prefix_len, anc, depth, Dmax, nxt,
-                                k_tree + l * skv, v_tree + l * skv, lws, w.layer.total, stream);
+                                page_size, block_table, max_pages, prefix_len, max_prefix_len, anc, depth, Dmax,
+                                nullptr, k_tree + l * skv, v_tree + l * skv, lws, w.layer.total, stream, ns, cur,
+                                &ns);
     if (rc != HYDRA_OK) return rc;
-    T* t = cur;
-    cur = nxt;
-    nxt = t;
   }
-  launch_norm<T>(static_cast<int>(M), d, eps, cur, nullptr, 1, nullptr, ln_f, h_out, stream);
+  const LayerBufs<T> lb = layer_bufs<T>(w.layer, lws, w.layer.total);
+  launch_norm<T>(static_cast<int>(M), d, eps, lb.x1, lb.acc, ns, nxt, ln_f, h_out, stream);
   HY_LAUNCH_CHECK("verify layers: final norm");
   return HYDRA_OK;
 }

@@ -17,6 +17,8 @@
 //   * optional fused epilogue: per row and workgroup, the top-k of the
 //     workgroup's 64 columns and (max, sum exp) over them, so the vocabulary
 //     reductions need no second pass over the logits.
+#include <type_traits>
+
 #include "common.h"
 
 namespace hydra {
@@ -33,6 +35,12 @@ struct ProjArgs {
   float* part;
   TopkPartials tp;
   int wpacked;  // W in the packed layout (packed_piece) rather than row-major [N][K]
+  // gated product (glu_F > 0; bf16, 4 waves, no split, no top-k): W holds
+  // gate rows [0, F) then up rows [F, 2F); workgroup b streams gate rows
+  // 32 b .. 32 b + 31 (waves 0, 1) and the same up rows (waves 2, 3) and
+  // writes glu_out[m][j] = bf16(silu(gate) * up) instead of Y
+  int glu_F;
+  bf16_t* glu_out;
 };
 
 // REM: the K range need not be a multiple of PF * KC (a multiple of KC is
@@ -56,7 +64,9 @@ __global__ __launch_bounds__(64 * WV) void proj_bf16_kernel(ProjArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int n_base = blockIdx.x * RPW + wave * 16;
+  const int n_base = a.glu_F > 0 ? (wave < 2 ? 32 * static_cast<int>(blockIdx.x) + 16 * wave
+                                             : a.glu_F + 32 * static_cast<int>(blockIdx.x) + 16 * (wave - 2))
+                                 : static_cast<int>(blockIdx.x) * RPW + wave * 16;
   const int k_begin = blockIdx.y * a.kper;
   const int k_end = REM && k_begin + a.kper > a.K ? a.K : k_begin + a.kper;  // REM: the last split may be short
   const int K0 = xs.mode == 0 ? K : xs.d;
@@ -158,6 +168,45 @@ __global__ __launch_bounds__(64 * WV) void proj_bf16_kernel(ProjArgs a) {
                                                           0, 0, 0);
       }
     }
+  }
+
+  if (!SPLIT && !TOPK && WV == 4 && a.glu_F > 0) {
+    // the up values through LDS (64 rows x 32 columns, padded), then waves
+    // 0 and 1 finish their gate columns; same expression as swiglu_rows
+    constexpr int UR = 33;
+    static_assert(MP * UR * 4 <= XLDS * 2, "the up tile fits the X staging area");
+    float* upt = reinterpret_cast<float*>(xlds);
+    __syncthreads();  // every wave is done with the last X chunk
+    if (wave >= 2) {
+#pragma unroll
+      for (int t = 0; t < MT; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          upt[(t * 16 + (lane & 15)) * UR + 16 * (wave - 2) + 4 * (lane >> 4) + i] = acc[t][i];
+    }
+    __syncthreads();
+    if (wave < 2) {
+      const int jl = 16 * wave + 4 * (lane >> 4);
+      const int j0 = 32 * static_cast<int>(blockIdx.x) + jl;
+#pragma unroll
+      for (int t = 0; t < MT; ++t) {
+        const int ml = t * 16 + (lane & 15), m = m_base + ml;
+        if (m >= M || j0 >= a.glu_F) continue;
+        uint32_t w2[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          uint32_t packed = 0;
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const float gate = acc[t][2 * h + e], up = upt[ml * UR + jl + 2 * h + e];
+            packed |= static_cast<uint32_t>(f32_to_bf16(gate / (1.0f + expf(-gate)) * up)) << (16 * e);
+          }
+          w2[h] = packed;
+        }
+        *reinterpret_cast<uint2*>(a.glu_out + static_cast<size_t>(m) * a.glu_F + j0) = make_uint2(w2[0], w2[1]);
+      }
+    }
+    return;
   }
 
   // D[n][m]: lane holds n = 4 * (lane / 16) + i, m = lane % 16 of each tile.
@@ -370,7 +419,7 @@ int launch_projection(int dtype, int M, int K, int N, XSource xs, const void* W,
     set_error("projection: packed weights take contiguous rows without split K (M=%d)", M);
     return HYDRA_ERR_UNSUPPORTED;
   }
-  ProjArgs a{M, K, N, xs, static_cast<const bf16_t*>(W), Y, map, ldy, K / nsplit, 0, part, tp, wpacked};
+  ProjArgs a{M, K, N, xs, static_cast<const bf16_t*>(W), Y, map, ldy, K / nsplit, 0, part, tp, wpacked, 0, nullptr};
   for (int m0 = 0; m0 < M; m0 += 256) {
     const int mc = M - m0 < 256 ? M - m0 : 256;
     a.m_base = m0;
@@ -424,13 +473,48 @@ int launch_projection_parts(int dtype, int M, int K, int N, const void* X, const
     return launch_projection(dtype | (wpacked ? HYDRA_VOCAB_PACKED : 0), M, K, N, xs, W, part, RowMap{M, 0, 0}, N,
                              1, nullptr, TopkPartials{nullptr, nullptr}, stream);
   ProjArgs a{M, K, N, xs, static_cast<const bf16_t*>(W), nullptr, RowMap{M, 0, 0}, N, kper, 0, part,
-             TopkPartials{nullptr, nullptr}, wpacked};
+             TopkPartials{nullptr, nullptr}, wpacked, 0, nullptr};
   for (int m0 = 0; m0 < M; m0 += 256) {
     const int mc = M - m0 < 256 ? M - m0 : 256;
     a.m_base = m0;
     const int rc = launch_bf16_mt<false>(mc, a, ns, stream);
     if (rc != HYDRA_OK) return rc;
   }
+  return HYDRA_OK;
+}
+
+bool projection_glu_supported(int dtype, int M, int K, int F) {
+  dtype &= ~HYDRA_LAYER_PACKED;
+  return dtype == HYDRA_BF16 && M >= 1 && M <= 64 && K % kPackChunk == 0 && F % 32 == 0;
+}
+
+int launch_projection_glu(int dtype, int M, int K, int F, const void* X, const void* W, bf16_t* g_out,
+                          hipStream_t stream) {
+  const int wpacked = (dtype & HYDRA_LAYER_PACKED) != 0;
+  if (!projection_glu_supported(dtype, M, K, F)) {
+    set_error("projection: the gated product needs bf16, 1..64 rows, K %% 256 == 0, F %% 32 == 0");
+    return HYDRA_ERR_UNSUPPORTED;
+  }
+  XSource xs{};
+  xs.x = X;
+  xs.ldx = K;
+  xs.mode = 0;
+  ProjArgs a{M, K, 2 * F, xs, static_cast<const bf16_t*>(W), nullptr, RowMap{M, 0, 0}, 2 * F, K, 0, nullptr,
+             TopkPartials{nullptr, nullptr}, wpacked, F, g_out};
+  const dim3 grid(F / 32, 1);
+  auto go = [&](auto MTC) {
+    constexpr int MT = decltype(MTC)::value;
+    if (K % (2 * kPackChunk) == 0)
+      proj_bf16_kernel<MT, 256, 2, 4, false, false, false><<<grid, 256, 0, stream>>>(a);
+    else if (K > 2 * kPackChunk)
+      proj_bf16_kernel<MT, 256, 2, 4, false, false, true><<<grid, 256, 0, stream>>>(a);
+    else
+      proj_bf16_kernel<MT, 256, 1, 4, false, false, false><<<grid, 256, 0, stream>>>(a);
+  };
+  if (M <= 16) go(std::integral_constant<int, 1>{});
+  else if (M <= 32) go(std::integral_constant<int, 2>{});
+  else go(std::integral_constant<int, 4>{});
+  HY_LAUNCH_CHECK("projection(gated)");
   return HYDRA_OK;
 }
 

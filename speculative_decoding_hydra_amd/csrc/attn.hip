@@ -229,9 +229,14 @@ __global__ __launch_bounds__(64 * WQ * WK, 1) void attn_tile_mfma(AttnArgs a) {
   const size_t head_off = static_cast<size_t>(hkv) << (a.page_shift + 7);
   const size_t tree_stride = static_cast<size_t>(a.Hkv) * kD;
   const size_t tree_base = (static_cast<size_t>(b) * N * a.Hkv + hkv) * kD;
-  // K operand of this lane: key row l32, chunk 2 ks + hl at (2 ks + hl) ^ kx
+  // K operand of this lane: key row l32, chunk 2 ks + hl at (2 ks + hl) ^ kx.
+  // K rows keep chunk c of key r at c ^ 2 (r % 8) ^ ((r / 16) % 2): a 16-byte
+  // read is served 16 lanes at a time (lanes 0-7 with 16-23, 8-15 with
+  // 24-31, ...), which here are keys r and r + 16 of one chunk; the last
+  // term puts those two in different bank groups (without it half of the
+  // LDS cycles went to bank conflicts). V rows keep c ^ 2 (r % 8).
   const int krow = l32 * kD;
-  const int kx = 2 * (l32 & 7);
+  const int kx = (2 * (l32 & 7)) ^ ((l32 >> 4) & 1);
   // V^T operands: lane 4 i + q of each 16-lane group points at key
   // 16 kc + 4 hl + 8 t + i, dims 32 dt + 16 (group % 2) + 4 q .. + 3; the
   // swizzle depends on the key mod 8 only, so kc and t are offsets
@@ -296,7 +301,8 @@ __global__ __launch_bounds__(64 * WQ * WK, 1) void attn_tile_mfma(AttnArgs a) {
 
     // DMA of this wave's share of group tile j into stage ST: instruction ins
     // (0..15) fills rows 4 (ins % 8) .. + 3 of K (ins < 8) or V; lane i writes
-    // position i % 16 of row i / 16 there, i.e. chunk (i % 16) ^ 2 (row % 8).
+    // position i % 16 of row i / 16 there, i.e. chunk (i % 16) ^ 2 (row % 8)
+    // (K rows 16 .. 31: also ^ 1).
     // The four keys of an instruction are consecutive slots of one page (or
     // four consecutive tree rows), so the source is a wave-uniform base (page
     // and slot, computed on the scalar unit) plus a per-lane offset fixed for
@@ -310,6 +316,9 @@ __global__ __launch_bounds__(64 * WQ * WK, 1) void attn_tile_mfma(AttnArgs a) {
         const int ins = wq * INS + n;
         const int tensor = ins >> 3;
         const int par = ins & 1;
+        // K rows 16 .. 31 of the tile (K instructions 4 .. 7) take the extra
+        // chunk swizzle; bit 4 of a per-lane source offset is bit 0 of its chunk
+        const uint32_t flip = tensor == 0 ? static_cast<uint32_t>((ins >> 2) & 1) << 4 : 0u;
         const char* src;
         int code;
         if (i < wnp) {
@@ -325,7 +334,7 @@ __global__ __launch_bounds__(64 * WQ * WK, 1) void attn_tile_mfma(AttnArgs a) {
           }
           const bf16_t* base = (tensor ? a.v_pages : a.k_pages) + pg * pstride + head_off +
                                (static_cast<size_t>(slot0) << 7);
-          src = reinterpret_cast<const char*>(base) + loff_pool[par];
+          src = reinterpret_cast<const char*>(base) + (loff_pool[par] ^ flip);
         } else {
           const int vu = kTK * (t0 + a.S * (i - wnp)) + 4 * (ins & 7);  // first tree row
           const int v = vu + lrow;
@@ -333,10 +342,10 @@ __global__ __launch_bounds__(64 * WQ * WK, 1) void attn_tile_mfma(AttnArgs a) {
           code = dv >= 0 && dv <= a.Dmax ? dv : -1;
           const bf16_t* tb = tensor ? a.v_tree : a.k_tree;
           if (vu + 3 < N) {
-            src = reinterpret_cast<const char*>(tb + tree_base + vu * tree_stride) + loff_tree[par];
+            src = reinterpret_cast<const char*>(tb + tree_base + vu * tree_stride) + (loff_tree[par] ^ flip);
           } else {  // the last rows: clamp each lane's row
             const int vc = v < N ? v : N - 1;
-            src = reinterpret_cast<const char*>(tb + tree_base + vc * tree_stride) + lchunk[par];
+            src = reinterpret_cast<const char*>(tb + tree_base + vc * tree_stride) + (lchunk[par] ^ flip);
           }
         }
         if (tensor == 0 && (lane & 15) == 0) s_kd[wk][decltype(ST)::value][4 * (ins & 7) + lrow] = code;

@@ -55,7 +55,6 @@ typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4_t;
 constexpr int kTK = 32;                     // keys per tile
 constexpr int kD = 128;                     // head dim of the matrix-core path
 constexpr int kTileElems = kTK * kD;        // one K or V tile: 8 KB
-constexpr int kMaxWGPages = 2048;           // page ids a workgroup stages in LDS
 
 // The running offset of a row moves only when a tile's maximum exceeds it by
 // more than this (log2 units): probabilities stay below 2^8, and most tiles
@@ -125,33 +124,44 @@ __device__ __forceinline__ void barrier_only() { asm volatile("s_waitcnt lgkmcnt
 
 // f(integral_constant<int, I>) for I = I0 .. N - 1, unrolled
 template <int I, int N, class F>
-__device__ __forceinline__ void static_for(F& f) {
+__device__ __forceinline__ void static_for(F&& f) {
   if constexpr (I < N) {
     f(std::integral_constant<int, I>{});
     static_for<I + 1, N>(f);
   }
 }
 
-template <int QC, int WQ, int WK, int NS>
-__global__ __launch_bounds__(64 * WQ * WK, 1) void attn_tile_mfma(AttnArgs a) {
-  static_assert(QC * WQ * WK == 8 && WQ >= 2 && NS >= 2 && NS <= 8 && 16 % WQ == 0, "layout");
-  constexpr int NT = 64 * WQ * WK;  // threads
-  constexpr int QW = 32 * QC;       // query rows of a wave
-  constexpr int QR = QW * WQ;       // query rows of the workgroup
-  constexpr int INS = 16 / WQ;      // 1 KB DMA instructions per wave per tile (16 per tile)
-  __shared__ __align__(16) bf16_t st0[WK][2][kTileElems];
-  __shared__ __align__(16) bf16_t st1[NS > 1 ? WK : 1][2][NS > 1 ? kTileElems : 8];
-  __shared__ __align__(16) bf16_t st2[NS > 2 ? WK : 1][2][NS > 2 ? kTileElems : 8];
-  __shared__ __align__(16) bf16_t st3[NS > 3 ? WK : 1][2][NS > 3 ? kTileElems : 8];
-  __shared__ __align__(16) bf16_t st4[NS > 4 ? WK : 1][2][NS > 4 ? kTileElems : 8];
-  __shared__ __align__(16) bf16_t st5[NS > 5 ? WK : 1][2][NS > 5 ? kTileElems : 8];
-  __shared__ __align__(16) bf16_t st6[NS > 6 ? WK : 1][2][NS > 6 ? kTileElems : 8];
-  __shared__ __align__(16) bf16_t st7[NS > 7 ? WK : 1][2][NS > 7 ? kTileElems : 8];
-  __shared__ int s_pages[kMaxWGPages];
-  __shared__ int s_dep[HYDRA_MAX_VERIFY];
+// 16-byte LDS read the compiler does not track (see tr_read), at a constant
+// offset from addr; the caller waits for it with an s_waitcnt that threads
+// the value through
+template <int OFF>
+__device__ __forceinline__ u32x4_t lds_read16(uint32_t addr) {
+  u32x4_t v;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF));
+  return v;
+}
+
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+
+// attn_tile_mfma: 8 waves, each 32 query rows of one (sequence, KV head);
+// WQ waves along the queries, WK key groups. Per key group a ring of four
+// stages (K and V of one 32-key tile, 16 KB) is filled by LDS DMA two tiles
+// ahead; the stage index is static in the unrolled loop, so every LDS read
+// names its stage by the instruction's offset field.
+template <int WQ, int WK>
+__global__ __launch_bounds__(512, 1) void attn_tile_mfma(AttnArgs a) {
+  static_assert(WQ * WK == 8 && 16 % WQ == 0, "layout");
+  constexpr int NS = 4;                           // stages
+  constexpr int NT = 512;                         // threads
+  constexpr int QR = 32 * WQ;                     // query rows of the workgroup
+  constexpr int INS = 16 / WQ;                    // 1 KB DMA instructions per wave per tile (16 per tile)
+  constexpr int kStageBytes = 2 * kTileElems * 2;  // a stage: K tile, then V tile
+  constexpr int kWinTiles = 128;                  // tiles of a window: page ids in two registers per lane
+  static_assert(NS * kStageBytes <= 65536, "stage offsets fit the LDS offset field");
+  // stages of each key group: one object, read only through untracked reads
+  // (a tracked read would make the compiler wait for every fill in flight)
+  __shared__ __align__(16) bf16_t stg[WK][NS][2][kTileElems];
   __shared__ int s_anc[QR][HYDRA_MAX_DEPTH + 1];
-  // per stage and key of a tile: -1 masked, -2 prefix key, else tree key depth
-  __shared__ __align__(16) int s_kd[WK][NS][kTK];
 
   // the wave index is uniform: readfirstlane keeps everything derived from it
   // (tile counts, pipeline branches) in scalar registers
@@ -183,15 +193,10 @@ __global__ __launch_bounds__(64 * WQ * WK, 1) void attn_tile_mfma(AttnArgs a) {
   const int t0 = a.S - 1 - split;
   const int ntr = t0 < ntt ? (ntt - 1 - t0) / a.S + 1 : 0;
 
-  // tree depths (the DMA issue reads them) with the first page ids; the
-  // ancestor rows and Q, needed only once tiles are computed, are loaded
-  // after the first tiles' DMA is in flight
-  if (ntr > 0)
-    for (int e = tid; e < N; e += NT) s_dep[e] = a.depth[static_cast<size_t>(b) * N + e];
-  const int q0 = qt * QR + wq * QW;
-  bf16x8_t qreg[QC][8];
-  // Q^T operands: column l32 of tile c is query row q0 + 32 c + l32, dims
-  // 16 ks + 8 hl .. + 7
+  const int q0 = qt * QR + wq * 32;
+  bf16x8_t qreg[8];
+  // Q^T operand: column l32 is query row q0 + l32, dims 16 ks + 8 hl .. + 7;
+  // the ancestor rows of the workgroup's queries go to LDS
   auto load_q = [&]() __attribute__((always_inline)) {
     if (ntr > 0) {
       for (int e = tid; e < QR * (a.Dmax + 1); e += NT) {
@@ -200,357 +205,416 @@ __global__ __launch_bounds__(64 * WQ * WK, 1) void attn_tile_mfma(AttnArgs a) {
         s_anc[rr][j] = qi < a.NQ ? a.anc[(static_cast<size_t>(b) * N + qi / G) * (a.Dmax + 1) + j] : -1;
       }
     }
+    const int qi = q0 + l32;
+    const bool qv = qi < a.NQ;
+    const int u = qv ? qi / G : 0, gq = qv ? qi % G : 0;
+    const bf16_t* qp = a.q + ((static_cast<size_t>(b) * N + u) * a.Hq + hkv * G + gq) * kD + 8 * hl;
 #pragma unroll
-    for (int c = 0; c < QC; ++c) {
-      const int qi = q0 + 32 * c + l32;
-      const bool qv = qi < a.NQ;
-      const int u = qv ? qi / G : 0, gq = qv ? qi % G : 0;
-      const bf16_t* qp = a.q + ((static_cast<size_t>(b) * N + u) * a.Hq + hkv * G + gq) * kD + 8 * hl;
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        const u32x4_t v = qv ? *reinterpret_cast<const u32x4_t*>(qp + 16 * ks) : u32x4_t{0u, 0u, 0u, 0u};
-        qreg[c][ks] = __builtin_bit_cast(bf16x8_t, v);
-      }
+    for (int ks = 0; ks < 8; ++ks) {
+      const u32x4_t v = qv ? *reinterpret_cast<const u32x4_t*>(qp + 16 * ks) : u32x4_t{0u, 0u, 0u, 0u};
+      qreg[ks] = __builtin_bit_cast(bf16x8_t, v);
     }
   };
 
-  float m_run[QC], l_run[QC];
-  f32x16_t oacc[QC][4];
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x16_t oacc[4];
 #pragma unroll
-  for (int c = 0; c < QC; ++c) m_run[c] = -INFINITY, l_run[c] = 0.f;
+  for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-  for (int c = 0; c < QC; ++c)
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[c][dt][r] = 0.f;
+    for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.f;
 
-  const size_t pstride = static_cast<size_t>(a.Hkv) << (a.page_shift + 7);  // elements per page
-  const size_t head_off = static_cast<size_t>(hkv) << (a.page_shift + 7);
-  const size_t tree_stride = static_cast<size_t>(a.Hkv) * kD;
-  const size_t tree_base = (static_cast<size_t>(b) * N * a.Hkv + hkv) * kD;
   // K operand of this lane: key row l32, chunk 2 ks + hl at (2 ks + hl) ^ kx.
   // K rows keep chunk c of key r at c ^ 2 (r % 8) ^ ((r / 16) % 2): a 16-byte
   // read is served 16 lanes at a time (lanes 0-7 with 16-23, 8-15 with
   // 24-31, ...), which here are keys r and r + 16 of one chunk; the last
-  // term puts those two in different bank groups (without it half of the
-  // LDS cycles went to bank conflicts). V rows keep c ^ 2 (r % 8).
-  const int krow = l32 * kD;
+  // term puts those two in different bank groups. V rows keep c ^ 2 (r % 8).
+  const uint32_t stg0 = lds_addr(&stg[wk][0][0][0]);
   const int kx = (2 * (l32 & 7)) ^ ((l32 >> 4) & 1);
+  uint32_t kaddr[8];  // stage 0 addresses; stage s is s * kStageBytes further
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) kaddr[ks] = stg0 + 2 * (l32 * kD + (((2 * ks + hl) ^ kx) << 3));
   // V^T operands: lane 4 i + q of each 16-lane group points at key
   // 16 kc + 4 hl + 8 t + i, dims 32 dt + 16 (group % 2) + 4 q .. + 3; the
   // swizzle depends on the key mod 8 only, so kc and t are offsets
   const int grp = lane >> 4, li = (lane >> 2) & 3, lq = lane & 3;
-  int voff[4];  // bytes from the tile's V base, per dt
+  uint32_t vaddr[4];
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) {
     const int row = 4 * hl + li;
     const int d0 = 32 * dt + 16 * (grp & 1) + 4 * lq;
-    voff[dt] = 2 * (row * kD + (((d0 >> 3) ^ (2 * (row & 7))) << 3) + (d0 & 7));
+    vaddr[dt] = stg0 + 2 * kTileElems + 2 * (row * kD + (((d0 >> 3) ^ (2 * (row & 7))) << 3) + (d0 & 7));
   }
 
-  auto stage_ptr = [&](auto ST) __attribute__((always_inline)) -> bf16_t* {
-    constexpr int sti = decltype(ST)::value;
-    if constexpr (sti == 0) return &st0[wk][0][0];
-    else if constexpr (sti == 1) return &st1[wk][0][0];
-    else if constexpr (sti == 2) return &st2[wk][0][0];
-    else if constexpr (sti == 3) return &st3[wk][0][0];
-    else if constexpr (sti == 4) return &st4[wk][0][0];
-    else if constexpr (sti == 5) return &st5[wk][0][0];
-    else if constexpr (sti == 6) return &st6[wk][0][0];
-    else return &st7[wk][0][0];
-  };
-
-  // per-lane byte offsets of the DMA sources: row lane / 16 of an
-  // instruction's four, chunk (lane % 16) ^ 2 (row % 8) with row % 8 =
-  // 4 (ins % 2) + lane / 16
+  // DMA: instruction ins (0..15) of a tile fills rows 4 (ins % 8) .. + 3 of K
+  // (ins < 8) or V; lane i writes position i % 16 of row i / 16 there, i.e.
+  // chunk (i % 16) ^ 2 (row % 8) (K rows 16 .. 31: also ^ 1, bit 4 of the
+  // source offset). This wave issues ins = wq INS .. + INS - 1: one tensor,
+  // rows rowbase .. + 4 INS - 1, which lie in one page (pages hold at least
+  // 16 keys and tiles start at multiples of 32). The source is a uniform
+  // base plus a per-lane 32-bit offset.
   const int lrow = lane >> 4;
-  uint32_t lchunk[2], loff_pool[2], loff_tree[2];
+  const int tensor = (wq * INS) >> 3;
+  const int rowbase = 4 * ((wq * INS) & 7);
+  const uint32_t flip = tensor == 0 ? static_cast<uint32_t>(((wq * INS) >> 2) & 1) << 4 : 0u;
+  const size_t tree_stride_b = static_cast<size_t>(a.Hkv) * kD * 2;
+  uint32_t dofs[INS], dofs_tree[INS];
 #pragma unroll
-  for (int par = 0; par < 2; ++par) {
-    const int ch = (lane & 15) ^ (2 * (4 * par + lrow));
-    lchunk[par] = ch * 16;
-    loff_pool[par] = lrow * kD * 2 + ch * 16;
-    loff_tree[par] = static_cast<uint32_t>(lrow * tree_stride * 2) + ch * 16;
+  for (int n = 0; n < INS; ++n) {
+    const uint32_t ch = static_cast<uint32_t>((lane & 15) ^ (2 * (4 * (n & 1) + lrow))) * 16;
+    dofs[n] = ((lrow * kD * 2 + ch) ^ flip) + n * 4 * kD * 2;
+    dofs_tree[n] = static_cast<uint32_t>((lrow + 4 * n) * tree_stride_b) + (ch ^ flip);
   }
+  const size_t pstride_b = (static_cast<size_t>(a.Hkv) << (a.page_shift + 7)) * 2;  // bytes per page
+  const char* kv_base = reinterpret_cast<const char*>((tensor ? a.v_pages : a.k_pages)) +
+                        (static_cast<size_t>(hkv) << (a.page_shift + 7)) * 2;
+  const char* tree_b = reinterpret_cast<const char*>(tensor ? a.v_tree : a.k_tree) +
+                       ((static_cast<size_t>(b) * N * a.Hkv + hkv) * kD) * 2;
 
-  // Windows of prefix tiles whose page ids fit in LDS (one window unless a
-  // split is longer than kWinTiles tiles); the tree tiles run in the last.
-  constexpr int kWinTiles = kMaxWGPages / 2 - 1;
+  // Windows of up to kWinTiles prefix tiles (one unless a split is longer);
+  // the tree tiles run in the last.
   for (int w0 = 0;; w0 += kWinTiles) {
     const int wnp = max(0, min(npt - w0, kWinTiles));
     const bool last = w0 + kWinTiles >= npt;
     const int T = wnp + (last ? ntr : 0);
     const int wp0 = p0 + kTK * w0;                    // first key of the window
     const int wp1 = min(p1, wp0 + kTK * kWinTiles);   // end of its prefix keys
-    const int pg0 = wp0 >> a.page_shift;
-    const int npg = wp1 > wp0 ? ((wp1 - 1) >> a.page_shift) - pg0 + 1 : 0;
     if (w0 > 0) __syncthreads();  // the previous window's readers are done
-    int bad = 0;
-    for (int e = tid; e < npg; e += NT) {
-      const int pg = a.block_table[static_cast<size_t>(b) * a.max_pages + pg0 + e];
-      s_pages[e] = pg;
-      bad |= pg < 0 || pg >= a.n_pages;
+    // page of this wave's rows in window tiles lane and lane + 64 (-1: none
+    // or out of range; those keys are masked and read page 0 instead)
+    int pgA = -1, pgB = -1, bad = 0;
+    {
+      const int32_t* bt = a.block_table + static_cast<size_t>(b) * a.max_pages;
+      const int kA = wp0 + kTK * lane + rowbase, kB = kA + 64 * kTK;
+      if (lane < wnp && kA < wp1) {
+        pgA = bt[kA >> a.page_shift];
+        bad |= pgA < 0 || pgA >= a.n_pages;
+        pgA = pgA < 0 || pgA >= a.n_pages ? -1 : pgA;
+      }
+      if (lane + 64 < wnp && kB < wp1) {
+        pgB = bt[kB >> a.page_shift];
+        bad |= pgB < 0 || pgB >= a.n_pages;
+        pgB = pgB < 0 || pgB >= a.n_pages ? -1 : pgB;
+      }
     }
     const bool pages_ok = __syncthreads_or(bad) == 0;
 
     // tiles of this key group: window tile wk + WK j, j < Tg (every group runs
-    // Tmax iterations so that shared-tile barriers pair up)
+    // Tmax iterations so that the shared barriers pair up); the first Tfull
+    // are whole prefix tiles
     const int Tg = T > wk ? (T - 1 - wk) / WK + 1 : 0;
     const int Tmax = (T + WK - 1) / WK;
+    const int wfull = pages_ok ? (wp1 - wp0) / kTK : 0;
+    const int Tfull = wfull > wk ? (wfull - 1 - wk) / WK + 1 : 0;
 
-    // DMA of this wave's share of group tile j into stage ST: instruction ins
-    // (0..15) fills rows 4 (ins % 8) .. + 3 of K (ins < 8) or V; lane i writes
-    // position i % 16 of row i / 16 there, i.e. chunk (i % 16) ^ 2 (row % 8)
-    // (K rows 16 .. 31: also ^ 1).
-    // The four keys of an instruction are consecutive slots of one page (or
-    // four consecutive tree rows), so the source is a wave-uniform base (page
-    // and slot, computed on the scalar unit) plus a per-lane offset fixed for
-    // the launch. The K instructions also record each key's mask code in s_kd.
-    auto issue = [&](auto ST, int j) __attribute__((always_inline)) {
-      if (j >= Tg) return;
+    // this wave's DMA share of group tile j into stage ST
+    auto issue = [&](auto FAST, auto ST, int j) __attribute__((always_inline)) {
+      if (!decltype(FAST)::value && j >= Tg) return;
       const int i = wk + WK * j;
-      bf16_t* kd = stage_ptr(ST);
+      bf16_t* dst = &stg[wk][decltype(ST)::value][tensor][rowbase * kD];
+      if (decltype(FAST)::value || i < wnp) {
+        int pg = __builtin_amdgcn_readlane(i < 64 ? pgA : pgB, i & 63);
+        if (!decltype(FAST)::value) pg = pg >= 0 ? pg : 0;
+        const int slot0 = (wp0 + kTK * i + rowbase) & (page_size - 1);  // of the share's first row
+        const char* src = kv_base + static_cast<size_t>(pg) * pstride_b + (static_cast<uint32_t>(slot0) << 8);
 #pragma unroll
-      for (int n = 0; n < INS; ++n) {
-        const int ins = wq * INS + n;
-        const int tensor = ins >> 3;
-        const int par = ins & 1;
-        // K rows 16 .. 31 of the tile (K instructions 4 .. 7) take the extra
-        // chunk swizzle; bit 4 of a per-lane source offset is bit 0 of its chunk
-        const uint32_t flip = tensor == 0 ? static_cast<uint32_t>((ins >> 2) & 1) << 4 : 0u;
-        const char* src;
-        int code;
-        if (i < wnp) {
-          const int tu = wp0 + kTK * i + 4 * (ins & 7);  // first key of the instruction
-          int pg = tu < wp1 ? __builtin_amdgcn_readfirstlane(s_pages[(tu >> a.page_shift) - pg0]) : -1;
-          const bool pvalid = pg >= 0 && pg < a.n_pages;
-          code = pvalid && tu + lrow < wp1 ? -2 : -1;
-          int slot0 = tu & (page_size - 1);
-          if (!pvalid) {  // masked: read four mapped slots instead
-            pg = __builtin_amdgcn_readfirstlane(s_pages[0]);
-            pg = pg >= 0 && pg < a.n_pages ? pg : 0;
-            slot0 = 0;
-          }
-          const bf16_t* base = (tensor ? a.v_pages : a.k_pages) + pg * pstride + head_off +
-                               (static_cast<size_t>(slot0) << 7);
-          src = reinterpret_cast<const char*>(base) + (loff_pool[par] ^ flip);
-        } else {
-          const int vu = kTK * (t0 + a.S * (i - wnp)) + 4 * (ins & 7);  // first tree row
-          const int v = vu + lrow;
-          const int dv = v < N ? s_dep[v] : -1;
-          code = dv >= 0 && dv <= a.Dmax ? dv : -1;
-          const bf16_t* tb = tensor ? a.v_tree : a.k_tree;
-          if (vu + 3 < N) {
-            src = reinterpret_cast<const char*>(tb + tree_base + vu * tree_stride) + (loff_tree[par] ^ flip);
-          } else {  // the last rows: clamp each lane's row
+        for (int n = 0; n < INS; ++n)
+          __builtin_amdgcn_global_load_lds((glb_void_t*)(src + dofs[n]), (lds_void_t*)(dst + 4 * n * kD), 16, 0, 0);
+      } else {
+        const int vu = kTK * (t0 + a.S * (i - wnp)) + rowbase;  // first tree row of the share
+        if (vu + 4 * INS <= N) {
+          const char* src = tree_b + static_cast<size_t>(vu) * tree_stride_b;
+#pragma unroll
+          for (int n = 0; n < INS; ++n)
+            __builtin_amdgcn_global_load_lds((glb_void_t*)(src + dofs_tree[n]), (lds_void_t*)(dst + 4 * n * kD), 16,
+                                             0, 0);
+        } else {  // the last rows: clamp each lane's row
+#pragma unroll
+          for (int n = 0; n < INS; ++n) {
+            const int v = vu + 4 * n + lrow;
             const int vc = v < N ? v : N - 1;
-            src = reinterpret_cast<const char*>(tb + tree_base + vc * tree_stride) + (lchunk[par] ^ flip);
+            const uint32_t ch = static_cast<uint32_t>((lane & 15) ^ (2 * (4 * (n & 1) + lrow))) * 16;
+            __builtin_amdgcn_global_load_lds((glb_void_t*)(tree_b + static_cast<size_t>(vc) * tree_stride_b + (ch ^ flip)),
+                                             (lds_void_t*)(dst + 4 * n * kD), 16, 0, 0);
           }
         }
-        if (tensor == 0 && (lane & 15) == 0) s_kd[wk][decltype(ST)::value][4 * (ins & 7) + lrow] = code;
-        __builtin_amdgcn_global_load_lds((glb_void_t*)src,
-                                         (lds_void_t*)(kd + tensor * kTileElems + 4 * (ins & 7) * kD), 16, 0, 0);
       }
     };
 
-    // one tile from stage ST: S^T, online softmax, O^T += V^T P^T
-    auto compute = [&](auto ST, int j) __attribute__((always_inline)) {
-      const bf16_t* kt = stage_ptr(ST);
-      const uint32_t vb = lds_addr(kt + kTileElems);
+    // scores of lane: key 8 (r / 4) + 4 hl + r % 4 of the tile, query column l32
+    auto mask = [&](int j, f32x16_t& s) __attribute__((always_inline)) {
       const int i = wk + WK * j;
-      f32x16_t sacc[QC];
+      if (i >= wnp) {
+        // tree rows vb0 .. vb0 + 31: bit k of mk is set when row vb0 + k is
+        // in the query's ancestor row (itself included)
+        const int vb0 = kTK * (t0 + a.S * (i - wnp));
+        const int* ar = &s_anc[wq * 32 + l32][0];
+        uint32_t mk = 0;
 #pragma unroll
-      for (int c = 0; c < QC; ++c)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[c][r] = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        const bf16x8_t ka =
-            __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(kt + krow + (((2 * ks + hl) ^ kx) << 3)));
-#pragma unroll
-        for (int c = 0; c < QC; ++c)
-          sacc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[c][ks], sacc[c], 0, 0, 0);
-      }
-      // V^T operands, in flight during the softmax: [kc][dt][t]
-      u32x2_t vr[2][4][2];
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt) {
-        vr[0][dt][0] = tr_read<0>(vb + voff[dt]);
-        vr[0][dt][1] = tr_read<8 * kD * 2>(vb + voff[dt]);
-        vr[1][dt][0] = tr_read<16 * kD * 2>(vb + voff[dt]);
-        vr[1][dt][1] = tr_read<24 * kD * 2>(vb + voff[dt]);
-      }
-      // scores of lane: key 8 (r / 4) + 4 hl + r % 4 of the tile, query column l32
-      const bool tree_tile = i >= wnp;
-      const bool masked = tree_tile || !pages_ok || wp0 + kTK * (i + 1) > wp1;
-      if (masked) {
-        // mask codes of this lane's keys 8 g + 4 hl + 0..3 (g = 0..3)
-        const int* kcode = &s_kd[wk][decltype(ST)::value][4 * hl];
-        const int vb0 = tree_tile ? kTK * (t0 + a.S * (i - wnp)) : 0;
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const int4 k4 = *reinterpret_cast<const int4*>(kcode + 8 * g4);
-          const int kc4[4] = {k4.x, k4.y, k4.z, k4.w};
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 4 * g4 + e, code = kc4[e];
-            const int v = vb0 + 8 * g4 + 4 * hl + e;
-#pragma unroll
-            for (int c = 0; c < QC; ++c) {
-              const bool vis = tree_tile ? code >= 0 && s_anc[wq * QW + 32 * c + l32][code < 0 ? 0 : code] == v
-                                         : code != -1;
-              sacc[c][r] = vis ? sacc[c][r] : -INFINITY;
-            }
+        for (int d = 0; d <= HYDRA_MAX_DEPTH; ++d) {
+          if (d <= a.Dmax) {
+            const uint32_t o = static_cast<uint32_t>(ar[d] - vb0);
+            mk |= o < 32u ? 1u << (o & 31u) : 0u;
           }
         }
-      }
-      bf16x8_t pb[QC][2];
+        mk >>= 4 * hl;
 #pragma unroll
-      for (int c = 0; c < QC; ++c) {
-        float mt = sacc[c][0];
-#pragma unroll
-        for (int r = 1; r < 16; ++r) mt = fmaxf(mt, sacc[c][r]);
-        mt = pair_max(mt) * a.scale_log2;
-        const bool grow = mt > m_run[c] + kRescaleSlack;
-        if (__any(grow)) {  // wave-uniform: rescale only when an offset moved
-          const float m_new = grow ? fmaxf(m_run[c], mt) : m_run[c];
-          const float alpha = m_new == m_run[c] ? 1.f : __builtin_amdgcn_exp2f(m_run[c] - m_new);
-          l_run[c] *= alpha;
-#pragma unroll
-          for (int dt = 0; dt < 4; ++dt) oacc[c][dt] *= alpha;
-          m_run[c] = m_new;
+        for (int r = 0; r < 16; ++r) s[r] = (mk >> (8 * (r >> 2) + (r & 3))) & 1u ? s[r] : -INFINITY;
+      } else {
+        // prefix keys: visible below wp1 and on a valid page
+        const int ts = wp0 + kTK * i;
+        bool pv0 = true, pv1 = true;  // pages of keys ts .. + 15 and ts + 16 .. + 31
+        if (!pages_ok) {
+          const int32_t* bt = a.block_table + static_cast<size_t>(b) * a.max_pages;
+          const int pa = ts < wp1 ? bt[ts >> a.page_shift] : -1;
+          const int pb2 = ts + 16 < wp1 ? bt[(ts + 16) >> a.page_shift] : -1;
+          pv0 = pa >= 0 && pa < a.n_pages;
+          pv1 = pb2 >= 0 && pb2 < a.n_pages;
         }
-        const float neg_m = m_run[c] == -INFINITY ? 0.f : -m_run[c];
-        float ps = 0.f;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float pe = __builtin_amdgcn_exp2f(fmaf(sacc[c][r], a.scale_log2, neg_m));
-          ps += pe;
-          pb[c][r >> 3][r & 7] = static_cast<__bf16>(pe);
-        }
-        l_run[c] += ps;
-      }
-      // the transposed reads have landed: thread their values through the wait
-      asm volatile("s_waitcnt lgkmcnt(0)"
-                   : "+v"(vr[0][0][0]), "+v"(vr[0][0][1]), "+v"(vr[0][1][0]), "+v"(vr[0][1][1]),
-                     "+v"(vr[0][2][0]), "+v"(vr[0][2][1]), "+v"(vr[0][3][0]), "+v"(vr[0][3][1]),
-                     "+v"(vr[1][0][0]), "+v"(vr[1][0][1]), "+v"(vr[1][1][0]), "+v"(vr[1][1][1]),
-                     "+v"(vr[1][2][0]), "+v"(vr[1][2][1]), "+v"(vr[1][3][0]), "+v"(vr[1][3][1]));
-#pragma unroll
-      for (int kc = 0; kc < 2; ++kc) {
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt) {
-          const u32x4_t w = {vr[kc][dt][0].x, vr[kc][dt][0].y, vr[kc][dt][1].x, vr[kc][dt][1].y};
-          const bf16x8_t va = __builtin_bit_cast(bf16x8_t, w);
-#pragma unroll
-          for (int c = 0; c < QC; ++c)
-            oacc[c][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[c][kc], oacc[c][dt], 0, 0, 0);
+          const int off = 8 * (r >> 2) + 4 * hl + (r & 3);
+          const bool vis = ts + off < wp1 && (off < 16 ? pv0 : pv1);
+          s[r] = vis ? s[r] : -INFINITY;
         }
       }
     };
 
-    // pipeline: NS - 1 tiles in flight ahead of the one being computed
-    auto iter = [&](auto ST, int j) __attribute__((always_inline)) {
-      constexpr int sti = decltype(ST)::value;
-      if (j + NS - 2 < Tg) __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 2) * INS));
-      else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-      // every wave's share of tile j landed; every wave finished tile j - 1
-      if constexpr (WQ > 1) barrier_only();
-      issue(std::integral_constant<int, (sti + NS - 1) % NS>{}, j + NS - 1);
-      if (j < Tg) compute(ST, j);
-    };
-    auto prologue = [&](auto P) __attribute__((always_inline)) { issue(P, decltype(P)::value); };
-    static_for<0, NS - 1>(prologue);
-    if (w0 == 0) load_q();
-    for (int j0 = 0; j0 < Tmax; j0 += NS) {
-      auto step = [&](auto P) __attribute__((always_inline)) {
-        if (j0 + decltype(P)::value < Tmax) iter(P, j0 + decltype(P)::value);
+    // One group tile j from stage ST: the next tile's K and this tile's V^T
+    // are read from LDS; the softmax of tile j runs on the vector unit while
+    // the matrix core computes S^T of tile j + 1 (into s_nxt), then
+    // O^T += V^T P^T. A wave issues in order and each S^T step depends on the
+    // previous one, so the exponentials are placed between the matrix
+    // instructions by hand (sched_barrier keeps the compiler from regrouping
+    // them):
+    //   K reads; mask, maximum; E0..E2 | S step ks, two V reads, E(3 + ks) |
+    //   O^T += V^T P^T for keys 0..15 with E11..E14 | E15, keys 16..31
+    // where E r = exponential and bf16 packing of score r. The row sum adds
+    // the packed probabilities (the values the product uses) by dot2.
+    auto compute = [&](auto FAST, auto ST, int j, f32x16_t& s_cur, f32x16_t& s_nxt) __attribute__((always_inline)) {
+      constexpr int st = decltype(ST)::value, sn = (st + 1) % NS;
+      u32x4_t kr[8];  // a stale stage after the last tile: the result is unused
+      kr[0] = lds_read16<sn * kStageBytes>(kaddr[0]);
+      kr[1] = lds_read16<sn * kStageBytes>(kaddr[1]);
+      kr[2] = lds_read16<sn * kStageBytes>(kaddr[2]);
+      kr[3] = lds_read16<sn * kStageBytes>(kaddr[3]);
+      kr[4] = lds_read16<sn * kStageBytes>(kaddr[4]);
+      kr[5] = lds_read16<sn * kStageBytes>(kaddr[5]);
+      kr[6] = lds_read16<sn * kStageBytes>(kaddr[6]);
+      kr[7] = lds_read16<sn * kStageBytes>(kaddr[7]);
+      if (!decltype(FAST)::value) mask(j, s_cur);
+      float mt = s_cur[0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mt = fmaxf(mt, s_cur[r]);
+      mt = pair_max(mt) * a.scale_log2;
+      const bool grow = mt > m_run + kRescaleSlack;
+      if (__any(grow)) {  // wave-uniform: rescale only when an offset moved
+        const float m_new = grow ? fmaxf(m_run, mt) : m_run;
+        const float alpha = m_new == m_run ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+        l_run *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) oacc[dt] *= alpha;
+        m_run = m_new;
+      }
+      const float neg_m = m_run == -INFINITY ? 0.f : -m_run;
+      float pe[16];
+      bf16x8_t pb[2];
+      auto E = [&](int r) __attribute__((always_inline)) {
+        pe[r] = __builtin_amdgcn_exp2f(fmaf(s_cur[r], a.scale_log2, neg_m));
+        if (r & 1) {
+          pb[r >> 3][(r & 7) - 1] = static_cast<__bf16>(pe[r - 1]);
+          pb[r >> 3][r & 7] = static_cast<__bf16>(pe[r]);
+        }
       };
-      static_for<0, NS>(step);
+      E(0);
+      E(1);
+      E(2);
+      __builtin_amdgcn_sched_barrier(0);
+      // the K operands have landed
+      asm volatile("s_waitcnt lgkmcnt(0)"
+                   : "+v"(kr[0]), "+v"(kr[1]), "+v"(kr[2]), "+v"(kr[3]), "+v"(kr[4]), "+v"(kr[5]), "+v"(kr[6]),
+                     "+v"(kr[7]));
+      // V^T of tile j: [kc][dt][t], keys 0..15 first
+      constexpr int vo = st * kStageBytes;
+      u32x2_t vr[2][4][2];
+      f32x16_t sn_acc;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sn_acc[r] = 0.f;
+      static_for<0, 8>([&](auto KS) __attribute__((always_inline)) {
+        constexpr int ks = decltype(KS)::value, kc = ks >> 2, dt = ks & 3;
+        sn_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kr[ks]), qreg[ks], sn_acc, 0, 0,
+                                                         0);
+        vr[kc][dt][0] = tr_read<vo + (16 * kc) * kD * 2>(vaddr[dt]);
+        vr[kc][dt][1] = tr_read<vo + (16 * kc + 8) * kD * 2>(vaddr[dt]);
+        E(3 + ks);
+        __builtin_amdgcn_sched_barrier(0);
+      });
+      s_nxt = sn_acc;
+      // the reads of keys 0..15 have landed (8 more after them)
+      asm volatile("s_waitcnt lgkmcnt(8)"
+                   : "+v"(vr[0][0][0]), "+v"(vr[0][0][1]), "+v"(vr[0][1][0]), "+v"(vr[0][1][1]),
+                     "+v"(vr[0][2][0]), "+v"(vr[0][2][1]), "+v"(vr[0][3][0]), "+v"(vr[0][3][1]));
+      const bf16x2_t ones = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
+      float ps = 0.f;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        const u32x4_t w = {vr[0][dt][0].x, vr[0][dt][0].y, vr[0][dt][1].x, vr[0][dt][1].y};
+        oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, w), pb[0], oacc[dt], 0, 0, 0);
+        E(11 + dt);
+        const bf16x2_t pp = {pb[0][2 * dt], pb[0][2 * dt + 1]};
+        ps = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, ps, false);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      E(15);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        // (built from the elements: a bit_cast of a lane of the packed vector
+        // is folded to its first lane by this compiler)
+        const bf16x2_t pp = {pb[1][2 * e], pb[1][2 * e + 1]};
+        ps = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, ps, false);
+      }
+      l_run += ps;
+      asm volatile("s_waitcnt lgkmcnt(0)"
+                   : "+v"(vr[1][0][0]), "+v"(vr[1][0][1]), "+v"(vr[1][1][0]), "+v"(vr[1][1][1]),
+                     "+v"(vr[1][2][0]), "+v"(vr[1][2][1]), "+v"(vr[1][3][0]), "+v"(vr[1][3][1]));
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        const u32x4_t w = {vr[1][dt][0].x, vr[1][dt][0].y, vr[1][dt][1].x, vr[1][dt][1].y};
+        oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, w), pb[1], oacc[dt], 0, 0, 0);
+      }
+    };
+
+    // iteration j (stage j % NS): every wave's share of tile j + 1 has
+    // landed and every wave is done with tile j - 1, whose stage takes tile
+    // j + NS - 1. FAST: tiles j .. j + NS - 1 are whole prefix tiles, so
+    // there is no mask, no tail test and the wait count is fixed.
+    auto iter = [&](auto FAST, auto ST, int j, f32x16_t& s_cur, f32x16_t& s_nxt) __attribute__((always_inline)) {
+      constexpr int st = decltype(ST)::value;
+      if (decltype(FAST)::value) {
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 3) * INS));
+      } else if (j + 1 < Tg) {
+        if (j + NS - 2 < Tg) __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 3) * INS));
+        else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+      }
+      barrier_only();
+      issue(FAST, std::integral_constant<int, (st + NS - 1) % NS>{}, j + NS - 1);
+      if (decltype(FAST)::value || j < Tg) compute(FAST, ST, j, s_cur, s_nxt);
+    };
+
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using I3 = std::integral_constant<int, 3>;
+    using Fast = std::integral_constant<bool, true>;
+    using Slow = std::integral_constant<bool, false>;
+    issue(Slow{}, I0{}, 0);
+    issue(Slow{}, I1{}, 1);
+    issue(Slow{}, I2{}, 2);
+    if (w0 == 0) {
+      load_q();
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // Q, and the first tiles
+    } else if (NS - 2 < Tg) {
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 2) * INS));
+    } else {
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    }
+    __syncthreads();  // tile 0 of every group (and the ancestor rows) in LDS
+    f32x16_t sa, sb;
+    if (Tg > 0) {
+      u32x4_t kr[8];
+      kr[0] = lds_read16<0>(kaddr[0]);
+      kr[1] = lds_read16<0>(kaddr[1]);
+      kr[2] = lds_read16<0>(kaddr[2]);
+      kr[3] = lds_read16<0>(kaddr[3]);
+      kr[4] = lds_read16<0>(kaddr[4]);
+      kr[5] = lds_read16<0>(kaddr[5]);
+      kr[6] = lds_read16<0>(kaddr[6]);
+      kr[7] = lds_read16<0>(kaddr[7]);
+      asm volatile("s_waitcnt lgkmcnt(0)"
+                   : "+v"(kr[0]), "+v"(kr[1]), "+v"(kr[2]), "+v"(kr[3]), "+v"(kr[4]), "+v"(kr[5]), "+v"(kr[6]),
+                     "+v"(kr[7]));
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sa[r] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks)
+        sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kr[ks]), qreg[ks], sa, 0, 0, 0);
+    }
+    // whole prefix tiles in groups of four, then the rest (tail, partial and
+    // tree tiles) one checked iteration at a time
+    const int jfast = max(0, Tfull - (NS - 1)) & ~3;
+    int j = 0;
+    for (; j < jfast; j += 4) {
+      iter(Fast{}, I0{}, j, sa, sb);
+      iter(Fast{}, I1{}, j + 1, sb, sa);
+      iter(Fast{}, I2{}, j + 2, sa, sb);
+      iter(Fast{}, I3{}, j + 3, sb, sa);
+    }
+    for (; j < Tmax; j += 4) {
+      iter(Slow{}, I0{}, j, sa, sb);
+      if (j + 1 < Tmax) iter(Slow{}, I1{}, j + 1, sb, sa);
+      if (j + 2 < Tmax) iter(Slow{}, I2{}, j + 2, sa, sb);
+      if (j + 3 < Tmax) iter(Slow{}, I3{}, j + 3, sb, sa);
     }
     if (last) break;
   }
 
   // column sums: each lane holds half of its column's keys
-#pragma unroll
-  for (int c = 0; c < QC; ++c) l_run[c] = pair_sum(l_run[c]);
+  l_run = pair_sum(l_run);
 
   if constexpr (WK > 1) {
     // key groups 1.. hand their states to group 0 through LDS (the stages
-    // are free once every wave is past its loop): O^T of a wave is QC * 16 KB
-    // and a stage object holds 16 WK KB
-    constexpr int kSlotFloats = QC * 4 * 16 * 64;
-    constexpr int per_obj = WK / QC;
-    static_assert(per_obj >= 1 && (WK - 1) * WQ <= NS * per_obj, "hand-over area");
-    auto xo_of = [&](int s) -> float* {
-      const int obj = s / per_obj;
-      float* base = obj == 0 ? reinterpret_cast<float*>(&st0[0][0][0])
-                  : obj == 1 ? reinterpret_cast<float*>(&st1[0][0][0])
-                  : obj == 2 ? reinterpret_cast<float*>(&st2[0][0][0])
-                             : reinterpret_cast<float*>(&st3[0][0][0]);
-      return base + (s % per_obj) * kSlotFloats;
-    };
-    float* xm = reinterpret_cast<float*>(&s_pages[0]);  // [2][WK - 1][WQ][QC][64]: m, then l
-    constexpr int kML = (WK - 1) * WQ * QC * 64;
-    static_assert(2 * kML <= kMaxWGPages, "m and l hand-over");
+    // are free once every wave is past its loop): O^T of a wave is 16 KB
+    constexpr int kSlotFloats = 4 * 16 * 64;
+    constexpr int kML = (WK - 1) * WQ * 64;
+    static_assert(((WK - 1) * WQ * kSlotFloats + 2 * kML) * 4 <= static_cast<int>(sizeof(stg)), "hand-over area");
+    float* xo0 = reinterpret_cast<float*>(&stg[0][0][0][0]);
+    float* xm = xo0 + (WK - 1) * WQ * kSlotFloats;  // [2][WK - 1][WQ][64]: m, then l
     __syncthreads();
     if (wk > 0) {
       const int slotw = (wk - 1) * WQ + wq;
-      float* xo = xo_of(slotw);
-#pragma unroll
-      for (int c = 0; c < QC; ++c) {
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) xo[(((c * 4 + dt) * 16 + r) << 6) + lane] = oacc[c][dt][r];
-        xm[((slotw * QC + c) << 6) + lane] = m_run[c];
-        xm[kML + ((slotw * QC + c) << 6) + lane] = l_run[c];
-      }
-    }
-    __syncthreads();
-    if (wk > 0) return;
-#pragma unroll
-    for (int c = 0; c < QC; ++c) {
-      float M = m_run[c];
-      for (int o = 1; o < WK; ++o) M = fmaxf(M, xm[((((o - 1) * WQ + wq) * QC + c) << 6) + lane]);
-      const float Mu = M == -INFINITY ? 0.f : M;
-      const float w0 = __builtin_amdgcn_exp2f(m_run[c] - Mu);
-      l_run[c] *= w0;
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt) oacc[c][dt] *= w0;
-      for (int o = 1; o < WK; ++o) {
-        const int slotw = (o - 1) * WQ + wq;
-        const float* xo = xo_of(slotw);
-        const float wo = __builtin_amdgcn_exp2f(xm[((slotw * QC + c) << 6) + lane] - Mu);
-        l_run[c] += wo * xm[kML + ((slotw * QC + c) << 6) + lane];
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[c][dt][r] += wo * xo[(((c * 4 + dt) * 16 + r) << 6) + lane];
-      }
-      m_run[c] = M;
-    }
-  }
-
-  // unnormalised partial of this split: rows (split, b, hkv, query)
-#pragma unroll
-  for (int c = 0; c < QC; ++c) {
-    const int qi = q0 + 32 * c + l32;
-    if (qi < a.NQ) {
-      const size_t row = (static_cast<size_t>(split * a.B + b) * a.Hkv + hkv) * a.NQpad + qi;
-      float* op = a.opart + row * kD + 4 * hl;
+      float* xo = xo0 + slotw * kSlotFloats;
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4)
-          *reinterpret_cast<float4*>(op + 32 * dt + 8 * r4) =
-              make_float4(oacc[c][dt][4 * r4], oacc[c][dt][4 * r4 + 1], oacc[c][dt][4 * r4 + 2],
-                          oacc[c][dt][4 * r4 + 3]);
-      if (hl == 0) {
-        a.mpart[row] = m_run[c];
-        a.lpart[row] = l_run[c];
-      }
+        for (int r = 0; r < 16; ++r) xo[((dt * 16 + r) << 6) + lane] = oacc[dt][r];
+      xm[(slotw << 6) + lane] = m_run;
+      xm[kML + (slotw << 6) + lane] = l_run;
+    }
+    __syncthreads();
+    if (wk > 0) return;
+    float M = m_run;
+    for (int o = 1; o < WK; ++o) M = fmaxf(M, xm[(((o - 1) * WQ + wq) << 6) + lane]);
+    const float Mu = M == -INFINITY ? 0.f : M;
+    const float w0 = __builtin_amdgcn_exp2f(m_run - Mu);
+    l_run *= w0;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) oacc[dt] *= w0;
+    for (int o = 1; o < WK; ++o) {
+      const int slotw = (o - 1) * WQ + wq;
+      const float* xo = xo0 + slotw * kSlotFloats;
+      const float wo = __builtin_amdgcn_exp2f(xm[(slotw << 6) + lane] - Mu);
+      l_run += wo * xm[kML + (slotw << 6) + lane];
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[dt][r] += wo * xo[((dt * 16 + r) << 6) + lane];
+    }
+    m_run = M;
+  }
+
+  // unnormalised partial of this split: rows (split, b, hkv, query)
+  const int qi = q0 + l32;
+  if (qi < a.NQ) {
+    const size_t row = (static_cast<size_t>(split * a.B + b) * a.Hkv + hkv) * a.NQpad + qi;
+    float* op = a.opart + row * kD + 4 * hl;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4)
+        *reinterpret_cast<float4*>(op + 32 * dt + 8 * r4) =
+            make_float4(oacc[dt][4 * r4], oacc[dt][4 * r4 + 1], oacc[dt][4 * r4 + 2], oacc[dt][4 * r4 + 3]);
+    if (hl == 0) {
+      a.mpart[row] = m_run;
+      a.lpart[row] = l_run;
     }
   }
 }
@@ -1096,29 +1160,23 @@ __global__ __launch_bounds__(64) void attn_simple(int B, int N, int Hq, int Hkv,
 
 
 struct TilePlan {
-  int qc, wq, wk, ns;  // 32-row query tiles per wave, waves along queries, key groups, stages
+  int wq, wk;  // waves along queries, key groups
   int S, QT, NQ, NQpad;
 };
 
-// Waves split the queries when a KV head has more than 64 query rows, else
-// the keys; splits aim at about one workgroup per CU (each at least four
-// tiles of the longest prefix, and short enough that its page ids fit the
-// LDS staging area). Each sequence cuts its own prefix into S equal ranges,
-// so the plan only sizes the work: any prefix_len up to the block table's
-// capacity is covered whatever max_prefix_len says.
+// Eight waves of 32 query rows: they split the queries when a KV head has
+// more than 128 query rows, else form two key groups of four. Splits aim at
+// about one workgroup per CU (each at least four tiles of the longest prefix,
+// and, where that allows, at most one 128-tile window). Each sequence cuts its
+// own prefix into S equal ranges, so the plan only sizes the work: any
+// prefix_len up to the block table's capacity is covered whatever
+// max_prefix_len says. (The tile kernel serves more than 64 query rows only.)
 TilePlan plan_tiles(int B, int N, int Hq, int Hkv, int max_prefix_len) {
   TilePlan p;
   p.NQ = N * (Hq / Hkv);
-  // eight waves of 32 query rows (two per SIMD)
-  p.qc = 1;
-  if (p.NQ <= 64) {
-    p.wq = 2, p.wk = 4, p.ns = 2;
-  } else if (p.NQ <= 128) {
-    p.wq = 4, p.wk = 2, p.ns = 4;
-  } else {
-    p.wq = 8, p.wk = 1, p.ns = 6;
-  }
-  const int qr = 32 * p.qc * p.wq;
+  if (p.NQ <= 128) p.wq = 4, p.wk = 2;
+  else p.wq = 8, p.wk = 1;
+  const int qr = 32 * p.wq;
   p.QT = (p.NQ + qr - 1) / qr;
   p.NQpad = p.QT * qr;
   const long long units = static_cast<long long>(B) * Hkv * p.QT;
@@ -1126,7 +1184,7 @@ TilePlan plan_tiles(int B, int N, int Hq, int Hkv, int max_prefix_len) {
   long long S = (256 + units / 2) / units;
   const long long smax = (Lr + 4 * kTK - 1) / (4 * kTK);
   if (S > smax) S = smax;
-  const long long smin = (Lr + (kMaxWGPages - 2) * 16 - 1) / ((kMaxWGPages - 2) * 16);
+  const long long smin = (Lr + 128 * kTK - 1) / (128 * kTK);
   if (S < smin) S = smin;
   if (S < 1) S = 1;
   p.S = static_cast<int>(S);
@@ -1272,9 +1330,8 @@ extern "C" int tree_attention_verify(int dtype, int B, int N, int Hq, int Hkv, i
   a.lpart = arena.take<float>(rows);
   const int grid = (a.nchunks + 7) / 8 * 8 * p.QT;
   const int nt = 64 * p.wq * p.wk;
-  if (p.wq == 2) attn_tile_mfma<1, 2, 4, 2><<<grid, nt, 0, stream>>>(a);
-  else if (p.wq == 4) attn_tile_mfma<1, 4, 2, 4><<<grid, nt, 0, stream>>>(a);
-  else attn_tile_mfma<1, 8, 1, 6><<<grid, nt, 0, stream>>>(a);
+  if (p.wq == 4) attn_tile_mfma<4, 2><<<grid, nt, 0, stream>>>(a);
+  else attn_tile_mfma<8, 1><<<grid, nt, 0, stream>>>(a);
   HY_LAUNCH_CHECK("tree_attention(tiles)");
   const long long cthreads = static_cast<long long>(B) * Hkv * p.NQ * (D / 4);
   attn_combine<bf16_t><<<static_cast<int>((cthreads + 255) / 256), 256, 0, stream>>>(

@@ -224,7 +224,7 @@ def commit_measure(w, rnd, dev, stream, layers=32, reps=20, use_graph=True):
 
     B, K = rnd.attn_out.shape[:2]
     dt = rnd.dtype
-    n_pages, _, ps, _ = dev["k_pages"].shape
+    n_pages, _, ps, _ = dev["k_pages"].shape[-4:]  # one layer's pool (target layers stack them)
     kt = torch.randn(layers, B, K, w.Hkv, w.D, device="cuda").to(dt)
     vt = torch.randn(layers, B, K, w.Hkv, w.D, device="cuda").to(dt)
     kp = torch.zeros(layers, n_pages, w.Hkv, ps, w.D, dtype=dt, device="cuda")
@@ -298,7 +298,10 @@ def layer_measure(w, rnd, dev, stream, reps=10, use_graph=True):
     code = 0 if dt == torch.float32 else 1
     ws = torch.empty(tree_decoder_layer_workspace_size(code, B, K, d, Hq, Hkv, D, F, mpl), dtype=torch.uint8,
                      device="cuda")
-    launch = lambda i: tree_decoder_layer(x, sets[i % 2], Hq, Hkv, dev["k_pages"], dev["v_pages"],  # noqa: E731
+    kp, vp = dev["k_pages"], dev["v_pages"]
+    if kp.dim() == 5:  # one pool per target layer: the first layer's
+        kp, vp = kp[0], vp[0]
+    launch = lambda i: tree_decoder_layer(x, sets[i % 2], Hq, Hkv, kp, vp,  # noqa: E731
                                           dev["block_table"], dev["prefix_len"], mpl, rnd.anc, rnd.depth, out, kt,
                                           vt, ws)
     launch(0)
@@ -537,12 +540,15 @@ def main():
         ev[1].record(stream)
         rnd.build()
         ev[2].record(stream)
-        rnd.attend(dev["q"], dev["k_tree"], dev["v_tree"], dev["k_pages"], dev["v_pages"], dev["block_table"],
-                   dev["prefix_len"])
+        if rnd.target is not None:  # the target's layers over the tree tokens
+            rnd.verify(dev["k_pages"], dev["v_pages"], dev["block_table"], dev["prefix_len"])
+        else:
+            rnd.attend(dev["q"], dev["k_tree"], dev["v_tree"], dev["k_pages"], dev["v_pages"], dev["block_table"],
+                       dev["prefix_len"])
         ev[3].record(stream)
         rnd.accept(dev.get("u_acc"), dev.get("u_res"))
         ev[4].record(stream)
-        rnd.commit(dev["k_tree"], dev["v_tree"], dev["k_pages"], dev["v_pages"], dev["block_table"],
+        rnd.commit(dev.get("k_tree"), dev.get("v_tree"), dev["k_pages"], dev["v_pages"], dev["block_table"],
                    dev["prefix_len"])
         ev[5].record(stream)
         torch.cuda.synchronize()
@@ -645,7 +651,8 @@ def main():
         "round_ms": round_ms,
         "round_bytes": rbytes,
         "round_hbm_frac": rbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-        "stages_ms": {"draft": stage_ms[0], "build": stage_ms[1], "attention": stage_ms[2],
+        "stages_ms": {"draft": stage_ms[0], "build": stage_ms[1],
+                      ("target_layers" if rnd.target is not None else "attention"): stage_ms[2],
                       "accept": stage_ms[3], "commit": stage_ms[4]},
         "commit_32_layers": commit,
         "decoder_layer": layer,

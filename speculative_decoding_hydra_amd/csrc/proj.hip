@@ -67,8 +67,15 @@ __global__ __launch_bounds__(64 * WV) void proj_bf16_kernel(ProjArgs a) {
   const int n_base = a.glu_F > 0 ? (wave < 2 ? 32 * static_cast<int>(blockIdx.x) + 16 * wave
                                              : a.glu_F + 32 * static_cast<int>(blockIdx.x) + 16 * (wave - 2))
                                  : static_cast<int>(blockIdx.x) * RPW + wave * 16;
-  const int k_begin = blockIdx.y * a.kper;
-  const int k_end = REM && k_begin + a.kper > a.K ? a.K : k_begin + a.kper;  // REM: the last split may be short
+  int k_begin, k_end;
+  if (a.kper > 0) {
+    k_begin = blockIdx.y * a.kper;
+    k_end = REM && k_begin + a.kper > a.K ? a.K : k_begin + a.kper;  // REM: the last split may be short
+  } else {  // balanced: -kper splits of whole chunks, sizes differing by at most one chunk
+    const int nsp = -a.kper, nch = a.K / KC;
+    k_begin = static_cast<int>(static_cast<long>(blockIdx.y) * nch / nsp) * KC;
+    k_end = static_cast<int>(static_cast<long>(blockIdx.y + 1) * nch / nsp) * KC;
+  }
   const int K0 = xs.mode == 0 ? K : xs.d;
   if (TOPK && a.tp.clear && blockIdx.x == 0 && blockIdx.y == 0 && tid < a.tp.nclear) a.tp.clear[tid] = 0;
 
@@ -135,11 +142,12 @@ __global__ __launch_bounds__(64 * WV) void proj_bf16_kernel(ProjArgs a) {
     xbuf[v] = *reinterpret_cast<const u32x4_t*>((k_begin < K0 ? xp0[v] : xp1[v]) + k_begin);
 
   const int k_last = k_end - KC;  // past-the-end prefetches re-read the last chunk
-  for (int kc0 = k_begin; kc0 < k_end; kc0 += PF * KC) {
+  // whole groups of PF chunks
+  const int k_main = REM ? k_begin + (k_end - k_begin) / (PF * KC) * (PF * KC) : k_end;
+  for (int kc0 = k_begin; kc0 < k_main; kc0 += PF * KC) {
 #pragma unroll
     for (int p = 0; p < PF; ++p) {
       const int kc = kc0 + p * KC;
-      if (REM && kc >= k_end) continue;  // uniform over the workgroup
       __syncthreads();
 #pragma unroll
       for (int v = 0; v < XV; ++v) *reinterpret_cast<u32x4_t*>(&xlds[xo[v]]) = xbuf[v];
@@ -170,6 +178,47 @@ __global__ __launch_bounds__(64 * WV) void proj_bf16_kernel(ProjArgs a) {
                                                           0, 0, 0);
       }
     }
+  }
+  if constexpr (REM) {
+    // REM: up to PF - 1 chunks after the whole groups, their W already in
+    // wbuf[0 ..]; the same steps as one pass of the loop above (kept out of
+    // the loop, whose body carries no branch: a branch around the chunk there
+    // costs about 18% at K = 11008, and a lambda shared with the loop made
+    // the compiler drain every load at the loop's back edge)
+    auto chunk = [&](const int p, const int kc) __attribute__((always_inline)) {
+      __syncthreads();
+#pragma unroll
+      for (int v = 0; v < XV; ++v) *reinterpret_cast<u32x4_t*>(&xlds[xo[v]]) = xbuf[v];
+      __syncthreads();
+      const int kx = kc < k_last ? kc + KC : kc;
+#pragma unroll
+      for (int v = 0; v < XV; ++v)
+        xbuf[v] = *reinterpret_cast<const u32x4_t*>((kx < K0 ? xp0[v] : xp1[v]) + kx);
+      const int kn = kc + PF * KC <= k_last ? kc + PF * KC : k_last;
+      // B operands double-buffered: step s + 1's LDS reads are in flight
+      // while step s's MFMAs run
+      const bf16_t* xrow = &xlds[(lane & 15) * LDS_ROW + (lane >> 4) * 8];
+      u32x4_t bq[2][MT];
+#pragma unroll
+      for (int t = 0; t < MT; ++t) bq[0][t] = *reinterpret_cast<const u32x4_t*>(xrow + t * 16 * LDS_ROW);
+#pragma unroll
+      for (int s = 0; s < STEPS; ++s) {
+        if (s + 1 < STEPS) {
+#pragma unroll
+          for (int t = 0; t < MT; ++t)
+            bq[(s + 1) & 1][t] = *reinterpret_cast<const u32x4_t*>(xrow + t * 16 * LDS_ROW + (s + 1) * 32);
+        }
+        const bf16x8_t av = __builtin_bit_cast(bf16x8_t, wbuf[p][s]);
+        wbuf[p][s] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(wat(kn + s * 32)));
+#pragma unroll
+        for (int t = 0; t < MT; ++t)
+          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8_t, bq[s & 1][t]), acc[t],
+                                                          0, 0, 0);
+      }
+    };
+#pragma unroll
+    for (int p = 0; p + 1 < PF; ++p)
+      if (k_main + p * KC < k_end) chunk(p, k_main + p * KC);
   }
 
   if (!SPLIT && !TOPK && WV == 4 && a.glu_F > 0) {
@@ -357,12 +406,24 @@ template <int MT, bool TOPK>
 int launch_bf16(const ProjArgs& a, int nsplit, hipStream_t stream) {
   constexpr int KC = MT <= 4 ? 256 : (MT <= 8 ? 128 : 64);
   constexpr int PF = MT <= 4 ? 2 : (MT <= 8 ? 4 : 8);
-  const bool ragged = a.K % a.kper != 0;  // split K with a shorter last range
-  if (!ragged && a.kper % (PF * KC) == 0) {
+  // the shortest K range of a workgroup, and whether every range is a whole
+  // number of PF-chunk groups
+  int kmin;
+  bool whole;
+  if (a.kper > 0) {
+    kmin = std::min(a.kper, a.K - (nsplit - 1) * a.kper);
+    whole = a.K % a.kper == 0 && a.kper % (PF * KC) == 0;
+  } else {  // balanced split ranges
+    const int nch = a.K / KC, ns = -a.kper;
+    kmin = nch / ns * KC;
+    whole = nch % ns == 0 && (nch / ns) % PF == 0;
+  }
+  const bool ragged = a.kper > 0 ? a.K % a.kper != 0 : (a.K / KC) % -a.kper != 0;
+  if (whole) {
     launch_bf16_pf<MT, PF, TOPK>(a, nsplit, stream);
-  } else if (a.kper > PF * KC) {
+  } else if (kmin > PF * KC) {
     launch_bf16_pf<MT, PF, TOPK, true>(a, nsplit, stream);  // e.g. K = 11008: 43 chunks of 256
-  } else if (ragged) {
+  } else if (ragged || kmin % KC != 0) {
     launch_bf16_pf<MT, 1, TOPK, true>(a, nsplit, stream);
   } else {
     launch_bf16_pf<MT, 1, TOPK>(a, nsplit, stream);  // K range of 256 .. PF*KC-256
@@ -466,15 +527,21 @@ int launch_projection_parts(int dtype, int M, int K, int N, const void* X, const
   // workgroup per CU, each K range a multiple of 256 (measured on MI355X:
   // the 7B decoder layer takes 177 us with 256 workgroups, 188 with 512 and
   // 190 with 1024; the 70B layer is the same for all three)
+  // (measured on MI355X at 64 rows, where every workgroup also stages a
+  // 64-row X chunk per weight chunk: a CU holding two workgroups of a launch
+  // gains nothing, so the count is rounded down: the 7B Q/K/V product takes
+  // 24.7 us in 192 workgroups, 26.9 in 384; at 16 rows and fewer it is
+  // rounded up)
   const int wg = (N + 63) / 64 * ((M + 255) / 256);
-  int ns = std::max(1, std::min({cap, 16, (256 + wg - 1) / wg, K / 256}));
-  const int kper = (K / 256 + ns - 1) / ns * 256;
-  ns = (K + kper - 1) / kper;
+  const int per_cu = M > 32 ? std::max(1, 256 / wg) : (256 + wg - 1) / wg;
+  const int ns = std::max(1, std::min({cap, 16, per_cu, K / 256}));
   *nsplit = ns;
   if (ns == 1)
     return launch_projection(dtype | (wpacked ? HYDRA_VOCAB_PACKED : 0), M, K, N, xs, W, part, RowMap{M, 0, 0}, N,
                              1, nullptr, TopkPartials{nullptr, nullptr}, stream);
-  ProjArgs a{M, K, N, xs, static_cast<const bf16_t*>(W), nullptr, RowMap{M, 0, 0}, N, kper, 0, part,
+  // split s takes chunks [s * nch / ns, (s + 1) * nch / ns) of the nch
+  // 256-column chunks of K (a negative kper asks the kernel for this)
+  ProjArgs a{M, K, N, xs, static_cast<const bf16_t*>(W), nullptr, RowMap{M, 0, 0}, N, -ns, 0, part,
              TopkPartials{nullptr, nullptr}, wpacked, 0, nullptr};
   for (int m0 = 0; m0 < M; m0 += 256) {
     const int mc = M - m0 < 256 ? M - m0 : 256;

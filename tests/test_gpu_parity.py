@@ -1065,6 +1065,10 @@ def _close(got, ref, dtype, what, stream=False):
     ("bf16", 2, ("cartesian", [2, 3]), 256, 8, 2, 32, 512, [5, 40], 2),
     ("bf16", 3, ("cartesian", [3, 2, 2]), 512, 4, 4, 128, 1024, [0, 17, 300], 1),
     ("bf16", 1, ("sparse", (10, 4, 2, 1), 64), 4096, 32, 32, 128, 11008, [2048], 1),
+    # head dim 128 at up to 16 and up to 32 rows (one- and two-tile row
+    # shapes of the streaming products; GQA in the first)
+    ("bf16", 1, ("cartesian", [2, 2]), 512, 4, 2, 128, 1024, [33], 2),
+    ("bf16", 2, ("cartesian", [3, 4]), 512, 8, 8, 128, 1024, [64, 1000], 1),
 ])
 def test_tree_decoder_layer(dtype, B, tree, d, Hq, Hkv, D, F, lens, layers):
     """Decoder layers over the tree rows (each with its own weights and paged

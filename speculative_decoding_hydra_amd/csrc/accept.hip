@@ -42,6 +42,7 @@ __global__ __launch_bounds__(64) void greedy_walk(int N, int Dmax, const int32_t
 constexpr int kWalkThreads = 1024;
 constexpr int kWalkWaves = kWalkThreads / 64;
 
+template <int NW = kWalkWaves>
 __device__ double block_sum_d(double v, double* red) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
@@ -50,10 +51,11 @@ __device__ double block_sum_d(double v, double* red) {
   if (lane == 0) red[wave] = v;
   __syncthreads();
   double t = 0.0;
-  for (int w = 0; w < kWalkWaves; ++w) t += red[w];
+  for (int w = 0; w < NW; ++w) t += red[w];
   return t;
 }
 
+template <int NW = kWalkWaves>
 __device__ float block_max_f(float v, float* red) {
   v = wave_max(v);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -61,7 +63,7 @@ __device__ float block_max_f(float v, float* red) {
   if (lane == 0) red[wave] = v;
   __syncthreads();
   float t = -INFINITY;
-  for (int w = 0; w < kWalkWaves; ++w) t = fmaxf(t, red[w]);
+  for (int w = 0; w < NW; ++w) t = fmaxf(t, red[w]);
   return t;
 }
 
@@ -382,13 +384,17 @@ __global__ __launch_bounds__(kWalkThreads) void typical_walk(int N, int V, int D
 }
 
 // ---------------------------------------------------------------------------
-// Register-resident rows (V <= EPT * kWalkThreads). The walks above stream a
-// logits row from memory on every pass (maximum, sum, residual, draw), one
-// load per thread at a time, so each pass costs tens of memory round trips.
-// Here a row is loaded once, with all of a thread's loads in flight together:
-// element x = i * kWalkThreads + tid sits in register i of thread tid, so
-// every load is coalesced, and the passes run on registers. The arithmetic is
-// the same as above, value for value.
+// Register-resident rows (V <= EPT * NT for a launch of NT threads). The walks
+// above stream a logits row from memory on every pass (maximum, sum,
+// residual, draw), one load per thread at a time, so each pass costs tens of
+// memory round trips. Here a row is loaded once, with all of a thread's loads
+// in flight together: element x = i * NT + tid sits in register i of thread
+// tid, so every load is coalesced, and the passes run on registers. The steps
+// are the walks' own; the float partial sums group the elements by thread of
+// the launch (float per thread and wave, float64 across waves).
+
+constexpr int kNodeThreads = 512;  // node kernels: two rows of up to 64 registers each without spilling
+constexpr int kNodeWaves = kNodeThreads / 64;
 
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -406,14 +412,15 @@ __device__ __forceinline__ float wave_sum_dpp(float v) {
   return __uint_as_float(c[0]) + __uint_as_float(c[1]);
 }
 
-// block sum: float within each wave (DPP), float64 across the waves
+// block sum: float within each wave (DPP), float64 across the NW waves
+template <int NW>
 __device__ __forceinline__ double block_sum_fd(float v, double* red) {
   v = wave_sum_dpp(v);
   __syncthreads();
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
   __syncthreads();
   double t = 0.0;
-  for (int w = 0; w < kWalkWaves; ++w) t += red[w];
+  for (int w = 0; w < NW; ++w) t += red[w];
   return t;
 }
 
@@ -421,7 +428,7 @@ __device__ __forceinline__ double block_sum_fd(float v, double* red) {
 // row `row` of the [rows][V] float matrix z; buffer loads share one lane
 // offset (register i adds i * 4 KB as a scalar offset), so all EPT loads are
 // in flight at once without a 64-bit address per load
-template <int EPT>
+template <int EPT, int NT>
 __device__ __forceinline__ void reg_load_scaled(float (&v)[EPT], const float* __restrict__ z, size_t row, int V,
                                                 float invT) {
   const size_t r = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(row));
@@ -430,39 +437,39 @@ __device__ __forceinline__ void reg_load_scaled(float (&v)[EPT], const float* __
   const int lane_off = static_cast<int>(threadIdx.x) * 4;
 #pragma unroll
   for (int i = 0; i < EPT; ++i)
-    v[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, lane_off, i * kWalkThreads * 4, 0));
+    v[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, lane_off, i * NT * 4, 0));
 #pragma unroll
   for (int i = 0; i < EPT; ++i) {
-    const int x = i * kWalkThreads + static_cast<int>(threadIdx.x);
+    const int x = i * NT + static_cast<int>(threadIdx.x);
     v[i] = x < V ? v[i] * invT : -INFINITY;  // past V the buffer returns 0
   }
 }
 
 // v <- exp(v - max v) (0 past V); returns the block sum in float64
-template <int EPT>
+template <int EPT, int NT>
 __device__ __forceinline__ double reg_exp(float (&v)[EPT], double* red, float* redf) {
   float mx = -INFINITY;
 #pragma unroll
   for (int i = 0; i < EPT; ++i) mx = fmaxf(mx, v[i]);
-  const float M = block_max_f(mx, redf);
+  const float M = block_max_f<NT / 64>(mx, redf);
   float s = 0.f;
 #pragma unroll
   for (int i = 0; i < EPT; ++i) {
     v[i] = v[i] == -INFINITY ? 0.f : exp2f((v[i] - M) * kLog2e);
     s += v[i];
   }
-  return block_sum_fd(s, red);
+  return block_sum_fd<NT / 64>(s, red);
 }
 
 // a[x] and b[x] for one token x < V, broadcast to the whole block
-template <int EPT>
+template <int EPT, int NT>
 __device__ __forceinline__ float2 reg_at2(const float (&a)[EPT], const float (&b)[EPT], int x, float2* s_bc) {
   __syncthreads();
-  if (static_cast<int>(threadIdx.x) == x % kWalkThreads) {
+  if (static_cast<int>(threadIdx.x) == x % NT) {
     float2 t = make_float2(0.f, 0.f);
 #pragma unroll
     for (int i = 0; i < EPT; ++i)
-      if (i == x / kWalkThreads) t = make_float2(a[i], b[i]);
+      if (i == x / NT) t = make_float2(a[i], b[i]);
     *s_bc = t;
   }
   __syncthreads();
@@ -471,11 +478,11 @@ __device__ __forceinline__ float2 reg_at2(const float (&a)[EPT], const float (&b
 
 // Inverse-CDF draw over the unnormalised r held in registers: the smallest x
 // with sum_{y <= x} r(y) > u * sum r. Tile i (register i of every thread,
-// ids i * kWalkThreads ...) is located from the tile sums (float per wave,
+// ids i * NT ...) is located from the tile sums (float per wave,
 // float64 across waves), then one float64 block scan inside it finds x; if
 // rounding between the two leaves no crossing there, the tile's last x with
 // r > 0 is taken. s_pick holds 3 ints.
-template <int EPT>
+template <int EPT, int NT>
 __device__ int reg_sample(const float (&r)[EPT], float u, double* s_tile, double* red, int* s_pick) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   __shared__ double s_thr, s_before;
@@ -486,7 +493,7 @@ __device__ int reg_sample(const float (&r)[EPT], float u, double* s_tile, double
   for (int i = 0; i < EPT; ++i) {
     const float t = wave_sum_dpp(r[i]);  // locates the tile only; the scan inside it is float64
     if (lane == 0) s_tile[wave * EPT + i] = t;
-    if (r[i] > 0.f) lastpos = i * kWalkThreads + tid;
+    if (r[i] > 0.f) lastpos = i * NT + tid;
   }
   if (tid == 0) {
     s_pick[0] = -1;
@@ -497,7 +504,7 @@ __device__ int reg_sample(const float (&r)[EPT], float u, double* s_tile, double
   if (lastpos >= 0) atomicMax(&s_pick[1], lastpos);
   if (tid < EPT) {
     double t = 0.0;
-    for (int w = 0; w < kWalkWaves; ++w) t += s_tile[w * EPT + tid];
+    for (int w = 0; w < (NT / 64); ++w) t += s_tile[w * EPT + tid];
     s_tsum[tid] = t;
   }
   __syncthreads();
@@ -537,8 +544,8 @@ __device__ int reg_sample(const float (&r)[EPT], float u, double* s_tile, double
     for (int w = 0; w < wave; ++w) woff += red[w];
     const double incl = woff + inc, excl = incl - val;
     const double thr = s_thr;
-    if (val > 0.f && excl <= thr && thr < incl) s_pick[0] = it * kWalkThreads + tid;
-    if (val > 0.f) atomicMax(&s_pick[2], it * kWalkThreads + tid);
+    if (val > 0.f && excl <= thr && thr < incl) s_pick[0] = it * NT + tid;
+    if (val > 0.f) atomicMax(&s_pick[2], it * NT + tid);
   }
   __syncthreads();
   // no crossing: u * total beyond the last tile (the last x with r > 0), or
@@ -570,17 +577,18 @@ __device__ __forceinline__ void load_parents(const int32_t* __restrict__ parent,
 // inverse-CDF draw from the residual (from p when u has no children or sits
 // at depth Dmax)
 template <int EPT>
-__global__ __launch_bounds__(kWalkThreads) void reject_node_reg(
+__global__ __launch_bounds__(kNodeThreads) void reject_node_reg(
     int N, int V, int R, int Dmax, float invT, const float* __restrict__ Z, const float* __restrict__ HZ,
     const int32_t* __restrict__ tok, const int32_t* __restrict__ parent, const int32_t* __restrict__ q_row,
     const float* __restrict__ u_acc, const float* __restrict__ u_res, int32_t* __restrict__ next,
     int32_t* __restrict__ draw) {
-  __shared__ double red[kWalkWaves];
-  __shared__ float redf[kWalkWaves];
-  __shared__ double s_tile[kWalkWaves * EPT];
+  __shared__ double red[kNodeWaves];
+  __shared__ float redf[kNodeWaves];
+  __shared__ double s_tile[kNodeWaves * EPT];
   __shared__ int s_pick[3];
   __shared__ int s_kid[3];
   __shared__ float2 s_bc;
+  __shared__ float3 s_next[2];
   __shared__ int s_par[HYDRA_MAX_VERIFY];
   const int b = blockIdx.x / N, u = blockIdx.x % N, tid = threadIdx.x;
   const size_t row = static_cast<size_t>(b) * N + u;
@@ -597,33 +605,46 @@ __global__ __launch_bounds__(kWalkThreads) void reject_node_reg(
     s_kid[2] = d;
   }
   __syncthreads();
-  for (int c = tid; c < N; c += kWalkThreads)
+  for (int c = tid; c < N; c += kNodeThreads)
     if (s_par[c] == u) {
       atomicMin(&s_kid[0], c);
       atomicAdd(&s_kid[1], 1);
     }
-  float r[EPT], q[EPT];
-  reg_load_scaled(r, Z, row, V, invT);
-  double total = reg_exp(r, red, redf);  // its barriers also publish s_kid
+  __syncthreads();
   const int c0 = s_kid[0], cnt = s_kid[1], depth = s_kid[2];
-  int taken = -1;
-  if (cnt > 0 && depth < Dmax) {
+  const bool tries = cnt > 0 && depth < Dmax;
+  // both rows in flight together: the target's, and the head row that
+  // drafted u's children when there are children to try
+  float r[EPT], q[EPT];
+  reg_load_scaled<EPT, kNodeThreads>(r, Z, row, V, invT);
+  if (tries) {
     const int qr = q_row[row];
-    reg_load_scaled(q, HZ, static_cast<size_t>(b) * R + (qr < 0 ? 0 : (qr >= R ? R - 1 : qr)), V, invT);
-    const float qinv = static_cast<float>(1.0 / reg_exp(q, red, redf));
+    const size_t hrow = static_cast<size_t>(b) * R + (qr < 0 ? 0 : (qr >= R ? R - 1 : qr));
+    reg_load_scaled<EPT, kNodeThreads>(q, HZ, hrow, V, invT);
+  }
+  double total = reg_exp<EPT, kNodeThreads>(r, red, redf);
+  int taken = -1;
+  if (tries) {
+    const float qinv = static_cast<float>(1.0 / reg_exp<EPT, kNodeThreads>(q, red, redf));
 #pragma unroll
     for (int i = 0; i < EPT; ++i) q[i] *= qinv;
+    auto child_tok = [&](int c) {
+      const int x = tok[static_cast<size_t>(b) * N + c];
+      return x < 0 ? 0 : (x >= V ? V - 1 : x);
+    };
+    float2 rq = reg_at2<EPT, kNodeThreads>(r, q, child_tok(c0), &s_bc);
     for (int j = 0; j < cnt; ++j) {
       const int c = c0 + j;
-      int x = tok[static_cast<size_t>(b) * N + c];
-      x = x < 0 ? 0 : (x >= V ? V - 1 : x);
-      const float2 rq = reg_at2(r, q, x, &s_bc);
       const float rx = static_cast<float>(rq.x / total);
       if (u_acc[static_cast<size_t>(b) * N + c] * rq.y < rx) {
         taken = c;
         break;
       }
-      // residual norm(max(r - q, 0)), kept unless it has no mass
+      // residual norm(max(r - q, 0)), kept unless it has no mass; the
+      // thread holding the next child's token posts that token's r before
+      // and after the update and its q, so the sum's barriers also publish
+      // the next lookup (two slots, alternating: a slot is rewritten only
+      // after every thread has passed the barriers that follow its read)
       const float rinv = static_cast<float>(1.0 / total);
       float nsf = 0.f;
 #pragma unroll
@@ -632,16 +653,31 @@ __global__ __launch_bounds__(kWalkThreads) void reject_node_reg(
         asm volatile("" : "+v"(t));  // recomputed below rather than kept: the rows fill the registers
         nsf += t;
       }
-      const double ns = block_sum_fd(nsf, red);
+      const bool more = j + 1 < cnt;
+      if (more) {
+        const int xn = child_tok(c + 1);
+        if (static_cast<int>(threadIdx.x) == xn % kNodeThreads) {
+          float3 t = make_float3(0.f, 0.f, 0.f);
+#pragma unroll
+          for (int i = 0; i < EPT; ++i)
+            if (i == xn / kNodeThreads) t = make_float3(r[i], fmaxf(r[i] * rinv - q[i], 0.f), q[i]);
+          s_next[j & 1] = t;
+        }
+      }
+      const double ns = block_sum_fd<kNodeWaves>(nsf, red);
       if (ns > 0.0) {
 #pragma unroll
         for (int i = 0; i < EPT; ++i) r[i] = fmaxf(r[i] * rinv - q[i], 0.f);
         total = ns;
       }
+      if (more) {
+        const float3 t = s_next[j & 1];
+        rq = make_float2(ns > 0.0 ? t.y : t.x, t.z);
+      }
     }
   }
   int x = -1;
-  if (taken < 0) x = reg_sample(r, u_res[row], s_tile, red, s_pick);
+  if (taken < 0) x = reg_sample<EPT, kNodeThreads>(r, u_res[row], s_tile, red, s_pick);
   if (tid == 0) {
     next[row] = taken;
     draw[row] = x;
@@ -652,17 +688,17 @@ __global__ __launch_bounds__(kWalkThreads) void reject_node_reg(
 // draw[b, u], the inverse-CDF draw from p at u (used if the kept branch ends
 // there)
 template <int EPT>
-__global__ __launch_bounds__(kWalkThreads) void typical_node_reg(int N, int V, float invT, float log_eps,
+__global__ __launch_bounds__(kNodeThreads) void typical_node_reg(int N, int V, float invT, float log_eps,
                                                                  float log_delta, const float* __restrict__ Z,
                                                                  const int32_t* __restrict__ tok,
                                                                  const int32_t* __restrict__ parent,
                                                                  const float* __restrict__ u_res,
                                                                  int32_t* __restrict__ pass,
                                                                  int32_t* __restrict__ draw) {
-  __shared__ double red[kWalkWaves];
-  __shared__ float redf[kWalkWaves];
-  __shared__ double s_tile[kWalkWaves * EPT];
-  __shared__ double s_w[kWalkWaves];
+  __shared__ double red[kNodeWaves];
+  __shared__ float redf[kNodeWaves];
+  __shared__ double s_tile[kNodeWaves * EPT];
+  __shared__ double s_w[kNodeWaves];
   __shared__ int s_pick[3];
   __shared__ int s_kid[2];
   const int b = blockIdx.x / N, u = blockIdx.x % N, tid = threadIdx.x;
@@ -673,17 +709,17 @@ __global__ __launch_bounds__(kWalkThreads) void typical_node_reg(int N, int V, f
     if (u == 0) pass[static_cast<size_t>(b) * N] = 1;  // the root
   }
   __syncthreads();
-  for (int c = tid; c < N; c += kWalkThreads)
+  for (int c = tid; c < N; c += kNodeThreads)
     if (parent[static_cast<size_t>(b) * N + c] == u) {
       atomicMin(&s_kid[0], c);
       atomicAdd(&s_kid[1], 1);
     }
   float r[EPT];
-  reg_load_scaled(r, Z, row, V, invT);
+  reg_load_scaled<EPT, kNodeThreads>(r, Z, row, V, invT);
   float mx = -INFINITY;
 #pragma unroll
   for (int i = 0; i < EPT; ++i) mx = fmaxf(mx, r[i]);
-  const float M = block_max_f(mx, redf);
+  const float M = block_max_f<kNodeWaves>(mx, redf);
   float Sf = 0.f, Wf = 0.f;
 #pragma unroll
   for (int i = 0; i < EPT; ++i) {
@@ -693,21 +729,21 @@ __global__ __launch_bounds__(kWalkThreads) void typical_node_reg(int N, int V, f
     Wf += r[i] == -INFINITY ? 0.f : e * t;
     r[i] = e;
   }
-  const double S = block_sum_d(Sf, red);
+  const double S = block_sum_d<kNodeWaves>(Sf, red);
   double Wd = Wf;
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) Wd += __shfl_xor(Wd, off, 64);
   if ((tid & 63) == 0) s_w[tid >> 6] = Wd;
   __syncthreads();
   double W = 0.0;
-  for (int w = 0; w < kWalkWaves; ++w) W += s_w[w];
+  for (int w = 0; w < kNodeWaves; ++w) W += s_w[w];
   const int c0 = s_kid[0], cnt = s_kid[1];
   if (cnt > 0) {
     const double logS = log(S);
     const double H = logS - W / S;
     const double log_tau = fmin(static_cast<double>(log_eps), static_cast<double>(log_delta) - H);
     const float* zu = Z + row * V;
-    for (int j = tid; j < cnt; j += kWalkThreads) {
+    for (int j = tid; j < cnt; j += kNodeThreads) {
       const int c = c0 + j;
       const int x = tok[static_cast<size_t>(b) * N + c];
       const bool ok = x >= 0 && x < V &&
@@ -715,7 +751,7 @@ __global__ __launch_bounds__(kWalkThreads) void typical_node_reg(int N, int V, f
       pass[static_cast<size_t>(b) * N + c] = ok ? 1 : 0;
     }
   }
-  const int x = reg_sample(r, u_res[row], s_tile, red, s_pick);
+  const int x = reg_sample<EPT, kNodeThreads>(r, u_res[row], s_tile, red, s_pick);
   if (tid == 0) draw[row] = x;
 }
 
@@ -810,9 +846,11 @@ __global__ __launch_bounds__(256) void typical_pick(int N, int Dmax, const int32
 }
 
 // register tiles per thread for a vocabulary of V, or 0 past 32 (streamed walks)
+// registers per row and thread of the node kernels, 0 when the row does not
+// fit (then the streaming walks run)
 int walk_ept(int V) {
-  const int e = (V + kWalkThreads - 1) / kWalkThreads;
-  for (int t = 1; t <= 32; t *= 2)
+  const int e = (V + kNodeThreads - 1) / kNodeThreads;
+  for (int t = 1; t <= 64; t *= 2)
     if (e <= t) return t;
   return 0;
 }
@@ -825,7 +863,8 @@ void with_ept(int ept, F f) {
     case 4: f(std::integral_constant<int, 4>{}); break;
     case 8: f(std::integral_constant<int, 8>{}); break;
     case 16: f(std::integral_constant<int, 16>{}); break;
-    default: f(std::integral_constant<int, 32>{}); break;
+    case 32: f(std::integral_constant<int, 32>{}); break;
+    default: f(std::integral_constant<int, 64>{}); break;
   }
 }
 
@@ -935,7 +974,7 @@ extern "C" int tree_accept(int dtype, int mode, int B, int N, int d, int V, int 
     const float invT = 1.0f / temperature;
     if (const int ept = walk_ept(V)) {
       with_ept(ept, [&](auto e) {
-        typical_node_reg<decltype(e)::value><<<M, kWalkThreads, 0, stream>>>(
+        typical_node_reg<decltype(e)::value><<<M, kNodeThreads, 0, stream>>>(
             N, V, invT, logf(eps), logf(delta), target_logits, tok, parent, u_res, pass, drawn);
       });
       HY_LAUNCH_CHECK("tree_accept: typical nodes");
@@ -959,7 +998,7 @@ extern "C" int tree_accept(int dtype, int mode, int B, int N, int d, int V, int 
     const float invT = 1.0f / temperature;
     if (const int ept = walk_ept(V)) {
       with_ept(ept, [&](auto e) {
-        reject_node_reg<decltype(e)::value><<<M, kWalkThreads, 0, stream>>>(
+        reject_node_reg<decltype(e)::value><<<M, kNodeThreads, 0, stream>>>(
             N, V, R, Dmax, invT, target_logits, head_logits, tok, parent, q_row, u_acc, u_res, nxt, drawn);
       });
       HY_LAUNCH_CHECK("tree_accept: rejection nodes");

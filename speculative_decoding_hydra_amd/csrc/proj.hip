@@ -35,10 +35,11 @@ struct ProjArgs {
   float* part;
   TopkPartials tp;
   int wpacked;  // W in the packed layout (packed_piece) rather than row-major [N][K]
-  // gated product (glu_F > 0; bf16, 4 waves, no split, no top-k): W holds
-  // gate rows [0, F) then up rows [F, 2F); workgroup b streams gate rows
-  // 32 b .. 32 b + 31 (waves 0, 1) and the same up rows (waves 2, 3) and
-  // writes glu_out[m][j] = bf16(silu(gate) * up) instead of Y
+  // gated product (glu_F > 0; bf16, WV = 2 G waves, no split, no top-k): W
+  // holds gate rows [0, F) then up rows [F, 2F); workgroup b streams gate
+  // rows 16 G b .. 16 G b + 16 G - 1 (waves 0 .. G - 1) and the same up rows
+  // (waves G .. 2 G - 1) and writes glu_out[m][j] = bf16(silu(gate) * up)
+  // instead of Y
   int glu_F;
   bf16_t* glu_out;
 };
@@ -53,10 +54,11 @@ __global__ __launch_bounds__(64 * WV) void proj_bf16_kernel(ProjArgs a) {
   constexpr int LDS_ROW = KC + 8;  // 16-byte pad: rows land on different banks
   constexpr int STEPS = KC / 32;
   constexpr int VPR = KC / 8;      // 16-byte vectors per LDS row
-  constexpr int XV = MP * VPR / NT;
+  constexpr int XV = (MP * VPR + NT - 1) / NT;  // X vectors per thread and chunk
+  constexpr bool XG = (MP * VPR) % NT != 0;      // ... the last one only for some threads
   constexpr int TROW = RPW + 1;    // epilogue tile row (floats)
   constexpr int XLDS = (TOPK && TROW * 2 > LDS_ROW) ? MP * TROW * 2 : MP * LDS_ROW;  // bf16 elements
-  static_assert(RPW % kProjRowsPerWG == 0, "partials come in 64-column blocks");
+  static_assert(!TOPK || RPW % kProjRowsPerWG == 0, "partials come in 64-column blocks");
   __shared__ __align__(16) bf16_t xlds[XLDS];
 
   const XSource& xs = a.xs;
@@ -64,9 +66,22 @@ __global__ __launch_bounds__(64 * WV) void proj_bf16_kernel(ProjArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int n_base = a.glu_F > 0 ? (wave < 2 ? 32 * static_cast<int>(blockIdx.x) + 16 * wave
-                                             : a.glu_F + 32 * static_cast<int>(blockIdx.x) + 16 * (wave - 2))
-                                 : static_cast<int>(blockIdx.x) * RPW + wave * 16;
+  // this wave's 16 rows of W; a wave whose rows lie past the end (the last
+  // workgroup of a launch whose row count is no multiple of RPW) streams the
+  // last tile again and stores nothing
+  constexpr int G = WV / 2;  // gated product: gate (and up) row groups per workgroup
+  int n_base;
+  bool idle;
+  if (a.glu_F > 0) {
+    const int col = 16 * G * static_cast<int>(blockIdx.x) + 16 * (wave < G ? wave : wave - G);
+    idle = col >= a.glu_F;
+    const int c = idle ? a.glu_F - 16 : col;
+    n_base = wave < G ? c : a.glu_F + c;
+  } else {
+    n_base = static_cast<int>(blockIdx.x) * RPW + wave * 16;
+    idle = n_base >= N;
+    if (idle) n_base = (N - 1) / 16 * 16;
+  }
   int k_begin, k_end;
   if (a.kper > 0) {
     k_begin = blockIdx.y * a.kper;
@@ -79,7 +94,6 @@ __global__ __launch_bounds__(64 * WV) void proj_bf16_kernel(ProjArgs a) {
   const int K0 = xs.mode == 0 ? K : xs.d;
   if (TOPK && a.tp.clear && blockIdx.x == 0 && blockIdx.y == 0 && tid < a.tp.nclear) a.tp.clear[tid] = 0;
 
-  static_assert((MP * VPR) % NT == 0, "X chunk splits evenly over the workgroup");
   // this lane's 16 bytes of W at column k (a multiple of 32) lie at
   // wp + (k / 256) * wcs + (k % 256 / 32) * wss: row-major, wp is the row
   // (rows past N re-read row N - 1) and the strides are 256 and 32 columns;
@@ -108,7 +122,7 @@ __global__ __launch_bounds__(64 * WV) void proj_bf16_kernel(ProjArgs a) {
   int xo[XV];
 #pragma unroll
   for (int v = 0; v < XV; ++v) {
-    const int idx = tid + v * NT;
+    const int idx = XG && tid + v * NT >= MP * VPR ? tid : tid + v * NT;  // (unused past the chunk)
     const int r = idx / VPR;
     const int c = (idx % VPR) * 8;
     xo[v] = r * LDS_ROW + c;
@@ -137,9 +151,10 @@ __global__ __launch_bounds__(64 * WV) void proj_bf16_kernel(ProjArgs a) {
 #pragma unroll
     for (int s = 0; s < STEPS; ++s) wbuf[p][s] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(wat(kp + s * 32)));
   }
+  const bool xlast = !XG || tid + (XV - 1) * NT < MP * VPR;  // this thread stages an X vector in slot XV - 1
 #pragma unroll
   for (int v = 0; v < XV; ++v)
-    xbuf[v] = *reinterpret_cast<const u32x4_t*>((k_begin < K0 ? xp0[v] : xp1[v]) + k_begin);
+    if (v + 1 < XV || xlast) xbuf[v] = *reinterpret_cast<const u32x4_t*>((k_begin < K0 ? xp0[v] : xp1[v]) + k_begin);
 
   const int k_last = k_end - KC;  // past-the-end prefetches re-read the last chunk
   // whole groups of PF chunks
@@ -150,12 +165,13 @@ __global__ __launch_bounds__(64 * WV) void proj_bf16_kernel(ProjArgs a) {
       const int kc = kc0 + p * KC;
       __syncthreads();
 #pragma unroll
-      for (int v = 0; v < XV; ++v) *reinterpret_cast<u32x4_t*>(&xlds[xo[v]]) = xbuf[v];
+      for (int v = 0; v < XV; ++v)
+        if (v + 1 < XV || xlast) *reinterpret_cast<u32x4_t*>(&xlds[xo[v]]) = xbuf[v];
       __syncthreads();
       const int kx = kc < k_last ? kc + KC : kc;
 #pragma unroll
       for (int v = 0; v < XV; ++v)
-        xbuf[v] = *reinterpret_cast<const u32x4_t*>((kx < K0 ? xp0[v] : xp1[v]) + kx);
+        if (v + 1 < XV || xlast) xbuf[v] = *reinterpret_cast<const u32x4_t*>((kx < K0 ? xp0[v] : xp1[v]) + kx);
       const int kn = kc + PF * KC <= k_last ? kc + PF * KC : k_last;
       // B operands double-buffered: step s + 1's LDS reads are in flight
       // while step s's MFMAs run
@@ -188,12 +204,13 @@ __global__ __launch_bounds__(64 * WV) void proj_bf16_kernel(ProjArgs a) {
     auto chunk = [&](const int p, const int kc) __attribute__((always_inline)) {
       __syncthreads();
 #pragma unroll
-      for (int v = 0; v < XV; ++v) *reinterpret_cast<u32x4_t*>(&xlds[xo[v]]) = xbuf[v];
+      for (int v = 0; v < XV; ++v)
+        if (v + 1 < XV || xlast) *reinterpret_cast<u32x4_t*>(&xlds[xo[v]]) = xbuf[v];
       __syncthreads();
       const int kx = kc < k_last ? kc + KC : kc;
 #pragma unroll
       for (int v = 0; v < XV; ++v)
-        xbuf[v] = *reinterpret_cast<const u32x4_t*>((kx < K0 ? xp0[v] : xp1[v]) + kx);
+        if (v + 1 < XV || xlast) xbuf[v] = *reinterpret_cast<const u32x4_t*>((kx < K0 ? xp0[v] : xp1[v]) + kx);
       const int kn = kc + PF * KC <= k_last ? kc + PF * KC : k_last;
       // B operands double-buffered: step s + 1's LDS reads are in flight
       // while step s's MFMAs run
@@ -221,24 +238,25 @@ __global__ __launch_bounds__(64 * WV) void proj_bf16_kernel(ProjArgs a) {
       if (k_main + p * KC < k_end) chunk(p, k_main + p * KC);
   }
 
-  if (!SPLIT && !TOPK && WV == 4 && a.glu_F > 0) {
-    // the up values through LDS (64 rows x 32 columns, padded), then waves
-    // 0 and 1 finish their gate columns; same expression as swiglu_rows
-    constexpr int UR = 33;
+  if constexpr (!SPLIT && !TOPK && WV % 2 == 0 && MT <= 4) {
+   if (a.glu_F > 0) {
+    // the up values through LDS (MP rows x 16 G columns, padded), then waves
+    // 0 .. G - 1 finish their gate columns; same expression as swiglu_rows
+    constexpr int UR = 16 * G + 1;
     static_assert(MP * UR * 4 <= XLDS * 2, "the up tile fits the X staging area");
     float* upt = reinterpret_cast<float*>(xlds);
     __syncthreads();  // every wave is done with the last X chunk
-    if (wave >= 2) {
+    if (wave >= G) {
 #pragma unroll
       for (int t = 0; t < MT; ++t)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          upt[(t * 16 + (lane & 15)) * UR + 16 * (wave - 2) + 4 * (lane >> 4) + i] = acc[t][i];
+          upt[(t * 16 + (lane & 15)) * UR + 16 * (wave - G) + 4 * (lane >> 4) + i] = acc[t][i];
     }
     __syncthreads();
-    if (wave < 2) {
+    if (wave < G) {
       const int jl = 16 * wave + 4 * (lane >> 4);
-      const int j0 = 32 * static_cast<int>(blockIdx.x) + jl;
+      const int j0 = 16 * G * static_cast<int>(blockIdx.x) + jl;
 #pragma unroll
       for (int t = 0; t < MT; ++t) {
         const int ml = t * 16 + (lane & 15), m = m_base + ml;
@@ -258,6 +276,7 @@ __global__ __launch_bounds__(64 * WV) void proj_bf16_kernel(ProjArgs a) {
       }
     }
     return;
+   }
   }
 
   // D[n][m]: lane holds n = 4 * (lane / 16) + i, m = lane % 16 of each tile.
@@ -265,7 +284,7 @@ __global__ __launch_bounds__(64 * WV) void proj_bf16_kernel(ProjArgs a) {
 #pragma unroll
   for (int t = 0; t < MT; ++t) {
     const int m = m_base + t * 16 + (lane & 15);
-    if (m >= M) continue;
+    if (m >= M || idle) continue;
     float* dst;
     if constexpr (SPLIT) {
       dst = a.part + (static_cast<size_t>(blockIdx.y) * M + m) * N;
@@ -441,6 +460,29 @@ int launch_bf16_mt(int mc, const ProjArgs& a, int nsplit, hipStream_t stream) {
   return launch_bf16<16, TOPK>(a, nsplit, stream);
 }
 
+// Gate column groups (16 columns each) per workgroup of the gated product,
+// which has 2 G waves. Measured on MI355X (64 rows, K = 4096, packed
+// weights): a CU streams its share at about the same rate with 4 waves as
+// with 8, and markedly slower with fewer, so a launch of at least 4-wave
+// workgroups takes as long as its busiest CU: with G = 2, 344 workgroups (F
+// = 11008) took 43-45 us against 26.6 for 256 (F = 8192) and 49.7 for 512
+// (F = 16384); G = 3 (230 workgroups, none doubled up on a CU) takes 37 us
+// and G = 4 (172 workgroups) 47 us.
+// The plan takes the G that leaves the busiest CU the fewest groups.
+int plan_glu(int F) {
+  const int pairs = F / 16;
+  int best = 2;
+  long best_cost = 1L << 62;
+  for (const int g : {2, 3}) {
+    const long cost = ((pairs + g - 1) / g + 255) / 256 * g;  // groups on the busiest CU
+    if (cost < best_cost) {
+      best = g;
+      best_cost = cost;
+    }
+  }
+  return best;
+}
+
 }  // namespace
 
 // Launch Y = X . W^T. With nsplit > 1 (bf16 only) writes float32 partials
@@ -554,35 +596,40 @@ int launch_projection_parts(int dtype, int M, int K, int N, const void* X, const
 
 bool projection_glu_supported(int dtype, int M, int K, int F) {
   dtype &= ~HYDRA_LAYER_PACKED;
-  return dtype == HYDRA_BF16 && M >= 1 && M <= 64 && K % kPackChunk == 0 && F % 32 == 0;
+  return dtype == HYDRA_BF16 && M >= 1 && M <= 64 && K % kPackChunk == 0 && F % 16 == 0;
 }
 
 int launch_projection_glu(int dtype, int M, int K, int F, const void* X, const void* W, bf16_t* g_out,
                           hipStream_t stream) {
   const int wpacked = (dtype & HYDRA_LAYER_PACKED) != 0;
   if (!projection_glu_supported(dtype, M, K, F)) {
-    set_error("projection: the gated product needs bf16, 1..64 rows, K %% 256 == 0, F %% 32 == 0");
+    set_error("projection: the gated product needs bf16, 1..64 rows, K %% 256 == 0, F %% 16 == 0");
     return HYDRA_ERR_UNSUPPORTED;
   }
+  const int G = plan_glu(F);
   XSource xs{};
   xs.x = X;
   xs.ldx = K;
   xs.mode = 0;
   ProjArgs a{M, K, 2 * F, xs, static_cast<const bf16_t*>(W), nullptr, RowMap{M, 0, 0}, 2 * F, K, 0, nullptr,
              TopkPartials{nullptr, nullptr}, wpacked, F, g_out};
-  const dim3 grid(F / 32, 1);
-  auto go = [&](auto MTC) {
-    constexpr int MT = decltype(MTC)::value;
+  const dim3 grid((F / 16 + G - 1) / G, 1);
+  auto go = [&](auto MTC, auto GC) {
+    constexpr int MT = decltype(MTC)::value, WV = 2 * decltype(GC)::value;
     if (K % (2 * kPackChunk) == 0)
-      proj_bf16_kernel<MT, 256, 2, 4, false, false, false><<<grid, 256, 0, stream>>>(a);
+      proj_bf16_kernel<MT, 256, 2, WV, false, false, false><<<grid, 64 * WV, 0, stream>>>(a);
     else if (K > 2 * kPackChunk)
-      proj_bf16_kernel<MT, 256, 2, 4, false, false, true><<<grid, 256, 0, stream>>>(a);
+      proj_bf16_kernel<MT, 256, 2, WV, false, false, true><<<grid, 64 * WV, 0, stream>>>(a);
     else
-      proj_bf16_kernel<MT, 256, 1, 4, false, false, false><<<grid, 256, 0, stream>>>(a);
+      proj_bf16_kernel<MT, 256, 1, WV, false, false, false><<<grid, 64 * WV, 0, stream>>>(a);
   };
-  if (M <= 16) go(std::integral_constant<int, 1>{});
-  else if (M <= 32) go(std::integral_constant<int, 2>{});
-  else go(std::integral_constant<int, 4>{});
+  auto go_g = [&](auto MTC) {
+    if (G == 3) go(MTC, std::integral_constant<int, 3>{});
+    else go(MTC, std::integral_constant<int, 2>{});
+  };
+  if (M <= 16) go_g(std::integral_constant<int, 1>{});
+  else if (M <= 32) go_g(std::integral_constant<int, 2>{});
+  else go_g(std::integral_constant<int, 4>{});
   HY_LAUNCH_CHECK("projection(gated)");
   return HYDRA_OK;
 }

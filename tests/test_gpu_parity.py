@@ -1069,6 +1069,11 @@ def _close(got, ref, dtype, what, stream=False):
     # shapes of the streaming products; GQA in the first)
     ("bf16", 1, ("cartesian", [2, 2]), 512, 4, 2, 128, 1024, [33], 2),
     ("bf16", 2, ("cartesian", [3, 4]), 512, 8, 8, 128, 1024, [64, 1000], 1),
+    # 96 and 192 heads' rows in the Q/K/V product (unsplit streaming launch)
+    # at 7 and 32 rows (GQA), and head dim 64 with K = 256
+    ("bf16", 1, ("cartesian", [2, 2]), 512, 32, 16, 128, 1024, [33], 1),
+    ("bf16", 2, ("cartesian", [3, 4]), 512, 32, 16, 128, 1024, [64, 1000], 2),
+    ("bf16", 1, ("cartesian", [2, 3]), 256, 64, 64, 64, 512, [40], 1),
 ])
 def test_tree_decoder_layer(dtype, B, tree, d, Hq, Hkv, D, F, lens, layers):
     """Decoder layers over the tree rows (each with its own weights and paged

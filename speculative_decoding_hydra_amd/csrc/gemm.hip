@@ -10,14 +10,20 @@
 //     BN / 2 (n) x 64 (m) each in v_mfma_f32_16x16x32_bf16 accumulators, so
 //     every operand read from LDS feeds 4 or BN / 32 MFMAs; BN = 256, or 128
 //     when one m tile covers M (twice the workgroups for 65-256 rows);
-//   * K advances in chunks of 64: the next chunk of W and X is loaded from
-//     global memory into registers while the current one is multiplied out
-//     of LDS (two LDS stages, one barrier per chunk);
+//   * K advances in chunks of 64 held in NS LDS stages (two at BN = 256,
+//     three at BN = 128), filled straight from global memory by DMA
+//     (global_load_lds_dwordx4, no staging registers) NS - 1 chunks ahead;
+//     one barrier per chunk; the operand reads are instructions the compiler
+//     does not track, so it does not wait for the fills in flight before
+//     them (measured at 1024 rows: 349-356 us against 355-369 us for the
+//     same kernel staging through registers);
 //   * workgroups are ordered so that the four m tiles of one n tile run on
 //     the same XCD back to back and share that W tile in its L2;
 //   * the epilogue writes Y and, per row and 64-column block, the largest key
 //     and optionally (max, sum exp), the same partials as the streaming
 //     projection leaves for the row merge.
+#include <type_traits>
+
 #include "common.h"
 
 namespace hydra {
@@ -75,13 +81,50 @@ __device__ __forceinline__ void col_ms(float& m, float& s) {
   ms_combine(m, s, __uint_as_float(c[1]), __uint_as_float(d[1]));
 }
 
-template <int BN>
-__global__ __launch_bounds__(GTHREADS, 2) void proj_gemm_kernel(GemmArgs a) {
-  constexpr int WN = BN / 2;        // n columns per wave
-  constexpr int NI = WN / 16;       // 16-column MFMA tiles per wave
-  constexpr int WLD = BN / 64;      // 16-byte W vectors per thread and chunk
-  __shared__ __align__(16) bf16_t wl[2][BN * GROW];
-  __shared__ __align__(16) bf16_t xl[2][GBM * GROW];
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glb_void_t;
+
+// s_waitcnt immediate waiting for vmcnt <= n only (gfx9 encoding)
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+// 16-byte LDS read issued as an instruction the compiler does not track: it
+// would otherwise wait for every DMA fill still in flight (the chunks ahead)
+// before the read. Its value is threaded through the s_waitcnt that follows
+// (wait_lds), so nothing reads it earlier.
+template <int OFF>
+__device__ __forceinline__ u32x4_t lds_read16(uint32_t addr) {
+  u32x4_t v;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF));
+  return v;
+}
+
+// 32-bit LDS address of a pointer into a __shared__ object
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) char*)(p)));
+}
+
+// f(integral_constant<int, I>) for I = I0 .. N - 1, unrolled
+template <int I, int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
+// NS LDS stages of one K chunk each (W tile rows, then X tile rows), filled
+// by DMA (global_load_lds_dwordx4) NS - 1 chunks ahead of use. (A 4-wave
+// variant with 128 x 128 wave tiles and operand reads double-buffered across
+// k steps took 435 us at 1024 rows: its accumulators fill the AGPRs and the
+// compiler shuttles them through VGPRs inside the loop.)
+template <int BN, int NS>
+__global__ __launch_bounds__(GTHREADS, 1) void proj_gemm_kernel(GemmArgs a) {
+  constexpr int WN = BN / 2;               // n columns per wave
+  constexpr int NI = WN / 16;              // 16-column MFMA tiles per wave
+  constexpr int ROWS = BN + GBM;           // LDS rows per stage (W, then X)
+  constexpr int STAGE = ROWS * GROW;       // bf16 elements per stage
+  constexpr int GROUPS = ROWS / 8 / 8;     // 8-row DMA groups per wave and chunk
+  __shared__ __align__(16) bf16_t lds[NS * STAGE];
   // XCD-aware order: workgroup b runs on XCD b % 8; slot s = b / 8 there
   // covers m tile s % mtiles of n tile (s / mtiles) * 8 + b % 8
   const int bx = blockIdx.x;
@@ -90,47 +133,40 @@ __global__ __launch_bounds__(GTHREADS, 2) void proj_gemm_kernel(GemmArgs a) {
   const int mtile = slot % a.mtiles;
   if (ntile >= a.ntiles) return;  // whole workgroup: no barrier is pending
   const int n0 = ntile * BN, m0 = mtile * GBM;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   if (a.tp.clear && bx == 0 && tid < a.tp.nclear) a.tp.clear[tid] = 0;
   const int kb = static_cast<int>(blockIdx.y) * a.kper;
   const int klen = a.K - kb < a.kper ? a.K - kb : a.kper;
   const int wn = wave & 1, wm = wave >> 1;  // 2 x 4 waves: WN n x 64 m each
 
-  // global -> register staging: WLD vectors of 16 bytes of W and 4 of X per
-  // thread; packed W (ldw < 0) is addressed piece by piece
-  const bf16_t* wsrc[WLD];
-  const bf16_t* xsrc[4];
-  int woff[WLD], xoff[4], wrn[WLD], wk[WLD];
+  // DMA: lane l of a wave's 8-row group lands at row 8 g + l / 8, position l %
+  // 8 of its row, which holds the row's 16-byte chunk (l % 8) ^ (row % 8)
+  const int drow = lane >> 3, dchunk = (lane & 7) ^ drow;
+  const bf16_t* src[GROUPS];
+  int srow[GROUPS];
+  bool isw[GROUPS];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int idx = tid + j * GTHREADS;
-    const int r = idx >> 3, c = (idx & 7) * 8;
-    const int m = m0 + r < a.M ? m0 + r : 0;
-    xsrc[j] = a.X + static_cast<size_t>(m) * a.ldx + kb + c;
-    xoff[j] = swz(r, idx & 7);
-    if (j < WLD) {
+  for (int j = 0; j < GROUPS; ++j) {
+    const int r = 8 * (wave + 8 * j) + drow;  // stage row
+    isw[j] = r < BN;
+    if (r < BN) {
       const int n = n0 + r < a.N ? n0 + r : a.N - 1;  // rows past the end re-read the last row
-      wsrc[j] = a.ldw < 0 ? a.W : a.W + static_cast<size_t>(n) * a.ldw + kb + c;
-      wrn[j] = n;
-      wk[j] = kb + c;
-      woff[j] = xoff[j];
+      srow[j] = n;
+      src[j] = a.ldw < 0 ? a.W : a.W + static_cast<size_t>(n) * a.ldw + kb + dchunk * 8;
+    } else {
+      const int m = m0 + r - BN < a.M ? m0 + r - BN : 0;
+      srow[j] = m;
+      src[j] = a.X + static_cast<size_t>(m) * a.ldx + kb + dchunk * 8;
     }
   }
-  u32x4_t wreg[WLD], xreg[4];
-  auto load = [&](int k0) {
+  bf16_t* const lds0 = lds;
+  auto issue = [&](int st, int k0) __attribute__((always_inline)) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if (j < WLD)
-        wreg[j] = *reinterpret_cast<const u32x4_t*>(a.ldw < 0 ? wsrc[j] + packed_piece(wrn[j], wk[j] + k0, a.N)
-                                                              : wsrc[j] + k0);
-      xreg[j] = *reinterpret_cast<const u32x4_t*>(xsrc[j] + k0);
-    }
-  };
-  auto store = [&](int st) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if (j < WLD) *reinterpret_cast<u32x4_t*>(&wl[st][woff[j]]) = wreg[j];
-      *reinterpret_cast<u32x4_t*>(&xl[st][xoff[j]]) = xreg[j];
+    for (int j = 0; j < GROUPS; ++j) {
+      const bf16_t* g = a.ldw < 0 && isw[j] ? src[j] + packed_piece(srow[j], kb + k0 + dchunk * 8, a.N) : src[j] + k0;
+      __builtin_amdgcn_global_load_lds((glb_void_t*)(g), (lds_void_t*)(lds0 + st * STAGE + (wave + 8 * j) * 8 * GROW),
+                                       16, 0, 0);
     }
   };
 
@@ -140,33 +176,56 @@ __global__ __launch_bounds__(GTHREADS, 2) void proj_gemm_kernel(GemmArgs a) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
+  // operand rows differ by multiples of 16, so the swizzle depends on the
+  // lane alone: k step s reads chunk 4 s + lane / 16 at position (4 s + lane
+  // / 16) ^ (lane % 8)
+  const int c0 = (lane >> 4) ^ (lane & 7);
+  const uint32_t base = lds_addr(lds);
+  const uint32_t arow0 = base + ((wn * WN + (lane & 15)) * GROW + c0 * 8) * 2;
+  const uint32_t arow1 = base + ((wn * WN + (lane & 15)) * GROW + (c0 ^ 4) * 8) * 2;
+  const uint32_t brow0 = base + ((BN + wm * 64 + (lane & 15)) * GROW + c0 * 8) * 2;
+  const uint32_t brow1 = base + ((BN + wm * 64 + (lane & 15)) * GROW + (c0 ^ 4) * 8) * 2;
+
   const int nk = klen / GBK;
-  load(0);
-  store(0);
-  if (nk > 1) load(GBK);
-  __syncthreads();
-  // operand rows differ by multiples of 16, so the swizzle depends on the lane alone
-  const int arow = swz(wn * WN + (lane & 15), lane >> 4), brow = swz(wm * 64 + (lane & 15), lane >> 4);
-  const int ks1 = ((4 ^ ((lane >> 4) ^ (lane & 7))) - ((lane >> 4) ^ (lane & 7))) * 8;  // k step 1 minus k step 0
+#pragma unroll
+  for (int p = 0; p + 1 < NS; ++p)
+    if (p < nk) issue(p, p * GBK);
   for (int c = 0; c < nk; ++c) {
-    const int st = c & 1;
-    if (c + 1 < nk) store(st ^ 1);  // chunk c + 1, loaded one chunk ago
-    if (c + 2 < nk) load((c + 2) * GBK);
-#pragma unroll
-    for (int ks = 0; ks < GBK / 32; ++ks) {
-      bf16x8_t bv[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        bv[j] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(&xl[st][brow + j * 16 * GROW + ks * ks1]));
-#pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        const bf16x8_t av =
-            __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(&wl[st][arow + i * 16 * GROW + ks * ks1]));
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv[j], acc[i][j], 0, 0, 0);
+    const int st = c % NS;
+    // this wave's fills of chunk c have landed (those of the chunks after it
+    // may still be in flight), then every wave's have and every wave is done
+    // with chunk c - 1, whose stage takes chunk c + NS - 1
+    if (c + NS - 2 < nk) __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 2) * GROUPS));
+    else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    asm volatile("s_barrier" ::: "memory");
+    if (c + NS - 1 < nk) issue((c + NS - 1) % NS, (c + NS - 1) * GBK);
+    const uint32_t so = static_cast<uint32_t>(st * STAGE * 2);
+    static_for<0, GBK / 32>([&](auto KS) __attribute__((always_inline)) {
+      constexpr int ks = decltype(KS)::value;
+      const uint32_t ab = (ks == 0 ? arow0 : arow1) + so, bb = (ks == 0 ? brow0 : brow1) + so;
+      u32x4_t bv[4], av[NI];
+      static_for<0, 4>([&](auto J) __attribute__((always_inline)) {
+        bv[decltype(J)::value] = lds_read16<decltype(J)::value * 16 * GROW * 2>(bb);
+      });
+      static_for<0, NI>([&](auto I) __attribute__((always_inline)) {
+        av[decltype(I)::value] = lds_read16<decltype(I)::value * 16 * GROW * 2>(ab);
+      });
+      if constexpr (NI == 8) {
+        asm volatile("s_waitcnt lgkmcnt(0)"
+                     : "+v"(bv[0]), "+v"(bv[1]), "+v"(bv[2]), "+v"(bv[3]), "+v"(av[0]), "+v"(av[1]), "+v"(av[2]),
+                       "+v"(av[3]), "+v"(av[4]), "+v"(av[5]), "+v"(av[6]), "+v"(av[7]));
+      } else {
+        asm volatile("s_waitcnt lgkmcnt(0)"
+                     : "+v"(bv[0]), "+v"(bv[1]), "+v"(bv[2]), "+v"(bv[3]), "+v"(av[0]), "+v"(av[1]), "+v"(av[2]),
+                       "+v"(av[3]));
       }
-    }
-    __syncthreads();
+#pragma unroll
+      for (int i = 0; i < NI; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av[i]),
+                                                              __builtin_bit_cast(bf16x8_t, bv[j]), acc[i][j], 0, 0, 0);
+    });
   }
 
   // D[n][m]: lane holds n = 16 i + 4 (lane / 16) + e, m = 16 j + lane % 16 of the wave tile
@@ -250,8 +309,8 @@ int launch_projection_gemm(int M, int K, int N, const bf16_t* X, int ldx, const 
   a.kper = K;
   a.ystride = 0;
   const int slots = (a.ntiles + 7) / 8 * a.mtiles;  // per XCD
-  if (bn == 128) proj_gemm_kernel<128><<<slots * 8, GTHREADS, 0, stream>>>(a);
-  else proj_gemm_kernel<256><<<slots * 8, GTHREADS, 0, stream>>>(a);
+  if (bn == 128) proj_gemm_kernel<128, 3><<<slots * 8, GTHREADS, 0, stream>>>(a);
+  else proj_gemm_kernel<256, 2><<<slots * 8, GTHREADS, 0, stream>>>(a);
   HY_LAUNCH_CHECK("projection(gemm)");
   return HYDRA_OK;
 }
@@ -277,8 +336,8 @@ int launch_projection_gemm_split(int M, int K, int N, const bf16_t* X, const bf1
   a.ystride = static_cast<size_t>(M) * N;
   const int slots = (a.ntiles + 7) / 8 * a.mtiles;
   const dim3 grid(slots * 8, nsplit);
-  if (bn == 128) proj_gemm_kernel<128><<<grid, GTHREADS, 0, stream>>>(a);
-  else proj_gemm_kernel<256><<<grid, GTHREADS, 0, stream>>>(a);
+  if (bn == 128) proj_gemm_kernel<128, 3><<<grid, GTHREADS, 0, stream>>>(a);
+  else proj_gemm_kernel<256, 2><<<grid, GTHREADS, 0, stream>>>(a);
   HY_LAUNCH_CHECK("projection(gemm, split K)");
   return HYDRA_OK;
 }

@@ -107,36 +107,26 @@ def measured_mfma():
     return t.get("counters") if t.get("gemm_hip_sha256_16") == file_hash("gemm.hip") else None
 
 
-def mfma_measure(W2s, M=1024, reps=10, use_graph=True):
-    """The tiled projection at an MFMA-bound row count (M rows of one
-    sequence batch x every tree row: 1024 x 32000 x 4096, the 16-sequence
-    target projection), with the arg-max epilogue of the target projection,
-    cycling the heads' W2 copies so the last-level cache cannot serve
-    repeats: flops / average launch time against the dense bf16 peak."""
+def _loop_us(call, n, reps, use_graph):
+    """Average microseconds of call(i), i = 0 .. reps - 1 (n distinct
+    operands cycled), launched back to back from one graph (or eagerly)."""
     import torch
 
-    from speculative_decoding_hydra_amd import hydra_vocab_projection, hydra_vocab_projection_workspace_size
-
-    N, K = W2s[0].shape
-    X = torch.randn(M, K, device="cuda").to(W2s[0].dtype)
-    Y = torch.empty(M, N, device="cuda")
-    ws = torch.empty(hydra_vocab_projection_workspace_size(M, N, 1), dtype=torch.uint8, device="cuda")
-    proj = lambda W: hydra_vocab_projection(X, W, Y, 1, ws)  # noqa: E731
-    for W in W2s:
-        proj(W)
+    for i in range(n):
+        call(i)
     torch.cuda.synchronize()
     g = None
     if use_graph:
         s = torch.cuda.Stream()
         s.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(s):
-            proj(W2s[0])
+            call(0)
         torch.cuda.current_stream().wait_stream(s)
         torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             for i in range(reps):
-                proj(W2s[i % len(W2s)])
+                call(i % n)
         g.replay()
         torch.cuda.synchronize()
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -145,18 +135,43 @@ def mfma_measure(W2s, M=1024, reps=10, use_graph=True):
         g.replay()
     else:
         for i in range(reps):
-            proj(W2s[i % len(W2s)])
+            call(i % n)
     b.record()
     torch.cuda.synchronize()
-    us = a.elapsed_time(b) / reps * 1e3
+    return a.elapsed_time(b) / reps * 1e3
+
+
+def mfma_measure(W2s, M=1024, reps=10, use_graph=True):
+    """The tiled projection at an MFMA-bound row count (M rows of one
+    sequence batch x every tree row: 1024 x 32000 x 4096, the 16-sequence
+    target projection), with the arg-max epilogue of the target projection,
+    cycling the heads' W2 copies so the last-level cache cannot serve
+    repeats: flops / average launch time against the dense bf16 peak. For
+    context, the vendor GEMM (hipBLASLt through torch.mm: bf16 output, no
+    epilogue) on as many row-major copies in the same loop form."""
+    import torch
+
+    from speculative_decoding_hydra_amd import hydra_vocab_projection, hydra_vocab_projection_workspace_size
+
+    N, K = W2s[0].shape
+    X = torch.randn(M, K, device="cuda").to(W2s[0].dtype)
+    Y = torch.empty(M, N, device="cuda")
+    ws = torch.empty(hydra_vocab_projection_workspace_size(M, N, 1), dtype=torch.uint8, device="cuda")
+    us = _loop_us(lambda i: hydra_vocab_projection(X, W2s[i], Y, 1, ws), len(W2s), reps, use_graph)
     flops = 2.0 * M * N * K
     tf = flops / (us * 1e-6) / 1e12
     from speculative_decoding_hydra_amd import PackedWeight
 
+    Wr = [(torch.randn(N, K, device="cuda") * 0.02).to(torch.bfloat16) for _ in range(len(W2s))]
+    Yb = torch.empty(M, N, device="cuda", dtype=torch.bfloat16)
+    us_bl = _loop_us(lambda i: torch.mm(X, Wr[i].t(), out=Yb), len(Wr), reps, use_graph)
+    del Wr, Yb
     return {"kernel": "proj_gemm_kernel (tiled vocabulary projection, arg-max epilogue)", "rows": M, "cols": N,
             "depth": K, "weight_layout": "packed" if isinstance(W2s[0], PackedWeight) else "row-major",
             "flops": flops, "avg_launch_us": us, "achieved_TFLOPs": tf, "peak_TFLOPs": MFMA_PEAK_TFLOPS,
-            "frac": tf / MFMA_PEAK_TFLOPS, "counters": measured_mfma()}
+            "frac": tf / MFMA_PEAK_TFLOPS,
+            "hipblaslt_same_loop": {"avg_launch_us": us_bl, "frac": flops / (us_bl * 1e-6) / 1e12 / MFMA_PEAK_TFLOPS},
+            "counters": measured_mfma()}
 
 
 def measured_traffic():

@@ -34,8 +34,15 @@ __global__ __launch_bounds__(256) void head_mlp_epilogue(int M, int d, int nspli
   for (size_t idx = blockIdx.x * 256ull + threadIdx.x; idx < total; idx += gridDim.x * 256ull) {
     const int m = static_cast<int>(idx / d);
     const int j = static_cast<int>(idx % d);
+    // the (at most 16) split partials, every load issued before the first add
+    float t[16];
+#pragma unroll
+    for (int s = 0; s < 16; ++s)
+      if (s < nsplit) t[s] = part[static_cast<size_t>(s) * total + idx];
     float a = 0.f;
-    for (int s = 0; s < nsplit; ++s) a += part[static_cast<size_t>(s) * total + idx];
+#pragma unroll
+    for (int s = 0; s < 16; ++s)
+      if (s < nsplit) a += t[s];
     a += load_f(b1, j);
     const float act = a / (1.0f + expf(-a));  // SiLU(a) = a * sigmoid(a)
     const float u = residual ? load_f(h, static_cast<size_t>(m / P) * d + j) + act : act;

@@ -50,9 +50,17 @@ __global__ __launch_bounds__(256) void gather_rows(int d, int P, int r0, int N, 
   }
 }
 
+// sum of the ns (at most 16) split partials of element i, in split order,
+// every load issued before the first add
 __device__ __forceinline__ float sum_parts(const float* __restrict__ p, int ns, size_t stride, size_t i) {
-  float v = p[i];
-  for (int s = 1; s < ns; ++s) v += p[s * stride + i];
+  float t[16];
+#pragma unroll
+  for (int s = 0; s < 16; ++s)
+    if (s < ns) t[s] = p[s * stride + i];
+  float v = t[0];
+#pragma unroll
+  for (int s = 1; s < 16; ++s)
+    if (s < ns) v += t[s];
   return v;
 }
 

@@ -64,10 +64,18 @@ __device__ __forceinline__ float rt<bf16_t>(float v) {
   return bf16_to_f32(f32_to_bf16(v));
 }
 
-// sum of the ns split-K partials of element i (stride floats apart)
+// sum of the ns (at most 16) split-K partials of element i (stride floats
+// apart), in split order; the bound is fixed so that every load is issued
+// before the first add
 __device__ __forceinline__ float psum(const float* __restrict__ p, int ns, size_t stride, size_t i) {
-  float v = p[i];
-  for (int s = 1; s < ns; ++s) v += p[s * stride + i];
+  float t[16];
+#pragma unroll
+  for (int s = 0; s < 16; ++s)
+    if (s < ns) t[s] = p[s * stride + i];
+  float v = t[0];
+#pragma unroll
+  for (int s = 1; s < 16; ++s)
+    if (s < ns) v += t[s];
   return v;
 }
 constexpr int kNormThreads = 256;

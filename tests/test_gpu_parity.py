@@ -1074,6 +1074,10 @@ def _close(got, ref, dtype, what, stream=False):
     ("bf16", 1, ("cartesian", [2, 2]), 512, 32, 16, 128, 1024, [33], 1),
     ("bf16", 2, ("cartesian", [3, 4]), 512, 32, 16, 128, 1024, [64, 1000], 2),
     ("bf16", 1, ("cartesian", [2, 3]), 256, 64, 64, 64, 512, [40], 1),
+    # 73 rows at the 7B width: tiled split products with eight partials, so
+    # the norms and the residual sum eight; and the 70B width at 7 rows
+    ("bf16", 1, ("cartesian", [8, 8]), 4096, 32, 32, 128, 11008, [64], 1),
+    ("bf16", 1, ("cartesian", [2, 2]), 8192, 8, 8, 128, 512, [40], 1),
 ])
 def test_tree_decoder_layer(dtype, B, tree, d, Hq, Hkv, D, F, lens, layers):
     """Decoder layers over the tree rows (each with its own weights and paged

@@ -69,6 +69,11 @@ extern "C" {
 #define HYDRA_BF16 1
 #define HYDRA_VOCAB_PACKED 0x100 /* dtype flag: vocabulary weights packed */
 #define HYDRA_LAYER_PACKED 0x200 /* dtype flag: decoder layer weights packed */
+/* dtype flag of hydra_draft_heads with folded embedding tables (emb_proj):
+ * W1[k] is the packed [d, d] copy of W1_k[:, :d], the h half (hydra_pack_weight
+ * of that contiguous half), the only part of W1 such a call reads. For callers
+ * that stream the h halves at the packed layout's rate. */
+#define HYDRA_W1H_PACKED 0x400
 
 #define HYDRA_MAX_DEPTH 8     /* deepest tree (number of draft heads used) */
 #define HYDRA_MAX_TOPK 16     /* widest fan-out of one node */

@@ -376,6 +376,7 @@ struct MergeArgs {
 // of a [d, ldw] matrix and K columns are read.
 struct MlpArgs {
   int M, K, d, ldw, heads;
+  int wpacked;  // W[y] is a packed [d, K] matrix (hydra_pack_weight), ldw unused
   int epi[HYDRA_MAX_DEPTH];
   XSource xs;
   const bf16_t* W[HYDRA_MAX_DEPTH];

@@ -127,7 +127,8 @@ DraftWs draft_ws(int dtype, int B, int d, int V, int hydra_mode, int Dmax, const
 extern "C" size_t hydra_draft_heads_workspace_size(int dtype, int B, int d, int V, int hydra_mode,
                                                    int Dmax, const int32_t* row_first) {
   if (B <= 0 || d <= 0 || V <= 0 || Dmax <= 0 || Dmax > HYDRA_MAX_DEPTH || !row_first) return 0;
-  return draft_ws(dtype & ~HYDRA_VOCAB_PACKED, B, d, V, hydra_mode, Dmax, row_first, nullptr).total;
+  return draft_ws(dtype & ~(HYDRA_VOCAB_PACKED | HYDRA_W1H_PACKED), B, d, V, hydra_mode, Dmax, row_first,
+                  nullptr).total;
 }
 
 extern "C" int hydra_draft_heads(int dtype, int B, int d, int V, int hydra_mode, int residual,
@@ -143,7 +144,8 @@ extern "C" int hydra_draft_heads(int dtype, int B, int d, int V, int hydra_mode,
   clear_error();
   hipStream_t stream = static_cast<hipStream_t>(stream_);
   const int vpack = dtype & HYDRA_VOCAB_PACKED;  // packed vocabulary weights (hydra_pack_weight)
-  dtype &= ~HYDRA_VOCAB_PACKED;
+  const int w1hp = (dtype & HYDRA_W1H_PACKED) != 0;  // packed h halves of W1 (folded calls)
+  dtype &= ~(HYDRA_VOCAB_PACKED | HYDRA_W1H_PACKED);
   HY_CHECK(dtype == HYDRA_F32 || dtype == HYDRA_BF16, HYDRA_ERR_INVALID, "draft_heads: bad dtype %d", dtype);
   HY_CHECK(!vpack || dtype == HYDRA_BF16, HYDRA_ERR_UNSUPPORTED, "draft_heads: packed vocabulary weights are bf16");
   HY_CHECK(B > 0 && d > 0 && V > 0, HYDRA_ERR_INVALID, "draft_heads: bad sizes B=%d d=%d V=%d", B, d, V);
@@ -209,6 +211,8 @@ extern "C" int hydra_draft_heads(int dtype, int B, int d, int V, int hydra_mode,
   // head k + 2 into slot k + 1.
   const bool folded = hydra_mode == 1 && emb_proj && dtype == HYDRA_BF16 && d % 256 == 0 &&
                       mlp_fused_supported(dtype, B, d, d) && merge_ffn_supported(B, d, d);
+  HY_CHECK(!w1hp || folded, HYDRA_ERR_UNSUPPORTED,
+           "draft_heads: packed W1 h halves need the folded path (bf16 Hydra heads with tables, d %% 256 == 0)");
   if (folded) {
     for (int k = 1; k <= Dmax; ++k)
       HY_CHECK(emb_proj[k - 1], HYDRA_ERR_INVALID, "draft_heads: null folded embedding table of head %d", k);
@@ -217,6 +221,7 @@ extern "C" int hydra_draft_heads(int dtype, int B, int d, int V, int hydra_mode,
     pre.K = d;
     pre.d = d;
     pre.ldw = 2 * d;
+    pre.wpacked = w1hp;
     pre.heads = Dmax >= 2 ? 2 : 1;
     pre.xs.x = h;
     pre.xs.ldx = d;
@@ -428,6 +433,7 @@ extern "C" int hydra_draft_heads(int dtype, int B, int d, int V, int hydra_mode,
       hf.K = d;
       hf.d = d;
       hf.ldw = 2 * d;
+      hf.wpacked = w1hp;
       hf.heads = 1;
       hf.xs.x = h;
       hf.xs.ldx = d;

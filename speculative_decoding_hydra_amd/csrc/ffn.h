@@ -19,7 +19,17 @@ __device__ __forceinline__ void mlp_tile(const MlpArgs& a, int tile, int y) {
   const int steps = kw / 32;
   const int K0 = xs.mode == 1 ? xs.d : a.K;  // mode 1: h below K0, the embedding above
 
+  // this lane's 16 bytes of W at step s (32 columns each): row-major, row n0
+  // + lane % 16 at column kb + 32 s + 8 (lane / 16); packed, the same piece
+  // is lane 8 * lane of the 1 KB block of 32-column group q = kb / 32 + s of
+  // tile n0 / 16 (packed_piece), so a wave reads 1 KB contiguous per step
   const bf16_t* wp = a.W[y] + static_cast<size_t>(n0 + (lane & 15)) * a.ldw + kb + (lane >> 4) * 8;
+  const size_t ptiles = static_cast<size_t>((a.d + 15) / 16);
+  auto wat = [&](int s) __attribute__((always_inline)) -> const bf16_t* {
+    if (!a.wpacked) return wp + s * 32;
+    const int q = (kb >> 5) + s;
+    return a.W[y] + ((static_cast<size_t>(q >> 3) * ptiles + tile) * 8 + (q & 7)) * 512 + lane * 8;
+  };
   const bf16_t* xp[MT];
 #pragma unroll
   for (int t = 0; t < MT; ++t) {
@@ -53,7 +63,7 @@ __device__ __forceinline__ void mlp_tile(const MlpArgs& a, int tile, int y) {
   u32x4_t wr[PF], xr[PF][MT];
 #pragma unroll
   for (int p = 0; p < PF; ++p) {
-    wr[p] = *reinterpret_cast<const u32x4_t*>(wp + p * 32);
+    wr[p] = *reinterpret_cast<const u32x4_t*>(wat(p));
 #pragma unroll
     for (int t = 0; t < MT; ++t) xr[p][t] = *reinterpret_cast<const u32x4_t*>(xp[t] + p * 32);
   }
@@ -63,7 +73,7 @@ __device__ __forceinline__ void mlp_tile(const MlpArgs& a, int tile, int y) {
     for (int p = 0; p < PF; ++p) {
       const int sn = s0 + p + PF <= last ? s0 + p + PF : last;  // past the end: re-read the last step
       const bf16x8_t av = __builtin_bit_cast(bf16x8_t, wr[p]);
-      wr[p] = *reinterpret_cast<const u32x4_t*>(wp + sn * 32);
+      wr[p] = *reinterpret_cast<const u32x4_t*>(wat(sn));
 #pragma unroll
       for (int t = 0; t < MT; ++t) {
         const bf16x8_t bv = __builtin_bit_cast(bf16x8_t, xr[p][t]);

@@ -17,6 +17,7 @@ from ._lib import lib
 
 HYDRA_F32, HYDRA_BF16 = 0, 1
 HYDRA_VOCAB_PACKED = 0x100  # dtype flag: the call's vocabulary weights are packed (hydra_pack_weight)
+HYDRA_W1H_PACKED = 0x400  # dtype flag: W1 holds the packed h halves of a folded call (hydra_pack_weight)
 HYDRA_LAYER_PACKED = 0x200  # dtype flag: the decoder layers' weights are packed
 MAX_DEPTH, MAX_TOPK, MAX_TREE, MAX_VERIFY = 8, 16, 1024, 256
 
@@ -285,14 +286,20 @@ def hydra_draft_heads(h, root_tok, emb, W1, b1, W2, dplan: DevicePlan, head_logi
         raise ValueError("W1, b1 and W2 need one entry per head")
     _draft_shapes("hydra_draft_heads", h, root_tok, emb if dplan.hydra else None, W2, dplan, head_logits, head_lse,
                   cand_tok, cand_logp, head_hidden)
+    # with folded tables W1 may be the packed h halves W1_k[:, :d] (all or none)
+    w1h = emb_proj is not None and any(isinstance(w, PackedWeight) for w in W1)
+    if w1h and not all(isinstance(w, PackedWeight) for w in W1):
+        raise ValueError("hydra_draft_heads: packed h halves of W1 come for every head or none")
     for k in range(n_heads):
-        in_k = (k + 2) * d if full_path else (2 * d if dplan.hydra else d)
+        in_k = d if w1h else ((k + 2) * d if full_path else (2 * d if dplan.hydra else d))
         _shapes("hydra_draft_heads", **{f"W1[{k}]": (W1[k], (d, in_k)), f"b1[{k}]": (b1[k], (d,))})
     arr = C.c_void_p * n_heads
     w1 = arr(*[_dev(w, "W1", h.dtype) for w in W1])
     bb = arr(*[_dev(w, "b1", h.dtype) for w in b1])
     w2 = arr(*[_dev(w, "W2", h.dtype) for w in W2])
     dt |= _vocab_flag("draft heads", W2)
+    if w1h:
+        dt |= HYDRA_W1H_PACKED
     rows = dplan.rows
     rf, rfp = _host_i32(rows.row_first)
     df, dfp = _host_i32(rows.depth_first)

@@ -137,10 +137,17 @@ class HydraRound:
         else:
             self.W2 = [pk(W) for W in weights["W2"]]
         self.emb_proj = None
+        self.W1h = None
         if fold_embedding:
             self.emb_proj = [z(V, d) for _ in weights["W1"]]
             for w1, t in zip(weights["W1"], self.emb_proj):
                 H.hydra_fold_embedding(weights["emb"], w1, t)
+            # the folded round reads only the h halves of W1: packed, they
+            # stream at the packed layout's rate
+            # (only where the library takes the folded path: bf16, d % 256 == 0,
+            # at most 16 sequences)
+            if self.pack_vocab and d % 256 == 0 and shape["B"] <= 16:
+                self.W1h = [H.hydra_pack_weight(w1[:, :d].contiguous()) for w1 in weights["W1"]]
 
     def draft(self, h, root_tok, stream=None):
         if self.attn is not None:
@@ -154,7 +161,7 @@ class HydraRound:
                                        self.head_lse, self.cand_tok, self.cand_logp, self.ws_draft,
                                        head_hidden=self.head_hidden, stream=stream)
             return
-        H.hydra_draft_heads(h, root_tok, self.w.get("emb"), self.w["W1"], self.w["b1"], self.W2, self.dplan,
+        H.hydra_draft_heads(h, root_tok, self.w.get("emb"), self.W1h or self.w["W1"], self.w["b1"], self.W2, self.dplan,
                             self.head_logits, self.head_lse, self.cand_tok, self.cand_logp, self.ws_draft,
                             head_hidden=self.head_hidden, residual=self.residual, emb_proj=self.emb_proj,
                             full_path=self.full_path, stream=stream)

@@ -590,6 +590,28 @@ def test_draft_four_heads_folded_and_streamed(tree, fold, residual):
     print(rep, flush=True)
 
 
+@pytest.mark.parametrize("d", [4096, 8192])
+def test_folded_heads_packed_h_halves_match_row_major(d):
+    """The folded round streams only the h halves of W1; read from their
+    packed copies (HYDRA_W1H_PACKED) they give bit-identical heads to the
+    row-major W1 (same products in the same order)."""
+    w = HI.workload("7b_sparse64", B=2, d=d, V=3000, L=(64,))
+    print(f"folded heads, packed h halves, d={d}", flush=True)
+    inp = HI.generate(w)
+    rnd, dev = T.round_inputs(inp, fold_embedding=True)
+    assert rnd.W1h is not None
+    outs = []
+    for packed in (True, False):
+        saved = rnd.W1h
+        rnd.W1h = saved if packed else None
+        rnd.draft(dev["h"], dev["root_tok"])
+        torch.cuda.synchronize()
+        outs.append([t.clone() for t in (rnd.cand_tok, rnd.cand_logp, rnd.head_logits, rnd.head_lse)])
+        rnd.W1h = saved
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
+
+
 @pytest.mark.parametrize("B,d,hid,V,tree", [
     (1, 4096, 1024, 32000, ("sparse", (10, 4, 2, 1), 64)),   # the 7B sketch shape
     (3, 256, 512, 1000, ("cartesian", (4, 3, 2))),

@@ -391,3 +391,18 @@ def test_packed_weight_size_and_the_mixing_rule(lib):
     assert _vocab_flag("t", [row, row]) == 0
     with pytest.raises(ValueError):
         _vocab_flag("t", [pw, row])
+
+
+def test_dtype_flags_match_the_header():
+    """The binding's dtype flags carry the values include/hydra.h defines
+    (the library parses them from the same integer)."""
+    import re
+
+    from speculative_decoding_hydra_amd import hydra as H
+
+    hdr = open(os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "hydra.h")).read()
+    for name in ("HYDRA_VOCAB_PACKED", "HYDRA_W1H_PACKED"):
+        m = re.search(rf"#define {name} (0x[0-9a-fA-F]+)", hdr)
+        assert m, name
+        assert getattr(H, name) == int(m.group(1), 16), name
+    assert len({H.HYDRA_VOCAB_PACKED, H.HYDRA_W1H_PACKED, 0x200}) == 3  # distinct bits (0x200: layer weights)
